@@ -1,0 +1,913 @@
+// C ABI of the decoder block: host-side validation, weight repacking, scratch
+// layout and the launch sequences of prefill and decode.  See llama_block.h for
+// the contract of every entry point.
+#include <cmath>
+#include <cstdarg>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+#include "llama_block.h"
+
+using namespace lb;
+
+// ---------------------------------------------------------------- errors
+static thread_local std::string g_err;
+
+static llama_status fail(llama_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+static llama_status hip_check(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(LLAMA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return LLAMA_OK;
+}
+
+#define HIP_TRY(call, what)                                                                  \
+  do {                                                                                       \
+    hipError_t _e = (call);                                                                  \
+    if (_e != hipSuccess) return fail(LLAMA_ERR_HIP, "%s: %s", what, hipGetErrorString(_e)); \
+  } while (0)
+
+extern "C" const char* llama_last_error(void) { return g_err.c_str(); }
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+static inline size_t esize(int dt) { return dt == LLAMA_F32 ? 4 : 2; }
+
+// ---------------------------------------------------------------- config
+struct Dims {
+  int D, H, G, d, F, Nq, Nkv, Nqkv, IB, n_rep;
+  bool bf16, q4;
+};
+
+static llama_status check_config(const llama_block_config* c, Dims* o) {
+  if (!c) return fail(LLAMA_ERR_INVALID_ARG, "config is NULL");
+  if (c->dim <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->ffn_dim <= 0 || c->max_seq <= 0)
+    return fail(LLAMA_ERR_INVALID_ARG, "dim, n_heads, n_kv_heads, ffn_dim and max_seq must be positive");
+  if (c->n_heads % c->n_kv_heads)
+    return fail(LLAMA_ERR_INVALID_ARG, "n_heads (%d) must be a multiple of n_kv_heads (%d)", c->n_heads, c->n_kv_heads);
+  if (c->dim % c->n_heads) return fail(LLAMA_ERR_INVALID_ARG, "dim (%d) must be a multiple of n_heads (%d)", c->dim, c->n_heads);
+  if (!(c->norm_eps > 0.f) || !std::isfinite(c->norm_eps)) return fail(LLAMA_ERR_INVALID_ARG, "norm_eps must be > 0");
+  if (!(c->rope_theta > 0.f) || !std::isfinite(c->rope_theta)) return fail(LLAMA_ERR_INVALID_ARG, "rope_theta must be > 0");
+  if (c->rope_traditional != 0 && c->rope_traditional != 1)
+    return fail(LLAMA_ERR_INVALID_ARG, "rope_traditional must be 0 or 1");
+  if (c->act_dtype != LLAMA_F32 && c->act_dtype != LLAMA_BF16) return fail(LLAMA_ERR_INVALID_ARG, "unknown act_dtype");
+  if (c->weight_format != LLAMA_W_DENSE && c->weight_format != LLAMA_W_Q4)
+    return fail(LLAMA_ERR_INVALID_ARG, "unknown weight_format");
+  Dims d{};
+  d.D = c->dim;
+  d.H = c->n_heads;
+  d.G = c->n_kv_heads;
+  d.d = c->dim / c->n_heads;
+  d.F = c->ffn_dim;
+  d.Nq = d.H * d.d;
+  d.Nkv = d.G * d.d;
+  d.Nqkv = d.Nq + 2 * d.Nkv;
+  d.n_rep = d.H / d.G;
+  d.bf16 = c->act_dtype == LLAMA_BF16;
+  d.q4 = c->weight_format == LLAMA_W_Q4;
+  if (d.d % 2) return fail(LLAMA_ERR_INVALID_ARG, "head_dim (%d) must be even for RoPE pairs", d.d);
+  if (d.bf16) {
+    if (d.d != 128) return fail(LLAMA_ERR_UNSUPPORTED, "bf16 path supports head_dim 128 only (got %d)", d.d);
+    if (d.D % 64 || d.F % 64) return fail(LLAMA_ERR_UNSUPPORTED, "bf16 path needs dim and ffn_dim multiples of 64");
+    if (d.n_rep > 16) return fail(LLAMA_ERR_UNSUPPORTED, "bf16 decode supports n_heads / n_kv_heads <= 16");
+    d.IB = 32;
+  } else {
+    if (d.d > 128) return fail(LLAMA_ERR_UNSUPPORTED, "fp32 path supports head_dim <= 128 (got %d)", d.d);
+    if (d.F % 16) return fail(LLAMA_ERR_UNSUPPORTED, "fp32 path needs ffn_dim multiple of 16");
+    d.IB = (d.F % 32) ? 16 : 32;
+  }
+  if (d.q4) {
+    if (!d.bf16) return fail(LLAMA_ERR_UNSUPPORTED, "4-bit weights need bf16 activations");
+    if (c->group_size != 64) return fail(LLAMA_ERR_UNSUPPORTED, "4-bit weights support group_size 64 only");
+  }
+  if (o) *o = d;
+  return LLAMA_OK;
+}
+
+// ---------------------------------------------------------------- weights
+struct Lin {            // a repacked linear inside the block's device memory
+  void* w = nullptr;    // dense E[N, K] or q4 uint32 [N, K/8]
+  bf16_t* s = nullptr;  // q4 scales [N, K/64]
+  bf16_t* b = nullptr;  // q4 biases
+  int N = 0, K = 0;
+};
+
+struct llama_block {
+  llama_block_config cfg;
+  Dims dm;
+  float2* rope;     // [max_seq][d/2]
+  float* gamma1;    // fp32 [D]
+  float* gamma2;
+  Lin qkv, o, w13, w2;
+};
+
+struct WLayout {
+  size_t rope, g1, g2, total;
+  size_t lin[4][3];  // per linear: w, s, b offsets
+};
+
+static void lin_shapes(const Dims& d, int NK[4][2]) {
+  NK[0][0] = d.Nqkv; NK[0][1] = d.D;
+  NK[1][0] = d.D;    NK[1][1] = d.Nq;
+  NK[2][0] = 2 * d.F; NK[2][1] = d.D;
+  NK[3][0] = d.D;    NK[3][1] = d.F;
+}
+
+static WLayout weight_layout(const llama_block_config& c, const Dims& d) {
+  WLayout L{};
+  size_t off = 0;
+  L.rope = off; off = align256(off + (size_t)c.max_seq * (d.d / 2) * sizeof(float2));
+  L.g1 = off; off = align256(off + (size_t)d.D * 4);
+  L.g2 = off; off = align256(off + (size_t)d.D * 4);
+  int NK[4][2];
+  lin_shapes(d, NK);
+  for (int i = 0; i < 4; ++i) {
+    size_t N = NK[i][0], K = NK[i][1];
+    L.lin[i][0] = off;
+    if (d.q4) {
+      off = align256(off + N * K / 2);
+      L.lin[i][1] = off; off = align256(off + N * (K / 64) * 2);
+      L.lin[i][2] = off; off = align256(off + N * (K / 64) * 2);
+    } else {
+      off = align256(off + N * K * esize(c.act_dtype));
+      L.lin[i][1] = L.lin[i][2] = 0;
+    }
+  }
+  L.total = off;
+  return L;
+}
+
+extern "C" size_t llama_block_weight_bytes(const llama_block_config* cfg) {
+  Dims d;
+  if (check_config(cfg, &d) != LLAMA_OK) return 0;
+  return weight_layout(*cfg, d).total;
+}
+
+static bool lin_ok(const llama_linear& l, bool q4) {
+  if (!l.w) return false;
+  if (q4 && (!l.scales || !l.biases)) return false;
+  return true;
+}
+
+// Copy one source linear into the repacked buffer with a row map (and, dense
+// only, a column scale).
+static void repack_linear(const Dims& d, int dt, const Lin& dst, const llama_linear& src, int rows, int K,
+                          const void* gamma, int row0, int ib, int ib_stride, int perm_d, hipStream_t s) {
+  if (d.q4) {
+    launch_repack_bytes((uint8_t*)dst.w, (const uint8_t*)src.w, rows, K / 2, row0, ib, ib_stride, perm_d, s);
+    launch_repack_bytes((uint8_t*)dst.s, (const uint8_t*)src.scales, rows, (K / 64) * 2, row0, ib, ib_stride, perm_d, s);
+    launch_repack_bytes((uint8_t*)dst.b, (const uint8_t*)src.biases, rows, (K / 64) * 2, row0, ib, ib_stride, perm_d, s);
+  } else if (dt == LLAMA_F32) {
+    launch_repack_rows<float>((float*)dst.w, (const float*)src.w, rows, K, (const float*)gamma, row0, ib, ib_stride,
+                              perm_d, s);
+  } else {
+    launch_repack_rows<bf16_t>((bf16_t*)dst.w, (const bf16_t*)src.w, rows, K, (const bf16_t*)gamma, row0, ib,
+                               ib_stride, perm_d, s);
+  }
+}
+
+extern "C" llama_status llama_block_create(const llama_block_config* cfg, const llama_block_weights* w, void* dev_mem,
+                                           size_t dev_bytes, void* stream, llama_block** out) {
+  Dims d;
+  llama_status st = check_config(cfg, &d);
+  if (st != LLAMA_OK) return st;
+  if (!w || !out || !dev_mem) return fail(LLAMA_ERR_INVALID_ARG, "weights, dev_mem and out must be non-NULL");
+  if (!w->attention_norm || !w->ffn_norm) return fail(LLAMA_ERR_INVALID_ARG, "norm weights must be non-NULL");
+  const llama_linear* ls[7] = {&w->wq, &w->wk, &w->wv, &w->wo, &w->w1, &w->w2, &w->w3};
+  for (int i = 0; i < 7; ++i)
+    if (!lin_ok(*ls[i], d.q4)) return fail(LLAMA_ERR_INVALID_ARG, "linear weight %d is incomplete", i);
+  if (((uintptr_t)dev_mem) & 255) return fail(LLAMA_ERR_INVALID_ARG, "dev_mem must be 256-byte aligned");
+  WLayout L = weight_layout(*cfg, d);
+  if (dev_bytes < L.total)
+    return fail(LLAMA_ERR_CAPACITY, "block memory too small: %zu < %zu bytes", dev_bytes, L.total);
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)dev_mem;
+
+  llama_block* b = new llama_block();
+  b->cfg = *cfg;
+  b->dm = d;
+  b->rope = (float2*)(base + L.rope);
+  b->gamma1 = (float*)(base + L.g1);
+  b->gamma2 = (float*)(base + L.g2);
+  Lin* lins[4] = {&b->qkv, &b->o, &b->w13, &b->w2};
+  int NK[4][2];
+  lin_shapes(d, NK);
+  for (int i = 0; i < 4; ++i) {
+    lins[i]->w = base + L.lin[i][0];
+    lins[i]->s = d.q4 ? (bf16_t*)(base + L.lin[i][1]) : nullptr;
+    lins[i]->b = d.q4 ? (bf16_t*)(base + L.lin[i][2]) : nullptr;
+    lins[i]->N = NK[i][0];
+    lins[i]->K = NK[i][1];
+  }
+
+  // RoPE table: angle = p * theta^(-2i/d), built in float64 (LLaMARoPE of page 二).
+  const int half = d.d / 2;
+  std::vector<float2> tab((size_t)cfg->max_seq * half);
+  for (int i = 0; i < half; ++i) {
+    const double w = std::pow((double)cfg->rope_theta, -2.0 * i / d.d);
+    for (int p = 0; p < cfg->max_seq; ++p) {
+      const double a = (double)p * w;
+      tab[(size_t)p * half + i] = make_float2((float)std::cos(a), (float)std::sin(a));
+    }
+  }
+  hipError_t e = hipMemcpyAsync(b->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) {
+    const int dt = cfg->act_dtype;
+    if (dt == LLAMA_F32) {
+      launch_to_f32<float>((const float*)w->attention_norm, b->gamma1, d.D, s);
+      launch_to_f32<float>((const float*)w->ffn_norm, b->gamma2, d.D, s);
+    } else {
+      launch_to_f32<bf16_t>((const bf16_t*)w->attention_norm, b->gamma1, d.D, s);
+      launch_to_f32<bf16_t>((const bf16_t*)w->ffn_norm, b->gamma2, d.D, s);
+    }
+    // dense weights take the norm weight of the RMSNorm in front of them:
+    // (x * r * gamma) W^T = r * (x (W diag(gamma))^T)
+    const void* g1 = d.q4 ? nullptr : w->attention_norm;
+    const void* g2 = d.q4 ? nullptr : w->ffn_norm;
+    const int pd = cfg->rope_traditional ? d.d : 0;
+    const int big = 1 << 30;
+    repack_linear(d, dt, b->qkv, w->wq, d.Nq, d.D, g1, 0, big, 0, pd, s);
+    repack_linear(d, dt, b->qkv, w->wk, d.Nkv, d.D, g1, d.Nq, big, 0, pd, s);
+    repack_linear(d, dt, b->qkv, w->wv, d.Nkv, d.D, g1, d.Nq + d.Nkv, big, 0, 0, s);
+    repack_linear(d, dt, b->o, w->wo, d.D, d.Nq, nullptr, 0, big, 0, 0, s);
+    repack_linear(d, dt, b->w13, w->w1, d.F, d.D, g2, 0, d.IB, 2 * d.IB, 0, s);
+    repack_linear(d, dt, b->w13, w->w3, d.F, d.D, g2, d.IB, d.IB, 2 * d.IB, 0, s);
+    repack_linear(d, dt, b->w2, w->w2, d.D, d.F, nullptr, 0, big, 0, 0, s);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    delete b;
+    return fail(LLAMA_ERR_HIP, "block create: %s", hipGetErrorString(e));
+  }
+  *out = b;
+  return LLAMA_OK;
+}
+
+extern "C" void llama_block_destroy(llama_block* b) { delete b; }
+
+// ---------------------------------------------------------------- cache
+struct llama_kvcache {
+  llama_kvcache_config cfg;
+  int pps, n_pages;
+  size_t page_elems, layer_bytes;
+  char* k_pool;
+  char* v_pool;
+  int32_t* table;
+  int32_t* lens;
+  std::vector<int32_t> lens_host;   // [n_layers][max_batch]
+  std::vector<int32_t> table_host;
+};
+
+struct CLayout {
+  size_t k, v, table, lens, total;
+  int pps, n_pages;
+  size_t page_elems, layer_bytes;
+};
+
+static llama_status check_cache_config(const llama_kvcache_config* c) {
+  if (!c) return fail(LLAMA_ERR_INVALID_ARG, "cache config is NULL");
+  if (c->n_layers <= 0 || c->max_batch <= 0 || c->max_seq <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->page_size <= 0)
+    return fail(LLAMA_ERR_INVALID_ARG, "cache dimensions must be positive");
+  if (c->page_size % 64) return fail(LLAMA_ERR_UNSUPPORTED, "page_size must be a multiple of 64");
+  if (c->dtype != LLAMA_F32 && c->dtype != LLAMA_BF16) return fail(LLAMA_ERR_INVALID_ARG, "unknown cache dtype");
+  if (c->max_batch > 256) return fail(LLAMA_ERR_UNSUPPORTED, "max_batch above 256");
+  return LLAMA_OK;
+}
+
+static CLayout cache_layout(const llama_kvcache_config& c) {
+  CLayout L{};
+  L.pps = (c.max_seq + c.page_size - 1) / c.page_size;
+  L.n_pages = c.max_batch * L.pps;
+  L.page_elems = (size_t)c.n_kv_heads * c.page_size * c.head_dim;
+  L.layer_bytes = (size_t)L.n_pages * L.page_elems * esize(c.dtype);
+  size_t off = 0;
+  L.k = off; off = align256(off + L.layer_bytes * c.n_layers);
+  L.v = off; off = align256(off + L.layer_bytes * c.n_layers);
+  L.table = off; off = align256(off + (size_t)L.n_pages * 4);
+  L.lens = off; off = align256(off + (size_t)c.n_layers * c.max_batch * 4);
+  L.total = off;
+  return L;
+}
+
+extern "C" size_t llama_kvcache_bytes(const llama_kvcache_config* c) {
+  if (check_cache_config(c) != LLAMA_OK) return 0;
+  return cache_layout(*c).total;
+}
+
+extern "C" llama_status llama_kvcache_init(const llama_kvcache_config* c, void* mem, size_t bytes, void* stream,
+                                           llama_kvcache** out) {
+  llama_status st = check_cache_config(c);
+  if (st != LLAMA_OK) return st;
+  if (!mem || !out) return fail(LLAMA_ERR_INVALID_ARG, "dev_mem and out must be non-NULL");
+  if (((uintptr_t)mem) & 255) return fail(LLAMA_ERR_INVALID_ARG, "dev_mem must be 256-byte aligned");
+  CLayout L = cache_layout(*c);
+  if (bytes < L.total) return fail(LLAMA_ERR_CAPACITY, "cache memory too small: %zu < %zu bytes", bytes, L.total);
+  llama_kvcache* kc = new llama_kvcache();
+  kc->cfg = *c;
+  kc->pps = L.pps;
+  kc->n_pages = L.n_pages;
+  kc->page_elems = L.page_elems;
+  kc->layer_bytes = L.layer_bytes;
+  kc->k_pool = (char*)mem + L.k;
+  kc->v_pool = (char*)mem + L.v;
+  kc->table = (int32_t*)((char*)mem + L.table);
+  kc->lens = (int32_t*)((char*)mem + L.lens);
+  kc->lens_host.assign((size_t)c->n_layers * c->max_batch, 0);
+  kc->table_host.resize(L.n_pages);
+  for (int i = 0; i < L.n_pages; ++i) kc->table_host[i] = i;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(kc->table, kc->table_host.data(), (size_t)L.n_pages * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) {
+    launch_fill_i32(kc->lens, c->n_layers * c->max_batch, 0, s);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    delete kc;
+    return fail(LLAMA_ERR_HIP, "cache init: %s", hipGetErrorString(e));
+  }
+  *out = kc;
+  return LLAMA_OK;
+}
+
+extern "C" void llama_kvcache_destroy(llama_kvcache* c) { delete c; }
+
+extern "C" llama_status llama_kvcache_set_block_table(llama_kvcache* c, const int32_t* t, void* stream) {
+  if (!c || !t) return fail(LLAMA_ERR_INVALID_ARG, "cache and table must be non-NULL");
+  std::vector<char> seen(c->n_pages, 0);
+  for (int i = 0; i < c->n_pages; ++i) {
+    if (t[i] < 0 || t[i] >= c->n_pages || seen[t[i]])
+      return fail(LLAMA_ERR_INVALID_ARG, "block table is not a permutation of 0..%d", c->n_pages - 1);
+    seen[t[i]] = 1;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(hipStreamSynchronize(s), "set_block_table");
+  HIP_TRY(hipMemcpy(c->table, t, (size_t)c->n_pages * 4, hipMemcpyHostToDevice), "set_block_table");
+  c->table_host.assign(t, t + c->n_pages);
+  return LLAMA_OK;
+}
+
+extern "C" llama_status llama_kvcache_set_lens(llama_kvcache* c, int32_t layer, const int32_t* lens, int32_t batch,
+                                               void* stream) {
+  if (!c || !lens) return fail(LLAMA_ERR_INVALID_ARG, "cache and lens must be non-NULL");
+  if (layer < -1 || layer >= c->cfg.n_layers) return fail(LLAMA_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (batch <= 0 || batch > c->cfg.max_batch) return fail(LLAMA_ERR_INVALID_ARG, "batch %d out of range", batch);
+  for (int b = 0; b < batch; ++b)
+    if (lens[b] < 0 || lens[b] > c->cfg.max_seq) return fail(LLAMA_ERR_CAPACITY, "lens[%d] = %d exceeds max_seq", b, lens[b]);
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(hipStreamSynchronize(s), "set_lens");
+  int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c->cfg.n_layers : layer + 1;
+  for (int l = l0; l < l1; ++l) {
+    HIP_TRY(hipMemcpy(c->lens + (size_t)l * c->cfg.max_batch, lens, (size_t)batch * 4, hipMemcpyHostToDevice), "set_lens");
+    std::memcpy(&c->lens_host[(size_t)l * c->cfg.max_batch], lens, (size_t)batch * 4);
+  }
+  return LLAMA_OK;
+}
+
+extern "C" llama_status llama_kvcache_get_lens(const llama_kvcache* c, int32_t layer, int32_t* lens, int32_t batch) {
+  if (!c || !lens) return fail(LLAMA_ERR_INVALID_ARG, "cache and lens must be non-NULL");
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(LLAMA_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (batch <= 0 || batch > c->cfg.max_batch) return fail(LLAMA_ERR_INVALID_ARG, "batch %d out of range", batch);
+  std::memcpy(lens, &c->lens_host[(size_t)layer * c->cfg.max_batch], (size_t)batch * 4);
+  return LLAMA_OK;
+}
+
+static KVView kv_view(const llama_kvcache* c, int layer) {
+  KVView v;
+  v.k = c->k_pool + (size_t)layer * c->layer_bytes;
+  v.v = c->v_pool + (size_t)layer * c->layer_bytes;
+  v.table = c->table;
+  v.lens = c->lens + (size_t)layer * c->cfg.max_batch;
+  v.G = c->cfg.n_kv_heads;
+  v.d = c->cfg.head_dim;
+  v.ps = c->cfg.page_size;
+  v.pps = c->pps;
+  return v;
+}
+
+static llama_status kv_copy_check(const llama_kvcache* c, int layer, int seq, int pos0, int n, const void* k,
+                                  const void* v) {
+  if (!c || !k || !v) return fail(LLAMA_ERR_INVALID_ARG, "cache, k and v must be non-NULL");
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(LLAMA_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (seq < 0 || seq >= c->cfg.max_batch) return fail(LLAMA_ERR_INVALID_ARG, "seq %d out of range", seq);
+  if (pos0 < 0 || n < 0) return fail(LLAMA_ERR_INVALID_ARG, "pos0 and n must be >= 0");
+  if ((long)pos0 + n > c->cfg.max_seq) return fail(LLAMA_ERR_CAPACITY, "positions beyond max_seq");
+  return LLAMA_OK;
+}
+
+extern "C" llama_status llama_kvcache_write(llama_kvcache* c, int32_t layer, int32_t seq, int32_t pos0, int32_t n,
+                                            const void* k, const void* v, void* stream) {
+  llama_status st = kv_copy_check(c, layer, seq, pos0, n, k, v);
+  if (st != LLAMA_OK) return st;
+  KVView kv = kv_view(c, layer);
+  if (c->cfg.dtype == LLAMA_F32)
+    launch_kv_write<float>(kv, seq, pos0, n, (const float*)k, (const float*)v, (hipStream_t)stream);
+  else
+    launch_kv_write<bf16_t>(kv, seq, pos0, n, (const bf16_t*)k, (const bf16_t*)v, (hipStream_t)stream);
+  return hip_check("kvcache_write");
+}
+
+extern "C" llama_status llama_kvcache_read(const llama_kvcache* c, int32_t layer, int32_t seq, int32_t pos0, int32_t n,
+                                           void* k, void* v, void* stream) {
+  llama_status st = kv_copy_check(c, layer, seq, pos0, n, k, v);
+  if (st != LLAMA_OK) return st;
+  KVView kv = kv_view(c, layer);
+  if (c->cfg.dtype == LLAMA_F32)
+    launch_kv_read<float>(kv, seq, pos0, n, (float*)k, (float*)v, (hipStream_t)stream);
+  else
+    launch_kv_read<bf16_t>(kv, seq, pos0, n, (bf16_t*)k, (bf16_t*)v, (hipStream_t)stream);
+  return hip_check("kvcache_read");
+}
+
+// ---------------------------------------------------------------- scratch
+static const int kSplitLen = 256;  // keys per decode-attention chunk
+
+// Split-K factor of a decode projection [M rows] x [N, K]: enough blocks to
+// cover the chip several times over, K slices that stay multiples of 32 and at
+// least 512 long.
+static int gemv_ks(int M, int N, int K) {
+  const int cols = (M > 16 && N % 128 == 0) ? 128 : 64;
+  const int tiles = N / cols;
+  int ks = 1;
+  while (tiles * ks < 768 && (K % (64 * ks)) == 0 && K / (2 * ks) >= 512) ks *= 2;
+  return ks;
+}
+
+struct SLayout {
+  size_t inv1, inv2, q, attn, h, g, part, ao, aml, xh, xsum, deq, total;
+  int n_splits;
+};
+
+// T = rows of this call (batch * seq_len), B = batch, decode = one-token call.
+static SLayout scratch_layout(const llama_block_config& c, const Dims& d, int T, int B, int max_seq, bool decode) {
+  SLayout L{};
+  const size_t E = esize(c.act_dtype);
+  size_t off = 0;
+  L.inv1 = off; off = align256(off + (size_t)T * 4);
+  L.inv2 = off; off = align256(off + (size_t)T * 4);
+  L.q = off; off = align256(off + (size_t)T * d.Nq * E);
+  L.attn = off; off = align256(off + (size_t)T * d.Nq * E);
+  L.h = off; off = align256(off + (size_t)T * d.D * E);
+  L.g = off; off = align256(off + (size_t)T * d.F * E);
+  size_t part = 0;
+  const int maxN = std::max(std::max(d.Nqkv, 2 * d.F), d.D);
+  if (!d.bf16) {
+    part = (size_t)T * maxN * 4;
+  } else if (decode && !d.q4) {
+    int NK[4][2];
+    lin_shapes(d, NK);
+    for (int i = 0; i < 4; ++i)
+      part = std::max(part, (size_t)gemv_ks(T, NK[i][0], NK[i][1]) * T * NK[i][0] * 4);
+  } else if (decode && d.q4) {
+    part = (size_t)T * maxN * 4;
+  }
+  L.part = off; off = align256(off + part);
+  L.n_splits = (max_seq + kSplitLen - 1) / kSplitLen;
+  size_t ao = (d.bf16 && decode) ? (size_t)B * d.H * L.n_splits * 128 * 4 : 0;
+  size_t aml = (d.bf16 && decode) ? (size_t)B * d.H * L.n_splits * 2 * 4 : 0;
+  L.ao = off; off = align256(off + ao);
+  L.aml = off; off = align256(off + aml);
+  const int maxK = std::max(std::max(d.D, d.Nq), d.F);
+  size_t xh = (d.q4 && decode) ? (size_t)T * maxK * 2 : 0;
+  size_t xs = (d.q4 && decode) ? (size_t)T * (maxK / 32) * 2 * 4 : 0;
+  L.xh = off; off = align256(off + xh);
+  L.xsum = off; off = align256(off + xs);
+  size_t deq = 0;
+  if (d.q4 && !decode) {
+    int NK[4][2];
+    lin_shapes(d, NK);
+    for (int i = 0; i < 4; ++i) deq = std::max(deq, (size_t)NK[i][0] * NK[i][1] * 2);
+  }
+  L.deq = off; off = align256(off + deq);
+  L.total = off;
+  return L;
+}
+
+extern "C" size_t llama_scratch_bytes(const llama_block_config* cfg, int32_t max_tokens, int32_t max_batch,
+                                      int32_t max_seq) {
+  Dims d;
+  if (check_config(cfg, &d) != LLAMA_OK || max_tokens < 0 || max_batch < 0 || max_seq <= 0) return 0;
+  size_t a = max_tokens > 0 ? scratch_layout(*cfg, d, max_tokens, std::max(1, max_batch), max_seq, false).total : 0;
+  size_t b = max_batch > 0 ? scratch_layout(*cfg, d, max_batch, max_batch, max_seq, true).total : 0;
+  return std::max(a, b);
+}
+
+extern "C" llama_status llama_block_diag(const llama_block* blk, void* scratch, int32_t which, int32_t tokens,
+                                         void** ptr) {
+  if (!blk || !scratch || !ptr) return fail(LLAMA_ERR_INVALID_ARG, "block, scratch and ptr must be non-NULL");
+  if (tokens <= 0) return fail(LLAMA_ERR_INVALID_ARG, "tokens must be positive");
+  SLayout L = scratch_layout(blk->cfg, blk->dm, tokens, 1, 1, false);
+  if (which == LLAMA_DIAG_ATTN) *ptr = (char*)scratch + L.attn;
+  else if (which == LLAMA_DIAG_H) *ptr = (char*)scratch + L.h;
+  else return fail(LLAMA_ERR_INVALID_ARG, "unknown diagnostic %d", which);
+  return LLAMA_OK;
+}
+
+// ---------------------------------------------------------------- block calls
+static llama_status check_call(const llama_block* blk, const llama_kvcache* c, int layer, const void* x, const void* y,
+                               int batch, int L, void* scratch, size_t sbytes, bool decode, SLayout* lay) {
+  if (!blk || !c) return fail(LLAMA_ERR_INVALID_ARG, "block and cache must be non-NULL");
+  if (!x || !y || !scratch) return fail(LLAMA_ERR_INVALID_ARG, "x, y and scratch must be non-NULL");
+  if (((uintptr_t)scratch) & 255) return fail(LLAMA_ERR_INVALID_ARG, "scratch must be 256-byte aligned");
+  const Dims& d = blk->dm;
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(LLAMA_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (batch <= 0 || batch > c->cfg.max_batch)
+    return fail(LLAMA_ERR_INVALID_ARG, "batch %d outside 1..%d", batch, c->cfg.max_batch);
+  if (L <= 0) return fail(LLAMA_ERR_INVALID_ARG, "seq_len must be positive");
+  if (c->cfg.n_kv_heads != d.G || c->cfg.head_dim != d.d || c->cfg.dtype != blk->cfg.act_dtype)
+    return fail(LLAMA_ERR_INVALID_ARG, "cache (kv heads %d, head_dim %d, dtype %d) does not match the block",
+                c->cfg.n_kv_heads, c->cfg.head_dim, c->cfg.dtype);
+  if (decode && d.q4 && batch > 4) return fail(LLAMA_ERR_UNSUPPORTED, "4-bit decode supports batch <= 4");
+  if (decode && d.bf16 && !d.q4 && batch > 64) return fail(LLAMA_ERR_UNSUPPORTED, "bf16 decode supports batch <= 64");
+  const int cap = std::min(c->cfg.max_seq, blk->cfg.max_seq);
+  int maxlen = 0;
+  for (int b = 0; b < batch; ++b) {
+    int len = c->lens_host[(size_t)layer * c->cfg.max_batch + b];
+    if ((long)len + L > cap)
+      return fail(LLAMA_ERR_CAPACITY, "sequence %d: %d cached + %d new exceeds capacity %d", b, len, L, cap);
+    maxlen = std::max(maxlen, len + L);
+  }
+  SLayout lo = scratch_layout(blk->cfg, d, batch * L, batch, c->cfg.max_seq, decode);
+  if (sbytes < lo.total) return fail(LLAMA_ERR_CAPACITY, "scratch too small: %zu < %zu bytes", sbytes, lo.total);
+  lo.n_splits = (maxlen + kSplitLen - 1) / kSplitLen;
+  *lay = lo;
+  return LLAMA_OK;
+}
+
+template <typename T>
+static void fp32_path(const llama_block* blk, KVView kv, const void* x, void* y, int B, int L, char* sc,
+                      const SLayout& S, hipStream_t s) {
+  const Dims& d = blk->dm;
+  const int M = B * L;
+  float* inv1 = (float*)(sc + S.inv1);
+  float* inv2 = (float*)(sc + S.inv2);
+  T* q = (T*)(sc + S.q);
+  T* attn = (T*)(sc + S.attn);
+  T* h = (T*)(sc + S.h);
+  T* g = (T*)(sc + S.g);
+  float* part = (float*)(sc + S.part);
+  const float eps = blk->cfg.norm_eps;
+  launch_rms_inv<T>((const T*)x, M, d.D, eps, inv1, s);
+  launch_gemm_simt<T>((const T*)x, (const T*)blk->qkv.w, part, M, d.Nqkv, d.D, s);
+  launch_epi_qkv<T>(part, 1, M, d.Nq, d.Nkv, inv1, L, blk->rope, blk->cfg.rope_traditional, q, kv, s);
+  launch_attn_simt<T>(q, kv, B, L, d.H, d.G, d.d, attn, s);
+  launch_gemm_simt<T>(attn, (const T*)blk->o.w, part, M, d.D, d.Nq, s);
+  launch_epi_resid<T>(part, 1, M, d.D, (const T*)x, h, eps, inv2, nullptr, 0, 0, s);
+  launch_gemm_simt<T>(h, (const T*)blk->w13.w, part, M, 2 * d.F, d.D, s);
+  launch_epi_swiglu<T>(part, 1, M, 2 * d.F, d.IB, inv2, g, s);
+  launch_gemm_simt<T>(g, (const T*)blk->w2.w, part, M, d.D, d.F, s);
+  launch_epi_resid<T>(part, 1, M, d.D, h, (T*)y, eps, nullptr, kv.lens, L, B, s);
+}
+
+static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void* y, int B, int L, char* sc,
+                         const SLayout& S, hipStream_t s) {
+  const Dims& d = blk->dm;
+  const int M = B * L;
+  float* inv1 = (float*)(sc + S.inv1);
+  float* inv2 = (float*)(sc + S.inv2);
+  bf16_t* q = (bf16_t*)(sc + S.q);
+  bf16_t* attn = (bf16_t*)(sc + S.attn);
+  bf16_t* h = (bf16_t*)(sc + S.h);
+  bf16_t* g = (bf16_t*)(sc + S.g);
+  bf16_t* deq = (bf16_t*)(sc + S.deq);
+  const float eps = blk->cfg.norm_eps;
+  auto weight = [&](const Lin& lin, const float* gamma) -> const bf16_t* {
+    if (!d.q4) return (const bf16_t*)lin.w;
+    launch_q4_dequant((const uint32_t*)lin.w, lin.s, lin.b, lin.N, lin.K, 64, gamma, deq, s);
+    return deq;
+  };
+  launch_rms_inv<bf16_t>((const bf16_t*)x, M, d.D, eps, inv1, s);
+  GemmArgs a{};
+  a.A = (const bf16_t*)x;
+  a.B = weight(blk->qkv, blk->gamma1);
+  a.M = M; a.N = d.Nqkv; a.K = d.D;
+  a.inv_rms = inv1;
+  a.q_out = q; a.Nq = d.Nq; a.Nkv = d.Nkv; a.L = L;
+  a.rope = blk->rope; a.traditional = blk->cfg.rope_traditional;
+  a.kv = kv;
+  launch_gemm_mfma(EPI_QKV, a, s);
+  launch_attn_prefill_bf16(q, kv, B, L, d.H, d.G, attn, s);
+  GemmArgs o{};
+  o.A = attn; o.B = weight(blk->o, nullptr); o.M = M; o.N = d.D; o.K = d.Nq;
+  o.resid = (const bf16_t*)x; o.out = h;
+  launch_gemm_mfma(EPI_RESID, o, s);
+  launch_rms_inv<bf16_t>(h, M, d.D, eps, inv2, s);
+  GemmArgs f{};
+  f.A = h; f.B = weight(blk->w13, blk->gamma2); f.M = M; f.N = 2 * d.F; f.K = d.D;
+  f.inv_rms = inv2; f.g_out = g;
+  launch_gemm_mfma(EPI_SWIGLU, f, s);
+  GemmArgs w2{};
+  w2.A = g; w2.B = weight(blk->w2, nullptr); w2.M = M; w2.N = d.D; w2.K = d.F;
+  w2.resid = h; w2.out = (bf16_t*)y;
+  w2.lens_add = kv.lens; w2.lens_inc = L; w2.n_seq = B;
+  launch_gemm_mfma(EPI_RESID, w2, s);
+}
+
+static void bf16_decode(const llama_block* blk, KVView kv, const void* x, void* y, int B, char* sc, const SLayout& S,
+                        int n_splits, hipStream_t s) {
+  const Dims& d = blk->dm;
+  float* inv1 = (float*)(sc + S.inv1);
+  float* inv2 = (float*)(sc + S.inv2);
+  bf16_t* q = (bf16_t*)(sc + S.q);
+  bf16_t* attn = (bf16_t*)(sc + S.attn);
+  bf16_t* h = (bf16_t*)(sc + S.h);
+  bf16_t* g = (bf16_t*)(sc + S.g);
+  float* part = (float*)(sc + S.part);
+  float* ao = (float*)(sc + S.ao);
+  float* aml = (float*)(sc + S.aml);
+  const float eps = blk->cfg.norm_eps;
+  launch_rms_inv<bf16_t>((const bf16_t*)x, B, d.D, eps, inv1, s);
+  if (!d.q4) {
+    int ks = gemv_ks(B, d.Nqkv, d.D);
+    launch_gemv_bf16((const bf16_t*)x, (const bf16_t*)blk->qkv.w, part, B, d.Nqkv, d.D, ks, s);
+    launch_epi_qkv<bf16_t>(part, ks, B, d.Nq, d.Nkv, inv1, 1, blk->rope, blk->cfg.rope_traditional, q, kv, s);
+    launch_attn_decode_bf16(q, kv, B, d.H, d.G, n_splits, kSplitLen, ao, aml, attn, s);
+    ks = gemv_ks(B, d.D, d.Nq);
+    launch_gemv_bf16(attn, (const bf16_t*)blk->o.w, part, B, d.D, d.Nq, ks, s);
+    launch_epi_resid<bf16_t>(part, ks, B, d.D, (const bf16_t*)x, h, eps, inv2, nullptr, 0, 0, s);
+    ks = gemv_ks(B, 2 * d.F, d.D);
+    launch_gemv_bf16(h, (const bf16_t*)blk->w13.w, part, B, 2 * d.F, d.D, ks, s);
+    launch_epi_swiglu<bf16_t>(part, ks, B, 2 * d.F, d.IB, inv2, g, s);
+    ks = gemv_ks(B, d.D, d.F);
+    launch_gemv_bf16(g, (const bf16_t*)blk->w2.w, part, B, d.D, d.F, ks, s);
+    launch_epi_resid<bf16_t>(part, ks, B, d.D, h, (bf16_t*)y, eps, nullptr, kv.lens, 1, B, s);
+  } else {
+    _Float16* xh = (_Float16*)(sc + S.xh);
+    float* xs = (float*)(sc + S.xsum);
+    auto gq = [&](const bf16_t* X, const float* inv, const float* gam, const Lin& lin) {
+      launch_gemv_q4(X, inv, gam, (const uint32_t*)lin.w, lin.s, lin.b, part, B, lin.N, lin.K, 64, xh, xs, s);
+    };
+    gq((const bf16_t*)x, inv1, blk->gamma1, blk->qkv);
+    launch_epi_qkv<bf16_t>(part, 1, B, d.Nq, d.Nkv, nullptr, 1, blk->rope, blk->cfg.rope_traditional, q, kv, s);
+    launch_attn_decode_bf16(q, kv, B, d.H, d.G, n_splits, kSplitLen, ao, aml, attn, s);
+    gq(attn, nullptr, nullptr, blk->o);
+    launch_epi_resid<bf16_t>(part, 1, B, d.D, (const bf16_t*)x, h, eps, inv2, nullptr, 0, 0, s);
+    gq(h, inv2, blk->gamma2, blk->w13);
+    launch_epi_swiglu<bf16_t>(part, 1, B, 2 * d.F, d.IB, nullptr, g, s);
+    gq(g, nullptr, nullptr, blk->w2);
+    launch_epi_resid<bf16_t>(part, 1, B, d.D, h, (bf16_t*)y, eps, nullptr, kv.lens, 1, B, s);
+  }
+}
+
+// Enqueue one block call.  n_splits_override > 0 fixes the decode attention
+// grid (graph capture, where lengths grow between replays).
+static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const void* x, void* y, int batch, int L,
+                            void* scratch, size_t sbytes, bool decode, int n_splits_override, hipStream_t s) {
+  SLayout S;
+  llama_status st = check_call(blk, c, layer, x, y, batch, L, scratch, sbytes, decode, &S);
+  if (st != LLAMA_OK) return st;
+  KVView kv = kv_view(c, layer);
+  char* sc = (char*)scratch;
+  const Dims& d = blk->dm;
+  if (!d.bf16) {
+    fp32_path<float>(blk, kv, x, y, batch, L, sc, S, s);
+  } else if (!decode) {
+    bf16_prefill(blk, kv, x, y, batch, L, sc, S, s);
+  } else {
+    bf16_decode(blk, kv, x, y, batch, sc, S, n_splits_override > 0 ? n_splits_override : S.n_splits, s);
+  }
+  st = hip_check(decode ? "block decode" : "block prefill");
+  if (st != LLAMA_OK) return st;
+  for (int b = 0; b < batch; ++b) c->lens_host[(size_t)layer * c->cfg.max_batch + b] += L;
+  return LLAMA_OK;
+}
+
+extern "C" llama_status llama_block_prefill(llama_block* blk, llama_kvcache* c, int32_t layer, const void* x, void* y,
+                                            int32_t batch, int32_t seq_len, void* scratch, size_t sbytes, void* stream) {
+  return enqueue(blk, c, layer, x, y, batch, seq_len, scratch, sbytes, false, 0, (hipStream_t)stream);
+}
+
+extern "C" llama_status llama_block_decode(llama_block* blk, llama_kvcache* c, int32_t layer, const void* x, void* y,
+                                           int32_t batch, void* scratch, size_t sbytes, void* stream) {
+  return enqueue(blk, c, layer, x, y, batch, 1, scratch, sbytes, true, 0, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------- stack ends
+extern "C" llama_status llama_embed(const void* table, int32_t vocab, int32_t dim, int32_t dtype, const int32_t* ids,
+                                    int32_t n, void* out, void* stream) {
+  if (!table || !ids || !out) return fail(LLAMA_ERR_INVALID_ARG, "table, ids and out must be non-NULL");
+  if (vocab <= 0 || dim <= 0 || n < 0) return fail(LLAMA_ERR_INVALID_ARG, "vocab and dim must be positive, n >= 0");
+  if (dtype == LLAMA_F32)
+    launch_embed<float>((const float*)table, vocab, dim, ids, n, (float*)out, (hipStream_t)stream);
+  else if (dtype == LLAMA_BF16)
+    launch_embed<bf16_t>((const bf16_t*)table, vocab, dim, ids, n, (bf16_t*)out, (hipStream_t)stream);
+  else
+    return fail(LLAMA_ERR_INVALID_ARG, "unknown dtype");
+  return hip_check("embed");
+}
+
+struct HLayout {
+  size_t inv, gam, xn, logits, part, xh, xsum, total;
+};
+static HLayout head_layout(int B, int D, int V) {
+  HLayout L{};
+  size_t off = 0;
+  L.inv = off; off = align256(off + (size_t)B * 4);
+  L.gam = off; off = align256(off + (size_t)D * 4);
+  L.xn = off; off = align256(off + (size_t)B * D * 4);
+  L.logits = off; off = align256(off + (size_t)B * V * 4);
+  L.part = off; off = align256(off + (size_t)B * V * 4);
+  L.xh = off; off = align256(off + (size_t)B * D * 2);
+  L.xsum = off; off = align256(off + (size_t)B * (D / 32 + 1) * 2 * 4);
+  L.total = off;
+  return L;
+}
+
+extern "C" size_t llama_head_scratch_bytes(int32_t batch, int32_t dim, int32_t vocab) {
+  if (batch <= 0 || dim <= 0 || vocab <= 0) return 0;
+  return head_layout(batch, dim, vocab).total;
+}
+
+static llama_status head_enqueue(const llama_linear* head, int wf, int gs, int dt, const void* fnorm, float eps,
+                                 const void* x, int B, int D, int V, float* logits, int32_t* ids, void* scratch,
+                                 size_t sbytes, hipStream_t s) {
+  if (!head || !head->w || !fnorm || !x || !ids || !scratch)
+    return fail(LLAMA_ERR_INVALID_ARG, "head, final_norm, x, ids and scratch must be non-NULL");
+  if (B <= 0 || D <= 0 || V <= 0) return fail(LLAMA_ERR_INVALID_ARG, "batch, dim and vocab must be positive");
+  if (wf == LLAMA_W_Q4) {
+    if (dt != LLAMA_BF16 || gs != 64 || D % 64 || B > 4 || !head->scales || !head->biases)
+      return fail(LLAMA_ERR_UNSUPPORTED, "4-bit head needs bf16 activations, group 64, dim % 64 == 0, batch <= 4");
+  } else if (wf != LLAMA_W_DENSE) {
+    return fail(LLAMA_ERR_INVALID_ARG, "unknown weight_format");
+  }
+  if (dt != LLAMA_F32 && dt != LLAMA_BF16) return fail(LLAMA_ERR_INVALID_ARG, "unknown act_dtype");
+  if (wf == LLAMA_W_DENSE && dt == LLAMA_BF16 && (D % 32 || V % 64))
+    return fail(LLAMA_ERR_UNSUPPORTED, "dense bf16 head needs dim % 32 == 0 and vocab % 64 == 0");
+  HLayout L = head_layout(B, D, V);
+  if (sbytes < L.total) return fail(LLAMA_ERR_CAPACITY, "head scratch too small: %zu < %zu", sbytes, L.total);
+  char* sc = (char*)scratch;
+  float* out = logits ? logits : (float*)(sc + L.logits);
+  if (wf == LLAMA_W_Q4) {
+    float* inv = (float*)(sc + L.inv);
+    float* gam = (float*)(sc + L.gam);
+    launch_rms_inv<bf16_t>((const bf16_t*)x, B, D, eps, inv, s);
+    launch_to_f32<bf16_t>((const bf16_t*)fnorm, gam, D, s);
+    launch_gemv_q4((const bf16_t*)x, inv, gam, (const uint32_t*)head->w, (const bf16_t*)head->scales,
+                   (const bf16_t*)head->biases, out, B, V, D, gs, (_Float16*)(sc + L.xh), (float*)(sc + L.xsum), s);
+  } else if (dt == LLAMA_F32) {
+    launch_rmsnorm_apply<float>((const float*)x, (const float*)fnorm, B, D, eps, (float*)(sc + L.xn), s);
+    launch_gemm_simt<float>((const float*)(sc + L.xn), (const float*)head->w, out, B, V, D, s);
+  } else {
+    launch_rmsnorm_apply<bf16_t>((const bf16_t*)x, (const bf16_t*)fnorm, B, D, eps, (bf16_t*)(sc + L.xn), s);
+    launch_gemv_bf16((const bf16_t*)(sc + L.xn), (const bf16_t*)head->w, out, B, V, D, 1, s);
+  }
+  launch_argmax(out, B, V, ids, s);
+  return hip_check("lm_head_argmax");
+}
+
+extern "C" llama_status llama_lm_head_argmax(const llama_linear* head, int32_t wf, int32_t gs, int32_t dt,
+                                             const void* fnorm, float eps, const void* x, int32_t B, int32_t D,
+                                             int32_t V, float* logits, int32_t* ids, void* scratch, size_t sbytes,
+                                             void* stream) {
+  return head_enqueue(head, wf, gs, dt, fnorm, eps, x, B, D, V, logits, ids, scratch, sbytes, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------- greedy generate
+// The generation loop of "生成过程" (MLX page): the prompt pass fills every
+// layer's cache and yields the first id; each decode step embeds the newest id
+// (read on the device, never copied to the host), runs every block on its cache
+// and yields the next.  One decode step is captured into a HIP graph and replayed.
+struct llama_stack {
+  std::vector<llama_block*> blocks;
+  const void* emb;
+  int vocab;
+  const void* fnorm;
+  llama_linear head;
+};
+
+extern "C" llama_status llama_stack_create(llama_block* const* blocks, int32_t n_layers, const void* embedding,
+                                           int32_t vocab, const void* final_norm, const llama_linear* output,
+                                           llama_stack** out) {
+  if (!blocks || n_layers <= 0 || !embedding || !final_norm || !output || !output->w || !out || vocab <= 0)
+    return fail(LLAMA_ERR_INVALID_ARG, "stack: NULL argument or non-positive size");
+  for (int i = 0; i < n_layers; ++i) {
+    if (!blocks[i]) return fail(LLAMA_ERR_INVALID_ARG, "stack: block %d is NULL", i);
+    const llama_block_config &a = blocks[0]->cfg, &b = blocks[i]->cfg;
+    if (std::memcmp(&a, &b, sizeof a)) return fail(LLAMA_ERR_INVALID_ARG, "stack: block %d has another config", i);
+  }
+  const llama_block_config& c = blocks[0]->cfg;
+  if (c.act_dtype != LLAMA_BF16) return fail(LLAMA_ERR_UNSUPPORTED, "stack: bf16 activations only");
+  if (c.weight_format == LLAMA_W_Q4 && (!output->scales || !output->biases))
+    return fail(LLAMA_ERR_INVALID_ARG, "stack: 4-bit head needs scales and biases");
+  llama_stack* st = new llama_stack();
+  st->blocks.assign(blocks, blocks + n_layers);
+  st->emb = embedding;
+  st->vocab = vocab;
+  st->fnorm = final_norm;
+  st->head = *output;
+  *out = st;
+  return LLAMA_OK;
+}
+
+extern "C" void llama_stack_destroy(llama_stack* st) { delete st; }
+
+struct StLayout {
+  size_t x, blk, head, cur, cursor, total, blk_bytes, head_bytes;
+};
+static StLayout stack_layout(const llama_stack* st, int max_prompt, int max_seq) {
+  const llama_block_config& c = st->blocks[0]->cfg;
+  StLayout L{};
+  size_t off = 0;
+  L.x = off; off = align256(off + (size_t)max_prompt * c.dim * 2);
+  L.blk_bytes = llama_scratch_bytes(&c, max_prompt, 1, max_seq);
+  L.blk = off; off = align256(off + L.blk_bytes);
+  L.head_bytes = head_layout(1, c.dim, st->vocab).total;
+  L.head = off; off = align256(off + L.head_bytes);
+  L.cur = off; off = align256(off + 4);
+  L.cursor = off; off = align256(off + 4);
+  L.total = off;
+  return L;
+}
+
+extern "C" size_t llama_stack_scratch_bytes(const llama_stack* st, int32_t max_prompt, int32_t max_seq) {
+  if (!st || max_prompt <= 0 || max_seq <= 0) return 0;
+  return stack_layout(st, max_prompt, max_seq).total;
+}
+
+extern "C" llama_status llama_stack_generate(llama_stack* st, llama_kvcache* cache, const int32_t* prompt, int32_t P,
+                                             int32_t n_steps, int32_t* ids_out, float* logits_out, void* scratch,
+                                             size_t sbytes, int32_t use_graph, void* stream) {
+  if (!st || !cache || !prompt || !ids_out || !scratch)
+    return fail(LLAMA_ERR_INVALID_ARG, "stack, cache, prompt, ids_out and scratch must be non-NULL");
+  if (P <= 0 || n_steps < 0) return fail(LLAMA_ERR_INVALID_ARG, "prompt_len must be > 0 and n_steps >= 0");
+  hipStream_t s = (hipStream_t)stream;
+  if (use_graph && !s) return fail(LLAMA_ERR_INVALID_ARG, "graph capture needs a non-null stream");
+  const int NL = (int)st->blocks.size();
+  const llama_block_config& c = st->blocks[0]->cfg;
+  if (cache->cfg.n_layers < NL) return fail(LLAMA_ERR_INVALID_ARG, "cache has %d layers, stack %d", cache->cfg.n_layers, NL);
+  for (int l = 0; l < NL; ++l)
+    if (cache->lens_host[(size_t)l * cache->cfg.max_batch] != 0)
+      return fail(LLAMA_ERR_INVALID_ARG, "cache layer %d of sequence 0 is not empty", l);
+  const int cap = std::min(cache->cfg.max_seq, c.max_seq);
+  if ((long)P + n_steps > cap) return fail(LLAMA_ERR_CAPACITY, "prompt + steps (%d) exceed capacity %d", P + n_steps, cap);
+  StLayout L = stack_layout(st, P, cache->cfg.max_seq);
+  if (sbytes < L.total) return fail(LLAMA_ERR_CAPACITY, "stack scratch too small: %zu < %zu", sbytes, L.total);
+  char* sc = (char*)scratch;
+  bf16_t* x = (bf16_t*)(sc + L.x);
+  void* bs = sc + L.blk;
+  void* hs = sc + L.head;
+  int32_t* cur = (int32_t*)(sc + L.cur);
+  int32_t* cursor = (int32_t*)(sc + L.cursor);
+  float* hlog = (float*)((char*)hs + head_layout(1, c.dim, st->vocab).logits);
+  const int D = c.dim, V = st->vocab;
+  llama_status r;
+  auto head = [&](const bf16_t* row) {
+    return head_enqueue(&st->head, c.weight_format, c.group_size, LLAMA_BF16, st->fnorm, c.norm_eps, row, 1, D, V,
+                        hlog, cur, hs, L.head_bytes, s);
+  };
+
+  launch_fill_i32(cursor, 1, 0, s);
+  launch_embed<bf16_t>((const bf16_t*)st->emb, V, D, prompt, P, x, s);
+  for (int l = 0; l < NL; ++l)
+    if ((r = enqueue(st->blocks[l], cache, l, x, x, 1, P, bs, L.blk_bytes, false, 0, s)) != LLAMA_OK) return r;
+  if ((r = head(x + (size_t)(P - 1) * D)) != LLAMA_OK) return r;
+  launch_emit(cur, ids_out, cursor, hlog, logits_out, V, s);
+
+  const int n_splits = (P + n_steps + kSplitLen - 1) / kSplitLen;
+  auto step = [&]() -> llama_status {
+    launch_embed<bf16_t>((const bf16_t*)st->emb, V, D, cur, 1, x, s);
+    for (int l = 0; l < NL; ++l) {
+      llama_status q = enqueue(st->blocks[l], cache, l, x, x, 1, 1, bs, L.blk_bytes, true, n_splits, s);
+      if (q != LLAMA_OK) return q;
+    }
+    llama_status q = head(x);
+    if (q != LLAMA_OK) return q;
+    launch_emit(cur, ids_out, cursor, hlog, logits_out, V, s);
+    return hip_check("decode step");
+  };
+  if (n_steps > 0) {
+    if (use_graph) {
+      hipGraph_t graph = nullptr;
+      hipGraphExec_t exec = nullptr;
+      HIP_TRY(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "begin capture");
+      llama_status q = step();
+      hipError_t e = hipStreamEndCapture(s, &graph);
+      if (q != LLAMA_OK) return q;
+      if (e != hipSuccess) return fail(LLAMA_ERR_HIP, "end capture: %s", hipGetErrorString(e));
+      e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+      if (e == hipSuccess)
+        for (int i = 0; i < n_steps && e == hipSuccess; ++i) e = hipGraphLaunch(exec, s);
+      if (e == hipSuccess) e = hipStreamSynchronize(s);
+      if (exec) (void)hipGraphExecDestroy(exec);
+      (void)hipGraphDestroy(graph);
+      if (e != hipSuccess) return fail(LLAMA_ERR_HIP, "graph replay: %s", hipGetErrorString(e));
+    } else {
+      for (int i = 0; i < n_steps; ++i)
+        if ((r = step()) != LLAMA_OK) return r;
+    }
+  }
+  HIP_TRY(hipStreamSynchronize(s), "generate");
+  for (int l = 0; l < NL; ++l) cache->lens_host[(size_t)l * cache->cfg.max_batch] = P + n_steps;
+  return LLAMA_OK;
+}

@@ -1,0 +1,95 @@
+// Shared device/host definitions for the gfx950 decoder-block kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#ifndef __HIP_DEVICE_COMPILE__
+#include <cstdio>
+#endif
+
+namespace lb {
+
+typedef uint16_t bf16_t;  // raw bfloat16 storage
+
+// MFMA operand / accumulator vector types (gfx950 builtins take __bf16 / _Float16 vectors).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+__host__ __device__ inline float bf16_to_f32(bf16_t h) {
+  uint32_t u = ((uint32_t)h) << 16;
+  float f;
+  __builtin_memcpy(&f, &u, 4);
+  return f;
+}
+
+// Round-to-nearest-even float -> bf16 (NaN kept quiet).
+__host__ __device__ inline bf16_t f32_to_bf16(float f) {
+  uint32_t u;
+  __builtin_memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// Element type traits: the fp32 and bf16 paths share templates through these.
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+  static __device__ __host__ inline float load(const float* p, size_t i) { return p[i]; }
+  static __device__ __host__ inline void store(float* p, size_t i, float v) { p[i] = v; }
+  static __device__ __host__ inline float to_f(float v) { return v; }
+  static __device__ __host__ inline float from_f(float v) { return v; }
+  // round a float to what storage keeps
+  static __device__ __host__ inline float round(float v) { return v; }
+};
+template <> struct Elt<bf16_t> {
+  static __device__ __host__ inline float load(const bf16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+  static __device__ __host__ inline void store(bf16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+  static __device__ __host__ inline float to_f(bf16_t v) { return bf16_to_f32(v); }
+  static __device__ __host__ inline bf16_t from_f(float v) { return f32_to_bf16(v); }
+  static __device__ __host__ inline float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+};
+
+// Paged KV cache view of one layer, passed by value to kernels.
+//   K page: [G][ps][d]   (slot-major, head_dim contiguous)
+//   V page: [G][d][ps]   (transposed: slots contiguous per head_dim row)
+struct KVView {
+  void* k;              // this layer's K pool base
+  void* v;              // this layer's V pool base
+  const int32_t* table; // [max_batch][pps]
+  int32_t* lens;        // this layer's lens [max_batch]
+  int32_t G, d, ps, pps;
+  __device__ __host__ inline size_t page_base(int b, int pos) const {
+    int page = table[(size_t)b * pps + pos / ps];
+    return (size_t)page * G * ps * d;
+  }
+  // element offsets
+  __device__ inline size_t k_off(int b, int pos, int g, int e) const {
+    return page_base(b, pos) + ((size_t)g * ps + (pos % ps)) * d + e;
+  }
+  __device__ inline size_t v_off(int b, int pos, int g, int e) const {
+    return page_base(b, pos) + ((size_t)g * d + e) * ps + (pos % ps);
+  }
+};
+
+__device__ inline float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ inline float warp_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ inline float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+// 16-byte vector load/store helpers.
+__device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ inline void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+}  // namespace lb

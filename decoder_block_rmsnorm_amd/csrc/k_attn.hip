@@ -1,0 +1,443 @@
+// Causal grouped-query attention over the paged KV cache:
+//   o[h] = softmax_j( q[h] . k[g][j] / sqrt(d) ) v[g][j],  j <= position,
+//   g = h / (H / G)
+// (LLaMAAttention of page 二 with its expand-then-reshape kv sharing; the causal
+// rule of "5. 因果掩码" and the KV cache of "2. 注意力机制", MLX page).
+//
+//  * k_attn_simt         : one wavefront per (token, head), lanes over head_dim,
+//                          online softmax over keys (fp32 path).
+//  * k_attn_prefill_bf16 : flash-style prefill: 128 queries of one head per
+//                          block, 64-key K / V^T tiles staged in LDS, S^T = K Q^T
+//                          and O^T = V^T P^T on 32x32x16 bf16 MFMA, fp32 online
+//                          softmax (the tiling idea credited to FlashAttention in
+//                          "Transformer 块的内部结构" of the reading-notes page).
+//  * k_attn_decode_bf16  : split-K decode: each wavefront streams a 256-key
+//                          chunk of one (sequence, kv head) straight from the
+//                          pages with 128-bit loads, serving all n_rep query heads
+//                          of the group with 16x16x32 MFMA; k_attn_merge combines
+//                          the chunks with a log-sum-exp merge in a fixed order.
+#include "kernels.hpp"
+
+namespace lb {
+
+// ===========================================================================
+// generic (fp32 path)
+// ===========================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void k_attn_simt(const T* q, KVView kv, int B, int L, int H, int G, int d,
+                                                   T* out) {
+  int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  if (wid >= B * L * H) return;
+  int h = wid % H;
+  int m = wid / H;
+  int b = m / L, l = m % L;
+  int g = h / (H / G);
+  int pos = kv.lens[b] + l;
+  const T* qr = q + (size_t)m * H * d + (size_t)h * d;
+  const float scale = 1.0f / sqrtf((float)d);
+  float q0 = lane < d ? Elt<T>::load(qr, lane) * scale : 0.f;
+  float q1 = lane + 64 < d ? Elt<T>::load(qr, lane + 64) * scale : 0.f;
+  const T* K = (const T*)kv.k;
+  const T* V = (const T*)kv.v;
+  float mx = -INFINITY, den = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int j = 0; j <= pos; ++j) {
+    float part = 0.f;
+    if (lane < d) part += q0 * Elt<T>::load(K, kv.k_off(b, j, g, lane));
+    if (lane + 64 < d) part += q1 * Elt<T>::load(K, kv.k_off(b, j, g, lane + 64));
+    float sc = warp_sum(part);
+    float mn = fmaxf(mx, sc);
+    float alpha = __expf(mx - mn);
+    float p = __expf(sc - mn);
+    den = den * alpha + p;
+    float v0 = lane < d ? Elt<T>::load(V, kv.v_off(b, j, g, lane)) : 0.f;
+    float v1 = lane + 64 < d ? Elt<T>::load(V, kv.v_off(b, j, g, lane + 64)) : 0.f;
+    o0 = o0 * alpha + p * v0;
+    o1 = o1 * alpha + p * v1;
+    mx = mn;
+  }
+  T* orow = out + (size_t)m * H * d + (size_t)h * d;
+  if (lane < d) Elt<T>::store(orow, lane, o0 / den);
+  if (lane + 64 < d) Elt<T>::store(orow, lane + 64, o1 / den);
+}
+
+template <typename T>
+void launch_attn_simt(const T* q, KVView kv, int B, int L, int H, int G, int d, T* out, hipStream_t s) {
+  int waves = B * L * H;
+  if (waves <= 0) return;
+  hipLaunchKernelGGL(k_attn_simt<T>, dim3((waves + 3) / 4), dim3(256), 0, s, q, kv, B, L, H, G, d, out);
+}
+
+template void launch_attn_simt<float>(const float*, KVView, int, int, int, int, int, float*, hipStream_t);
+template void launch_attn_simt<bf16_t>(const bf16_t*, KVView, int, int, int, int, int, bf16_t*, hipStream_t);
+
+// ===========================================================================
+// bf16 flash prefill, head_dim 128
+// ===========================================================================
+namespace fa {
+constexpr int D = 128;
+constexpr int BQ = 128;        // queries per block (4 waves x 32)
+constexpr int BK = 64;         // keys per tile
+constexpr int KST = D + 8;     // LDS row stride (bf16) of the K tile  [key][d]
+constexpr int VST = BK + 8;    // LDS row stride (bf16) of the V^T tile [d][key]
+constexpr int K_ELEMS = BK * KST;
+constexpr int V_ELEMS = D * VST;
+}  // namespace fa
+
+__device__ inline bf16x8 as_bf16x8(uint4 v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+__global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __restrict__ q, KVView kv, int B,
+                                                             int L, int H, int G, bf16_t* __restrict__ out) {
+  using namespace fa;
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (K_ELEMS + V_ELEMS)];
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int n_qt = gridDim.z;
+  const int qt = n_qt - 1 - blockIdx.z;  // heavy (late) query tiles first
+  const int g = h / (H / G);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hg = lane >> 5;
+  const int S = kv.lens[b];               // tokens cached before this call
+  const int q_first = qt * BQ;            // first query index (within the new tokens)
+  const int wq0 = q_first + wave * 32;    // this wave's first query
+  const int nq_valid = L - q_first;       // queries of this block that exist
+  const int kmax_block = S + min(q_first + BQ, L);   // keys [0, kmax_block)
+  const int n_tiles = (kmax_block + BK - 1) / BK;
+  const int my_q = wq0 + l32;             // query handled by this lane (as an S^T column)
+  const int my_pos = S + my_q;
+  const int wave_kmax = S + min(wq0 + 32, L);        // keys this wave needs: [0, wave_kmax)
+
+  // Q^T fragments (B operand): lane holds Q[q = l32][d = 16*kc + 8*hg .. +7]
+  bf16x8 qf[8];
+  {
+    const bool ok = my_q < L;
+    const bf16_t* qrow = q + ((size_t)(b * L + (ok ? my_q : 0)) * H + h) * D;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      uint4 v = ok ? ld16(qrow + 16 * kc + 8 * hg) : make_uint4(0, 0, 0, 0);
+      qf[kc] = as_bf16x8(v);
+    }
+  }
+
+  const bf16_t* Kp = (const bf16_t*)kv.k;
+  const bf16_t* Vp = (const bf16_t*)kv.v;
+  // tile loader: K tile 64 keys x 128 d (16 chunks of 16 B per key row); V^T tile
+  // 128 d rows x 64 keys (8 chunks per row).  1024 chunks each, 4 per thread.
+  // Slots at or past kmax_block hold no key of this call (stale or never
+  // written); they are zeroed so that a 0 softmax weight never meets a NaN.
+  uint4 kreg[4], vreg[4];
+  auto load_tile = [&](int t) {
+    int key0 = t * BK;
+    size_t base = kv.page_base(b, key0);
+    int slot0 = key0 % kv.ps;
+    int nvalid = kmax_block - key0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = tid + 256 * i;
+      int kr = c >> 4, kc = c & 15;
+      kreg[i] = kr < nvalid ? ld16(Kp + base + ((size_t)g * kv.ps + slot0 + kr) * D + kc * 8) : make_uint4(0, 0, 0, 0);
+      int vr = c >> 3, vc = c & 7;
+      uint4 v = ld16(Vp + base + ((size_t)g * D + vr) * kv.ps + slot0 + vc * 8);
+      int nok = nvalid - vc * 8;
+      if (nok < 8) {
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e >= nok) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+        v = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      vreg[i] = v;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    bf16_t* ks = smem + buf * (K_ELEMS + V_ELEMS);
+    bf16_t* vs = ks + K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = tid + 256 * i;
+      int kr = c >> 4, kc = c & 15;
+      st16(ks + kr * KST + kc * 8, kreg[i]);
+      int vr = c >> 3, vc = c & 7;
+      st16(vs + vr * VST + vc * 8, vreg[i]);
+    }
+  };
+
+  f32x16 o_acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o_acc[i] = (f32x16){};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
+
+  if (n_tiles > 0) load_tile(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    store_tile(buf);
+    __syncthreads();
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    const int key0 = t * BK;
+    if (key0 < wave_kmax && nq_valid > wave * 32) {
+      const bf16_t* ks = smem + buf * (K_ELEMS + V_ELEMS);
+      const bf16_t* vs = ks + K_ELEMS;
+      // S^T = K Q^T : 2 key subtiles of 32
+      f32x16 s_acc[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        s_acc[st] = (f32x16){};
+#pragma unroll
+        for (int kc = 0; kc < 8; ++kc) {
+          bf16x8 a = as_bf16x8(ld16(ks + (st * 32 + l32) * KST + kc * 16 + hg * 8));
+          s_acc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s_acc[st], 0, 0, 0);
+        }
+      }
+      // scale, causal mask, online softmax (query = column l32; rows = keys)
+      const bool need_mask = key0 + BK - 1 > S + wq0;  // some key may exceed some query position
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float v = s_acc[st][i] * sl2;
+          if (need_mask) {
+            int key = key0 + st * 32 + 8 * (i >> 2) + 4 * hg + (i & 3);
+            if (key > my_pos) v = -INFINITY;
+          }
+          s_acc[st][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m_run, tmax);
+      // a fully masked row so far keeps m = -inf; use 0 as the exponent base then
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2f(m_run - m_use);
+      float psum = 0.f;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = exp2f(s_acc[st][i] - m_use);
+          s_acc[st][i] = p;
+          psum += p;
+        }
+      psum += __shfl_xor(psum, 32, 64);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) o_acc[ds] *= alpha;
+      // O^T += V^T P^T : 4 key chunks of 16 (B operand straight from S^T registers)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int st = c >> 1, r0 = 8 * (c & 1);
+        uint4 pw;
+        pw.x = pack_bf16x2(s_acc[st][r0 + 0], s_acc[st][r0 + 1]);
+        pw.y = pack_bf16x2(s_acc[st][r0 + 2], s_acc[st][r0 + 3]);
+        pw.z = pack_bf16x2(s_acc[st][r0 + 4], s_acc[st][r0 + 5]);
+        pw.w = pack_bf16x2(s_acc[st][r0 + 6], s_acc[st][r0 + 7]);
+        bf16x8 pb = as_bf16x8(pw);
+        const int kA = 16 * c + 4 * hg;  // keys kA..kA+3 and kA+8..kA+11
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds) {
+          const bf16_t* vr = vs + (ds * 32 + l32) * VST;
+          uint2 lo = *reinterpret_cast<const uint2*>(vr + kA);
+          uint2 hi = *reinterpret_cast<const uint2*>(vr + kA + 8);
+          bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+          o_acc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o_acc[ds], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // write O[q][d] = O^T / l : lane holds q = l32, d = 32*ds + 8*(i/4) + 4*hg + i%4
+  if (my_q < L) {
+    const float inv = 1.0f / l_run;
+    bf16_t* orow = out + ((size_t)(b * L + my_q) * H + h) * D;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        int dd = 32 * ds + 8 * r4 + 4 * hg;
+        uint2 w;
+        w.x = pack_bf16x2(o_acc[ds][4 * r4 + 0] * inv, o_acc[ds][4 * r4 + 1] * inv);
+        w.y = pack_bf16x2(o_acc[ds][4 * r4 + 2] * inv, o_acc[ds][4 * r4 + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + dd) = w;
+      }
+  }
+}
+
+void launch_attn_prefill_bf16(const bf16_t* q, KVView kv, int B, int L, int H, int G, bf16_t* out, hipStream_t s) {
+  if (B <= 0 || L <= 0) return;
+  dim3 grid(H, B, (L + fa::BQ - 1) / fa::BQ);
+  hipLaunchKernelGGL(k_attn_prefill_bf16, grid, dim3(256), 0, s, q, kv, B, L, H, G, out);
+}
+
+// ===========================================================================
+// bf16 split-K decode, head_dim 128
+// ===========================================================================
+// One wavefront = one (sequence b, kv head g, key chunk c of split_len keys).
+// Query columns: the n_rep (<= 16) query heads of group g, padded to 16.
+// S^T (16 keys x 16 q) = K (16 x 32 d) Q^T via 16x16x32 MFMA, 4 d-chunks;
+// O^T (16 d x 16 q) += V^T (16 d x 32 keys) P^T, 8 d-subtiles.
+// Partials: part_o [B][H][n_splits][128], part_ml [B][H][n_splits][2] (max, sum).
+__global__ __launch_bounds__(256) void k_attn_decode_bf16(const bf16_t* __restrict__ q, KVView kv, int B, int H,
+                                                         int G, int n_splits, int split_len,
+                                                         float* __restrict__ part_o, float* __restrict__ part_ml) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l16 = lane & 15, hg = lane >> 4;
+  const int wid = blockIdx.x * 4 + wave;
+  const int total = B * G * n_splits;
+  if (wid >= total) return;
+  const int c = wid % n_splits;
+  const int g = (wid / n_splits) % G;
+  const int b = wid / (n_splits * G);
+  const int n_rep = H / G;
+  const int pos = kv.lens[b];               // the new token's position; keys 0..pos
+  const int nkeys = pos + 1;
+  const int k_begin = c * split_len;
+  const int k_end = min(nkeys, k_begin + split_len);
+  const bool qvalid = l16 < n_rep;
+  const int hq = g * n_rep + (qvalid ? l16 : 0);
+
+  // Q^T fragments: lane holds Q[q = l16][d = 32*kc + 8*hg .. +7]
+  bf16x8 qf[4];
+  {
+    const bf16_t* qrow = q + ((size_t)b * H + hq) * 128;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) qf[kc] = as_bf16x8(qvalid ? ld16(qrow + 32 * kc + 8 * hg) : make_uint4(0, 0, 0, 0));
+  }
+  const bf16_t* Kp = (const bf16_t*)kv.k;
+  const bf16_t* Vp = (const bf16_t*)kv.v;
+  const float sl2 = 1.4426950408889634f / sqrtf(128.f);
+  f32x4 o_acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o_acc[i] = (f32x4){};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int k0 = k_begin; k0 < k_end; k0 += 32) {
+    // keys k0 .. k0+31 lie in one page (page size is a multiple of 64, k0 % 32 == 0)
+    const size_t base = kv.page_base(b, k0);
+    const int slot0 = k0 % kv.ps;
+    const bf16_t* kpage = Kp + base + (size_t)g * kv.ps * 128;
+    const bf16_t* vpage = Vp + base + (size_t)g * 128 * kv.ps;
+    f32x4 s_acc[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      s_acc[st] = (f32x4){};
+      const bf16_t* krow = kpage + (size_t)(slot0 + st * 16 + l16) * 128;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        bf16x8 a = as_bf16x8(ld16(krow + 32 * kc + 8 * hg));
+        s_acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kc], s_acc[st], 0, 0, 0);
+      }
+    }
+    // lane: query l16, keys st*16 + 4*hg + i
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int key = k0 + st * 16 + 4 * hg + i;
+        float v = key < k_end ? s_acc[st][i] * sl2 : -INFINITY;
+        s_acc[st][i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float p = exp2f(s_acc[st][i] - m_new);
+        s_acc[st][i] = p;
+        psum += p;
+      }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    // P^T as B operand: k index 8*hg + j <-> key (j<4: 4*hg + j; j>=4: 16 + 4*hg + j-4)
+    uint4 pw;
+    pw.x = pack_bf16x2(s_acc[0][0], s_acc[0][1]);
+    pw.y = pack_bf16x2(s_acc[0][2], s_acc[0][3]);
+    pw.z = pack_bf16x2(s_acc[1][0], s_acc[1][1]);
+    pw.w = pack_bf16x2(s_acc[1][2], s_acc[1][3]);
+    const bf16x8 pb = as_bf16x8(pw);
+    const bool tail = k0 + 32 > k_end;
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) {
+      o_acc[ds] *= alpha;
+      const bf16_t* vr = vpage + (size_t)(ds * 16 + l16) * kv.ps + slot0;
+      uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * hg);
+      uint2 hi = *reinterpret_cast<const uint2*>(vr + 16 + 4 * hg);
+      if (tail) {  // keys past k_end: zero (a stale NaN times weight 0 would poison the sum)
+        uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          int key = k0 + (e < 4 ? 4 * hg + e : 16 + 4 * hg + e - 4);
+          if (key >= k_end) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+        }
+        lo = make_uint2(w[0], w[1]);
+        hi = make_uint2(w[2], w[3]);
+      }
+      bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      o_acc[ds] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o_acc[ds], 0, 0, 0);
+    }
+  }
+  // lane: O^T[d = 16*ds + 4*hg + i][q = l16]
+  if (qvalid) {
+    const size_t pi = (((size_t)b * H + hq) * n_splits + c);
+    float* po = part_o + pi * 128;
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds)
+      *reinterpret_cast<float4*>(po + 16 * ds + 4 * hg) =
+          make_float4(o_acc[ds][0], o_acc[ds][1], o_acc[ds][2], o_acc[ds][3]);
+    if (hg == 0) {
+      part_ml[pi * 2 + 0] = m_run;
+      part_ml[pi * 2 + 1] = l_run;
+    }
+  }
+}
+
+// One wavefront per (b, h): o = sum_c e^(m_c - M) O_c / sum_c e^(m_c - M) l_c
+__global__ __launch_bounds__(256) void k_attn_merge(const float* part_o, const float* part_ml, int BH,
+                                                    int n_splits, bf16_t* out) {
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (wid >= BH) return;
+  const float* ml = part_ml + (size_t)wid * n_splits * 2;
+  float M = -INFINITY;
+  for (int c = 0; c < n_splits; ++c) M = fmaxf(M, ml[2 * c]);
+  float den = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int c = 0; c < n_splits; ++c) {
+    float mc = ml[2 * c];
+    if (mc == -INFINITY) continue;
+    float w = exp2f(mc - M);
+    den += w * ml[2 * c + 1];
+    const float* po = part_o + ((size_t)wid * n_splits + c) * 128;
+    o0 += w * po[lane];
+    o1 += w * po[lane + 64];
+  }
+  bf16_t* orow = out + (size_t)wid * 128;
+  orow[lane] = f32_to_bf16(o0 / den);
+  orow[lane + 64] = f32_to_bf16(o1 / den);
+}
+
+void launch_attn_decode_bf16(const bf16_t* q, KVView kv, int B, int H, int G, int n_splits, int split_len,
+                             float* part_o, float* part_ml, bf16_t* out, hipStream_t s) {
+  if (B <= 0) return;
+  int waves = B * G * n_splits;
+  hipLaunchKernelGGL(k_attn_decode_bf16, dim3((waves + 3) / 4), dim3(256), 0, s, q, kv, B, H, G, n_splits,
+                     split_len, part_o, part_ml);
+  int bh = B * H;
+  hipLaunchKernelGGL(k_attn_merge, dim3((bh + 3) / 4), dim3(256), 0, s, part_o, part_ml, bh, n_splits, out);
+}
+
+}  // namespace lb

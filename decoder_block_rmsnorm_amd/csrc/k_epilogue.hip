@@ -1,0 +1,164 @@
+// Reduce-and-finish kernels behind the split-K decode GEMMs and the fp32 GEMM.
+// Each sums the fp32 partials [ks][M][N] in a fixed order (deterministic, no
+// atomics) and applies what follows the projection in the block:
+//   qkv   : RMSNorm row scale, RoPE on q and k, cache append of k and v;
+//   resid : residual add (+ the next RMSNorm's statistics, + cache-length bump);
+//   swiglu: RMSNorm row scale, silu(gate) * up.
+#include "kernels.hpp"
+
+namespace lb {
+
+__device__ inline float sum_parts(const float* part, int ks, size_t stride, size_t idx) {
+  float v = 0.f;
+  for (int s = 0; s < ks; ++s) v += part[(size_t)s * stride + idx];
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// q/k/v finish.  Columns come in the repacked order: per head, pair i is
+// (i, i + d/2).  For the interleaved ("traditional") layout the wq/wk rows were
+// permuted at creation so that adjacent pairs (2i, 2i+1) land at (i, i + d/2);
+// the write below puts them back.  RoPE as in LLaMARoPE (page 二) with the
+// angle table built in float64 on the host; the cache offset is the number of
+// tokens already cached ("2. 注意力机制" KV-cache fragment, MLX page).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(64) void k_epi_qkv(const float* part, int ks, int M, int Nq, int Nkv,
+                                                const float* inv_rms, int L, const float2* rope,
+                                                int traditional, T* q_out, KVView kv) {
+  int m = blockIdx.x;
+  int head = blockIdx.y;          // 0..H-1 q, H..H+G-1 k, then v
+  int d = kv.d, half = d >> 1;
+  int i = threadIdx.x;
+  if (i >= half) return;
+  int N = Nq + 2 * Nkv;
+  size_t stride = (size_t)M * N;
+  int c0 = head * d;
+  float r = inv_rms ? inv_rms[m] : 1.0f;
+  float a = sum_parts(part, ks, stride, (size_t)m * N + c0 + i) * r;
+  float b = sum_parts(part, ks, stride, (size_t)m * N + c0 + i + half) * r;
+  int bseq = m / L, l = m % L;
+  int pos = kv.lens[bseq] + l;
+  int H = Nq / d;
+  if (c0 < Nq + Nkv) {
+    float2 cs = rope[(size_t)pos * half + i];
+    float a2 = a * cs.x - b * cs.y;
+    float b2 = b * cs.x + a * cs.y;
+    a = a2;
+    b = b2;
+  }
+  int ca = traditional ? 2 * i : i;
+  int cb = traditional ? 2 * i + 1 : i + half;
+  if (c0 < Nq) {
+    Elt<T>::store(q_out, (size_t)m * Nq + c0 + ca, a);
+    Elt<T>::store(q_out, (size_t)m * Nq + c0 + cb, b);
+  } else if (c0 < Nq + Nkv) {
+    int g = head - H;
+    T* K = (T*)kv.k;
+    Elt<T>::store(K, kv.k_off(bseq, pos, g, ca), a);
+    Elt<T>::store(K, kv.k_off(bseq, pos, g, cb), b);
+  } else {
+    int g = head - H - Nkv / d;
+    T* V = (T*)kv.v;
+    Elt<T>::store(V, kv.v_off(bseq, pos, g, i), a);
+    Elt<T>::store(V, kv.v_off(bseq, pos, g, i + half), b);
+  }
+}
+
+template <typename T>
+void launch_epi_qkv(const float* part, int ks, int M, int Nq, int Nkv, const float* inv_rms, int L,
+                    const float2* rope, int traditional, T* q_out, KVView kv, hipStream_t s) {
+  if (M <= 0) return;
+  dim3 grid(M, (Nq + 2 * Nkv) / kv.d);
+  hipLaunchKernelGGL(k_epi_qkv<T>, grid, dim3(64), 0, s, part, ks, M, Nq, Nkv, inv_rms, L, rope, traditional,
+                     q_out, kv);
+}
+
+// ---------------------------------------------------------------------------
+// Residual add: out = resid + sum(partials) (LLaMABlock, page 二; "数据流动"),
+// rounded to the storage type; optionally the RMSNorm statistics of the stored
+// row for the next projection, and the cache-length bump after the block.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_epi_resid(const float* part, int ks, int M, int N, const T* resid,
+                                                   T* out, float eps, float* inv_rms_out, int32_t* lens_add,
+                                                   int lens_inc, int n_seq) {
+  int m = blockIdx.x;
+  size_t stride = (size_t)M * N;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < N; c += 256) {
+    size_t idx = (size_t)m * N + c;
+    float v = Elt<T>::round(Elt<T>::load(resid, idx) + sum_parts(part, ks, stride, idx));
+    Elt<T>::store(out, idx, v);
+    ss += v * v;
+  }
+  if (inv_rms_out) {
+    __shared__ float red[4];
+    ss = warp_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) inv_rms_out[m] = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)N + eps);
+  }
+  if (lens_add && m == 0 && threadIdx.x < n_seq) lens_add[threadIdx.x] += lens_inc;
+}
+
+template <typename T>
+void launch_epi_resid(const float* part, int ks, int M, int N, const T* resid, T* out, float eps,
+                      float* inv_rms_out, int32_t* lens_add, int lens_inc, int n_seq, hipStream_t s) {
+  if (M <= 0) return;
+  hipLaunchKernelGGL(k_epi_resid<T>, dim3(M), dim3(256), 0, s, part, ks, M, N, resid, out, eps, inv_rms_out,
+                     lens_add, lens_inc, n_seq);
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU: g = silu(w1 n) * (w3 n) ("3. 前馈网络", MLX page; LLaMAMLP, page 二).
+// w1/w3 rows are interleaved in blocks of ib: block 2j holds w1 rows
+// j*ib .. j*ib+ib-1, block 2j+1 the same w3 rows.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_epi_swiglu(const float* part, int ks, int M, int F2, int ib,
+                                                    const float* inv_rms, T* g_out) {
+  int m = blockIdx.y;
+  int F = F2 >> 1;
+  int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= F) return;
+  size_t stride = (size_t)M * F2;
+  int jb = j / ib, w = j % ib;
+  int cg = jb * 2 * ib + w;
+  float r = inv_rms ? inv_rms[m] : 1.0f;
+  float a = sum_parts(part, ks, stride, (size_t)m * F2 + cg) * r;
+  float b = sum_parts(part, ks, stride, (size_t)m * F2 + cg + ib) * r;
+  Elt<T>::store(g_out, (size_t)m * F + j, silu_f(a) * b);
+}
+
+template <typename T>
+void launch_epi_swiglu(const float* part, int ks, int M, int F2, int ib, const float* inv_rms, T* g_out,
+                       hipStream_t s) {
+  if (M <= 0) return;
+  dim3 grid((F2 / 2 + 255) / 256, M);
+  hipLaunchKernelGGL(k_epi_swiglu<T>, grid, dim3(256), 0, s, part, ks, M, F2, ib, inv_rms, g_out);
+}
+
+__global__ __launch_bounds__(256) void k_reduce_f32(const float* part, int ks, int M, int N, float* out) {
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  size_t total = (size_t)M * N;
+  if (i < total) out[i] = sum_parts(part, ks, total, i);
+}
+
+void launch_reduce_f32(const float* part, int ks, int M, int N, float* out, hipStream_t s) {
+  size_t total = (size_t)M * N;
+  if (!total) return;
+  hipLaunchKernelGGL(k_reduce_f32, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, ks, M, N, out);
+}
+
+#define INST(T)                                                                                           \
+  template void launch_epi_qkv<T>(const float*, int, int, int, int, const float*, int, const float2*, int, T*, \
+                                  KVView, hipStream_t);                                                   \
+  template void launch_epi_resid<T>(const float*, int, int, int, const T*, T*, float, float*, int32_t*, int, \
+                                    int, hipStream_t);                                                    \
+  template void launch_epi_swiglu<T>(const float*, int, int, int, int, const float*, T*, hipStream_t);
+INST(float)
+INST(bf16_t)
+#undef INST
+
+}  // namespace lb

@@ -1,0 +1,248 @@
+// Decode-time projections (one token per sequence, M = batch <= 64): every
+// weight byte is read exactly once per step, so these kernels are HBM-bound.
+//
+// k_gemv_bf16: split-K skinny GEMM on v_mfma_f32_16x16x32_bf16.  A block owns
+//   NW*64 output columns and one K slice; each wavefront streams its 16*NW
+//   weight rows straight from HBM into MFMA B-operand registers with 128-bit
+//   loads (8 per lane in flight per 256-wide K chunk, prefetched one chunk
+//   ahead), while the activations of the chunk sit in LDS for all four
+//   wavefronts.  fp32 partials [ks][M][N] go to a reduce-and-finish kernel.
+//
+// k_gemv_q4: 4-bit group-affine weights (group 64 along the input dim, the MLX
+//   quantization config of "模型配置"): W = s * code + b.  Per 8-code word,
+//   one shift and four v_and_or_b32 turn nibble pairs into fp16 pairs
+//   (1024 + code or 1024 + 16 code, exact), v_dot2_f32_f16 multiplies them with
+//   pre-scaled fp16 activations; the 1024 offset and the bias are removed per
+//   32-code chunk with precomputed activation sums:
+//       sum_k W x = sum_chunks  s * (A - 1024 * Xh) + b * X.
+#include "kernels.hpp"
+
+namespace lb {
+
+__device__ inline bf16x8 v_as_bf16x8(uint4 v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+namespace gv {
+constexpr int KC = 256;         // K chunk staged per step
+constexpr int XST = KC + 8;     // LDS row stride (bf16)
+}  // namespace gv
+
+template <int NW>
+__global__ __launch_bounds__(256) void k_gemv_bf16(const bf16_t* __restrict__ X, const bf16_t* __restrict__ W,
+                                                  float* __restrict__ part, int M, int N, int K, int ksl) {
+  using namespace gv;
+  __shared__ __attribute__((aligned(16))) bf16_t xs[64 * XST];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, hg = lane >> 4;
+  const int n_blk = blockIdx.x;
+  const int ksi = blockIdx.y;
+  const int kb = ksi * ksl, ke = min(K, kb + ksl);
+  const int MT = (M + 15) >> 4;
+  const int nrow0 = n_blk * (64 * NW) + wave * (16 * NW);
+
+  f32x4 acc[4][NW];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NW; ++j) acc[i][j] = (f32x4){};
+
+  uint4 wr[NW][8];
+  auto wload = [&](int k0) {
+    const int nkc = min(8, (ke - k0) >> 5);
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const bf16_t* wrow = W + (size_t)(nrow0 + j * 16 + l16) * K + k0 + 8 * hg;
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc)
+        if (kc < nkc) wr[j][kc] = ld16(wrow + 32 * kc);
+    }
+  };
+
+  if (kb < ke) wload(kb);
+  for (int k0 = kb; k0 < ke; k0 += KC) {
+    const int nk = min(KC, ke - k0);
+    // stage X[0:M, k0:k0+nk] (rows >= M read as zero)
+    const int chunks = MT * 16 * (nk >> 3);
+    __syncthreads();
+    for (int c = tid; c < chunks; c += 256) {
+      int r = c / (nk >> 3), kc = c % (nk >> 3);
+      uint4 v = r < M ? ld16(X + (size_t)r * K + k0 + kc * 8) : make_uint4(0, 0, 0, 0);
+      st16(xs + r * XST + kc * 8, v);
+    }
+    __syncthreads();
+    uint4 cur[NW][8];
+#pragma unroll
+    for (int j = 0; j < NW; ++j)
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) cur[j][kc] = wr[j][kc];
+    if (k0 + KC < ke) wload(k0 + KC);
+    const int nkc = nk >> 5;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      if (kc < nkc) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          if (mt < MT) {
+            bf16x8 xa = v_as_bf16x8(ld16(xs + (mt * 16 + l16) * XST + 32 * kc + 8 * hg));
+#pragma unroll
+            for (int j = 0; j < NW; ++j)
+              acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, v_as_bf16x8(cur[j][kc]), acc[mt][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+  // lane: C[m = 16*mt + 4*hg + i][n = nrow0 + 16*j + l16]
+  float* pp = part + (size_t)ksi * M * N;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    if (mt >= MT) break;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = mt * 16 + 4 * hg + i;
+      if (m < M) {
+#pragma unroll
+        for (int j = 0; j < NW; ++j) pp[(size_t)m * N + nrow0 + 16 * j + l16] = acc[mt][j][i];
+      }
+    }
+  }
+}
+
+void launch_gemv_bf16(const bf16_t* X, const bf16_t* W, float* partial, int M, int N, int K, int ks, hipStream_t s) {
+  if (M <= 0 || N <= 0) return;
+  const int ksl = K / ks;
+  if (M > 16 && (N % 128) == 0) {
+    dim3 grid(N / 128, ks);
+    hipLaunchKernelGGL(k_gemv_bf16<2>, grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl);
+  } else {
+    dim3 grid(N / 64, ks);
+    hipLaunchKernelGGL(k_gemv_bf16<1>, grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl);
+  }
+}
+
+// ===========================================================================
+// 4-bit GEMV
+// ===========================================================================
+// Activation preparation, once per call: per row m,
+//   xh  [M][K] fp16 in word-pair order: for the 8 codes k0..k0+7 of one word,
+//        (x0, x4), (x1/16, x5/16), (x2, x6), (x3/16, x7/16);
+//   xsum[M][K/32][2] = (sum of the xh values of the chunk, sum of x of the chunk).
+// x = x_in * inv_rms * gamma when those are given (RMSNorm feeding the GEMV).
+__global__ __launch_bounds__(256) void k_q4_prep(const bf16_t* X, const float* inv_rms, const float* gamma, int M,
+                                                 int K, _Float16* xh, float* xsum) {
+  const int m = blockIdx.y;
+  const int chunk = blockIdx.x * 4 + (threadIdx.x >> 6);  // 32 codes per chunk
+  const int lane = threadIdx.x & 63;
+  if (chunk >= K / 32 || m >= M) return;
+  // lane < 32 handles one code of the chunk
+  float x = 0.f;
+  float h = 0.f;
+  const int k = chunk * 32 + (lane & 31);
+  if (lane < 32) {
+    x = bf16_to_f32(X[(size_t)m * K + k]);
+    if (inv_rms) x *= inv_rms[m];
+    if (gamma) x *= gamma[k];
+    const int j = k & 7;                 // code position inside its word
+    const float sc = (j & 1) ? (1.0f / 16.0f) : 1.0f;
+    _Float16 hv = (_Float16)(x * sc);
+    h = (float)hv;
+    // slot inside the word's 8 fp16: pair p = j % 4, half = j / 4
+    const int p = j & 3, half = j >> 2;
+    xh[(size_t)m * K + (k & ~7) + 2 * p + half] = hv;
+  }
+  float hs = warp_sum(lane < 32 ? h : 0.f);
+  float xsv = warp_sum(lane < 32 ? x : 0.f);
+  if (lane == 0) {
+    xsum[((size_t)m * (K / 32) + chunk) * 2 + 0] = hs;
+    xsum[((size_t)m * (K / 32) + chunk) * 2 + 1] = xsv;
+  }
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ inline half2_t u32_as_h2(uint32_t u) {
+  half2_t r;
+  __builtin_memcpy(&r, &u, 4);
+  return r;
+}
+
+template <int MR>
+__global__ __launch_bounds__(256) void k_gemv_q4(const _Float16* __restrict__ xh, const float* __restrict__ xsum,
+                                                const uint32_t* __restrict__ words, const bf16_t* __restrict__ scales,
+                                                const bf16_t* __restrict__ biases, float* __restrict__ y, int M, int N,
+                                                int K, int gs, int rows_per_wave) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nchunk = K / 32;
+  const int ngrp = K / gs;
+  const int cpg = gs / 32;  // chunks per group
+  const int row0 = (blockIdx.x * 4 + wave) * rows_per_wave;
+  for (int rr = 0; rr < rows_per_wave; ++rr) {
+    const int n = row0 + rr;
+    if (n >= N) return;
+    const uint32_t* wrow = words + (size_t)n * (K / 8);
+    float acc[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+    for (int c = lane; c < nchunk; c += 64) {
+      const uint4 w = ld16(wrow + c * 4);
+      const int g = c / cpg;
+      const float s = bf16_to_f32(scales[(size_t)n * ngrp + g]);
+      const float b = bf16_to_f32(biases[(size_t)n * ngrp + g]);
+      const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+      uint32_t qp[16];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t u = wv[t], u8 = wv[t] >> 8;
+        qp[4 * t + 0] = (u & 0x000F000Fu) | 0x64006400u;
+        qp[4 * t + 1] = (u & 0x00F000F0u) | 0x64006400u;
+        qp[4 * t + 2] = (u8 & 0x000F000Fu) | 0x64006400u;
+        qp[4 * t + 3] = (u8 & 0x00F000F0u) | 0x64006400u;
+      }
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        if (m < M) {
+          const uint4* xp = reinterpret_cast<const uint4*>(xh + (size_t)m * K + c * 32);
+          float a = 0.f;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint4 xv = xp[t];
+            a = __builtin_amdgcn_fdot2(u32_as_h2(qp[4 * t + 0]), u32_as_h2(xv.x), a, false);
+            a = __builtin_amdgcn_fdot2(u32_as_h2(qp[4 * t + 1]), u32_as_h2(xv.y), a, false);
+            a = __builtin_amdgcn_fdot2(u32_as_h2(qp[4 * t + 2]), u32_as_h2(xv.z), a, false);
+            a = __builtin_amdgcn_fdot2(u32_as_h2(qp[4 * t + 3]), u32_as_h2(xv.w), a, false);
+          }
+          const float* xsm = xsum + ((size_t)m * nchunk + c) * 2;
+          acc[m] += s * (a - 1024.0f * xsm[0]) + b * xsm[1];
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      if (m < M) {
+        float v = warp_sum(acc[m]);
+        if (lane == 0) y[(size_t)m * N + n] = v;
+      }
+    }
+  }
+}
+
+void launch_gemv_q4(const bf16_t* X, const float* inv_rms, const float* gamma, const uint32_t* words,
+                    const bf16_t* scales, const bf16_t* biases, float* y, int M, int N, int K, int gs,
+                    _Float16* xh_buf, float* xsum_buf, hipStream_t s) {
+  if (M <= 0 || N <= 0) return;
+  dim3 pg((K / 32 + 3) / 4, M);
+  hipLaunchKernelGGL(k_q4_prep, pg, dim3(256), 0, s, X, inv_rms, gamma, M, K, xh_buf, xsum_buf);
+  const int rpw = 2;
+  const int blocks = (N + 4 * rpw - 1) / (4 * rpw);
+  if (M == 1)
+    hipLaunchKernelGGL(k_gemv_q4<1>, dim3(blocks), dim3(256), 0, s, xh_buf, xsum_buf, words, scales, biases, y, M,
+                       N, K, gs, rpw);
+  else
+    hipLaunchKernelGGL(k_gemv_q4<4>, dim3(blocks), dim3(256), 0, s, xh_buf, xsum_buf, words, scales, biases, y, M,
+                       N, K, gs, rpw);
+}
+
+}  // namespace lb

@@ -1,0 +1,312 @@
+// Small kernels: RMSNorm statistics, embedding gather, argmax, cache copies,
+// weight repacking and 4-bit dequantisation.
+#include "kernels.hpp"
+
+namespace lb {
+
+// ---------------------------------------------------------------------------
+// RMSNorm statistics -- "4. RMSNorm" of the MLX page / LLaMARMSNorm of page 二:
+// inv = 1 / sqrt(mean(x^2) + eps).  One wavefront per row, fp32 sum of squares
+// reduced across the 64 lanes.  The gamma multiply is folded elsewhere (into the
+// next GEMM's weights, or applied by rmsnorm_apply).
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ inline float row_sumsq(const T* row, int D, int lane) {
+  float ss = 0.f;
+  for (int i = lane; i < D; i += 64) {
+    float v = Elt<T>::load(row, i);
+    ss += v * v;
+  }
+  return warp_sum(ss);
+}
+
+template <>
+__device__ inline float row_sumsq<bf16_t>(const bf16_t* row, int D, int lane) {
+  float ss = 0.f;
+  if ((D & 7) == 0) {
+    for (int i = lane * 8; i < D; i += 512) {
+      uint4 w = ld16(row + i);
+      uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float a = bf16_to_f32((bf16_t)(u[j] & 0xffff));
+        float b = bf16_to_f32((bf16_t)(u[j] >> 16));
+        ss += a * a + b * b;
+      }
+    }
+  } else {
+    for (int i = lane; i < D; i += 64) {
+      float v = bf16_to_f32(row[i]);
+      ss += v * v;
+    }
+  }
+  return warp_sum(ss);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_rms_inv(const T* x, int rows, int D, float eps, float* inv) {
+  int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float ss = row_sumsq<T>(x + (size_t)row * D, D, lane);
+  if (lane == 0) inv[row] = 1.0f / sqrtf(ss / (float)D + eps);
+}
+
+template <typename T>
+void launch_rms_inv(const T* x, int rows, int D, float eps, float* inv, hipStream_t s) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(k_rms_inv<T>, dim3((rows + 3) / 4), dim3(256), 0, s, x, rows, D, eps, inv);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_rmsnorm_apply(const T* x, const T* gamma, int rows, int D,
+                                                       float eps, T* out) {
+  int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const T* xr = x + (size_t)row * D;
+  float ss = row_sumsq<T>(xr, D, lane);
+  float r = 1.0f / sqrtf(ss / (float)D + eps);
+  for (int i = lane; i < D; i += 64)
+    Elt<T>::store(out, (size_t)row * D + i, Elt<T>::load(xr, i) * r * Elt<T>::load(gamma, i));
+}
+
+template <typename T>
+void launch_rmsnorm_apply(const T* x, const T* gamma, int rows, int D, float eps, T* out, hipStream_t s) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(k_rmsnorm_apply<T>, dim3((rows + 3) / 4), dim3(256), 0, s, x, gamma, rows, D, eps, out);
+}
+
+// ---------------------------------------------------------------------------
+// Embedding lookup -- "1. 嵌入层" of the MLX page: out[i] = table[ids[i]].
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_embed(const T* table, int vocab, int D, const int32_t* ids, T* out) {
+  int i = blockIdx.x;
+  int id = ids[i];
+  bool ok = id >= 0 && id < vocab;
+  for (int c = threadIdx.x; c < D; c += 256)
+    out[(size_t)i * D + c] = ok ? table[(size_t)id * D + c] : T(0);
+}
+
+template <typename T>
+void launch_embed(const T* table, int vocab, int D, const int32_t* ids, int n, T* out, hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_embed<T>, dim3(n), dim3(256), 0, s, table, vocab, D, ids, out);
+}
+
+// ---------------------------------------------------------------------------
+// Greedy choice -- argmax at temperature 0 ("生成过程", MLX page): the first
+// index holding the largest logit.  Block reduction keeps (value, index) with
+// the lower index on equal values, so the result is deterministic.
+// ---------------------------------------------------------------------------
+__device__ inline void better(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+}
+
+__global__ __launch_bounds__(1024) void k_argmax(const float* logits, int vocab, int32_t* ids) {
+  const float* row = logits + (size_t)blockIdx.x * vocab;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < vocab; i += 1024) better(bv, bi, row[i], i);
+  for (int o = 32; o > 0; o >>= 1) {
+    float ov = __shfl_xor(bv, o, 64);
+    int oi = __shfl_xor(bi, o, 64);
+    better(bv, bi, ov, oi);
+  }
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { sv[w] = bv; si[w] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float v = sv[0];
+    int id = si[0];
+    for (int k = 1; k < 16; ++k) better(v, id, sv[k], si[k]);
+    ids[blockIdx.x] = (id == 0x7fffffff) ? 0 : id;
+  }
+}
+
+void launch_argmax(const float* logits, int rows, int vocab, int32_t* ids, hipStream_t s) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(k_argmax, dim3(rows), dim3(1024), 0, s, logits, vocab, ids);
+}
+
+// ---------------------------------------------------------------------------
+// Paged cache <-> canonical [n, G, d] copies (cache pre-fill and read-back).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_kv_copy(KVView kv, int seq, int pos0, int n, const T* kin,
+                                                 const T* vin, T* kout, T* vout) {
+  size_t total = (size_t)n * kv.G * kv.d;
+  T* K = (T*)kv.k;
+  T* V = (T*)kv.v;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
+    int e = (int)(i % kv.d);
+    int g = (int)((i / kv.d) % kv.G);
+    int t = (int)(i / ((size_t)kv.d * kv.G));
+    int pos = pos0 + t;
+    size_t ko = kv.k_off(seq, pos, g, e), vo = kv.v_off(seq, pos, g, e);
+    if (kin) {
+      K[ko] = kin[i];
+      V[vo] = vin[i];
+    } else {
+      kout[i] = K[ko];
+      vout[i] = V[vo];
+    }
+  }
+}
+
+template <typename T>
+void launch_kv_write(KVView kv, int seq, int pos0, int n, const T* k, const T* v, hipStream_t s) {
+  size_t total = (size_t)n * kv.G * kv.d;
+  if (!total) return;
+  int blocks = (int)((total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192);
+  hipLaunchKernelGGL(k_kv_copy<T>, dim3(blocks), dim3(256), 0, s, kv, seq, pos0, n, k, v, (T*)nullptr,
+                     (T*)nullptr);
+}
+
+template <typename T>
+void launch_kv_read(KVView kv, int seq, int pos0, int n, T* k, T* v, hipStream_t s) {
+  size_t total = (size_t)n * kv.G * kv.d;
+  if (!total) return;
+  int blocks = (int)((total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192);
+  hipLaunchKernelGGL(k_kv_copy<T>, dim3(blocks), dim3(256), 0, s, kv, seq, pos0, n, (const T*)nullptr,
+                     (const T*)nullptr, k, v);
+}
+
+__global__ void k_fill_i32(int32_t* p, int n, int32_t v) {
+  int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+void launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
+}
+
+// ---------------------------------------------------------------------------
+// Weight repacking (runs once at block creation).
+// ---------------------------------------------------------------------------
+__device__ inline int repack_dst_row(int r, int row0, int ib, int ib_stride, int perm_d) {
+  if (perm_d > 0) {
+    int local = r % perm_d;
+    int dl = (local & 1) ? (perm_d / 2 + local / 2) : (local / 2);
+    r = (r / perm_d) * perm_d + dl;
+  }
+  return row0 + (r / ib) * ib_stride + (r % ib);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_repack_rows(T* dst, const T* src, int rows, int K, const T* gamma,
+                                                     int row0, int ib, int ib_stride, int perm_d) {
+  int r = blockIdx.x;
+  int dr = repack_dst_row(r, row0, ib, ib_stride, perm_d);
+  for (int c = threadIdx.x; c < K; c += 256) {
+    float v = Elt<T>::load(src, (size_t)r * K + c);
+    if (gamma) v *= Elt<T>::load(gamma, c);
+    Elt<T>::store(dst, (size_t)dr * K + c, v);
+  }
+}
+
+template <typename T>
+void launch_repack_rows(T* dst, const T* src, int rows, int K, const T* gamma, int row0, int ib, int ib_stride,
+                        int perm_d, hipStream_t s) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(k_repack_rows<T>, dim3(rows), dim3(256), 0, s, dst, src, rows, K, gamma, row0, ib,
+                     ib_stride, perm_d);
+}
+
+__global__ __launch_bounds__(256) void k_repack_bytes(uint8_t* dst, const uint8_t* src, int rows, int rb,
+                                                      int row0, int ib, int ib_stride, int perm_d) {
+  int r = blockIdx.x;
+  int dr = repack_dst_row(r, row0, ib, ib_stride, perm_d);
+  for (int c = threadIdx.x; c < rb; c += 256) dst[(size_t)dr * rb + c] = src[(size_t)r * rb + c];
+}
+
+void launch_repack_bytes(uint8_t* dst, const uint8_t* src, int rows, int row_bytes, int row0, int ib,
+                         int ib_stride, int perm_d, hipStream_t s) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(k_repack_bytes, dim3(rows), dim3(256), 0, s, dst, src, rows, row_bytes, row0, ib,
+                     ib_stride, perm_d);
+}
+
+// ---------------------------------------------------------------------------
+// 4-bit group-affine dequantisation to bf16 (prompt pass of the quantized
+// stack): W[o, k] = scale[o, k/gs] * code[o, k] + bias[o, k/gs], the 4-bit /
+// group-64 format of the MLX quantization config ("模型配置").  The norm weight
+// of the following RMSNorm-fed GEMM is folded in (gamma_k) before rounding.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_q4_dequant(const uint32_t* words, const bf16_t* scales,
+                                                    const bf16_t* biases, int N, int K, int gs,
+                                                    const float* gamma, bf16_t* out) {
+  int row = blockIdx.x;
+  int nw = K / 8;
+  const uint32_t* wr = words + (size_t)row * nw;
+  for (int w = threadIdx.x; w < nw; w += 256) {
+    uint32_t u = wr[w];
+    int k0 = w * 8;
+    int g = k0 / gs;
+    float sc = bf16_to_f32(scales[(size_t)row * (K / gs) + g]);
+    float bi = bf16_to_f32(biases[(size_t)row * (K / gs) + g]);
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float a = sc * (float)((u >> (8 * j)) & 15u) + bi;
+      float b = sc * (float)((u >> (8 * j + 4)) & 15u) + bi;
+      if (gamma) { a *= gamma[k0 + 2 * j]; b *= gamma[k0 + 2 * j + 1]; }
+      o[j] = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    }
+    st16(out + (size_t)row * K + k0, make_uint4(o[0], o[1], o[2], o[3]));
+  }
+}
+
+void launch_q4_dequant(const uint32_t* words, const bf16_t* scales, const bf16_t* biases, int N, int K, int gs,
+                       const float* gamma, bf16_t* out, hipStream_t s) {
+  if (N <= 0) return;
+  hipLaunchKernelGGL(k_q4_dequant, dim3(N), dim3(256), 0, s, words, scales, biases, N, K, gs, gamma, out);
+}
+
+template <typename T>
+__global__ void k_to_f32(const T* src, float* dst, int n) {
+  int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = Elt<T>::load(src, i);
+}
+template <typename T>
+void launch_to_f32(const T* src, float* dst, int n, hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_to_f32<T>, dim3((n + 255) / 256), dim3(256), 0, s, src, dst, n);
+}
+
+// ---------------------------------------------------------------------------
+// Generation bookkeeping: ids_out[*cursor] = *cur_id (and the logits row),
+// then *cursor += 1.  Keeps the emitted ids on the device between steps.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_emit(const int32_t* cur_id, int32_t* ids_out, int32_t* cursor,
+                                              const float* logits, float* logits_out, int V) {
+  const int c = *cursor;
+  if (threadIdx.x == 0) ids_out[c] = *cur_id;
+  if (logits_out)
+    for (int i = threadIdx.x; i < V; i += 256) logits_out[(size_t)c * V + i] = logits[i];
+  __syncthreads();
+  if (threadIdx.x == 0) *cursor = c + 1;
+}
+
+void launch_emit(const int32_t* cur_id, int32_t* ids_out, int32_t* cursor, const float* logits, float* logits_out,
+                 int V, hipStream_t s) {
+  hipLaunchKernelGGL(k_emit, dim3(1), dim3(256), 0, s, cur_id, ids_out, cursor, logits, logits_out, V);
+}
+
+// explicit instantiations
+#define INST(T)                                                                                     \
+  template void launch_rms_inv<T>(const T*, int, int, float, float*, hipStream_t);                  \
+  template void launch_rmsnorm_apply<T>(const T*, const T*, int, int, float, T*, hipStream_t);      \
+  template void launch_embed<T>(const T*, int, int, const int32_t*, int, T*, hipStream_t);          \
+  template void launch_kv_write<T>(KVView, int, int, int, const T*, const T*, hipStream_t);         \
+  template void launch_kv_read<T>(KVView, int, int, int, T*, T*, hipStream_t);                      \
+  template void launch_repack_rows<T>(T*, const T*, int, int, const T*, int, int, int, int, hipStream_t); \
+  template void launch_to_f32<T>(const T*, float*, int, hipStream_t);
+INST(float)
+INST(bf16_t)
+#undef INST
+
+}  // namespace lb

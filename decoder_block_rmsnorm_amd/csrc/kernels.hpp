@@ -1,0 +1,109 @@
+// Host-side launchers of the gfx950 kernels (one definition per .hip file).
+#pragma once
+#include "common.hpp"
+
+namespace lb {
+
+// ---------------------------------------------------------------- k_misc.hip
+// inv_rms[r] = 1 / sqrt(mean(x[r,:]^2) + eps) for rows of x [rows, D].
+template <typename T>
+void launch_rms_inv(const T* x, int rows, int D, float eps, float* inv_rms, hipStream_t s);
+// out[r,:] = x[r,:] * inv_rms(x[r]) * gamma  (act dtype out)
+template <typename T>
+void launch_rmsnorm_apply(const T* x, const T* gamma, int rows, int D, float eps, T* out, hipStream_t s);
+template <typename T>
+void launch_embed(const T* table, int vocab, int D, const int32_t* ids, int n, T* out, hipStream_t s);
+// ids[r] = first index of the max of logits[r, :vocab]
+void launch_argmax(const float* logits, int rows, int vocab, int32_t* ids, hipStream_t s);
+// canonical [n, G, d] <-> paged
+template <typename T>
+void launch_kv_write(KVView kv, int seq, int pos0, int n, const T* k, const T* v, hipStream_t s);
+template <typename T>
+void launch_kv_read(KVView kv, int seq, int pos0, int n, T* k, T* v, hipStream_t s);
+void launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
+// Row repack.  Source row r first moves inside its head when perm_d > 0
+// (local index j -> j/2 for even j, perm_d/2 + j/2 for odd j: interleaved pairs
+// become (i, i + d/2) pairs), then lands at dst row row0 + (r'/ib)*ib_stride + r'%ib.
+// gamma (optional, length K) scales the columns (norm weight folding).
+template <typename T>
+void launch_repack_rows(T* dst, const T* src, int rows, int K, const T* gamma, int row0, int ib,
+                        int ib_stride, int perm_d, hipStream_t s);
+void launch_repack_bytes(uint8_t* dst, const uint8_t* src, int rows, int row_bytes, int row0, int ib,
+                         int ib_stride, int perm_d, hipStream_t s);
+// dense bf16 [N, K] = (scale * code + bias) * gamma_k (gamma may be null)
+void launch_q4_dequant(const uint32_t* words, const bf16_t* scales, const bf16_t* biases, int N, int K,
+                       int gs, const float* gamma, bf16_t* out, hipStream_t s);
+template <typename T>
+void launch_to_f32(const T* src, float* dst, int n, hipStream_t s);
+// ids_out[*cursor] = *cur_id; logits_out[*cursor] = logits (if logits_out); ++*cursor
+void launch_emit(const int32_t* cur_id, int32_t* ids_out, int32_t* cursor, const float* logits, float* logits_out,
+                 int V, hipStream_t s);
+
+// ----------------------------------------------------------- k_gemm_simt.hip
+// C[M, N] (fp32) = A[M, K] * B[N, K]^T   (generic; used by the fp32 path)
+template <typename T>
+void launch_gemm_simt(const T* A, const T* B, float* C, int M, int N, int K, hipStream_t s);
+
+// ----------------------------------------------------------- k_gemm_mfma.hip
+enum GemmEpi { EPI_F32 = 0, EPI_QKV = 1, EPI_SWIGLU = 2, EPI_RESID = 3 };
+struct GemmArgs {
+  const bf16_t* A;  // [M, K]
+  const bf16_t* B;  // [N, K]
+  int M, N, K;
+  // EPI_F32
+  float* C;
+  // row scale (QKV / SWIGLU): inv_rms[M]
+  const float* inv_rms;
+  // EPI_QKV
+  bf16_t* q_out;          // [M, Nq]
+  int Nq, Nkv, L;         // row m = b * L + l
+  const float2* rope;     // [max_seq][64] (cos, sin)
+  int traditional;
+  KVView kv;
+  // EPI_SWIGLU
+  bf16_t* g_out;          // [M, N/2]
+  // EPI_RESID
+  const bf16_t* resid;    // [M, N]
+  bf16_t* out;            // [M, N]
+  int32_t* lens_add;      // if non-null: lens_add[b] += lens_inc for b < n_seq (block 0)
+  int lens_inc, n_seq;
+};
+void launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- k_gemv.hip
+// partial[ks][M][N] (fp32) = X[M, kslice] * W[N, kslice]^T (bf16, M <= 64)
+void launch_gemv_bf16(const bf16_t* X, const bf16_t* W, float* partial, int M, int N, int K, int ks,
+                      hipStream_t s);
+// y[M][N] (fp32) = xhat W^T, W 4-bit group affine, xhat = x * inv_rms * gamma (each
+// optional), M <= 4.  xh_buf: fp16 [M, K]; xsum_buf: fp32 [M, K/32, 2] (scratch).
+void launch_gemv_q4(const bf16_t* X, const float* inv_rms, const float* gamma, const uint32_t* words,
+                    const bf16_t* scales, const bf16_t* biases, float* y, int M, int N, int K, int gs,
+                    _Float16* xh_buf, float* xsum_buf, hipStream_t s);
+
+// ------------------------------------------------------------ k_epilogue.hip
+// All take fp32 partials [ks][M][N] and reduce them in a fixed order.
+template <typename T>
+void launch_epi_qkv(const float* part, int ks, int M, int Nq, int Nkv, const float* inv_rms, int L,
+                    const float2* rope, int traditional, T* q_out, KVView kv, hipStream_t s);
+template <typename T>
+void launch_epi_resid(const float* part, int ks, int M, int N, const T* resid, T* out, float eps,
+                      float* inv_rms_out, int32_t* lens_add, int lens_inc, int n_seq, hipStream_t s);
+template <typename T>
+void launch_epi_swiglu(const float* part, int ks, int M, int F2, int ib, const float* inv_rms, T* g_out,
+                       hipStream_t s);
+// logits[M][N] = sum_ks part
+void launch_reduce_f32(const float* part, int ks, int M, int N, float* out, hipStream_t s);
+
+// ---------------------------------------------------------------- k_attn.hip
+// generic causal attention over the paged cache (fp32 path):
+// q [T, H*d] with row m = b*L + l at position lens_before[b] + l; out [T, H*d]
+template <typename T>
+void launch_attn_simt(const T* q, KVView kv, int B, int L, int H, int G, int d, T* out, hipStream_t s);
+// bf16 flash prefill (d = 128)
+void launch_attn_prefill_bf16(const bf16_t* q, KVView kv, int B, int L, int H, int G, bf16_t* out,
+                              hipStream_t s);
+// bf16 split-K decode (d = 128): one token per sequence at position lens[b] (already appended)
+void launch_attn_decode_bf16(const bf16_t* q, KVView kv, int B, int H, int G, int n_splits, int split_len,
+                             float* part_o, float* part_ml, bf16_t* out, hipStream_t s);
+
+}  // namespace lb

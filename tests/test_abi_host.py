@@ -1,0 +1,128 @@
+"""Host-side tests of the C ABI (CPU only, no kernel is launched).
+
+The library must load, export every entry point that include/llama_block.h
+declares, and reject invalid arguments on the host with the documented status
+before touching the device.
+"""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import decoder_block_rmsnorm_amd as L
+from decoder_block_rmsnorm_amd import _abi
+
+HEADER = _abi.HEADER
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(llama_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_header_declares_and_library_exports_every_entry_point():
+    names = _declared()
+    assert len(names) >= 20
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+    assert set(names) == set(_abi.SIGNATURES), "binding and header disagree"
+    out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (llama_[a-z0-9_]+)", out))
+    assert set(names) <= exported
+
+
+def cfg(**kw):
+    base = dict(dim=4096, n_heads=32, n_kv_heads=32, ffn_dim=11008, norm_eps=1e-5, rope_theta=1e4,
+                rope_traditional=False, act_dtype=L.LLAMA_BF16, weight_format=L.LLAMA_W_DENSE, group_size=64,
+                max_seq=4097)
+    base.update(kw)
+    return L.block_config(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_kv_heads=5), L.LLAMA_ERR_INVALID_ARG),          # H % G != 0
+    (dict(dim=4000), L.LLAMA_ERR_INVALID_ARG),             # dim % n_heads != 0
+    (dict(norm_eps=0.0), L.LLAMA_ERR_INVALID_ARG),
+    (dict(norm_eps=-1e-5), L.LLAMA_ERR_INVALID_ARG),
+    (dict(rope_theta=0.0), L.LLAMA_ERR_INVALID_ARG),
+    (dict(act_dtype=7), L.LLAMA_ERR_INVALID_ARG),
+    (dict(weight_format=3), L.LLAMA_ERR_INVALID_ARG),
+    (dict(max_seq=0), L.LLAMA_ERR_INVALID_ARG),
+    (dict(dim=3072, n_heads=32, n_kv_heads=32), L.LLAMA_ERR_UNSUPPORTED),   # head_dim 96 in bf16
+    (dict(ffn_dim=11000), L.LLAMA_ERR_UNSUPPORTED),        # ffn % 64 != 0 in bf16
+    (dict(weight_format=L.LLAMA_W_Q4, act_dtype=L.LLAMA_F32, dim=256, n_heads=4, n_kv_heads=4, ffn_dim=688),
+     L.LLAMA_ERR_UNSUPPORTED),
+    (dict(weight_format=L.LLAMA_W_Q4, group_size=32), L.LLAMA_ERR_UNSUPPORTED),
+    (dict(n_heads=64, n_kv_heads=2, dim=8192), L.LLAMA_ERR_UNSUPPORTED),    # n_rep 32 > 16
+])
+def test_invalid_configs_rejected_on_host(kw, status):
+    c = cfg(**kw)
+    assert L.llama_block_weight_bytes(c) == 0
+    assert L.llama_scratch_bytes(c, 16, 1, 64) == 0
+    with pytest.raises(L.LlamaError) as e:
+        L.llama_block_create(c, L.llama_block_weights(), 0, 0, 0)
+    assert e.value.status == status, e.value
+
+
+def test_valid_configs_size_and_null_pointers():
+    c = cfg()
+    wb = L.llama_block_weight_bytes(c)
+    # repacked weights (bf16) + RoPE table + fp32 norm weights
+    lin = 4096 * (3 * 4096) + 4096 * 4096 + 3 * 4096 * 11008
+    assert 2 * lin <= wb <= 2 * lin + 4097 * 64 * 8 + 4 * 4096 * 2 + 64 * 256
+    assert L.llama_scratch_bytes(c, 2048, 1, 4097) > 2048 * 4096 * 2
+    with pytest.raises(L.LlamaError) as e:
+        L.llama_block_create(c, L.llama_block_weights(), 0, 0, 0)     # NULL weights / memory
+    assert e.value.status == L.LLAMA_ERR_INVALID_ARG
+    t = L.block_config(256, 4, 4, 688, act_dtype=L.LLAMA_F32, rope_traditional=True, max_seq=40)
+    assert L.llama_block_weight_bytes(t) > 790528 * 4
+
+
+def test_kvcache_config_validation():
+    ok = L.llama_kvcache_config(40, 1, 640, 40, 128, 64, L.LLAMA_BF16)
+    n = L.llama_kvcache_bytes(ok)
+    assert n >= 2 * 40 * 10 * 64 * 40 * 128 * 2           # 10 pages of 64 per layer, K and V
+    for bad, status in [(L.llama_kvcache_config(1, 1, 64, 4, 64, 48, L.LLAMA_F32), L.LLAMA_ERR_UNSUPPORTED),
+                        (L.llama_kvcache_config(0, 1, 64, 4, 64, 64, L.LLAMA_F32), L.LLAMA_ERR_INVALID_ARG),
+                        (L.llama_kvcache_config(1, 1, 64, 4, 64, 64, 9), L.LLAMA_ERR_INVALID_ARG)]:
+        assert L.llama_kvcache_bytes(bad) == 0
+        with pytest.raises(L.LlamaError) as e:
+            L.llama_kvcache_init(bad, 0, 0, 0)
+        assert e.value.status == status
+    with pytest.raises(L.LlamaError) as e:
+        L.llama_kvcache_init(ok, 0, n, 0)                 # NULL memory
+    assert e.value.status == L.LLAMA_ERR_INVALID_ARG
+    with pytest.raises(L.LlamaError) as e:
+        L.llama_kvcache_init(ok, 256, n - 256, 0)         # too small (checked before any access)
+    assert e.value.status == L.LLAMA_ERR_CAPACITY
+
+
+def test_null_handles_and_head_validation():
+    with pytest.raises(L.LlamaError) as e:
+        L.llama_block_prefill(None, None, 0, None, None, 1, 1, None, 0, 0)
+    assert e.value.status == L.LLAMA_ERR_INVALID_ARG
+    with pytest.raises(L.LlamaError) as e:
+        L.llama_block_decode(None, None, 0, None, None, 1, None, 0, 0)
+    assert e.value.status == L.LLAMA_ERR_INVALID_ARG
+    with pytest.raises(L.LlamaError):
+        L.llama_lm_head_argmax(L.llama_linear(), 0, 64, 1, None, 1e-5, None, 1, 64, 100, None, None, None, 0, 0)
+    assert L.llama_head_scratch_bytes(1, 5120, 32000) >= 32000 * 4
+    assert L.llama_head_scratch_bytes(0, 5120, 32000) == 0
+    with pytest.raises(L.LlamaError) as e:
+        L.llama_stack_create([], None, 0, None, L.llama_linear())
+    assert e.value.status == L.LLAMA_ERR_INVALID_ARG
+    assert "stack" in L.llama_last_error()
+
+
+def test_product_path_does_not_import_the_oracle():
+    import decoder_block_rmsnorm_amd
+    pkg = os.path.dirname(decoder_block_rmsnorm_amd.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                txt = open(os.path.join(root, f), errors="ignore").read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f

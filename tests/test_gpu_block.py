@@ -1,0 +1,248 @@
+"""GPU parity of the decoder block against the CPU oracle (small shapes that
+still span several tiles, ragged tails and cache offsets).
+
+Bars: fp32 max relative error (inf-norm) <= 1e-4; bf16 and 4-bit relative L2
+error <= 1e-2 per output tensor, also on the attention output before wo and on
+the feed-forward branch.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import ref
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _flush(*a):
+    print(*a, flush=True)
+
+
+def _run_prefill(s, w, x, lens=None, kv=None, max_seq=None, page_size=64):
+    """x: [B, L, D] numpy.  lens/kv: optional pre-existing cache per sequence."""
+    B, Lq, D = x.shape
+    max_seq = max_seq or (max(lens or [0]) + Lq + 8)
+    blk, wd = G.make_block(s, w, max_seq)
+    cache = G.make_cache(s, 1, B, max_seq, page_size)
+    if lens is not None:
+        for b in range(B):
+            if lens[b]:
+                cache.write(0, b, 0, G.tdev(kv[0][b], s.dtype), G.tdev(kv[1][b], s.dtype))
+        cache.set_lens(0, lens)
+    sc = G.scratch(blk, B * Lq, B, max_seq)
+    xd = G.tdev(x.reshape(B * Lq, D), s.dtype)
+    y = torch.empty_like(xd)
+    blk.prefill(cache, 0, xd, y, B, Lq, sc)
+    torch.cuda.synchronize()
+    return blk, cache, sc, G.thost(y).reshape(B, Lq, D)
+
+
+def _oracle(s, w, x, lens=None, kv=None):
+    kc = vc = None
+    if lens is not None:
+        kc = [kv[0][b][:lens[b]] for b in range(x.shape[0])]
+        vc = [kv[1][b][:lens[b]] for b in range(x.shape[0])]
+    return ref.block_forward(x, w, s, kc, vc)
+
+
+def _check_branches(s, blk, sc, r, y, B, Lq):
+    T = B * Lq
+    attn = G.diag(blk, sc, 0, T, s.n_heads * s.head_dim, s.dtype)
+    h = G.diag(blk, sc, 1, T, s.dim, s.dtype)
+    ra = np.concatenate(r["attn"])
+    rh = np.concatenate(r["h"])
+    rf = np.concatenate(r["ffn"])
+    G.check(s.dtype, attn, ra, "attention output (before wo)")
+    G.check(s.dtype, h, rh, "h = x + wo o")
+    G.check(s.dtype, y.reshape(T, -1) - h, rf, "feed-forward branch", tol_f32=1e-3)
+
+
+# ------------------------------------------------------------------ fp32 --
+def test_tiny_fp32_prefill32_then_8_decode_steps():
+    wl = W.get("tiny_f32_d256_prefill32_decode8")
+    inp = W.draw_block_workload(wl)
+    s, w, x = wl.shape, inp["weights"], inp["x"]           # x [1, 40, 256]
+    _flush("case: tiny fp32 block, prefill 32 + 8 decode")
+    blk, wd = G.make_block(s, w, 64)
+    cache = G.make_cache(s, 1, 1, 64)
+    sc = G.scratch(blk, 32, 1, 64)
+    xd = G.tdev(x[0], "f32")
+    y = torch.empty_like(xd)
+    blk.prefill(cache, 0, xd[:32], y[:32], 1, 32, sc)
+    for t in range(32, 40):
+        blk.decode(cache, 0, xd[t:t + 1], y[t:t + 1], 1, sc)
+    torch.cuda.synchronize()
+    got = G.thost(y)
+    pre = ref.block_forward(x[:, :32], w, s)
+    G.check("f32", got[:32], pre["y"][0], "prefill y")
+    kc, vc = list(pre["k_new"]), list(pre["v_new"])
+    for t in range(32, 40):
+        r = ref.block_forward(x[:, t:t + 1], w, s, kc, vc)
+        G.check("f32", got[t:t + 1], r["y"][0], f"decode step {t - 31} y")
+        kc[0] = np.concatenate([kc[0], r["k_new"][0]])
+        vc[0] = np.concatenate([vc[0], r["v_new"][0]])
+    assert cache.get_lens(0, 1) == [40]
+    # the cache holds exactly the rotated keys / values the oracle produced
+    k = torch.empty((40, s.n_kv_heads, s.head_dim), device="cuda")
+    v = torch.empty_like(k)
+    cache.read(0, 0, 0, 40, k, v)
+    G.check("f32", G.thost(k), kc[0], "cache K")
+    G.check("f32", G.thost(v), vc[0], "cache V")
+
+
+@pytest.mark.parametrize("traditional", [False, True])
+def test_fp32_gqa_chunked_prefill_ragged_cache(traditional):
+    s = dataclasses.replace(W.TEST_SHAPES["tiny_gqa_d128"], traditional=traditional)
+    rng = W.Rng(5)
+    w = W.draw_block_weights(s, rng)
+    x = rng.normal((3, 7, s.dim), 1.0, "f32")
+    lens = [0, 5, 70]
+    kv = (rng.normal((3, 70, s.n_kv_heads, s.head_dim), 1.0, "f32"),
+          rng.normal((3, 70, s.n_kv_heads, s.head_dim), 1.0, "f32"))
+    _flush(f"case: fp32 GQA chunked prefill traditional={traditional}")
+    blk, cache, sc, y = _run_prefill(s, w, x, lens, kv, max_seq=128)
+    r = _oracle(s, w, x, lens, kv)
+    G.check("f32", y, np.stack(r["y"]), "y")
+    _check_branches(s, blk, sc, r, y, 3, 7)
+    assert cache.get_lens(0, 3) == [7, 12, 77]
+
+
+# ------------------------------------------------------------------ bf16 --
+SMALL_MHA = W.BlockShape(dim=512, n_heads=4, n_kv_heads=4, ffn_dim=1536, dtype="bf16")
+SMALL_GQA = W.BlockShape(dim=1024, n_heads=8, n_kv_heads=2, ffn_dim=2816, dtype="bf16")
+
+
+@pytest.mark.parametrize("traditional", [False, True])
+def test_bf16_prefill_mha_several_tiles_ragged(traditional):
+    s = dataclasses.replace(SMALL_MHA, traditional=traditional)
+    rng = W.Rng(11)
+    x = rng.normal((2, 300, s.dim), 1.0, "bf16")
+    w = W.draw_block_weights(s, rng)
+    _flush(f"case: bf16 MHA prefill B=2 L=300 traditional={traditional}")
+    blk, cache, sc, y = _run_prefill(s, w, x)
+    r = _oracle(s, w, x)
+    G.check("bf16", y, np.stack(r["y"]), "y")
+    _check_branches(s, blk, sc, r, y, 2, 300)
+    k = torch.empty((300, s.n_kv_heads, s.head_dim), device="cuda", dtype=torch.bfloat16)
+    v = torch.empty_like(k)
+    cache.read(0, 1, 0, 300, k, v)
+    G.check("bf16", G.thost(k), r["k_new"][1], "cache K (rotated)")
+    G.check("bf16", G.thost(v), r["v_new"][1], "cache V")
+
+
+def test_bf16_prefill_gqa_with_cached_prefix():
+    s = SMALL_GQA
+    rng = W.Rng(12)
+    x = rng.normal((2, 200, s.dim), 1.0, "bf16")
+    lens = [64, 130]
+    kv = (rng.normal((2, 130, s.n_kv_heads, s.head_dim), 1.0, "bf16"),
+          rng.normal((2, 130, s.n_kv_heads, s.head_dim), 1.0, "bf16"))
+    w = W.draw_block_weights(s, rng)
+    _flush("case: bf16 GQA(4) chunked prefill B=2 L=200 after 64/130 cached")
+    blk, cache, sc, y = _run_prefill(s, w, x, lens, kv)
+    r = _oracle(s, w, x, lens, kv)
+    G.check("bf16", y, np.stack(r["y"]), "y")
+    _check_branches(s, blk, sc, r, y, 2, 200)
+
+
+@pytest.mark.parametrize("shape", ["mha", "gqa"])
+def test_bf16_decode_ragged_lengths(shape):
+    s = dataclasses.replace(SMALL_MHA if shape == "mha" else SMALL_GQA, traditional=(shape == "mha"))
+    rng = W.Rng(13)
+    lens = [300, 1, 64, 255, 257]
+    B = len(lens)
+    x = rng.normal((B, 1, s.dim), 1.0, "bf16")
+    kv = (rng.normal((B, 300, s.n_kv_heads, s.head_dim), 1.0, "bf16"),
+          rng.normal((B, 300, s.n_kv_heads, s.head_dim), 1.0, "bf16"))
+    w = W.draw_block_weights(s, rng)
+    _flush(f"case: bf16 {shape} decode B={B} lens={lens}")
+    max_seq = 320
+    blk, wd = G.make_block(s, w, max_seq)
+    cache = G.make_cache(s, 1, B, max_seq)
+    for b in range(B):
+        cache.write(0, b, 0, G.tdev(kv[0][b, :lens[b]], s.dtype), G.tdev(kv[1][b, :lens[b]], s.dtype))
+    cache.set_lens(0, lens)
+    sc = G.scratch(blk, B, B, max_seq)
+    xd = G.tdev(x.reshape(B, s.dim), s.dtype)
+    y = torch.empty_like(xd)
+    blk.decode(cache, 0, xd, y, B, sc)
+    torch.cuda.synchronize()
+    r = _oracle(s, w, x, lens, kv)
+    got = G.thost(y).reshape(B, 1, s.dim)
+    G.check("bf16", got, np.stack(r["y"]), "y")
+    _check_branches(s, blk, sc, r, got, B, 1)
+    assert cache.get_lens(0, B) == [l + 1 for l in lens]
+
+
+def test_bf16_prefill_then_decode_steps_match_oracle():
+    s = SMALL_GQA
+    rng = W.Rng(14)
+    x = rng.normal((2, 103, s.dim), 1.0, "bf16")
+    w = W.draw_block_weights(s, rng)
+    _flush("case: bf16 prefill 100 then 3 decode steps")
+    max_seq = 128
+    blk, wd = G.make_block(s, w, max_seq)
+    cache = G.make_cache(s, 1, 2, max_seq)
+    sc = G.scratch(blk, 200, 2, max_seq)
+    xd = G.tdev(x, s.dtype)
+    y = torch.empty_like(xd)
+    blk.prefill(cache, 0, xd[:, :100].contiguous(), y[:, :100], 2, 100, sc)
+    yp = G.thost(y[:, :100])
+    outs = []
+    for t in range(100, 103):
+        yt = torch.empty((2, s.dim), device="cuda", dtype=torch.bfloat16)
+        blk.decode(cache, 0, xd[:, t].contiguous(), yt, 2, sc)
+        outs.append(G.thost(yt))
+    torch.cuda.synchronize()
+    full = ref.stack_arrays(ref.block_forward(x, w, s), "y")   # one causal pass over all 103
+    G.check("bf16", yp, full[:, :100], "prefill rows")
+    for i, t in enumerate(range(100, 103)):
+        G.check("bf16", outs[i], full[:, t], f"decode step {i + 1}")
+
+
+# ------------------------------------------------------------------ 4-bit --
+SMALL_Q4 = W.BlockShape(dim=512, n_heads=4, n_kv_heads=4, ffn_dim=1536, dtype="bf16", weight_format="q4",
+                        traditional=True)
+
+
+@pytest.mark.parametrize("B", [1, 3])
+def test_q4_decode(B):
+    s = SMALL_Q4
+    rng = W.Rng(15)
+    lens = [77, 200, 3][:B]
+    x = rng.normal((B, 1, s.dim), 1.0, "bf16")
+    kv = (rng.normal((B, 200, s.n_kv_heads, s.head_dim), 1.0, "bf16"),
+          rng.normal((B, 200, s.n_kv_heads, s.head_dim), 1.0, "bf16"))
+    w = W.draw_block_weights(s, rng)
+    _flush(f"case: 4-bit decode B={B}")
+    max_seq = 256
+    blk, wd = G.make_block(s, w, max_seq)
+    cache = G.make_cache(s, 1, B, max_seq)
+    for b in range(B):
+        cache.write(0, b, 0, G.tdev(kv[0][b, :lens[b]], "bf16"), G.tdev(kv[1][b, :lens[b]], "bf16"))
+    cache.set_lens(0, lens)
+    sc = G.scratch(blk, B, B, max_seq)
+    xd = G.tdev(x.reshape(B, s.dim), "bf16")
+    y = torch.empty_like(xd)
+    blk.decode(cache, 0, xd, y, B, sc)
+    torch.cuda.synchronize()
+    r = _oracle(s, w, x, lens, kv)
+    got = G.thost(y).reshape(B, 1, s.dim)
+    G.check("bf16", got, np.stack(r["y"]), "y")
+    _check_branches(s, blk, sc, r, got, B, 1)
+
+
+def test_q4_prefill():
+    s = SMALL_Q4
+    rng = W.Rng(16)
+    x = rng.normal((1, 150, s.dim), 1.0, "bf16")
+    w = W.draw_block_weights(s, rng)
+    _flush("case: 4-bit prefill L=150")
+    blk, cache, sc, y = _run_prefill(s, w, x)
+    r = _oracle(s, w, x)
+    G.check("bf16", y, np.stack(r["y"]), "y")
+    _check_branches(s, blk, sc, r, y, 1, 150)
