@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Throughput of the MI355X decoder block on its synthetic workloads.
+
+Default (N=1): the LLaMA-2-7B-shaped block, causal prefill of one 2048-token
+prompt (bf16), reported as prefill TFLOP/s with the roofline of its dominant
+kernel; plus the LLaMA-2-13B-shaped decode (16 sequences against 4096-token
+caches) as tokens/s with its HBM roofline; plus the CPU oracle timed on this
+host on a bounded sample.  Prints ONE JSON line on stdout.
+
+A step is one llama_block_prefill (or llama_block_decode) call over the whole
+batch, inputs resident in HBM.  Phase times come from HIP events recorded by
+the library on the stream it launches on (llama_block_profile_*).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decoder-block prefill TFLOP/s + decode tokens/s; % MFMA / HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PREFILL_PHASES = ["rms_x", "qkv_gemm_rope_append", "attention_prefill", "wo_gemm_residual", "rms_h",
+                  "w13_gemm_swiglu", "w2_gemm_residual"]
+DECODE_PHASES = ["rms_x", "qkv_gemv", "qkv_finish_rope_append", "attention_decode", "wo_gemv", "wo_residual_rms",
+                 "w13_gemv", "swiglu", "w2_gemv", "w2_residual"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _setup(wl, max_seq, n_layers):
+    import torch
+    import workloads as W
+    import decoder_block_rmsnorm_amd as L
+    from tests import gpu_util as G
+    t0 = time.time()
+    inp = W.draw_block_workload(wl)
+    log(f"[bench] {wl.name}: inputs drawn in {time.time() - t0:.1f}s")
+    s = wl.shape
+    blk, wd = G.make_block(s, inp["weights"], max_seq)
+    del wd
+    cache = L.KVCache(n_layers, wl.batch, max_seq, s.n_kv_heads, s.head_dim, dtype=G.act_code(s.dtype))
+    torch.cuda.synchronize()
+    return inp, blk, cache
+
+
+def bench_prefill(wl, steps, warmup):
+    import torch
+    import workloads as W
+    from tests import gpu_util as G
+    s, B, Lq = wl.shape, wl.batch, wl.seq_len
+    # one cache layer per call so that every call starts from an empty cache
+    inp, blk, cache = _setup(wl, Lq, steps + warmup)
+    sc = G.scratch(blk, B * Lq, B, Lq)
+    x = G.tdev(inp["x"].reshape(B * Lq, s.dim), s.dtype)
+    y = torch.empty_like(x)
+    for i in range(warmup):
+        blk.prefill(cache, i, x, y, B, Lq, sc)
+    torch.cuda.synchronize()
+    blk.profile_start(steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(steps):
+        blk.prefill(cache, warmup + i, x, y, B, Lq, sc)
+    e1.record()
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    ph_ms, ncalls = blk.profile_read()
+    flops = W.prefill_flops(s, B, Lq)
+    lin = W.linear_flops(s, B * Lq)
+    attn_flops = flops - sum(lin.values())
+    ph_flops = [0.0, lin["qkv"], attn_flops, lin["wo"], 0.0, lin["w13"], lin["w2"]]
+    phases = {}
+    for name, ms, fl in zip(PREFILL_PHASES, ph_ms, ph_flops):
+        avg = ms / max(ncalls, 1)
+        phases[name] = {"avg_us": round(avg * 1e3, 2),
+                        "tflops": round(fl / (avg * 1e-3) / 1e12, 1) if fl and avg > 0 else None}
+    dom = max(range(len(ph_ms)), key=lambda i: ph_ms[i])
+    avg_dom = ph_ms[dom] / ncalls * 1e-3
+    achieved = ph_flops[dom] / avg_dom / 1e12
+    ms = total_ms / steps
+    return {
+        "ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12, "tokens_per_s": B * Lq / (ms * 1e-3),
+        "flops_per_step": flops, "phases": phases,
+        "roofline": {"kernel": PREFILL_PHASES[dom], "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": ph_flops[dom], "avg_launch_us": round(avg_dom * 1e6, 2)},
+    }
+
+
+def bench_decode(wl, steps, warmup):
+    import torch
+    import workloads as W
+    from tests import gpu_util as G
+    s, B, S0 = wl.shape, wl.batch, wl.cache_len
+    max_seq = S0 + warmup + steps + 1
+    inp, blk, cache = _setup(wl, max_seq, 1)
+    for b in range(B):
+        cache.write(0, b, 0, G.tdev(inp["k_cache"][b], s.dtype), G.tdev(inp["v_cache"][b], s.dtype))
+    cache.set_lens(0, [S0] * B)
+    del inp["k_cache"], inp["v_cache"]
+    sc = G.scratch(blk, B, B, max_seq)
+    x = G.tdev(inp["x"].reshape(B, s.dim), s.dtype)
+    y = torch.empty_like(x)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")   # > the 256 MB last-level cache
+    for _ in range(warmup):
+        blk.decode(cache, 0, x, y, B, sc)
+    torch.cuda.synchronize()
+    blk.profile_start(steps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        flush.zero_()
+        ev[i][0].record()
+        blk.decode(cache, 0, x, y, B, sc)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    times = [a.elapsed_time(b) for a, b in ev]
+    ph_ms, ncalls = blk.profile_read()
+    byts = [W.decode_bytes(s, B, S0 + warmup + i) for i in range(steps)]
+    ms = sum(times) / steps
+    tot_bytes = sum(b["total"] for b in byts) / steps
+    kv_bytes = sum(b["kv_read"] + b["kv_write"] for b in byts) / steps
+    attn_us = ph_ms[3] / ncalls * 1e3
+    phases = {n: {"avg_us": round(v / ncalls * 1e3, 2)} for n, v in zip(DECODE_PHASES, ph_ms)}
+    w_phase = {"qkv_gemv": 1, "wo_gemv": 4, "w13_gemv": 6, "w2_gemv": 8}
+    lb = {"qkv_gemv": s.dim * (s.n_heads + 2 * s.n_kv_heads) * s.head_dim,
+          "wo_gemv": s.n_heads * s.head_dim * s.dim, "w13_gemv": 2 * s.dim * s.ffn_dim, "w2_gemv": s.ffn_dim * s.dim}
+    esz = 2 if s.dtype == "bf16" else 4
+    for n, i in w_phase.items():
+        us = ph_ms[i] / ncalls * 1e3
+        phases[n]["gbs"] = round(lb[n] * esz / (us * 1e-6) / 1e9, 1)
+    phases["attention_decode"]["gbs"] = round(kv_bytes / (attn_us * 1e-6) / 1e9, 1)
+    achieved = kv_bytes / (attn_us * 1e-6) / 1e9
+    return {
+        "workload": wl.name, "batch": B, "cache_len": S0, "us_per_step": round(ms * 1e3, 2),
+        "tokens_per_s": round(B / (ms * 1e-3), 1), "bytes_per_step": tot_bytes,
+        "hbm_frac_step": round(tot_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "phases": phases,
+        "roofline": {"kernel": "attention_decode", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None, "bytes_per_launch": kv_bytes, "avg_launch_us": round(attn_us, 2)},
+    }
+
+
+def cpu_baseline(wl, sample_tokens):
+    """The oracle, as it stands, timed on this host on the first `sample_tokens`
+    tokens of the same prompt (a causal prefill of that shorter prompt)."""
+    import numpy as np
+    import workloads as W
+    from oracle import ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    inp = W.draw_block_workload(wl)
+    x = inp["x"][:, :sample_tokens]
+    t0 = time.perf_counter()
+    ref.block_forward(x, inp["weights"], wl.shape)
+    dt = time.perf_counter() - t0
+    fl = W.prefill_flops(wl.shape, wl.batch, sample_tokens)
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"causal prefill of the first {sample_tokens} of the {wl.seq_len} prompt tokens "
+                      f"(batch {wl.batch}), float64 numpy, {dt:.1f} s; {fl / 1e12:.3f} TFLOP counted",
+            "cpu": cpu}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_block_prefill_b1_l2048")
+    ap.add_argument("--decode-workload", default="llama13b_block_decode_b16_kv4096",
+                    help="decode workload reported beside the prefill line ('' to skip)")
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="prompt tokens the oracle baseline runs (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the block's data-parallel "
+              "sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wl = W.get(args.workload)
+    if wl.mode != "prefill":
+        raise SystemExit("--workload must be a prefill workload; decode workloads go to --decode-workload")
+    log(f"[bench] prefill {wl.name}: warmup {args.warmup}, steps {args.steps}")
+    pre = bench_prefill(wl, args.steps, args.warmup)
+    log(f"[bench] prefill {pre['ms_per_step']:.3f} ms/step, {pre['tflops']:.1f} TFLOP/s")
+    out = {
+        "metric": METRIC, "value": round(pre["tflops"], 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) weights, 1+U(-0.1,0.1) norm weights)",
+        "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seq_len, "dim": wl.shape.dim,
+                   "n_heads": wl.shape.n_heads, "n_kv_heads": wl.shape.n_kv_heads, "ffn_dim": wl.shape.ffn_dim,
+                   "tokens_per_s": round(pre["tokens_per_s"], 1), "frac_of_peak_block": round(
+                       pre["tflops"] / PEAK_BF16_TFLOPS, 4)},
+        "roofline": pre["roofline"],
+        "prefill_phases": pre["phases"],
+    }
+    if args.decode_workload:
+        dw = W.get(args.decode_workload)
+        del pre
+        torch.cuda.empty_cache()
+        log(f"[bench] decode {dw.name}")
+        dec = bench_decode(dw, args.steps, args.warmup)
+        log(f"[bench] decode {dec['us_per_step']} us/step, {dec['tokens_per_s']} tok/s")
+        out["decode"] = dec
+    if args.cpu_sample > 0:
+        log(f"[bench] cpu oracle baseline on {args.cpu_sample} tokens")
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

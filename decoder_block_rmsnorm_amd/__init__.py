@@ -17,7 +17,7 @@ import ctypes as C
 from typing import Dict, Optional, Sequence
 
 from . import _abi
-from ._abi import (LLAMA_BF16, LLAMA_DIAG_ATTN, LLAMA_DIAG_H, LLAMA_ERR_CAPACITY, LLAMA_ERR_HIP,  # noqa: F401
+from ._abi import (LLAMA_BF16, LLAMA_DIAG_ATTN, LLAMA_DIAG_FFN, LLAMA_DIAG_H, LLAMA_ERR_CAPACITY, LLAMA_ERR_HIP,  # noqa: F401
                    LLAMA_ERR_INVALID_ARG, LLAMA_ERR_UNSUPPORTED, LLAMA_F32, LLAMA_OK, LLAMA_W_DENSE, LLAMA_W_Q4,
                    STATUS_NAMES, llama_block_config, llama_block_weights, llama_kvcache_config, llama_linear)
 
@@ -99,6 +99,21 @@ def llama_block_diag(blk, scratch, which: int, tokens: int) -> int:
     out = C.c_void_p()
     _check(lib().llama_block_diag(blk, _ptr(scratch), which, tokens, C.byref(out)))
     return out.value
+
+
+def llama_block_set_diag(blk, enable: int) -> None:
+    _check(lib().llama_block_set_diag(blk, int(enable)))
+
+
+def llama_block_profile_start(blk, max_calls: int) -> None:
+    _check(lib().llama_block_profile_start(blk, max_calls))
+
+
+def llama_block_profile_read(blk, max_phases: int = 16):
+    ms = (C.c_float * max_phases)()
+    n_ph, n_calls = C.c_int32(), C.c_int32()
+    _check(lib().llama_block_profile_read(blk, ms, max_phases, C.byref(n_ph), C.byref(n_calls)))
+    return list(ms)[:n_ph.value], n_calls.value
 
 
 def llama_kvcache_bytes(cfg: llama_kvcache_config) -> int:
@@ -226,6 +241,16 @@ class Block:
 
     def diag(self, scratch, which: int, tokens: int) -> int:
         return llama_block_diag(self.handle, scratch, which, tokens)
+
+    def set_diag(self, enable: bool) -> None:
+        llama_block_set_diag(self.handle, int(enable))
+
+    def profile_start(self, max_calls: int) -> None:
+        llama_block_profile_start(self.handle, max_calls)
+
+    def profile_read(self):
+        """-> (per-phase summed milliseconds, number of calls)"""
+        return llama_block_profile_read(self.handle)
 
     def __del__(self):
         h = getattr(self, "handle", None)

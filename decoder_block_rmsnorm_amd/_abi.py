@@ -11,7 +11,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "llama_block.h")
 LLAMA_OK, LLAMA_ERR_INVALID_ARG, LLAMA_ERR_UNSUPPORTED, LLAMA_ERR_CAPACITY, LLAMA_ERR_HIP = 0, -1, -2, -3, -4
 LLAMA_F32, LLAMA_BF16 = 0, 1
 LLAMA_W_DENSE, LLAMA_W_Q4 = 0, 1
-LLAMA_DIAG_ATTN, LLAMA_DIAG_H = 0, 1
+LLAMA_DIAG_ATTN, LLAMA_DIAG_H, LLAMA_DIAG_FFN = 0, 1, 2
 
 STATUS_NAMES = {0: "LLAMA_OK", -1: "LLAMA_ERR_INVALID_ARG", -2: "LLAMA_ERR_UNSUPPORTED",
                 -3: "LLAMA_ERR_CAPACITY", -4: "LLAMA_ERR_HIP"}
@@ -51,6 +51,9 @@ SIGNATURES = {
     "llama_block_prefill": (I32, [P, P, I32, P, P, I32, I32, P, SZ, P]),
     "llama_block_decode": (I32, [P, P, I32, P, P, I32, P, SZ, P]),
     "llama_block_diag": (I32, [P, P, I32, I32, PP]),
+    "llama_block_set_diag": (I32, [P, I32]),
+    "llama_block_profile_start": (I32, [P, I32]),
+    "llama_block_profile_read": (I32, [P, C.POINTER(C.c_float), I32, PI32, PI32]),
     "llama_kvcache_bytes": (SZ, [C.POINTER(llama_kvcache_config)]),
     "llama_kvcache_init": (I32, [C.POINTER(llama_kvcache_config), P, SZ, P, PP]),
     "llama_kvcache_destroy": (None, [P]),

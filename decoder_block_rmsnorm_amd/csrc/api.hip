@@ -108,6 +108,24 @@ struct llama_block {
   float* gamma1;    // fp32 [D]
   float* gamma2;
   Lin qkv, o, w13, w2;
+  int diag = 0;     // store the feed-forward branch for LLAMA_DIAG_FFN
+  // profiling: events [max_calls][kMaxMarks], calls recorded so far
+  std::vector<hipEvent_t> ev;
+  int prof_max = 0, prof_calls = 0, prof_marks = 0;
+  ~llama_block() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  }
+};
+
+static const int kMaxMarks = 12;
+
+// Records an event before the first kernel and after each phase of one call.
+struct Marker {
+  hipEvent_t* ev = nullptr;
+  int i = 0;
+  void operator()(hipStream_t s) {
+    if (ev && i < kMaxMarks) (void)hipEventRecord(ev[i++], s);
+  }
 };
 
 struct WLayout {
@@ -445,7 +463,7 @@ static int gemv_ks(int M, int N, int K) {
 }
 
 struct SLayout {
-  size_t inv1, inv2, q, attn, h, g, part, ao, aml, xh, xsum, deq, total;
+  size_t inv1, inv2, q, attn, h, g, ffn, part, ao, aml, xh, xsum, deq, total;
   int n_splits;
 };
 
@@ -460,6 +478,7 @@ static SLayout scratch_layout(const llama_block_config& c, const Dims& d, int T,
   L.attn = off; off = align256(off + (size_t)T * d.Nq * E);
   L.h = off; off = align256(off + (size_t)T * d.D * E);
   L.g = off; off = align256(off + (size_t)T * d.F * E);
+  L.ffn = off; off = align256(off + (size_t)T * d.D * E);
   size_t part = 0;
   const int maxN = std::max(std::max(d.Nqkv, 2 * d.F), d.D);
   if (!d.bf16) {
@@ -510,7 +529,48 @@ extern "C" llama_status llama_block_diag(const llama_block* blk, void* scratch, 
   SLayout L = scratch_layout(blk->cfg, blk->dm, tokens, 1, 1, false);
   if (which == LLAMA_DIAG_ATTN) *ptr = (char*)scratch + L.attn;
   else if (which == LLAMA_DIAG_H) *ptr = (char*)scratch + L.h;
+  else if (which == LLAMA_DIAG_FFN) *ptr = (char*)scratch + L.ffn;
   else return fail(LLAMA_ERR_INVALID_ARG, "unknown diagnostic %d", which);
+  return LLAMA_OK;
+}
+
+extern "C" llama_status llama_block_profile_start(llama_block* blk, int32_t max_calls) {
+  if (!blk || max_calls <= 0) return fail(LLAMA_ERR_INVALID_ARG, "block must be non-NULL and max_calls > 0");
+  const size_t need = (size_t)max_calls * kMaxMarks;
+  while (blk->ev.size() < need) {
+    hipEvent_t e;
+    HIP_TRY(hipEventCreate(&e), "profile_start");
+    blk->ev.push_back(e);
+  }
+  blk->prof_max = max_calls;
+  blk->prof_calls = 0;
+  blk->prof_marks = 0;
+  return LLAMA_OK;
+}
+
+extern "C" llama_status llama_block_profile_read(llama_block* blk, float* ms, int32_t max_phases, int32_t* n_phases,
+                                                 int32_t* n_calls) {
+  if (!blk || !ms || !n_phases || !n_calls) return fail(LLAMA_ERR_INVALID_ARG, "NULL argument");
+  const int np = std::max(0, std::min(blk->prof_marks - 1, (int)max_phases));
+  for (int p = 0; p < np; ++p) ms[p] = 0.f;
+  for (int c = 0; c < blk->prof_calls; ++c) {
+    hipEvent_t* e = &blk->ev[(size_t)c * kMaxMarks];
+    HIP_TRY(hipEventSynchronize(e[blk->prof_marks - 1]), "profile_read");
+    for (int p = 0; p < np; ++p) {
+      float t = 0.f;
+      HIP_TRY(hipEventElapsedTime(&t, e[p], e[p + 1]), "profile_read");
+      ms[p] += t;
+    }
+  }
+  *n_phases = np;
+  *n_calls = blk->prof_calls;
+  blk->prof_max = blk->prof_calls = 0;
+  return LLAMA_OK;
+}
+
+extern "C" llama_status llama_block_set_diag(llama_block* blk, int32_t enable) {
+  if (!blk) return fail(LLAMA_ERR_INVALID_ARG, "block is NULL");
+  blk->diag = enable ? 1 : 0;
   return LLAMA_OK;
 }
 
@@ -547,7 +607,7 @@ static llama_status check_call(const llama_block* blk, const llama_kvcache* c, i
 
 template <typename T>
 static void fp32_path(const llama_block* blk, KVView kv, const void* x, void* y, int B, int L, char* sc,
-                      const SLayout& S, hipStream_t s) {
+                      const SLayout& S, Marker& mk, hipStream_t s) {
   const Dims& d = blk->dm;
   const int M = B * L;
   float* inv1 = (float*)(sc + S.inv1);
@@ -558,20 +618,32 @@ static void fp32_path(const llama_block* blk, KVView kv, const void* x, void* y,
   T* g = (T*)(sc + S.g);
   float* part = (float*)(sc + S.part);
   const float eps = blk->cfg.norm_eps;
+  mk(s);
   launch_rms_inv<T>((const T*)x, M, d.D, eps, inv1, s);
+  mk(s);
   launch_gemm_simt<T>((const T*)x, (const T*)blk->qkv.w, part, M, d.Nqkv, d.D, s);
+  mk(s);
   launch_epi_qkv<T>(part, 1, M, d.Nq, d.Nkv, inv1, L, blk->rope, blk->cfg.rope_traditional, q, kv, s);
+  mk(s);
   launch_attn_simt<T>(q, kv, B, L, d.H, d.G, d.d, attn, s);
+  mk(s);
   launch_gemm_simt<T>(attn, (const T*)blk->o.w, part, M, d.D, d.Nq, s);
-  launch_epi_resid<T>(part, 1, M, d.D, (const T*)x, h, eps, inv2, nullptr, 0, 0, s);
+  mk(s);
+  launch_epi_resid<T>(part, 1, M, d.D, (const T*)x, h, eps, inv2, nullptr, 0, 0, nullptr, s);
+  mk(s);
   launch_gemm_simt<T>(h, (const T*)blk->w13.w, part, M, 2 * d.F, d.D, s);
+  mk(s);
   launch_epi_swiglu<T>(part, 1, M, 2 * d.F, d.IB, inv2, g, s);
+  mk(s);
   launch_gemm_simt<T>(g, (const T*)blk->w2.w, part, M, d.D, d.F, s);
-  launch_epi_resid<T>(part, 1, M, d.D, h, (T*)y, eps, nullptr, kv.lens, L, B, s);
+  mk(s);
+  launch_epi_resid<T>(part, 1, M, d.D, h, (T*)y, eps, nullptr, kv.lens, L, B, blk->diag ? (T*)(sc + S.ffn) : nullptr,
+                      s);
+  mk(s);
 }
 
 static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void* y, int B, int L, char* sc,
-                         const SLayout& S, hipStream_t s) {
+                         const SLayout& S, Marker& mk, hipStream_t s) {
   const Dims& d = blk->dm;
   const int M = B * L;
   float* inv1 = (float*)(sc + S.inv1);
@@ -587,7 +659,9 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
     launch_q4_dequant((const uint32_t*)lin.w, lin.s, lin.b, lin.N, lin.K, 64, gamma, deq, s);
     return deq;
   };
+  mk(s);
   launch_rms_inv<bf16_t>((const bf16_t*)x, M, d.D, eps, inv1, s);
+  mk(s);
   GemmArgs a{};
   a.A = (const bf16_t*)x;
   a.B = weight(blk->qkv, blk->gamma1);
@@ -597,25 +671,32 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
   a.rope = blk->rope; a.traditional = blk->cfg.rope_traditional;
   a.kv = kv;
   launch_gemm_mfma(EPI_QKV, a, s);
+  mk(s);
   launch_attn_prefill_bf16(q, kv, B, L, d.H, d.G, attn, s);
+  mk(s);
   GemmArgs o{};
   o.A = attn; o.B = weight(blk->o, nullptr); o.M = M; o.N = d.D; o.K = d.Nq;
   o.resid = (const bf16_t*)x; o.out = h;
   launch_gemm_mfma(EPI_RESID, o, s);
+  mk(s);
   launch_rms_inv<bf16_t>(h, M, d.D, eps, inv2, s);
+  mk(s);
   GemmArgs f{};
   f.A = h; f.B = weight(blk->w13, blk->gamma2); f.M = M; f.N = 2 * d.F; f.K = d.D;
   f.inv_rms = inv2; f.g_out = g;
   launch_gemm_mfma(EPI_SWIGLU, f, s);
+  mk(s);
   GemmArgs w2{};
   w2.A = g; w2.B = weight(blk->w2, nullptr); w2.M = M; w2.N = d.D; w2.K = d.F;
   w2.resid = h; w2.out = (bf16_t*)y;
   w2.lens_add = kv.lens; w2.lens_inc = L; w2.n_seq = B;
+  w2.branch = blk->diag ? (bf16_t*)(sc + S.ffn) : nullptr;
   launch_gemm_mfma(EPI_RESID, w2, s);
+  mk(s);
 }
 
 static void bf16_decode(const llama_block* blk, KVView kv, const void* x, void* y, int B, char* sc, const SLayout& S,
-                        int n_splits, hipStream_t s) {
+                        int n_splits, Marker& mk, hipStream_t s) {
   const Dims& d = blk->dm;
   float* inv1 = (float*)(sc + S.inv1);
   float* inv2 = (float*)(sc + S.inv2);
@@ -626,22 +707,34 @@ static void bf16_decode(const llama_block* blk, KVView kv, const void* x, void* 
   float* part = (float*)(sc + S.part);
   float* ao = (float*)(sc + S.ao);
   float* aml = (float*)(sc + S.aml);
+  bf16_t* ffn = blk->diag ? (bf16_t*)(sc + S.ffn) : nullptr;
   const float eps = blk->cfg.norm_eps;
+  mk(s);
   launch_rms_inv<bf16_t>((const bf16_t*)x, B, d.D, eps, inv1, s);
+  mk(s);
   if (!d.q4) {
     int ks = gemv_ks(B, d.Nqkv, d.D);
     launch_gemv_bf16((const bf16_t*)x, (const bf16_t*)blk->qkv.w, part, B, d.Nqkv, d.D, ks, s);
+    mk(s);
     launch_epi_qkv<bf16_t>(part, ks, B, d.Nq, d.Nkv, inv1, 1, blk->rope, blk->cfg.rope_traditional, q, kv, s);
+    mk(s);
     launch_attn_decode_bf16(q, kv, B, d.H, d.G, n_splits, kSplitLen, ao, aml, attn, s);
+    mk(s);
     ks = gemv_ks(B, d.D, d.Nq);
     launch_gemv_bf16(attn, (const bf16_t*)blk->o.w, part, B, d.D, d.Nq, ks, s);
-    launch_epi_resid<bf16_t>(part, ks, B, d.D, (const bf16_t*)x, h, eps, inv2, nullptr, 0, 0, s);
+    mk(s);
+    launch_epi_resid<bf16_t>(part, ks, B, d.D, (const bf16_t*)x, h, eps, inv2, nullptr, 0, 0, nullptr, s);
+    mk(s);
     ks = gemv_ks(B, 2 * d.F, d.D);
     launch_gemv_bf16(h, (const bf16_t*)blk->w13.w, part, B, 2 * d.F, d.D, ks, s);
+    mk(s);
     launch_epi_swiglu<bf16_t>(part, ks, B, 2 * d.F, d.IB, inv2, g, s);
+    mk(s);
     ks = gemv_ks(B, d.D, d.F);
     launch_gemv_bf16(g, (const bf16_t*)blk->w2.w, part, B, d.D, d.F, ks, s);
-    launch_epi_resid<bf16_t>(part, ks, B, d.D, h, (bf16_t*)y, eps, nullptr, kv.lens, 1, B, s);
+    mk(s);
+    launch_epi_resid<bf16_t>(part, ks, B, d.D, h, (bf16_t*)y, eps, nullptr, kv.lens, 1, B, ffn, s);
+    mk(s);
   } else {
     _Float16* xh = (_Float16*)(sc + S.xh);
     float* xs = (float*)(sc + S.xsum);
@@ -649,14 +742,23 @@ static void bf16_decode(const llama_block* blk, KVView kv, const void* x, void* 
       launch_gemv_q4(X, inv, gam, (const uint32_t*)lin.w, lin.s, lin.b, part, B, lin.N, lin.K, 64, xh, xs, s);
     };
     gq((const bf16_t*)x, inv1, blk->gamma1, blk->qkv);
+    mk(s);
     launch_epi_qkv<bf16_t>(part, 1, B, d.Nq, d.Nkv, nullptr, 1, blk->rope, blk->cfg.rope_traditional, q, kv, s);
+    mk(s);
     launch_attn_decode_bf16(q, kv, B, d.H, d.G, n_splits, kSplitLen, ao, aml, attn, s);
+    mk(s);
     gq(attn, nullptr, nullptr, blk->o);
-    launch_epi_resid<bf16_t>(part, 1, B, d.D, (const bf16_t*)x, h, eps, inv2, nullptr, 0, 0, s);
+    mk(s);
+    launch_epi_resid<bf16_t>(part, 1, B, d.D, (const bf16_t*)x, h, eps, inv2, nullptr, 0, 0, nullptr, s);
+    mk(s);
     gq(h, inv2, blk->gamma2, blk->w13);
+    mk(s);
     launch_epi_swiglu<bf16_t>(part, 1, B, 2 * d.F, d.IB, nullptr, g, s);
+    mk(s);
     gq(g, nullptr, nullptr, blk->w2);
-    launch_epi_resid<bf16_t>(part, 1, B, d.D, h, (bf16_t*)y, eps, nullptr, kv.lens, 1, B, s);
+    mk(s);
+    launch_epi_resid<bf16_t>(part, 1, B, d.D, h, (bf16_t*)y, eps, nullptr, kv.lens, 1, B, ffn, s);
+    mk(s);
   }
 }
 
@@ -670,13 +772,16 @@ static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const
   KVView kv = kv_view(c, layer);
   char* sc = (char*)scratch;
   const Dims& d = blk->dm;
+  Marker mk;
+  if (blk->prof_calls < blk->prof_max) mk.ev = &blk->ev[(size_t)(blk->prof_calls++) * kMaxMarks];
   if (!d.bf16) {
-    fp32_path<float>(blk, kv, x, y, batch, L, sc, S, s);
+    fp32_path<float>(blk, kv, x, y, batch, L, sc, S, mk, s);
   } else if (!decode) {
-    bf16_prefill(blk, kv, x, y, batch, L, sc, S, s);
+    bf16_prefill(blk, kv, x, y, batch, L, sc, S, mk, s);
   } else {
-    bf16_decode(blk, kv, x, y, batch, sc, S, n_splits_override > 0 ? n_splits_override : S.n_splits, s);
+    bf16_decode(blk, kv, x, y, batch, sc, S, n_splits_override > 0 ? n_splits_override : S.n_splits, mk, s);
   }
+  if (mk.ev) blk->prof_marks = mk.i;
   st = hip_check(decode ? "block decode" : "block prefill");
   if (st != LLAMA_OK) return st;
   for (int b = 0; b < batch; ++b) c->lens_host[(size_t)layer * c->cfg.max_batch + b] += L;

@@ -82,13 +82,15 @@ void launch_epi_qkv(const float* part, int ks, int M, int Nq, int Nkv, const flo
 template <typename T>
 __global__ __launch_bounds__(256) void k_epi_resid(const float* part, int ks, int M, int N, const T* resid,
                                                    T* out, float eps, float* inv_rms_out, int32_t* lens_add,
-                                                   int lens_inc, int n_seq) {
+                                                   int lens_inc, int n_seq, T* branch) {
   int m = blockIdx.x;
   size_t stride = (size_t)M * N;
   float ss = 0.f;
   for (int c = threadIdx.x; c < N; c += 256) {
     size_t idx = (size_t)m * N + c;
-    float v = Elt<T>::round(Elt<T>::load(resid, idx) + sum_parts(part, ks, stride, idx));
+    const float f = sum_parts(part, ks, stride, idx);
+    if (branch) Elt<T>::store(branch, idx, f);
+    float v = Elt<T>::round(Elt<T>::load(resid, idx) + f);
     Elt<T>::store(out, idx, v);
     ss += v * v;
   }
@@ -104,10 +106,10 @@ __global__ __launch_bounds__(256) void k_epi_resid(const float* part, int ks, in
 
 template <typename T>
 void launch_epi_resid(const float* part, int ks, int M, int N, const T* resid, T* out, float eps,
-                      float* inv_rms_out, int32_t* lens_add, int lens_inc, int n_seq, hipStream_t s) {
+                      float* inv_rms_out, int32_t* lens_add, int lens_inc, int n_seq, T* branch, hipStream_t s) {
   if (M <= 0) return;
   hipLaunchKernelGGL(k_epi_resid<T>, dim3(M), dim3(256), 0, s, part, ks, M, N, resid, out, eps, inv_rms_out,
-                     lens_add, lens_inc, n_seq);
+                     lens_add, lens_inc, n_seq, branch);
 }
 
 // ---------------------------------------------------------------------------
@@ -155,7 +157,7 @@ void launch_reduce_f32(const float* part, int ks, int M, int N, float* out, hipS
   template void launch_epi_qkv<T>(const float*, int, int, int, int, const float*, int, const float2*, int, T*, \
                                   KVView, hipStream_t);                                                   \
   template void launch_epi_resid<T>(const float*, int, int, int, const T*, T*, float, float*, int32_t*, int, \
-                                    int, hipStream_t);                                                    \
+                                    int, T*, hipStream_t);                                                \
   template void launch_epi_swiglu<T>(const float*, int, int, int, int, const float*, T*, hipStream_t);
 INST(float)
 INST(bf16_t)

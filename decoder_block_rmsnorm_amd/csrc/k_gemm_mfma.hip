@@ -142,6 +142,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           size_t idx = (size_t)row * N + wcol0 + j * 32 + l32;
+          if (a.branch) a.branch[idx] = f32_to_bf16(acc[i][j][r]);
           a.out[idx] = f32_to_bf16(bf16_to_f32(a.resid[idx]) + acc[i][j][r]);
         }
       } else if constexpr (EPI == EPI_SWIGLU) {

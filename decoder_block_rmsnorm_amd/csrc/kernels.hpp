@@ -67,6 +67,7 @@ struct GemmArgs {
   bf16_t* out;            // [M, N]
   int32_t* lens_add;      // if non-null: lens_add[b] += lens_inc for b < n_seq (block 0)
   int lens_inc, n_seq;
+  bf16_t* branch;         // if non-null: the product before the residual add [M, N]
 };
 void launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t s);
 
@@ -87,7 +88,7 @@ void launch_epi_qkv(const float* part, int ks, int M, int Nq, int Nkv, const flo
                     const float2* rope, int traditional, T* q_out, KVView kv, hipStream_t s);
 template <typename T>
 void launch_epi_resid(const float* part, int ks, int M, int N, const T* resid, T* out, float eps,
-                      float* inv_rms_out, int32_t* lens_add, int lens_inc, int n_seq, hipStream_t s);
+                      float* inv_rms_out, int32_t* lens_add, int lens_inc, int n_seq, T* branch, hipStream_t s);
 template <typename T>
 void launch_epi_swiglu(const float* part, int ks, int M, int F2, int ib, const float* inv_rms, T* g_out,
                        hipStream_t s);

@@ -133,14 +133,34 @@ llama_status llama_block_decode(llama_block* blk, llama_kvcache* cache, int32_t 
                                 void* y, int32_t batch, void* scratch, size_t scratch_bytes,
                                 void* stream);
 
-/* Diagnostics: after a prefill/decode call with the same (batch, seq_len) and
+/* Diagnostics: after a prefill/decode call with the same token count and
  * scratch, points *ptr at a transient of that call inside scratch:
  *   LLAMA_DIAG_ATTN = attention output before wo, act_dtype [tokens, n_heads*head_dim];
- *   LLAMA_DIAG_H    = x + wo o, act_dtype [tokens, dim].
- * (The feed-forward branch is y - h.) Valid until the next call using scratch. */
-enum { LLAMA_DIAG_ATTN = 0, LLAMA_DIAG_H = 1 };
+ *   LLAMA_DIAG_H    = x + wo o, act_dtype [tokens, dim];
+ *   LLAMA_DIAG_FFN  = the feed-forward branch w2(silu(w1 n) * (w3 n)) before the
+ *                     residual add, act_dtype [tokens, dim]; written only while
+ *                     llama_block_set_diag(blk, 1) is in effect (one extra store).
+ * Valid until the next call using scratch. */
+enum { LLAMA_DIAG_ATTN = 0, LLAMA_DIAG_H = 1, LLAMA_DIAG_FFN = 2 };
 llama_status llama_block_diag(const llama_block* blk, void* scratch, int32_t which, int32_t tokens,
                               void** ptr);
+llama_status llama_block_set_diag(llama_block* blk, int32_t enable);
+
+/* Per-phase timing (profiling aid).  profile_start arms HIP events for the next
+ * max_calls prefill/decode calls of this block: each call records an event on its
+ * stream before its first kernel and after each phase.  profile_read waits for
+ * those events, writes the summed milliseconds of each phase over the recorded
+ * calls to phase_ms[0 .. *n_phases) (at most max_phases), the number of calls to
+ * *n_calls, and disarms.  Phases, in launch order:
+ *   bf16 prefill : rms(x), qkv gemm+rope+append, attention, wo gemm+residual,
+ *                  rms(h), w1/w3 gemm+swiglu, w2 gemm+residual            (7)
+ *   decode, fp32 : rms(x), qkv projection, qkv finish, attention, wo projection,
+ *                  residual(+rms), w1/w3 projection, swiglu, w2 projection,
+ *                  residual                                                (10)
+ * Not for calls captured into a graph. */
+llama_status llama_block_profile_start(llama_block* blk, int32_t max_calls);
+llama_status llama_block_profile_read(llama_block* blk, float* phase_ms, int32_t max_phases, int32_t* n_phases,
+                                      int32_t* n_calls);
 
 /* ------------------------------------------------------------------ cache */
 

@@ -254,3 +254,39 @@ def draw_block_workload(w: Workload, seed: Optional[int] = None) -> Dict[str, ob
         out["k_cache"], out["v_cache"] = draw_decode_caches(w, rng)
     out["weights"] = draw_block_weights(w.shape, rng)
     return out
+
+
+# --------------------------------------------------------------------------
+# algorithmic work (measurement bookkeeping)
+# --------------------------------------------------------------------------
+def prefill_flops(s: BlockShape, batch: int, seq_len: int, cached: int = 0) -> float:
+    """2 * tokens * linear params + causal attention: 4 * H * d per (query, key <= query) pair."""
+    T = batch * seq_len
+    pairs = batch * (seq_len * cached + seq_len * (seq_len + 1) // 2)
+    return 2.0 * T * s.linear_params + 4.0 * s.n_heads * s.head_dim * pairs
+
+
+def linear_flops(s: BlockShape, tokens: int) -> dict:
+    d, hd = s.dim, s.head_dim
+    return {"qkv": 2.0 * tokens * d * (s.n_heads + 2 * s.n_kv_heads) * hd,
+            "wo": 2.0 * tokens * s.n_heads * hd * d,
+            "w13": 2.0 * tokens * d * 2 * s.ffn_dim,
+            "w2": 2.0 * tokens * s.ffn_dim * d}
+
+
+def weight_bytes(s: BlockShape) -> float:
+    if s.weight_format == "q4":
+        return s.linear_params * (0.5 + 2 * 2 / s.group_size)
+    return s.linear_params * (4 if s.dtype == "f32" else 2)
+
+
+def decode_bytes(s: BlockShape, batch: int, cached: int) -> dict:
+    """One decode step: every weight byte once, every cached K/V byte once (keys 0..cached),
+    the new K/V rows written, block input read and output written."""
+    e = 4 if s.dtype == "f32" else 2
+    kv_read = batch * (cached + 1) * s.n_kv_heads * s.head_dim * 2 * e
+    kv_write = batch * s.n_kv_heads * s.head_dim * 2 * e
+    act = batch * s.dim * 2 * e
+    w = weight_bytes(s)
+    return {"weights": w, "kv_read": kv_read, "kv_write": kv_write, "act": act,
+            "total": w + kv_read + kv_write + act}
