@@ -27,8 +27,8 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PREFILL_PHASES = ["rms_x", "qkv_gemm_rope_append", "attention_prefill", "wo_gemm_residual", "rms_h",
                   "w13_gemm_swiglu", "w2_gemm_residual"]
-DECODE_PHASES = ["rms_x", "qkv_gemv", "qkv_finish_rope_append", "attention_decode", "wo_gemv", "wo_residual_rms",
-                 "w13_gemv", "swiglu", "w2_gemv", "w2_residual"]
+DECODE_PHASES = ["qkv_gemv_and_x_stats", "qkv_finish_rope_append", "attention_decode", "wo_gemv",
+                 "wo_residual_h_stats", "w13_gemv", "swiglu", "w2_gemv", "w2_residual"]
 
 
 def log(*a):
@@ -128,10 +128,10 @@ def bench_decode(wl, steps, warmup):
     ms = sum(times) / steps
     tot_bytes = sum(b["total"] for b in byts) / steps
     kv_bytes = sum(b["kv_read"] + b["kv_write"] for b in byts) / steps
-    attn_us = ph_ms[3] / ncalls * 1e3
+    attn_us = ph_ms[2] / ncalls * 1e3
     phases = {n: {"avg_us": round(v / ncalls * 1e3, 2)} for n, v in zip(DECODE_PHASES, ph_ms)}
-    w_phase = {"qkv_gemv": 1, "wo_gemv": 4, "w13_gemv": 6, "w2_gemv": 8}
-    lb = {"qkv_gemv": s.dim * (s.n_heads + 2 * s.n_kv_heads) * s.head_dim,
+    w_phase = {"qkv_gemv_and_x_stats": 0, "wo_gemv": 3, "w13_gemv": 5, "w2_gemv": 7}
+    lb = {"qkv_gemv_and_x_stats": s.dim * (s.n_heads + 2 * s.n_kv_heads) * s.head_dim,
           "wo_gemv": s.n_heads * s.head_dim * s.dim, "w13_gemv": 2 * s.dim * s.ffn_dim, "w2_gemv": s.ffn_dim * s.dim}
     esz = 2 if s.dtype == "bf16" else 4
     for n, i in w_phase.items():

@@ -254,9 +254,9 @@ class Block:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h:
-            llama_block_destroy(h)
-            self.handle = None
+        if h and _abi is not None and _abi._lib is not None:
+            _abi._lib.llama_block_destroy(h)
+        self.handle = None
 
 
 class KVCache:
@@ -289,9 +289,9 @@ class KVCache:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h:
-            llama_kvcache_destroy(h)
-            self.handle = None
+        if h and _abi is not None and _abi._lib is not None:
+            _abi._lib.llama_kvcache_destroy(h)
+        self.handle = None
 
 
 class Stack:
@@ -314,6 +314,6 @@ class Stack:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h:
-            llama_stack_destroy(h)
-            self.handle = None
+        if h and _abi is not None and _abi._lib is not None:
+            _abi._lib.llama_stack_destroy(h)
+        self.handle = None

@@ -463,8 +463,8 @@ static int gemv_ks(int M, int N, int K) {
 }
 
 struct SLayout {
-  size_t inv1, inv2, q, attn, h, g, ffn, part, ao, aml, xh, xsum, deq, total;
-  int n_splits;
+  size_t inv1, inv2, ssx, ssh, q, attn, h, g, ffn, part, ao, aml, xh, xsum, deq, total;
+  int n_splits, ks_qkv, nb_h;
 };
 
 // T = rows of this call (batch * seq_len), B = batch, decode = one-token call.
@@ -474,6 +474,12 @@ static SLayout scratch_layout(const llama_block_config& c, const Dims& d, int T,
   size_t off = 0;
   L.inv1 = off; off = align256(off + (size_t)T * 4);
   L.inv2 = off; off = align256(off + (size_t)T * 4);
+  // partial row statistics: of x per K slice of the decode QKV projection, of h
+  // per 256-column block of the residual epilogue
+  L.ks_qkv = gemv_ks(T, d.Nqkv, d.D);
+  L.nb_h = (d.D + 255) / 256;
+  L.ssx = off; off = align256(off + (size_t)L.ks_qkv * T * 4);
+  L.ssh = off; off = align256(off + (size_t)L.nb_h * T * 4);
   L.q = off; off = align256(off + (size_t)T * d.Nq * E);
   L.attn = off; off = align256(off + (size_t)T * d.Nq * E);
   L.h = off; off = align256(off + (size_t)T * d.D * E);
@@ -611,7 +617,6 @@ static void fp32_path(const llama_block* blk, KVView kv, const void* x, void* y,
   const Dims& d = blk->dm;
   const int M = B * L;
   float* inv1 = (float*)(sc + S.inv1);
-  float* inv2 = (float*)(sc + S.inv2);
   T* q = (T*)(sc + S.q);
   T* attn = (T*)(sc + S.attn);
   T* h = (T*)(sc + S.h);
@@ -623,22 +628,26 @@ static void fp32_path(const llama_block* blk, KVView kv, const void* x, void* y,
   mk(s);
   launch_gemm_simt<T>((const T*)x, (const T*)blk->qkv.w, part, M, d.Nqkv, d.D, s);
   mk(s);
-  launch_epi_qkv<T>(part, 1, M, d.Nq, d.Nkv, inv1, L, blk->rope, blk->cfg.rope_traditional, q, kv, s);
+  RowStat st1;
+  st1.inv = inv1;
+  launch_epi_qkv<T>(part, 1, M, d.Nq, d.Nkv, st1, L, blk->rope, blk->cfg.rope_traditional, q, kv, s);
   mk(s);
   launch_attn_simt<T>(q, kv, B, L, d.H, d.G, d.d, attn, s);
   mk(s);
   launch_gemm_simt<T>(attn, (const T*)blk->o.w, part, M, d.D, d.Nq, s);
   mk(s);
-  launch_epi_resid<T>(part, 1, M, d.D, (const T*)x, h, eps, inv2, nullptr, 0, 0, nullptr, s);
+  float* ssh = (float*)(sc + S.ssh);
+  launch_epi_resid<T>(part, 1, M, d.D, (const T*)x, h, ssh, nullptr, 0, 0, nullptr, s);
   mk(s);
   launch_gemm_simt<T>(h, (const T*)blk->w13.w, part, M, 2 * d.F, d.D, s);
   mk(s);
-  launch_epi_swiglu<T>(part, 1, M, 2 * d.F, d.IB, inv2, g, s);
+  RowStat st2;
+  st2.ss = ssh; st2.nb = S.nb_h; st2.M = M; st2.n = d.D; st2.eps = eps;
+  launch_epi_swiglu<T>(part, 1, M, 2 * d.F, d.IB, st2, g, s);
   mk(s);
   launch_gemm_simt<T>(g, (const T*)blk->w2.w, part, M, d.D, d.F, s);
   mk(s);
-  launch_epi_resid<T>(part, 1, M, d.D, h, (T*)y, eps, nullptr, kv.lens, L, B, blk->diag ? (T*)(sc + S.ffn) : nullptr,
-                      s);
+  launch_epi_resid<T>(part, 1, M, d.D, h, (T*)y, nullptr, kv.lens, L, B, blk->diag ? (T*)(sc + S.ffn) : nullptr, s);
   mk(s);
 }
 
@@ -652,12 +661,14 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
   bf16_t* attn = (bf16_t*)(sc + S.attn);
   bf16_t* h = (bf16_t*)(sc + S.h);
   bf16_t* g = (bf16_t*)(sc + S.g);
-  bf16_t* deq = (bf16_t*)(sc + S.deq);
+  _Float16* deq = (_Float16*)(sc + S.deq);
   const float eps = blk->cfg.norm_eps;
+  // 4-bit weights: dequantized (gamma folded) to fp16 right before their GEMM,
+  // which then runs on fp16 MFMA
   auto weight = [&](const Lin& lin, const float* gamma) -> const bf16_t* {
     if (!d.q4) return (const bf16_t*)lin.w;
     launch_q4_dequant((const uint32_t*)lin.w, lin.s, lin.b, lin.N, lin.K, 64, gamma, deq, s);
-    return deq;
+    return (const bf16_t*)deq;
   };
   mk(s);
   launch_rms_inv<bf16_t>((const bf16_t*)x, M, d.D, eps, inv1, s);
@@ -665,7 +676,7 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
   GemmArgs a{};
   a.A = (const bf16_t*)x;
   a.B = weight(blk->qkv, blk->gamma1);
-  a.M = M; a.N = d.Nqkv; a.K = d.D;
+  a.M = M; a.N = d.Nqkv; a.K = d.D; a.b_f16 = d.q4;
   a.inv_rms = inv1;
   a.q_out = q; a.Nq = d.Nq; a.Nkv = d.Nkv; a.L = L;
   a.rope = blk->rope; a.traditional = blk->cfg.rope_traditional;
@@ -675,19 +686,19 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
   launch_attn_prefill_bf16(q, kv, B, L, d.H, d.G, attn, s);
   mk(s);
   GemmArgs o{};
-  o.A = attn; o.B = weight(blk->o, nullptr); o.M = M; o.N = d.D; o.K = d.Nq;
+  o.A = attn; o.B = weight(blk->o, nullptr); o.M = M; o.N = d.D; o.K = d.Nq; o.b_f16 = d.q4;
   o.resid = (const bf16_t*)x; o.out = h;
   launch_gemm_mfma(EPI_RESID, o, s);
   mk(s);
   launch_rms_inv<bf16_t>(h, M, d.D, eps, inv2, s);
   mk(s);
   GemmArgs f{};
-  f.A = h; f.B = weight(blk->w13, blk->gamma2); f.M = M; f.N = 2 * d.F; f.K = d.D;
+  f.A = h; f.B = weight(blk->w13, blk->gamma2); f.M = M; f.N = 2 * d.F; f.K = d.D; f.b_f16 = d.q4;
   f.inv_rms = inv2; f.g_out = g;
   launch_gemm_mfma(EPI_SWIGLU, f, s);
   mk(s);
   GemmArgs w2{};
-  w2.A = g; w2.B = weight(blk->w2, nullptr); w2.M = M; w2.N = d.D; w2.K = d.F;
+  w2.A = g; w2.B = weight(blk->w2, nullptr); w2.M = M; w2.N = d.D; w2.K = d.F; w2.b_f16 = d.q4;
   w2.resid = h; w2.out = (bf16_t*)y;
   w2.lens_add = kv.lens; w2.lens_inc = L; w2.n_seq = B;
   w2.branch = blk->diag ? (bf16_t*)(sc + S.ffn) : nullptr;
@@ -698,8 +709,6 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
 static void bf16_decode(const llama_block* blk, KVView kv, const void* x, void* y, int B, char* sc, const SLayout& S,
                         int n_splits, Marker& mk, hipStream_t s) {
   const Dims& d = blk->dm;
-  float* inv1 = (float*)(sc + S.inv1);
-  float* inv2 = (float*)(sc + S.inv2);
   bf16_t* q = (bf16_t*)(sc + S.q);
   bf16_t* attn = (bf16_t*)(sc + S.attn);
   bf16_t* h = (bf16_t*)(sc + S.h);
@@ -707,57 +716,64 @@ static void bf16_decode(const llama_block* blk, KVView kv, const void* x, void* 
   float* part = (float*)(sc + S.part);
   float* ao = (float*)(sc + S.ao);
   float* aml = (float*)(sc + S.aml);
+  float* ssx = (float*)(sc + S.ssx);
+  float* ssh = (float*)(sc + S.ssh);
   bf16_t* ffn = blk->diag ? (bf16_t*)(sc + S.ffn) : nullptr;
   const float eps = blk->cfg.norm_eps;
-  mk(s);
-  launch_rms_inv<bf16_t>((const bf16_t*)x, B, d.D, eps, inv1, s);
+  RowStat none;
+  RowStat sth;  // statistic of h from the wo residual epilogue
+  sth.ss = ssh; sth.nb = S.nb_h; sth.M = B; sth.n = d.D; sth.eps = eps;
   mk(s);
   if (!d.q4) {
+    // the QKV projection also emits sum(x^2) per K slice: attention_norm's statistic
     int ks = gemv_ks(B, d.Nqkv, d.D);
-    launch_gemv_bf16((const bf16_t*)x, (const bf16_t*)blk->qkv.w, part, B, d.Nqkv, d.D, ks, s);
+    launch_gemv_bf16((const bf16_t*)x, (const bf16_t*)blk->qkv.w, part, B, d.Nqkv, d.D, ks, ssx, s);
     mk(s);
-    launch_epi_qkv<bf16_t>(part, ks, B, d.Nq, d.Nkv, inv1, 1, blk->rope, blk->cfg.rope_traditional, q, kv, s);
+    RowStat stx;
+    stx.ss = ssx; stx.nb = ks; stx.M = B; stx.n = d.D; stx.eps = eps;
+    launch_epi_qkv<bf16_t>(part, ks, B, d.Nq, d.Nkv, stx, 1, blk->rope, blk->cfg.rope_traditional, q, kv, s);
     mk(s);
     launch_attn_decode_bf16(q, kv, B, d.H, d.G, n_splits, kSplitLen, ao, aml, attn, s);
     mk(s);
     ks = gemv_ks(B, d.D, d.Nq);
-    launch_gemv_bf16(attn, (const bf16_t*)blk->o.w, part, B, d.D, d.Nq, ks, s);
+    launch_gemv_bf16(attn, (const bf16_t*)blk->o.w, part, B, d.D, d.Nq, ks, nullptr, s);
     mk(s);
-    launch_epi_resid<bf16_t>(part, ks, B, d.D, (const bf16_t*)x, h, eps, inv2, nullptr, 0, 0, nullptr, s);
+    launch_epi_resid<bf16_t>(part, ks, B, d.D, (const bf16_t*)x, h, ssh, nullptr, 0, 0, nullptr, s);
     mk(s);
     ks = gemv_ks(B, 2 * d.F, d.D);
-    launch_gemv_bf16(h, (const bf16_t*)blk->w13.w, part, B, 2 * d.F, d.D, ks, s);
+    launch_gemv_bf16(h, (const bf16_t*)blk->w13.w, part, B, 2 * d.F, d.D, ks, nullptr, s);
     mk(s);
-    launch_epi_swiglu<bf16_t>(part, ks, B, 2 * d.F, d.IB, inv2, g, s);
+    launch_epi_swiglu<bf16_t>(part, ks, B, 2 * d.F, d.IB, sth, g, s);
     mk(s);
     ks = gemv_ks(B, d.D, d.F);
-    launch_gemv_bf16(g, (const bf16_t*)blk->w2.w, part, B, d.D, d.F, ks, s);
+    launch_gemv_bf16(g, (const bf16_t*)blk->w2.w, part, B, d.D, d.F, ks, nullptr, s);
     mk(s);
-    launch_epi_resid<bf16_t>(part, ks, B, d.D, h, (bf16_t*)y, eps, nullptr, kv.lens, 1, B, ffn, s);
+    launch_epi_resid<bf16_t>(part, ks, B, d.D, h, (bf16_t*)y, nullptr, kv.lens, 1, B, ffn, s);
     mk(s);
   } else {
     _Float16* xh = (_Float16*)(sc + S.xh);
     float* xs = (float*)(sc + S.xsum);
-    auto gq = [&](const bf16_t* X, const float* inv, const float* gam, const Lin& lin) {
-      launch_gemv_q4(X, inv, gam, (const uint32_t*)lin.w, lin.s, lin.b, part, B, lin.N, lin.K, 64, xh, xs, s);
+    auto gq = [&](const bf16_t* X, int norm, RowStat st, const float* gam, const Lin& lin) {
+      launch_gemv_q4(X, norm, st, eps, gam, (const uint32_t*)lin.w, lin.s, lin.b, part, B, lin.N, lin.K, 64, xh, xs,
+                     s);
     };
-    gq((const bf16_t*)x, inv1, blk->gamma1, blk->qkv);
+    gq((const bf16_t*)x, 1, none, blk->gamma1, blk->qkv);
     mk(s);
-    launch_epi_qkv<bf16_t>(part, 1, B, d.Nq, d.Nkv, nullptr, 1, blk->rope, blk->cfg.rope_traditional, q, kv, s);
+    launch_epi_qkv<bf16_t>(part, 1, B, d.Nq, d.Nkv, none, 1, blk->rope, blk->cfg.rope_traditional, q, kv, s);
     mk(s);
     launch_attn_decode_bf16(q, kv, B, d.H, d.G, n_splits, kSplitLen, ao, aml, attn, s);
     mk(s);
-    gq(attn, nullptr, nullptr, blk->o);
+    gq(attn, 0, none, nullptr, blk->o);
     mk(s);
-    launch_epi_resid<bf16_t>(part, 1, B, d.D, (const bf16_t*)x, h, eps, inv2, nullptr, 0, 0, nullptr, s);
+    launch_epi_resid<bf16_t>(part, 1, B, d.D, (const bf16_t*)x, h, ssh, nullptr, 0, 0, nullptr, s);
     mk(s);
-    gq(h, inv2, blk->gamma2, blk->w13);
+    gq(h, 2, sth, blk->gamma2, blk->w13);
     mk(s);
-    launch_epi_swiglu<bf16_t>(part, 1, B, 2 * d.F, d.IB, nullptr, g, s);
+    launch_epi_swiglu<bf16_t>(part, 1, B, 2 * d.F, d.IB, none, g, s);
     mk(s);
-    gq(g, nullptr, nullptr, blk->w2);
+    gq(g, 0, none, nullptr, blk->w2);
     mk(s);
-    launch_epi_resid<bf16_t>(part, 1, B, d.D, h, (bf16_t*)y, eps, nullptr, kv.lens, 1, B, ffn, s);
+    launch_epi_resid<bf16_t>(part, 1, B, d.D, h, (bf16_t*)y, nullptr, kv.lens, 1, B, ffn, s);
     mk(s);
   }
 }
@@ -854,18 +870,16 @@ static llama_status head_enqueue(const llama_linear* head, int wf, int gs, int d
   char* sc = (char*)scratch;
   float* out = logits ? logits : (float*)(sc + L.logits);
   if (wf == LLAMA_W_Q4) {
-    float* inv = (float*)(sc + L.inv);
     float* gam = (float*)(sc + L.gam);
-    launch_rms_inv<bf16_t>((const bf16_t*)x, B, D, eps, inv, s);
     launch_to_f32<bf16_t>((const bf16_t*)fnorm, gam, D, s);
-    launch_gemv_q4((const bf16_t*)x, inv, gam, (const uint32_t*)head->w, (const bf16_t*)head->scales,
+    launch_gemv_q4((const bf16_t*)x, 1, RowStat(), eps, gam, (const uint32_t*)head->w, (const bf16_t*)head->scales,
                    (const bf16_t*)head->biases, out, B, V, D, gs, (_Float16*)(sc + L.xh), (float*)(sc + L.xsum), s);
   } else if (dt == LLAMA_F32) {
     launch_rmsnorm_apply<float>((const float*)x, (const float*)fnorm, B, D, eps, (float*)(sc + L.xn), s);
     launch_gemm_simt<float>((const float*)(sc + L.xn), (const float*)head->w, out, B, V, D, s);
   } else {
     launch_rmsnorm_apply<bf16_t>((const bf16_t*)x, (const bf16_t*)fnorm, B, D, eps, (bf16_t*)(sc + L.xn), s);
-    launch_gemv_bf16((const bf16_t*)(sc + L.xn), (const bf16_t*)head->w, out, B, V, D, 1, s);
+    launch_gemv_bf16((const bf16_t*)(sc + L.xn), (const bf16_t*)head->w, out, B, V, D, 1, nullptr, s);
   }
   launch_argmax(out, B, V, ids, s);
   return hip_check("lm_head_argmax");

@@ -2,7 +2,8 @@
 // Each sums the fp32 partials [ks][M][N] in a fixed order (deterministic, no
 // atomics) and applies what follows the projection in the block:
 //   qkv   : RMSNorm row scale, RoPE on q and k, cache append of k and v;
-//   resid : residual add (+ the next RMSNorm's statistics, + cache-length bump);
+//   resid : residual add (+ the next RMSNorm's partial statistics, + the
+//           feed-forward branch diagnostic, + the cache-length bump);
 //   swiglu: RMSNorm row scale, silu(gate) * up.
 #include "kernels.hpp"
 
@@ -23,9 +24,8 @@ __device__ inline float sum_parts(const float* part, int ks, size_t stride, size
 // tokens already cached ("2. 注意力机制" KV-cache fragment, MLX page).
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(64) void k_epi_qkv(const float* part, int ks, int M, int Nq, int Nkv,
-                                                const float* inv_rms, int L, const float2* rope,
-                                                int traditional, T* q_out, KVView kv) {
+__global__ __launch_bounds__(64) void k_epi_qkv(const float* part, int ks, int M, int Nq, int Nkv, RowStat stat,
+                                                int L, const float2* rope, int traditional, T* q_out, KVView kv) {
   int m = blockIdx.x;
   int head = blockIdx.y;          // 0..H-1 q, H..H+G-1 k, then v
   int d = kv.d, half = d >> 1;
@@ -34,7 +34,7 @@ __global__ __launch_bounds__(64) void k_epi_qkv(const float* part, int ks, int M
   int N = Nq + 2 * Nkv;
   size_t stride = (size_t)M * N;
   int c0 = head * d;
-  float r = inv_rms ? inv_rms[m] : 1.0f;
+  float r = stat.get(m);
   float a = sum_parts(part, ks, stride, (size_t)m * N + c0 + i) * r;
   float b = sum_parts(part, ks, stride, (size_t)m * N + c0 + i + half) * r;
   int bseq = m / L, l = m % L;
@@ -66,50 +66,53 @@ __global__ __launch_bounds__(64) void k_epi_qkv(const float* part, int ks, int M
 }
 
 template <typename T>
-void launch_epi_qkv(const float* part, int ks, int M, int Nq, int Nkv, const float* inv_rms, int L,
-                    const float2* rope, int traditional, T* q_out, KVView kv, hipStream_t s) {
+void launch_epi_qkv(const float* part, int ks, int M, int Nq, int Nkv, RowStat stat, int L, const float2* rope,
+                    int traditional, T* q_out, KVView kv, hipStream_t s) {
   if (M <= 0) return;
   dim3 grid(M, (Nq + 2 * Nkv) / kv.d);
-  hipLaunchKernelGGL(k_epi_qkv<T>, grid, dim3(64), 0, s, part, ks, M, Nq, Nkv, inv_rms, L, rope, traditional,
-                     q_out, kv);
+  hipLaunchKernelGGL(k_epi_qkv<T>, grid, dim3(64), 0, s, part, ks, M, Nq, Nkv, stat, L, rope, traditional, q_out,
+                     kv);
 }
 
 // ---------------------------------------------------------------------------
 // Residual add: out = resid + sum(partials) (LLaMABlock, page 二; "数据流动"),
-// rounded to the storage type; optionally the RMSNorm statistics of the stored
-// row for the next projection, and the cache-length bump after the block.
+// rounded to the storage type.  One thread per column, blocks over (256-column
+// chunk, row); optionally each block's sum of squares of the stored values (the
+// next RMSNorm's statistic, reduced by its consumer), the feed-forward branch
+// itself, and the cache-length bump after the block.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void k_epi_resid(const float* part, int ks, int M, int N, const T* resid,
-                                                   T* out, float eps, float* inv_rms_out, int32_t* lens_add,
-                                                   int lens_inc, int n_seq, T* branch) {
-  int m = blockIdx.x;
-  size_t stride = (size_t)M * N;
-  float ss = 0.f;
-  for (int c = threadIdx.x; c < N; c += 256) {
-    size_t idx = (size_t)m * N + c;
+__global__ __launch_bounds__(256) void k_epi_resid(const float* part, int ks, int M, int N, const T* resid, T* out,
+                                                   float* ss_out, int32_t* lens_add, int lens_inc, int n_seq,
+                                                   T* branch) {
+  const int m = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const size_t stride = (size_t)M * N;
+  float v = 0.f;
+  if (c < N) {
+    const size_t idx = (size_t)m * N + c;
     const float f = sum_parts(part, ks, stride, idx);
     if (branch) Elt<T>::store(branch, idx, f);
-    float v = Elt<T>::round(Elt<T>::load(resid, idx) + f);
+    v = Elt<T>::round(Elt<T>::load(resid, idx) + f);
     Elt<T>::store(out, idx, v);
-    ss += v * v;
   }
-  if (inv_rms_out) {
+  if (ss_out) {
     __shared__ float red[4];
-    ss = warp_sum(ss);
+    const float ss = warp_sum(v * v);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
-    if (threadIdx.x == 0) inv_rms_out[m] = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)N + eps);
+    if (threadIdx.x == 0) ss_out[(size_t)blockIdx.x * M + m] = (red[0] + red[1]) + (red[2] + red[3]);
   }
-  if (lens_add && m == 0 && threadIdx.x < n_seq) lens_add[threadIdx.x] += lens_inc;
+  if (lens_add && m == 0 && blockIdx.x == 0 && threadIdx.x < n_seq) lens_add[threadIdx.x] += lens_inc;
 }
 
 template <typename T>
-void launch_epi_resid(const float* part, int ks, int M, int N, const T* resid, T* out, float eps,
-                      float* inv_rms_out, int32_t* lens_add, int lens_inc, int n_seq, T* branch, hipStream_t s) {
+void launch_epi_resid(const float* part, int ks, int M, int N, const T* resid, T* out, float* ss_out,
+                      int32_t* lens_add, int lens_inc, int n_seq, T* branch, hipStream_t s) {
   if (M <= 0) return;
-  hipLaunchKernelGGL(k_epi_resid<T>, dim3(M), dim3(256), 0, s, part, ks, M, N, resid, out, eps, inv_rms_out,
-                     lens_add, lens_inc, n_seq, branch);
+  dim3 grid((N + 255) / 256, M);
+  hipLaunchKernelGGL(k_epi_resid<T>, grid, dim3(256), 0, s, part, ks, M, N, resid, out, ss_out, lens_add,
+                     lens_inc, n_seq, branch);
 }
 
 // ---------------------------------------------------------------------------
@@ -118,8 +121,8 @@ void launch_epi_resid(const float* part, int ks, int M, int N, const T* resid, T
 // j*ib .. j*ib+ib-1, block 2j+1 the same w3 rows.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void k_epi_swiglu(const float* part, int ks, int M, int F2, int ib,
-                                                    const float* inv_rms, T* g_out) {
+__global__ __launch_bounds__(256) void k_epi_swiglu(const float* part, int ks, int M, int F2, int ib, RowStat stat,
+                                                    T* g_out) {
   int m = blockIdx.y;
   int F = F2 >> 1;
   int j = blockIdx.x * 256 + threadIdx.x;
@@ -127,18 +130,17 @@ __global__ __launch_bounds__(256) void k_epi_swiglu(const float* part, int ks, i
   size_t stride = (size_t)M * F2;
   int jb = j / ib, w = j % ib;
   int cg = jb * 2 * ib + w;
-  float r = inv_rms ? inv_rms[m] : 1.0f;
+  float r = stat.get(m);
   float a = sum_parts(part, ks, stride, (size_t)m * F2 + cg) * r;
   float b = sum_parts(part, ks, stride, (size_t)m * F2 + cg + ib) * r;
   Elt<T>::store(g_out, (size_t)m * F + j, silu_f(a) * b);
 }
 
 template <typename T>
-void launch_epi_swiglu(const float* part, int ks, int M, int F2, int ib, const float* inv_rms, T* g_out,
-                       hipStream_t s) {
+void launch_epi_swiglu(const float* part, int ks, int M, int F2, int ib, RowStat stat, T* g_out, hipStream_t s) {
   if (M <= 0) return;
   dim3 grid((F2 / 2 + 255) / 256, M);
-  hipLaunchKernelGGL(k_epi_swiglu<T>, grid, dim3(256), 0, s, part, ks, M, F2, ib, inv_rms, g_out);
+  hipLaunchKernelGGL(k_epi_swiglu<T>, grid, dim3(256), 0, s, part, ks, M, F2, ib, stat, g_out);
 }
 
 __global__ __launch_bounds__(256) void k_reduce_f32(const float* part, int ks, int M, int N, float* out) {
@@ -153,12 +155,12 @@ void launch_reduce_f32(const float* part, int ks, int M, int N, float* out, hipS
   hipLaunchKernelGGL(k_reduce_f32, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, ks, M, N, out);
 }
 
-#define INST(T)                                                                                           \
-  template void launch_epi_qkv<T>(const float*, int, int, int, int, const float*, int, const float2*, int, T*, \
-                                  KVView, hipStream_t);                                                   \
-  template void launch_epi_resid<T>(const float*, int, int, int, const T*, T*, float, float*, int32_t*, int, \
-                                    int, T*, hipStream_t);                                                \
-  template void launch_epi_swiglu<T>(const float*, int, int, int, int, const float*, T*, hipStream_t);
+#define INST(T)                                                                                                 \
+  template void launch_epi_qkv<T>(const float*, int, int, int, int, RowStat, int, const float2*, int, T*, KVView, \
+                                  hipStream_t);                                                                 \
+  template void launch_epi_resid<T>(const float*, int, int, int, const T*, T*, float*, int32_t*, int, int, T*,    \
+                                    hipStream_t);                                                               \
+  template void launch_epi_swiglu<T>(const float*, int, int, int, int, RowStat, T*, hipStream_t);
 INST(float)
 INST(bf16_t)
 #undef INST

@@ -16,6 +16,8 @@
 // one barrier per K step.  Blocks are renumbered XCD-major and walked in
 // GROUP_M-row bands so that co-resident blocks of one XCD share A and B tiles
 // in that XCD's L2.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace lb {
@@ -26,13 +28,46 @@ constexpr int LDS_ST = BK + 8;  // bf16 per LDS row
 constexpr int GROUP_M = 8;
 }  // namespace gm
 
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E), so that
+// accumulator registers are always indexed by constants (a runtime index would
+// push the accumulator array to scratch memory).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 __device__ inline bf16x8 u4_as_bf16x8(uint4 v) {
   bf16x8 r;
   __builtin_memcpy(&r, &v, 16);
   return r;
 }
 
-template <int BM, int BN, int EPI>
+// F16: B holds fp16 values (4-bit weights dequantized to fp16); A (bf16) is
+// converted to fp16 on its way into LDS and the MFMA runs on fp16 operands.
+__device__ inline uint4 bf16x8_to_f16x8(uint4 v) {
+  uint32_t in[4] = {v.x, v.y, v.z, v.w}, out[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const _Float16 lo = (_Float16)bf16_to_f32((bf16_t)(in[j] & 0xffffu));
+    const _Float16 hi = (_Float16)bf16_to_f32((bf16_t)(in[j] >> 16));
+    uint16_t l, h;
+    __builtin_memcpy(&l, &lo, 2);
+    __builtin_memcpy(&h, &hi, 2);
+    out[j] = (uint32_t)l | ((uint32_t)h << 16);
+  }
+  return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+__device__ inline f16x8 u4_as_f16x8(uint4 v) {
+  f16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+template <int BM, int BN, int EPI, bool F16>
 __global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmArgs a) {
   using namespace gm;
   constexpr int WN = BN / 128;
@@ -87,7 +122,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       int c = tid + 256 * i;
-      st16(As(buf) + (c >> 3) * LDS_ST + (c & 7) * 8, ra[i]);
+      st16(As(buf) + (c >> 3) * LDS_ST + (c & 7) * 8, F16 ? bf16x8_to_f16x8(ra[i]) : ra[i]);
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
@@ -113,22 +148,129 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmArgs a) {
     const bf16_t* bs = Bs(buf) + (wn * 128 + l32) * LDS_ST + hg * 8;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[MI], bfr[4];
+      uint4 af[MI], bfr[4];
 #pragma unroll
-      for (int i = 0; i < MI; ++i) af[i] = u4_as_bf16x8(ld16(as + i * 32 * LDS_ST + kk * 16));
+      for (int i = 0; i < MI; ++i) af[i] = ld16(as + i * 32 * LDS_ST + kk * 16);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = u4_as_bf16x8(ld16(bs + j * 32 * LDS_ST + kk * 16));
+      for (int j = 0; j < 4; ++j) bfr[j] = ld16(bs + j * 32 * LDS_ST + kk * 16);
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (F16)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(u4_as_f16x8(af[i]), u4_as_f16x8(bfr[j]), acc[i][j],
+                                                               0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_as_bf16x8(af[i]), u4_as_bf16x8(bfr[j]),
+                                                                acc[i][j], 0, 0, 0);
+        }
     }
   }
 
   // ---------------- epilogue: lane holds column l32 of each 32x32 subtile,
   // rows 8*(r/4) + 4*hg + r%4 for register r.
   const int wcol0 = n0 + wn * 128;  // first column of this wavefront (head aligned)
+  if constexpr (EPI == EPI_QKV) {
+    // Per-row cache metadata once per block, into the (now free) LDS: position,
+    // and the element offset of the row's page.
+    __syncthreads();
+    int* s_pos = reinterpret_cast<int*>(lds);
+    long long* s_page = reinterpret_cast<long long*>(lds + 4 * BM);  // 8-byte aligned
+    for (int r = tid; r < BM; r += 256) {
+      const int row = m0 + r;
+      if (row < M) {
+        const int bseq = row / a.L;
+        const int pos = a.kv.lens[bseq] + (row - bseq * a.L);
+        s_pos[r] = pos;
+        s_page[r] = (long long)a.kv.page_base(bseq, pos);
+      }
+    }
+    __syncthreads();
+    const bool is_q = wcol0 < a.Nq;
+    const bool is_k = !is_q && wcol0 < a.Nq + a.Nkv;
+    const int ps = a.kv.ps;
+    const int g = is_q ? 0 : (is_k ? (wcol0 - a.Nq) >> 7 : (wcol0 - a.Nq - a.Nkv) >> 7);
+    static_for<0, MI>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      static_for<0, 4>([&](auto r4c) {
+        constexpr int r4 = decltype(r4c)::value;
+        const int rl0 = wm * WTM + i * 32 + 8 * r4 + 4 * hg;  // first of 4 consecutive rows
+        float v0[2][4], v1[2][4];
+        static_for<0, 4>([&](auto qc) {
+          constexpr int q = decltype(qc)::value;
+          const int rl = rl0 + q, row = m0 + rl;
+          const float rs = row < M ? a.inv_rms[row] : 0.f;
+          const int pos = row < M ? s_pos[rl] : 0;
+          static_for<0, 2>([&](auto jc) {
+            constexpr int jp = decltype(jc)::value;
+            const int pi = jp * 32 + l32;  // pair index: columns pi and pi + 64 of the head
+            float x0 = acc[i][jp][4 * r4 + q] * rs, x1 = acc[i][jp + 2][4 * r4 + q] * rs;
+            if (is_q || is_k) {
+              const float2 cs = a.rope[(size_t)pos * 64 + pi];
+              const float y0 = x0 * cs.x - x1 * cs.y;
+              const float y1 = x1 * cs.x + x0 * cs.y;
+              x0 = y0;
+              x1 = y1;
+            }
+            v0[jp][q] = x0;
+            v1[jp][q] = x1;
+          });
+        });
+        if (is_q || is_k) {
+          static_for<0, 4>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            const int rl = rl0 + q, row = m0 + rl;
+            if (row < M) {
+              bf16_t* dst = is_q ? a.q_out + (size_t)row * a.Nq + wcol0
+                                 : (bf16_t*)a.kv.k + s_page[rl] + ((size_t)g * ps + (s_pos[rl] % ps)) * 128;
+              static_for<0, 2>([&](auto jc) {
+                constexpr int jp = decltype(jc)::value;
+                const int pi = jp * 32 + l32;
+                const int ca = a.traditional ? 2 * pi : pi;
+                const int cb = a.traditional ? 2 * pi + 1 : pi + 64;
+                dst[ca] = f32_to_bf16(v0[jp][q]);
+                dst[cb] = f32_to_bf16(v1[jp][q]);
+              });
+            }
+          });
+        } else {
+          // V is stored transposed per page ([g][d][slot]): 4 consecutive rows of
+          // one sequence at 4-aligned consecutive positions are 4 adjacent slots.
+          bf16_t* Vc = (bf16_t*)a.kv.v;
+          const int row0 = m0 + rl0;
+          bool vec = row0 + 3 < M;
+          if (vec) {
+            const int p0 = s_pos[rl0];
+            vec = (p0 & 3) == 0 && s_pos[rl0 + 3] == p0 + 3 && s_page[rl0 + 3] == s_page[rl0];
+          }
+          static_for<0, 2>([&](auto jc) {
+            constexpr int jp = decltype(jc)::value;
+            const int pi = jp * 32 + l32;
+            if (vec) {
+              const size_t base = s_page[rl0] + (size_t)g * 128 * ps + (s_pos[rl0] % ps);
+              uint2 w0, w1;
+              w0.x = (uint32_t)f32_to_bf16(v0[jp][0]) | ((uint32_t)f32_to_bf16(v0[jp][1]) << 16);
+              w0.y = (uint32_t)f32_to_bf16(v0[jp][2]) | ((uint32_t)f32_to_bf16(v0[jp][3]) << 16);
+              w1.x = (uint32_t)f32_to_bf16(v1[jp][0]) | ((uint32_t)f32_to_bf16(v1[jp][1]) << 16);
+              w1.y = (uint32_t)f32_to_bf16(v1[jp][2]) | ((uint32_t)f32_to_bf16(v1[jp][3]) << 16);
+              *reinterpret_cast<uint2*>(Vc + base + (size_t)pi * ps) = w0;
+              *reinterpret_cast<uint2*>(Vc + base + (size_t)(pi + 64) * ps) = w1;
+            } else {
+              static_for<0, 4>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                const int rl = rl0 + q;
+                if (m0 + rl < M) {
+                  const size_t base = s_page[rl] + (size_t)g * 128 * ps + (s_pos[rl] % ps);
+                  Vc[base + (size_t)pi * ps] = f32_to_bf16(v0[jp][q]);
+                  Vc[base + (size_t)(pi + 64) * ps] = f32_to_bf16(v1[jp][q]);
+                }
+              });
+            }
+          });
+        }
+      });
+    });
+  } else {
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -157,83 +299,52 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmArgs a) {
           float gt = acc[i][2 * jp][r] * rs, up = acc[i][2 * jp + 1][r] * rs;
           a.g_out[(size_t)row * F + j] = f32_to_bf16(silu_f(gt) * up);
         }
-      } else {  // EPI_QKV
-        const float rs = a.inv_rms[row];
-        const int bseq = row / a.L, l = row - bseq * a.L;
-        const int pos = a.kv.lens[bseq] + l;
-        const bool is_q = wcol0 < a.Nq;
-        const bool is_k = !is_q && wcol0 < a.Nq + a.Nkv;
-#pragma unroll
-        for (int jp = 0; jp < 2; ++jp) {
-          const int pi = jp * 32 + l32;  // pair index: columns pi and pi + 64 of the head
-          float x0 = acc[i][jp][r] * rs, x1 = acc[i][jp + 2][r] * rs;
-          if (is_q || is_k) {
-            float2 cs = a.rope[(size_t)pos * 64 + pi];
-            float y0 = x0 * cs.x - x1 * cs.y;
-            float y1 = x1 * cs.x + x0 * cs.y;
-            x0 = y0;
-            x1 = y1;
-          }
-          if (is_q) {
-            const int ca = a.traditional ? 2 * pi : pi;
-            const int cb = a.traditional ? 2 * pi + 1 : pi + 64;
-            bf16_t* qr = a.q_out + (size_t)row * a.Nq + wcol0;
-            qr[ca] = f32_to_bf16(x0);
-            qr[cb] = f32_to_bf16(x1);
-          } else if (is_k) {
-            const int ca = a.traditional ? 2 * pi : pi;
-            const int cb = a.traditional ? 2 * pi + 1 : pi + 64;
-            const int g = (wcol0 - a.Nq) >> 7;
-            bf16_t* Kc = (bf16_t*)a.kv.k;
-            Kc[a.kv.k_off(bseq, pos, g, ca)] = f32_to_bf16(x0);
-            Kc[a.kv.k_off(bseq, pos, g, cb)] = f32_to_bf16(x1);
-          } else {
-            const int g = (wcol0 - a.Nq - a.Nkv) >> 7;
-            bf16_t* Vc = (bf16_t*)a.kv.v;
-            Vc[a.kv.v_off(bseq, pos, g, pi)] = f32_to_bf16(x0);
-            Vc[a.kv.v_off(bseq, pos, g, pi + 64)] = f32_to_bf16(x1);
-          }
-        }
       }
     }
+  }
   }
   if constexpr (EPI == EPI_RESID) {
     if (a.lens_add && blockIdx.x == 0 && tid < a.n_seq) a.lens_add[tid] += a.lens_inc;
   }
 }
 
-template <int BM, int BN, int EPI>
+template <int BM, int BN, int EPI, bool F16>
 static void launch_cfg(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * (a.N / BN);
   const size_t lds = (size_t)2 * (BM + BN) * gm::LDS_ST * sizeof(bf16_t);
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)k_gemm_mfma<BM, BN, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)lds);
+    (void)hipFuncSetAttribute((const void*)k_gemm_mfma<BM, BN, EPI, F16>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, EPI>), dim3(tiles), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, EPI, F16>), dim3(tiles), dim3(256), lds, s, a);
 }
 
-template <int EPI>
+template <int EPI, bool F16>
 static void launch_epi(const GemmArgs& a, hipStream_t s) {
   // Pick the largest tile that still gives about one wave of blocks per CU.
   const long t256 = (long)((a.M + 255) / 256) * (a.N / 256);
   const bool n256 = (a.N % 256) == 0;
-  if (n256 && t256 >= 240) return launch_cfg<256, 256, EPI>(a, s);
-  if (n256 && (long)((a.M + 127) / 128) * (a.N / 256) >= 200) return launch_cfg<128, 256, EPI>(a, s);
-  if (n256) return launch_cfg<128, 256, EPI>(a, s);
-  return launch_cfg<128, 128, EPI>(a, s);
+  if (n256 && t256 >= 240) return launch_cfg<256, 256, EPI, F16>(a, s);
+  if (n256) return launch_cfg<128, 256, EPI, F16>(a, s);
+  return launch_cfg<128, 128, EPI, F16>(a, s);
+}
+
+template <bool F16>
+static void launch_any(int epi, const GemmArgs& a, hipStream_t s) {
+  switch (epi) {
+    case EPI_F32: return launch_epi<EPI_F32, F16>(a, s);
+    case EPI_QKV: return launch_epi<EPI_QKV, F16>(a, s);
+    case EPI_SWIGLU: return launch_epi<EPI_SWIGLU, F16>(a, s);
+    default: return launch_epi<EPI_RESID, F16>(a, s);
+  }
 }
 
 void launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0) return;
-  switch (epi) {
-    case EPI_F32: return launch_epi<EPI_F32>(a, s);
-    case EPI_QKV: return launch_epi<EPI_QKV>(a, s);
-    case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(a, s);
-    default: return launch_epi<EPI_RESID>(a, s);
-  }
+  if (a.b_f16) launch_any<true>(epi, a, s);
+  else launch_any<false>(epi, a, s);
 }
 
 }  // namespace lb

@@ -32,9 +32,15 @@ constexpr int XST = KC + 8;     // LDS row stride (bf16)
 
 template <int NW>
 __global__ __launch_bounds__(256) void k_gemv_bf16(const bf16_t* __restrict__ X, const bf16_t* __restrict__ W,
-                                                  float* __restrict__ part, int M, int N, int K, int ksl) {
+                                                  float* __restrict__ part, int M, int N, int K, int ksl,
+                                                  float* __restrict__ ss_out) {
   using namespace gv;
   __shared__ __attribute__((aligned(16))) bf16_t xs[64 * XST];
+  __shared__ float ssrow[64];
+  // the first column-block of each K slice also sums x^2 of the rows it stages
+  // (the RMSNorm statistic of the input, reduced over slices by its consumer)
+  const bool do_ss = ss_out != nullptr && blockIdx.x == 0;
+  if (threadIdx.x < 64) ssrow[threadIdx.x] = 0.f;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, hg = lane >> 4;
   const int n_blk = blockIdx.x;
@@ -80,6 +86,17 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const bf16_t* __restrict__ X,
       for (int kc = 0; kc < 8; ++kc) cur[j][kc] = wr[j][kc];
     if (k0 + KC < ke) wload(k0 + KC);
     const int nkc = nk >> 5;
+    if (do_ss) {
+      for (int r = wave; r < M; r += 4) {
+        float t = 0.f;
+        for (int c = lane; c < nk; c += 64) {
+          const float v = bf16_to_f32(xs[r * XST + c]);
+          t += v * v;
+        }
+        t = warp_sum(t);
+        if (lane == 0) ssrow[r] += t;
+      }
+    }
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       if (kc < nkc) {
@@ -94,6 +111,10 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const bf16_t* __restrict__ X,
         }
       }
     }
+  }
+  if (do_ss) {
+    __syncthreads();
+    if (tid < M) ss_out[(size_t)ksi * M + tid] = ssrow[tid];
   }
   // lane: C[m = 16*mt + 4*hg + i][n = nrow0 + 16*j + l16]
   float* pp = part + (size_t)ksi * M * N;
@@ -111,53 +132,68 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const bf16_t* __restrict__ X,
   }
 }
 
-void launch_gemv_bf16(const bf16_t* X, const bf16_t* W, float* partial, int M, int N, int K, int ks, hipStream_t s) {
+void launch_gemv_bf16(const bf16_t* X, const bf16_t* W, float* partial, int M, int N, int K, int ks,
+                      float* ss_out, hipStream_t s) {
   if (M <= 0 || N <= 0) return;
   const int ksl = K / ks;
   if (M > 16 && (N % 128) == 0) {
     dim3 grid(N / 128, ks);
-    hipLaunchKernelGGL(k_gemv_bf16<2>, grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl);
+    hipLaunchKernelGGL(k_gemv_bf16<2>, grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl, ss_out);
   } else {
     dim3 grid(N / 64, ks);
-    hipLaunchKernelGGL(k_gemv_bf16<1>, grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl);
+    hipLaunchKernelGGL(k_gemv_bf16<1>, grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl, ss_out);
   }
 }
 
 // ===========================================================================
 // 4-bit GEMV
 // ===========================================================================
-// Activation preparation, once per call: per row m,
+// Activation preparation, once per call: one block per row m computes
 //   xh  [M][K] fp16 in word-pair order: for the 8 codes k0..k0+7 of one word,
 //        (x0, x4), (x1/16, x5/16), (x2, x6), (x3/16, x7/16);
-//   xsum[M][K/32][2] = (sum of the xh values of the chunk, sum of x of the chunk).
-// x = x_in * inv_rms * gamma when those are given (RMSNorm feeding the GEMV).
-__global__ __launch_bounds__(256) void k_q4_prep(const bf16_t* X, const float* inv_rms, const float* gamma, int M,
-                                                 int K, _Float16* xh, float* xsum) {
-  const int m = blockIdx.y;
-  const int chunk = blockIdx.x * 4 + (threadIdx.x >> 6);  // 32 codes per chunk
-  const int lane = threadIdx.x & 63;
-  if (chunk >= K / 32 || m >= M) return;
-  // lane < 32 handles one code of the chunk
-  float x = 0.f;
-  float h = 0.f;
-  const int k = chunk * 32 + (lane & 31);
-  if (lane < 32) {
-    x = bf16_to_f32(X[(size_t)m * K + k]);
-    if (inv_rms) x *= inv_rms[m];
-    if (gamma) x *= gamma[k];
-    const int j = k & 7;                 // code position inside its word
-    const float sc = (j & 1) ? (1.0f / 16.0f) : 1.0f;
-    _Float16 hv = (_Float16)(x * sc);
-    h = (float)hv;
-    // slot inside the word's 8 fp16: pair p = j % 4, half = j / 4
-    const int p = j & 3, half = j >> 2;
-    xh[(size_t)m * K + (k & ~7) + 2 * p + half] = hv;
+//   xsum[M][K/32][2] = (sum of the xh values of the chunk, sum of x of the chunk)
+// with x = x_in * r * gamma_k when an RMSNorm feeds the projection (norm 1: r
+// from this row's own mean square; norm 2: r from the producer's statistic).
+__global__ __launch_bounds__(1024) void k_q4_prep(const bf16_t* X, int norm, RowStat stat, float eps,
+                                                  const float* gamma, int M, int K, _Float16* xh, float* xsum) {
+  const int m = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bf16_t* xr = X + (size_t)m * K;
+  float r = 1.0f;
+  if (norm == 1) {
+    __shared__ float red[16];
+    float t = 0.f;
+    for (int k = threadIdx.x; k < K; k += 1024) {
+      const float v = bf16_to_f32(xr[k]);
+      t += v * v;
+    }
+    t = warp_sum(t);
+    if (lane == 0) red[wave] = t;
+    __syncthreads();
+    float tot = 0.f;
+    for (int w = 0; w < 16; ++w) tot += red[w];
+    r = 1.0f / sqrtf(tot / (float)K + eps);
+  } else if (norm == 2) {
+    r = stat.get(m);
   }
-  float hs = warp_sum(lane < 32 ? h : 0.f);
-  float xsv = warp_sum(lane < 32 ? x : 0.f);
-  if (lane == 0) {
-    xsum[((size_t)m * (K / 32) + chunk) * 2 + 0] = hs;
-    xsum[((size_t)m * (K / 32) + chunk) * 2 + 1] = xsv;
+  for (int chunk = wave; chunk < K / 32; chunk += 16) {
+    float x = 0.f, h = 0.f;
+    if (lane < 32) {
+      const int k = chunk * 32 + lane;
+      x = bf16_to_f32(xr[k]);
+      if (norm) x *= r * gamma[k];
+      const int j = k & 7;                 // code position inside its word
+      const _Float16 hv = (_Float16)(x * ((j & 1) ? (1.0f / 16.0f) : 1.0f));
+      h = (float)hv;
+      // slot inside the word's 8 fp16: pair p = j % 4, half j / 4
+      xh[(size_t)m * K + (k & ~7) + 2 * (j & 3) + (j >> 2)] = hv;
+    }
+    const float hs = warp_sum(h);
+    const float xsv = warp_sum(x);
+    if (lane == 0) {
+      xsum[((size_t)m * (K / 32) + chunk) * 2 + 0] = hs;
+      xsum[((size_t)m * (K / 32) + chunk) * 2 + 1] = xsv;
+    }
   }
 }
 
@@ -229,12 +265,11 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const _Float16* __restrict__ xh
   }
 }
 
-void launch_gemv_q4(const bf16_t* X, const float* inv_rms, const float* gamma, const uint32_t* words,
-                    const bf16_t* scales, const bf16_t* biases, float* y, int M, int N, int K, int gs,
-                    _Float16* xh_buf, float* xsum_buf, hipStream_t s) {
+void launch_gemv_q4(const bf16_t* X, int norm, RowStat stat, float eps, const float* gamma,
+                    const uint32_t* words, const bf16_t* scales, const bf16_t* biases, float* y, int M, int N,
+                    int K, int gs, _Float16* xh_buf, float* xsum_buf, hipStream_t s) {
   if (M <= 0 || N <= 0) return;
-  dim3 pg((K / 32 + 3) / 4, M);
-  hipLaunchKernelGGL(k_q4_prep, pg, dim3(256), 0, s, X, inv_rms, gamma, M, K, xh_buf, xsum_buf);
+  hipLaunchKernelGGL(k_q4_prep, dim3(M), dim3(1024), 0, s, X, norm, stat, eps, gamma, M, K, xh_buf, xsum_buf);
   const int rpw = 2;
   const int blocks = (N + 4 * rpw - 1) / (4 * rpw);
   if (M == 1)

@@ -231,14 +231,15 @@ void launch_repack_bytes(uint8_t* dst, const uint8_t* src, int rows, int row_byt
 }
 
 // ---------------------------------------------------------------------------
-// 4-bit group-affine dequantisation to bf16 (prompt pass of the quantized
+// 4-bit group-affine dequantisation to fp16 (prompt pass of the quantized
 // stack): W[o, k] = scale[o, k/gs] * code[o, k] + bias[o, k/gs], the 4-bit /
 // group-64 format of the MLX quantization config ("模型配置").  The norm weight
-// of the following RMSNorm-fed GEMM is folded in (gamma_k) before rounding.
+// of the following RMSNorm-fed GEMM is folded in (gamma_k) before the single
+// rounding to fp16 (11 significant bits: 4x finer than bf16).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_q4_dequant(const uint32_t* words, const bf16_t* scales,
                                                     const bf16_t* biases, int N, int K, int gs,
-                                                    const float* gamma, bf16_t* out) {
+                                                    const float* gamma, _Float16* out) {
   int row = blockIdx.x;
   int nw = K / 8;
   const uint32_t* wr = words + (size_t)row * nw;
@@ -254,14 +255,18 @@ __global__ __launch_bounds__(256) void k_q4_dequant(const uint32_t* words, const
       float a = sc * (float)((u >> (8 * j)) & 15u) + bi;
       float b = sc * (float)((u >> (8 * j + 4)) & 15u) + bi;
       if (gamma) { a *= gamma[k0 + 2 * j]; b *= gamma[k0 + 2 * j + 1]; }
-      o[j] = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+      const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+      uint16_t ua, ub;
+      __builtin_memcpy(&ua, &ha, 2);
+      __builtin_memcpy(&ub, &hb, 2);
+      o[j] = (uint32_t)ua | ((uint32_t)ub << 16);
     }
     st16(out + (size_t)row * K + k0, make_uint4(o[0], o[1], o[2], o[3]));
   }
 }
 
 void launch_q4_dequant(const uint32_t* words, const bf16_t* scales, const bf16_t* biases, int N, int K, int gs,
-                       const float* gamma, bf16_t* out, hipStream_t s) {
+                       const float* gamma, _Float16* out, hipStream_t s) {
   if (N <= 0) return;
   hipLaunchKernelGGL(k_q4_dequant, dim3(N), dim3(256), 0, s, words, scales, biases, N, K, gs, gamma, out);
 }

@@ -4,6 +4,23 @@
 
 namespace lb {
 
+// RMSNorm row statistic of row m, from whichever source a producer left:
+//   inv[m] directly, or partial sums of squares ss[j * M + m] (j < nb) over the
+//   n elements of the row, reduced here in a fixed order; neither: 1.
+struct RowStat {
+  const float* inv = nullptr;
+  const float* ss = nullptr;
+  int nb = 0, M = 0, n = 1;
+  float eps = 0.f;
+  __device__ inline float get(int m) const {
+    if (inv) return inv[m];
+    if (!ss) return 1.0f;
+    float t = 0.f;
+    for (int j = 0; j < nb; ++j) t += ss[(size_t)j * M + m];
+    return 1.0f / sqrtf(t / (float)n + eps);
+  }
+};
+
 // ---------------------------------------------------------------- k_misc.hip
 // inv_rms[r] = 1 / sqrt(mean(x[r,:]^2) + eps) for rows of x [rows, D].
 template <typename T>
@@ -30,9 +47,9 @@ void launch_repack_rows(T* dst, const T* src, int rows, int K, const T* gamma, i
                         int ib_stride, int perm_d, hipStream_t s);
 void launch_repack_bytes(uint8_t* dst, const uint8_t* src, int rows, int row_bytes, int row0, int ib,
                          int ib_stride, int perm_d, hipStream_t s);
-// dense bf16 [N, K] = (scale * code + bias) * gamma_k (gamma may be null)
+// dense fp16 [N, K] = (scale * code + bias) * gamma_k (gamma may be null)
 void launch_q4_dequant(const uint32_t* words, const bf16_t* scales, const bf16_t* biases, int N, int K,
-                       int gs, const float* gamma, bf16_t* out, hipStream_t s);
+                       int gs, const float* gamma, _Float16* out, hipStream_t s);
 template <typename T>
 void launch_to_f32(const T* src, float* dst, int n, hipStream_t s);
 // ids_out[*cursor] = *cur_id; logits_out[*cursor] = logits (if logits_out); ++*cursor
@@ -47,9 +64,10 @@ void launch_gemm_simt(const T* A, const T* B, float* C, int M, int N, int K, hip
 // ----------------------------------------------------------- k_gemm_mfma.hip
 enum GemmEpi { EPI_F32 = 0, EPI_QKV = 1, EPI_SWIGLU = 2, EPI_RESID = 3 };
 struct GemmArgs {
-  const bf16_t* A;  // [M, K]
-  const bf16_t* B;  // [N, K]
+  const bf16_t* A;  // [M, K] bf16
+  const bf16_t* B;  // [N, K] bf16, or fp16 bit patterns when b_f16
   int M, N, K;
+  int b_f16;        // B is fp16: A is converted to fp16 and the MFMA runs on fp16
   // EPI_F32
   float* C;
   // row scale (QKV / SWIGLU): inv_rms[M]
@@ -72,25 +90,29 @@ struct GemmArgs {
 void launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- k_gemv.hip
-// partial[ks][M][N] (fp32) = X[M, kslice] * W[N, kslice]^T (bf16, M <= 64)
+// partial[ks][M][N] (fp32) = X[M, kslice] * W[N, kslice]^T (bf16, M <= 64).
+// ss_out (optional): sum of squares of each X row over each K slice, [ks][M].
 void launch_gemv_bf16(const bf16_t* X, const bf16_t* W, float* partial, int M, int N, int K, int ks,
-                      hipStream_t s);
-// y[M][N] (fp32) = xhat W^T, W 4-bit group affine, xhat = x * inv_rms * gamma (each
-// optional), M <= 4.  xh_buf: fp16 [M, K]; xsum_buf: fp32 [M, K/32, 2] (scratch).
-void launch_gemv_q4(const bf16_t* X, const float* inv_rms, const float* gamma, const uint32_t* words,
-                    const bf16_t* scales, const bf16_t* biases, float* y, int M, int N, int K, int gs,
-                    _Float16* xh_buf, float* xsum_buf, hipStream_t s);
+                      float* ss_out, hipStream_t s);
+// y[M][N] (fp32) = xhat W^T, W 4-bit group affine, xhat = x * r * gamma, M <= 4.
+// norm: 0 = no RMSNorm (r = 1, gamma unused), 1 = r from the row itself (eps),
+// 2 = r from `stat`.  xh_buf: fp16 [M, K]; xsum_buf: fp32 [M, K/32, 2] (scratch).
+void launch_gemv_q4(const bf16_t* X, int norm, RowStat stat, float eps, const float* gamma,
+                    const uint32_t* words, const bf16_t* scales, const bf16_t* biases, float* y, int M, int N,
+                    int K, int gs, _Float16* xh_buf, float* xsum_buf, hipStream_t s);
 
 // ------------------------------------------------------------ k_epilogue.hip
 // All take fp32 partials [ks][M][N] and reduce them in a fixed order.
 template <typename T>
-void launch_epi_qkv(const float* part, int ks, int M, int Nq, int Nkv, const float* inv_rms, int L,
+void launch_epi_qkv(const float* part, int ks, int M, int Nq, int Nkv, RowStat stat, int L,
                     const float2* rope, int traditional, T* q_out, KVView kv, hipStream_t s);
+// out = resid + sum(part); ss_out (optional): per-256-column-block sums of squares of
+// the stored rows, [ceil(N/256)][M] (a RowStat source for the next RMSNorm).
 template <typename T>
-void launch_epi_resid(const float* part, int ks, int M, int N, const T* resid, T* out, float eps,
-                      float* inv_rms_out, int32_t* lens_add, int lens_inc, int n_seq, T* branch, hipStream_t s);
+void launch_epi_resid(const float* part, int ks, int M, int N, const T* resid, T* out, float* ss_out,
+                      int32_t* lens_add, int lens_inc, int n_seq, T* branch, hipStream_t s);
 template <typename T>
-void launch_epi_swiglu(const float* part, int ks, int M, int F2, int ib, const float* inv_rms, T* g_out,
+void launch_epi_swiglu(const float* part, int ks, int M, int F2, int ib, RowStat stat, T* g_out,
                        hipStream_t s);
 // logits[M][N] = sum_ks part
 void launch_reduce_f32(const float* part, int ks, int M, int N, float* out, hipStream_t s);

@@ -154,9 +154,11 @@ llama_status llama_block_set_diag(llama_block* blk, int32_t enable);
  * *n_calls, and disarms.  Phases, in launch order:
  *   bf16 prefill : rms(x), qkv gemm+rope+append, attention, wo gemm+residual,
  *                  rms(h), w1/w3 gemm+swiglu, w2 gemm+residual            (7)
- *   decode, fp32 : rms(x), qkv projection, qkv finish, attention, wo projection,
- *                  residual(+rms), w1/w3 projection, swiglu, w2 projection,
- *                  residual                                                (10)
+ *   fp32         : rms(x), qkv projection, qkv finish, attention, wo projection,
+ *                  residual, w1/w3 projection, swiglu, w2 projection, residual (10)
+ *   bf16 decode  : qkv projection (+ x statistics), qkv finish, attention,
+ *                  wo projection, residual (+ h statistics), w1/w3 projection,
+ *                  swiglu, w2 projection, residual                          (9)
  * Not for calls captured into a graph. */
 llama_status llama_block_profile_start(llama_block* blk, int32_t max_calls);
 llama_status llama_block_profile_read(llama_block* blk, float* phase_ms, int32_t max_phases, int32_t* n_phases,

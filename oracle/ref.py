@@ -193,6 +193,8 @@ def block_forward(x: np.ndarray, w: Dict[str, object], shape, k_cache: Optional[
     x = np.asarray(x, dtype=F64)
     B, L, D = x.shape
     H, G, d = shape.n_heads, shape.n_kv_heads, shape.head_dim
+    # each weight converted to float64 (or dequantized) once for all sequences
+    w = {k: (v if k.endswith("norm") else weight_matrix(v)) for k, v in w.items()}
     res = {k: [] for k in ("y", "h", "attn", "ffn", "k_new", "v_new", "q", "rows")}
     for b in range(B):
         S = 0 if k_cache is None else int(np.asarray(k_cache[b]).shape[0])
@@ -252,6 +254,9 @@ def greedy_generate(ids: np.ndarray, layers: Sequence[Dict[str, object]], head: 
     ("生成过程" on the MLX page).  Returns the emitted ids (steps + 1 of them:
     one from the prompt pass, one per step) and the logits behind each."""
     ids = np.asarray(ids).reshape(1, -1)
+    # weights as float64 once (4-bit ones dequantized once), not once per step
+    layers = [{k: (v if k.endswith("norm") else weight_matrix(v)) for k, v in w.items()} for w in layers]
+    head = dict(head, output=weight_matrix(head["output"]))
     kc: List[List[np.ndarray]] = [[np.zeros((0, shape.n_kv_heads, shape.head_dim))] for _ in layers]
     vc: List[List[np.ndarray]] = [[np.zeros((0, shape.n_kv_heads, shape.head_dim))] for _ in layers]
     x = embed(head["embedding"], ids)                     # [1, L, D]
