@@ -496,6 +496,11 @@ static SLayout scratch_layout(const llama_block_config& c, const Dims& d, int T,
       part = std::max(part, (size_t)gemv_ks(T, NK[i][0], NK[i][1]) * T * NK[i][0] * 4);
   } else if (decode && d.q4) {
     part = (size_t)T * maxN * 4;
+  } else {
+    // prefill: wo / w2 split along K when their tile grid is small; a split
+    // needs fewer than 200 tiles of 256 x 256, which bounds the rows it covers
+    const long rows_split = 256L * std::max(0L, (199L * 256 / d.D));
+    part = (size_t)kMaxSplitK * std::min<long>(T, rows_split) * d.D * 4;
   }
   L.part = off; off = align256(off + part);
   L.n_splits = (max_seq + kSplitLen - 1) / kSplitLen;
@@ -685,10 +690,25 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
   mk(s);
   launch_attn_prefill_bf16(q, kv, B, L, d.H, d.G, attn, s);
   mk(s);
-  GemmArgs o{};
-  o.A = attn; o.B = weight(blk->o, nullptr); o.M = M; o.N = d.D; o.K = d.Nq; o.b_f16 = d.q4;
-  o.resid = (const bf16_t*)x; o.out = h;
-  launch_gemm_mfma(EPI_RESID, o, s);
+  // wo and w2 (N = dim) give few output tiles at small T: there the K range is
+  // split, every slice writes fp32 partials and the residual epilogue kernel
+  // adds them (in slice order) to the residual.
+  float* part = (float*)(sc + S.part);
+  auto resid_gemm = [&](const bf16_t* A, const Lin& lin, const bf16_t* resid, bf16_t* out, int K, int32_t* lens_add,
+                        int lens_inc, bf16_t* branch) {
+    GemmArgs g{};
+    g.A = A; g.B = weight(lin, nullptr); g.M = M; g.N = d.D; g.K = K; g.b_f16 = d.q4;
+    const int ks = gemm_split_k(M, d.D, K);
+    if (ks > 1) {
+      g.C = part; g.ksplit = ks;
+      launch_gemm_mfma(EPI_F32, g, s);
+      launch_epi_resid<bf16_t>(part, ks, M, d.D, resid, out, nullptr, lens_add, lens_inc, B, branch, s);
+    } else {
+      g.resid = resid; g.out = out; g.lens_add = lens_add; g.lens_inc = lens_inc; g.n_seq = B; g.branch = branch;
+      launch_gemm_mfma(EPI_RESID, g, s);
+    }
+  };
+  resid_gemm(attn, blk->o, (const bf16_t*)x, h, d.Nq, nullptr, 0, nullptr);
   mk(s);
   launch_rms_inv<bf16_t>(h, M, d.D, eps, inv2, s);
   mk(s);
@@ -697,12 +717,7 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
   f.inv_rms = inv2; f.g_out = g;
   launch_gemm_mfma(EPI_SWIGLU, f, s);
   mk(s);
-  GemmArgs w2{};
-  w2.A = g; w2.B = weight(blk->w2, nullptr); w2.M = M; w2.N = d.D; w2.K = d.F; w2.b_f16 = d.q4;
-  w2.resid = h; w2.out = (bf16_t*)y;
-  w2.lens_add = kv.lens; w2.lens_inc = L; w2.n_seq = B;
-  w2.branch = blk->diag ? (bf16_t*)(sc + S.ffn) : nullptr;
-  launch_gemm_mfma(EPI_RESID, w2, s);
+  resid_gemm(g, blk->w2, h, (bf16_t*)y, d.F, kv.lens, L, blk->diag ? (bf16_t*)(sc + S.ffn) : nullptr);
   mk(s);
 }
 

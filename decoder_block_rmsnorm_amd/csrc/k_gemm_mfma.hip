@@ -16,6 +16,8 @@
 // one barrier per K step.  Blocks are renumbered XCD-major and walked in
 // GROUP_M-row bands so that co-resident blocks of one XCD share A and B tiles
 // in that XCD's L2.
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -67,26 +69,37 @@ __device__ inline f16x8 u4_as_f16x8(uint4 v) {
   return r;
 }
 
-template <int BM, int BN, int EPI, bool F16>
-__global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmArgs a) {
+// NW wavefronts per block (4 or 8), DEPTH K steps of global loads in flight
+// (1 or 2 register sets).
+template <int BM, int BN, int NW, int DEPTH, int EPI, bool F16>
+__global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
   using namespace gm;
+  constexpr int NT = NW * 64;
   constexpr int WN = BN / 128;
-  constexpr int WM = 4 / WN;
+  constexpr int WM = NW / WN;
   constexpr int WTM = BM / WM;
   constexpr int MI = WTM / 32;
-  constexpr int A_CH = BM * 8 / 256;  // 16-byte chunks per thread per K step
-  constexpr int B_CH = BN * 8 / 256;
+  constexpr int A_CH = BM * 8 / NT;  // 16-byte chunks per thread per K step
+  constexpr int B_CH = BN * 8 / NT;
+  static_assert(MI >= 1 && A_CH >= 1 && B_CH >= 1, "tile / wave split");
   extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
   // buffer b: A tile at lds + b * (BM + BN) * LDS_ST, B tile right after it
   auto As = [&](int b) { return lds + b * (BM + BN) * LDS_ST; };
   auto Bs = [&](int b) { return lds + b * (BM + BN) * LDS_ST + BM * LDS_ST; };
 
-  const int M = a.M, N = a.N, K = a.K;
+  const int M = a.M, N = a.N;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
-  // XCD-major renumbering, then grouped ordering
+  // XCD-major renumbering, then grouped ordering; K slice = slowest index
   const int nblk = gridDim.x;
   int bid = blockIdx.x;
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int ntile = tiles_m * tiles_n;
+  const int ksi = bid / ntile;
+  bid -= ksi * ntile;
+  const int K = a.K;                          // row stride of A and B
+  const int Kslice = a.K / (a.ksplit > 0 ? a.ksplit : 1);
+  const bf16_t* Ag = a.A + (size_t)ksi * Kslice;
+  const bf16_t* Bg = a.B + (size_t)ksi * Kslice;
   const int per_group = GROUP_M * tiles_n;
   const int group = bid / per_group;
   const int first_m = group * GROUP_M;
@@ -99,34 +112,42 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmArgs a) {
   const int l32 = lane & 31, hg = lane >> 5;
   const int wm = wave / WN, wn = wave % WN;
 
-  const bf16_t* Ag = a.A;
-  const bf16_t* Bg = a.B;
-  uint4 ra[A_CH], rb[B_CH];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
+  // Two register sets of prefetched K steps: the global loads of step kt+2 are
+  // issued while step kt is multiplied, so each load has two MFMA phases to land.
+  uint4 ra0[A_CH], rb0[B_CH], ra1[A_CH], rb1[B_CH];
+  // Tile bases are uniform (scalar registers); per-lane offsets are 32-bit
+  // element offsets (operands are < 2^31 elements), so each load needs one VGPR
+  // of address instead of two.
+  const bf16_t* Atile = Ag + (size_t)m0 * K;
+  const bf16_t* Btile = Bg + (size_t)n0 * K;
+  uint32_t aoff[A_CH], boff[B_CH];
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      int c = tid + 256 * i;
-      int r = c >> 3, kc = c & 7;
-      int gr = min(m0 + r, M - 1);
-      ra[i] = ld16(Ag + (size_t)gr * K + k0 + kc * 8);
-    }
+  for (int i = 0; i < A_CH; ++i) {
+    const int c = tid + NT * i, r = c >> 3, kc = c & 7;
+    aoff[i] = (uint32_t)(min(r, M - 1 - m0) * K + kc * 8);
+  }
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      int c = tid + 256 * i;
-      int r = c >> 3, kc = c & 7;
-      rb[i] = ld16(Bg + (size_t)(n0 + r) * K + k0 + kc * 8);
-    }
+  for (int i = 0; i < B_CH; ++i) {
+    const int c = tid + NT * i, r = c >> 3, kc = c & 7;
+    boff[i] = (uint32_t)(r * K + kc * 8);
+  }
+  auto gload = [&](int kt, uint4(&ra)[A_CH], uint4(&rb)[B_CH]) {
+    const bf16_t* at = Atile + kt * BK;
+    const bf16_t* bt = Btile + kt * BK;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) ra[i] = ld16(at + aoff[i]);
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) rb[i] = ld16(bt + boff[i]);
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, const uint4(&ra)[A_CH], const uint4(&rb)[B_CH]) {
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
-      int c = tid + 256 * i;
+      int c = tid + NT * i;
       st16(As(buf) + (c >> 3) * LDS_ST + (c & 7) * 8, F16 ? bf16x8_to_f16x8(ra[i]) : ra[i]);
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
-      int c = tid + 256 * i;
+      int c = tid + NT * i;
       st16(Bs(buf) + (c >> 3) * LDS_ST + (c & 7) * 8, rb[i]);
     }
   };
@@ -137,33 +158,83 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
 
-  const int KT = K / BK;
-  gload(0);
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    lstore(buf);
-    __syncthreads();
-    if (kt + 1 < KT) gload(kt + 1);
+  // One K step from LDS buffer `buf`: fragments of sub-step kk+1 are read while
+  // the MFMAs of sub-step kk run (two fragment register sets), and the
+  // scheduler is asked to interleave one LDS read between MFMAs.
+  auto compute = [&](int buf) {
     const bf16_t* as = As(buf) + (wm * WTM + l32) * LDS_ST + hg * 8;
     const bf16_t* bs = Bs(buf) + (wn * 128 + l32) * LDS_ST + hg * 8;
+    // 4 wavefronts (one per SIMD): fragments double-buffered so the next
+    // sub-step's LDS reads overlap this sub-step's MFMAs.  8 wavefronts: one
+    // fragment set (registers go to the second prefetch set instead); the other
+    // wavefront on the SIMD covers the LDS latency.
+    constexpr int FS = NW == 4 ? 2 : 1;
+    uint4 fa[FS][MI], fb[FS][4];
+    auto lfrag = [&](int kk, uint4(&a_)[MI], uint4(&b_)[4]) {
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      uint4 af[MI], bfr[4];
+      for (int i = 0; i < MI; ++i) a_[i] = ld16(as + i * 32 * LDS_ST + kk * 16);
 #pragma unroll
-      for (int i = 0; i < MI; ++i) af[i] = ld16(as + i * 32 * LDS_ST + kk * 16);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = ld16(bs + j * 32 * LDS_ST + kk * 16);
+      for (int j = 0; j < 4; ++j) b_[j] = ld16(bs + j * 32 * LDS_ST + kk * 16);
+    };
+    auto mfmas = [&](const uint4(&a_)[MI], const uint4(&b_)[4]) {
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if constexpr (F16)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(u4_as_f16x8(af[i]), u4_as_f16x8(bfr[j]), acc[i][j],
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(u4_as_f16x8(a_[i]), u4_as_f16x8(b_[j]), acc[i][j],
                                                                0, 0, 0);
           else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_as_bf16x8(af[i]), u4_as_bf16x8(bfr[j]),
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_as_bf16x8(a_[i]), u4_as_bf16x8(b_[j]),
                                                                 acc[i][j], 0, 0, 0);
         }
+    };
+    if constexpr (FS == 2) {
+      lfrag(0, fa[0], fb[0]);
+      static_for<0, BK / 16>([&](auto kc) {
+        constexpr int kk = decltype(kc)::value;
+        constexpr int cur = kk & 1;
+        if constexpr (kk + 1 < BK / 16) lfrag(kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+        // fence: the reads above are issued before, and stay before, these MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(fa[cur], fb[cur]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        lfrag(kk, fa[0], fb[0]);
+        mfmas(fa[0], fb[0]);
+      }
+    }
+  };
+
+  // LDS buffer b is rewritten two steps after it was read; the barrier of the
+  // step in between guarantees every wavefront has finished reading it.
+  const int KT = Kslice / BK;
+  if constexpr (DEPTH == 2) {
+    gload(0, ra0, rb0);
+    if (KT > 1) gload(1, ra1, rb1);
+    for (int kt = 0; kt < KT; kt += 2) {
+      lstore(0, ra0, rb0);
+      __syncthreads();
+      if (kt + 2 < KT) gload(kt + 2, ra0, rb0);
+      compute(0);
+      if (kt + 1 < KT) {
+        lstore(1, ra1, rb1);
+        __syncthreads();
+        if (kt + 3 < KT) gload(kt + 3, ra1, rb1);
+        compute(1);
+      }
+    }
+  } else {
+    gload(0, ra0, rb0);
+    for (int kt = 0; kt < KT; ++kt) {
+      const int buf = kt & 1;
+      lstore(buf, ra0, rb0);
+      __syncthreads();
+      if (kt + 1 < KT) gload(kt + 1, ra0, rb0);
+      compute(buf);
     }
   }
 
@@ -176,7 +247,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmArgs a) {
     __syncthreads();
     int* s_pos = reinterpret_cast<int*>(lds);
     long long* s_page = reinterpret_cast<long long*>(lds + 4 * BM);  // 8-byte aligned
-    for (int r = tid; r < BM; r += 256) {
+    for (int r = tid; r < BM; r += NT) {
       const int row = m0 + r;
       if (row < M) {
         const int bseq = row / a.L;
@@ -279,7 +350,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmArgs a) {
       if (row >= M) continue;
       if constexpr (EPI == EPI_F32) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a.C[(size_t)row * N + wcol0 + j * 32 + l32] = acc[i][j][r];
+        for (int j = 0; j < 4; ++j)
+          a.C[(size_t)ksi * M * N + (size_t)row * N + wcol0 + j * 32 + l32] = acc[i][j][r];
       } else if constexpr (EPI == EPI_RESID) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -308,27 +380,50 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mfma(GemmArgs a) {
   }
 }
 
-template <int BM, int BN, int EPI, bool F16>
+template <int BM, int BN, int NW, int DEPTH, int EPI, bool F16>
 static void launch_cfg(const GemmArgs& a, hipStream_t s) {
-  const int tiles = ((a.M + BM - 1) / BM) * (a.N / BN);
+  const int tiles = ((a.M + BM - 1) / BM) * (a.N / BN) * (EPI == EPI_F32 && a.ksplit > 1 ? a.ksplit : 1);
   const size_t lds = (size_t)2 * (BM + BN) * gm::LDS_ST * sizeof(bf16_t);
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)k_gemm_mfma<BM, BN, EPI, F16>,
+    (void)hipFuncSetAttribute((const void*)k_gemm_mfma<BM, BN, NW, DEPTH, EPI, F16>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, EPI, F16>), dim3(tiles), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, DEPTH, EPI, F16>), dim3(tiles), dim3(NW * 64), lds, s, a);
+}
+
+// Tile choice; LLAMA_BLOCK_GEMM_TILE = "256x256w8", "256x256w4", "128x256w4" or
+// "128x128w4" forces one (for measurements).
+static int forced_tile() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("LLAMA_BLOCK_GEMM_TILE");
+    v = 0;
+    if (e) {
+      if (!strcmp(e, "256x256w8")) v = 1;
+      else if (!strcmp(e, "256x256w4")) v = 2;
+      else if (!strcmp(e, "128x256w4")) v = 3;
+      else if (!strcmp(e, "128x128w4")) v = 4;
+    }
+  }
+  return v;
 }
 
 template <int EPI, bool F16>
 static void launch_epi(const GemmArgs& a, hipStream_t s) {
-  // Pick the largest tile that still gives about one wave of blocks per CU.
-  const long t256 = (long)((a.M + 255) / 256) * (a.N / 256);
   const bool n256 = (a.N % 256) == 0;
-  if (n256 && t256 >= 240) return launch_cfg<256, 256, EPI, F16>(a, s);
-  if (n256) return launch_cfg<128, 256, EPI, F16>(a, s);
-  return launch_cfg<128, 128, EPI, F16>(a, s);
+  const int f = forced_tile();
+  if (EPI == EPI_F32 && a.ksplit > 1) return launch_cfg<256, 256, 8, 2, EPI, F16>(a, s);
+  if (f == 1 && n256) return launch_cfg<256, 256, 8, 2, EPI, F16>(a, s);
+  if (f == 2 && n256) return launch_cfg<256, 256, 4, 1, EPI, F16>(a, s);
+  if (f == 3 && n256) return launch_cfg<128, 256, 4, 2, EPI, F16>(a, s);
+  if (f == 4) return launch_cfg<128, 128, 4, 2, EPI, F16>(a, s);
+  // default: the largest tile that still gives about one wave of blocks per CU
+  const long t256 = (long)((a.M + 255) / 256) * (a.N / 256);
+  if (n256 && t256 >= 240) return launch_cfg<256, 256, 8, 2, EPI, F16>(a, s);
+  if (n256) return launch_cfg<128, 256, 4, 2, EPI, F16>(a, s);
+  return launch_cfg<128, 128, 4, 2, EPI, F16>(a, s);
 }
 
 template <bool F16>
@@ -339,6 +434,16 @@ static void launch_any(int epi, const GemmArgs& a, hipStream_t s) {
     case EPI_SWIGLU: return launch_epi<EPI_SWIGLU, F16>(a, s);
     default: return launch_epi<EPI_RESID, F16>(a, s);
   }
+}
+
+int gemm_split_k(int M, int N, int K) {
+  if (N % 256) return 1;
+  const long t256 = (long)((M + 255) / 256) * (N / 256);
+  int ks = 1;
+  // double while the grid is short of about 200 tiles and each slice keeps
+  // at least 512 of K in whole 64-wide steps
+  while (ks < kMaxSplitK && ks * t256 < 200 && K % (128 * ks) == 0 && K / (2 * ks) >= 512) ks *= 2;
+  return ks;
 }
 
 void launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t s) {

@@ -68,6 +68,7 @@ struct GemmArgs {
   const bf16_t* B;  // [N, K] bf16, or fp16 bit patterns when b_f16
   int M, N, K;
   int b_f16;        // B is fp16: A is converted to fp16 and the MFMA runs on fp16
+  int ksplit;       // EPI_F32 only: K split into ksplit slices, slice s -> C + s*M*N
   // EPI_F32
   float* C;
   // row scale (QKV / SWIGLU): inv_rms[M]
@@ -88,6 +89,10 @@ struct GemmArgs {
   bf16_t* branch;         // if non-null: the product before the residual add [M, N]
 };
 void launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t s);
+// K slices (1, 2 or 4) for an [M, N] x K product whose 256x256 tile grid alone
+// leaves the chip short of work; slice s writes fp32 partials at C + s*M*N
+constexpr int kMaxSplitK = 4;
+int gemm_split_k(int M, int N, int K);
 
 // ---------------------------------------------------------------- k_gemv.hip
 // partial[ks][M][N] (fp32) = X[M, kslice] * W[N, kslice]^T (bf16, M <= 64).
