@@ -120,14 +120,14 @@ def llama_kvcache_bytes(cfg: llama_kvcache_config) -> int:
     return lib().llama_kvcache_bytes(C.byref(cfg))
 
 
-def llama_kvcache_init(cfg, dev_mem, dev_bytes: int, stream=None) -> int:
+def llama_kvcache_alloc(cfg, dev_mem, dev_bytes: int, stream=None) -> int:
     out = C.c_void_p()
-    _check(lib().llama_kvcache_init(C.byref(cfg), _ptr(dev_mem), dev_bytes, _stream(stream), C.byref(out)))
+    _check(lib().llama_kvcache_alloc(C.byref(cfg), _ptr(dev_mem), dev_bytes, _stream(stream), C.byref(out)))
     return out.value
 
 
-def llama_kvcache_destroy(cache: int) -> None:
-    lib().llama_kvcache_destroy(cache)
+def llama_kvcache_free(cache: int) -> None:
+    lib().llama_kvcache_free(cache)
 
 
 def llama_kvcache_set_block_table(cache, table_host: Sequence[int], stream=None) -> None:
@@ -260,16 +260,16 @@ class Block:
 
 
 class KVCache:
-    """Paged KV cache in one device buffer (see llama_kvcache_init)."""
+    """Paged KV cache in one device buffer (see llama_kvcache_alloc)."""
 
     def __init__(self, n_layers, max_batch, max_seq, n_kv_heads, head_dim, dtype=LLAMA_BF16, page_size=64,
                  stream=None):
         self.cfg = llama_kvcache_config(n_layers, max_batch, max_seq, n_kv_heads, head_dim, page_size, dtype)
         nbytes = llama_kvcache_bytes(self.cfg)
         if nbytes == 0:
-            llama_kvcache_init(self.cfg, 0, 0, stream)
+            llama_kvcache_alloc(self.cfg, 0, 0, stream)
         self.mem = _device_bytes(nbytes)
-        self.handle = llama_kvcache_init(self.cfg, self.mem, nbytes, stream)
+        self.handle = llama_kvcache_alloc(self.cfg, self.mem, nbytes, stream)
         self.pages_per_seq = -(-max_seq // page_size)
 
     def write(self, layer, seq, pos0, k, v, stream=None):
@@ -290,7 +290,7 @@ class KVCache:
     def __del__(self):
         h = getattr(self, "handle", None)
         if h and _abi is not None and _abi._lib is not None:
-            _abi._lib.llama_kvcache_destroy(h)
+            _abi._lib.llama_kvcache_free(h)
         self.handle = None
 
 

@@ -55,8 +55,8 @@ SIGNATURES = {
     "llama_block_profile_start": (I32, [P, I32]),
     "llama_block_profile_read": (I32, [P, C.POINTER(C.c_float), I32, PI32, PI32]),
     "llama_kvcache_bytes": (SZ, [C.POINTER(llama_kvcache_config)]),
-    "llama_kvcache_init": (I32, [C.POINTER(llama_kvcache_config), P, SZ, P, PP]),
-    "llama_kvcache_destroy": (None, [P]),
+    "llama_kvcache_alloc": (I32, [C.POINTER(llama_kvcache_config), P, SZ, P, PP]),
+    "llama_kvcache_free": (None, [P]),
     "llama_kvcache_set_block_table": (I32, [P, PI32, P]),
     "llama_kvcache_set_lens": (I32, [P, I32, PI32, I32, P]),
     "llama_kvcache_get_lens": (I32, [P, I32, PI32, I32]),

@@ -323,7 +323,7 @@ extern "C" size_t llama_kvcache_bytes(const llama_kvcache_config* c) {
   return cache_layout(*c).total;
 }
 
-extern "C" llama_status llama_kvcache_init(const llama_kvcache_config* c, void* mem, size_t bytes, void* stream,
+extern "C" llama_status llama_kvcache_alloc(const llama_kvcache_config* c, void* mem, size_t bytes, void* stream,
                                            llama_kvcache** out) {
   llama_status st = check_cache_config(c);
   if (st != LLAMA_OK) return st;
@@ -359,7 +359,7 @@ extern "C" llama_status llama_kvcache_init(const llama_kvcache_config* c, void* 
   return LLAMA_OK;
 }
 
-extern "C" void llama_kvcache_destroy(llama_kvcache* c) { delete c; }
+extern "C" void llama_kvcache_free(llama_kvcache* c) { delete c; }
 
 extern "C" llama_status llama_kvcache_set_block_table(llama_kvcache* c, const int32_t* t, void* stream) {
   if (!c || !t) return fail(LLAMA_ERR_INVALID_ARG, "cache and table must be non-NULL");

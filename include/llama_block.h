@@ -181,9 +181,9 @@ size_t llama_kvcache_bytes(const llama_kvcache_config* cfg);
 
 /* Lay the cache out in dev_mem (>= llama_kvcache_bytes, 256-byte aligned): identity
  * block table, all lens 0.  Enqueued on stream and waited for. */
-llama_status llama_kvcache_init(const llama_kvcache_config* cfg, void* dev_mem, size_t dev_bytes,
-                                void* stream, llama_kvcache** out);
-void llama_kvcache_destroy(llama_kvcache* cache);
+llama_status llama_kvcache_alloc(const llama_kvcache_config* cfg, void* dev_mem, size_t dev_bytes,
+                                 void* stream, llama_kvcache** out);
+void llama_kvcache_free(llama_kvcache* cache);
 
 /* Replace the block table (table_host: int32 [max_batch][pages_per_seq], a
  * permutation of 0 .. max_batch*pages_per_seq-1).  Copied synchronously. */

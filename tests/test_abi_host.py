@@ -91,13 +91,13 @@ def test_kvcache_config_validation():
                         (L.llama_kvcache_config(1, 1, 64, 4, 64, 64, 9), L.LLAMA_ERR_INVALID_ARG)]:
         assert L.llama_kvcache_bytes(bad) == 0
         with pytest.raises(L.LlamaError) as e:
-            L.llama_kvcache_init(bad, 0, 0, 0)
+            L.llama_kvcache_alloc(bad, 0, 0, 0)
         assert e.value.status == status
     with pytest.raises(L.LlamaError) as e:
-        L.llama_kvcache_init(ok, 0, n, 0)                 # NULL memory
+        L.llama_kvcache_alloc(ok, 0, n, 0)                 # NULL memory
     assert e.value.status == L.LLAMA_ERR_INVALID_ARG
     with pytest.raises(L.LlamaError) as e:
-        L.llama_kvcache_init(ok, 256, n - 256, 0)         # too small (checked before any access)
+        L.llama_kvcache_alloc(ok, 256, n - 256, 0)         # too small (checked before any access)
     assert e.value.status == L.LLAMA_ERR_CAPACITY
 
 
