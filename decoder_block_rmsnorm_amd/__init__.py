@@ -105,8 +105,8 @@ def llama_block_set_diag(blk, enable: int) -> None:
     _check(lib().llama_block_set_diag(blk, int(enable)))
 
 
-def llama_block_profile_start(blk, max_calls: int) -> None:
-    _check(lib().llama_block_profile_start(blk, max_calls))
+def llama_block_profile_start(blk, max_calls: int, phase_mask: int = 0) -> None:
+    _check(lib().llama_block_profile_start(blk, max_calls, phase_mask))
 
 
 def llama_block_profile_read(blk, max_phases: int = 16):
@@ -245,8 +245,11 @@ class Block:
     def set_diag(self, enable: bool) -> None:
         llama_block_set_diag(self.handle, int(enable))
 
-    def profile_start(self, max_calls: int) -> None:
-        llama_block_profile_start(self.handle, max_calls)
+    def profile_start(self, max_calls: int, phases=None) -> None:
+        """Time the next max_calls calls; phases: indices of the phases to time
+        (None: all)."""
+        mask = 0 if phases is None else sum(1 << p for p in phases)
+        llama_block_profile_start(self.handle, max_calls, mask)
 
     def profile_read(self):
         """-> (per-phase summed milliseconds, number of calls)"""

@@ -52,7 +52,7 @@ SIGNATURES = {
     "llama_block_decode": (I32, [P, P, I32, P, P, I32, P, SZ, P]),
     "llama_block_diag": (I32, [P, P, I32, I32, PP]),
     "llama_block_set_diag": (I32, [P, I32]),
-    "llama_block_profile_start": (I32, [P, I32]),
+    "llama_block_profile_start": (I32, [P, I32, C.c_uint32]),
     "llama_block_profile_read": (I32, [P, C.POINTER(C.c_float), I32, PI32, PI32]),
     "llama_kvcache_bytes": (SZ, [C.POINTER(llama_kvcache_config)]),
     "llama_kvcache_alloc": (I32, [C.POINTER(llama_kvcache_config), P, SZ, P, PP]),

@@ -112,6 +112,7 @@ struct llama_block {
   // profiling: events [max_calls][kMaxMarks], calls recorded so far
   std::vector<hipEvent_t> ev;
   int prof_max = 0, prof_calls = 0, prof_marks = 0;
+  uint32_t prof_mask = 0;  // phases timed (bit p = phase p); all when 0
   ~llama_block() {
     for (hipEvent_t e : ev) (void)hipEventDestroy(e);
   }
@@ -120,11 +121,17 @@ struct llama_block {
 static const int kMaxMarks = 12;
 
 // Records an event before the first kernel and after each phase of one call.
+// Phase boundary b (before phase b, after phase b-1) gets an event only when
+// one of those two phases is timed.
 struct Marker {
   hipEvent_t* ev = nullptr;
+  uint32_t mask = 0;
   int i = 0;
   void operator()(hipStream_t s) {
-    if (ev && i < kMaxMarks) (void)hipEventRecord(ev[i++], s);
+    if (!ev || i >= kMaxMarks) return;
+    const bool need = mask == 0 || ((mask >> i) & 1u) || (i > 0 && ((mask >> (i - 1)) & 1u));
+    if (need) (void)hipEventRecord(ev[i], s);
+    ++i;
   }
 };
 
@@ -545,12 +552,14 @@ extern "C" llama_status llama_block_diag(const llama_block* blk, void* scratch, 
   return LLAMA_OK;
 }
 
-extern "C" llama_status llama_block_profile_start(llama_block* blk, int32_t max_calls) {
+extern "C" llama_status llama_block_profile_start(llama_block* blk, int32_t max_calls, uint32_t phase_mask) {
   if (!blk || max_calls <= 0) return fail(LLAMA_ERR_INVALID_ARG, "block must be non-NULL and max_calls > 0");
+  blk->prof_mask = phase_mask;
   const size_t need = (size_t)max_calls * kMaxMarks;
   while (blk->ev.size() < need) {
     hipEvent_t e;
-    HIP_TRY(hipEventCreate(&e), "profile_start");
+    // timing-only events: no system-scope fence (no cache write-back between kernels)
+    HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableSystemFence), "profile_start");
     blk->ev.push_back(e);
   }
   blk->prof_max = max_calls;
@@ -566,8 +575,9 @@ extern "C" llama_status llama_block_profile_read(llama_block* blk, float* ms, in
   for (int p = 0; p < np; ++p) ms[p] = 0.f;
   for (int c = 0; c < blk->prof_calls; ++c) {
     hipEvent_t* e = &blk->ev[(size_t)c * kMaxMarks];
-    HIP_TRY(hipEventSynchronize(e[blk->prof_marks - 1]), "profile_read");
+    HIP_TRY(hipDeviceSynchronize(), "profile_read");
     for (int p = 0; p < np; ++p) {
+      if (blk->prof_mask && !((blk->prof_mask >> p) & 1u)) continue;
       float t = 0.f;
       HIP_TRY(hipEventElapsedTime(&t, e[p], e[p + 1]), "profile_read");
       ms[p] += t;
@@ -804,7 +814,10 @@ static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const
   char* sc = (char*)scratch;
   const Dims& d = blk->dm;
   Marker mk;
-  if (blk->prof_calls < blk->prof_max) mk.ev = &blk->ev[(size_t)(blk->prof_calls++) * kMaxMarks];
+  if (blk->prof_calls < blk->prof_max) {
+    mk.ev = &blk->ev[(size_t)(blk->prof_calls++) * kMaxMarks];
+    mk.mask = blk->prof_mask;
+  }
   if (!d.bf16) {
     fp32_path<float>(blk, kv, x, y, batch, L, sc, S, mk, s);
   } else if (!decode) {

@@ -284,6 +284,14 @@ void launch_attn_prefill_bf16(const bf16_t* q, KVView kv, int B, int L, int H, i
 // S^T (16 keys x 16 q) = K (16 x 32 d) Q^T via 16x16x32 MFMA, 4 d-chunks;
 // O^T (16 d x 16 q) += V^T (16 d x 32 keys) P^T, 8 d-subtiles.
 // Partials: part_o [B][H][n_splits][128], part_ml [B][H][n_splits][2] (max, sum).
+// Keys are processed 64 per step (a step never crosses a page: pages are a
+// multiple of 64 slots).  The four 16-key S tiles load their K rows in an order
+// that leaves every lane holding 8 consecutive keys of one 32-key half for its
+// query column: tile st = 2*half + t, A-row r loads key 32*half + 8*(r/4) +
+// 4*t + r%4, so accumulator element i of lane group hg is key 32*half + 8*hg +
+// 4*t + i.  Those 8 probabilities are then directly the B operand of the P.V
+// MFMA, and the matching V^T operand is one 16-byte load of 8 consecutive
+// slots of a transposed V page row.
 __global__ __launch_bounds__(256) void k_attn_decode_bf16(const bf16_t* __restrict__ q, KVView kv, int B, int H,
                                                          int G, int n_splits, int split_len,
                                                          float* __restrict__ part_o, float* __restrict__ part_ml) {
@@ -317,32 +325,42 @@ __global__ __launch_bounds__(256) void k_attn_decode_bf16(const bf16_t* __restri
 #pragma unroll
   for (int i = 0; i < 8; ++i) o_acc[i] = (f32x4){};
   float m_run = -INFINITY, l_run = 0.f;
+  // key offset (inside a 64-key step) of the K row this lane loads for tile st
+  const int krow_lo = 8 * (l16 >> 2) + (l16 & 3);
 
-  for (int k0 = k_begin; k0 < k_end; k0 += 32) {
-    // keys k0 .. k0+31 lie in one page (page size is a multiple of 64, k0 % 32 == 0)
+  for (int k0 = k_begin; k0 < k_end; k0 += 64) {
     const size_t base = kv.page_base(b, k0);
     const int slot0 = k0 % kv.ps;
     const bf16_t* kpage = Kp + base + (size_t)g * kv.ps * 128;
     const bf16_t* vpage = Vp + base + (size_t)g * 128 * kv.ps;
-    f32x4 s_acc[2];
+    uint4 kr[4][4], vr[8][2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      s_acc[st] = (f32x4){};
-      const bf16_t* krow = kpage + (size_t)(slot0 + st * 16 + l16) * 128;
+    for (int st = 0; st < 4; ++st) {
+      const bf16_t* krow = kpage + (size_t)(slot0 + 32 * (st >> 1) + 4 * (st & 1) + krow_lo) * 128 + 8 * hg;
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        bf16x8 a = as_bf16x8(ld16(krow + 32 * kc + 8 * hg));
-        s_acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[kc], s_acc[st], 0, 0, 0);
-      }
+      for (int kc = 0; kc < 4; ++kc) kr[st][kc] = ld16(krow + 32 * kc);
     }
-    // lane: query l16, keys st*16 + 4*hg + i
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) {
+      const bf16_t* vrow = vpage + (size_t)(ds * 16 + l16) * kv.ps + slot0 + 8 * hg;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) vr[ds][hf] = ld16(vrow + 32 * hf);
+    }
+    f32x4 s_acc[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      s_acc[st] = (f32x4){};
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        s_acc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[st][kc]), qf[kc], s_acc[st], 0, 0, 0);
+    }
     float tmax = -INFINITY;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        int key = k0 + st * 16 + 4 * hg + i;
-        float v = key < k_end ? s_acc[st][i] * sl2 : -INFINITY;
+        const int key = k0 + 32 * (st >> 1) + 8 * hg + 4 * (st & 1) + i;
+        const float v = key < k_end ? s_acc[st][i] * sl2 : -INFINITY;
         s_acc[st][i] = v;
         tmax = fmaxf(tmax, v);
       }
@@ -352,10 +370,10 @@ __global__ __launch_bounds__(256) void k_attn_decode_bf16(const bf16_t* __restri
     const float alpha = exp2f(m_run - m_new);
     float psum = 0.f;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float p = exp2f(s_acc[st][i] - m_new);
+        const float p = exp2f(s_acc[st][i] - m_new);
         s_acc[st][i] = p;
         psum += p;
       }
@@ -363,32 +381,36 @@ __global__ __launch_bounds__(256) void k_attn_decode_bf16(const bf16_t* __restri
     psum += __shfl_xor(psum, 32, 64);
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    // P^T as B operand: k index 8*hg + j <-> key (j<4: 4*hg + j; j>=4: 16 + 4*hg + j-4)
-    uint4 pw;
-    pw.x = pack_bf16x2(s_acc[0][0], s_acc[0][1]);
-    pw.y = pack_bf16x2(s_acc[0][2], s_acc[0][3]);
-    pw.z = pack_bf16x2(s_acc[1][0], s_acc[1][1]);
-    pw.w = pack_bf16x2(s_acc[1][2], s_acc[1][3]);
-    const bf16x8 pb = as_bf16x8(pw);
-    const bool tail = k0 + 32 > k_end;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      uint4 pw;
+      pw.x = pack_bf16x2(s_acc[2 * hf][0], s_acc[2 * hf][1]);
+      pw.y = pack_bf16x2(s_acc[2 * hf][2], s_acc[2 * hf][3]);
+      pw.z = pack_bf16x2(s_acc[2 * hf + 1][0], s_acc[2 * hf + 1][1]);
+      pw.w = pack_bf16x2(s_acc[2 * hf + 1][2], s_acc[2 * hf + 1][3]);
+      pb[hf] = as_bf16x8(pw);
+    }
+    if (k0 + 64 > k_end) {
+      // slots past the last key: zero the values (a stale NaN times weight 0
+      // would poison the sum)
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          uint32_t w[4] = {vr[ds][hf].x, vr[ds][hf].y, vr[ds][hf].z, vr[ds][hf].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (k0 + 32 * hf + 8 * hg + e >= k_end) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          vr[ds][hf] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) {
       o_acc[ds] *= alpha;
-      const bf16_t* vr = vpage + (size_t)(ds * 16 + l16) * kv.ps + slot0;
-      uint2 lo = *reinterpret_cast<const uint2*>(vr + 4 * hg);
-      uint2 hi = *reinterpret_cast<const uint2*>(vr + 16 + 4 * hg);
-      if (tail) {  // keys past k_end: zero (a stale NaN times weight 0 would poison the sum)
-        uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          int key = k0 + (e < 4 ? 4 * hg + e : 16 + 4 * hg + e - 4);
-          if (key >= k_end) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-        }
-        lo = make_uint2(w[0], w[1]);
-        hi = make_uint2(w[2], w[3]);
-      }
-      bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-      o_acc[ds] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o_acc[ds], 0, 0, 0);
+      for (int hf = 0; hf < 2; ++hf)
+        o_acc[ds] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vr[ds][hf]), pb[hf], o_acc[ds], 0, 0, 0);
     }
   }
   // lane: O^T[d = 16*ds + 4*hg + i][q = l16]
@@ -406,25 +428,53 @@ __global__ __launch_bounds__(256) void k_attn_decode_bf16(const bf16_t* __restri
   }
 }
 
-// One wavefront per (b, h): o = sum_c e^(m_c - M) O_c / sum_c e^(m_c - M) l_c
-__global__ __launch_bounds__(256) void k_attn_merge(const float* part_o, const float* part_ml, int BH,
-                                                    int n_splits, bf16_t* out) {
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+// One wavefront per (b, h): o = sum_c e^(m_c - M) O_c / sum_c e^(m_c - M) l_c,
+// summed in chunk order.  Lane c computes the weight of chunk c (64 chunks at a
+// time, shared by shuffles); each lane owns two of the 128 output columns.
+__global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_ml, int BH, int n_splits,
+                                                    bf16_t* __restrict__ out) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wid = blockIdx.x * 4 + wave;
   if (wid >= BH) return;
   const float* ml = part_ml + (size_t)wid * n_splits * 2;
+  const float* po = part_o + (size_t)wid * n_splits * 128;
+  float o0 = 0.f, o1 = 0.f, den = 0.f;
   float M = -INFINITY;
-  for (int c = 0; c < n_splits; ++c) M = fmaxf(M, ml[2 * c]);
-  float den = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int c = 0; c < n_splits; ++c) {
-    float mc = ml[2 * c];
-    if (mc == -INFINITY) continue;
-    float w = exp2f(mc - M);
-    den += w * ml[2 * c + 1];
-    const float* po = part_o + ((size_t)wid * n_splits + c) * 128;
-    o0 += w * po[lane];
-    o1 += w * po[lane + 64];
+  for (int c = lane; c < n_splits; c += 64) M = fmaxf(M, ml[2 * c]);
+  M = warp_max(M);
+  for (int c0 = 0; c0 < n_splits; c0 += 64) {
+    const int c = c0 + lane;
+    float w = 0.f, dl = 0.f;
+    if (c < n_splits) {
+      const float mc = ml[2 * c];
+      w = mc == -INFINITY ? 0.f : exp2f(mc - M);
+      dl = w * ml[2 * c + 1];
+    }
+    den += dl;
+    const int nc = min(64, n_splits - c0);
+    int j = 0;
+    for (; j + 4 <= nc; j += 4) {
+      float a[4], bb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[u] = po[(size_t)(c0 + j + u) * 128 + lane];
+        bb[u] = po[(size_t)(c0 + j + u) * 128 + lane + 64];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wu = __shfl(w, j + u, 64);
+        o0 += wu * a[u];
+        o1 += wu * bb[u];
+      }
+    }
+    for (; j < nc; ++j) {
+      const float wu = __shfl(w, j, 64);
+      o0 += wu * po[(size_t)(c0 + j) * 128 + lane];
+      o1 += wu * po[(size_t)(c0 + j) * 128 + lane + 64];
+    }
   }
+  den = warp_sum(den);
   bf16_t* orow = out + (size_t)wid * 128;
   orow[lane] = f32_to_bf16(o0 / den);
   orow[lane + 64] = f32_to_bf16(o1 / den);

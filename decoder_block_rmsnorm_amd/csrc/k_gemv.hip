@@ -26,71 +26,76 @@ __device__ inline bf16x8 v_as_bf16x8(uint4 v) {
 }
 
 namespace gv {
-constexpr int KC = 256;         // K chunk staged per step
+constexpr int KC = 256;         // K chunk per pipeline step
 constexpr int XST = KC + 8;     // LDS row stride (bf16)
 }  // namespace gv
 
-template <int NW>
+// Pipeline per block: the weight rows of chunk c+2 and the activations of chunk
+// c+1 are in flight while chunk c is multiplied.  Program order is chosen for
+// the in-order vmcnt counter: the activations of c+1 are requested before the
+// weights of c+2, so waiting for them never waits for the newer weights.
+template <int NW, int MT>
 __global__ __launch_bounds__(256) void k_gemv_bf16(const bf16_t* __restrict__ X, const bf16_t* __restrict__ W,
                                                   float* __restrict__ part, int M, int N, int K, int ksl,
                                                   float* __restrict__ ss_out) {
   using namespace gv;
-  __shared__ __attribute__((aligned(16))) bf16_t xs[64 * XST];
-  __shared__ float ssrow[64];
+  constexpr int ROWS = MT * 16;
+  constexpr int XL = ROWS * (KC / 8) / 256;   // 16-byte activation pieces per thread per chunk
+  __shared__ __attribute__((aligned(16))) bf16_t xs[2][ROWS * XST];
+  __shared__ float ssrow[ROWS];
   // the first column-block of each K slice also sums x^2 of the rows it stages
   // (the RMSNorm statistic of the input, reduced over slices by its consumer)
   const bool do_ss = ss_out != nullptr && blockIdx.x == 0;
-  if (threadIdx.x < 64) ssrow[threadIdx.x] = 0.f;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, hg = lane >> 4;
-  const int n_blk = blockIdx.x;
+  if (tid < ROWS) ssrow[tid] = 0.f;
   const int ksi = blockIdx.y;
   const int kb = ksi * ksl, ke = min(K, kb + ksl);
-  const int MT = (M + 15) >> 4;
-  const int nrow0 = n_blk * (64 * NW) + wave * (16 * NW);
+  const int nch = (ke - kb + KC - 1) / KC;
+  const int nrow0 = blockIdx.x * (64 * NW) + wave * (16 * NW);
 
-  f32x4 acc[4][NW];
+  f32x4 acc[MT][NW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < NW; ++j) acc[i][j] = (f32x4){};
 
-  uint4 wr[NW][8];
-  auto wload = [&](int k0) {
+  uint4 w0[NW][8], w1[NW][8], xr[XL];
+  auto wload = [&](int c, uint4(&w)[NW][8]) {
+    const int k0 = kb + c * KC;
     const int nkc = min(8, (ke - k0) >> 5);
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
       const bf16_t* wrow = W + (size_t)(nrow0 + j * 16 + l16) * K + k0 + 8 * hg;
 #pragma unroll
       for (int kc = 0; kc < 8; ++kc)
-        if (kc < nkc) wr[j][kc] = ld16(wrow + 32 * kc);
+        if (kc < nkc) w[j][kc] = ld16(wrow + 32 * kc);
     }
   };
-
-  if (kb < ke) wload(kb);
-  for (int k0 = kb; k0 < ke; k0 += KC) {
-    const int nk = min(KC, ke - k0);
-    // stage X[0:M, k0:k0+nk] (rows >= M read as zero)
-    const int chunks = MT * 16 * (nk >> 3);
-    __syncthreads();
-    for (int c = tid; c < chunks; c += 256) {
-      int r = c / (nk >> 3), kc = c % (nk >> 3);
-      uint4 v = r < M ? ld16(X + (size_t)r * K + k0 + kc * 8) : make_uint4(0, 0, 0, 0);
-      st16(xs + r * XST + kc * 8, v);
+  // piece p of a chunk: row p / 32, 8 columns at 8 * (p % 32); rows >= M and
+  // columns past the slice read as zero
+  auto xload = [&](int c) {
+    const int k0 = kb + c * KC;
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int p = tid + 256 * i, r = p >> 5, col = (p & 31) * 8;
+      xr[i] = (r < M && k0 + col < ke) ? ld16(X + (size_t)r * K + k0 + col) : make_uint4(0, 0, 0, 0);
     }
-    __syncthreads();
-    uint4 cur[NW][8];
+  };
+  auto xstore = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < NW; ++j)
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc) cur[j][kc] = wr[j][kc];
-    if (k0 + KC < ke) wload(k0 + KC);
-    const int nkc = nk >> 5;
+    for (int i = 0; i < XL; ++i) {
+      const int p = tid + 256 * i, r = p >> 5, col = (p & 31) * 8;
+      st16(&xs[buf][r * XST + col], xr[i]);
+    }
+  };
+  auto compute = [&](int buf, int c, const uint4(&w)[NW][8]) {
+    const int nkc = min(8, (ke - kb - c * KC) >> 5);
     if (do_ss) {
       for (int r = wave; r < M; r += 4) {
         float t = 0.f;
-        for (int c = lane; c < nk; c += 64) {
-          const float v = bf16_to_f32(xs[r * XST + c]);
+        for (int col = lane; col < nkc * 32; col += 64) {
+          const float v = bf16_to_f32(xs[buf][r * XST + col]);
           t += v * v;
         }
         t = warp_sum(t);
@@ -101,26 +106,41 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const bf16_t* __restrict__ X,
     for (int kc = 0; kc < 8; ++kc) {
       if (kc < nkc) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          if (mt < MT) {
-            bf16x8 xa = v_as_bf16x8(ld16(xs + (mt * 16 + l16) * XST + 32 * kc + 8 * hg));
+        for (int mt = 0; mt < MT; ++mt) {
+          bf16x8 xa = v_as_bf16x8(ld16(&xs[buf][(mt * 16 + l16) * XST + 32 * kc + 8 * hg]));
 #pragma unroll
-            for (int j = 0; j < NW; ++j)
-              acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, v_as_bf16x8(cur[j][kc]), acc[mt][j], 0, 0, 0);
-          }
+          for (int j = 0; j < NW; ++j)
+            acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, v_as_bf16x8(w[j][kc]), acc[mt][j], 0, 0, 0);
         }
       }
     }
-  }
-  if (do_ss) {
+  };
+
+  if (nch > 0) {
+    xload(0);
+    wload(0, w0);
+    if (nch > 1) wload(1, w1);
+    xstore(0);
     __syncthreads();
-    if (tid < M) ss_out[(size_t)ksi * M + tid] = ssrow[tid];
   }
+  for (int c = 0; c < nch; c += 2) {
+    if (c + 1 < nch) xload(c + 1);
+    compute(0, c, w0);
+    if (c + 2 < nch) wload(c + 2, w0);
+    if (c + 1 < nch) xstore(1);
+    __syncthreads();
+    if (c + 1 >= nch) break;
+    if (c + 2 < nch) xload(c + 2);
+    compute(1, c + 1, w1);
+    if (c + 3 < nch) wload(c + 3, w1);
+    if (c + 2 < nch) xstore(0);
+    __syncthreads();
+  }
+  if (do_ss && tid < M) ss_out[(size_t)ksi * M + tid] = ssrow[tid];
   // lane: C[m = 16*mt + 4*hg + i][n = nrow0 + 16*j + l16]
   float* pp = part + (size_t)ksi * M * N;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    if (mt >= MT) break;
+  for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = mt * 16 + 4 * hg + i;
@@ -138,10 +158,18 @@ void launch_gemv_bf16(const bf16_t* X, const bf16_t* W, float* partial, int M, i
   const int ksl = K / ks;
   if (M > 16 && (N % 128) == 0) {
     dim3 grid(N / 128, ks);
-    hipLaunchKernelGGL(k_gemv_bf16<2>, grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl, ss_out);
+    if (M <= 32)
+      hipLaunchKernelGGL((k_gemv_bf16<2, 2>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl, ss_out);
+    else
+      hipLaunchKernelGGL((k_gemv_bf16<2, 4>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl, ss_out);
   } else {
     dim3 grid(N / 64, ks);
-    hipLaunchKernelGGL(k_gemv_bf16<1>, grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl, ss_out);
+    if (M <= 16)
+      hipLaunchKernelGGL((k_gemv_bf16<1, 1>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl, ss_out);
+    else if (M <= 32)
+      hipLaunchKernelGGL((k_gemv_bf16<1, 2>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl, ss_out);
+    else
+      hipLaunchKernelGGL((k_gemv_bf16<1, 4>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl, ss_out);
   }
 }
 

@@ -148,10 +148,12 @@ llama_status llama_block_set_diag(llama_block* blk, int32_t enable);
 
 /* Per-phase timing (profiling aid).  profile_start arms HIP events for the next
  * max_calls prefill/decode calls of this block: each call records an event on its
- * stream before its first kernel and after each phase.  profile_read waits for
- * those events, writes the summed milliseconds of each phase over the recorded
- * calls to phase_ms[0 .. *n_phases) (at most max_phases), the number of calls to
- * *n_calls, and disarms.  Phases, in launch order:
+ * stream at the boundaries of the phases selected by phase_mask (bit p = phase p;
+ * 0 = every phase).  Each event costs a few microseconds of stream time, so a
+ * mask with one phase disturbs the timing least.  profile_read waits for the
+ * device, writes the summed milliseconds of each phase over the recorded calls to
+ * phase_ms[0 .. *n_phases) (at most max_phases; 0 for phases not selected), the
+ * number of calls to *n_calls, and disarms.  Phases, in launch order:
  *   bf16 prefill : rms(x), qkv gemm+rope+append, attention, wo gemm+residual,
  *                  rms(h), w1/w3 gemm+swiglu, w2 gemm+residual            (7)
  *   fp32         : rms(x), qkv projection, qkv finish, attention, wo projection,
@@ -160,7 +162,7 @@ llama_status llama_block_set_diag(llama_block* blk, int32_t enable);
  *                  wo projection, residual (+ h statistics), w1/w3 projection,
  *                  swiglu, w2 projection, residual                          (9)
  * Not for calls captured into a graph. */
-llama_status llama_block_profile_start(llama_block* blk, int32_t max_calls);
+llama_status llama_block_profile_start(llama_block* blk, int32_t max_calls, uint32_t phase_mask);
 llama_status llama_block_profile_read(llama_block* blk, float* phase_ms, int32_t max_phases, int32_t* n_phases,
                                       int32_t* n_calls);
 
