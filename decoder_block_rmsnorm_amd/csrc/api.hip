@@ -162,6 +162,10 @@ static WLayout weight_layout(const llama_block_config& c, const Dims& d) {
       off = align256(off + N * K / 2);
       L.lin[i][1] = off; off = align256(off + N * (K / 64) * 2);
       L.lin[i][2] = off; off = align256(off + N * (K / 64) * 2);
+    } else if (d.bf16) {
+      // tiled layout: K padded to whole 256-column chunks
+      off = align256(off + N * (size_t)tiled_chunks((int)K) * kTileK * 2);
+      L.lin[i][1] = L.lin[i][2] = 0;
     } else {
       off = align256(off + N * K * esize(c.act_dtype));
       L.lin[i][1] = L.lin[i][2] = 0;
@@ -193,10 +197,10 @@ static void repack_linear(const Dims& d, int dt, const Lin& dst, const llama_lin
     launch_repack_bytes((uint8_t*)dst.b, (const uint8_t*)src.biases, rows, (K / 64) * 2, row0, ib, ib_stride, perm_d, s);
   } else if (dt == LLAMA_F32) {
     launch_repack_rows<float>((float*)dst.w, (const float*)src.w, rows, K, (const float*)gamma, row0, ib, ib_stride,
-                              perm_d, s);
+                              perm_d, 0, s);
   } else {
     launch_repack_rows<bf16_t>((bf16_t*)dst.w, (const bf16_t*)src.w, rows, K, (const bf16_t*)gamma, row0, ib,
-                               ib_stride, perm_d, s);
+                               ib_stride, perm_d, 1, s);
   }
 }
 
@@ -461,11 +465,14 @@ static const int kSplitLen = 256;  // keys per decode-attention chunk
 // Split-K factor of a decode projection [M rows] x [N, K]: enough blocks to
 // cover the chip several times over, K slices that stay multiples of 32 and at
 // least 512 long.
+// K slices of a decode projection: double while the grid is short of 768
+// blocks and every slice keeps at least two 256-column chunks.
 static int gemv_ks(int M, int N, int K) {
   const int cols = (M > 16 && N % 128 == 0) ? 128 : 64;
   const int tiles = N / cols;
+  const int nchk = tiled_chunks(K);
   int ks = 1;
-  while (tiles * ks < 768 && (K % (64 * ks)) == 0 && K / (2 * ks) >= 512) ks *= 2;
+  while (tiles * ks < 768 && 4 * ks <= nchk) ks *= 2;
   return ks;
 }
 
@@ -752,7 +759,7 @@ static void bf16_decode(const llama_block* blk, KVView kv, const void* x, void* 
   if (!d.q4) {
     // the QKV projection also emits sum(x^2) per K slice: attention_norm's statistic
     int ks = gemv_ks(B, d.Nqkv, d.D);
-    launch_gemv_bf16((const bf16_t*)x, (const bf16_t*)blk->qkv.w, part, B, d.Nqkv, d.D, ks, ssx, s);
+    launch_gemv_bf16((const bf16_t*)x, (const bf16_t*)blk->qkv.w, true, part, B, d.Nqkv, d.D, ks, ssx, s);
     mk(s);
     RowStat stx;
     stx.ss = ssx; stx.nb = ks; stx.M = B; stx.n = d.D; stx.eps = eps;
@@ -761,17 +768,17 @@ static void bf16_decode(const llama_block* blk, KVView kv, const void* x, void* 
     launch_attn_decode_bf16(q, kv, B, d.H, d.G, n_splits, kSplitLen, ao, aml, attn, s);
     mk(s);
     ks = gemv_ks(B, d.D, d.Nq);
-    launch_gemv_bf16(attn, (const bf16_t*)blk->o.w, part, B, d.D, d.Nq, ks, nullptr, s);
+    launch_gemv_bf16(attn, (const bf16_t*)blk->o.w, true, part, B, d.D, d.Nq, ks, nullptr, s);
     mk(s);
     launch_epi_resid<bf16_t>(part, ks, B, d.D, (const bf16_t*)x, h, ssh, nullptr, 0, 0, nullptr, s);
     mk(s);
     ks = gemv_ks(B, 2 * d.F, d.D);
-    launch_gemv_bf16(h, (const bf16_t*)blk->w13.w, part, B, 2 * d.F, d.D, ks, nullptr, s);
+    launch_gemv_bf16(h, (const bf16_t*)blk->w13.w, true, part, B, 2 * d.F, d.D, ks, nullptr, s);
     mk(s);
     launch_epi_swiglu<bf16_t>(part, ks, B, 2 * d.F, d.IB, sth, g, s);
     mk(s);
     ks = gemv_ks(B, d.D, d.F);
-    launch_gemv_bf16(g, (const bf16_t*)blk->w2.w, part, B, d.D, d.F, ks, nullptr, s);
+    launch_gemv_bf16(g, (const bf16_t*)blk->w2.w, true, part, B, d.D, d.F, ks, nullptr, s);
     mk(s);
     launch_epi_resid<bf16_t>(part, ks, B, d.D, h, (bf16_t*)y, nullptr, kv.lens, 1, B, ffn, s);
     mk(s);
@@ -907,7 +914,7 @@ static llama_status head_enqueue(const llama_linear* head, int wf, int gs, int d
     launch_gemm_simt<float>((const float*)(sc + L.xn), (const float*)head->w, out, B, V, D, s);
   } else {
     launch_rmsnorm_apply<bf16_t>((const bf16_t*)x, (const bf16_t*)fnorm, B, D, eps, (bf16_t*)(sc + L.xn), s);
-    launch_gemv_bf16((const bf16_t*)(sc + L.xn), (const bf16_t*)head->w, out, B, V, D, 1, nullptr, s);
+    launch_gemv_bf16((const bf16_t*)(sc + L.xn), (const bf16_t*)head->w, false, out, B, V, D, 1, nullptr, s);
   }
   launch_argmax(out, B, V, ids, s);
   return hip_check("lm_head_argmax");

@@ -89,6 +89,20 @@ __device__ inline float warp_max(float v) {
 __device__ inline float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
 // 16-byte vector load/store helpers.
+// Tiled layout of the bf16 dense weights [N][K]: 16-row groups by 256-column
+// chunks, each (group, chunk) tile 8 KB contiguous, chunks of a group in order.
+// Inside a tile, the 32-column block kb is 1 KB holding 64 pieces of 16 bytes:
+// piece 16*j + r = row r of the group, columns 32*kb + 8*j .. 8*j + 7.  One
+// wavefront-wide 16-byte load of a block (lane = piece) is then one contiguous
+// kilobyte and lands as the B operand of v_mfma_f32_16x16x32_bf16 (lane l holds
+// B[k = 8*(l/16) + e][n = l%16]).  K is padded to a multiple of 256 (kTileK).
+constexpr int kTileK = 256;
+__host__ __device__ inline int tiled_chunks(int K) { return (K + kTileK - 1) / kTileK; }
+__host__ __device__ inline size_t tiled_off(int n, int k, int nchk) {
+  return ((((size_t)(n >> 4) * nchk + (k >> 8)) * 8 + ((k >> 5) & 7)) * 64 + (((k >> 3) & 3) * 16 + (n & 15))) * 8 +
+         (k & 7);
+}
+
 __device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ inline void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 

@@ -98,8 +98,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
   bid -= ksi * ntile;
   const int K = a.K;                          // row stride of A and B
   const int Kslice = a.K / (a.ksplit > 0 ? a.ksplit : 1);
+  // B: fp16 row-major [N][K] (dequantized 4-bit weights) or bf16 in the tiled
+  // layout, where column k of a 16-row group sits at (k / 32) * 512 + ... and
+  // a 64-wide K step of one group is 2 KB contiguous
+  const int nchk = tiled_chunks(a.K);
   const bf16_t* Ag = a.A + (size_t)ksi * Kslice;
-  const bf16_t* Bg = a.B + (size_t)ksi * Kslice;
+  const bf16_t* Bg = a.B + (size_t)ksi * Kslice * (F16 ? 1 : 16);
   const int per_group = GROUP_M * tiles_n;
   const int group = bid / per_group;
   const int first_m = group * GROUP_M;
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
   // element offsets (operands are < 2^31 elements), so each load needs one VGPR
   // of address instead of two.
   const bf16_t* Atile = Ag + (size_t)m0 * K;
-  const bf16_t* Btile = Bg + (size_t)n0 * K;
+  const bf16_t* Btile = Bg + (F16 ? (size_t)n0 * K : (size_t)(n0 >> 4) * nchk * (kTileK * 16));
   uint32_t aoff[A_CH], boff[B_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
@@ -128,12 +132,17 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
   }
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + NT * i, r = c >> 3, kc = c & 7;
-    boff[i] = (uint32_t)(r * K + kc * 8);
+    const int c = tid + NT * i;
+    if constexpr (F16) {
+      boff[i] = (uint32_t)((c >> 3) * K + (c & 7) * 8);
+    } else {
+      // piece c of a K step: group c / 128, 1 KB block (c / 64) % 2, lane c % 64
+      boff[i] = (uint32_t)((c >> 7) * nchk * (kTileK * 16) + ((c >> 6) & 1) * 512 + (c & 63) * 8);
+    }
   }
   auto gload = [&](int kt, uint4(&ra)[A_CH], uint4(&rb)[B_CH]) {
     const bf16_t* at = Atile + kt * BK;
-    const bf16_t* bt = Btile + kt * BK;
+    const bf16_t* bt = Btile + (size_t)kt * BK * (F16 ? 1 : 16);
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) ra[i] = ld16(at + aoff[i]);
 #pragma unroll
@@ -148,7 +157,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       int c = tid + NT * i;
-      st16(Bs(buf) + (c >> 3) * LDS_ST + (c & 7) * 8, rb[i]);
+      if constexpr (F16)
+        st16(Bs(buf) + (c >> 3) * LDS_ST + (c & 7) * 8, rb[i]);
+      else  // row 16 * group + lane % 16, columns 32 * block + 8 * (lane / 16)
+        st16(Bs(buf) + ((c >> 7) * 16 + (c & 15)) * LDS_ST + ((c >> 6) & 1) * 32 + ((c >> 4) & 3) * 8, rb[i]);
     }
   };
 

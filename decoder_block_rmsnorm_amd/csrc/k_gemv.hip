@@ -34,9 +34,13 @@ constexpr int XST = KC + 8;     // LDS row stride (bf16)
 // c+1 are in flight while chunk c is multiplied.  Program order is chosen for
 // the in-order vmcnt counter: the activations of c+1 are requested before the
 // weights of c+2, so waiting for them never waits for the newer weights.
-template <int NW, int MT>
+//
+// W is in the tiled layout (TILED: each wavefront load instruction reads one
+// contiguous kilobyte) or row-major [N][K].  K slice ksi of ks covers the
+// 256-column chunks [ksi * nchk / ks, (ksi + 1) * nchk / ks).
+template <int NW, int MT, bool TILED>
 __global__ __launch_bounds__(256) void k_gemv_bf16(const bf16_t* __restrict__ X, const bf16_t* __restrict__ W,
-                                                  float* __restrict__ part, int M, int N, int K, int ksl,
+                                                  float* __restrict__ part, int M, int N, int K, int ks,
                                                   float* __restrict__ ss_out) {
   using namespace gv;
   constexpr int ROWS = MT * 16;
@@ -50,8 +54,10 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const bf16_t* __restrict__ X,
   const int l16 = lane & 15, hg = lane >> 4;
   if (tid < ROWS) ssrow[tid] = 0.f;
   const int ksi = blockIdx.y;
-  const int kb = ksi * ksl, ke = min(K, kb + ksl);
-  const int nch = (ke - kb + KC - 1) / KC;
+  const int nchk = (K + KC - 1) / KC;
+  const int c0 = ksi * nchk / ks, c1 = (ksi + 1) * nchk / ks;
+  const int kb = c0 * KC, ke = min(K, c1 * KC);
+  const int nch = c1 - c0;
   const int nrow0 = blockIdx.x * (64 * NW) + wave * (16 * NW);
 
   f32x4 acc[MT][NW];
@@ -66,10 +72,17 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const bf16_t* __restrict__ X,
     const int nkc = min(8, (ke - k0) >> 5);
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
-      const bf16_t* wrow = W + (size_t)(nrow0 + j * 16 + l16) * K + k0 + 8 * hg;
+      if constexpr (TILED) {
+        const bf16_t* t = W + ((size_t)((nrow0 >> 4) + j) * nchk + c0 + c) * (KC * 16) + lane * 8;
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc)
-        if (kc < nkc) w[j][kc] = ld16(wrow + 32 * kc);
+        for (int kc = 0; kc < 8; ++kc)
+          if (kc < nkc) w[j][kc] = ld16(t + 512 * kc);
+      } else {
+        const bf16_t* wrow = W + (size_t)(nrow0 + j * 16 + l16) * K + k0 + 8 * hg;
+#pragma unroll
+        for (int kc = 0; kc < 8; ++kc)
+          if (kc < nkc) w[j][kc] = ld16(wrow + 32 * kc);
+      }
     }
   };
   // piece p of a chunk: row p / 32, 8 columns at 8 * (p % 32); rows >= M and
@@ -152,25 +165,31 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const bf16_t* __restrict__ X,
   }
 }
 
-void launch_gemv_bf16(const bf16_t* X, const bf16_t* W, float* partial, int M, int N, int K, int ks,
-                      float* ss_out, hipStream_t s) {
-  if (M <= 0 || N <= 0) return;
-  const int ksl = K / ks;
+template <bool TILED>
+static void gemv_dispatch(const bf16_t* X, const bf16_t* W, float* partial, int M, int N, int K, int ks,
+                          float* ss_out, hipStream_t s) {
   if (M > 16 && (N % 128) == 0) {
     dim3 grid(N / 128, ks);
     if (M <= 32)
-      hipLaunchKernelGGL((k_gemv_bf16<2, 2>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl, ss_out);
+      hipLaunchKernelGGL((k_gemv_bf16<2, 2, TILED>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ks, ss_out);
     else
-      hipLaunchKernelGGL((k_gemv_bf16<2, 4>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl, ss_out);
+      hipLaunchKernelGGL((k_gemv_bf16<2, 4, TILED>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ks, ss_out);
   } else {
     dim3 grid(N / 64, ks);
     if (M <= 16)
-      hipLaunchKernelGGL((k_gemv_bf16<1, 1>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl, ss_out);
+      hipLaunchKernelGGL((k_gemv_bf16<1, 1, TILED>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ks, ss_out);
     else if (M <= 32)
-      hipLaunchKernelGGL((k_gemv_bf16<1, 2>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl, ss_out);
+      hipLaunchKernelGGL((k_gemv_bf16<1, 2, TILED>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ks, ss_out);
     else
-      hipLaunchKernelGGL((k_gemv_bf16<1, 4>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ksl, ss_out);
+      hipLaunchKernelGGL((k_gemv_bf16<1, 4, TILED>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ks, ss_out);
   }
+}
+
+void launch_gemv_bf16(const bf16_t* X, const bf16_t* W, bool tiled, float* partial, int M, int N, int K, int ks,
+                      float* ss_out, hipStream_t s) {
+  if (M <= 0 || N <= 0) return;
+  if (tiled) gemv_dispatch<true>(X, W, partial, M, N, K, ks, ss_out, s);
+  else gemv_dispatch<false>(X, W, partial, M, N, K, ks, ss_out, s);
 }
 
 // ===========================================================================

@@ -196,24 +196,26 @@ __device__ inline int repack_dst_row(int r, int row0, int ib, int ib_stride, int
   return row0 + (r / ib) * ib_stride + (r % ib);
 }
 
+// tiled != 0: destination in the tiled layout (row-major otherwise)
 template <typename T>
 __global__ __launch_bounds__(256) void k_repack_rows(T* dst, const T* src, int rows, int K, const T* gamma,
-                                                     int row0, int ib, int ib_stride, int perm_d) {
+                                                     int row0, int ib, int ib_stride, int perm_d, int tiled) {
   int r = blockIdx.x;
   int dr = repack_dst_row(r, row0, ib, ib_stride, perm_d);
+  const int nchk = tiled_chunks(K);
   for (int c = threadIdx.x; c < K; c += 256) {
     float v = Elt<T>::load(src, (size_t)r * K + c);
     if (gamma) v *= Elt<T>::load(gamma, c);
-    Elt<T>::store(dst, (size_t)dr * K + c, v);
+    Elt<T>::store(dst, tiled ? tiled_off(dr, c, nchk) : (size_t)dr * K + c, v);
   }
 }
 
 template <typename T>
 void launch_repack_rows(T* dst, const T* src, int rows, int K, const T* gamma, int row0, int ib, int ib_stride,
-                        int perm_d, hipStream_t s) {
+                        int perm_d, int tiled, hipStream_t s) {
   if (rows <= 0) return;
   hipLaunchKernelGGL(k_repack_rows<T>, dim3(rows), dim3(256), 0, s, dst, src, rows, K, gamma, row0, ib,
-                     ib_stride, perm_d);
+                     ib_stride, perm_d, tiled);
 }
 
 __global__ __launch_bounds__(256) void k_repack_bytes(uint8_t* dst, const uint8_t* src, int rows, int rb,
@@ -308,7 +310,7 @@ void launch_emit(const int32_t* cur_id, int32_t* ids_out, int32_t* cursor, const
   template void launch_embed<T>(const T*, int, int, const int32_t*, int, T*, hipStream_t);          \
   template void launch_kv_write<T>(KVView, int, int, int, const T*, const T*, hipStream_t);         \
   template void launch_kv_read<T>(KVView, int, int, int, T*, T*, hipStream_t);                      \
-  template void launch_repack_rows<T>(T*, const T*, int, int, const T*, int, int, int, int, hipStream_t); \
+  template void launch_repack_rows<T>(T*, const T*, int, int, const T*, int, int, int, int, int, hipStream_t); \
   template void launch_to_f32<T>(const T*, float*, int, hipStream_t);
 INST(float)
 INST(bf16_t)

@@ -44,7 +44,7 @@ void launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
 // gamma (optional, length K) scales the columns (norm weight folding).
 template <typename T>
 void launch_repack_rows(T* dst, const T* src, int rows, int K, const T* gamma, int row0, int ib,
-                        int ib_stride, int perm_d, hipStream_t s);
+                        int ib_stride, int perm_d, int tiled, hipStream_t s);
 void launch_repack_bytes(uint8_t* dst, const uint8_t* src, int rows, int row_bytes, int row0, int ib,
                          int ib_stride, int perm_d, hipStream_t s);
 // dense fp16 [N, K] = (scale * code + bias) * gamma_k (gamma may be null)
@@ -95,9 +95,11 @@ constexpr int kMaxSplitK = 4;
 int gemm_split_k(int M, int N, int K);
 
 // ---------------------------------------------------------------- k_gemv.hip
-// partial[ks][M][N] (fp32) = X[M, kslice] * W[N, kslice]^T (bf16, M <= 64).
+// partial[ks][M][N] (fp32) = X[M, kslice] * W[N, kslice]^T (bf16, M <= 64),
+// W tiled (tiled_off) or row-major; slice s = 256-column chunks
+// [s * nchk / ks, (s + 1) * nchk / ks), nchk = tiled_chunks(K).
 // ss_out (optional): sum of squares of each X row over each K slice, [ks][M].
-void launch_gemv_bf16(const bf16_t* X, const bf16_t* W, float* partial, int M, int N, int K, int ks,
+void launch_gemv_bf16(const bf16_t* X, const bf16_t* W, bool tiled, float* partial, int M, int N, int K, int ks,
                       float* ss_out, hipStream_t s);
 // y[M][N] (fp32) = xhat W^T, W 4-bit group affine, xhat = x * r * gamma, M <= 4.
 // norm: 0 = no RMSNorm (r = 1, gamma unused), 1 = r from the row itself (eps),
