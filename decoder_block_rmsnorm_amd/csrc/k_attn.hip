@@ -292,12 +292,15 @@ void launch_attn_prefill_bf16(const bf16_t* q, KVView kv, int B, int L, int H, i
 // 4*t + i.  Those 8 probabilities are then directly the B operand of the P.V
 // MFMA, and the matching V^T operand is one 16-byte load of 8 consecutive
 // slots of a transposed V page row.
-__global__ __launch_bounds__(256) void k_attn_decode_bf16(const bf16_t* __restrict__ q, KVView kv, int B, int H,
-                                                         int G, int n_splits, int split_len,
-                                                         float* __restrict__ part_o, float* __restrict__ part_ml) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+// two wavefronts per SIMD: the register budget of one 64-key step (K, V, P, O)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_decode_bf16(
+    const bf16_t* __restrict__ q, KVView kv, int B, int H, int G, int n_splits, int split_len,
+    float* __restrict__ part_o, float* __restrict__ part_ml) {
+  const int lane = threadIdx.x & 63;
   const int l16 = lane & 15, hg = lane >> 4;
-  const int wid = blockIdx.x * 4 + wave;
+  // wave-uniform indices in scalar registers: the lens and block-table reads are
+  // scalar loads, counted apart from the vector loads in flight
+  const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   const int total = B * G * n_splits;
   if (wid >= total) return;
   const int c = wid % n_splits;

@@ -9,9 +9,19 @@
 
 namespace lb {
 
+// slices summed in order; loads issued four at a time
 __device__ inline float sum_parts(const float* part, int ks, size_t stride, size_t idx) {
   float v = 0.f;
-  for (int s = 0; s < ks; ++s) v += part[(size_t)s * stride + idx];
+  int s = 0;
+  for (; s + 4 <= ks; s += 4) {
+    const float a = part[(size_t)s * stride + idx], b = part[(size_t)(s + 1) * stride + idx];
+    const float c = part[(size_t)(s + 2) * stride + idx], e = part[(size_t)(s + 3) * stride + idx];
+    v += a;
+    v += b;
+    v += c;
+    v += e;
+  }
+  for (; s < ks; ++s) v += part[(size_t)s * stride + idx];
   return v;
 }
 
@@ -30,11 +40,11 @@ __global__ __launch_bounds__(64) void k_epi_qkv(const float* part, int ks, int M
   int head = blockIdx.y;          // 0..H-1 q, H..H+G-1 k, then v
   int d = kv.d, half = d >> 1;
   int i = threadIdx.x;
+  float r = stat.get_block(m);
   if (i >= half) return;
   int N = Nq + 2 * Nkv;
   size_t stride = (size_t)M * N;
   int c0 = head * d;
-  float r = stat.get(m);
   float a = sum_parts(part, ks, stride, (size_t)m * N + c0 + i) * r;
   float b = sum_parts(part, ks, stride, (size_t)m * N + c0 + i + half) * r;
   int bseq = m / L, l = m % L;
@@ -126,11 +136,11 @@ __global__ __launch_bounds__(256) void k_epi_swiglu(const float* part, int ks, i
   int m = blockIdx.y;
   int F = F2 >> 1;
   int j = blockIdx.x * 256 + threadIdx.x;
+  float r = stat.get_block(m);
   if (j >= F) return;
   size_t stride = (size_t)M * F2;
   int jb = j / ib, w = j % ib;
   int cg = jb * 2 * ib + w;
-  float r = stat.get(m);
   float a = sum_parts(part, ks, stride, (size_t)m * F2 + cg) * r;
   float b = sum_parts(part, ks, stride, (size_t)m * F2 + cg + ib) * r;
   Elt<T>::store(g_out, (size_t)m * F + j, silu_f(a) * b);

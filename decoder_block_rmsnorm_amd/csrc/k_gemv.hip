@@ -221,7 +221,7 @@ __global__ __launch_bounds__(1024) void k_q4_prep(const bf16_t* X, int norm, Row
     for (int w = 0; w < 16; ++w) tot += red[w];
     r = 1.0f / sqrtf(tot / (float)K + eps);
   } else if (norm == 2) {
-    r = stat.get(m);
+    r = stat.get_block(m);
   }
   for (int chunk = wave; chunk < K / 32; chunk += 16) {
     float x = 0.f, h = 0.f;

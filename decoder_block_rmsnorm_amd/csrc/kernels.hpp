@@ -12,12 +12,25 @@ struct RowStat {
   const float* ss = nullptr;
   int nb = 0, M = 0, n = 1;
   float eps = 0.f;
-  __device__ inline float get(int m) const {
-    if (inv) return inv[m];
-    if (!ss) return 1.0f;
-    float t = 0.f;
-    for (int j = 0; j < nb; ++j) t += ss[(size_t)j * M + m];
-    return 1.0f / sqrtf(t / (float)n + eps);
+  // 1/rms of row m, computed by the first wavefront of the block (its lanes
+  // sum the nb partials) and shared: every thread of the block must call it,
+  // with the same m, before any thread leaves.
+  __device__ inline float get_block(int m) const {
+    __shared__ float s_r;
+    if (threadIdx.x < 64) {
+      float v = 1.0f;
+      if (inv) {
+        v = inv[m];
+      } else if (ss) {
+        float t = 0.f;
+        for (int j = threadIdx.x; j < nb; j += 64) t += ss[(size_t)j * M + m];
+        t = warp_sum(t);
+        v = 1.0f / sqrtf(t / (float)n + eps);
+      }
+      if (threadIdx.x == 0) s_r = v;
+    }
+    __syncthreads();
+    return s_r;
   }
 };
 
