@@ -51,59 +51,85 @@ def _setup(wl, max_seq, n_layers):
     return inp, blk, cache
 
 
+def _phase_table(names, ph_ms, ncalls, extra=None):
+    out = {}
+    for i, (name, ms) in enumerate(zip(names, ph_ms)):
+        out[name] = {"avg_us": round(ms / max(ncalls, 1) * 1e3, 2)}
+        if extra:
+            out[name].update(extra(i, ms / max(ncalls, 1)))
+    return out
+
+
 def bench_prefill(wl, steps, warmup):
+    """Prefill: the timed region is `steps` back-to-back calls bracketed by two
+    events; the dominant kernel (the w1/w3 GEMM) is timed inside it by events
+    attached to its own launches.  The per-phase breakdown comes from a separate
+    untimed pass with an event at every phase boundary."""
     import torch
     import workloads as W
     from tests import gpu_util as G
     s, B, Lq = wl.shape, wl.batch, wl.seq_len
     # one cache layer per call so that every call starts from an empty cache
-    inp, blk, cache = _setup(wl, Lq, steps + warmup)
+    inp, blk, cache = _setup(wl, Lq, warmup + 2 * steps)
     sc = G.scratch(blk, B * Lq, B, Lq)
     x = G.tdev(inp["x"].reshape(B * Lq, s.dim), s.dtype)
     y = torch.empty_like(x)
-    for i in range(warmup):
-        blk.prefill(cache, i, x, y, B, Lq, sc)
-    torch.cuda.synchronize()
-    # timed region: the calls back to back, the library's timing-only events at
-    # every phase boundary on the stream it launches on
-    blk.profile_start(steps)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(steps):
-        blk.prefill(cache, warmup + i, x, y, B, Lq, sc)
-    e1.record()
-    torch.cuda.synchronize()
-    total_ms = e0.elapsed_time(e1)
-    ph_ms, ncalls = blk.profile_read()
+    layer = 0
+    for _ in range(warmup):
+        blk.prefill(cache, layer, x, y, B, Lq, sc)
+        layer += 1
     flops = W.prefill_flops(s, B, Lq)
     lin = W.linear_flops(s, B * Lq)
     attn_flops = flops - sum(lin.values())
     ph_flops = [0.0, lin["qkv"], attn_flops, lin["wo"], 0.0, lin["w13"], lin["w2"]]
-    phases = {}
-    for name, ms, fl in zip(PREFILL_PHASES, ph_ms, ph_flops):
-        avg = ms / max(ncalls, 1)
-        phases[name] = {"avg_us": round(avg * 1e3, 2),
-                        "tflops": round(fl / (avg * 1e-3) / 1e12, 1) if fl and avg > 0 else None}
-    dom = max(range(len(ph_ms)), key=lambda i: ph_ms[i])
-    avg_dom = ph_ms[dom] / ncalls * 1e-3
+    # breakdown pass
+    torch.cuda.synchronize()
+    blk.profile_start(steps)
+    for _ in range(steps):
+        blk.prefill(cache, layer, x, y, B, Lq, sc)
+        layer += 1
+    ph_ms, ncalls = blk.profile_read()
+
+    def tf(i, avg_ms):
+        return {"tflops": round(ph_flops[i] / (avg_ms * 1e-3) / 1e12, 1) if ph_flops[i] and avg_ms > 0 else None}
+    phases = _phase_table(PREFILL_PHASES, ph_ms, ncalls, tf)
+    # timed region
+    dom = PREFILL_PHASES.index("w13_gemm_swiglu")
+    blk.profile_start(steps, phases=[dom])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        blk.prefill(cache, layer, x, y, B, Lq, sc)
+        layer += 1
+    e1.record()
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    dom_ms, dcalls = blk.profile_read()
+    avg_dom = dom_ms[dom] / dcalls * 1e-3
     achieved = ph_flops[dom] / avg_dom / 1e12
     ms = total_ms / steps
     return {
         "ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12, "tokens_per_s": B * Lq / (ms * 1e-3),
         "flops_per_step": flops, "phases": phases,
-        "roofline": {"kernel": PREFILL_PHASES[dom], "bound": "mfma", "achieved": round(achieved, 1),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "flops_per_launch": ph_flops[dom], "avg_launch_us": round(avg_dom * 1e6, 2)},
+        "roofline": {"kernel": "k_gemm_mfma (w1/w3 + SwiGLU epilogue)", "bound": "mfma",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": ph_flops[dom], "avg_launch_us": round(avg_dom * 1e6, 2)},
     }
 
 
 def bench_decode(wl, steps, warmup):
+    """Decode: every step reads 512 MB first (more than the 256 MB last-level
+    cache, and a read leaves no dirty lines) so no weight or cache byte is served
+    from it.  Step time = (time of `steps` x [flush, decode] - time of `steps` x
+    [flush]) / steps, each loop bracketed by two events; the attention kernels
+    are timed inside the first loop by events attached to their launches."""
     import torch
     import workloads as W
     from tests import gpu_util as G
     s, B, S0 = wl.shape, wl.batch, wl.cache_len
-    max_seq = S0 + warmup + steps + 1
+    max_seq = S0 + warmup + 2 * steps + 1
     inp, blk, cache = _setup(wl, max_seq, 1)
     for b in range(B):
         cache.write(0, b, 0, G.tdev(inp["k_cache"][b], s.dtype), G.tdev(inp["v_cache"][b], s.dtype))
@@ -112,40 +138,56 @@ def bench_decode(wl, steps, warmup):
     sc = G.scratch(blk, B, B, max_seq)
     x = G.tdev(inp["x"].reshape(B, s.dim), s.dtype)
     y = torch.empty_like(x)
-    # 512 MB read between steps (more than the 256 MB last-level cache) so that no
-    # weight or cache byte is served from it; a read leaves no dirty lines behind
     flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
     for _ in range(warmup):
-        blk.decode(cache, 0, x, y, B, sc)
-    torch.cuda.synchronize()
-    # timed region: each step is bracketed by the library's timing-only events
-    # (first and last phase boundary of the call) on the stream it launches on
-    blk.profile_start(steps)
-    for i in range(steps):
         flush.sum()
         blk.decode(cache, 0, x, y, B, sc)
     torch.cuda.synchronize()
+    # breakdown pass (events at every phase boundary)
+    blk.profile_start(steps)
+    for _ in range(steps):
+        flush.sum()
+        blk.decode(cache, 0, x, y, B, sc)
     ph_ms, ncalls = blk.profile_read()
-    byts = [W.decode_bytes(s, B, S0 + warmup + i) for i in range(steps)]
-    ms = sum(ph_ms) / ncalls
+    lens0 = S0 + warmup + steps
+    att = DECODE_PHASES.index("attention_decode")
+    blk.profile_start(steps, phases=[att])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(steps):
+        flush.sum()
+        blk.decode(cache, 0, x, y, B, sc)
+    ev[1].record()
+    for _ in range(steps):
+        flush.sum()
+    ev[2].record()
+    torch.cuda.synchronize()
+    t_loop, t_flush = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
+    att_ms, acalls = blk.profile_read()
+    ms = (t_loop - t_flush) / steps
+    byts = [W.decode_bytes(s, B, lens0 + i) for i in range(steps)]
     tot_bytes = sum(b["total"] for b in byts) / steps
     kv_bytes = sum(b["kv_read"] + b["kv_write"] for b in byts) / steps
-    attn_us = ph_ms[2] / ncalls * 1e3
-    phases = {n: {"avg_us": round(v / ncalls * 1e3, 2)} for n, v in zip(DECODE_PHASES, ph_ms)}
-    w_phase = {"qkv_gemv_and_x_stats": 0, "wo_gemv": 3, "w13_gemv": 5, "w2_gemv": 7}
-    lb = {"qkv_gemv_and_x_stats": s.dim * (s.n_heads + 2 * s.n_kv_heads) * s.head_dim,
-          "wo_gemv": s.n_heads * s.head_dim * s.dim, "w13_gemv": 2 * s.dim * s.ffn_dim, "w2_gemv": s.ffn_dim * s.dim}
+    attn_us = att_ms[att] / acalls * 1e3
+    lb = {0: s.dim * (s.n_heads + 2 * s.n_kv_heads) * s.head_dim, 3: s.n_heads * s.head_dim * s.dim,
+          5: 2 * s.dim * s.ffn_dim, 7: s.ffn_dim * s.dim}
     esz = 2 if s.dtype == "bf16" else 4
-    for n, i in w_phase.items():
-        us = ph_ms[i] / ncalls * 1e3
-        phases[n]["gbs"] = round(lb[n] * esz / (us * 1e-6) / 1e9, 1)
-    phases["attention_decode"]["gbs"] = round(kv_bytes / (attn_us * 1e-6) / 1e9, 1)
+
+    def gbs(i, avg_ms):
+        if i in lb:
+            return {"gbs": round(lb[i] * esz / (avg_ms * 1e-3) / 1e9, 1)}
+        if i == att:
+            return {"gbs": round(kv_bytes / (avg_ms * 1e-3) / 1e9, 1)}
+        return {}
+    phases = _phase_table(DECODE_PHASES, ph_ms, ncalls, gbs)
     achieved = kv_bytes / (attn_us * 1e-6) / 1e9
     return {
         "workload": wl.name, "batch": B, "cache_len": S0, "us_per_step": round(ms * 1e3, 2),
         "tokens_per_s": round(B / (ms * 1e-3), 1), "bytes_per_step": tot_bytes,
-        "hbm_frac_step": round(tot_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "phases": phases,
-        "roofline": {"kernel": "attention_decode", "bound": "hbm", "achieved": round(achieved, 1),
+        "hbm_frac_step": round(tot_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "phases_sum_us": round(sum(ph_ms) / ncalls * 1e3, 2), "phases": phases,
+        "roofline": {"kernel": "k_attn_decode_bf16 + k_attn_merge", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": None, "bytes_per_launch": kv_bytes, "avg_launch_us": round(attn_us, 2)},
     }

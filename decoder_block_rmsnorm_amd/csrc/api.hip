@@ -12,6 +12,10 @@
 
 using namespace lb;
 
+namespace lb {
+thread_local LaunchClock g_clock;
+}  // namespace lb
+
 // ---------------------------------------------------------------- errors
 static thread_local std::string g_err;
 
@@ -123,12 +127,21 @@ static const int kMaxMarks = 12;
 // Records an event before the first kernel and after each phase of one call.
 // Phase boundary b (before phase b, after phase b-1) gets an event only when
 // one of those two phases is timed.
+//
+// clocked >= 0: the single timed phase is timed by events attached to its own
+// kernel launches (g_clock) instead of marker packets.
 struct Marker {
   hipEvent_t* ev = nullptr;
   uint32_t mask = 0;
   int i = 0;
+  int clocked = -1;
   void operator()(hipStream_t s) {
     if (!ev || i >= kMaxMarks) return;
+    if (clocked >= 0) {
+      g_clock = i == clocked ? LaunchClock{ev[i], ev[i + 1]} : LaunchClock{};
+      ++i;
+      return;
+    }
     const bool need = mask == 0 || ((mask >> i) & 1u) || (i > 0 && ((mask >> (i - 1)) & 1u));
     if (need) (void)hipEventRecord(ev[i], s);
     ++i;
@@ -824,6 +837,10 @@ static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const
   if (blk->prof_calls < blk->prof_max) {
     mk.ev = &blk->ev[(size_t)(blk->prof_calls++) * kMaxMarks];
     mk.mask = blk->prof_mask;
+    // phases whose kernels take launch-attached events: the w1/w3 GEMM of the
+    // bf16 prefill (phase 5) and the decode attention (phase 2)
+    const uint32_t clockable = !d.bf16 ? 0u : decode ? (1u << 2) : (1u << 5);
+    if (mk.mask != 0 && (mk.mask & (mk.mask - 1)) == 0 && (mk.mask & clockable)) mk.clocked = __builtin_ctz(mk.mask);
   }
   if (!d.bf16) {
     fp32_path<float>(blk, kv, x, y, batch, L, sc, S, mk, s);
@@ -833,6 +850,7 @@ static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const
     bf16_decode(blk, kv, x, y, batch, sc, S, n_splits_override > 0 ? n_splits_override : S.n_splits, mk, s);
   }
   if (mk.ev) blk->prof_marks = mk.i;
+  g_clock = LaunchClock{};
   st = hip_check(decode ? "block decode" : "block prefill");
   if (st != LLAMA_OK) return st;
   for (int b = 0; b < batch; ++b) c->lens_host[(size_t)layer * c->cfg.max_batch + b] += L;

@@ -1,5 +1,6 @@
 // Shared device/host definitions for the gfx950 decoder-block kernels.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -487,10 +487,12 @@ void launch_attn_decode_bf16(const bf16_t* q, KVView kv, int B, int H, int G, in
                              float* part_o, float* part_ml, bf16_t* out, hipStream_t s) {
   if (B <= 0) return;
   int waves = B * G * n_splits;
-  hipLaunchKernelGGL(k_attn_decode_bf16, dim3((waves + 3) / 4), dim3(256), 0, s, q, kv, B, H, G, n_splits,
+  hipExtLaunchKernelGGL(k_attn_decode_bf16, dim3((waves + 3) / 4), dim3(256), 0, s, g_clock.start, nullptr, 0, q, kv, B, H, G, n_splits,
                      split_len, part_o, part_ml);
   int bh = B * H;
-  hipLaunchKernelGGL(k_attn_merge, dim3((bh + 3) / 4), dim3(256), 0, s, part_o, part_ml, bh, n_splits, out);
+  hipExtLaunchKernelGGL(k_attn_merge, dim3((bh + 3) / 4), dim3(256), 0, s, nullptr, g_clock.stop, 0, part_o, part_ml,
+                        bh, n_splits, out);
+  g_clock = LaunchClock{};
 }
 
 }  // namespace lb

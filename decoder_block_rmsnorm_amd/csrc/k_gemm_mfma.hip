@@ -402,7 +402,9 @@ static void launch_cfg(const GemmArgs& a, hipStream_t s) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, DEPTH, EPI, F16>), dim3(tiles), dim3(NW * 64), lds, s, a);
+  hipExtLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, DEPTH, EPI, F16>), dim3(tiles), dim3(NW * 64), lds, s,
+                        g_clock.start, g_clock.stop, 0, a);
+  g_clock = LaunchClock{};
 }
 
 // Tile choice; LLAMA_BLOCK_GEMM_TILE = "256x256w8", "256x256w4", "128x256w4" or

@@ -34,6 +34,16 @@ struct RowStat {
   }
 };
 
+// Launch-attached timing events (profiling aid).  When set, the prefill GEMM
+// launch records `start` and `stop` in its own dispatch, and the decode
+// attention records `start` with its main kernel and `stop` with its merge
+// kernel; each launcher clears what it used.  No extra stream packets, so the
+// timed phase adds no gap to the stream.
+struct LaunchClock {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchClock g_clock;
+
 // ---------------------------------------------------------------- k_misc.hip
 // inv_rms[r] = 1 / sqrt(mean(x[r,:]^2) + eps) for rows of x [rows, D].
 template <typename T>
