@@ -30,6 +30,28 @@ constexpr int LDS_ST = BK + 8;  // bf16 per LDS row
 constexpr int GROUP_M = 8;
 }  // namespace gm
 
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt with only the vector-memory counter constrained (vmcnt <= n)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at LDS byte address lds_addr + 16 l (lds_addr wave-uniform, passed in M0).
+// Written as inline asm so that the compiler, which cannot tell the stages of
+// the ring apart, does not make every LDS read wait for every load in flight;
+// the kernel waits on the vector-memory counter itself (wait_vmcnt) before the
+// barrier that publishes a stage.  The instruction has no register result: its
+// address registers are read at issue.  M0 is set in the same statement.
+// Address = sbase (wave-uniform, scalar registers) + voff (per lane, 32-bit).
+__device__ __forceinline__ void lds_dma16(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E), so that
 // accumulator registers are always indexed by constants (a runtime index would
 // push the accumulator array to scratch memory).
@@ -70,7 +92,9 @@ __device__ inline f16x8 u4_as_f16x8(uint4 v) {
 }
 
 // NW wavefronts per block (4 or 8), DEPTH K steps of global loads in flight
-// (1 or 2 register sets).
+// (1 or 2 register sets).  DEPTH 0 (bf16 tiled B, 256 x 256, 4 wavefronts):
+// global -> LDS direct loads (global_load_lds_dwordx4) into a four-stage ring of
+// 32-wide K steps, no register staging; see the main loop below.
 template <int BM, int BN, int NW, int DEPTH, int EPI, bool F16>
 __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
   using namespace gm;
@@ -223,8 +247,145 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
 
   // LDS buffer b is rewritten two steps after it was read; the barrier of the
   // step in between guarantees every wavefront has finished reading it.
-  const int KT = Kslice / BK;
-  if constexpr (DEPTH == 2) {
+  if constexpr (DEPTH == 0 || DEPTH == 3 || DEPTH == 4) {
+    // Direct-to-LDS ring (DEPTH 0: 32-wide K steps in 4 stages; DEPTH 3:
+    // 64-wide K steps in 2 stages).  A stage holds the A and B tiles of one K
+    // step as 16-row x 32-column blocks of 1 KB in the tiled weight format
+    // (piece 16*j + r = row r of the group, columns 8j .. 8j+7), block (kb, g)
+    // at (kb * 16 + g) KB: every direct load instruction of a wavefront fills
+    // one contiguous kilobyte (lane l -> piece l), and every 16-lane phase of a
+    // fragment read touches 256 contiguous bytes (no bank conflicts).  Each
+    // wavefront loads 4 row groups of A and of B per 32 columns of the step.
+    //
+    // Schedule of step kt, sub-steps kk of 16 (fragments of kk = 0 already in
+    // registers): read the fragments of kk+1, then the MFMAs of kk; before the
+    // MFMAs of the last sub-step: wait for this wavefront's loads of step kt+1,
+    // barrier (all loads of kt+1 landed, every wavefront done reading stage
+    // kt), refill stage kt with step kt+STG, read the kk = 0 fragments of step
+    // kt+1.  The matrix cores stay busy across the barrier.
+    constexpr int BKS = DEPTH == 3 ? 64 : 32;          // K step
+    constexpr int STG = DEPTH == 0 ? 4 : DEPTH == 3 ? 2 : 5;   // stages
+    constexpr int NKB = BKS / 32;                      // 32-column blocks per step
+    constexpr int NKK = BKS / 16;                      // MFMA sub-steps per step
+    constexpr int LPS = 8 * NKB;                       // direct loads per wavefront per step
+    static_assert(!F16 && NW == 4 && BM == 256 && BN == 256, "direct-LDS configuration");
+    constexpr int SA = BM * BKS, SB = BN * BKS;        // bf16 per stage
+    const int KT = Kslice / BKS;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int r16 = lane & 15, j4 = lane >> 4;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)(char*)lds);
+    // Per-lane byte offsets (32-bit: the host keeps A below 4 GB) from the
+    // slice bases: A rows of this lane's pieces (clamped: rows past M load row
+    // M-1, whose results are never stored), B pieces of this lane's groups.
+    uint32_t voa[4], vob[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      voa[i] = (uint32_t)(min(m0 + 16 * (wv * 4 + i) + r16, M - 1) * K + 8 * j4) * 2;
+      vob[i] = (uint32_t)(((wv * 4 + i) * nchk * (kTileK * 16) + lane * 8) * 2);
+    }
+    const char* abase = (const char*)Ag;
+    const char* bbase = (const char*)Btile;
+    // direct load number idx (0 .. LPS-1) of step kt: 32-column block idx / 8,
+    // row group wv * 4 + (idx % 8) / 2, A (even idx) or B (odd idx)
+    auto issue_one = [&](int kt, int idx) {
+      const uint32_t la = lds_base + (uint32_t)((kt % STG) * (SA + SB)) * 2;
+      const int kb = idx >> 3, i = (idx & 7) >> 1, g = wv * 4 + i;
+      if ((idx & 1) == 0)
+        lds_dma16(voa[i], abase + (size_t)(kt * BKS + kb * 32) * 2, la + (kb * 16 + g) * 1024);
+      else
+        lds_dma16(vob[i], bbase + (size_t)(kt * NKB + kb) * 1024, la + SA * 2 + (kb * 16 + g) * 1024);
+    };
+    // lane's piece inside a pair of groups: fragment rows 32t + l%32, k = 8*(l/32)
+    const int fpiece = (16 * (lane >> 5) + r16) * 8 + ((lane >> 4) & 1) * 512;
+    // fragment read number q (0 .. MI+3): A tile q, or B tile q - MI
+    auto lfrag_one = [&](int st, int kk, int q, uint4(&a_)[MI], uint4(&b_)[4]) {
+      const bf16_t* la = lds + st * (SA + SB) + fpiece + (kk >> 1) * 16 * 512 + (kk & 1) * 256;
+      if (q < MI) a_[q] = ld16(la + (wm * (WTM / 16) + 2 * q) * 512);
+      else b_[q - MI] = ld16(la + SA + (wn * 8 + 2 * (q - MI)) * 512);
+    };
+    // wait until this wavefront's loads of step t have landed, given the steps
+    // issued up to step `last`
+    auto wait_step = [&](int t, int last) {
+      const int later = max(0, min(STG - 1, last - t));
+      if constexpr (STG > 4) {
+        if (later >= 4) return wait_vmcnt<4 * LPS>();
+      }
+      if constexpr (STG > 3) {
+        if (later >= 3) return wait_vmcnt<3 * LPS>();
+      }
+      if constexpr (STG > 2) {
+        if (later >= 2) return wait_vmcnt<2 * LPS>();
+      }
+      if (later >= 1) return wait_vmcnt<LPS>();
+      wait_vmcnt<0>();
+    };
+    constexpr int NF = MI + 4;                 // fragment reads per sub-step
+    constexpr int NM = MI * 4;                 // MFMAs per sub-step
+    static_assert(NM >= NF, "interleave slots");
+    // The MFMAs of one sub-step, with one other instruction slotted in after
+    // each: while an MFMA runs the wavefront issues the next load, so the
+    // matrix core is never left waiting on an issue.
+    auto mfmas_with = [&](const uint4(&a_)[MI], const uint4(&b_)[4], auto&& slot) {
+      static_for<0, NM>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        acc[q / 4][q % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_as_bf16x8(a_[q / 4]), u4_as_bf16x8(b_[q % 4]),
+                                                                    acc[q / 4][q % 4], 0, 0, 0);
+        slot(q);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    uint4 fa[2][MI], fb[2][4];
+#pragma unroll
+    for (int t = 0; t < STG; ++t)
+      if (t < KT) {
+#pragma unroll
+        for (int idx = 0; idx < LPS; ++idx) issue_one(t, idx);
+      }
+    int last = min(STG, KT) - 1;
+    wait_step(0, last);
+    asm volatile("s_barrier" ::: "memory");
+    // nothing but LDS reads may be pending on the lgkm counter inside the loop
+    // (a scalar load in flight would force every fragment wait to lgkmcnt(0))
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    for (int q = 0; q < NF; ++q) lfrag_one(0, 0, q, fa[0], fb[0]);
+    for (int kt = 0; kt < KT; ++kt) {
+      const int st = kt % STG;
+      static_for<0, NKK>([&](auto kc) {
+        constexpr int kk = decltype(kc)::value;
+        constexpr int cur = kk & 1;
+        // this sub-step's fragments were read during the previous one
+        __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kk + 1 < NKK) {
+          mfmas_with(fa[cur], fb[cur], [&](int slot) {
+            if (slot < NF) lfrag_one(st, kk + 1, slot, fa[cur ^ 1], fb[cur ^ 1]);
+          });
+        } else {
+          // (after the last step this waits for nothing and reads an unused
+          // stage; kept unconditional so the reads stay in one straight line)
+          wait_step(kt + 1, last);
+          // this stage's fragment reads are complete (waited above); barrier:
+          // every wavefront is done with stage st, and step kt+1 has landed
+          asm volatile("s_barrier" ::: "memory");
+          const bool refill = kt + STG < KT;
+          const int nxt = (kt + 1) % STG;
+          __builtin_amdgcn_sched_barrier(0);
+          // slots: fragment reads of step kt+1 first (needed soonest), then the
+          // direct loads of step kt+STG into stage st
+          mfmas_with(fa[cur], fb[cur], [&](int slot) {
+            if (slot < NF) lfrag_one(nxt, 0, slot, fa[cur ^ 1], fb[cur ^ 1]);
+            else if (refill && slot - NF < LPS) issue_one(kt + STG, slot - NF);
+          });
+          if (refill) {
+#pragma unroll
+            for (int idx = NM - NF; idx < LPS; ++idx) issue_one(kt + STG, idx);
+            last = kt + STG;
+          }
+        }
+      });
+    }
+  } else if constexpr (DEPTH == 2) {
+    const int KT = Kslice / BK;
     gload(0, ra0, rb0);
     if (KT > 1) gload(1, ra1, rb1);
     for (int kt = 0; kt < KT; kt += 2) {
@@ -240,6 +401,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
       }
     }
   } else {
+    const int KT = Kslice / BK;
     gload(0, ra0, rb0);
     for (int kt = 0; kt < KT; ++kt) {
       const int buf = kt & 1;
@@ -395,7 +557,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
 template <int BM, int BN, int NW, int DEPTH, int EPI, bool F16>
 static void launch_cfg(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * (a.N / BN) * (EPI == EPI_F32 && a.ksplit > 1 ? a.ksplit : 1);
-  const size_t lds = (size_t)2 * (BM + BN) * gm::LDS_ST * sizeof(bf16_t);
+  const size_t lds = DEPTH == 4 ? (size_t)(BM + BN) * 160 * sizeof(bf16_t)
+                     : DEPTH == 0 || DEPTH == 3 ? (size_t)(BM + BN) * 128 * sizeof(bf16_t)
+                                : (size_t)2 * (BM + BN) * gm::LDS_ST * sizeof(bf16_t);
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void*)k_gemm_mfma<BM, BN, NW, DEPTH, EPI, F16>,
@@ -407,8 +571,8 @@ static void launch_cfg(const GemmArgs& a, hipStream_t s) {
   g_clock = LaunchClock{};
 }
 
-// Tile choice; LLAMA_BLOCK_GEMM_TILE = "256x256w8", "256x256w4", "128x256w4" or
-// "128x128w4" forces one (for measurements).
+// Tile choice; LLAMA_BLOCK_GEMM_TILE = "256x256d" (direct-to-LDS), "256x256w8",
+// "256x256w4", "128x256w4" or "128x128w4" forces one (for measurements).
 static int forced_tile() {
   static int v = -1;
   if (v < 0) {
@@ -419,6 +583,9 @@ static int forced_tile() {
       else if (!strcmp(e, "256x256w4")) v = 2;
       else if (!strcmp(e, "128x256w4")) v = 3;
       else if (!strcmp(e, "128x128w4")) v = 4;
+      else if (!strcmp(e, "256x256d")) v = 5;
+      else if (!strcmp(e, "256x256d64")) v = 6;
+      else if (!strcmp(e, "256x256d5")) v = 7;
     }
   }
   return v;
@@ -428,6 +595,14 @@ template <int EPI, bool F16>
 static void launch_epi(const GemmArgs& a, hipStream_t s) {
   const bool n256 = (a.N % 256) == 0;
   const int f = forced_tile();
+  if constexpr (!F16) {
+    // direct-to-LDS tiles address A with 32-bit per-lane byte offsets
+    const bool a32 = (size_t)a.M * a.K * sizeof(bf16_t) < ((size_t)1 << 32);
+    const bool big = a32 && n256 && (EPI == EPI_F32 && a.ksplit > 1 || ((a.M + 255) / 256) * (a.N / 256) >= 240);
+    if (f == 6 && big) return launch_cfg<256, 256, 4, 3, EPI, F16>(a, s);
+    if (f == 7 && big) return launch_cfg<256, 256, 4, 4, EPI, F16>(a, s);
+    if ((f == 0 || f == 5) && big) return launch_cfg<256, 256, 4, 0, EPI, F16>(a, s);
+  }
   if (EPI == EPI_F32 && a.ksplit > 1) return launch_cfg<256, 256, 8, 2, EPI, F16>(a, s);
   if (f == 1 && n256) return launch_cfg<256, 256, 8, 2, EPI, F16>(a, s);
   if (f == 2 && n256) return launch_cfg<256, 256, 4, 1, EPI, F16>(a, s);
