@@ -51,6 +51,11 @@ def _setup(wl, max_seq, n_layers):
     return inp, blk, cache
 
 
+def _traffic_bytes(kernel):
+    t = recorded_traffic(kernel)
+    return None if t is None else t["bytes"]
+
+
 def _phase_table(names, ph_ms, ncalls, extra=None):
     out = {}
     for i, (name, ms) in enumerate(zip(names, ph_ms)):
@@ -114,7 +119,8 @@ def bench_prefill(wl, steps, warmup):
         "flops_per_step": flops, "phases": phases,
         "roofline": {"kernel": "k_gemm_mfma (w1/w3 + SwiGLU epilogue)", "bound": "mfma",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic_bytes(f"prefill_w13:{wl.name}"),
                      "flops_per_launch": ph_flops[dom], "avg_launch_us": round(avg_dom * 1e6, 2)},
     }
 
@@ -189,14 +195,15 @@ def bench_decode(wl, steps, warmup):
         "phases_sum_us": round(sum(ph_ms) / ncalls * 1e3, 2), "phases": phases,
         "roofline": {"kernel": "k_attn_decode_bf16 + k_attn_merge", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None, "bytes_per_launch": kv_bytes, "avg_launch_us": round(attn_us, 2)},
+                     "traffic": _traffic_bytes(f"decode_attention:{wl.name}"), "bytes_per_launch": kv_bytes,
+                     "avg_launch_us": round(attn_us, 2)},
     }
 
 
-def cpu_baseline(wl, sample_tokens):
-    """The oracle, as it stands, timed on this host on the first `sample_tokens`
-    tokens of the same prompt (a causal prefill of that shorter prompt)."""
-    import numpy as np
+def cpu_baseline(wl, min_seconds):
+    """The oracle, as it stands, timed on this host: the causal prefill of the
+    whole prompt of the same workload, repeated until at least `min_seconds`
+    of CPU time have passed (at least once)."""
     import workloads as W
     from oracle import ref
     try:
@@ -205,11 +212,14 @@ def cpu_baseline(wl, sample_tokens):
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     inp = W.draw_block_workload(wl)
-    x = inp["x"][:, :sample_tokens]
-    t0 = time.perf_counter()
-    ref.block_forward(x, inp["weights"], wl.shape)
-    dt = time.perf_counter() - t0
-    fl = W.prefill_flops(wl.shape, wl.batch, sample_tokens)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        ref.block_forward(inp["x"], inp["weights"], wl.shape)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    fl = W.prefill_flops(wl.shape, wl.batch, wl.seq_len) * reps
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -219,9 +229,48 @@ def cpu_baseline(wl, sample_tokens):
     except OSError:
         pass
     return {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"causal prefill of the first {sample_tokens} of the {wl.seq_len} prompt tokens "
-                      f"(batch {wl.batch}), float64 numpy, {dt:.1f} s; {fl / 1e12:.3f} TFLOP counted",
+            "sample": f"{reps} x the causal prefill of the whole {wl.seq_len}-token prompt (batch {wl.batch}) "
+                      f"of {wl.name}, float64 numpy, {dt:.1f} s; {fl / 1e12:.3f} TFLOP counted",
             "cpu": cpu}
+
+
+def _source_sha(path):
+    import hashlib
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the counter summary committed in
+    profiles/hbm_traffic.md (FETCH_SIZE + WRITE_SIZE, each scaled by the copy
+    calibration), or None when none is recorded or the kernel's source file
+    has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if not line.startswith("traffic:"):
+            continue
+        kv = dict(t.split("=", 1) for t in line.split()[1:])
+        if kv.get("kernel") != kernel:
+            continue
+        if _source_sha(kv["source"]) != kv["sha256"]:
+            return None
+        return {"bytes": int(kv["bytes_per_launch"]), "fetch_bytes": int(kv["fetch_bytes"]),
+                "write_bytes": int(kv["write_bytes"]), "source": kv["source"]}
+    return None
+
+
+def copy_probe(mb, reps):
+    """A plain device copy of `mb` MiB, `reps` times: the known-size kernel that
+    calibrates the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.ones(mb << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": mb << 20, "reps": reps}), flush=True)
 
 
 def main():
@@ -232,7 +281,10 @@ def main():
     ap.add_argument("--workload", default="llama7b_block_prefill_b1_l2048")
     ap.add_argument("--decode-workload", default="llama13b_block_decode_b16_kv4096",
                     help="decode workload reported beside the prefill line ('' to skip)")
-    ap.add_argument("--cpu-sample", type=int, default=1024, help="prompt tokens the oracle baseline runs (0: skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="minimum seconds of oracle time for the CPU baseline (0: skip)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the block's data-parallel "
@@ -242,6 +294,8 @@ def main():
     import workloads as W
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        return copy_probe(args.copy_probe, max(args.steps, 1))
     wl = W.get(args.workload)
     if wl.mode != "prefill":
         raise SystemExit("--workload must be a prefill workload; decode workloads go to --decode-workload")
@@ -268,9 +322,9 @@ def main():
         dec = bench_decode(dw, args.steps, args.warmup)
         log(f"[bench] decode {dec['us_per_step']} us/step, {dec['tokens_per_s']} tok/s")
         out["decode"] = dec
-    if args.cpu_sample > 0:
-        log(f"[bench] cpu oracle baseline on {args.cpu_sample} tokens")
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+    if args.cpu_seconds > 0:
+        log(f"[bench] cpu oracle baseline, at least {args.cpu_seconds} s")
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
