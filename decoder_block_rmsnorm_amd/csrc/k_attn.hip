@@ -94,15 +94,22 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }
 
+// Causal work per query tile grows with its index, so when the grid is large
+// enough a block takes the pair (z, n_qt - 1 - z): every block then does the
+// same amount of work.
 __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __restrict__ q, KVView kv, int B,
-                                                             int L, int H, int G, bf16_t* __restrict__ out) {
+                                                             int L, int H, int G, int n_qt, int paired,
+                                                             bf16_t* __restrict__ out) {
   using namespace fa;
   __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (K_ELEMS + V_ELEMS)];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
-  const int n_qt = gridDim.z;
-  const int qt = n_qt - 1 - blockIdx.z;  // heavy (late) query tiles first
   const int g = h / (H / G);
+  for (int pass = 0; pass < 2; ++pass) {
+  // unpaired: one tile per block, heavy (late) query tiles first
+  const int qt = !paired ? n_qt - 1 - (int)blockIdx.z : pass == 0 ? n_qt - 1 - (int)blockIdx.z : (int)blockIdx.z;
+  if (pass == 1 && (!paired || qt >= n_qt - 1 - (int)blockIdx.z)) break;   // (middle tile of an odd count: done)
+  __syncthreads();   // LDS of the previous pass is free
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hg = lane >> 5;
   const int S = kv.lens[b];               // tokens cached before this call
@@ -186,14 +193,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
     if (key0 < wave_kmax && nq_valid > wave * 32) {
       const bf16_t* ks = smem + buf * (K_ELEMS + V_ELEMS);
       const bf16_t* vs = ks + K_ELEMS;
-      // S^T = K Q^T : 2 key subtiles of 32
+      // S^T = K Q^T : 2 key subtiles of 32.  A-row r = 8a + 4h + m of subtile st
+      // holds key 32 st + 16 (a / 2) + 8 h + 4 (a % 2) + m, so that afterwards
+      // lane group hg holds keys 16 c + 8 hg + 0..7 of each 16-key chunk c: the
+      // P.V operands are then 8 consecutive keys (one 16-byte V^T read).
+      const int krow = 16 * (l32 >> 4) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
       f32x16 s_acc[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         s_acc[st] = (f32x16){};
 #pragma unroll
         for (int kc = 0; kc < 8; ++kc) {
-          bf16x8 a = as_bf16x8(ld16(ks + (st * 32 + l32) * KST + kc * 16 + hg * 8));
+          bf16x8 a = as_bf16x8(ld16(ks + (st * 32 + krow) * KST + kc * 16 + hg * 8));
           s_acc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s_acc[st], 0, 0, 0);
         }
       }
@@ -206,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
         for (int i = 0; i < 16; ++i) {
           float v = s_acc[st][i] * sl2;
           if (need_mask) {
-            int key = key0 + st * 32 + 8 * (i >> 2) + 4 * hg + (i & 3);
+            int key = key0 + st * 32 + 16 * (i >> 3) + 8 * hg + (i & 7);
             if (key > my_pos) v = -INFINITY;
           }
           s_acc[st][i] = v;
@@ -240,14 +251,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
         pw.y = pack_bf16x2(s_acc[st][r0 + 2], s_acc[st][r0 + 3]);
         pw.z = pack_bf16x2(s_acc[st][r0 + 4], s_acc[st][r0 + 5]);
         pw.w = pack_bf16x2(s_acc[st][r0 + 6], s_acc[st][r0 + 7]);
-        bf16x8 pb = as_bf16x8(pw);
-        const int kA = 16 * c + 4 * hg;  // keys kA..kA+3 and kA+8..kA+11
+        bf16x8 pb = as_bf16x8(pw);   // P^T: keys 16 c + 8 hg + 0..7 of query l32
 #pragma unroll
         for (int ds = 0; ds < 4; ++ds) {
-          const bf16_t* vr = vs + (ds * 32 + l32) * VST;
-          uint2 lo = *reinterpret_cast<const uint2*>(vr + kA);
-          uint2 hi = *reinterpret_cast<const uint2*>(vr + kA + 8);
-          bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+          bf16x8 a = as_bf16x8(ld16(vs + (ds * 32 + l32) * VST + 16 * c + 8 * hg));
           o_acc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o_acc[ds], 0, 0, 0);
         }
       }
@@ -268,12 +275,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
         *reinterpret_cast<uint2*>(orow + dd) = w;
       }
   }
+  }  // pass
 }
 
 void launch_attn_prefill_bf16(const bf16_t* q, KVView kv, int B, int L, int H, int G, bf16_t* out, hipStream_t s) {
   if (B <= 0 || L <= 0) return;
-  dim3 grid(H, B, (L + fa::BQ - 1) / fa::BQ);
-  hipLaunchKernelGGL(k_attn_prefill_bf16, grid, dim3(256), 0, s, q, kv, B, L, H, G, out);
+  const int n_qt = (L + fa::BQ - 1) / fa::BQ;
+  // (measured: no faster than one tile per block at the configurations here,
+  // so pairing is off)
+  const int paired = 0;
+  dim3 grid(H, B, paired ? (n_qt + 1) / 2 : n_qt);
+  hipLaunchKernelGGL(k_attn_prefill_bf16, grid, dim3(256), 0, s, q, kv, B, L, H, G, n_qt, paired, out);
 }
 
 // ===========================================================================
