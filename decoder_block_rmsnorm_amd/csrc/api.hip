@@ -435,6 +435,7 @@ static KVView kv_view(const llama_kvcache* c, int layer) {
   v.d = c->cfg.head_dim;
   v.ps = c->cfg.page_size;
   v.pps = c->pps;
+  v.tiled = c->cfg.dtype == LLAMA_BF16 && c->cfg.head_dim == 128;
   return v;
 }
 

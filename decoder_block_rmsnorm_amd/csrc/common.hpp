@@ -54,24 +54,47 @@ template <> struct Elt<bf16_t> {
   static __device__ __host__ inline float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
 };
 
-// Paged KV cache view of one layer, passed by value to kernels.
-//   K page: [G][ps][d]   (slot-major, head_dim contiguous)
-//   V page: [G][d][ps]   (transposed: slots contiguous per head_dim row)
+// Paged KV cache view of one layer, passed by value to kernels.  A page holds
+// ps slots for each of the G kv heads: per head a K block and a V block of
+// ps * d elements each.
+//   fp32 (row-major):  K block [ps][d], V block [d][ps] (transposed).
+//   bf16, d = 128 (tiled): each block is ps/64 sub-blocks of 64 slots in the
+//   operand order of the decode attention's 16x16x32 MFMAs, so that every
+//   wavefront-wide 16-byte load there is one contiguous kilobyte:
+//     K: fragment (st, kc) = 1 KB at ((st * 4 + kc) * 64 + lane) * 8, lane =
+//        16 * (d % 32 / 8) + r, holding key 32 (st / 2) + 8 (r / 4) + 4 (st % 2)
+//        + r % 4 and dims 32 kc + 8 (lane / 16) .. + 7;
+//     V: fragment (ds, hf) = 1 KB at ((ds * 2 + hf) * 64 + lane) * 8, lane =
+//        16 * (key % 32 / 8) + d % 16, holding dim 16 ds + d % 16 and keys
+//        32 hf + 8 (lane / 16) .. + 7.
+//   Within a 16-byte piece, 8 consecutive dims (K) or 8 consecutive keys (V).
+__host__ __device__ inline int kv_tiled_k(int slot, int e) {
+  const int k = slot & 63;
+  const int st = 2 * (k >> 5) + ((k >> 2) & 1), r = 4 * ((k >> 3) & 3) + (k & 3);
+  return (slot >> 6) * (64 * 128) + ((st * 4 + (e >> 5)) * 64 + ((e >> 3) & 3) * 16 + r) * 8 + (e & 7);
+}
+__host__ __device__ inline int kv_tiled_v(int slot, int e) {
+  const int k = slot & 63;
+  return (slot >> 6) * (64 * 128) + (((e >> 4) * 2 + (k >> 5)) * 64 + ((k >> 3) & 3) * 16 + (e & 15)) * 8 + (k & 7);
+}
 struct KVView {
   void* k;              // this layer's K pool base
   void* v;              // this layer's V pool base
   const int32_t* table; // [max_batch][pps]
   int32_t* lens;        // this layer's lens [max_batch]
   int32_t G, d, ps, pps;
+  int32_t tiled;        // bf16 / d = 128 operand-order layout (see above)
   __device__ __host__ inline size_t page_base(int b, int pos) const {
     int page = table[(size_t)b * pps + pos / ps];
     return (size_t)page * G * ps * d;
   }
   // element offsets
   __device__ inline size_t k_off(int b, int pos, int g, int e) const {
+    if (tiled) return page_base(b, pos) + (size_t)g * ps * d + kv_tiled_k(pos % ps, e);
     return page_base(b, pos) + ((size_t)g * ps + (pos % ps)) * d + e;
   }
   __device__ inline size_t v_off(int b, int pos, int g, int e) const {
+    if (tiled) return page_base(b, pos) + (size_t)g * ps * d + kv_tiled_v(pos % ps, e);
     return page_base(b, pos) + ((size_t)g * d + e) * ps + (pos % ps);
   }
 };

@@ -150,9 +150,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
     for (int i = 0; i < 4; ++i) {
       int c = tid + 256 * i;
       int kr = c >> 4, kc = c & 15;
-      kreg[i] = kr < nvalid ? ld16(Kp + base + ((size_t)g * kv.ps + slot0 + kr) * D + kc * 8) : make_uint4(0, 0, 0, 0);
+      const size_t blk = base + (size_t)g * kv.ps * D;   // this head's K (and V) block of the page
+      kreg[i] = kr < nvalid ? ld16(Kp + blk + kv_tiled_k(slot0 + kr, kc * 8)) : make_uint4(0, 0, 0, 0);
       int vr = c >> 3, vc = c & 7;
-      uint4 v = ld16(Vp + base + ((size_t)g * D + vr) * kv.ps + slot0 + vc * 8);
+      uint4 v = ld16(Vp + blk + kv_tiled_v(slot0 + vc * 8, vr));
       int nok = nvalid - vc * 8;
       if (nok < 8) {
         uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -340,27 +341,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int i = 0; i < 8; ++i) o_acc[i] = (f32x4){};
   float m_run = -INFINITY, l_run = 0.f;
-  // key offset (inside a 64-key step) of the K row this lane loads for tile st
-  const int krow_lo = 8 * (l16 >> 2) + (l16 & 3);
-
   for (int k0 = k_begin; k0 < k_end; k0 += 64) {
     const size_t base = kv.page_base(b, k0);
-    const int slot0 = k0 % kv.ps;
-    const bf16_t* kpage = Kp + base + (size_t)g * kv.ps * 128;
-    const bf16_t* vpage = Vp + base + (size_t)g * 128 * kv.ps;
+    // this head's K and V blocks, 64-slot sub-block of k0 (tiled layout)
+    const size_t sub = base + (size_t)g * kv.ps * 128 + (size_t)((k0 % kv.ps) >> 6) * (64 * 128);
+    const bf16_t* kpage = Kp + sub + lane * 8;
+    const bf16_t* vpage = Vp + sub + lane * 8;
     uint4 kr[4][4], vr[8][2];
+    // each load: one contiguous KB holding this tile's operand fragment
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const bf16_t* krow = kpage + (size_t)(slot0 + 32 * (st >> 1) + 4 * (st & 1) + krow_lo) * 128 + 8 * hg;
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) kr[st][kc] = ld16(krow + 32 * kc);
-    }
+      for (int kc = 0; kc < 4; ++kc) kr[st][kc] = ld16(kpage + (st * 4 + kc) * 512);
 #pragma unroll
-    for (int ds = 0; ds < 8; ++ds) {
-      const bf16_t* vrow = vpage + (size_t)(ds * 16 + l16) * kv.ps + slot0 + 8 * hg;
+    for (int ds = 0; ds < 8; ++ds)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) vr[ds][hf] = ld16(vrow + 32 * hf);
-    }
+      for (int hf = 0; hf < 2; ++hf) vr[ds][hf] = ld16(vpage + (ds * 2 + hf) * 512);
     f32x4 s_acc[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {

@@ -466,21 +466,23 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
             constexpr int q = decltype(qc)::value;
             const int rl = rl0 + q, row = m0 + rl;
             if (row < M) {
+              // q row, or this key's slot in the head's K block (tiled layout)
               bf16_t* dst = is_q ? a.q_out + (size_t)row * a.Nq + wcol0
-                                 : (bf16_t*)a.kv.k + s_page[rl] + ((size_t)g * ps + (s_pos[rl] % ps)) * 128;
+                                 : (bf16_t*)a.kv.k + s_page[rl] + (size_t)g * ps * 128;
+              const int slot = is_q ? 0 : s_pos[rl] % ps;
               static_for<0, 2>([&](auto jc) {
                 constexpr int jp = decltype(jc)::value;
                 const int pi = jp * 32 + l32;
                 const int ca = a.traditional ? 2 * pi : pi;
                 const int cb = a.traditional ? 2 * pi + 1 : pi + 64;
-                dst[ca] = f32_to_bf16(v0[jp][q]);
-                dst[cb] = f32_to_bf16(v1[jp][q]);
+                dst[is_q ? ca : kv_tiled_k(slot, ca)] = f32_to_bf16(v0[jp][q]);
+                dst[is_q ? cb : kv_tiled_k(slot, cb)] = f32_to_bf16(v1[jp][q]);
               });
             }
           });
         } else {
-          // V is stored transposed per page ([g][d][slot]): 4 consecutive rows of
-          // one sequence at 4-aligned consecutive positions are 4 adjacent slots.
+          // V (tiled layout): 4 consecutive rows of one sequence at 4-aligned
+          // consecutive positions are 4 adjacent elements for each dim.
           bf16_t* Vc = (bf16_t*)a.kv.v;
           const int row0 = m0 + rl0;
           bool vec = row0 + 3 < M;
@@ -492,22 +494,24 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
             constexpr int jp = decltype(jc)::value;
             const int pi = jp * 32 + l32;
             if (vec) {
-              const size_t base = s_page[rl0] + (size_t)g * 128 * ps + (s_pos[rl0] % ps);
+              const size_t base = s_page[rl0] + (size_t)g * 128 * ps;
+              const int slot = s_pos[rl0] % ps;
               uint2 w0, w1;
               w0.x = (uint32_t)f32_to_bf16(v0[jp][0]) | ((uint32_t)f32_to_bf16(v0[jp][1]) << 16);
               w0.y = (uint32_t)f32_to_bf16(v0[jp][2]) | ((uint32_t)f32_to_bf16(v0[jp][3]) << 16);
               w1.x = (uint32_t)f32_to_bf16(v1[jp][0]) | ((uint32_t)f32_to_bf16(v1[jp][1]) << 16);
               w1.y = (uint32_t)f32_to_bf16(v1[jp][2]) | ((uint32_t)f32_to_bf16(v1[jp][3]) << 16);
-              *reinterpret_cast<uint2*>(Vc + base + (size_t)pi * ps) = w0;
-              *reinterpret_cast<uint2*>(Vc + base + (size_t)(pi + 64) * ps) = w1;
+              *reinterpret_cast<uint2*>(Vc + base + kv_tiled_v(slot, pi)) = w0;
+              *reinterpret_cast<uint2*>(Vc + base + kv_tiled_v(slot, pi + 64)) = w1;
             } else {
               static_for<0, 4>([&](auto qc) {
                 constexpr int q = decltype(qc)::value;
                 const int rl = rl0 + q;
                 if (m0 + rl < M) {
-                  const size_t base = s_page[rl] + (size_t)g * 128 * ps + (s_pos[rl] % ps);
-                  Vc[base + (size_t)pi * ps] = f32_to_bf16(v0[jp][q]);
-                  Vc[base + (size_t)(pi + 64) * ps] = f32_to_bf16(v1[jp][q]);
+                  const size_t base = s_page[rl] + (size_t)g * 128 * ps;
+                  const int slot = s_pos[rl] % ps;
+                  Vc[base + kv_tiled_v(slot, pi)] = f32_to_bf16(v0[jp][q]);
+                  Vc[base + kv_tiled_v(slot, pi + 64)] = f32_to_bf16(v1[jp][q]);
                 }
               });
             }
