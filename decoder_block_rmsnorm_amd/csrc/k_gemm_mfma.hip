@@ -413,12 +413,22 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
   }
 
   // ---------------- epilogue: lane holds column l32 of each 32x32 subtile,
-  // rows 8*(r/4) + 4*hg + r%4 for register r.
+  // rows 8*(r/4) + 4*hg + r%4 for register r.  Results go through a per-wave
+  // LDS staging area, 32 rows at a time, so that global stores (and the
+  // residual loads) are 16-byte pieces of contiguous rows.
   const int wcol0 = n0 + wn * 128;  // first column of this wavefront (head aligned)
+  __syncthreads();                  // main-loop LDS is free
+  // [0, 4 KB): per-row cache metadata (EPI_QKV); then 17 KB per wavefront
+  char* stage = reinterpret_cast<char*>(lds) + 4096 + wave * 17408;
+  auto wave_sync = [&]() {
+    // LDS accesses of one wavefront complete in order once waited for
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+  };
   if constexpr (EPI == EPI_QKV) {
-    // Per-row cache metadata once per block, into the (now free) LDS: position,
-    // and the element offset of the row's page.
-    __syncthreads();
+    // Per-row cache metadata once per block: position, and the element offset
+    // of the row's page.
     int* s_pos = reinterpret_cast<int*>(lds);
     long long* s_page = reinterpret_cast<long long*>(lds + 4 * BM);  // 8-byte aligned
     for (int r = tid; r < BM; r += NT) {
@@ -435,123 +445,173 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     const bool is_k = !is_q && wcol0 < a.Nq + a.Nkv;
     const int ps = a.kv.ps;
     const int g = is_q ? 0 : (is_k ? (wcol0 - a.Nq) >> 7 : (wcol0 - a.Nq - a.Nkv) >> 7);
+    bf16_t* sq = reinterpret_cast<bf16_t*>(stage);   // Q/K: [32 rows][136]; V: [128 dims][40]
+    constexpr int QST = 136, VTS = 40;
     static_for<0, MI>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      static_for<0, 4>([&](auto r4c) {
-        constexpr int r4 = decltype(r4c)::value;
-        const int rl0 = wm * WTM + i * 32 + 8 * r4 + 4 * hg;  // first of 4 consecutive rows
-        float v0[2][4], v1[2][4];
-        static_for<0, 4>([&](auto qc) {
-          constexpr int q = decltype(qc)::value;
-          const int rl = rl0 + q, row = m0 + rl;
-          const float rs = row < M ? a.inv_rms[row] : 0.f;
-          const int pos = row < M ? s_pos[rl] : 0;
-          static_for<0, 2>([&](auto jc) {
-            constexpr int jp = decltype(jc)::value;
-            const int pi = jp * 32 + l32;  // pair index: columns pi and pi + 64 of the head
-            float x0 = acc[i][jp][4 * r4 + q] * rs, x1 = acc[i][jp + 2][4 * r4 + q] * rs;
-            if (is_q || is_k) {
-              const float2 cs = a.rope[(size_t)pos * 64 + pi];
-              const float y0 = x0 * cs.x - x1 * cs.y;
-              const float y1 = x1 * cs.x + x0 * cs.y;
-              x0 = y0;
-              x1 = y1;
-            }
-            v0[jp][q] = x0;
-            v1[jp][q] = x1;
-          });
+      const int rb = wm * WTM + i * 32;   // block-local first row of this subtile
+      // all of this subtile's row scales and rotation factors are requested
+      // before any is used (one batch of loads in flight, not 32 round trips)
+      float rsv[16];
+      float2 csv[16][2];
+      static_for<0, 16>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const int lr = 8 * (r >> 2) + 4 * hg + (r & 3);
+        const int row = m0 + rb + lr;
+        const int pos = row < M ? s_pos[rb + lr] : 0;
+        rsv[r] = row < M ? a.inv_rms[row] : 0.f;
+        static_for<0, 2>([&](auto jc) {
+          constexpr int jp = decltype(jc)::value;
+          csv[r][jp] = (is_q || is_k) ? a.rope[(size_t)pos * 64 + jp * 32 + l32] : make_float2(1.f, 0.f);
         });
-        if (is_q || is_k) {
-          static_for<0, 4>([&](auto qc) {
-            constexpr int q = decltype(qc)::value;
-            const int rl = rl0 + q, row = m0 + rl;
-            if (row < M) {
-              // q row, or this key's slot in the head's K block (tiled layout)
-              bf16_t* dst = is_q ? a.q_out + (size_t)row * a.Nq + wcol0
-                                 : (bf16_t*)a.kv.k + s_page[rl] + (size_t)g * ps * 128;
-              const int slot = is_q ? 0 : s_pos[rl] % ps;
-              static_for<0, 2>([&](auto jc) {
-                constexpr int jp = decltype(jc)::value;
-                const int pi = jp * 32 + l32;
-                const int ca = a.traditional ? 2 * pi : pi;
-                const int cb = a.traditional ? 2 * pi + 1 : pi + 64;
-                dst[is_q ? ca : kv_tiled_k(slot, ca)] = f32_to_bf16(v0[jp][q]);
-                dst[is_q ? cb : kv_tiled_k(slot, cb)] = f32_to_bf16(v1[jp][q]);
-              });
-            }
-          });
-        } else {
-          // V (tiled layout): 4 consecutive rows of one sequence at 4-aligned
-          // consecutive positions are 4 adjacent elements for each dim.
-          bf16_t* Vc = (bf16_t*)a.kv.v;
-          const int row0 = m0 + rl0;
-          bool vec = row0 + 3 < M;
-          if (vec) {
-            const int p0 = s_pos[rl0];
-            vec = (p0 & 3) == 0 && s_pos[rl0 + 3] == p0 + 3 && s_page[rl0 + 3] == s_page[rl0];
-          }
-          static_for<0, 2>([&](auto jc) {
-            constexpr int jp = decltype(jc)::value;
-            const int pi = jp * 32 + l32;
-            if (vec) {
-              const size_t base = s_page[rl0] + (size_t)g * 128 * ps;
-              const int slot = s_pos[rl0] % ps;
-              uint2 w0, w1;
-              w0.x = (uint32_t)f32_to_bf16(v0[jp][0]) | ((uint32_t)f32_to_bf16(v0[jp][1]) << 16);
-              w0.y = (uint32_t)f32_to_bf16(v0[jp][2]) | ((uint32_t)f32_to_bf16(v0[jp][3]) << 16);
-              w1.x = (uint32_t)f32_to_bf16(v1[jp][0]) | ((uint32_t)f32_to_bf16(v1[jp][1]) << 16);
-              w1.y = (uint32_t)f32_to_bf16(v1[jp][2]) | ((uint32_t)f32_to_bf16(v1[jp][3]) << 16);
-              *reinterpret_cast<uint2*>(Vc + base + kv_tiled_v(slot, pi)) = w0;
-              *reinterpret_cast<uint2*>(Vc + base + kv_tiled_v(slot, pi + 64)) = w1;
-            } else {
-              static_for<0, 4>([&](auto qc) {
-                constexpr int q = decltype(qc)::value;
-                const int rl = rl0 + q;
-                if (m0 + rl < M) {
-                  const size_t base = s_page[rl] + (size_t)g * 128 * ps;
-                  const int slot = s_pos[rl] % ps;
-                  Vc[base + kv_tiled_v(slot, pi)] = f32_to_bf16(v0[jp][q]);
-                  Vc[base + kv_tiled_v(slot, pi + 64)] = f32_to_bf16(v1[jp][q]);
-                }
-              });
-            }
-          });
-        }
       });
+      static_for<0, 16>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const int lr = 8 * (r >> 2) + 4 * hg + (r & 3);   // row inside the subtile
+        const float rs = rsv[r];
+        static_for<0, 2>([&](auto jc) {
+          constexpr int jp = decltype(jc)::value;
+          const int pi = jp * 32 + l32;  // pair index: columns pi and pi + 64 of the head
+          float x0 = acc[i][jp][r] * rs, x1 = acc[i][jp + 2][r] * rs;
+          if (is_q || is_k) {
+            const float2 cs = csv[r][jp];
+            const float y0 = x0 * cs.x - x1 * cs.y;
+            const float y1 = x1 * cs.x + x0 * cs.y;
+            x0 = y0;
+            x1 = y1;
+          }
+          const int ca = (is_q || is_k) && a.traditional ? 2 * pi : pi;
+          const int cb = (is_q || is_k) && a.traditional ? 2 * pi + 1 : pi + 64;
+          if (is_q || is_k) {
+            sq[lr * QST + ca] = f32_to_bf16(x0);
+            sq[lr * QST + cb] = f32_to_bf16(x1);
+          } else {
+            sq[ca * VTS + lr] = f32_to_bf16(x0);
+            sq[cb * VTS + lr] = f32_to_bf16(x1);
+          }
+        });
+      });
+      wave_sync();
+      if (is_q || is_k) {
+        // 32 rows x 16 pieces of 8 columns
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int c = lane + 64 * t, lr = c >> 4, pc = c & 15;
+          const int row = m0 + rb + lr;
+          if (row < M) {
+            const uint4 v = ld16(sq + lr * QST + 8 * pc);
+            if (is_q) {
+              st16(a.q_out + (size_t)row * a.Nq + wcol0 + 8 * pc, v);
+            } else {
+              bf16_t* kb = (bf16_t*)a.kv.k + s_page[rb + lr] + (size_t)g * ps * 128;
+              st16(kb + kv_tiled_k(s_pos[rb + lr] % ps, 8 * pc), v);
+            }
+          }
+        }
+      } else {
+        // 128 dims x 4 pieces of 8 tokens; a piece whose 8 rows are 8 consecutive
+        // 8-aligned positions of one sequence and page is one 16-byte store
+        bf16_t* Vc = (bf16_t*)a.kv.v;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int c = lane + 64 * t, dd = c >> 2, p8 = c & 3;
+          const int lr0 = 8 * p8, row0 = m0 + rb + lr0;
+          if (row0 >= M) continue;
+          const int p0 = s_pos[rb + lr0];
+          const bool vec = row0 + 7 < M && (p0 & 7) == 0 && s_pos[rb + lr0 + 7] == p0 + 7 &&
+                           s_page[rb + lr0 + 7] == s_page[rb + lr0];
+          if (vec) {
+            st16(Vc + s_page[rb + lr0] + (size_t)g * 128 * ps + kv_tiled_v(p0 % ps, dd), ld16(sq + dd * VTS + lr0));
+          } else {
+            for (int e = 0; e < 8 && row0 + e < M; ++e)
+              Vc[s_page[rb + lr0 + e] + (size_t)g * 128 * ps + kv_tiled_v(s_pos[rb + lr0 + e] % ps, dd)] =
+                  sq[dd * VTS + lr0 + e];
+          }
+        }
+      }
+      wave_sync();
     });
-  } else {
+  } else if constexpr (EPI == EPI_F32) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
+    for (int i = 0; i < MI; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * hg + (r & 3);
-      if (row >= M) continue;
-      if constexpr (EPI == EPI_F32) {
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * hg + (r & 3);
+        if (row >= M) continue;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           a.C[(size_t)ksi * M * N + (size_t)row * N + wcol0 + j * 32 + l32] = acc[i][j][r];
-      } else if constexpr (EPI == EPI_RESID) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          size_t idx = (size_t)row * N + wcol0 + j * 32 + l32;
-          if (a.branch) a.branch[idx] = f32_to_bf16(acc[i][j][r]);
-          a.out[idx] = f32_to_bf16(bf16_to_f32(a.resid[idx]) + acc[i][j][r]);
-        }
-      } else if constexpr (EPI == EPI_SWIGLU) {
-        const float rs = a.inv_rms[row];
-        const int F = N >> 1;
-#pragma unroll
-        for (int jp = 0; jp < 2; ++jp) {
-          // interleave block of 32: columns wcol0 + 64*jp .. +31 are w1 rows,
-          // the next 32 the matching w3 rows
-          const int blk = (wcol0 + 64 * jp) >> 5;
-          const int j = (blk >> 1) * 32 + l32;
-          float gt = acc[i][2 * jp][r] * rs, up = acc[i][2 * jp + 1][r] * rs;
-          a.g_out[(size_t)row * F + j] = f32_to_bf16(silu_f(gt) * up);
-        }
       }
     }
-  }
+  } else if constexpr (EPI == EPI_RESID) {
+    float* sf = reinterpret_cast<float*>(stage);   // [32 rows][132] fp32
+    constexpr int FST = 132;
+    static_for<0, MI>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int rb = wm * WTM + i * 32;
+      static_for<0, 16>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const int lr = 8 * (r >> 2) + 4 * hg + (r & 3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sf[lr * FST + j * 32 + l32] = acc[i][j][r];
+      });
+      wave_sync();
+      // 32 rows x 16 pieces of 8 columns: out = resid + acc, rounded once
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int c = lane + 64 * t, lr = c >> 4, pc = c & 15;
+        const int row = m0 + rb + lr;
+        if (row < M) {
+          const size_t idx = (size_t)row * N + wcol0 + 8 * pc;
+          const float4 f0 = *reinterpret_cast<const float4*>(sf + lr * FST + 8 * pc);
+          const float4 f1 = *reinterpret_cast<const float4*>(sf + lr * FST + 8 * pc + 4);
+          const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+          const uint4 rv = ld16(a.resid + idx);
+          const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+          uint32_t ow[4], bw[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float r0 = bf16_to_f32((bf16_t)(rw[e] & 0xffffu)), r1 = bf16_to_f32((bf16_t)(rw[e] >> 16));
+            ow[e] = (uint32_t)f32_to_bf16(r0 + f[2 * e]) | ((uint32_t)f32_to_bf16(r1 + f[2 * e + 1]) << 16);
+            bw[e] = (uint32_t)f32_to_bf16(f[2 * e]) | ((uint32_t)f32_to_bf16(f[2 * e + 1]) << 16);
+          }
+          st16(a.out + idx, make_uint4(ow[0], ow[1], ow[2], ow[3]));
+          if (a.branch) st16(a.branch + idx, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+        }
+      }
+      wave_sync();
+    });
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    bf16_t* sg = reinterpret_cast<bf16_t*>(stage);   // [32 rows][72] bf16: this wave's 64 g columns
+    constexpr int GST = 72;
+    const int F = N >> 1;
+    // interleave blocks of 32: columns wcol0 + 64*jp .. +31 are w1 rows, the
+    // next 32 the matching w3 rows; this wave's g columns start at wcol0 / 2
+    const int gcol0 = wcol0 >> 1;
+    static_for<0, MI>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int rb = wm * WTM + i * 32;
+      static_for<0, 16>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const int lr = 8 * (r >> 2) + 4 * hg + (r & 3);
+        const int row = m0 + rb + lr;
+        const float rs = row < M ? a.inv_rms[row] : 0.f;
+#pragma unroll
+        for (int jp = 0; jp < 2; ++jp) {
+          const float gt = acc[i][2 * jp][r] * rs, up = acc[i][2 * jp + 1][r] * rs;
+          sg[lr * GST + jp * 32 + l32] = f32_to_bf16(silu_f(gt) * up);
+        }
+      });
+      wave_sync();
+      // 32 rows x 8 pieces of 8 g columns
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int c = lane + 64 * t, lr = c >> 3, pc = c & 7;
+        const int row = m0 + rb + lr;
+        if (row < M) st16(a.g_out + (size_t)row * F + gcol0 + 8 * pc, ld16(sg + lr * GST + 8 * pc));
+      }
+      wave_sync();
+    });
   }
   if constexpr (EPI == EPI_RESID) {
     if (a.lens_add && blockIdx.x == 0 && tid < a.n_seq) a.lens_add[tid] += a.lens_inc;
