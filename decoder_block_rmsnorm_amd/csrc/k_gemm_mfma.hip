@@ -16,6 +16,7 @@
 // one barrier per K step.  Blocks are renumbered XCD-major and walked in
 // GROUP_M-row bands so that co-resident blocks of one XCD share A and B tiles
 // in that XCD's L2.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <type_traits>
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
 
   // LDS buffer b is rewritten two steps after it was read; the barrier of the
   // step in between guarantees every wavefront has finished reading it.
-  if constexpr (DEPTH == 0 || DEPTH == 3 || DEPTH == 4) {
+  if constexpr (DEPTH == 0 || DEPTH == 3 || DEPTH == 4) {   // (BM 128 or 256 with DEPTH 0)
     // Direct-to-LDS ring (DEPTH 0: 32-wide K steps in 4 stages; DEPTH 3:
     // 64-wide K steps in 2 stages).  A stage holds the A and B tiles of one K
     // step as 16-row x 32-column blocks of 1 KB in the tiled weight format
@@ -267,8 +268,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     constexpr int STG = DEPTH == 0 ? 4 : DEPTH == 3 ? 2 : 5;   // stages
     constexpr int NKB = BKS / 32;                      // 32-column blocks per step
     constexpr int NKK = BKS / 16;                      // MFMA sub-steps per step
-    constexpr int LPS = 8 * NKB;                       // direct loads per wavefront per step
-    static_assert(!F16 && NW == 4 && BM == 256 && BN == 256, "direct-LDS configuration");
+    constexpr int LPS = (BM / 64 + 4) * NKB;           // direct loads per wavefront per step
+    static_assert(!F16 && NW == 4 && BN == 256 && (BM == 256 || (BM == 128 && DEPTH == 0)), "direct-LDS configuration");
+    constexpr int AG = BM / 64, BG = 4;                // A and B row groups each wavefront loads
     constexpr int SA = BM * BKS, SB = BN * BKS;        // bf16 per stage
     const int KT = Kslice / BKS;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -277,31 +279,33 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     // Per-lane byte offsets (32-bit: the host keeps A below 4 GB) from the
     // slice bases: A rows of this lane's pieces (clamped: rows past M load row
     // M-1, whose results are never stored), B pieces of this lane's groups.
-    uint32_t voa[4], vob[4];
+    uint32_t voa[AG], vob[BG];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      voa[i] = (uint32_t)(min(m0 + 16 * (wv * 4 + i) + r16, M - 1) * K + 8 * j4) * 2;
-      vob[i] = (uint32_t)(((wv * 4 + i) * nchk * (kTileK * 16) + lane * 8) * 2);
-    }
+    for (int i = 0; i < AG; ++i) voa[i] = (uint32_t)(min(m0 + 16 * (wv * AG + i) + r16, M - 1) * K + 8 * j4) * 2;
+#pragma unroll
+    for (int i = 0; i < BG; ++i) vob[i] = (uint32_t)(((wv * BG + i) * nchk * (kTileK * 16) + lane * 8) * 2);
     const char* abase = (const char*)Ag;
     const char* bbase = (const char*)Btile;
-    // direct load number idx (0 .. LPS-1) of step kt: 32-column block idx / 8,
-    // row group wv * 4 + (idx % 8) / 2, A (even idx) or B (odd idx)
+    // direct load number idx (0 .. LPS-1) of step kt: 32-column block
+    // idx / (AG + BG); inside a block, A and B groups alternate while both
+    // last (A on even numbers), then the remaining B groups
     auto issue_one = [&](int kt, int idx) {
       const uint32_t la = lds_base + (uint32_t)((kt % STG) * (SA + SB)) * 2;
-      const int kb = idx >> 3, i = (idx & 7) >> 1, g = wv * 4 + i;
-      if ((idx & 1) == 0)
-        lds_dma16(voa[i], abase + (size_t)(kt * BKS + kb * 32) * 2, la + (kb * 16 + g) * 1024);
+      const int kb = idx / (AG + BG), q = idx % (AG + BG);
+      const bool is_a = q < 2 * AG && (q & 1) == 0;
+      const int i = q < 2 * AG ? q >> 1 : q - AG;
+      if (is_a)
+        lds_dma16(voa[i], abase + (size_t)(kt * BKS + kb * 32) * 2, la + (kb * (BM / 16) + wv * AG + i) * 1024);
       else
-        lds_dma16(vob[i], bbase + (size_t)(kt * NKB + kb) * 1024, la + SA * 2 + (kb * 16 + g) * 1024);
+        lds_dma16(vob[i], bbase + (size_t)(kt * NKB + kb) * 1024, la + SA * 2 + (kb * 16 + wv * BG + i) * 1024);
     };
     // lane's piece inside a pair of groups: fragment rows 32t + l%32, k = 8*(l/32)
     const int fpiece = (16 * (lane >> 5) + r16) * 8 + ((lane >> 4) & 1) * 512;
     // fragment read number q (0 .. MI+3): A tile q, or B tile q - MI
     auto lfrag_one = [&](int st, int kk, int q, uint4(&a_)[MI], uint4(&b_)[4]) {
-      const bf16_t* la = lds + st * (SA + SB) + fpiece + (kk >> 1) * 16 * 512 + (kk & 1) * 256;
-      if (q < MI) a_[q] = ld16(la + (wm * (WTM / 16) + 2 * q) * 512);
-      else b_[q - MI] = ld16(la + SA + (wn * 8 + 2 * (q - MI)) * 512);
+      const bf16_t* la = lds + st * (SA + SB) + fpiece + (kk & 1) * 256;
+      if (q < MI) a_[q] = ld16(la + (kk >> 1) * (BM / 16) * 512 + (wm * (WTM / 16) + 2 * q) * 512);
+      else b_[q - MI] = ld16(la + SA + (kk >> 1) * 16 * 512 + (wn * 8 + 2 * (q - MI)) * 512);
     };
     // wait until this wavefront's loads of step t have landed, given the steps
     // issued up to step `last`
@@ -622,7 +626,7 @@ template <int BM, int BN, int NW, int DEPTH, int EPI, bool F16>
 static void launch_cfg(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * (a.N / BN) * (EPI == EPI_F32 && a.ksplit > 1 ? a.ksplit : 1);
   const size_t lds = DEPTH == 4 ? (size_t)(BM + BN) * 160 * sizeof(bf16_t)
-                     : DEPTH == 0 || DEPTH == 3 ? (size_t)(BM + BN) * 128 * sizeof(bf16_t)
+                     : DEPTH == 0 || DEPTH == 3 ? std::max<size_t>((size_t)(BM + BN) * 128 * sizeof(bf16_t), 4096 + 4 * 17408)
                                 : (size_t)2 * (BM + BN) * gm::LDS_ST * sizeof(bf16_t);
   static bool attr_set = false;
   if (!attr_set) {
@@ -650,6 +654,7 @@ static int forced_tile() {
       else if (!strcmp(e, "256x256d")) v = 5;
       else if (!strcmp(e, "256x256d64")) v = 6;
       else if (!strcmp(e, "256x256d5")) v = 7;
+      else if (!strcmp(e, "128x256d")) v = 8;
     }
   }
   return v;
@@ -663,6 +668,12 @@ static void launch_epi(const GemmArgs& a, hipStream_t s) {
     // direct-to-LDS tiles address A with 32-bit per-lane byte offsets
     const bool a32 = (size_t)a.M * a.K * sizeof(bf16_t) < ((size_t)1 << 32);
     const bool big = a32 && n256 && (EPI == EPI_F32 && a.ksplit > 1 || ((a.M + 255) / 256) * (a.N / 256) >= 240);
+    // 128-row tiles when their rounds of 256 blocks finish sooner (half the
+    // work each, counted 20% dearer: measured) than those of 256-row tiles
+    const long t256 = (long)((a.M + 255) / 256) * (a.N / 256), t128 = (long)((a.M + 127) / 128) * (a.N / 256);
+    const bool use128 = ((t128 + 255) / 256) * 0.6 < (double)((t256 + 255) / 256);
+    if (f == 8 && a32 && n256) return launch_cfg<128, 256, 4, 0, EPI, F16>(a, s);
+    if (f == 0 && big && use128 && !(EPI == EPI_F32 && a.ksplit > 1)) return launch_cfg<128, 256, 4, 0, EPI, F16>(a, s);
     if (f == 6 && big) return launch_cfg<256, 256, 4, 3, EPI, F16>(a, s);
     if (f == 7 && big) return launch_cfg<256, 256, 4, 4, EPI, F16>(a, s);
     if ((f == 0 || f == 5) && big) return launch_cfg<256, 256, 4, 0, EPI, F16>(a, s);
