@@ -27,13 +27,20 @@ __host__ __device__ inline float bf16_to_f32(bf16_t h) {
   return f;
 }
 
-// Round-to-nearest-even float -> bf16 (NaN kept quiet).
-__host__ __device__ inline bf16_t f32_to_bf16(float f) {
+// float -> bf16, round to nearest even (one v_cvt_pk_bf16_f32; NaN stays NaN).
+__device__ inline bf16_t f32_to_bf16(float f) {
+  const __bf16 h = (__bf16)f;
+  bf16_t r;
+  __builtin_memcpy(&r, &h, 2);
+  return r;
+}
+// two floats -> packed bf16 pair (a in the low half), one instruction
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
+  const bf16x2v v = {(__bf16)a, (__bf16)b};
   uint32_t u;
-  __builtin_memcpy(&u, &f, 4);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  __builtin_memcpy(&u, &v, 4);
+  return u;
 }
 
 // Element type traits: the fp32 and bf16 paths share templates through these.
@@ -48,10 +55,10 @@ template <> struct Elt<float> {
 };
 template <> struct Elt<bf16_t> {
   static __device__ __host__ inline float load(const bf16_t* p, size_t i) { return bf16_to_f32(p[i]); }
-  static __device__ __host__ inline void store(bf16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+  static __device__ inline void store(bf16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
   static __device__ __host__ inline float to_f(bf16_t v) { return bf16_to_f32(v); }
-  static __device__ __host__ inline bf16_t from_f(float v) { return f32_to_bf16(v); }
-  static __device__ __host__ inline float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+  static __device__ inline bf16_t from_f(float v) { return f32_to_bf16(v); }
+  static __device__ inline float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
 };
 
 // Paged KV cache view of one layer, passed by value to kernels.  A page holds

@@ -90,9 +90,6 @@ __device__ inline bf16x8 as_bf16x8(uint4 v) {
   return r;
 }
 
-__device__ inline uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-}
 
 // Causal work per query tile grows with its index, so when the grid is large
 // enough a block takes the pair (z, n_qt - 1 - z): every block then does the

@@ -576,8 +576,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float r0 = bf16_to_f32((bf16_t)(rw[e] & 0xffffu)), r1 = bf16_to_f32((bf16_t)(rw[e] >> 16));
-            ow[e] = (uint32_t)f32_to_bf16(r0 + f[2 * e]) | ((uint32_t)f32_to_bf16(r1 + f[2 * e + 1]) << 16);
-            bw[e] = (uint32_t)f32_to_bf16(f[2 * e]) | ((uint32_t)f32_to_bf16(f[2 * e + 1]) << 16);
+            ow[e] = pack_bf16x2(r0 + f[2 * e], r1 + f[2 * e + 1]);
+            bw[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
           }
           st16(a.out + idx, make_uint4(ow[0], ow[1], ow[2], ow[3]));
           if (a.branch) st16(a.branch + idx, make_uint4(bw[0], bw[1], bw[2], bw[3]));
