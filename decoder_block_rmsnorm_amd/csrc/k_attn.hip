@@ -207,13 +207,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
         }
       }
       // scale, causal mask, online softmax (query = column l32; rows = keys)
+      // (scores stay unscaled; the running max m is kept in log2 units, so
+      // p = 2^(s * log2(e)/sqrt(d) - m) is one fma and one v_exp_f32)
       const bool need_mask = key0 + BK - 1 > S + wq0;  // some key may exceed some query position
       float tmax = -INFINITY;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float v = s_acc[st][i] * sl2;
+          float v = s_acc[st][i];
           if (need_mask) {
             int key = key0 + st * 32 + 16 * (i >> 3) + 8 * hg + (i & 7);
             if (key > my_pos) v = -INFINITY;
@@ -222,16 +224,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
           tmax = fmaxf(tmax, v);
         }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax);
+      const float m_new = fmaxf(m_run, tmax * sl2);
       // a fully masked row so far keeps m = -inf; use 0 as the exponent base then
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
       float psum = 0.f;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float p = exp2f(s_acc[st][i] - m_use);
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[st][i], sl2, -m_use));
           s_acc[st][i] = p;
           psum += p;
         }
@@ -368,20 +370,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = k0 + 32 * (st >> 1) + 8 * hg + 4 * (st & 1) + i;
-        const float v = key < k_end ? s_acc[st][i] * sl2 : -INFINITY;
+        const float v = key < k_end ? s_acc[st][i] : -INFINITY;
         s_acc[st][i] = v;
         tmax = fmaxf(tmax, v);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
+    // running max in log2 units: p = 2^(s * log2(e)/sqrt(d) - m), one fma + v_exp_f32
+    const float m_new = fmaxf(m_run, tmax * sl2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float psum = 0.f;
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(s_acc[st][i] - m_new);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[st][i], sl2, -m_new));
         s_acc[st][i] = p;
         psum += p;
       }
@@ -456,7 +459,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
     float w = 0.f, dl = 0.f;
     if (c < n_splits) {
       const float mc = ml[2 * c];
-      w = mc == -INFINITY ? 0.f : exp2f(mc - M);
+      w = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - M);
       dl = w * ml[2 * c + 1];
     }
     den += dl;
