@@ -479,14 +479,17 @@ static const int kSplitLen = 256;  // keys per decode-attention chunk
 // Split-K factor of a decode projection [M rows] x [N, K]: enough blocks to
 // cover the chip several times over, K slices that stay multiples of 32 and at
 // least 512 long.
-// K slices of a decode projection: double while the grid is short of 768
-// blocks and every slice keeps at least two 256-column chunks.
+// K slices of a decode GEMV: double while the grid is short of the block
+// count that keeps HBM busy and each slice keeps at least four 256-wide chunks.
+// At M > 16 (64-row activation tiles) the fp32 partials cost 4 * ks * M / K of
+// the weight bytes, so fewer blocks are asked for (measured at M = 16 and 64).
 static int gemv_ks(int M, int N, int K) {
   const int cols = (M > 16 && N % 128 == 0) ? 128 : 64;
   const int tiles = N / cols;
   const int nchk = tiled_chunks(K);
+  const int target = M > 16 ? 256 : 384;
   int ks = 1;
-  while (tiles * ks < 768 && 4 * ks <= nchk) ks *= 2;
+  while (tiles * ks < target && 4 * ks <= nchk) ks *= 2;
   return ks;
 }
 
@@ -729,7 +732,7 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
                         int lens_inc, bf16_t* branch) {
     GemmArgs g{};
     g.A = A; g.B = weight(lin, nullptr); g.M = M; g.N = d.D; g.K = K; g.b_f16 = d.q4;
-    const int ks = gemm_split_k(M, d.D, K);
+    const int ks = gemm_split_k(M, d.D, K, d.q4);
     if (ks > 1) {
       g.C = part; g.ksplit = ks;
       launch_gemm_mfma(EPI_F32, g, s);

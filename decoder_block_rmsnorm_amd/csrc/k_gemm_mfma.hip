@@ -674,6 +674,8 @@ static void launch_epi(const GemmArgs& a, hipStream_t s) {
     const bool use128 = ((t128 + 255) / 256) * 0.6 < (double)((t256 + 255) / 256);
     if (f == 8 && a32 && n256) return launch_cfg<128, 256, 4, 0, EPI, F16>(a, s);
     if (f == 0 && big && use128 && !(EPI == EPI_F32 && a.ksplit > 1)) return launch_cfg<128, 256, 4, 0, EPI, F16>(a, s);
+    if (f == 0 && !big && a32 && n256 && t128 >= 240 && !(EPI == EPI_F32 && a.ksplit > 1))
+      return launch_cfg<128, 256, 4, 0, EPI, F16>(a, s);
     if (f == 6 && big) return launch_cfg<256, 256, 4, 3, EPI, F16>(a, s);
     if (f == 7 && big) return launch_cfg<256, 256, 4, 4, EPI, F16>(a, s);
     if ((f == 0 || f == 5) && big) return launch_cfg<256, 256, 4, 0, EPI, F16>(a, s);
@@ -700,9 +702,13 @@ static void launch_any(int epi, const GemmArgs& a, hipStream_t s) {
   }
 }
 
-int gemm_split_k(int M, int N, int K) {
+int gemm_split_k(int M, int N, int K, bool b_f16) {
   if (N % 256) return 1;
-  const long t256 = (long)((M + 255) / 256) * (N / 256);
+  const long t256 = (long)((M + 255) / 256) * (N / 256), t128 = (long)((M + 127) / 128) * (N / 256);
+  // up to K = 8192, unsplit 128x256 direct-to-LDS tiles beat a 2-way split
+  // once they fill the chip: the split's fp32 partials cost a round trip
+  // of 2*M*N*4 bytes per slice (measured on 2048x4096x4096 and x11008)
+  if (!b_f16 && t256 < 240 && t128 >= 240 && K <= 8192 && (size_t)M * K * sizeof(bf16_t) < ((size_t)1 << 32)) return 1;
   int ks = 1;
   // double while the grid is short of about 200 tiles and each slice keeps
   // at least 512 of K in whole 64-wide steps

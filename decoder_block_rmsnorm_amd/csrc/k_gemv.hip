@@ -34,29 +34,35 @@ constexpr int XST = KC + 8;     // LDS row stride (bf16)
 // c+1 are in flight while chunk c is multiplied.  Program order is chosen for
 // the in-order vmcnt counter: the activations of c+1 are requested before the
 // weights of c+2, so waiting for them never waits for the newer weights.
+// Every load of the steady-state loop is unconditional (out-of-range addresses
+// are clamped, and the values they bring are multiplied by zeros), so the
+// compiler can count outstanding loads exactly and never has to drain them.
 //
 // W is in the tiled layout (TILED: each wavefront load instruction reads one
-// contiguous kilobyte) or row-major [N][K].  K slice ksi of ks covers the
-// 256-column chunks [ksi * nchk / ks, (ksi + 1) * nchk / ks).
+// contiguous kilobyte; the padding of the last chunk is zero) or row-major
+// [N][K].  K slice ksi of ks covers the 256-column chunks
+// [ksi * nchk / ks, (ksi + 1) * nchk / ks).  K is a multiple of 8.
 template <int NW, int MT, bool TILED>
-__global__ __launch_bounds__(256) void k_gemv_bf16(const bf16_t* __restrict__ X, const bf16_t* __restrict__ W,
-                                                  float* __restrict__ part, int M, int N, int K, int ks,
-                                                  float* __restrict__ ss_out) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemv_bf16(
+    const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, float* __restrict__ part, int M, int N, int K, int ks,
+    float* __restrict__ ss_out) {
   using namespace gv;
   constexpr int ROWS = MT * 16;
   constexpr int XL = ROWS * (KC / 8) / 256;   // 16-byte activation pieces per thread per chunk
   __shared__ __attribute__((aligned(16))) bf16_t xs[2][ROWS * XST];
-  __shared__ float ssrow[ROWS];
   // the first column-block of each K slice also sums x^2 of the rows it stages
-  // (the RMSNorm statistic of the input, reduced over slices by its consumer)
+  // (the RMSNorm statistic of the input, reduced over slices by its consumer):
+  // each thread accumulates the squares of its own activation pieces
   const bool do_ss = ss_out != nullptr && blockIdx.x == 0;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, hg = lane >> 4;
-  if (tid < ROWS) ssrow[tid] = 0.f;
+  float ssp[XL];
+#pragma unroll
+  for (int i = 0; i < XL; ++i) ssp[i] = 0.f;
   const int ksi = blockIdx.y;
   const int nchk = (K + KC - 1) / KC;
   const int c0 = ksi * nchk / ks, c1 = (ksi + 1) * nchk / ks;
-  const int kb = c0 * KC, ke = min(K, c1 * KC);
+  const int kb = c0 * KC;
   const int nch = c1 - c0;
   const int nrow0 = blockIdx.x * (64 * NW) + wave * (16 * NW);
 
@@ -68,31 +74,31 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const bf16_t* __restrict__ X,
 
   uint4 w0[NW][8], w1[NW][8], xr[XL];
   auto wload = [&](int c, uint4(&w)[NW][8]) {
-    const int k0 = kb + c * KC;
-    const int nkc = min(8, (ke - k0) >> 5);
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
       if constexpr (TILED) {
         const bf16_t* t = W + ((size_t)((nrow0 >> 4) + j) * nchk + c0 + c) * (KC * 16) + lane * 8;
 #pragma unroll
-        for (int kc = 0; kc < 8; ++kc)
-          if (kc < nkc) w[j][kc] = ld16(t + 512 * kc);
+        for (int kc = 0; kc < 8; ++kc) w[j][kc] = ld16(t + 512 * kc);
       } else {
-        const bf16_t* wrow = W + (size_t)(nrow0 + j * 16 + l16) * K + k0 + 8 * hg;
+        const bf16_t* wrow = W + (size_t)(nrow0 + j * 16 + l16) * K;
+        const int k0 = kb + c * KC + 8 * hg;
 #pragma unroll
-        for (int kc = 0; kc < 8; ++kc)
-          if (kc < nkc) w[j][kc] = ld16(wrow + 32 * kc);
+        for (int kc = 0; kc < 8; ++kc) w[j][kc] = ld16(wrow + min(k0 + 32 * kc, K - 8));
       }
     }
   };
-  // piece p of a chunk: row p / 32, 8 columns at 8 * (p % 32); rows >= M and
-  // columns past the slice read as zero
+  // piece p of a chunk: row p / 32, 8 columns at 8 * (p % 32); rows >= M
+  // repeat row M - 1 (their products are never stored), columns >= K are zero
   auto xload = [&](int c) {
     const int k0 = kb + c * KC;
 #pragma unroll
     for (int i = 0; i < XL; ++i) {
-      const int p = tid + 256 * i, r = p >> 5, col = (p & 31) * 8;
-      xr[i] = (r < M && k0 + col < ke) ? ld16(X + (size_t)r * K + k0 + col) : make_uint4(0, 0, 0, 0);
+      const int p = tid + 256 * i, r = min(p >> 5, M - 1), col = k0 + (p & 31) * 8;
+      const uint32_t keep = col < K ? 0xffffffffu : 0u;
+      uint4 v = ld16(X + (size_t)r * K + min(col, K - 8));
+      v.x &= keep; v.y &= keep; v.z &= keep; v.w &= keep;
+      xr[i] = v;
     }
   };
   auto xstore = [&](int buf) {
@@ -100,56 +106,83 @@ __global__ __launch_bounds__(256) void k_gemv_bf16(const bf16_t* __restrict__ X,
     for (int i = 0; i < XL; ++i) {
       const int p = tid + 256 * i, r = p >> 5, col = (p & 31) * 8;
       st16(&xs[buf][r * XST + col], xr[i]);
-    }
-  };
-  auto compute = [&](int buf, int c, const uint4(&w)[NW][8]) {
-    const int nkc = min(8, (ke - kb - c * KC) >> 5);
-    if (do_ss) {
-      for (int r = wave; r < M; r += 4) {
-        float t = 0.f;
-        for (int col = lane; col < nkc * 32; col += 64) {
-          const float v = bf16_to_f32(xs[buf][r * XST + col]);
-          t += v * v;
+      if (do_ss) {
+        const bf16x8 v = v_as_bf16x8(xr[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = (float)v[e];
+          ssp[i] += f * f;
         }
-        t = warp_sum(t);
-        if (lane == 0) ssrow[r] += t;
       }
     }
+  };
+  auto compute = [&](int buf, const uint4(&w)[NW][8]) {
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
-      if (kc < nkc) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          bf16x8 xa = v_as_bf16x8(ld16(&xs[buf][(mt * 16 + l16) * XST + 32 * kc + 8 * hg]));
+      for (int mt = 0; mt < MT; ++mt) {
+        bf16x8 xa = v_as_bf16x8(ld16(&xs[buf][(mt * 16 + l16) * XST + 32 * kc + 8 * hg]));
 #pragma unroll
-          for (int j = 0; j < NW; ++j)
-            acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, v_as_bf16x8(w[j][kc]), acc[mt][j], 0, 0, 0);
-        }
+        for (int j = 0; j < NW; ++j)
+          acc[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, v_as_bf16x8(w[j][kc]), acc[mt][j], 0, 0, 0);
       }
     }
   };
 
-  if (nch > 0) {
+  // buffer reuse: a chunk's activations are stored into the LDS buffer read
+  // two computes earlier, with a barrier in between
+  if (nch >= 2) {
     xload(0);
     wload(0, w0);
-    if (nch > 1) wload(1, w1);
+    wload(1, w1);
     xstore(0);
     __syncthreads();
-  }
-  for (int c = 0; c < nch; c += 2) {
-    if (c + 1 < nch) xload(c + 1);
-    compute(0, c, w0);
+    int c = 0;
+    for (; c + 3 < nch; c += 2) {
+      xload(c + 1);
+      compute(0, w0);
+      wload(c + 2, w0);
+      xstore(1);
+      __syncthreads();
+      xload(c + 2);
+      compute(1, w1);
+      wload(c + 3, w1);
+      xstore(0);
+      __syncthreads();
+    }
+    // two or three chunks left: w0 holds chunk c, w1 chunk c + 1
+    xload(c + 1);
+    compute(0, w0);
     if (c + 2 < nch) wload(c + 2, w0);
-    if (c + 1 < nch) xstore(1);
+    xstore(1);
     __syncthreads();
-    if (c + 1 >= nch) break;
-    if (c + 2 < nch) xload(c + 2);
-    compute(1, c + 1, w1);
-    if (c + 3 < nch) wload(c + 3, w1);
-    if (c + 2 < nch) xstore(0);
+    if (c + 2 < nch) {
+      xload(c + 2);
+      compute(1, w1);
+      xstore(0);
+      __syncthreads();
+      compute(0, w0);
+    } else {
+      compute(1, w1);
+    }
+  } else if (nch == 1) {
+    xload(0);
+    wload(0, w0);
+    xstore(0);
     __syncthreads();
+    compute(0, w0);
   }
-  if (do_ss && tid < M) ss_out[(size_t)ksi * M + tid] = ssrow[tid];
+  if (do_ss) {
+    // the 32 pieces of row (tid + 256 i) / 32 sit in 32 adjacent lanes
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      float t = ssp[i];
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) t += __shfl_xor(t, o, 32);
+      const int r = (tid + 256 * i) >> 5;
+      if ((tid & 31) == 0 && r < M) ss_out[(size_t)ksi * M + r] = t;
+    }
+  }
   // lane: C[m = 16*mt + 4*hg + i][n = nrow0 + 16*j + l16]
   float* pp = part + (size_t)ksi * M * N;
 #pragma unroll

@@ -203,9 +203,15 @@ __global__ __launch_bounds__(256) void k_repack_rows(T* dst, const T* src, int r
   int r = blockIdx.x;
   int dr = repack_dst_row(r, row0, ib, ib_stride, perm_d);
   const int nchk = tiled_chunks(K);
-  for (int c = threadIdx.x; c < K; c += 256) {
-    float v = Elt<T>::load(src, (size_t)r * K + c);
-    if (gamma) v *= Elt<T>::load(gamma, c);
+  // the tiled layout's padding past K is written as zeros: readers may take
+  // whole chunks
+  const int kend = tiled ? nchk * kTileK : K;
+  for (int c = threadIdx.x; c < kend; c += 256) {
+    float v = 0.f;
+    if (c < K) {
+      v = Elt<T>::load(src, (size_t)r * K + c);
+      if (gamma) v *= Elt<T>::load(gamma, c);
+    }
     Elt<T>::store(dst, tiled ? tiled_off(dr, c, nchk) : (size_t)dr * K + c, v);
   }
 }

@@ -112,10 +112,11 @@ struct GemmArgs {
   bf16_t* branch;         // if non-null: the product before the residual add [M, N]
 };
 void launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t s);
-// K slices (1, 2 or 4) for an [M, N] x K product whose 256x256 tile grid alone
-// leaves the chip short of work; slice s writes fp32 partials at C + s*M*N
+// K slices (1, 2 or 4) for an [M, N] x K product (B in fp16 when b_f16) whose
+// tile grid alone leaves the chip short of work; slice s writes fp32 partials
+// at C + s*M*N
 constexpr int kMaxSplitK = 4;
-int gemm_split_k(int M, int N, int K);
+int gemm_split_k(int M, int N, int K, bool b_f16);
 
 // ---------------------------------------------------------------- k_gemv.hip
 // partial[ks][M][N] (fp32) = X[M, kslice] * W[N, kslice]^T (bf16, M <= 64),
