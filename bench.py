@@ -28,7 +28,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 PREFILL_PHASES = ["rms_x", "qkv_gemm_rope_append", "attention_prefill", "wo_gemm_residual", "rms_h",
                   "w13_gemm_swiglu", "w2_gemm_residual"]
 DECODE_PHASES = ["qkv_gemv_and_x_stats", "qkv_finish_rope_append", "attention_decode", "wo_gemv",
-                 "wo_residual_h_stats", "w13_gemv", "swiglu", "w2_gemv", "w2_residual"]
+                 "wo_residual_h_stats", "w13_gemv_swiglu", "w2_gemv", "w2_residual"]
 
 
 def log(*a):
@@ -177,7 +177,7 @@ def bench_decode(wl, steps, warmup):
     kv_bytes = sum(b["kv_read"] + b["kv_write"] for b in byts) / steps
     attn_us = att_ms[att] / acalls * 1e3
     lb = {0: s.dim * (s.n_heads + 2 * s.n_kv_heads) * s.head_dim, 3: s.n_heads * s.head_dim * s.dim,
-          5: 2 * s.dim * s.ffn_dim, 7: s.ffn_dim * s.dim}
+          5: 2 * s.dim * s.ffn_dim, 6: s.ffn_dim * s.dim}
     esz = 2 if s.dtype == "bf16" else 4
 
     def gbs(i, avg_ms):

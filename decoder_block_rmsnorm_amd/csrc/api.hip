@@ -484,8 +484,7 @@ static const int kSplitLen = 256;  // keys per decode-attention chunk
 // At M > 16 (64-row activation tiles) the fp32 partials cost 4 * ks * M / K of
 // the weight bytes, so fewer blocks are asked for (measured at M = 16 and 64).
 static int gemv_ks(int M, int N, int K) {
-  const int cols = (M > 16 && N % 128 == 0) ? 128 : 64;
-  const int tiles = N / cols;
+  const int tiles = N / gemv_cols(M, N);
   const int nchk = tiled_chunks(K);
   const int target = M > 16 ? 256 : 384;
   int ks = 1;
@@ -789,10 +788,16 @@ static void bf16_decode(const llama_block* blk, KVView kv, const void* x, void* 
     mk(s);
     launch_epi_resid<bf16_t>(part, ks, B, d.D, (const bf16_t*)x, h, ssh, nullptr, 0, 0, nullptr, s);
     mk(s);
+    // enough column tiles to fill the chip unsplit: SwiGLU in the GEMV itself
     ks = gemv_ks(B, 2 * d.F, d.D);
-    launch_gemv_bf16(h, (const bf16_t*)blk->w13.w, true, part, B, 2 * d.F, d.D, ks, nullptr, s);
-    mk(s);
-    launch_epi_swiglu<bf16_t>(part, ks, B, 2 * d.F, d.IB, sth, g, s);
+    if (ks == 1) {
+      GemvSwiglu sw{};
+      sw.stat = sth; sw.ib = d.IB; sw.g_out = g;
+      launch_gemv_swiglu(h, (const bf16_t*)blk->w13.w, B, 2 * d.F, d.D, sw, s);
+    } else {
+      launch_gemv_bf16(h, (const bf16_t*)blk->w13.w, true, part, B, 2 * d.F, d.D, ks, nullptr, s);
+      launch_epi_swiglu<bf16_t>(part, ks, B, 2 * d.F, d.IB, sth, g, s);
+    }
     mk(s);
     ks = gemv_ks(B, d.D, d.F);
     launch_gemv_bf16(g, (const bf16_t*)blk->w2.w, true, part, B, d.D, d.F, ks, nullptr, s);

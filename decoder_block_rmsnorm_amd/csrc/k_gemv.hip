@@ -6,7 +6,9 @@
 //   weight rows straight from HBM into MFMA B-operand registers with 128-bit
 //   loads (8 per lane in flight per 256-wide K chunk, prefetched one chunk
 //   ahead), while the activations of the chunk sit in LDS for all four
-//   wavefronts.  fp32 partials [ks][M][N] go to a reduce-and-finish kernel.
+//   wavefronts.  fp32 partials [ks][M][N] go to a reduce-and-finish kernel,
+//   or, unsplit (ks = 1), the W1/W3 product is finished in place: RMSNorm row
+//   scale and silu(gate) * up (EPI_SWIGLU).
 //
 // k_gemv_q4: 4-bit group-affine weights (group 64 along the input dim, the MLX
 //   quantization config of "模型配置"): W = s * code + b.  Per 8-code word,
@@ -42,18 +44,18 @@ constexpr int XST = KC + 8;     // LDS row stride (bf16)
 // contiguous kilobyte; the padding of the last chunk is zero) or row-major
 // [N][K].  K slice ksi of ks covers the 256-column chunks
 // [ksi * nchk / ks, (ksi + 1) * nchk / ks).  K is a multiple of 8.
-template <int NW, int MT, bool TILED>
+template <int NW, int MT, bool TILED, bool SS, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemv_bf16(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, float* __restrict__ part, int M, int N, int K, int ks,
-    float* __restrict__ ss_out) {
+    float* __restrict__ ss_out, GemvSwiglu e) {
   using namespace gv;
   constexpr int ROWS = MT * 16;
   constexpr int XL = ROWS * (KC / 8) / 256;   // 16-byte activation pieces per thread per chunk
   __shared__ __attribute__((aligned(16))) bf16_t xs[2][ROWS * XST];
-  // the first column-block of each K slice also sums x^2 of the rows it stages
-  // (the RMSNorm statistic of the input, reduced over slices by its consumer):
-  // each thread accumulates the squares of its own activation pieces
-  const bool do_ss = ss_out != nullptr && blockIdx.x == 0;
+  // SS: the first column-block of each K slice also sums x^2 of the rows it
+  // stages (the RMSNorm statistic of the input, reduced over slices by its
+  // consumer); each thread accumulates the squares of its own activation pieces
+  const bool do_ss = SS && blockIdx.x == 0;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, hg = lane >> 4;
   float ssp[XL];
@@ -131,10 +133,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
   // buffer reuse: a chunk's activations are stored into the LDS buffer read
   // two computes earlier, with a barrier in between
+  // EPI_SWIGLU: 1/rms of the input rows, from the producer's partial sums of
+  // squares (four threads per row, each over every fourth partial, combined in
+  // a fixed order), requested once the first chunks are on their way
+  __shared__ float s_r[ROWS];
+  auto row_scale = [&]() {
+    const int m = tid >> 2, qq = tid & 3;
+    float t = 0.f;
+    if (m < M) {
+      if (e.stat.inv) {
+        if (qq == 0) t = e.stat.inv[m];
+      } else {
+        for (int b = qq; b < e.stat.nb; b += 4) t += e.stat.ss[(size_t)b * e.stat.M + m];
+      }
+    }
+    t += __shfl_xor(t, 1);
+    t += __shfl_xor(t, 2);
+    if (m < ROWS && qq == 0) s_r[m] = e.stat.inv ? t : 1.0f / sqrtf(t / (float)e.stat.n + e.stat.eps);
+  };
+
   if (nch >= 2) {
     xload(0);
     wload(0, w0);
     wload(1, w1);
+    if constexpr (EPI == EPI_SWIGLU) row_scale();
     xstore(0);
     __syncthreads();
     int c = 0;
@@ -168,6 +190,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   } else if (nch == 1) {
     xload(0);
     wload(0, w0);
+    if constexpr (EPI == EPI_SWIGLU) row_scale();
     xstore(0);
     __syncthreads();
     compute(0, w0);
@@ -184,45 +207,85 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
   }
   // lane: C[m = 16*mt + 4*hg + i][n = nrow0 + 16*j + l16]
-  float* pp = part + (size_t)ksi * M * N;
+  if constexpr (EPI == EPI_F32) {
+    float* pp = part + (size_t)ksi * M * N;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = mt * 16 + 4 * hg + i;
-      if (m < M) {
+      for (int i = 0; i < 4; ++i) {
+        const int m = mt * 16 + 4 * hg + i;
+        if (m < M) {
 #pragma unroll
-        for (int j = 0; j < NW; ++j) pp[(size_t)m * N + nrow0 + 16 * j + l16] = acc[mt][j][i];
+          for (int j = 0; j < NW; ++j) pp[(size_t)m * N + nrow0 + 16 * j + l16] = acc[mt][j][i];
+        }
       }
+    }
+  } else {
+    // the block's 64*NW rows hold whole (w1 block, w3 block) pairs of ib rows:
+    // stage them as [row][m] (padded) in the activation buffers' LDS
+    constexpr int LS = ROWS + 1;
+    float* stage = reinterpret_cast<float*>(&xs[0][0]);
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < NW; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) stage[(16 * NW * wave + 16 * j + l16) * LS + mt * 16 + 4 * hg + i] = acc[mt][j][i];
+    __syncthreads();
+    constexpr int OUT = 32 * NW;  // outputs per row from this block
+    const int F = N >> 1, ib = e.ib, j0 = blockIdx.x * OUT, r0 = blockIdx.x * 64 * NW;
+    for (int p = tid; p < OUT * M; p += 256) {
+      const int m = p / OUT, jg = j0 + p % OUT;
+      const int ra = (jg / ib) * 2 * ib + jg % ib - r0;
+      const float r = s_r[m];
+      const float a = stage[ra * LS + m] * r, b = stage[(ra + ib) * LS + m] * r;
+      Elt<bf16_t>::store(e.g_out, (size_t)m * F + jg, silu_f(a) * b);
     }
   }
 }
 
-template <bool TILED>
-static void gemv_dispatch(const bf16_t* X, const bf16_t* W, float* partial, int M, int N, int K, int ks,
-                          float* ss_out, hipStream_t s) {
-  if (M > 16 && (N % 128) == 0) {
-    dim3 grid(N / 128, ks);
-    if (M <= 32)
-      hipLaunchKernelGGL((k_gemv_bf16<2, 2, TILED>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ks, ss_out);
-    else
-      hipLaunchKernelGGL((k_gemv_bf16<2, 4, TILED>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ks, ss_out);
-  } else {
-    dim3 grid(N / 64, ks);
-    if (M <= 16)
-      hipLaunchKernelGGL((k_gemv_bf16<1, 1, TILED>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ks, ss_out);
-    else if (M <= 32)
-      hipLaunchKernelGGL((k_gemv_bf16<1, 2, TILED>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ks, ss_out);
-    else
-      hipLaunchKernelGGL((k_gemv_bf16<1, 4, TILED>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ks, ss_out);
-  }
+int gemv_cols(int M, int N) { return (M > 16 && (N % 128) == 0) ? 128 : 64; }
+
+template <int NW, bool TILED, bool SS, int EPI>
+static void gemv_mt(const bf16_t* X, const bf16_t* W, float* partial, int M, int N, int K, int ks, float* ss_out,
+                    const GemvSwiglu& e, hipStream_t s) {
+  dim3 grid(N / (64 * NW), ks);
+  if (M <= 16)
+    hipLaunchKernelGGL((k_gemv_bf16<NW, 1, TILED, SS, EPI>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ks,
+                       ss_out, e);
+  else if (M <= 32)
+    hipLaunchKernelGGL((k_gemv_bf16<NW, 2, TILED, SS, EPI>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ks,
+                       ss_out, e);
+  else
+    hipLaunchKernelGGL((k_gemv_bf16<NW, 4, TILED, SS, EPI>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ks,
+                       ss_out, e);
+}
+
+template <bool TILED, bool SS>
+static void gemv_nw(const bf16_t* X, const bf16_t* W, float* partial, int M, int N, int K, int ks, float* ss_out,
+                    hipStream_t s) {
+  const GemvSwiglu none{};
+  if (gemv_cols(M, N) == 128) gemv_mt<2, TILED, SS, EPI_F32>(X, W, partial, M, N, K, ks, ss_out, none, s);
+  else gemv_mt<1, TILED, SS, EPI_F32>(X, W, partial, M, N, K, ks, ss_out, none, s);
 }
 
 void launch_gemv_bf16(const bf16_t* X, const bf16_t* W, bool tiled, float* partial, int M, int N, int K, int ks,
                       float* ss_out, hipStream_t s) {
   if (M <= 0 || N <= 0) return;
-  if (tiled) gemv_dispatch<true>(X, W, partial, M, N, K, ks, ss_out, s);
-  else gemv_dispatch<false>(X, W, partial, M, N, K, ks, ss_out, s);
+  if (tiled) {
+    if (ss_out) gemv_nw<true, true>(X, W, partial, M, N, K, ks, ss_out, s);
+    else gemv_nw<true, false>(X, W, partial, M, N, K, ks, ss_out, s);
+  } else {
+    gemv_nw<false, false>(X, W, partial, M, N, K, ks, nullptr, s);
+  }
+}
+
+void launch_gemv_swiglu(const bf16_t* X, const bf16_t* W, int M, int N, int K, const GemvSwiglu& e,
+                        hipStream_t s) {
+  if (M <= 0 || N <= 0) return;
+  if (gemv_cols(M, N) == 128) gemv_mt<2, true, false, EPI_SWIGLU>(X, W, nullptr, M, N, K, 1, nullptr, e, s);
+  else gemv_mt<1, true, false, EPI_SWIGLU>(X, W, nullptr, M, N, K, 1, nullptr, e, s);
 }
 
 // ===========================================================================

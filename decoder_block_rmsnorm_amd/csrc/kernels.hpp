@@ -125,6 +125,18 @@ int gemm_split_k(int M, int N, int K, bool b_f16);
 // ss_out (optional): sum of squares of each X row over each K slice, [ks][M].
 void launch_gemv_bf16(const bf16_t* X, const bf16_t* W, bool tiled, float* partial, int M, int N, int K, int ks,
                       float* ss_out, hipStream_t s);
+// columns of W per GEMV block (64 or 128)
+int gemv_cols(int M, int N);
+// g[M][N/2] (bf16) = silu(y1 * r) * (y3 * r) for y = X W^T over all of K
+// (W tiled, rows interleaved in blocks of ib: w1 rows, then the same w3 rows),
+// r = 1/rms of row m from stat.  No scratch.
+struct GemvSwiglu {
+  RowStat stat;
+  int ib;
+  bf16_t* g_out;
+};
+void launch_gemv_swiglu(const bf16_t* X, const bf16_t* W, int M, int N, int K, const GemvSwiglu& e,
+                        hipStream_t s);
 // y[M][N] (fp32) = xhat W^T, W 4-bit group affine, xhat = x * r * gamma, M <= 4.
 // norm: 0 = no RMSNorm (r = 1, gamma unused), 1 = r from the row itself (eps),
 // 2 = r from `stat`.  xh_buf: fp16 [M, K]; xsum_buf: fp32 [M, K/32, 2] (scratch).

@@ -159,8 +159,8 @@ llama_status llama_block_set_diag(llama_block* blk, int32_t enable);
  *   fp32         : rms(x), qkv projection, qkv finish, attention, wo projection,
  *                  residual, w1/w3 projection, swiglu, w2 projection, residual (10)
  *   bf16 decode  : qkv projection (+ x statistics), qkv finish, attention,
- *                  wo projection, residual (+ h statistics), w1/w3 projection,
- *                  swiglu, w2 projection, residual                          (9)
+ *                  wo projection, residual (+ h statistics), w1/w3
+ *                  projection + swiglu, w2 projection, residual             (8)
  * Not for calls captured into a graph. */
 llama_status llama_block_profile_start(llama_block* blk, int32_t max_calls, uint32_t phase_mask);
 llama_status llama_block_profile_read(llama_block* blk, float* phase_ms, int32_t max_phases, int32_t* n_phases,
