@@ -151,18 +151,32 @@ def test_bf16_prefill_gqa_with_cached_prefix():
     _check_branches(s, blk, sc, r, y, 2, 200)
 
 
-@pytest.mark.parametrize("shape", ["mha", "gqa"])
+# 64 sequences x 4 kv heads of 8 query heads each: the decode attention
+# lengthens its key splits past 256 (to about one resident round of
+# wavefronts), here to 320-key splits over ragged lengths
+WIDE_GQA = W.BlockShape(dim=4096, n_heads=32, n_kv_heads=4, ffn_dim=512, dtype="bf16")
+
+
+def _long_split_lens():
+    r = W.Rng(21)
+    return [int(v) for v in r.g.integers(1, 2300, size=60)] + [1, 319, 320, 2301]
+
+
+@pytest.mark.parametrize("shape", ["mha", "gqa", "gqa_long_splits"])
 def test_bf16_decode_ragged_lengths(shape):
-    s = dataclasses.replace(SMALL_MHA if shape == "mha" else SMALL_GQA, traditional=(shape == "mha"))
+    if shape == "gqa_long_splits":
+        s, lens = WIDE_GQA, _long_split_lens()
+    else:
+        s = dataclasses.replace(SMALL_MHA if shape == "mha" else SMALL_GQA, traditional=(shape == "mha"))
+        lens = [300, 1, 64, 255, 257]
     rng = W.Rng(13)
-    lens = [300, 1, 64, 255, 257]
-    B = len(lens)
+    B, S = len(lens), max(lens)
     x = rng.normal((B, 1, s.dim), 1.0, "bf16")
-    kv = (rng.normal((B, 300, s.n_kv_heads, s.head_dim), 1.0, "bf16"),
-          rng.normal((B, 300, s.n_kv_heads, s.head_dim), 1.0, "bf16"))
+    kv = (rng.normal((B, S, s.n_kv_heads, s.head_dim), 1.0, "bf16"),
+          rng.normal((B, S, s.n_kv_heads, s.head_dim), 1.0, "bf16"))
     w = W.draw_block_weights(s, rng)
     _flush(f"case: bf16 {shape} decode B={B} lens={lens}")
-    max_seq = 320
+    max_seq = (S + 1 + 63) // 64 * 64
     blk, wd = G.make_block(s, w, max_seq)
     cache = G.make_cache(s, 1, B, max_seq)
     for b in range(B):
