@@ -488,20 +488,17 @@ static int attn_split_len(const Dims& d, int B, int maxlen) {
   return std::max(kSplitLen, (sl + 63) / 64 * 64);
 }
 
-// Split-K factor of a decode projection [M rows] x [N, K]: enough blocks to
-// cover the chip several times over, K slices that stay multiples of 32 and at
-// least 512 long.
-// K slices of a decode GEMV: double while the grid is short of the block
-// count that keeps HBM busy and each slice keeps at least four 256-wide chunks.
-// At M > 16 (64-row activation tiles) the fp32 partials cost 4 * ks * M / K of
-// the weight bytes, so fewer blocks are asked for (measured at M = 16 and 64).
+// K slices of a decode GEMV (any count; slices are runs of whole 256-wide
+// chunks, at least four each).  The grid is sized to one pass of blocks over
+// the chip: 256 blocks (one per CU) at M > 16, whose blocks hold 64 activation
+// rows, 512 at M <= 16, twice that for a K of 64 chunks or more (measured on
+// the 13B- and 70B-shaped projections at M = 16 and 64: a partly filled second
+// round of blocks costs more than fewer, longer slices).
 static int gemv_ks(int M, int N, int K) {
   const int tiles = N / gemv_cols(M, N);
   const int nchk = tiled_chunks(K);
-  const int target = M > 16 ? 256 : 384;
-  int ks = 1;
-  while (tiles * ks < target && 4 * ks <= nchk) ks *= 2;
-  return ks;
+  const int target = (M > 16 ? 256 : 512) * (nchk >= 64 ? 2 : 1);
+  return std::max(1, std::min(target / tiles, nchk / 4));
 }
 
 struct SLayout {
