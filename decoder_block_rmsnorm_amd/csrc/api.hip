@@ -213,7 +213,7 @@ static void repack_linear(const Dims& d, int dt, const Lin& dst, const llama_lin
                               perm_d, 0, s);
   } else {
     launch_repack_rows<bf16_t>((bf16_t*)dst.w, (const bf16_t*)src.w, rows, K, (const bf16_t*)gamma, row0, ib,
-                               ib_stride, perm_d, 1, s);
+                               ib_stride, perm_d, dst.N / 16, s);
   }
 }
 

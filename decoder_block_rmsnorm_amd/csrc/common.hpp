@@ -120,17 +120,21 @@ __device__ inline float warp_max(float v) {
 __device__ inline float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
 // 16-byte vector load/store helpers.
-// Tiled layout of the bf16 dense weights [N][K]: 16-row groups by 256-column
-// chunks, each (group, chunk) tile 8 KB contiguous, chunks of a group in order.
-// Inside a tile, the 32-column block kb is 1 KB holding 64 pieces of 16 bytes:
-// piece 16*j + r = row r of the group, columns 32*kb + 8*j .. 8*j + 7.  One
-// wavefront-wide 16-byte load of a block (lane = piece) is then one contiguous
-// kilobyte and lands as the B operand of v_mfma_f32_16x16x32_bf16 (lane l holds
+// Tiled layout of the bf16 dense weights [N][K] (N a multiple of 16): 16-row
+// groups by 256-column chunks, each (group, chunk) tile 8 KB contiguous, stored
+// chunk-major: tile (g, c) at (c * ngroups + g) * 8 KB, so that all the groups'
+// tiles of one chunk form one contiguous region (a grid streaming the matrix
+// chunk by chunk sweeps memory in address order).  Inside a tile, the
+// 32-column block kb is 1 KB holding 64 pieces of 16 bytes: piece 16*j + r =
+// row r of the group, columns 32*kb + 8*j .. 8*j + 7.  One wavefront-wide
+// 16-byte load of a block (lane = piece) is then one contiguous kilobyte and
+// lands as the B operand of v_mfma_f32_16x16x32_bf16 (lane l holds
 // B[k = 8*(l/16) + e][n = l%16]).  K is padded to a multiple of 256 (kTileK).
 constexpr int kTileK = 256;
+constexpr int kTileElems = kTileK * 16;  // bf16 per (group, chunk) tile
 __host__ __device__ inline int tiled_chunks(int K) { return (K + kTileK - 1) / kTileK; }
-__host__ __device__ inline size_t tiled_off(int n, int k, int nchk) {
-  return ((((size_t)(n >> 4) * nchk + (k >> 8)) * 8 + ((k >> 5) & 7)) * 64 + (((k >> 3) & 3) * 16 + (n & 15))) * 8 +
+__host__ __device__ inline size_t tiled_off(int n, int k, int ngroups) {
+  return ((((size_t)(k >> 8) * ngroups + (n >> 4)) * 8 + ((k >> 5) & 7)) * 64 + (((k >> 3) & 3) * 16 + (n & 15))) * 8 +
          (k & 7);
 }
 

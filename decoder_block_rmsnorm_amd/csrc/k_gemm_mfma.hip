@@ -124,11 +124,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
   const int K = a.K;                          // row stride of A and B
   const int Kslice = a.K / (a.ksplit > 0 ? a.ksplit : 1);
   // B: fp16 row-major [N][K] (dequantized 4-bit weights) or bf16 in the tiled
-  // layout, where column k of a 16-row group sits at (k / 32) * 512 + ... and
-  // a 64-wide K step of one group is 2 KB contiguous
-  const int nchk = tiled_chunks(a.K);
-  const bf16_t* Ag = a.A + (size_t)ksi * Kslice;
-  const bf16_t* Bg = a.B + (size_t)ksi * Kslice * (F16 ? 1 : 16);
+  // layout (chunk-major): the 32-column block holding column k of 16-row group
+  // g sits at tblk(k) + g * kTileElems, and a 64-wide K step that starts on a
+  // multiple of 64 stays inside one chunk (2 KB of each group)
+  const int ngr = N >> 4;
+  auto tblk = [&](int k) { return (size_t)(k >> 8) * ngr * kTileElems + ((k >> 5) & 7) * 512; };
+  const int kslice0 = ksi * Kslice;
+  const bf16_t* Ag = a.A + (size_t)kslice0;
+  const bf16_t* Bg = a.B + (F16 ? (size_t)kslice0 : 0);
   const int per_group = GROUP_M * tiles_n;
   const int group = bid / per_group;
   const int first_m = group * GROUP_M;
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
   // element offsets (operands are < 2^31 elements), so each load needs one VGPR
   // of address instead of two.
   const bf16_t* Atile = Ag + (size_t)m0 * K;
-  const bf16_t* Btile = Bg + (F16 ? (size_t)n0 * K : (size_t)(n0 >> 4) * nchk * (kTileK * 16));
+  const bf16_t* Btile = Bg + (F16 ? (size_t)n0 * K : (size_t)(n0 >> 4) * kTileElems);
   uint32_t aoff[A_CH], boff[B_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
@@ -162,12 +165,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
       boff[i] = (uint32_t)((c >> 3) * K + (c & 7) * 8);
     } else {
       // piece c of a K step: group c / 128, 1 KB block (c / 64) % 2, lane c % 64
-      boff[i] = (uint32_t)((c >> 7) * nchk * (kTileK * 16) + ((c >> 6) & 1) * 512 + (c & 63) * 8);
+      boff[i] = (uint32_t)((c >> 7) * kTileElems + ((c >> 6) & 1) * 512 + (c & 63) * 8);
     }
   }
   auto gload = [&](int kt, uint4(&ra)[A_CH], uint4(&rb)[B_CH]) {
     const bf16_t* at = Atile + kt * BK;
-    const bf16_t* bt = Btile + (size_t)kt * BK * (F16 ? 1 : 16);
+    const bf16_t* bt = Btile + (F16 ? (size_t)kt * BK : tblk(kslice0 + kt * BK));
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) ra[i] = ld16(at + aoff[i]);
 #pragma unroll
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < AG; ++i) voa[i] = (uint32_t)(min(m0 + 16 * (wv * AG + i) + r16, M - 1) * K + 8 * j4) * 2;
 #pragma unroll
-    for (int i = 0; i < BG; ++i) vob[i] = (uint32_t)(((wv * BG + i) * nchk * (kTileK * 16) + lane * 8) * 2);
+    for (int i = 0; i < BG; ++i) vob[i] = (uint32_t)(((wv * BG + i) * kTileElems + lane * 8) * 2);
     const char* abase = (const char*)Ag;
     const char* bbase = (const char*)Btile;
     // direct load number idx (0 .. LPS-1) of step kt: 32-column block
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
       if (is_a)
         lds_dma16(voa[i], abase + (size_t)(kt * BKS + kb * 32) * 2, la + (kb * (BM / 16) + wv * AG + i) * 1024);
       else
-        lds_dma16(vob[i], bbase + (size_t)(kt * NKB + kb) * 1024, la + SA * 2 + (kb * 16 + wv * BG + i) * 1024);
+        lds_dma16(vob[i], bbase + tblk(kslice0 + kt * BKS + kb * 32) * 2, la + SA * 2 + (kb * 16 + wv * BG + i) * 1024);
     };
     // lane's piece inside a pair of groups: fragment rows 32t + l%32, k = 8*(l/32)
     const int fpiece = (16 * (lane >> 5) + r16) * 8 + ((lane >> 4) & 1) * 512;

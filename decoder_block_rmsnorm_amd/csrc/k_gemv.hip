@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
       if constexpr (TILED) {
-        const bf16_t* t = W + ((size_t)((nrow0 >> 4) + j) * nchk + c0 + c) * (KC * 16) + lane * 8;
+        const bf16_t* t = W + ((size_t)(c0 + c) * (N >> 4) + (nrow0 >> 4) + j) * kTileElems + lane * 8;
 #pragma unroll
         for (int kc = 0; kc < 8; ++kc) w[j][kc] = ld16(t + 512 * kc);
       } else {

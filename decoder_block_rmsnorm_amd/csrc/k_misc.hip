@@ -199,29 +199,28 @@ __device__ inline int repack_dst_row(int r, int row0, int ib, int ib_stride, int
 // tiled != 0: destination in the tiled layout (row-major otherwise)
 template <typename T>
 __global__ __launch_bounds__(256) void k_repack_rows(T* dst, const T* src, int rows, int K, const T* gamma,
-                                                     int row0, int ib, int ib_stride, int perm_d, int tiled) {
+                                                     int row0, int ib, int ib_stride, int perm_d, int tgroups) {
   int r = blockIdx.x;
   int dr = repack_dst_row(r, row0, ib, ib_stride, perm_d);
-  const int nchk = tiled_chunks(K);
-  // the tiled layout's padding past K is written as zeros: readers may take
-  // whole chunks
-  const int kend = tiled ? nchk * kTileK : K;
+  // tgroups > 0: tiled layout of a [16 * tgroups][K] matrix, whose padding past
+  // K is written as zeros (readers may take whole chunks)
+  const int kend = tgroups ? tiled_chunks(K) * kTileK : K;
   for (int c = threadIdx.x; c < kend; c += 256) {
     float v = 0.f;
     if (c < K) {
       v = Elt<T>::load(src, (size_t)r * K + c);
       if (gamma) v *= Elt<T>::load(gamma, c);
     }
-    Elt<T>::store(dst, tiled ? tiled_off(dr, c, nchk) : (size_t)dr * K + c, v);
+    Elt<T>::store(dst, tgroups ? tiled_off(dr, c, tgroups) : (size_t)dr * K + c, v);
   }
 }
 
 template <typename T>
 void launch_repack_rows(T* dst, const T* src, int rows, int K, const T* gamma, int row0, int ib, int ib_stride,
-                        int perm_d, int tiled, hipStream_t s) {
+                        int perm_d, int tgroups, hipStream_t s) {
   if (rows <= 0) return;
   hipLaunchKernelGGL(k_repack_rows<T>, dim3(rows), dim3(256), 0, s, dst, src, rows, K, gamma, row0, ib,
-                     ib_stride, perm_d, tiled);
+                     ib_stride, perm_d, tgroups);
 }
 
 __global__ __launch_bounds__(256) void k_repack_bytes(uint8_t* dst, const uint8_t* src, int rows, int rb,

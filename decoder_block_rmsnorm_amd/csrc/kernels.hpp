@@ -65,9 +65,10 @@ void launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
 // (local index j -> j/2 for even j, perm_d/2 + j/2 for odd j: interleaved pairs
 // become (i, i + d/2) pairs), then lands at dst row row0 + (r'/ib)*ib_stride + r'%ib.
 // gamma (optional, length K) scales the columns (norm weight folding).
+// tgroups > 0: dst is in the tiled layout of a [16 * tgroups][K] matrix.
 template <typename T>
 void launch_repack_rows(T* dst, const T* src, int rows, int K, const T* gamma, int row0, int ib,
-                        int ib_stride, int perm_d, int tiled, hipStream_t s);
+                        int ib_stride, int perm_d, int tgroups, hipStream_t s);
 void launch_repack_bytes(uint8_t* dst, const uint8_t* src, int rows, int row_bytes, int row0, int ib,
                          int ib_stride, int perm_d, hipStream_t s);
 // dense fp16 [N, K] = (scale * code + bias) * gamma_k (gamma may be null)
