@@ -106,6 +106,10 @@ struct KVView {
   }
 };
 
+// Workgroup barrier for LDS communication: waits for this wave's LDS accesses,
+// not for its global loads in flight.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ inline float warp_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

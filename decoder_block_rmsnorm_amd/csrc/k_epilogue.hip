@@ -40,18 +40,28 @@ __global__ __launch_bounds__(64) void k_epi_qkv(const float* part, int ks, int M
   int head = blockIdx.y;          // 0..H-1 q, H..H+G-1 k, then v
   int d = kv.d, half = d >> 1;
   int i = threadIdx.x;
-  float r = stat.get_block(m);
-  if (i >= half) return;
+  const bool act = i < half;
   int N = Nq + 2 * Nkv;
   size_t stride = (size_t)M * N;
   int c0 = head * d;
-  float a = sum_parts(part, ks, stride, (size_t)m * N + c0 + i) * r;
-  float b = sum_parts(part, ks, stride, (size_t)m * N + c0 + i + half) * r;
   int bseq = m / L, l = m % L;
   int pos = kv.lens[bseq] + l;
   int H = Nq / d;
+  // the statistic's partials, the slices and the rotation factors are
+  // requested together, then the row scale is shared
+  const float pv = stat.pre(m);
+  float a = 0.f, b = 0.f;
+  float2 cs = make_float2(1.f, 0.f);
+  if (act) {
+    a = sum_parts(part, ks, stride, (size_t)m * N + c0 + i);
+    b = sum_parts(part, ks, stride, (size_t)m * N + c0 + i + half);
+    if (c0 < Nq + Nkv) cs = rope[(size_t)pos * half + i];
+  }
+  const float r = stat.finish_block(pv);
+  if (!act) return;
+  a *= r;
+  b *= r;
   if (c0 < Nq + Nkv) {
-    float2 cs = rope[(size_t)pos * half + i];
     float a2 = a * cs.x - b * cs.y;
     float b2 = b * cs.x + a * cs.y;
     a = a2;
@@ -136,14 +146,18 @@ __global__ __launch_bounds__(256) void k_epi_swiglu(const float* part, int ks, i
   int m = blockIdx.y;
   int F = F2 >> 1;
   int j = blockIdx.x * 256 + threadIdx.x;
-  float r = stat.get_block(m);
-  if (j >= F) return;
   size_t stride = (size_t)M * F2;
   int jb = j / ib, w = j % ib;
   int cg = jb * 2 * ib + w;
-  float a = sum_parts(part, ks, stride, (size_t)m * F2 + cg) * r;
-  float b = sum_parts(part, ks, stride, (size_t)m * F2 + cg + ib) * r;
-  Elt<T>::store(g_out, (size_t)m * F + j, silu_f(a) * b);
+  const float pv = stat.pre(m);
+  float a = 0.f, b = 0.f;
+  if (j < F) {
+    a = sum_parts(part, ks, stride, (size_t)m * F2 + cg);
+    b = sum_parts(part, ks, stride, (size_t)m * F2 + cg + ib);
+  }
+  const float r = stat.finish_block(pv);
+  if (j >= F) return;
+  Elt<T>::store(g_out, (size_t)m * F + j, silu_f(a * r) * (b * r));
 }
 
 template <typename T>

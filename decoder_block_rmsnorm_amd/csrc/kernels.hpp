@@ -14,24 +14,34 @@ struct RowStat {
   float eps = 0.f;
   // 1/rms of row m, computed by the first wavefront of the block (its lanes
   // sum the nb partials) and shared: every thread of the block must call it,
-  // with the same m, before any thread leaves.
-  __device__ inline float get_block(int m) const {
+  // with the same m, before any thread leaves.  In two halves so that a caller
+  // can request its own loads in between: pre() requests this thread's share
+  // of the partials, finish_block() reduces them and shares the result through
+  // LDS (a barrier that waits for LDS traffic only, not for loads in flight).
+  __device__ inline float pre(int m) const {
+    float v = 0.f;
+    if (threadIdx.x < 64) {
+      if (inv) {
+        if (threadIdx.x == 0) v = inv[m];
+      } else if (ss) {
+        if ((int)threadIdx.x < nb) v = ss[(size_t)threadIdx.x * M + m];
+        for (int j = threadIdx.x + 64; j < nb; j += 64) v += ss[(size_t)j * M + m];
+      }
+    }
+    return v;
+  }
+  __device__ inline float finish_block(float v) const {
     __shared__ float s_r;
     if (threadIdx.x < 64) {
-      float v = 1.0f;
-      if (inv) {
-        v = inv[m];
-      } else if (ss) {
-        float t = 0.f;
-        for (int j = threadIdx.x; j < nb; j += 64) t += ss[(size_t)j * M + m];
-        t = warp_sum(t);
-        v = 1.0f / sqrtf(t / (float)n + eps);
-      }
-      if (threadIdx.x == 0) s_r = v;
+      float r = 1.0f;
+      if (inv) r = warp_sum(v);
+      else if (ss) r = 1.0f / sqrtf(warp_sum(v) / (float)n + eps);
+      if (threadIdx.x == 0) s_r = r;
     }
-    __syncthreads();
+    lds_barrier();
     return s_r;
   }
+  __device__ inline float get_block(int m) const { return finish_block(pre(m)); }
 };
 
 // Launch-attached timing events (profiling aid).  When set, the prefill GEMM
