@@ -200,6 +200,69 @@ def bench_decode(wl, steps, warmup):
     }
 
 
+def bench_stack(wl, reps):
+    """The 40-layer 4-bit stack: embedding, blocks, final norm, output head and
+    greedy argmax, each call on one stream with its decode step replayed from a
+    HIP graph.  Prompt pass = a call with one greedy step; decode step time =
+    (call with n steps - call with 1 step) / (n - 1), which leaves the prompt
+    pass and the graph capture out.  Best of `reps` calls each."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import decoder_block_rmsnorm_amd as L
+    from tests import gpu_util as G
+    s, P, n = wl.shape, wl.seq_len, wl.decode_steps
+    max_seq = P + n
+    t0 = time.time()
+    blocks, keep = [], []
+    for item in W.draw_stack(wl, W.Rng(wl.seed)):
+        if item[0] == "ids":
+            ids = item[1]
+        elif item[0] == "layer":
+            blk, wd = G.make_block(s, item[2], max_seq)
+            blocks.append(blk)
+            del wd
+        else:
+            head = item[1]
+    emb, fn, out = G.tdev(head["embedding"], "bf16"), G.tdev(head["norm"], "bf16"), G.q4_dev(head["output"])
+    stack = L.Stack(blocks, emb, wl.vocab, fn, out)
+    log(f"[bench] {wl.name}: stack built in {time.time() - t0:.1f}s")
+    sc = torch.empty(stack.scratch_bytes(P, max_seq), dtype=torch.uint8, device="cuda")
+    prompt = torch.from_numpy(ids.reshape(-1).astype(np.int32)).cuda()
+    out_ids = torch.zeros(n + 1, dtype=torch.int32, device="cuda")
+    logits = torch.zeros((n + 1, wl.vocab), dtype=torch.float32, device="cuda")
+    st = torch.cuda.Stream()
+
+    def run(steps):
+        cache = G.make_cache(s, wl.n_layers, 1, max_seq)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(st):
+            e0.record(st)
+            stack.generate(cache, prompt, steps, out_ids, logits, sc, use_graph=True, stream=st)
+            e1.record(st)
+        torch.cuda.synchronize()
+        del cache
+        return e0.elapsed_time(e1)
+    run(1)
+    t1 = min(run(1) for _ in range(reps))
+    tn = min(run(n) for _ in range(reps))
+    step_ms = (tn - t1) / (n - 1)
+    prompt_ms = t1 - step_ms
+    # bytes of one step at the mean cache length: every weight and cached K/V
+    # byte once, plus the output head (4-bit) and the logits
+    mean_cached = P + n / 2
+    layer = W.decode_bytes(s, 1, int(mean_cached))["total"]
+    head_bytes = wl.vocab * s.dim * (0.5 + 2 * 2 / s.group_size) + wl.vocab * 4
+    step_bytes = wl.n_layers * layer + head_bytes
+    flops = wl.n_layers * W.prefill_flops(s, 1, P) + 2.0 * wl.vocab * s.dim   # head: last token only
+    return {"workload": wl.name, "prompt_tokens": P, "prompt_ms": round(prompt_ms, 3),
+            "prompt_tflops": round(flops / (prompt_ms * 1e-3) / 1e12, 1),
+            "decode_steps": n, "decode_us_per_step": round(step_ms * 1e3, 1),
+            "decode_tokens_per_s": round(1.0 / (step_ms * 1e-3), 1), "bytes_per_step": step_bytes,
+            "hbm_frac_step": round(step_bytes / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(wl, min_seconds):
     """The oracle, as it stands, timed on this host: the causal prefill of the
     whole prompt of the same workload, repeated until at least `min_seconds`
@@ -281,6 +344,8 @@ def main():
     ap.add_argument("--workload", default="llama7b_block_prefill_b1_l2048")
     ap.add_argument("--decode-workload", default="llama13b_block_decode_b16_kv4096",
                     help="decode workload reported beside the prefill line ('' to skip)")
+    ap.add_argument("--stack-workload", default="",
+                    help="also time the 40-layer 4-bit stack workload (prompt pass and greedy steps)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="minimum seconds of oracle time for the CPU baseline (0: skip)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -322,6 +387,12 @@ def main():
         dec = bench_decode(dw, args.steps, args.warmup)
         log(f"[bench] decode {dec['us_per_step']} us/step, {dec['tokens_per_s']} tok/s")
         out["decode"] = dec
+    if args.stack_workload:
+        sw = W.get(args.stack_workload)
+        torch.cuda.empty_cache()
+        log(f"[bench] stack {sw.name}")
+        out["stack"] = bench_stack(sw, 2)
+        log(f"[bench] stack decode {out['stack']['decode_us_per_step']} us/step")
     if args.cpu_seconds > 0:
         log(f"[bench] cpu oracle baseline, at least {args.cpu_seconds} s")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
