@@ -534,7 +534,9 @@ static SLayout scratch_layout(const llama_block_config& c, const Dims& d, int T,
     for (int i = 0; i < 4; ++i)
       part = std::max(part, (size_t)gemv_ks(T, NK[i][0], NK[i][1]) * T * NK[i][0] * 4);
   } else if (decode && d.q4) {
-    part = (size_t)T * maxN * 4;
+    // the single-row 4-bit GEMV may split long K ranges
+    const int ksq = std::max(gemv_q4_ks(T, d.D), std::max(gemv_q4_ks(T, d.Nq), gemv_q4_ks(T, d.F)));
+    part = (size_t)ksq * T * maxN * 4;
   } else {
     // prefill: wo / w2 split along K when their tile grid is small; a split
     // needs fewer than 200 tiles of 256 x 256, which bounds the rows it covers
@@ -824,21 +826,22 @@ static void bf16_decode(const llama_block* blk, KVView kv, const void* x, void* 
     };
     gq((const bf16_t*)x, 1, none, blk->gamma1, blk->qkv);
     mk(s);
-    launch_epi_qkv<bf16_t>(part, 1, B, d.Nq, d.Nkv, none, 1, blk->rope, blk->cfg.rope_traditional, q, kv, s);
+    launch_epi_qkv<bf16_t>(part, gemv_q4_ks(B, d.D), B, d.Nq, d.Nkv, none, 1, blk->rope, blk->cfg.rope_traditional,
+                           q, kv, s);
     mk(s);
     launch_attn_decode_bf16(q, kv, B, d.H, d.G, n_splits, split_len, ao, aml, attn, s);
     mk(s);
     gq(attn, 0, none, nullptr, blk->o);
     mk(s);
-    launch_epi_resid<bf16_t>(part, 1, B, d.D, (const bf16_t*)x, h, ssh, nullptr, 0, 0, nullptr, s);
+    launch_epi_resid<bf16_t>(part, gemv_q4_ks(B, d.Nq), B, d.D, (const bf16_t*)x, h, ssh, nullptr, 0, 0, nullptr, s);
     mk(s);
     gq(h, 2, sth, blk->gamma2, blk->w13);
     mk(s);
-    launch_epi_swiglu<bf16_t>(part, 1, B, 2 * d.F, d.IB, none, g, s);
+    launch_epi_swiglu<bf16_t>(part, gemv_q4_ks(B, d.D), B, 2 * d.F, d.IB, none, g, s);
     mk(s);
     gq(g, 0, none, nullptr, blk->w2);
     mk(s);
-    launch_epi_resid<bf16_t>(part, 1, B, d.D, h, (bf16_t*)y, nullptr, kv.lens, 1, B, ffn, s);
+    launch_epi_resid<bf16_t>(part, gemv_q4_ks(B, d.F), B, d.D, h, (bf16_t*)y, nullptr, kv.lens, 1, B, ffn, s);
     mk(s);
   }
 }
@@ -945,6 +948,7 @@ static llama_status head_enqueue(const llama_linear* head, int wf, int gs, int d
   char* sc = (char*)scratch;
   float* out = logits ? logits : (float*)(sc + L.logits);
   if (wf == LLAMA_W_Q4) {
+    if (gemv_q4_ks(B, D) != 1) return fail(LLAMA_ERR_UNSUPPORTED, "4-bit head supports dim <= 8192");
     float* gam = (float*)(sc + L.gam);
     launch_to_f32<bf16_t>((const bf16_t*)fnorm, gam, D, s);
     launch_gemv_q4((const bf16_t*)x, 1, RowStat(), eps, gam, (const uint32_t*)head->w, (const bf16_t*)head->scales,

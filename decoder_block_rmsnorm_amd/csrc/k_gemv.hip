@@ -408,10 +408,173 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const _Float16* __restrict__ xh
   }
 }
 
+// One row of activations (M = 1, the single-sequence decode of the stack).
+// No preparation pass: in K slice ksi (blockIdx.y) lane l of every wavefront
+// owns the 32-code chunks c0 + l + 64 i (i < NI) of every weight row, so it
+// converts its chunks of x once (RMSNorm row scale and gamma applied, fp16
+// pairs in the word order of the nibble trick, the two chunk sums) and keeps
+// them in registers for all the rows of its wavefront.  Rows go in groups of
+// R, the codes and group scales of the next group requested before the
+// current one is multiplied.  y[ksi][N]: fp32 partial sums of the slices.
+template <int NI, int R>
+__global__ __launch_bounds__(256) void k_gemv_q4_m1(const bf16_t* __restrict__ X, int norm, RowStat stat, float eps,
+                                                   const float* __restrict__ gamma, const uint32_t* __restrict__ words,
+                                                   const bf16_t* __restrict__ scales,
+                                                   const bf16_t* __restrict__ biases, float* __restrict__ y, int N,
+                                                   int K, int ks, int rows_per_wave) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nchunk = K / 32, ngrp = K / 64;
+  const int ksi = blockIdx.y;
+  const int c0 = ksi * nchunk / ks, c1 = (ksi + 1) * nchunk / ks;
+  const int row0 = (blockIdx.x * 4 + wave) * rows_per_wave;
+  const int nrows = min(rows_per_wave, N - row0);
+  float* yo = y + (size_t)ksi * N;
+  uint4 wc[2][R][NI];
+  float sv[2][R][NI], bv[2][R][NI];
+  // rows past the wavefront's last one repeat it, lanes past the slice repeat
+  // its last chunk (loaded, never used)
+  auto load_group = [&](int g, auto bc) {
+    constexpr int b = decltype(bc)::value;
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int n = row0 + min(g * R + q, nrows - 1);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int c = min(c0 + lane + 64 * i, c1 - 1);
+        wc[b][q][i] = ld16(words + (size_t)n * (K / 8) + c * 4);
+        sv[b][q][i] = bf16_to_f32(scales[(size_t)n * ngrp + c / 2]);
+        bv[b][q][i] = bf16_to_f32(biases[(size_t)n * ngrp + c / 2]);
+      }
+    }
+  };
+  // the first group's codes go out first: nothing below waits for them
+  if (nrows > 0) load_group(0, std::integral_constant<int, 0>{});
+  // this lane's chunks of x-hat = x * gamma (the RMSNorm row scale r multiplies
+  // each row's sum at the end): word t of chunk i holds codes 8t .. 8t+7 as the
+  // fp16 pairs (x0, x4), (x1/16, x5/16), (x2, x6), (x3/16, x7/16)
+  float ssq = 0.f;   // sum of x^2 over this lane's chunks
+  uint32_t xw[NI][16];
+  float hs[NI], xs[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int c = c0 + lane + 64 * i;
+    hs[i] = 0.f;
+    xs[i] = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float v[8];
+      if (c < c1) {
+        const int k0 = c * 32 + 8 * t;
+        const bf16x8 xb = v_as_bf16x8(ld16(X + k0));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v[e] = (float)xb[e];
+          ssq += v[e] * v[e];
+        }
+        if (norm) {
+          const f32x4 g0 = *reinterpret_cast<const f32x4*>(gamma + k0);
+          const f32x4 g1 = *reinterpret_cast<const f32x4*>(gamma + k0 + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] *= g0[e];
+            v[e + 4] *= g1[e];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float sc = (p & 1) ? (1.0f / 16.0f) : 1.0f;
+        const _Float16 lo = (_Float16)(v[p] * sc), hi = (_Float16)(v[p + 4] * sc);
+        hs[i] += (float)lo + (float)hi;
+        xs[i] += v[p] + v[p + 4];
+        uint16_t l16, h16;
+        __builtin_memcpy(&l16, &lo, 2);
+        __builtin_memcpy(&h16, &hi, 2);
+        xw[i][4 * t + p] = (uint32_t)l16 | ((uint32_t)h16 << 16);
+      }
+    }
+  }
+  // row scale: 1 (norm 0), from the row's mean square (norm 1: a wavefront
+  // covers the whole row when K is not split, else the block reads it), or
+  // from the producer's statistic (norm 2)
+  float r = 1.0f;
+  if (norm == 1) {
+    if (ks == 1) {
+      r = 1.0f / sqrtf(warp_sum(ssq) / (float)K + eps);
+    } else {
+      __shared__ float red[4];
+      float t = 0.f;
+      for (int k = tid * 8; k < K; k += 256 * 8) {
+        const bf16x8 v = v_as_bf16x8(ld16(X + k));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t += (float)v[e] * (float)v[e];
+      }
+      t = warp_sum(t);
+      if (lane == 0) red[wave] = t;
+      __syncthreads();
+      r = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)K + eps);
+    }
+  } else if (norm == 2) {
+    r = stat.get_block(0);
+  }
+  auto group = [&](int g, auto bc) {
+    constexpr int b = decltype(bc)::value;
+    if ((g + 1) * R < nrows) load_group(g + 1, std::integral_constant<int, b ^ 1>{});
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        if (c0 + lane + 64 * i < c1) {
+          const uint32_t wv4[4] = {wc[b][q][i].x, wc[b][q][i].y, wc[b][q][i].z, wc[b][q][i].w};
+          float a = 0.f;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t u = wv4[t], u8 = wv4[t] >> 8;
+            a = __builtin_amdgcn_fdot2(u32_as_h2((u & 0x000F000Fu) | 0x64006400u), u32_as_h2(xw[i][4 * t + 0]), a, false);
+            a = __builtin_amdgcn_fdot2(u32_as_h2((u & 0x00F000F0u) | 0x64006400u), u32_as_h2(xw[i][4 * t + 1]), a, false);
+            a = __builtin_amdgcn_fdot2(u32_as_h2((u8 & 0x000F000Fu) | 0x64006400u), u32_as_h2(xw[i][4 * t + 2]), a, false);
+            a = __builtin_amdgcn_fdot2(u32_as_h2((u8 & 0x00F000F0u) | 0x64006400u), u32_as_h2(xw[i][4 * t + 3]), a, false);
+          }
+          acc += sv[b][q][i] * (a - 1024.0f * hs[i]) + bv[b][q][i] * xs[i];
+        }
+      }
+      acc = warp_sum(acc);
+      if (lane == 0 && g * R + q < nrows) yo[row0 + g * R + q] = acc * r;
+    }
+  };
+  const int ngroups = (nrows + R - 1) / R;
+  for (int g = 0; g < ngroups; g += 2) {
+    group(g, std::integral_constant<int, 0>{});
+    if (g + 1 < ngroups) group(g + 1, std::integral_constant<int, 1>{});
+  }
+}
+
+// K slices of the single-row 4-bit GEMV: at most 256 chunks (4 per lane) each
+int gemv_q4_ks(int M, int K) { return M == 1 ? (K / 32 + 255) / 256 : 1; }
+
 void launch_gemv_q4(const bf16_t* X, int norm, RowStat stat, float eps, const float* gamma,
                     const uint32_t* words, const bf16_t* scales, const bf16_t* biases, float* y, int M, int N,
                     int K, int gs, _Float16* xh_buf, float* xsum_buf, hipStream_t s) {
   if (M <= 0 || N <= 0) return;
+  if (M == 1) {
+    const int ks = gemv_q4_ks(M, K);
+    const int ni = ((K / 32 + ks - 1) / ks + 63) / 64;   // chunks per lane in the longest slice
+    // rows per wavefront: enough to amortize each lane's conversion of its
+    // chunks of x, a grid of about 384 blocks over the slices
+    const int rpw = std::max(4, (N * ks + 768) / 1536);
+    const dim3 grid((N + 4 * rpw - 1) / (4 * rpw), ks);
+#define Q4M1(n, r)                                                                                         \
+  case n:                                                                                                  \
+    hipLaunchKernelGGL((k_gemv_q4_m1<n, r>), grid, dim3(256), 0, s, X, norm, stat, eps, gamma, words, scales, \
+                       biases, y, N, K, ks, rpw);                                                          \
+    return;
+    switch (ni) { Q4M1(1, 4) Q4M1(2, 4) Q4M1(3, 4) Q4M1(4, 2) }
+#undef Q4M1
+  }
   hipLaunchKernelGGL(k_q4_prep, dim3(M), dim3(1024), 0, s, X, norm, stat, eps, gamma, M, K, xh_buf, xsum_buf);
   const int rpw = 2;
   const int blocks = (N + 4 * rpw - 1) / (4 * rpw);

@@ -151,9 +151,12 @@ void launch_gemv_swiglu(const bf16_t* X, const bf16_t* W, int M, int N, int K, c
 // y[M][N] (fp32) = xhat W^T, W 4-bit group affine, xhat = x * r * gamma, M <= 4.
 // norm: 0 = no RMSNorm (r = 1, gamma unused), 1 = r from the row itself (eps),
 // 2 = r from `stat`.  xh_buf: fp16 [M, K]; xsum_buf: fp32 [M, K/32, 2] (scratch).
+// y: fp32 partials [gemv_q4_ks(M, K)][M][N] (one slice unless M = 1 and K is
+// long).  xh_buf / xsum_buf are used for M > 1 only.
 void launch_gemv_q4(const bf16_t* X, int norm, RowStat stat, float eps, const float* gamma,
                     const uint32_t* words, const bf16_t* scales, const bf16_t* biases, float* y, int M, int N,
                     int K, int gs, _Float16* xh_buf, float* xsum_buf, hipStream_t s);
+int gemv_q4_ks(int M, int K);
 
 // ------------------------------------------------------------ k_epilogue.hip
 // All take fp32 partials [ks][M][N] and reduce them in a fixed order.
