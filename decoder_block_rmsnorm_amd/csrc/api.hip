@@ -475,6 +475,7 @@ extern "C" llama_status llama_kvcache_read(const llama_kvcache* c, int32_t layer
 
 // ---------------------------------------------------------------- scratch
 static const int kSplitLen = 256;  // keys per decode-attention chunk (the least)
+static const int kStackSplit = 64; // keys per chunk in the stack's single-sequence decode
 
 // Keys per decode-attention split.  Each split of a sequence and kv head
 // writes n_rep rows of fp32 partial output for the merge; with grouped heads
@@ -507,7 +508,9 @@ struct SLayout {
 };
 
 // T = rows of this call (batch * seq_len), B = batch, decode = one-token call.
-static SLayout scratch_layout(const llama_block_config& c, const Dims& d, int T, int B, int max_seq, bool decode) {
+// split_min: the shortest decode-attention key split the calls will use
+static SLayout scratch_layout(const llama_block_config& c, const Dims& d, int T, int B, int max_seq, bool decode,
+                              int split_min = kSplitLen) {
   SLayout L{};
   const size_t E = esize(c.act_dtype);
   size_t off = 0;
@@ -544,8 +547,8 @@ static SLayout scratch_layout(const llama_block_config& c, const Dims& d, int T,
     part = (size_t)kMaxSplitK * std::min<long>(T, rows_split) * d.D * 4;
   }
   L.part = off; off = align256(off + part);
-  L.n_splits = (max_seq + kSplitLen - 1) / kSplitLen;
-  L.split_len = kSplitLen;
+  L.n_splits = (max_seq + split_min - 1) / split_min;
+  L.split_len = split_min;
   size_t ao = (d.bf16 && decode) ? (size_t)B * d.H * L.n_splits * 128 * 4 : 0;
   size_t aml = (d.bf16 && decode) ? (size_t)B * d.H * L.n_splits * 2 * 4 : 0;
   L.ao = off; off = align256(off + ao);
@@ -632,7 +635,8 @@ extern "C" llama_status llama_block_set_diag(llama_block* blk, int32_t enable) {
 
 // ---------------------------------------------------------------- block calls
 static llama_status check_call(const llama_block* blk, const llama_kvcache* c, int layer, const void* x, const void* y,
-                               int batch, int L, void* scratch, size_t sbytes, bool decode, SLayout* lay) {
+                               int batch, int L, void* scratch, size_t sbytes, bool decode, int split_min,
+                               SLayout* lay) {
   if (!blk || !c) return fail(LLAMA_ERR_INVALID_ARG, "block and cache must be non-NULL");
   if (!x || !y || !scratch) return fail(LLAMA_ERR_INVALID_ARG, "x, y and scratch must be non-NULL");
   if (((uintptr_t)scratch) & 255) return fail(LLAMA_ERR_INVALID_ARG, "scratch must be 256-byte aligned");
@@ -654,7 +658,7 @@ static llama_status check_call(const llama_block* blk, const llama_kvcache* c, i
       return fail(LLAMA_ERR_CAPACITY, "sequence %d: %d cached + %d new exceeds capacity %d", b, len, L, cap);
     maxlen = std::max(maxlen, len + L);
   }
-  SLayout lo = scratch_layout(blk->cfg, d, batch * L, batch, c->cfg.max_seq, decode);
+  SLayout lo = scratch_layout(blk->cfg, d, batch * L, batch, c->cfg.max_seq, decode, split_min);
   if (sbytes < lo.total) return fail(LLAMA_ERR_CAPACITY, "scratch too small: %zu < %zu bytes", sbytes, lo.total);
   lo.split_len = attn_split_len(d, batch, maxlen);
   lo.n_splits = (maxlen + lo.split_len - 1) / lo.split_len;
@@ -850,9 +854,11 @@ static void bf16_decode(const llama_block* blk, KVView kv, const void* x, void* 
 // grid, with splits of kSplitLen keys (graph capture, where lengths grow
 // between replays).
 static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const void* x, void* y, int batch, int L,
-                            void* scratch, size_t sbytes, bool decode, int n_splits_override, hipStream_t s) {
+                            void* scratch, size_t sbytes, bool decode, int n_splits_override, int split_len_override,
+                            hipStream_t s) {
   SLayout S;
-  llama_status st = check_call(blk, c, layer, x, y, batch, L, scratch, sbytes, decode, &S);
+  llama_status st = check_call(blk, c, layer, x, y, batch, L, scratch, sbytes, decode,
+                               n_splits_override > 0 ? split_len_override : kSplitLen, &S);
   if (st != LLAMA_OK) return st;
   KVView kv = kv_view(c, layer);
   char* sc = (char*)scratch;
@@ -871,7 +877,7 @@ static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const
   } else if (!decode) {
     bf16_prefill(blk, kv, x, y, batch, L, sc, S, mk, s);
   } else {
-    if (n_splits_override > 0) bf16_decode(blk, kv, x, y, batch, sc, S, n_splits_override, kSplitLen, mk, s);
+    if (n_splits_override > 0) bf16_decode(blk, kv, x, y, batch, sc, S, n_splits_override, split_len_override, mk, s);
     else bf16_decode(blk, kv, x, y, batch, sc, S, S.n_splits, S.split_len, mk, s);
   }
   if (mk.ev) blk->prof_marks = mk.i;
@@ -884,12 +890,12 @@ static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const
 
 extern "C" llama_status llama_block_prefill(llama_block* blk, llama_kvcache* c, int32_t layer, const void* x, void* y,
                                             int32_t batch, int32_t seq_len, void* scratch, size_t sbytes, void* stream) {
-  return enqueue(blk, c, layer, x, y, batch, seq_len, scratch, sbytes, false, 0, (hipStream_t)stream);
+  return enqueue(blk, c, layer, x, y, batch, seq_len, scratch, sbytes, false, 0, 0, (hipStream_t)stream);
 }
 
 extern "C" llama_status llama_block_decode(llama_block* blk, llama_kvcache* c, int32_t layer, const void* x, void* y,
                                            int32_t batch, void* scratch, size_t sbytes, void* stream) {
-  return enqueue(blk, c, layer, x, y, batch, 1, scratch, sbytes, true, 0, (hipStream_t)stream);
+  return enqueue(blk, c, layer, x, y, batch, 1, scratch, sbytes, true, 0, 0, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------- stack ends
@@ -1018,7 +1024,9 @@ static StLayout stack_layout(const llama_stack* st, int max_prompt, int max_seq)
   StLayout L{};
   size_t off = 0;
   L.x = off; off = align256(off + (size_t)max_prompt * c.dim * 2);
-  L.blk_bytes = llama_scratch_bytes(&c, max_prompt, 1, max_seq);
+  const Dims& d = st->blocks[0]->dm;
+  L.blk_bytes = std::max(scratch_layout(c, d, max_prompt, 1, max_seq, false).total,
+                         scratch_layout(c, d, 1, 1, max_seq, true, kStackSplit).total);
   L.blk = off; off = align256(off + L.blk_bytes);
   L.head_bytes = head_layout(1, c.dim, st->vocab).total;
   L.head = off; off = align256(off + L.head_bytes);
@@ -1068,15 +1076,17 @@ extern "C" llama_status llama_stack_generate(llama_stack* st, llama_kvcache* cac
   launch_fill_i32(cursor, 1, 0, s);
   launch_embed<bf16_t>((const bf16_t*)st->emb, V, D, prompt, P, x, s);
   for (int l = 0; l < NL; ++l)
-    if ((r = enqueue(st->blocks[l], cache, l, x, x, 1, P, bs, L.blk_bytes, false, 0, s)) != LLAMA_OK) return r;
+    if ((r = enqueue(st->blocks[l], cache, l, x, x, 1, P, bs, L.blk_bytes, false, 0, 0, s)) != LLAMA_OK) return r;
   if ((r = head(x + (size_t)(P - 1) * D)) != LLAMA_OK) return r;
   launch_emit(cur, ids_out, cursor, hlog, logits_out, V, s);
 
-  const int n_splits = (P + n_steps + kSplitLen - 1) / kSplitLen;
+  // one sequence: short key splits (more wavefronts for a short cache), fixed
+  // for the whole capture
+  const int n_splits = (P + n_steps + kStackSplit - 1) / kStackSplit;
   auto step = [&]() -> llama_status {
     launch_embed<bf16_t>((const bf16_t*)st->emb, V, D, cur, 1, x, s);
     for (int l = 0; l < NL; ++l) {
-      llama_status q = enqueue(st->blocks[l], cache, l, x, x, 1, 1, bs, L.blk_bytes, true, n_splits, s);
+      llama_status q = enqueue(st->blocks[l], cache, l, x, x, 1, 1, bs, L.blk_bytes, true, n_splits, kStackSplit, s);
       if (q != LLAMA_OK) return q;
     }
     llama_status q = head(x);
