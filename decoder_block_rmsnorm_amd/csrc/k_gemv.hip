@@ -522,7 +522,9 @@ __global__ __launch_bounds__(256) void k_gemv_q4_m1(const bf16_t* __restrict__ X
   }
   auto group = [&](int g, auto bc) {
     constexpr int b = decltype(bc)::value;
-    if ((g + 1) * R < nrows) load_group(g + 1, std::integral_constant<int, b ^ 1>{});
+    // (unconditional, so the compiler's waits for this group stay exact; after
+    // the last group it repeats the wavefront's last rows, just read)
+    load_group(g + 1, std::integral_constant<int, b ^ 1>{});
 #pragma unroll
     for (int q = 0; q < R; ++q) {
       float acc = 0.f;
