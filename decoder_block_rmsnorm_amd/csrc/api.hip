@@ -502,6 +502,13 @@ static int gemv_ks(int M, int N, int K) {
   return std::max(1, std::min(target / tiles, nchk / 4));
 }
 
+// 4-bit decode of one sequence runs the single-row kernels with their
+// epilogues fused (every K of the block at most 32768)
+static bool q4_single(const Dims& d, int T, bool decode) {
+  return d.q4 && decode && T == 1 && q4_fused_blocks(d.D, d.Nq) > 0 && q4_fused_blocks(d.Nqkv, d.D) > 0 &&
+         q4_fused_blocks(2 * d.F, d.D) > 0 && q4_fused_blocks(d.D, d.F) > 0;
+}
+
 struct SLayout {
   size_t inv1, inv2, ssx, ssh, q, attn, h, g, ffn, part, ao, aml, xh, xsum, deq, total;
   int n_splits, split_len, ks_qkv, nb_h;
@@ -518,10 +525,13 @@ static SLayout scratch_layout(const llama_block_config& c, const Dims& d, int T,
   L.inv2 = off; off = align256(off + (size_t)T * 4);
   // partial row statistics: of x per K slice of the decode QKV projection, of h
   // per 256-column block of the residual epilogue
+  // (one partial per block of the single-row 4-bit wo kernel); sized alike for
+  // prefill and decode so that the buffers after it sit at the same offsets
   L.ks_qkv = gemv_ks(T, d.Nqkv, d.D);
-  L.nb_h = (d.D + 255) / 256;
+  const int nb_q4 = d.q4 ? q4_fused_blocks(d.D, d.Nq) : 0;
+  L.nb_h = q4_single(d, T, decode) ? nb_q4 : (d.D + 255) / 256;
   L.ssx = off; off = align256(off + (size_t)L.ks_qkv * T * 4);
-  L.ssh = off; off = align256(off + (size_t)L.nb_h * T * 4);
+  L.ssh = off; off = align256(off + (size_t)std::max(nb_q4, (d.D + 255) / 256) * T * 4);
   L.q = off; off = align256(off + (size_t)T * d.Nq * E);
   L.attn = off; off = align256(off + (size_t)T * d.Nq * E);
   L.h = off; off = align256(off + (size_t)T * d.D * E);
@@ -537,9 +547,7 @@ static SLayout scratch_layout(const llama_block_config& c, const Dims& d, int T,
     for (int i = 0; i < 4; ++i)
       part = std::max(part, (size_t)gemv_ks(T, NK[i][0], NK[i][1]) * T * NK[i][0] * 4);
   } else if (decode && d.q4) {
-    // the single-row 4-bit GEMV may split long K ranges
-    const int ksq = std::max(gemv_q4_ks(T, d.D), std::max(gemv_q4_ks(T, d.Nq), gemv_q4_ks(T, d.F)));
-    part = (size_t)ksq * T * maxN * 4;
+    part = (size_t)T * maxN * 4;
   } else {
     // prefill: wo / w2 split along K when their tile grid is small; a split
     // needs fewer than 200 tiles of 256 x 256, which bounds the rows it covers
@@ -821,6 +829,31 @@ static void bf16_decode(const llama_block* blk, KVView kv, const void* x, void* 
     mk(s);
     launch_epi_resid<bf16_t>(part, ks, B, d.D, h, (bf16_t*)y, nullptr, kv.lens, 1, B, ffn, s);
     mk(s);
+  } else if (q4_single(d, B, true)) {
+    // one sequence: each projection and what follows it in one kernel
+    auto lin_q4 = [&](const Lin& lin, Q4Fused e, const bf16_t* X) {
+      e.N = lin.N;
+      e.K = lin.K;
+      e.eps = eps;
+      launch_q4_fused(X, (const uint32_t*)lin.w, lin.s, lin.b, e, s);
+      mk(s);
+    };
+    Q4Fused e{};
+    e.epi = Q4E_QKV; e.norm = 1; e.gamma = blk->gamma1;
+    e.Nq = d.Nq; e.Nkv = d.Nkv; e.rope = blk->rope; e.traditional = blk->cfg.rope_traditional; e.q_out = q;
+    e.kv = kv;
+    lin_q4(blk->qkv, e, (const bf16_t*)x);
+    launch_attn_decode_bf16(q, kv, B, d.H, d.G, n_splits, split_len, ao, aml, attn, s);
+    mk(s);
+    e = Q4Fused{};
+    e.epi = Q4E_RESID; e.resid = (const bf16_t*)x; e.out = h; e.ss_out = ssh;
+    lin_q4(blk->o, e, attn);
+    e = Q4Fused{};
+    e.epi = Q4E_SWIGLU; e.norm = 2; e.stat = sth; e.gamma = blk->gamma2; e.ib = d.IB; e.g_out = g;
+    lin_q4(blk->w13, e, h);
+    e = Q4Fused{};
+    e.epi = Q4E_RESID; e.resid = h; e.out = (bf16_t*)y; e.lens_add = kv.lens; e.branch = ffn;
+    lin_q4(blk->w2, e, g);
   } else {
     _Float16* xh = (_Float16*)(sc + S.xh);
     float* xs = (float*)(sc + S.xsum);
@@ -830,22 +863,22 @@ static void bf16_decode(const llama_block* blk, KVView kv, const void* x, void* 
     };
     gq((const bf16_t*)x, 1, none, blk->gamma1, blk->qkv);
     mk(s);
-    launch_epi_qkv<bf16_t>(part, gemv_q4_ks(B, d.D), B, d.Nq, d.Nkv, none, 1, blk->rope, blk->cfg.rope_traditional,
+    launch_epi_qkv<bf16_t>(part, 1, B, d.Nq, d.Nkv, none, 1, blk->rope, blk->cfg.rope_traditional,
                            q, kv, s);
     mk(s);
     launch_attn_decode_bf16(q, kv, B, d.H, d.G, n_splits, split_len, ao, aml, attn, s);
     mk(s);
     gq(attn, 0, none, nullptr, blk->o);
     mk(s);
-    launch_epi_resid<bf16_t>(part, gemv_q4_ks(B, d.Nq), B, d.D, (const bf16_t*)x, h, ssh, nullptr, 0, 0, nullptr, s);
+    launch_epi_resid<bf16_t>(part, 1, B, d.D, (const bf16_t*)x, h, ssh, nullptr, 0, 0, nullptr, s);
     mk(s);
     gq(h, 2, sth, blk->gamma2, blk->w13);
     mk(s);
-    launch_epi_swiglu<bf16_t>(part, gemv_q4_ks(B, d.D), B, 2 * d.F, d.IB, none, g, s);
+    launch_epi_swiglu<bf16_t>(part, 1, B, 2 * d.F, d.IB, none, g, s);
     mk(s);
     gq(g, 0, none, nullptr, blk->w2);
     mk(s);
-    launch_epi_resid<bf16_t>(part, gemv_q4_ks(B, d.F), B, d.D, h, (bf16_t*)y, nullptr, kv.lens, 1, B, ffn, s);
+    launch_epi_resid<bf16_t>(part, 1, B, d.D, h, (bf16_t*)y, nullptr, kv.lens, 1, B, ffn, s);
     mk(s);
   }
 }
@@ -954,7 +987,6 @@ static llama_status head_enqueue(const llama_linear* head, int wf, int gs, int d
   char* sc = (char*)scratch;
   float* out = logits ? logits : (float*)(sc + L.logits);
   if (wf == LLAMA_W_Q4) {
-    if (gemv_q4_ks(B, D) != 1) return fail(LLAMA_ERR_UNSUPPORTED, "4-bit head supports dim <= 8192");
     float* gam = (float*)(sc + L.gam);
     launch_to_f32<bf16_t>((const bf16_t*)fnorm, gam, D, s);
     launch_gemv_q4((const bf16_t*)x, 1, RowStat(), eps, gam, (const uint32_t*)head->w, (const bf16_t*)head->scales,

@@ -408,53 +408,33 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const _Float16* __restrict__ xh
   }
 }
 
-// One row of activations (M = 1, the single-sequence decode of the stack).
-// No preparation pass: in K slice ksi (blockIdx.y) lane l of every wavefront
-// owns the 32-code chunks c0 + l + 64 i (i < NI) of every weight row, so it
-// converts its chunks of x once (RMSNorm row scale and gamma applied, fp16
-// pairs in the word order of the nibble trick, the two chunk sums) and keeps
-// them in registers for all the rows of its wavefront.  Rows go in groups of
-// R, the codes and group scales of the next group requested before the
-// current one is multiplied.  y[ksi][N]: fp32 partial sums of the slices.
-template <int NI, int R>
-__global__ __launch_bounds__(256) void k_gemv_q4_m1(const bf16_t* __restrict__ X, int norm, RowStat stat, float eps,
-                                                   const float* __restrict__ gamma, const uint32_t* __restrict__ words,
-                                                   const bf16_t* __restrict__ scales,
-                                                   const bf16_t* __restrict__ biases, float* __restrict__ y, int N,
-                                                   int K, int ks, int rows_per_wave) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int nchunk = K / 32, ngrp = K / 64;
-  const int ksi = blockIdx.y;
-  const int c0 = ksi * nchunk / ks, c1 = (ksi + 1) * nchunk / ks;
-  const int row0 = (blockIdx.x * 4 + wave) * rows_per_wave;
-  const int nrows = min(rows_per_wave, N - row0);
-  float* yo = y + (size_t)ksi * N;
-  uint4 wc[2][R][NI];
-  float sv[2][R][NI], bv[2][R][NI];
-  // rows past the wavefront's last one repeat it, lanes past the slice repeat
-  // its last chunk (loaded, never used)
-  auto load_group = [&](int g, auto bc) {
-    constexpr int b = decltype(bc)::value;
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-      const int n = row0 + min(g * R + q, nrows - 1);
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int c = min(c0 + lane + 64 * i, c1 - 1);
-        wc[b][q][i] = ld16(words + (size_t)n * (K / 8) + c * 4);
-        sv[b][q][i] = bf16_to_f32(scales[(size_t)n * ngrp + c / 2]);
-        bv[b][q][i] = bf16_to_f32(biases[(size_t)n * ngrp + c / 2]);
-      }
-    }
-  };
-  // the first group's codes go out first: nothing below waits for them
-  if (nrows > 0) load_group(0, std::integral_constant<int, 0>{});
-  // this lane's chunks of x-hat = x * gamma (the RMSNorm row scale r multiplies
-  // each row's sum at the end): word t of chunk i holds codes 8t .. 8t+7 as the
-  // fp16 pairs (x0, x4), (x1/16, x5/16), (x2, x6), (x3/16, x7/16)
-  float ssq = 0.f;   // sum of x^2 over this lane's chunks
-  uint32_t xw[NI][16];
-  float hs[NI], xs[NI];
+// One row of activations (M = 1, the single-sequence decode of the stack),
+// with what follows the projection in the block done in the same kernel.
+// No preparation pass: the block's 4 wavefronts form 4 / kp row sets, each
+// split over kp parts of K; lane l of a wavefront owns the 32-code chunks
+// c0 + l + 64 i (i < NI) of its part, converts its chunks of x once (gamma
+// applied, fp16 pairs in the word order of the nibble trick, the two chunk
+// sums) and keeps them in registers for all the rows of its set.  Rows go in
+// groups of R, the codes and group scales of the next group requested before
+// the current one is multiplied.  Row sums land in LDS; after one barrier the
+// block applies the RMSNorm row scale (a per-row scalar, so it multiplies the
+// sum) and its epilogue, one thread per output element:
+//   Q4E_PLAIN : y[n] = the projection (fp32);
+//   Q4E_QKV   : q/k/v with RoPE, k and v appended to the cache (the block's
+//               rows are RoPE pairs (i, i + d/2) of whole heads);
+//   Q4E_RESID : out = resid + projection, the next RMSNorm's partial sum of
+//               squares per block, optional branch copy and cache-length bump;
+//   Q4E_SWIGLU: g = silu(w1 n) * (w3 n) (the block's rows are w1/w3 pairs).
+constexpr int kQ4MaxRB = 256;   // rows per block at most
+
+// lane's chunks of x-hat = x * gamma: word t of chunk i holds codes 8t .. 8t+7
+// as the fp16 pairs (x0, x4), (x1/16, x5/16), (x2, x6), (x3/16, x7/16); hs =
+// sum of those fp16 values, xs = sum of the fp32 ones.  Returns the lane's
+// sum of x^2 (before gamma).
+template <int NI>
+__device__ inline float q4_xhat(const bf16_t* __restrict__ X, const float* __restrict__ gamma, int c0, int c1,
+                                int lane, uint32_t (&xw)[NI][16], float (&hs)[NI], float (&xs)[NI]) {
+  float ssq = 0.f;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int c = c0 + lane + 64 * i;
@@ -471,7 +451,7 @@ __global__ __launch_bounds__(256) void k_gemv_q4_m1(const bf16_t* __restrict__ X
           v[e] = (float)xb[e];
           ssq += v[e] * v[e];
         }
-        if (norm) {
+        if (gamma) {
           const f32x4 g0 = *reinterpret_cast<const f32x4*>(gamma + k0);
           const f32x4 g1 = *reinterpret_cast<const f32x4*>(gamma + k0 + 4);
 #pragma unroll
@@ -497,33 +477,87 @@ __global__ __launch_bounds__(256) void k_gemv_q4_m1(const bf16_t* __restrict__ X
       }
     }
   }
-  // row scale: 1 (norm 0), from the row's mean square (norm 1: a wavefront
-  // covers the whole row when K is not split, else the block reads it), or
-  // from the producer's statistic (norm 2)
-  float r = 1.0f;
-  if (norm == 1) {
-    if (ks == 1) {
-      r = 1.0f / sqrtf(warp_sum(ssq) / (float)K + eps);
-    } else {
-      __shared__ float red[4];
-      float t = 0.f;
-      for (int k = tid * 8; k < K; k += 256 * 8) {
-        const bf16x8 v = v_as_bf16x8(ld16(X + k));
+  return ssq;
+}
+
+// weight row of the block's local row lr (ok: it exists)
+template <int EPI>
+__device__ inline int q4_row(const Q4Fused& e, int RB, int lr, bool& ok) {
+  if (EPI == Q4E_PLAIN || EPI == Q4E_RESID) {
+    const int n = blockIdx.x * RB + lr;
+    ok = n < e.N;
+    return n;
+  }
+  const int half = RB >> 1, hi = lr >= half ? 1 : 0, p = blockIdx.x * half + lr - hi * half;
+  ok = p < (e.N >> 1);
+  if (EPI == Q4E_SWIGLU) return (p / e.ib) * 2 * e.ib + p % e.ib + hi * e.ib;
+  const int hd = e.kv.d >> 1;
+  return (p / hd) * e.kv.d + p % hd + hi * hd;
+}
+
+template <int NI, int R, int EPI>
+__global__ __launch_bounds__(256) void k_q4_fused(const bf16_t* __restrict__ X, const uint32_t* __restrict__ words,
+                                                 const bf16_t* __restrict__ scales,
+                                                 const bf16_t* __restrict__ biases, Q4Fused e) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int K = e.K, nchunk = K / 32, ngrp = K / 64;
+  const int kp = e.kp, kpi = wave % kp, rs = wave / kp;
+  const int c0 = kpi * nchunk / kp, c1 = (kpi + 1) * nchunk / kp;
+  const int rpw = e.rpw, RB = 4 * rpw / kp, half = RB >> 1;
+  __shared__ float ys[4][kQ4MaxRB];
+  __shared__ float ssq_l[4];
+  __shared__ float red[4];
+  uint4 wc[2][R][NI];
+  float sv[2][R][NI], bv[2][R][NI];
+  // rows past the set's last one repeat it, rows that do not exist read the
+  // block's first row, lanes past the part repeat its last chunk (all loaded,
+  // never used)
+  auto load_group = [&](int g, auto bc) {
+    constexpr int b = decltype(bc)::value;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) t += (float)v[e] * (float)v[e];
+    for (int q = 0; q < R; ++q) {
+      bool ok;
+      int n = q4_row<EPI>(e, RB, rs * rpw + min(g * R + q, rpw - 1), ok);
+      if (!ok) n = q4_row<EPI>(e, RB, 0, ok);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int c = min(c0 + lane + 64 * i, c1 - 1);
+        wc[b][q][i] = ld16(words + (size_t)n * (K / 8) + c * 4);
+        sv[b][q][i] = bf16_to_f32(scales[(size_t)n * ngrp + c / 2]);
+        bv[b][q][i] = bf16_to_f32(biases[(size_t)n * ngrp + c / 2]);
       }
-      t = warp_sum(t);
-      if (lane == 0) red[wave] = t;
-      __syncthreads();
-      r = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)K + eps);
     }
-  } else if (norm == 2) {
-    r = stat.get_block(0);
+  };
+  // the first group's codes go out first, then the epilogue's own operands
+  load_group(0, std::integral_constant<int, 0>{});
+  bool own_ok = false;
+  int own_row = 0;
+  float rv = 0.f;
+  float2 cs = make_float2(1.f, 0.f);
+  int pos = 0;
+  if (EPI == Q4E_RESID) {
+    own_row = blockIdx.x * RB + tid;
+    own_ok = tid < RB && own_row < e.N;
+    if (own_ok) rv = bf16_to_f32(e.resid[own_row]);
+  } else if (EPI == Q4E_QKV) {
+    const int hd = e.kv.d >> 1;
+    own_row = blockIdx.x * half + tid;   // pair index
+    own_ok = tid < half && own_row < (e.N >> 1);
+    pos = e.kv.lens[0];
+    if (own_ok && (own_row / hd) * e.kv.d < e.Nq + e.Nkv) cs = e.rope[(size_t)pos * hd + own_row % hd];
+  }
+  const float pv = e.norm == 2 ? e.stat.pre(0) : 0.f;
+  uint32_t xw[NI][16];
+  float hs[NI], xs[NI];
+  float ssq = q4_xhat<NI>(X, e.norm ? e.gamma : nullptr, c0, c1, lane, xw, hs, xs);
+  if (e.norm == 1) {
+    ssq = warp_sum(ssq);
+    if (rs == 0 && lane == 0) ssq_l[kpi] = ssq;
   }
   auto group = [&](int g, auto bc) {
     constexpr int b = decltype(bc)::value;
     // (unconditional, so the compiler's waits for this group stay exact; after
-    // the last group it repeats the wavefront's last rows, just read)
+    // the last group it repeats rows just read)
     load_group(g + 1, std::integral_constant<int, b ^ 1>{});
 #pragma unroll
     for (int q = 0; q < R; ++q) {
@@ -545,37 +579,142 @@ __global__ __launch_bounds__(256) void k_gemv_q4_m1(const bf16_t* __restrict__ X
         }
       }
       acc = warp_sum(acc);
-      if (lane == 0 && g * R + q < nrows) yo[row0 + g * R + q] = acc * r;
+      if (lane == 0 && g * R + q < rpw) ys[kpi][rs * rpw + g * R + q] = acc;
     }
   };
-  const int ngroups = (nrows + R - 1) / R;
+  const int ngroups = (rpw + R - 1) / R;
   for (int g = 0; g < ngroups; g += 2) {
     group(g, std::integral_constant<int, 0>{});
     if (g + 1 < ngroups) group(g + 1, std::integral_constant<int, 1>{});
   }
+  __syncthreads();
+  // row scale: 1 (norm 0), from the row's mean square over all of K (norm 1),
+  // or from the producer's statistic (norm 2)
+  float r = 1.0f;
+  if (e.norm == 1) {
+    float t = 0.f;
+    for (int k = 0; k < kp; ++k) t += ssq_l[k];
+    r = 1.0f / sqrtf(t / (float)K + e.eps);
+  } else if (e.norm == 2) {
+    r = e.stat.finish_block(pv);
+  }
+  auto sum_row = [&](int lr) {
+    float v = 0.f;
+    for (int k = 0; k < kp; ++k) v += ys[k][lr];
+    return v * r;
+  };
+  if (EPI == Q4E_PLAIN) {
+    bool ok;
+    const int n = q4_row<EPI>(e, RB, tid, ok);
+    if (tid < RB && ok) e.y[n] = sum_row(tid);
+  } else if (EPI == Q4E_RESID) {
+    float o = 0.f;
+    if (own_ok) {
+      const float f = sum_row(tid);
+      if (e.branch) e.branch[own_row] = f32_to_bf16(f);
+      o = Elt<bf16_t>::round(rv + f);
+      e.out[own_row] = f32_to_bf16(o);
+    }
+    if (e.ss_out) {
+      const float t = warp_sum(o * o);
+      if (lane == 0) red[wave] = t;
+      __syncthreads();
+      if (tid == 0) e.ss_out[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+    }
+    if (e.lens_add && blockIdx.x == 0 && tid == 0) e.lens_add[0] += 1;
+  } else if (EPI == Q4E_SWIGLU) {
+    const int j = blockIdx.x * half + tid;
+    if (tid < half && j < (e.N >> 1)) e.g_out[j] = f32_to_bf16(silu_f(sum_row(tid)) * sum_row(tid + half));
+  } else if (EPI == Q4E_QKV) {
+    if (own_ok) {
+      const int d = e.kv.d, hd = d >> 1;
+      const int head = own_row / hd, i = own_row % hd, cb0 = head * d;
+      float a = sum_row(tid), b = sum_row(tid + half);
+      if (cb0 < e.Nq + e.Nkv) {
+        const float a2 = a * cs.x - b * cs.y, b2 = b * cs.x + a * cs.y;
+        a = a2;
+        b = b2;
+      }
+      const int ca = e.traditional ? 2 * i : i, cb = e.traditional ? 2 * i + 1 : i + hd;
+      if (cb0 < e.Nq) {
+        e.q_out[cb0 + ca] = f32_to_bf16(a);
+        e.q_out[cb0 + cb] = f32_to_bf16(b);
+      } else if (cb0 < e.Nq + e.Nkv) {
+        const int g = (cb0 - e.Nq) / d;
+        bf16_t* Kc = (bf16_t*)e.kv.k;
+        Kc[e.kv.k_off(0, pos, g, ca)] = f32_to_bf16(a);
+        Kc[e.kv.k_off(0, pos, g, cb)] = f32_to_bf16(b);
+      } else {
+        const int g = (cb0 - e.Nq - e.Nkv) / d;
+        bf16_t* Vc = (bf16_t*)e.kv.v;
+        Vc[e.kv.v_off(0, pos, g, i)] = f32_to_bf16(a);
+        Vc[e.kv.v_off(0, pos, g, i + hd)] = f32_to_bf16(b);
+      }
+    }
+  }
 }
 
-// K slices of the single-row 4-bit GEMV: at most 256 chunks (4 per lane) each
-int gemv_q4_ks(int M, int K) { return M == 1 ? (K / 32 + 255) / 256 : 1; }
+// K parts per block, chunks per lane and rows per wavefront of the single-row
+// kernel; false when K is too long for one block (more than 1024 chunks)
+static bool q4_fused_shape(int N, int K, int& kp, int& ni, int& rpw) {
+  const int nchunk = K / 32;
+  if (nchunk < 1 || nchunk > 1024) return false;
+  kp = nchunk <= 256 ? 1 : nchunk <= 512 ? 2 : 4;
+  ni = ((nchunk + kp - 1) / kp + 63) / 64;
+  // rows per wavefront: enough to amortize each lane's conversion of its
+  // chunks of x, a grid of about 384 blocks; the block's rows even (pairs)
+  // and at most kQ4MaxRB
+  rpw = std::max(4, (N * kp + 768) / 1536);
+  rpw = std::min(rpw, kQ4MaxRB * kp / 4);
+  if (kp == 4) rpw = (rpw + 1) & ~1;
+  return true;
+}
+
+int q4_fused_blocks(int N, int K) {
+  int kp, ni, rpw;
+  if (!q4_fused_shape(N, K, kp, ni, rpw)) return 0;
+  const int RB = 4 * rpw / kp;
+  return (N + RB - 1) / RB;
+}
+
+bool launch_q4_fused(const bf16_t* X, const uint32_t* words, const bf16_t* scales, const bf16_t* biases,
+                     Q4Fused e, hipStream_t s) {
+  int kp, ni, rpw;
+  if (e.N <= 0) return true;
+  if (!q4_fused_shape(e.N, e.K, kp, ni, rpw)) return false;
+  if (e.epi != Q4E_PLAIN && e.epi != Q4E_RESID && (e.N & 1)) return false;
+  e.kp = kp;
+  e.rpw = rpw;
+  const dim3 grid(q4_fused_blocks(e.N, e.K));
+#define Q4F(n, r, E)                                                                                     \
+  case n:                                                                                                \
+    hipLaunchKernelGGL((k_q4_fused<n, r, E>), grid, dim3(256), 0, s, X, words, scales, biases, e);     \
+    return true;
+#define Q4FE(E)                                                                     \
+  case E:                                                                           \
+    switch (ni) { Q4F(1, 4, E) Q4F(2, 4, E) Q4F(3, 4, E) Q4F(4, 2, E) } \
+    break;
+  switch (e.epi) { Q4FE(Q4E_PLAIN) Q4FE(Q4E_QKV) Q4FE(Q4E_RESID) Q4FE(Q4E_SWIGLU) }
+#undef Q4FE
+#undef Q4F
+  return false;
+}
 
 void launch_gemv_q4(const bf16_t* X, int norm, RowStat stat, float eps, const float* gamma,
                     const uint32_t* words, const bf16_t* scales, const bf16_t* biases, float* y, int M, int N,
                     int K, int gs, _Float16* xh_buf, float* xsum_buf, hipStream_t s) {
   if (M <= 0 || N <= 0) return;
   if (M == 1) {
-    const int ks = gemv_q4_ks(M, K);
-    const int ni = ((K / 32 + ks - 1) / ks + 63) / 64;   // chunks per lane in the longest slice
-    // rows per wavefront: enough to amortize each lane's conversion of its
-    // chunks of x, a grid of about 384 blocks over the slices
-    const int rpw = std::max(4, (N * ks + 768) / 1536);
-    const dim3 grid((N + 4 * rpw - 1) / (4 * rpw), ks);
-#define Q4M1(n, r)                                                                                         \
-  case n:                                                                                                  \
-    hipLaunchKernelGGL((k_gemv_q4_m1<n, r>), grid, dim3(256), 0, s, X, norm, stat, eps, gamma, words, scales, \
-                       biases, y, N, K, ks, rpw);                                                          \
-    return;
-    switch (ni) { Q4M1(1, 4) Q4M1(2, 4) Q4M1(3, 4) Q4M1(4, 2) }
-#undef Q4M1
+    Q4Fused e{};
+    e.epi = Q4E_PLAIN;
+    e.N = N;
+    e.K = K;
+    e.norm = norm;
+    e.stat = stat;
+    e.eps = eps;
+    e.gamma = gamma;
+    e.y = y;
+    if (launch_q4_fused(X, words, scales, biases, e, s)) return;
   }
   hipLaunchKernelGGL(k_q4_prep, dim3(M), dim3(1024), 0, s, X, norm, stat, eps, gamma, M, K, xh_buf, xsum_buf);
   const int rpw = 2;

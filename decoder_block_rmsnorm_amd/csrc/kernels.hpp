@@ -150,13 +150,48 @@ void launch_gemv_swiglu(const bf16_t* X, const bf16_t* W, int M, int N, int K, c
                         hipStream_t s);
 // y[M][N] (fp32) = xhat W^T, W 4-bit group affine, xhat = x * r * gamma, M <= 4.
 // norm: 0 = no RMSNorm (r = 1, gamma unused), 1 = r from the row itself (eps),
-// 2 = r from `stat`.  xh_buf: fp16 [M, K]; xsum_buf: fp32 [M, K/32, 2] (scratch).
-// y: fp32 partials [gemv_q4_ks(M, K)][M][N] (one slice unless M = 1 and K is
-// long).  xh_buf / xsum_buf are used for M > 1 only.
+// 2 = r from `stat`.  xh_buf: fp16 [M, K]; xsum_buf: fp32 [M, K/32, 2] (scratch,
+// used unless M = 1 and K <= 32768).
 void launch_gemv_q4(const bf16_t* X, int norm, RowStat stat, float eps, const float* gamma,
                     const uint32_t* words, const bf16_t* scales, const bf16_t* biases, float* y, int M, int N,
                     int K, int gs, _Float16* xh_buf, float* xsum_buf, hipStream_t s);
-int gemv_q4_ks(int M, int K);
+// Single-row (M = 1) 4-bit projection X W^T (W: N rows, K inputs, groups of 64)
+// with its epilogue in the same kernel, bf16 activations.  r and gamma as in
+// launch_gemv_q4.
+enum Q4Epi { Q4E_PLAIN = 0, Q4E_QKV = 1, Q4E_RESID = 2, Q4E_SWIGLU = 3 };
+struct Q4Fused {
+  int epi, N, K;
+  int kp, rpw;            // set by the launcher
+  int norm;
+  RowStat stat;
+  float eps;
+  const float* gamma;
+  float* y;               // PLAIN: [N]
+  // QKV (rows in the repacked order: per head, RoPE pair i is (i, i + d/2)):
+  // q_out [Nq]; k, v appended at position kv.lens[0] of sequence 0
+  int Nq, Nkv;
+  const float2* rope;
+  int traditional;
+  bf16_t* q_out;
+  KVView kv;
+  // RESID: out = resid + y [N]; ss_out (optional): one sum of squares of the
+  // stored values per block [q4_fused_blocks]; branch (optional): y in bf16;
+  // lens_add (optional): lens_add[0] += 1
+  const bf16_t* resid;
+  bf16_t* out;
+  float* ss_out;
+  int32_t* lens_add;
+  bf16_t* branch;
+  // SWIGLU: rows interleaved in blocks of ib (w1 rows, then the same w3 rows);
+  // g_out [N/2]
+  int ib;
+  bf16_t* g_out;
+};
+// false (nothing launched) when K > 32768 or a paired epilogue has odd N
+bool launch_q4_fused(const bf16_t* X, const uint32_t* words, const bf16_t* scales, const bf16_t* biases,
+                     Q4Fused e, hipStream_t s);
+// blocks of the single-row kernel for [N, K] (0: not supported)
+int q4_fused_blocks(int N, int K);
 
 // ------------------------------------------------------------ k_epilogue.hip
 // All take fp32 partials [ks][M][N] and reduce them in a fixed order.

@@ -161,6 +161,10 @@ llama_status llama_block_set_diag(llama_block* blk, int32_t enable);
  *   bf16 decode  : qkv projection (+ x statistics), qkv finish, attention,
  *                  wo projection, residual (+ h statistics), w1/w3
  *                  projection + swiglu, w2 projection, residual             (8)
+ *   4-bit decode : one sequence: qkv projection+rope+append, attention, wo
+ *                  projection+residual, w1/w3 projection+swiglu, w2
+ *                  projection+residual (5); more: as bf16 decode, the w1/w3
+ *                  projection and swiglu apart                              (9)
  * Not for calls captured into a graph. */
 llama_status llama_block_profile_start(llama_block* blk, int32_t max_calls, uint32_t phase_mask);
 llama_status llama_block_profile_read(llama_block* blk, float* phase_ms, int32_t max_phases, int32_t* n_phases,

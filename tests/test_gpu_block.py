@@ -228,14 +228,33 @@ SMALL_Q4 = W.BlockShape(dim=512, n_heads=4, n_kv_heads=4, ffn_dim=1536, dtype="b
 
 @pytest.mark.parametrize("B", [1, 3])
 def test_q4_decode(B):
-    s = SMALL_Q4
-    rng = W.Rng(15)
+    _q4_decode_case(SMALL_Q4, B, 15)
+
+
+# One sequence runs each projection with its epilogue in one kernel; K longer
+# than 256 chunks of 32 splits over the block's wavefronts (2 or 4 parts, here
+# of unequal lengths), with grouped-query heads and both RoPE layouts.
+Q4_SINGLE = {
+    "gqa_halves_k2": W.BlockShape(dim=512, n_heads=4, n_kv_heads=2, ffn_dim=9280, dtype="bf16", weight_format="q4",
+                                  traditional=False),
+    "long_ffn_k4": W.BlockShape(dim=512, n_heads=4, n_kv_heads=4, ffn_dim=17472, dtype="bf16", weight_format="q4",
+                                traditional=True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(Q4_SINGLE))
+def test_q4_decode_single_row_k_parts(name):
+    _q4_decode_case(Q4_SINGLE[name], 1, 17)
+
+
+def _q4_decode_case(s, B, seed):
+    rng = W.Rng(seed)
     lens = [77, 200, 3][:B]
     x = rng.normal((B, 1, s.dim), 1.0, "bf16")
     kv = (rng.normal((B, 200, s.n_kv_heads, s.head_dim), 1.0, "bf16"),
           rng.normal((B, 200, s.n_kv_heads, s.head_dim), 1.0, "bf16"))
     w = W.draw_block_weights(s, rng)
-    _flush(f"case: 4-bit decode B={B}")
+    _flush(f"case: 4-bit decode B={B} dim={s.dim} ffn={s.ffn_dim} kv_heads={s.n_kv_heads}")
     max_seq = 256
     blk, wd = G.make_block(s, w, max_seq)
     cache = G.make_cache(s, 1, B, max_seq)
