@@ -427,10 +427,44 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const _Float16* __restrict__ xh
 //   Q4E_SWIGLU: g = silu(w1 n) * (w3 n) (the block's rows are w1/w3 pairs).
 constexpr int kQ4MaxRB = 256;   // rows per block at most
 
-// lane's chunks of x-hat = x * gamma: word t of chunk i holds codes 8t .. 8t+7
-// as the fp16 pairs (x0, x4), (x1/16, x5/16), (x2, x6), (x3/16, x7/16); hs =
-// sum of those fp16 values, xs = sum of the fp32 ones.  Returns the lane's
-// sum of x^2 (before gamma).
+// One 8-code unit of x-hat = x * gamma (word t of a chunk covers codes 8t ..
+// 8t+7): the fp16 pairs (x0, x4), (x1/16, x5/16), (x2, x6), (x3/16, x7/16) in
+// the word order of the nibble trick, the sum of those fp16 values (hsum) and
+// of the fp32 ones (xsum); adds the unit's x^2 (before gamma) to ssq.
+__device__ inline void q4_unit(uint4 xraw, bool use_g, f32x4 g0, f32x4 g1, uint32_t (&w)[4], float& hsum,
+                               float& xsum, float& ssq) {
+  const bf16x8 xb = v_as_bf16x8(xraw);
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    v[e] = (float)xb[e];
+    ssq += v[e] * v[e];
+  }
+  if (use_g) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] *= g0[e];
+      v[e + 4] *= g1[e];
+    }
+  }
+  hsum = 0.f;
+  xsum = 0.f;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float sc = (p & 1) ? (1.0f / 16.0f) : 1.0f;
+    const _Float16 lo = (_Float16)(v[p] * sc), hi = (_Float16)(v[p + 4] * sc);
+    hsum += (float)lo + (float)hi;
+    xsum += v[p] + v[p + 4];
+    uint16_t l16, h16;
+    __builtin_memcpy(&l16, &lo, 2);
+    __builtin_memcpy(&h16, &hi, 2);
+    w[p] = (uint32_t)l16 | ((uint32_t)h16 << 16);
+  }
+}
+
+// lane's chunks c0 + lane + 64 i (i < NI, c < c1; zero past c1) of x-hat:
+// xw[i][4t + p] = word p of unit t, hs / xs = chunk sums.  Returns the lane's
+// sum of x^2.
 template <int NI>
 __device__ inline float q4_xhat(const bf16_t* __restrict__ X, const float* __restrict__ gamma, int c0, int c1,
                                 int lane, uint32_t (&xw)[NI][16], float (&hs)[NI], float (&xs)[NI]) {
@@ -442,39 +476,23 @@ __device__ inline float q4_xhat(const bf16_t* __restrict__ X, const float* __res
     xs[i] = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      float v[8];
+      uint4 xr = make_uint4(0, 0, 0, 0);
+      f32x4 g0 = {1.f, 1.f, 1.f, 1.f}, g1 = g0;
       if (c < c1) {
         const int k0 = c * 32 + 8 * t;
-        const bf16x8 xb = v_as_bf16x8(ld16(X + k0));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          v[e] = (float)xb[e];
-          ssq += v[e] * v[e];
-        }
+        xr = ld16(X + k0);
         if (gamma) {
-          const f32x4 g0 = *reinterpret_cast<const f32x4*>(gamma + k0);
-          const f32x4 g1 = *reinterpret_cast<const f32x4*>(gamma + k0 + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[e] *= g0[e];
-            v[e + 4] *= g1[e];
-          }
+          g0 = *reinterpret_cast<const f32x4*>(gamma + k0);
+          g1 = *reinterpret_cast<const f32x4*>(gamma + k0 + 4);
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.f;
       }
+      uint32_t w[4];
+      float h, x;
+      q4_unit(xr, gamma != nullptr, g0, g1, w, h, x, ssq);
+      hs[i] += h;
+      xs[i] += x;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const float sc = (p & 1) ? (1.0f / 16.0f) : 1.0f;
-        const _Float16 lo = (_Float16)(v[p] * sc), hi = (_Float16)(v[p + 4] * sc);
-        hs[i] += (float)lo + (float)hi;
-        xs[i] += v[p] + v[p + 4];
-        uint16_t l16, h16;
-        __builtin_memcpy(&l16, &lo, 2);
-        __builtin_memcpy(&h16, &hi, 2);
-        xw[i][4 * t + p] = (uint32_t)l16 | ((uint32_t)h16 << 16);
-      }
+      for (int p = 0; p < 4; ++p) xw[i][4 * t + p] = w[p];
     }
   }
   return ssq;
@@ -495,18 +513,59 @@ __device__ inline int q4_row(const Q4Fused& e, int RB, int lr, bool& ok) {
   return (p / hd) * e.kv.d + p % hd + hi * hd;
 }
 
-template <int NI, int R, int EPI>
+template <int NI, int KP, int R, int EPI>
 __global__ __launch_bounds__(256) void k_q4_fused(const bf16_t* __restrict__ X, const uint32_t* __restrict__ words,
                                                  const bf16_t* __restrict__ scales,
                                                  const bf16_t* __restrict__ biases, Q4Fused e) {
+  constexpr int kp = KP, NSETS = 4 / KP;   // K parts, row sets (wavefronts per part)
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int K = e.K, nchunk = K / 32, ngrp = K / 64;
-  const int kp = e.kp, kpi = wave % kp, rs = wave / kp;
+  const int kpi = wave % kp, rs = wave / kp;
   const int c0 = kpi * nchunk / kp, c1 = (kpi + 1) * nchunk / kp;
   const int rpw = e.rpw, RB = 4 * rpw / kp, half = RB >> 1;
+  const float* gamma = e.norm ? e.gamma : nullptr;
   __shared__ float ys[4][kQ4MaxRB];
-  __shared__ float ssq_l[4];
+  __shared__ float ssq_w[4];
   __shared__ float red[4];
+  // x-hat shared by the wavefronts of a part: unit (i, t) of lane l
+  constexpr int NSH = NSETS > 1 ? KP * NI * 4 * 64 : 1;
+  __shared__ uint4 xl[NSH];
+  __shared__ float2 hl[NSH];
+  // norm 2: the producer's partial sums of squares (lane l: partials l + 64 u,
+  // clamped, unconditional so that no wait below covers later loads),
+  // requested before everything else and summed after the rows
+  constexpr int SU = 8;
+  float sp[SU];
+  float r_inv = 1.f;
+  if (e.norm == 2) {
+    if (e.stat.inv) {
+      r_inv = e.stat.inv[0];
+    } else if (e.stat.ss) {
+#pragma unroll
+      for (int u = 0; u < SU; ++u) sp[u] = e.stat.ss[(size_t)min(lane + 64 * u, e.stat.nb - 1) * e.stat.M];
+    }
+  }
+  // with several row sets per part, set rs converts units t = rs * KP + tt of
+  // every chunk of the part (tt < KP); its x and gamma go out before the codes
+  uint4 xr[NI][KP];
+  f32x4 gr[NI][KP][2];
+  if constexpr (NSETS > 1) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int c = c0 + lane + 64 * i;
+#pragma unroll
+      for (int tt = 0; tt < KP; ++tt) {
+        // (lanes past the part read its last chunk and convert zeros)
+        const int k0 = min(c, c1 - 1) * 32 + 8 * (rs * KP + tt);
+        xr[i][tt] = ld16(X + k0);
+        gr[i][tt][0] = gr[i][tt][1] = f32x4{1.f, 1.f, 1.f, 1.f};
+        if (gamma) {
+          gr[i][tt][0] = *reinterpret_cast<const f32x4*>(gamma + k0);
+          gr[i][tt][1] = *reinterpret_cast<const f32x4*>(gamma + k0 + 4);
+        }
+      }
+    }
+  }
   uint4 wc[2][R][NI];
   float sv[2][R][NI], bv[2][R][NI];
   // rows past the set's last one repeat it, rows that do not exist read the
@@ -530,29 +589,69 @@ __global__ __launch_bounds__(256) void k_q4_fused(const bf16_t* __restrict__ X, 
   };
   // the first group's codes go out first, then the epilogue's own operands
   load_group(0, std::integral_constant<int, 0>{});
+  // (loads with clamped indices, not under a condition: a conditional load is
+  // waited for at once, and that wait would cover the codes requested above)
   bool own_ok = false;
   int own_row = 0;
-  float rv = 0.f;
+  bf16_t rv = 0;
   float2 cs = make_float2(1.f, 0.f);
   int pos = 0;
   if (EPI == Q4E_RESID) {
     own_row = blockIdx.x * RB + tid;
     own_ok = tid < RB && own_row < e.N;
-    if (own_ok) rv = bf16_to_f32(e.resid[own_row]);
+    rv = e.resid[min(own_row, e.N - 1)];
   } else if (EPI == Q4E_QKV) {
     const int hd = e.kv.d >> 1;
     own_row = blockIdx.x * half + tid;   // pair index
     own_ok = tid < half && own_row < (e.N >> 1);
     pos = e.kv.lens[0];
-    if (own_ok && (own_row / hd) * e.kv.d < e.Nq + e.Nkv) cs = e.rope[(size_t)pos * hd + own_row % hd];
+    cs = e.rope[(size_t)pos * hd + own_row % hd];
   }
-  const float pv = e.norm == 2 ? e.stat.pre(0) : 0.f;
+  // everything above is requested before the conversion below starts
+  __builtin_amdgcn_sched_barrier(0);
   uint32_t xw[NI][16];
   float hs[NI], xs[NI];
-  float ssq = q4_xhat<NI>(X, e.norm ? e.gamma : nullptr, c0, c1, lane, xw, hs, xs);
+  float ssq = 0.f;
+  if constexpr (NSETS > 1) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const bool inpart = c0 + lane + 64 * i < c1;
+#pragma unroll
+      for (int tt = 0; tt < KP; ++tt) {
+        uint32_t w[4];
+        float h, x;
+        q4_unit(inpart ? xr[i][tt] : make_uint4(0, 0, 0, 0), gamma != nullptr, gr[i][tt][0], gr[i][tt][1], w, h,
+                x, ssq);
+        const int u = ((kpi * NI + i) * 4 + rs * KP + tt) * 64 + lane;
+        xl[u] = make_uint4(w[0], w[1], w[2], w[3]);
+        hl[u] = make_float2(h, x);
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      hs[i] = 0.f;
+      xs[i] = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int u = ((kpi * NI + i) * 4 + t) * 64 + lane;
+        const uint4 w = xl[u];
+        const float2 h = hl[u];
+        xw[i][4 * t + 0] = w.x;
+        xw[i][4 * t + 1] = w.y;
+        xw[i][4 * t + 2] = w.z;
+        xw[i][4 * t + 3] = w.w;
+        hs[i] += h.x;
+        xs[i] += h.y;
+      }
+    }
+  } else {
+    ssq = q4_xhat<NI>(X, gamma, c0, c1, lane, xw, hs, xs);
+  }
+  // every wavefront's x^2 covers a disjoint share of K, together all of it
   if (e.norm == 1) {
     ssq = warp_sum(ssq);
-    if (rs == 0 && lane == 0) ssq_l[kpi] = ssq;
+    if (lane == 0) ssq_w[wave] = ssq;
   }
   auto group = [&](int g, auto bc) {
     constexpr int b = decltype(bc)::value;
@@ -592,11 +691,19 @@ __global__ __launch_bounds__(256) void k_q4_fused(const bf16_t* __restrict__ X, 
   // or from the producer's statistic (norm 2)
   float r = 1.0f;
   if (e.norm == 1) {
-    float t = 0.f;
-    for (int k = 0; k < kp; ++k) t += ssq_l[k];
-    r = 1.0f / sqrtf(t / (float)K + e.eps);
+    r = 1.0f / sqrtf(((ssq_w[0] + ssq_w[1]) + (ssq_w[2] + ssq_w[3])) / (float)K + e.eps);
   } else if (e.norm == 2) {
-    r = e.stat.finish_block(pv);
+    if (e.stat.inv) {
+      r = r_inv;
+    } else if (e.stat.ss) {
+      // (every wavefront reduces the same values in the same order)
+      float v = 0.f;
+#pragma unroll
+      for (int u = 0; u < SU; ++u)
+        if (lane + 64 * u < e.stat.nb) v += sp[u];
+      for (int j = lane + 64 * SU; j < e.stat.nb; j += 64) v += e.stat.ss[(size_t)j * e.stat.M];
+      r = 1.0f / sqrtf(warp_sum(v) / (float)e.stat.n + e.stat.eps);
+    }
   }
   auto sum_row = [&](int lr) {
     float v = 0.f;
@@ -612,7 +719,7 @@ __global__ __launch_bounds__(256) void k_q4_fused(const bf16_t* __restrict__ X, 
     if (own_ok) {
       const float f = sum_row(tid);
       if (e.branch) e.branch[own_row] = f32_to_bf16(f);
-      o = Elt<bf16_t>::round(rv + f);
+      o = Elt<bf16_t>::round(bf16_to_f32(rv) + f);
       e.out[own_row] = f32_to_bf16(o);
     }
     if (e.ss_out) {
@@ -686,13 +793,17 @@ bool launch_q4_fused(const bf16_t* X, const uint32_t* words, const bf16_t* scale
   e.kp = kp;
   e.rpw = rpw;
   const dim3 grid(q4_fused_blocks(e.N, e.K));
-#define Q4F(n, r, E)                                                                                     \
-  case n:                                                                                                \
-    hipLaunchKernelGGL((k_q4_fused<n, r, E>), grid, dim3(256), 0, s, X, words, scales, biases, e);     \
-    return true;
-#define Q4FE(E)                                                                     \
-  case E:                                                                           \
-    switch (ni) { Q4F(1, 4, E) Q4F(2, 4, E) Q4F(3, 4, E) Q4F(4, 2, E) } \
+#define Q4F(n, k, r, E)                                                                                \
+  if (ni == n && kp == k) {                                                                            \
+    hipLaunchKernelGGL((k_q4_fused<n, k, r, E>), grid, dim3(256), 0, s, X, words, scales, biases, e);  \
+    return true;                                                                                       \
+  }
+  // (a part of more than 256 chunks is split further, so parts of kp > 1
+  // hold more than 128 chunks: 3 or 4 per lane)
+#define Q4FE(E)                                                                                   \
+  case E:                                                                                         \
+    Q4F(1, 1, 4, E) Q4F(2, 1, 4, E) Q4F(3, 1, 4, E) Q4F(4, 1, 2, E) Q4F(3, 2, 4, E) Q4F(4, 2, 2, E) \
+    Q4F(3, 4, 4, E) Q4F(4, 4, 2, E)                                                               \
     break;
   switch (e.epi) { Q4FE(Q4E_PLAIN) Q4FE(Q4E_QKV) Q4FE(Q4E_RESID) Q4FE(Q4E_SWIGLU) }
 #undef Q4FE
