@@ -412,11 +412,14 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const _Float16* __restrict__ xh
 // with what follows the projection in the block done in the same kernel.
 // No preparation pass: the block's 4 wavefronts form 4 / kp row sets, each
 // split over kp parts of K; lane l of a wavefront owns the 32-code chunks
-// c0 + l + 64 i (i < NI) of its part, converts its chunks of x once (gamma
-// applied, fp16 pairs in the word order of the nibble trick, the two chunk
-// sums) and keeps them in registers for all the rows of its set.  Rows go in
-// groups of R, the codes and group scales of the next group requested before
-// the current one is multiplied.  Row sums land in LDS; after one barrier the
+// c0 + l + 64 i (i < NI) of its part and keeps x-hat for them in registers
+// (gamma applied, fp16 pairs in the word order of the nibble trick, the two
+// chunk sums) for all the rows of its set; the wavefronts of a part convert a
+// share of it each and exchange it through LDS.  Rows go in groups of R
+// through a ring of NB register buffers, the codes and group scales of group
+// g + NB - 1 requested before group g is multiplied (R = 1, NB = 2 measured
+// best: fewer registers, three wavefronts per SIMD, beat deeper rings).  Row
+// sums land in LDS; after one barrier the
 // block applies the RMSNorm row scale (a per-row scalar, so it multiplies the
 // sum) and its epilogue, one thread per output element:
 //   Q4E_PLAIN : y[n] = the projection (fp32);
@@ -426,6 +429,15 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const _Float16* __restrict__ xh
 //               squares per block, optional branch copy and cache-length bump;
 //   Q4E_SWIGLU: g = silu(w1 n) * (w3 n) (the block's rows are w1/w3 pairs).
 constexpr int kQ4MaxRB = 256;   // rows per block at most
+
+// f(integral_constant<int, i>) for i = I .. N-1, unrolled at compile time
+template <int I, int N, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // One 8-code unit of x-hat = x * gamma (word t of a chunk covers codes 8t ..
 // 8t+7): the fp16 pairs (x0, x4), (x1/16, x5/16), (x2, x6), (x3/16, x7/16) in
@@ -513,7 +525,7 @@ __device__ inline int q4_row(const Q4Fused& e, int RB, int lr, bool& ok) {
   return (p / hd) * e.kv.d + p % hd + hi * hd;
 }
 
-template <int NI, int KP, int R, int EPI>
+template <int NI, int KP, int R, int NB, int EPI>
 __global__ __launch_bounds__(256) void k_q4_fused(const bf16_t* __restrict__ X, const uint32_t* __restrict__ words,
                                                  const bf16_t* __restrict__ scales,
                                                  const bf16_t* __restrict__ biases, Q4Fused e) {
@@ -566,8 +578,9 @@ __global__ __launch_bounds__(256) void k_q4_fused(const bf16_t* __restrict__ X, 
       }
     }
   }
-  uint4 wc[2][R][NI];
-  float sv[2][R][NI], bv[2][R][NI];
+  // a ring of NB buffers of R rows: NB - 1 groups in flight
+  uint4 wc[NB][R][NI];
+  float sv[NB][R][NI], bv[NB][R][NI];
   // rows past the set's last one repeat it, rows that do not exist read the
   // block's first row, lanes past the part repeat its last chunk (all loaded,
   // never used)
@@ -587,8 +600,8 @@ __global__ __launch_bounds__(256) void k_q4_fused(const bf16_t* __restrict__ X, 
       }
     }
   };
-  // the first group's codes go out first, then the epilogue's own operands
-  load_group(0, std::integral_constant<int, 0>{});
+  // the first NB - 1 groups' codes go out first, then the epilogue's own operands
+  static_for<0, NB - 1>([&](auto j) { load_group(decltype(j)::value, j); });
   // (loads with clamped indices, not under a condition: a conditional load is
   // waited for at once, and that wait would cover the codes requested above)
   bool own_ok = false;
@@ -655,9 +668,9 @@ __global__ __launch_bounds__(256) void k_q4_fused(const bf16_t* __restrict__ X, 
   }
   auto group = [&](int g, auto bc) {
     constexpr int b = decltype(bc)::value;
-    // (unconditional, so the compiler's waits for this group stay exact; after
+    // (unconditional, so the compiler's waits for this group stay exact; past
     // the last group it repeats rows just read)
-    load_group(g + 1, std::integral_constant<int, b ^ 1>{});
+    load_group(g + NB - 1, std::integral_constant<int, (b + NB - 1) % NB>{});
 #pragma unroll
     for (int q = 0; q < R; ++q) {
       float acc = 0.f;
@@ -682,9 +695,10 @@ __global__ __launch_bounds__(256) void k_q4_fused(const bf16_t* __restrict__ X, 
     }
   };
   const int ngroups = (rpw + R - 1) / R;
-  for (int g = 0; g < ngroups; g += 2) {
-    group(g, std::integral_constant<int, 0>{});
-    if (g + 1 < ngroups) group(g + 1, std::integral_constant<int, 1>{});
+  for (int g = 0; g < ngroups; g += NB) {
+    static_for<0, NB>([&](auto j) {
+      if (g + decltype(j)::value < ngroups) group(g + decltype(j)::value, j);
+    });
   }
   __syncthreads();
   // row scale: 1 (norm 0), from the row's mean square over all of K (norm 1),
@@ -768,10 +782,11 @@ static bool q4_fused_shape(int N, int K, int& kp, int& ni, int& rpw) {
   if (nchunk < 1 || nchunk > 1024) return false;
   kp = nchunk <= 256 ? 1 : nchunk <= 512 ? 2 : 4;
   ni = ((nchunk + kp - 1) / kp + 63) / 64;
-  // rows per wavefront: enough to amortize each lane's conversion of its
-  // chunks of x, a grid of about 384 blocks; the block's rows even (pairs)
-  // and at most kQ4MaxRB
-  rpw = std::max(4, (N * kp + 768) / 1536);
+  // rows per wavefront: at least 4 (to amortize the conversion of x), else
+  // few enough for a grid of at most 512 blocks, two per compute unit (more,
+  // shorter blocks measured slower); the block's rows even (pairs) and at most
+  // kQ4MaxRB
+  rpw = std::max(4, (N * kp + 2047) / 2048);
   rpw = std::min(rpw, kQ4MaxRB * kp / 4);
   if (kp == 4) rpw = (rpw + 1) & ~1;
   return true;
@@ -793,17 +808,17 @@ bool launch_q4_fused(const bf16_t* X, const uint32_t* words, const bf16_t* scale
   e.kp = kp;
   e.rpw = rpw;
   const dim3 grid(q4_fused_blocks(e.N, e.K));
-#define Q4F(n, k, r, E)                                                                                \
-  if (ni == n && kp == k) {                                                                            \
-    hipLaunchKernelGGL((k_q4_fused<n, k, r, E>), grid, dim3(256), 0, s, X, words, scales, biases, e);  \
-    return true;                                                                                       \
+#define Q4F(n, k, r, nb, E)                                                                               \
+  if (ni == n && kp == k) {                                                                               \
+    hipLaunchKernelGGL((k_q4_fused<n, k, r, nb, E>), grid, dim3(256), 0, s, X, words, scales, biases, e); \
+    return true;                                                                                          \
   }
   // (a part of more than 256 chunks is split further, so parts of kp > 1
   // hold more than 128 chunks: 3 or 4 per lane)
 #define Q4FE(E)                                                                                   \
   case E:                                                                                         \
-    Q4F(1, 1, 4, E) Q4F(2, 1, 4, E) Q4F(3, 1, 4, E) Q4F(4, 1, 2, E) Q4F(3, 2, 4, E) Q4F(4, 2, 2, E) \
-    Q4F(3, 4, 4, E) Q4F(4, 4, 2, E)                                                               \
+    Q4F(1, 1, 1, 2, E) Q4F(2, 1, 1, 2, E) Q4F(3, 1, 1, 2, E) Q4F(4, 1, 1, 2, E) Q4F(3, 2, 1, 2, E)   \
+    Q4F(4, 2, 1, 2, E) Q4F(3, 4, 1, 2, E) Q4F(4, 4, 1, 2, E)                                       \
     break;
   switch (e.epi) { Q4FE(Q4E_PLAIN) Q4FE(Q4E_QKV) Q4FE(Q4E_RESID) Q4FE(Q4E_SWIGLU) }
 #undef Q4FE
