@@ -304,20 +304,31 @@ void launch_attn_prefill_bf16(const bf16_t* q, KVView kv, int B, int L, int H, i
 // 4*t + i.  Those 8 probabilities are then directly the B operand of the P.V
 // MFMA, and the matching V^T operand is one 16-byte load of 8 consecutive
 // slots of a transposed V page row.
+// BM (few sequences and kv heads, a short cache): one block of 8 wavefronts per
+// (b, g), wavefront c taking keys [c * split_len, (c + 1) * split_len); the 8
+// partials are merged through LDS in the same block, so no second kernel.
 // two wavefronts per SIMD: the register budget of one 64-key step (K, V, P, O)
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_decode_bf16(
+template <bool BM>
+__global__ __launch_bounds__(BM ? 512 : 256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_decode_bf16(
     const bf16_t* __restrict__ q, KVView kv, int B, int H, int G, int n_splits, int split_len,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, bf16_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15, hg = lane >> 4;
   // wave-uniform indices in scalar registers: the lens and block-table reads are
   // scalar loads, counted apart from the vector loads in flight
-  const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
-  const int total = B * G * n_splits;
-  if (wid >= total) return;
-  const int c = wid % n_splits;
-  const int g = (wid / n_splits) % G;
-  const int b = wid / (n_splits * G);
+  int c, g, b;
+  if constexpr (BM) {
+    c = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    g = __builtin_amdgcn_readfirstlane(blockIdx.x % G);
+    b = __builtin_amdgcn_readfirstlane(blockIdx.x / G);
+  } else {
+    const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+    const int total = B * G * n_splits;
+    if (wid >= total) return;
+    c = wid % n_splits;
+    g = (wid / n_splits) % G;
+    b = wid / (n_splits * G);
+  }
   const int n_rep = H / G;
   const int pos = kv.lens[b];               // the new token's position; keys 0..pos
   const int nkeys = pos + 1;
@@ -425,6 +436,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
   // lane: O^T[d = 16*ds + 4*hg + i][q = l16]
+  if constexpr (BM) {
+    // rows padded to 132 floats: the 16 query columns' writes spread over banks
+    __shared__ float so[8][16][132];
+    __shared__ float2 sml[8][16];
+    if (qvalid) {
+#pragma unroll
+      for (int ds = 0; ds < 8; ++ds)
+        *reinterpret_cast<float4*>(&so[c][l16][16 * ds + 4 * hg]) =
+            make_float4(o_acc[ds][0], o_acc[ds][1], o_acc[ds][2], o_acc[ds][3]);
+      if (hg == 0) sml[c][l16] = make_float2(m_run, l_run);
+    }
+    __syncthreads();
+    // wavefront w merges query heads w, w + 8, ... of the group: o = sum_c
+    // e^(m_c - M) O_c / sum_c e^(m_c - M) l_c in split order
+    for (int r = c; r < n_rep; r += 8) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) M = fmaxf(M, sml[j][r].x);
+      float o0 = 0.f, o1 = 0.f, den = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float mj = sml[j][r].x;
+        const float w = mj == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mj - M);
+        den += w * sml[j][r].y;
+        o0 += w * so[j][r][lane];
+        o1 += w * so[j][r][lane + 64];
+      }
+      bf16_t* orow = out + ((size_t)b * H + g * n_rep + r) * 128;
+      orow[lane] = f32_to_bf16(o0 / den);
+      orow[lane + 64] = f32_to_bf16(o1 / den);
+    }
+    return;
+  }
   if (qvalid) {
     const size_t pi = (((size_t)b * H + hq) * n_splits + c);
     float* po = part_o + pi * 128;
@@ -494,9 +538,20 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
 void launch_attn_decode_bf16(const bf16_t* q, KVView kv, int B, int H, int G, int n_splits, int split_len,
                              float* part_o, float* part_ml, bf16_t* out, hipStream_t s) {
   if (B <= 0) return;
+  // the keys the splits cover (at least every cached key)
+  const long keys = (long)n_splits * split_len;
+  if (B * G <= 128 && keys <= 2048) {
+    // few (b, g) pairs and a short cache: one block each, eight key ranges of
+    // whole 64-key steps, merged in the block
+    const int sl8 = (int)(((keys + 7) / 8 + 63) / 64 * 64);
+    hipExtLaunchKernelGGL(k_attn_decode_bf16<true>, dim3(B * G), dim3(512), 0, s, g_clock.start, g_clock.stop, 0, q,
+                          kv, B, H, G, 8, sl8, part_o, part_ml, out);
+    g_clock = LaunchClock{};
+    return;
+  }
   int waves = B * G * n_splits;
-  hipExtLaunchKernelGGL(k_attn_decode_bf16, dim3((waves + 3) / 4), dim3(256), 0, s, g_clock.start, nullptr, 0, q, kv, B, H, G, n_splits,
-                     split_len, part_o, part_ml);
+  hipExtLaunchKernelGGL(k_attn_decode_bf16<false>, dim3((waves + 3) / 4), dim3(256), 0, s, g_clock.start, nullptr, 0, q, kv, B, H, G, n_splits,
+                     split_len, part_o, part_ml, nullptr);
   int bh = B * H;
   hipExtLaunchKernelGGL(k_attn_merge, dim3((bh + 3) / 4), dim3(256), 0, s, nullptr, g_clock.stop, 0, part_o, part_ml,
                         bh, n_splits, out);
