@@ -510,7 +510,7 @@ static bool q4_single(const Dims& d, int T, bool decode) {
 }
 
 struct SLayout {
-  size_t inv1, inv2, ssx, ssh, q, attn, h, g, ffn, part, ao, aml, xh, xsum, deq, total;
+  size_t inv1, inv2, ssx, ssh, q, attn, h, g, ffn, part, ao, aml, xh, xsum, deq, a16, total;
   int n_splits, split_len, ks_qkv, nb_h;
 };
 
@@ -570,9 +570,11 @@ static SLayout scratch_layout(const llama_block_config& c, const Dims& d, int T,
   if (d.q4 && !decode) {
     int NK[4][2];
     lin_shapes(d, NK);
-    for (int i = 0; i < 4; ++i) deq = std::max(deq, (size_t)NK[i][0] * NK[i][1] * 2);
+    for (int i = 0; i < 4; ++i) deq = std::max(deq, (size_t)NK[i][0] * tiled_chunks(NK[i][1]) * kTileK * 2);
   }
   L.deq = off; off = align256(off + deq);
+  // 4-bit prompt pass: fp16 copy of a GEMM's A
+  L.a16 = off; off = align256(off + ((d.q4 && !decode) ? (size_t)T * maxK * 2 : 0));
   L.total = off;
   return L;
 }
@@ -725,21 +727,32 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
   bf16_t* h = (bf16_t*)(sc + S.h);
   bf16_t* g = (bf16_t*)(sc + S.g);
   _Float16* deq = (_Float16*)(sc + S.deq);
+  _Float16* a16 = (_Float16*)(sc + S.a16);
   const float eps = blk->cfg.norm_eps;
   // 4-bit weights: dequantized (gamma folded) to fp16 right before their GEMM,
-  // which then runs on fp16 MFMA
-  auto weight = [&](const Lin& lin, const float* gamma) -> const bf16_t* {
-    if (!d.q4) return (const bf16_t*)lin.w;
-    launch_q4_dequant((const uint32_t*)lin.w, lin.s, lin.b, lin.N, lin.K, 64, gamma, deq, s);
-    return (const bf16_t*)deq;
+  // which then runs on fp16 MFMA; where the shape allows, B tiled and A copied
+  // to fp16 so that the GEMM takes the direct-to-LDS tiles
+  auto operands = [&](GemmArgs& g, const bf16_t* A, const Lin& lin, const float* gamma) {
+    g.A = A;
+    if (!d.q4) {
+      g.B = (const bf16_t*)lin.w;
+      return;
+    }
+    g.b_f16 = 1;
+    g.a_f16 = gemm_f16_direct_ok(M, lin.N, lin.K);
+    launch_q4_dequant((const uint32_t*)lin.w, lin.s, lin.b, lin.N, lin.K, 64, gamma, g.a_f16, deq, s);
+    g.B = (const bf16_t*)deq;
+    if (g.a_f16) {
+      launch_bf16_to_f16(A, a16, (size_t)M * lin.K, s);
+      g.A = (const bf16_t*)a16;
+    }
   };
   mk(s);
   launch_rms_inv<bf16_t>((const bf16_t*)x, M, d.D, eps, inv1, s);
   mk(s);
   GemmArgs a{};
-  a.A = (const bf16_t*)x;
-  a.B = weight(blk->qkv, blk->gamma1);
-  a.M = M; a.N = d.Nqkv; a.K = d.D; a.b_f16 = d.q4;
+  operands(a, (const bf16_t*)x, blk->qkv, blk->gamma1);
+  a.M = M; a.N = d.Nqkv; a.K = d.D;
   a.inv_rms = inv1;
   a.q_out = q; a.Nq = d.Nq; a.Nkv = d.Nkv; a.L = L;
   a.rope = blk->rope; a.traditional = blk->cfg.rope_traditional;
@@ -755,8 +768,9 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
   auto resid_gemm = [&](const bf16_t* A, const Lin& lin, const bf16_t* resid, bf16_t* out, int K, int32_t* lens_add,
                         int lens_inc, bf16_t* branch) {
     GemmArgs g{};
-    g.A = A; g.B = weight(lin, nullptr); g.M = M; g.N = d.D; g.K = K; g.b_f16 = d.q4;
-    const int ks = gemm_split_k(M, d.D, K, d.q4);
+    operands(g, A, lin, nullptr);
+    g.M = M; g.N = d.D; g.K = K;
+    const int ks = gemm_split_k(M, d.D, K, g.b_f16 && !g.a_f16);
     if (ks > 1) {
       g.C = part; g.ksplit = ks;
       launch_gemm_mfma(EPI_F32, g, s);
@@ -771,7 +785,8 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
   launch_rms_inv<bf16_t>(h, M, d.D, eps, inv2, s);
   mk(s);
   GemmArgs f{};
-  f.A = h; f.B = weight(blk->w13, blk->gamma2); f.M = M; f.N = 2 * d.F; f.K = d.D; f.b_f16 = d.q4;
+  operands(f, h, blk->w13, blk->gamma2);
+  f.M = M; f.N = 2 * d.F; f.K = d.D;
   f.inv_rms = inv2; f.g_out = g;
   launch_gemm_mfma(EPI_SWIGLU, f, s);
   mk(s);

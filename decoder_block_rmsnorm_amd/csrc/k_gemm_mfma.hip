@@ -70,8 +70,10 @@ __device__ inline bf16x8 u4_as_bf16x8(uint4 v) {
   return r;
 }
 
-// F16: B holds fp16 values (4-bit weights dequantized to fp16); A (bf16) is
-// converted to fp16 on its way into LDS and the MFMA runs on fp16 operands.
+// F16: the MFMA runs on fp16 operands (4-bit weights dequantized to fp16).
+// Register-staged tiles: B fp16 row-major, A (bf16) converted to fp16 on its
+// way into LDS.  Direct-to-LDS tiles: A already fp16 in memory, B fp16 in the
+// tiled layout.
 __device__ inline uint4 bf16x8_to_f16x8(uint4 v) {
   uint32_t in[4] = {v.x, v.y, v.z, v.w}, out[4];
 #pragma unroll
@@ -131,7 +133,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
   auto tblk = [&](int k) { return (size_t)(k >> 8) * ngr * kTileElems + ((k >> 5) & 7) * 512; };
   const int kslice0 = ksi * Kslice;
   const bf16_t* Ag = a.A + (size_t)kslice0;
-  const bf16_t* Bg = a.B + (F16 ? (size_t)kslice0 : 0);
+  constexpr bool DIRECT = DEPTH == 0 || DEPTH == 3 || DEPTH == 4;
+  constexpr bool BROW = F16 && !DIRECT;   // B row-major (else tiled)
+  const bf16_t* Bg = a.B + (BROW ? (size_t)kslice0 : 0);
   const int per_group = GROUP_M * tiles_n;
   const int group = bid / per_group;
   const int first_m = group * GROUP_M;
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
   // element offsets (operands are < 2^31 elements), so each load needs one VGPR
   // of address instead of two.
   const bf16_t* Atile = Ag + (size_t)m0 * K;
-  const bf16_t* Btile = Bg + (F16 ? (size_t)n0 * K : (size_t)(n0 >> 4) * kTileElems);
+  const bf16_t* Btile = Bg + (BROW ? (size_t)n0 * K : (size_t)(n0 >> 4) * kTileElems);
   uint32_t aoff[A_CH], boff[B_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
     const int c = tid + NT * i;
-    if constexpr (F16) {
+    if constexpr (BROW) {
       boff[i] = (uint32_t)((c >> 3) * K + (c & 7) * 8);
     } else {
       // piece c of a K step: group c / 128, 1 KB block (c / 64) % 2, lane c % 64
@@ -170,7 +174,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
   }
   auto gload = [&](int kt, uint4(&ra)[A_CH], uint4(&rb)[B_CH]) {
     const bf16_t* at = Atile + kt * BK;
-    const bf16_t* bt = Btile + (F16 ? (size_t)kt * BK : tblk(kslice0 + kt * BK));
+    const bf16_t* bt = Btile + (BROW ? (size_t)kt * BK : tblk(kslice0 + kt * BK));
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) ra[i] = ld16(at + aoff[i]);
 #pragma unroll
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       int c = tid + NT * i;
-      if constexpr (F16)
+      if constexpr (BROW)
         st16(Bs(buf) + (c >> 3) * LDS_ST + (c & 7) * 8, rb[i]);
       else  // row 16 * group + lane % 16, columns 32 * block + 8 * (lane / 16)
         st16(Bs(buf) + ((c >> 7) * 16 + (c & 15)) * LDS_ST + ((c >> 6) & 1) * 32 + ((c >> 4) & 3) * 8, rb[i]);
@@ -272,7 +276,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     constexpr int NKB = BKS / 32;                      // 32-column blocks per step
     constexpr int NKK = BKS / 16;                      // MFMA sub-steps per step
     constexpr int LPS = (BM / 64 + 4) * NKB;           // direct loads per wavefront per step
-    static_assert(!F16 && NW == 4 && BN == 256 && (BM == 256 || (BM == 128 && DEPTH == 0)), "direct-LDS configuration");
+    static_assert((!F16 || DEPTH == 0) && NW == 4 && BN == 256 && (BM == 256 || (BM == 128 && DEPTH == 0)),
+                  "direct-LDS configuration");
     constexpr int AG = BM / 64, BG = 4;                // A and B row groups each wavefront loads
     constexpr int SA = BM * BKS, SB = BN * BKS;        // bf16 per stage
     const int KT = Kslice / BKS;
@@ -335,8 +340,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     auto mfmas_with = [&](const uint4(&a_)[MI], const uint4(&b_)[4], auto&& slot) {
       static_for<0, NM>([&](auto qc) {
         constexpr int q = decltype(qc)::value;
-        acc[q / 4][q % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_as_bf16x8(a_[q / 4]), u4_as_bf16x8(b_[q % 4]),
-                                                                    acc[q / 4][q % 4], 0, 0, 0);
+        if constexpr (F16)
+          acc[q / 4][q % 4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(u4_as_f16x8(a_[q / 4]), u4_as_f16x8(b_[q % 4]),
+                                                                     acc[q / 4][q % 4], 0, 0, 0);
+        else
+          acc[q / 4][q % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(u4_as_bf16x8(a_[q / 4]),
+                                                                      u4_as_bf16x8(b_[q % 4]), acc[q / 4][q % 4], 0, 0, 0);
         slot(q);
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -667,6 +676,16 @@ template <int EPI, bool F16>
 static void launch_epi(const GemmArgs& a, hipStream_t s) {
   const bool n256 = (a.N % 256) == 0;
   const int f = forced_tile();
+  if constexpr (F16) {
+    if (a.a_f16) {
+      // fp16 A and tiled fp16 B (gemm_f16_direct_ok): direct-to-LDS tiles,
+      // the tile height chosen as for bf16
+      const long t256 = (long)((a.M + 255) / 256) * (a.N / 256), t128 = (long)((a.M + 127) / 128) * (a.N / 256);
+      const bool use128 = ((t128 + 255) / 256) * 0.6 < (double)((t256 + 255) / 256);
+      if ((EPI == EPI_F32 && a.ksplit > 1) || (t256 >= 240 && !use128)) return launch_cfg<256, 256, 4, 0, EPI, true>(a, s);
+      return launch_cfg<128, 256, 4, 0, EPI, true>(a, s);
+    }
+  }
   if constexpr (!F16) {
     // direct-to-LDS tiles address A with 32-bit per-lane byte offsets
     const bool a32 = (size_t)a.M * a.K * sizeof(bf16_t) < ((size_t)1 << 32);
@@ -703,6 +722,10 @@ static void launch_any(int epi, const GemmArgs& a, hipStream_t s) {
     case EPI_SWIGLU: return launch_epi<EPI_SWIGLU, F16>(a, s);
     default: return launch_epi<EPI_RESID, F16>(a, s);
   }
+}
+
+bool gemm_f16_direct_ok(int M, int N, int K) {
+  return N % 256 == 0 && (size_t)M * K * sizeof(bf16_t) < ((size_t)1 << 32);
 }
 
 int gemm_split_k(int M, int N, int K, bool b_f16) {

@@ -242,40 +242,86 @@ void launch_repack_bytes(uint8_t* dst, const uint8_t* src, int rows, int row_byt
 // stack): W[o, k] = scale[o, k/gs] * code[o, k] + bias[o, k/gs], the 4-bit /
 // group-64 format of the MLX quantization config ("模型配置").  The norm weight
 // of the following RMSNorm-fed GEMM is folded in (gamma_k) before the single
-// rounding to fp16 (11 significant bits: 4x finer than bf16).
+// rounding to fp16 (11 significant bits: 4x finer than bf16).  Row-major
+// (one block per row), or in the tiled layout of the dense weights (one block
+// per 16-row x 256-column tile, written as one contiguous 8 KB run; zeros past
+// K up to the chunk boundary); one word of 8 codes -> one 16-byte store.
 // ---------------------------------------------------------------------------
+__device__ inline uint4 q4_dequant_word(const uint32_t* words, const bf16_t* scales, const bf16_t* biases, int row,
+                                        int K, int gs, const float* gamma, int k0) {
+  const uint32_t u = words[(size_t)row * (K / 8) + k0 / 8];
+  const int g = k0 / gs;
+  const float sc = bf16_to_f32(scales[(size_t)row * (K / gs) + g]);
+  const float bi = bf16_to_f32(biases[(size_t)row * (K / gs) + g]);
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float a = sc * (float)((u >> (8 * j)) & 15u) + bi;
+    float b = sc * (float)((u >> (8 * j + 4)) & 15u) + bi;
+    if (gamma) { a *= gamma[k0 + 2 * j]; b *= gamma[k0 + 2 * j + 1]; }
+    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+    uint16_t ua, ub;
+    __builtin_memcpy(&ua, &ha, 2);
+    __builtin_memcpy(&ub, &hb, 2);
+    o[j] = (uint32_t)ua | ((uint32_t)ub << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 __global__ __launch_bounds__(256) void k_q4_dequant(const uint32_t* words, const bf16_t* scales,
                                                     const bf16_t* biases, int N, int K, int gs,
                                                     const float* gamma, _Float16* out) {
-  int row = blockIdx.x;
-  int nw = K / 8;
-  const uint32_t* wr = words + (size_t)row * nw;
-  for (int w = threadIdx.x; w < nw; w += 256) {
-    uint32_t u = wr[w];
-    int k0 = w * 8;
-    int g = k0 / gs;
-    float sc = bf16_to_f32(scales[(size_t)row * (K / gs) + g]);
-    float bi = bf16_to_f32(biases[(size_t)row * (K / gs) + g]);
-    uint32_t o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float a = sc * (float)((u >> (8 * j)) & 15u) + bi;
-      float b = sc * (float)((u >> (8 * j + 4)) & 15u) + bi;
-      if (gamma) { a *= gamma[k0 + 2 * j]; b *= gamma[k0 + 2 * j + 1]; }
-      const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-      uint16_t ua, ub;
-      __builtin_memcpy(&ua, &ha, 2);
-      __builtin_memcpy(&ub, &hb, 2);
-      o[j] = (uint32_t)ua | ((uint32_t)ub << 16);
-    }
-    st16(out + (size_t)row * K + k0, make_uint4(o[0], o[1], o[2], o[3]));
+  const int row = blockIdx.x;
+  for (int w = threadIdx.x; w < K / 8; w += 256)
+    st16(out + (size_t)row * K + w * 8, q4_dequant_word(words, scales, biases, row, K, gs, gamma, w * 8));
+}
+
+// tile (16-row group blockIdx.x, 256-column chunk blockIdx.y): piece p of its
+// 8 KB = 1 KB block p / 64 (32 columns), rows p % 16, columns 8 * ((p / 16) % 4)
+__global__ __launch_bounds__(256) void k_q4_dequant_tiled(const uint32_t* words, const bf16_t* scales,
+                                                          const bf16_t* biases, int N, int K, int gs,
+                                                          const float* gamma, _Float16* out) {
+  const int g = blockIdx.x, c = blockIdx.y;
+  _Float16* tile = out + ((size_t)c * (N >> 4) + g) * kTileElems;
+  for (int p = threadIdx.x; p < kTileElems / 8; p += 256) {
+    const int row = g * 16 + (p & 15), k0 = c * kTileK + (p >> 6) * 32 + ((p >> 4) & 3) * 8;
+    const uint4 v = k0 < K ? q4_dequant_word(words, scales, biases, row, K, gs, gamma, k0) : make_uint4(0, 0, 0, 0);
+    st16(tile + p * 8, v);
   }
 }
 
 void launch_q4_dequant(const uint32_t* words, const bf16_t* scales, const bf16_t* biases, int N, int K, int gs,
-                       const float* gamma, _Float16* out, hipStream_t s) {
+                       const float* gamma, bool tiled, _Float16* out, hipStream_t s) {
   if (N <= 0) return;
-  hipLaunchKernelGGL(k_q4_dequant, dim3(N), dim3(256), 0, s, words, scales, biases, N, K, gs, gamma, out);
+  if (tiled)
+    hipLaunchKernelGGL(k_q4_dequant_tiled, dim3(N >> 4, tiled_chunks(K)), dim3(256), 0, s, words, scales, biases, N,
+                       K, gs, gamma, out);
+  else
+    hipLaunchKernelGGL(k_q4_dequant, dim3(N), dim3(256), 0, s, words, scales, biases, N, K, gs, gamma, out);
+}
+
+// fp16 copy of bf16 values, 8 per thread (n % 8 == 0; |v| < 65504 on its uses)
+__global__ __launch_bounds__(256) void k_bf16_to_f16(const bf16_t* src, _Float16* dst, size_t n8) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const uint4 v = ld16(src + i * 8);
+  const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const _Float16 lo = (_Float16)__uint_as_float(in[j] << 16), hi = (_Float16)__uint_as_float(in[j] & 0xffff0000u);
+    uint16_t l, h;
+    __builtin_memcpy(&l, &lo, 2);
+    __builtin_memcpy(&h, &hi, 2);
+    o[j] = (uint32_t)l | ((uint32_t)h << 16);
+  }
+  st16(dst + i * 8, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+void launch_bf16_to_f16(const bf16_t* src, _Float16* dst, size_t n, hipStream_t s) {
+  const size_t n8 = n / 8;
+  if (!n8) return;
+  hipLaunchKernelGGL(k_bf16_to_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, src, dst, n8);
 }
 
 template <typename T>

@@ -81,9 +81,12 @@ void launch_repack_rows(T* dst, const T* src, int rows, int K, const T* gamma, i
                         int ib_stride, int perm_d, int tgroups, hipStream_t s);
 void launch_repack_bytes(uint8_t* dst, const uint8_t* src, int rows, int row_bytes, int row0, int ib,
                          int ib_stride, int perm_d, hipStream_t s);
-// dense fp16 [N, K] = (scale * code + bias) * gamma_k (gamma may be null)
+// fp16 (scale * code + bias) * gamma_k (gamma may be null): row-major [N, K], or
+// (tiled) in the tiled layout of an [N, K] weight (N % 16 == 0, tiled_chunks(K) *
+// 256 columns, zero past K)
 void launch_q4_dequant(const uint32_t* words, const bf16_t* scales, const bf16_t* biases, int N, int K,
-                       int gs, const float* gamma, _Float16* out, hipStream_t s);
+                       int gs, const float* gamma, bool tiled, _Float16* out, hipStream_t s);
+void launch_bf16_to_f16(const bf16_t* src, _Float16* dst, size_t n, hipStream_t s);
 template <typename T>
 void launch_to_f32(const T* src, float* dst, int n, hipStream_t s);
 // ids_out[*cursor] = *cur_id; logits_out[*cursor] = logits (if logits_out); ++*cursor
@@ -101,7 +104,10 @@ struct GemmArgs {
   const bf16_t* A;  // [M, K] bf16
   const bf16_t* B;  // [N, K] bf16, or fp16 bit patterns when b_f16
   int M, N, K;
-  int b_f16;        // B is fp16: A is converted to fp16 and the MFMA runs on fp16
+  int b_f16;        // B is fp16 and the MFMA runs on fp16: B row-major, A (bf16)
+                    // converted on the way into LDS; or, with a_f16, A fp16 and
+                    // B fp16 in the tiled layout (gemm_f16_direct_ok shapes)
+  int a_f16;
   int ksplit;       // EPI_F32 only: K split into ksplit slices, slice s -> C + s*M*N
   // EPI_F32
   float* C;
@@ -128,6 +134,8 @@ void launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t s);
 // at C + s*M*N
 constexpr int kMaxSplitK = 4;
 int gemm_split_k(int M, int N, int K, bool b_f16);
+// shapes whose fp16 GEMM can take A fp16 and B tiled (direct-to-LDS tiles)
+bool gemm_f16_direct_ok(int M, int N, int K);
 
 // ---------------------------------------------------------------- k_gemv.hip
 // partial[ks][M][N] (fp32) = X[M, kslice] * W[N, kslice]^T (bf16, M <= 64),
