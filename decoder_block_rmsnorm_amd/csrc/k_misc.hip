@@ -276,17 +276,45 @@ __global__ __launch_bounds__(256) void k_q4_dequant(const uint32_t* words, const
     st16(out + (size_t)row * K + w * 8, q4_dequant_word(words, scales, biases, row, K, gs, gamma, w * 8));
 }
 
-// tile (16-row group blockIdx.x, 256-column chunk blockIdx.y): piece p of its
-// 8 KB = 1 KB block p / 64 (32 columns), rows p % 16, columns 8 * ((p / 16) % 4)
-__global__ __launch_bounds__(256) void k_q4_dequant_tiled(const uint32_t* words, const bf16_t* scales,
+// tile (16-row group blockIdx.x, 256-column chunk blockIdx.y), 128 threads:
+// thread (r = t % 16, 32-column block kb = t / 16) expands 32 codes of row
+// 16 g + r (one 16-byte load) into the four 16-byte pieces kb * 64 + 16 j + r
+// of the tile, so that each store instruction writes 256 contiguous bytes per
+// 16 lanes
+__global__ __launch_bounds__(128) void k_q4_dequant_tiled(const uint32_t* words, const bf16_t* scales,
                                                           const bf16_t* biases, int N, int K, int gs,
                                                           const float* gamma, _Float16* out) {
   const int g = blockIdx.x, c = blockIdx.y;
+  const int r = threadIdx.x & 15, kb = threadIdx.x >> 4;
+  const int row = g * 16 + r, kbase = c * kTileK + kb * 32;
   _Float16* tile = out + ((size_t)c * (N >> 4) + g) * kTileElems;
-  for (int p = threadIdx.x; p < kTileElems / 8; p += 256) {
-    const int row = g * 16 + (p & 15), k0 = c * kTileK + (p >> 6) * 32 + ((p >> 4) & 3) * 8;
-    const uint4 v = k0 < K ? q4_dequant_word(words, scales, biases, row, K, gs, gamma, k0) : make_uint4(0, 0, 0, 0);
-    st16(tile + p * 8, v);
+  uint32_t u[4] = {0u, 0u, 0u, 0u};
+  float sc = 0.f, bi = 0.f;
+  const bool in = kbase < K;   // (K % 32 == 0: a block is inside K or past it)
+  if (in) {
+    const uint4 w = ld16(words + (size_t)row * (K / 8) + kbase / 8);
+    u[0] = w.x; u[1] = w.y; u[2] = w.z; u[3] = w.w;
+    sc = bf16_to_f32(scales[(size_t)row * (K / gs) + kbase / gs]);
+    bi = bf16_to_f32(biases[(size_t)row * (K / gs) + kbase / gs]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t o[4] = {0u, 0u, 0u, 0u};
+    if (in) {
+      const int k0 = kbase + 8 * j;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float a = sc * (float)((u[j] >> (8 * e)) & 15u) + bi;
+        float b = sc * (float)((u[j] >> (8 * e + 4)) & 15u) + bi;
+        if (gamma) { a *= gamma[k0 + 2 * e]; b *= gamma[k0 + 2 * e + 1]; }
+        const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+        uint16_t ua, ub;
+        __builtin_memcpy(&ua, &ha, 2);
+        __builtin_memcpy(&ub, &hb, 2);
+        o[e] = (uint32_t)ua | ((uint32_t)ub << 16);
+      }
+    }
+    st16(tile + (kb * 64 + 16 * j + r) * 8, make_uint4(o[0], o[1], o[2], o[3]));
   }
 }
 
@@ -294,7 +322,7 @@ void launch_q4_dequant(const uint32_t* words, const bf16_t* scales, const bf16_t
                        const float* gamma, bool tiled, _Float16* out, hipStream_t s) {
   if (N <= 0) return;
   if (tiled)
-    hipLaunchKernelGGL(k_q4_dequant_tiled, dim3(N >> 4, tiled_chunks(K)), dim3(256), 0, s, words, scales, biases, N,
+    hipLaunchKernelGGL(k_q4_dequant_tiled, dim3(N >> 4, tiled_chunks(K)), dim3(128), 0, s, words, scales, biases, N,
                        K, gs, gamma, out);
   else
     hipLaunchKernelGGL(k_q4_dequant, dim3(N), dim3(256), 0, s, words, scales, biases, N, K, gs, gamma, out);
