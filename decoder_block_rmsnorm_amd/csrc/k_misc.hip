@@ -302,11 +302,20 @@ __global__ __launch_bounds__(128) void k_q4_dequant_tiled(const uint32_t* words,
     uint32_t o[4] = {0u, 0u, 0u, 0u};
     if (in) {
       const int k0 = kbase + 8 * j;
+      float gm[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+      if (gamma) {
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(gamma + k0);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(gamma + k0 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          gm[e] = g0[e];
+          gm[e + 4] = g1[e];
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float a = sc * (float)((u[j] >> (8 * e)) & 15u) + bi;
-        float b = sc * (float)((u[j] >> (8 * e + 4)) & 15u) + bi;
-        if (gamma) { a *= gamma[k0 + 2 * e]; b *= gamma[k0 + 2 * e + 1]; }
+        const float a = (sc * (float)((u[j] >> (8 * e)) & 15u) + bi) * gm[2 * e];
+        const float b = (sc * (float)((u[j] >> (8 * e + 4)) & 15u) + bi) * gm[2 * e + 1];
         const _Float16 ha = (_Float16)a, hb = (_Float16)b;
         uint16_t ua, ub;
         __builtin_memcpy(&ua, &ha, 2);
