@@ -159,13 +159,17 @@ WIDE_GQA = W.BlockShape(dim=4096, n_heads=32, n_kv_heads=4, ffn_dim=512, dtype="
 
 def _long_split_lens():
     r = W.Rng(21)
-    return [int(v) for v in r.g.integers(1, 2300, size=60)] + [1, 319, 320, 2301]
+    return [int(v) for v in r.g.integers(1, 2300, size=59)] + [0, 1, 319, 320, 2301]
 
 
-@pytest.mark.parametrize("shape", ["mha", "gqa", "gqa_long_splits"])
+# "empty_cache": sequences at position 0 (the token attends to itself only)
+# next to short ones, on the path that merges key ranges inside one block
+@pytest.mark.parametrize("shape", ["mha", "gqa", "gqa_long_splits", "empty_cache"])
 def test_bf16_decode_ragged_lengths(shape):
     if shape == "gqa_long_splits":
         s, lens = WIDE_GQA, _long_split_lens()
+    elif shape == "empty_cache":
+        s, lens = SMALL_GQA, [0, 5, 0, 63]
     else:
         s = dataclasses.replace(SMALL_MHA if shape == "mha" else SMALL_GQA, traditional=(shape == "mha"))
         lens = [300, 1, 64, 255, 257]
@@ -180,7 +184,8 @@ def test_bf16_decode_ragged_lengths(shape):
     blk, wd = G.make_block(s, w, max_seq)
     cache = G.make_cache(s, 1, B, max_seq)
     for b in range(B):
-        cache.write(0, b, 0, G.tdev(kv[0][b, :lens[b]], s.dtype), G.tdev(kv[1][b, :lens[b]], s.dtype))
+        if lens[b]:
+            cache.write(0, b, 0, G.tdev(kv[0][b, :lens[b]], s.dtype), G.tdev(kv[1][b, :lens[b]], s.dtype))
     cache.set_lens(0, lens)
     sc = G.scratch(blk, B, B, max_seq)
     blk.set_diag(True)
@@ -247,9 +252,13 @@ def test_q4_decode_single_row_k_parts(name):
     _q4_decode_case(Q4_SINGLE[name], 1, 17)
 
 
-def _q4_decode_case(s, B, seed):
+def test_q4_decode_single_row_empty_cache():
+    _q4_decode_case(SMALL_Q4, 1, 18, lens=[0])
+
+
+def _q4_decode_case(s, B, seed, lens=None):
     rng = W.Rng(seed)
-    lens = [77, 200, 3][:B]
+    lens = lens or [77, 200, 3][:B]
     x = rng.normal((B, 1, s.dim), 1.0, "bf16")
     kv = (rng.normal((B, 200, s.n_kv_heads, s.head_dim), 1.0, "bf16"),
           rng.normal((B, 200, s.n_kv_heads, s.head_dim), 1.0, "bf16"))
@@ -259,7 +268,8 @@ def _q4_decode_case(s, B, seed):
     blk, wd = G.make_block(s, w, max_seq)
     cache = G.make_cache(s, 1, B, max_seq)
     for b in range(B):
-        cache.write(0, b, 0, G.tdev(kv[0][b, :lens[b]], "bf16"), G.tdev(kv[1][b, :lens[b]], "bf16"))
+        if lens[b]:
+            cache.write(0, b, 0, G.tdev(kv[0][b, :lens[b]], "bf16"), G.tdev(kv[1][b, :lens[b]], "bf16"))
     cache.set_lens(0, lens)
     sc = G.scratch(blk, B, B, max_seq)
     blk.set_diag(True)
