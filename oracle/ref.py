@@ -12,10 +12,10 @@ cited below are:
 * "iOS设备上运行LLaMA2-13B：基于苹果MLX框架的完整技术指南" (geoz.com.cn)
   -- sections "LLaMA 2 的结构分析" (module tree), "模型配置" (config.json),
   "核心模块实现" 2-5 (attention with KV cache, FeedForward, RMSNorm, causal
-  mask) and "生成过程" (generation loop).
+  mask) and "生成过程" (generation loop, greedy and sampled).
 * "LLaMA架构深度解析：从开源大模型设计到高效推理的工程实现全流程"
   (developer.cloud.tencent.com.cn) -- section 二 (LLaMARMSNorm, LLaMARoPE,
-  LLaMAAttention, LLaMAMLP, LLaMABlock, LLaMA classes).
+  LLaMAAttention, LLaMAMLP, LLaMABlock, LLaMA classes, LLaMA.generate).
 * "老码农和你一起学AI系列：关于LLaMA解码器" (jsqmd.com) -- sections
   "解码器块的核心组件" and "数据流动" (pre-norm data flow).
 * "《Hands-On Large Language Models》阅读笔记(二)" (yanbin.blog) -- sections
@@ -29,7 +29,9 @@ reason in the design notes of the repository):
   rotation sign as the rotate-half form;
 * GQA maps query head h to kv head floor(h / n_rep);
 * future keys are excluded (weight exactly 0);
-* 4-bit weights dequantize as scale * code + bias per group of 64 inputs.
+* 4-bit weights dequantize as scale * code + bias per group of 64 inputs;
+* a sampled token is chosen by a given uniform u, cumulative mass taken in
+  vocabulary order; ties with the last nucleus token are kept.
 """
 from __future__ import annotations
 
@@ -246,6 +248,41 @@ def argmax_first(v: np.ndarray) -> int:
     """Index of the largest value; the lowest index wins a tie."""
     v = np.asarray(v)
     return int(np.flatnonzero(v == v.max())[0])
+
+
+# ---------------------------------------------------------------------------
+# Sampling -- "生成过程" (MLX page): at temperature 0 the next id is the argmax,
+# above 0 a multinomial draw from softmax(logits / temperature).  LLaMA.generate
+# (page 二) limits the draw to the nucleus: tokens in order of decreasing
+# probability up to and including the first one at which the cumulative
+# probability exceeds top_p.
+# Readings: the random draw comes in as u in [0, 1); u selects the first token,
+# in vocabulary order, at which the cumulative kept probability exceeds
+# u * (kept probability) -- the same distribution as a draw in sorted order;
+# tokens tied with the last nucleus token are kept too.
+# ---------------------------------------------------------------------------
+def sample_probs(logits: np.ndarray, temperature: float, top_p: float) -> np.ndarray:
+    """Unnormalised kept probabilities (0 outside the nucleus)."""
+    z = np.asarray(logits, dtype=F64) / temperature
+    e = np.exp(z - z.max())
+    p = e / e.sum()
+    if top_p >= 1.0:
+        return p
+    order = np.argsort(-p, kind="stable")
+    cum = np.cumsum(p[order])
+    over = np.flatnonzero(cum > top_p)
+    if over.size == 0:
+        return p
+    thr = p[order[over[0]]]
+    return np.where(p >= thr, p, 0.0)
+
+
+def sample(logits: np.ndarray, temperature: float, top_p: float, u: float) -> int:
+    if temperature <= 0.0:
+        return argmax_first(logits)
+    q = sample_probs(logits, temperature, top_p)
+    c = np.cumsum(q)
+    return int(np.flatnonzero(c > u * c[-1])[0])
 
 
 def greedy_generate(ids: np.ndarray, layers: Sequence[Dict[str, object]], head: Dict[str, object],

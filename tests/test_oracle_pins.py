@@ -377,3 +377,64 @@ def test_greedy_cached_equals_recompute_without_cache():
         nxt = ref.argmax_first(logits)
         assert nxt == out["ids"][t]
         seq.append(nxt)
+
+
+# ---------------------------------------------------------------- sampling --
+# "生成过程" (MLX page): temperature 0 is argmax, above 0 a multinomial draw from
+# softmax(logits / T); LLaMA.generate (page 二): the draw is limited to the
+# nucleus (tokens by decreasing probability up to the first at which the
+# cumulative probability exceeds top_p).  Pins: closed forms on a 3-token
+# vocabulary, exact stratified frequencies, and the limits T -> 0, top_p -> 0.
+
+def test_sample_closed_form_three_tokens():
+    z = np.log([1.0, 2.0, 3.0])           # p = 1/6, 2/6, 3/6; cumulative 1/6, 1/2, 1
+    assert ref.sample(z, 1.0, 1.0, 0.1) == 0
+    assert ref.sample(z, 1.0, 1.0, 0.17) == 1
+    assert ref.sample(z, 1.0, 1.0, 0.49) == 1
+    assert ref.sample(z, 1.0, 1.0, 0.5) == 2      # cumulative must exceed u
+    assert ref.sample(z, 1.0, 1.0, 0.999) == 2
+    # temperature 2: p proportional to sqrt(1, 2, 3)
+    r = np.sqrt([1.0, 2.0, 3.0])
+    c = np.cumsum(r) / r.sum()
+    assert ref.sample(z, 2.0, 1.0, c[0] - 1e-9) == 0
+    assert ref.sample(z, 2.0, 1.0, c[0] + 1e-9) == 1
+    assert ref.sample(z, 2.0, 1.0, c[1] + 1e-9) == 2
+
+
+def test_sample_nucleus_closed_form():
+    z = np.log([0.2, 0.5, 0.3])           # sorted: 0.5, 0.3, 0.2; cumulative 0.5, 0.8, 1.0
+    # top_p 0.6: first cumulative over 0.6 is at 0.3 -> kept {1, 2}, mass 0.8
+    q = ref.sample_probs(z, 1.0, 0.6)
+    assert np.allclose(q, [0.0, 0.5, 0.3])
+    assert ref.sample(z, 1.0, 0.6, 0.6) == 1       # 0.48 < 0.5
+    assert ref.sample(z, 1.0, 0.6, 0.7) == 2       # 0.56 > 0.5
+    # top_p equal to a cumulative value: strict 'exceeds' keeps one more token
+    assert np.allclose(ref.sample_probs(z, 1.0, 0.5 + 1e-12), [0.0, 0.5, 0.3])
+    assert np.allclose(ref.sample_probs(z, 1.0, 0.49), [0.0, 0.5, 0.0])
+    # ties with the last nucleus token are all kept
+    zt = np.log([0.4, 0.3, 0.3])
+    assert np.allclose(ref.sample_probs(zt, 1.0, 0.5), [0.4, 0.3, 0.3])
+
+
+def test_sample_stratified_frequencies_equal_probabilities():
+    rng = np.random.default_rng(5)
+    z = rng.normal(size=50) * 2.0
+    p = np.exp(z - z.max())
+    p /= p.sum()
+    n = 20000
+    counts = np.zeros(50)
+    for j in range(n):
+        counts[ref.sample(z, 1.0, 1.0, (j + 0.5) / n)] += 1
+    # each token owns an interval of length p_i of [0, 1): the grid puts
+    # n * p_i +- 1 points in it
+    assert np.all(np.abs(counts - n * p) <= 1.0 + 1e-9)
+
+
+def test_sample_limits_are_argmax():
+    rng = np.random.default_rng(6)
+    for _ in range(20):
+        z = rng.normal(size=300)
+        best = ref.argmax_first(z)
+        assert ref.sample(z, 0.0, 0.9, 0.7) == best
+        assert ref.sample(z, 1e-6, 1.0, float(rng.random())) == best
+        assert ref.sample(z, 1.0, 1e-9, float(rng.random())) == best
