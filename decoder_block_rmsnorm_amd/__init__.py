@@ -179,6 +179,14 @@ def llama_stack_destroy(st: int) -> None:
     lib().llama_stack_destroy(st)
 
 
+def llama_sample(logits, batch, vocab, temperature, top_p, u, ids, stream=None) -> None:
+    _check(lib().llama_sample(_ptr(logits), batch, vocab, temperature, top_p, _ptr(u), _ptr(ids), _stream(stream)))
+
+
+def llama_stack_set_sampling(st, temperature, top_p, u) -> None:
+    _check(lib().llama_stack_set_sampling(st, temperature, top_p, _ptr(u)))
+
+
 def llama_stack_scratch_bytes(st, max_prompt: int, max_seq: int) -> int:
     return lib().llama_stack_scratch_bytes(st, max_prompt, max_seq)
 
@@ -298,7 +306,7 @@ class KVCache:
 
 
 class Stack:
-    """n_layers blocks + embedding + final norm + output head, greedy generation."""
+    """n_layers blocks + embedding + final norm + output head; greedy or sampled generation."""
 
     def __init__(self, blocks: Sequence[Block], embedding, vocab: int, final_norm, output):
         self.blocks = list(blocks)
@@ -309,6 +317,12 @@ class Stack:
 
     def scratch_bytes(self, max_prompt: int, max_seq: int) -> int:
         return llama_stack_scratch_bytes(self.handle, max_prompt, max_seq)
+
+    def set_sampling(self, temperature: float, top_p: float = 1.0, u=None) -> None:
+        """Greedy at temperature <= 0; else u (fp32 [n_steps + 1] on the device,
+        kept alive here) gives the draw of each emitted id."""
+        self._u = u
+        llama_stack_set_sampling(self.handle, temperature, top_p, u)
 
     def generate(self, cache: KVCache, prompt, n_steps: int, ids_out, logits_out, scratch, use_graph=True,
                  stream=None) -> None:

@@ -65,8 +65,10 @@ SIGNATURES = {
     "llama_embed": (I32, [P, I32, I32, I32, P, I32, P, P]),
     "llama_head_scratch_bytes": (SZ, [I32, I32, I32]),
     "llama_lm_head_argmax": (I32, [C.POINTER(llama_linear), I32, I32, I32, P, F32, P, I32, I32, I32, P, P, P, SZ, P]),
+    "llama_sample": (I32, [P, I32, I32, F32, F32, P, P, P]),
     "llama_stack_create": (I32, [C.POINTER(C.c_void_p), I32, P, I32, P, C.POINTER(llama_linear), PP]),
     "llama_stack_destroy": (None, [P]),
+    "llama_stack_set_sampling": (I32, [P, F32, F32, P]),
     "llama_stack_scratch_bytes": (SZ, [P, I32, I32]),
     "llama_stack_generate": (I32, [P, P, P, I32, I32, P, P, P, SZ, I32, P]),
     "llama_last_error": (C.c_char_p, []),

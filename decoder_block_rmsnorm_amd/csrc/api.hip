@@ -982,9 +982,17 @@ extern "C" size_t llama_head_scratch_bytes(int32_t batch, int32_t dim, int32_t v
   return head_layout(batch, dim, vocab).total;
 }
 
+// The next-id rule of the generate loop: temperature <= 0 = greedy, else a draw
+// (u[*u_off]) from the nucleus of softmax(logits / temperature).
+struct Sampling {
+  float temperature = 0.f, top_p = 1.f;
+  const float* u = nullptr;
+  const int32_t* u_off = nullptr;
+};
+
 static llama_status head_enqueue(const llama_linear* head, int wf, int gs, int dt, const void* fnorm, float eps,
                                  const void* x, int B, int D, int V, float* logits, int32_t* ids, void* scratch,
-                                 size_t sbytes, hipStream_t s) {
+                                 size_t sbytes, hipStream_t s, const Sampling& smp = Sampling()) {
   if (!head || !head->w || !fnorm || !x || !ids || !scratch)
     return fail(LLAMA_ERR_INVALID_ARG, "head, final_norm, x, ids and scratch must be non-NULL");
   if (B <= 0 || D <= 0 || V <= 0) return fail(LLAMA_ERR_INVALID_ARG, "batch, dim and vocab must be positive");
@@ -1013,7 +1021,8 @@ static llama_status head_enqueue(const llama_linear* head, int wf, int gs, int d
     launch_rmsnorm_apply<bf16_t>((const bf16_t*)x, (const bf16_t*)fnorm, B, D, eps, (bf16_t*)(sc + L.xn), s);
     launch_gemv_bf16((const bf16_t*)(sc + L.xn), (const bf16_t*)head->w, false, out, B, V, D, 1, nullptr, s);
   }
-  launch_argmax(out, B, V, ids, s);
+  if (smp.temperature > 0.f) launch_sample(out, B, V, smp.temperature, smp.top_p, smp.u, smp.u_off, ids, s);
+  else launch_argmax(out, B, V, ids, s);
   return hip_check("lm_head_argmax");
 }
 
@@ -1022,6 +1031,16 @@ extern "C" llama_status llama_lm_head_argmax(const llama_linear* head, int32_t w
                                              int32_t V, float* logits, int32_t* ids, void* scratch, size_t sbytes,
                                              void* stream) {
   return head_enqueue(head, wf, gs, dt, fnorm, eps, x, B, D, V, logits, ids, scratch, sbytes, (hipStream_t)stream);
+}
+
+extern "C" llama_status llama_sample(const float* logits, int32_t batch, int32_t vocab, float temperature,
+                                     float top_p, const float* u, int32_t* ids, void* stream) {
+  if (!logits || !ids || (temperature > 0.f && !u))
+    return fail(LLAMA_ERR_INVALID_ARG, "logits, ids and (temperature > 0) u must be non-NULL");
+  if (batch <= 0 || vocab <= 0) return fail(LLAMA_ERR_INVALID_ARG, "batch and vocab must be positive");
+  if (!(top_p > 0.f && top_p <= 1.f)) return fail(LLAMA_ERR_INVALID_ARG, "top_p must lie in (0, 1]");
+  launch_sample(logits, batch, vocab, temperature, top_p, u, nullptr, ids, (hipStream_t)stream);
+  return hip_check("sample");
 }
 
 // ---------------------------------------------------------------- greedy generate
@@ -1035,6 +1054,7 @@ struct llama_stack {
   int vocab;
   const void* fnorm;
   llama_linear head;
+  Sampling smp;     // u_off is filled in by generate
 };
 
 extern "C" llama_status llama_stack_create(llama_block* const* blocks, int32_t n_layers, const void* embedding,
@@ -1083,6 +1103,16 @@ static StLayout stack_layout(const llama_stack* st, int max_prompt, int max_seq)
   return L;
 }
 
+extern "C" llama_status llama_stack_set_sampling(llama_stack* st, float temperature, float top_p, const float* u) {
+  if (!st) return fail(LLAMA_ERR_INVALID_ARG, "stack must be non-NULL");
+  if (temperature > 0.f && !u) return fail(LLAMA_ERR_INVALID_ARG, "temperature > 0 needs the draws u");
+  if (!(top_p > 0.f && top_p <= 1.f)) return fail(LLAMA_ERR_INVALID_ARG, "top_p must lie in (0, 1]");
+  st->smp.temperature = temperature;
+  st->smp.top_p = top_p;
+  st->smp.u = temperature > 0.f ? u : nullptr;
+  return LLAMA_OK;
+}
+
 extern "C" size_t llama_stack_scratch_bytes(const llama_stack* st, int32_t max_prompt, int32_t max_seq) {
   if (!st || max_prompt <= 0 || max_seq <= 0) return 0;
   return stack_layout(st, max_prompt, max_seq).total;
@@ -1116,8 +1146,11 @@ extern "C" llama_status llama_stack_generate(llama_stack* st, llama_kvcache* cac
   const int D = c.dim, V = st->vocab;
   llama_status r;
   auto head = [&](const bf16_t* row) {
+    // (the draw of emitted id j is u[j]: the cursor counts the ids emitted so far)
+    Sampling smp = st->smp;
+    smp.u_off = cursor;
     return head_enqueue(&st->head, c.weight_format, c.group_size, LLAMA_BF16, st->fnorm, c.norm_eps, row, 1, D, V,
-                        hlog, cur, hs, L.head_bytes, s);
+                        hlog, cur, hs, L.head_bytes, s, smp);
   };
 
   launch_fill_i32(cursor, 1, 0, s);

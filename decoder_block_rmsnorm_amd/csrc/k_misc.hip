@@ -133,6 +133,125 @@ void launch_argmax(const float* logits, int rows, int vocab, int32_t* ids, hipSt
 }
 
 // ---------------------------------------------------------------------------
+// Sampled next id ("生成过程", MLX page: a multinomial draw from
+// softmax(logits / T) when T > 0; LLaMA.generate, page 二: limited to the
+// nucleus, the most probable tokens up to and including the first at which
+// their cumulative probability exceeds top_p).  One block per row, 256 threads.
+//   e_i = 2^((z_i - max) * log2(e) / T), recomputed by the same instructions in
+//   every pass (so every pass sees the same values; no scratch);
+//   nucleus: the kept tokens are e_i >= thr, thr = the largest e value whose
+//   tail mass (the sum of all e_j >= it) exceeds top_p * sum(e), found by
+//   bisection over the bit patterns of positive floats (ordered like their
+//   values); tokens tied with it are kept;
+//   draw: the first index, in vocabulary order, at which the cumulative kept
+//   mass exceeds u * (kept mass), u = u[*u_off or row].  Each thread sums one
+//   contiguous 1/256 of the row, one thread turns the 256 sums into prefixes
+//   in order, so the chunks' intervals [prefix, next prefix) tile [0, total)
+//   exactly and one chunk holds the crossing.
+// ---------------------------------------------------------------------------
+__device__ inline float block_reduce256(float v, bool is_max, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float w = __shfl_xor(v, o, 64);
+    v = is_max ? fmaxf(v, w) : v + w;
+  }
+  __syncthreads();   // red is reused by consecutive reductions
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return is_max ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) : (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ __launch_bounds__(256) void k_sample(const float* logits, int vocab, float temperature, float top_p,
+                                                const float* u, const int32_t* u_off, int32_t* ids) {
+  const float* z = logits + (size_t)blockIdx.x * vocab;
+  const int tid = threadIdx.x;
+  __shared__ float red[4];
+  __shared__ float pre[257];
+  __shared__ int found, last_kept;
+  float m = -INFINITY;
+  for (int i = tid; i < vocab; i += 256) m = fmaxf(m, z[i]);
+  m = block_reduce256(m, true, red);
+  const float k2 = 1.4426950408889634f / temperature;
+  auto e_of = [&](int i) { return __builtin_amdgcn_exp2f((z[i] - m) * k2); };
+  float thr = 0.f;
+  if (top_p < 1.f) {
+    float tot = 0.f;
+    for (int i = tid; i < vocab; i += 256) tot += e_of(i);
+    const float target = top_p * block_reduce256(tot, false, red);
+    // invariant: tail(lo) > target >= tail(hi); e <= 1, so tail(1 + ulp) = 0
+    uint32_t lo = 0u, hi = 0x3f800001u;
+    while (hi - lo > 1u) {
+      const uint32_t mid = lo + ((hi - lo) >> 1);
+      const float t = __uint_as_float(mid);
+      float sm = 0.f;
+      for (int i = tid; i < vocab; i += 256) {
+        const float e = e_of(i);
+        if (e >= t) sm += e;
+      }
+      if (block_reduce256(sm, false, red) > target) lo = mid;
+      else hi = mid;
+    }
+    thr = __uint_as_float(lo);
+  }
+  const int C = (vocab + 255) / 256;
+  const int i0 = min(vocab, tid * C), i1 = min(vocab, i0 + C);
+  float cs = 0.f;
+  int lk = -1;
+  for (int i = i0; i < i1; ++i) {
+    const float e = e_of(i);
+    if (e >= thr) {
+      cs += e;
+      lk = i;
+    }
+  }
+  pre[tid] = cs;
+  if (tid == 0) {
+    found = 0x7fffffff;
+    last_kept = -1;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float run = 0.f;
+    for (int t = 0; t < 256; ++t) {
+      const float c = pre[t];
+      pre[t] = run;
+      run = run + c;
+    }
+    pre[256] = run;
+  }
+  atomicMax(&last_kept, lk);
+  __syncthreads();
+  const float target = u[u_off ? *u_off : blockIdx.x] * pre[256];
+  if (pre[tid] <= target && target < pre[tid + 1]) {
+    // the chunk holding the crossing (its own running sum may round short of
+    // it: then its last kept token)
+    float run = pre[tid];
+    int pick = lk;
+    for (int i = i0; i < i1; ++i) {
+      const float e = e_of(i);
+      if (e >= thr) {
+        run += e;
+        if (run > target) {
+          pick = i;
+          break;
+        }
+      }
+    }
+    atomicMin(&found, pick);
+  }
+  __syncthreads();
+  // (u * total rounded up to total: the last kept token)
+  if (tid == 0) ids[blockIdx.x] = found != 0x7fffffff ? found : max(last_kept, 0);
+}
+
+void launch_sample(const float* logits, int rows, int vocab, float temperature, float top_p, const float* u,
+                   const int32_t* u_off, int32_t* ids, hipStream_t s) {
+  if (rows <= 0) return;
+  if (temperature <= 0.f) return launch_argmax(logits, rows, vocab, ids, s);
+  hipLaunchKernelGGL(k_sample, dim3(rows), dim3(256), 0, s, logits, vocab, temperature, top_p, u, u_off, ids);
+}
+
+// ---------------------------------------------------------------------------
 // Paged cache <-> canonical [n, G, d] copies (cache pre-fill and read-back).
 // ---------------------------------------------------------------------------
 template <typename T>

@@ -65,6 +65,10 @@ template <typename T>
 void launch_embed(const T* table, int vocab, int D, const int32_t* ids, int n, T* out, hipStream_t s);
 // ids[r] = first index of the max of logits[r, :vocab]
 void launch_argmax(const float* logits, int rows, int vocab, int32_t* ids, hipStream_t s);
+// ids[r] = sampled id of row r (temperature <= 0: argmax), draw u[*u_off] when
+// u_off is given (one row), else u[r]
+void launch_sample(const float* logits, int rows, int vocab, float temperature, float top_p, const float* u,
+                   const int32_t* u_off, int32_t* ids, hipStream_t s);
 // canonical [n, G, d] <-> paged
 template <typename T>
 void launch_kv_write(KVView kv, int seq, int pos0, int n, const T* k, const T* v, hipStream_t s);

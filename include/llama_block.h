@@ -234,6 +234,21 @@ llama_status llama_lm_head_argmax(const llama_linear* head, int32_t weight_forma
                                   int32_t batch, int32_t dim, int32_t vocab, float* logits_dev,
                                   int32_t* ids_dev, void* scratch, size_t scratch_bytes, void* stream);
 
+/* Sampled next id ("生成过程", MLX page: greedy argmax at temperature 0, a
+ * multinomial draw from softmax(logits / temperature) above it; LLaMA.generate,
+ * page 二: the draw limited to the nucleus, the most probable tokens up to and
+ * including the first at which their cumulative probability exceeds top_p).
+ * logits_dev: fp32 [batch, vocab]; u_dev: fp32 [batch] draws in [0, 1) (the
+ * caller's random numbers; unused and may be NULL at temperature <= 0);
+ * ids_dev: int32 [batch].  Row b takes the first index, in vocabulary order, at
+ * which the cumulative kept probability exceeds u_dev[b] times the kept
+ * probability; tokens tied with the last nucleus token are kept; top_p = 1 keeps
+ * every token.  Temperature <= 0: the argmax, lowest index on ties.
+ * Errors: LLAMA_ERR_INVALID_ARG for NULL pointers, batch or vocab <= 0, or top_p
+ * outside (0, 1]. */
+llama_status llama_sample(const float* logits_dev, int32_t batch, int32_t vocab, float temperature, float top_p,
+                          const float* u_dev, int32_t* ids_dev, void* stream);
+
 /* ------------------------------------------------------- greedy generate */
 
 /* A stack of n_layers blocks (same config) + embedding + final norm + head,
@@ -246,6 +261,12 @@ llama_status llama_stack_create(llama_block* const* blocks, int32_t n_layers, co
                                 int32_t vocab, const void* final_norm, const llama_linear* output,
                                 llama_stack** out);
 void llama_stack_destroy(llama_stack* st);
+
+/* Next-id rule of later llama_stack_generate calls: temperature <= 0 (the
+ * default) = greedy; above 0, the draw of llama_sample with u_dev[j] for the
+ * j-th emitted id (j = 0 from the prompt pass), u_dev: fp32 [n_steps + 1] on the
+ * device, read during generate (kept, not owned).  Errors as llama_sample. */
+llama_status llama_stack_set_sampling(llama_stack* st, float temperature, float top_p, const float* u_dev);
 
 /* Scratch for llama_stack_generate with a prompt of up to max_prompt tokens. */
 size_t llama_stack_scratch_bytes(const llama_stack* st, int32_t max_prompt, int32_t max_seq);

@@ -118,6 +118,18 @@ def test_null_handles_and_head_validation():
     assert "stack" in L.llama_last_error()
 
 
+def test_sample_argument_validation():
+    # every check happens before any device work (the pointers are never used)
+    for args in [(1, 1, 10, 1.0, 1.5, 1, 1), (1, 1, 10, 1.0, 0.0, 1, 1), (1, 0, 10, 1.0, 0.9, 1, 1),
+                 (1, 1, 0, 1.0, 0.9, 1, 1), (1, 1, 10, 1.0, 0.9, None, 1), (None, 1, 10, 0.0, 1.0, None, 1)]:
+        with pytest.raises(L.LlamaError) as e:
+            L.llama_sample(*args, 0)
+        assert e.value.status == L.LLAMA_ERR_INVALID_ARG
+    with pytest.raises(L.LlamaError) as e:
+        L.llama_stack_set_sampling(None, 1.0, 0.9, 1)
+    assert e.value.status == L.LLAMA_ERR_INVALID_ARG
+
+
 def test_product_path_does_not_import_the_oracle():
     import decoder_block_rmsnorm_amd
     pkg = os.path.dirname(decoder_block_rmsnorm_amd.__file__)
