@@ -99,6 +99,42 @@ def test_small_q4_stack_generate_graph_equals_eager_and_oracle():
     assert n >= 1
 
 
+def test_small_q4_stack_sampled_generation():
+    """Sampled generate loop (temperature 0.8, nucleus 0.9; the draws u are
+    seeded inputs): graph replay equals eager launches, every emitted id is
+    llama_sample's choice on that step's logits with the same draw, and one the
+    oracle's sampler allows on those logits (within a 1e-5 band of the draw)."""
+    s = W.BlockShape(dim=512, n_heads=4, n_kv_heads=4, ffn_dim=1536, dtype="bf16", weight_format="q4",
+                     traditional=True)
+    wl = W.Workload("small_q4_stack", s, "stack", batch=1, seq_len=40, decode_steps=12, n_layers=2, vocab=1000,
+                    seed=31)
+    _flush("case: small 4-bit stack, sampled generation T=0.8 top_p=0.9")
+    max_seq = 64
+    s, ids, layers_np, head, blocks, stack, keep = _build(wl, max_seq)
+    T, top_p = 0.8, 0.9
+    u = torch.from_numpy(W.Rng(41).g.random(13).astype(np.float32)).cuda()
+    stack.set_sampling(T, top_p, u)
+    g_ids, g_log, _ = _generate(stack, s, wl, ids, 12, True, max_seq)
+    e_ids, e_log, _ = _generate(stack, s, wl, ids, 12, False, max_seq)
+    assert np.array_equal(g_ids, e_ids) and np.array_equal(g_log, e_log), "graph replay differs from eager launches"
+    lg = torch.from_numpy(g_log).cuda()
+    one = torch.empty(13, dtype=torch.int32, device="cuda")
+    L.llama_sample(lg, 13, wl.vocab, T, top_p, u, one)
+    torch.cuda.synchronize()
+    assert np.array_equal(one.cpu().numpy(), g_ids)
+    uh = u.cpu().numpy()
+    greedy_steps = 0
+    for t in range(13):
+        z = g_log[t].astype(np.float64)
+        allowed = {ref.sample(z, T, top_p, min(float(uh[t]) * f, 1 - 1e-12)) for f in (1 - 1e-5, 1.0, 1 + 1e-5)}
+        assert int(g_ids[t]) in allowed
+        greedy_steps += int(g_ids[t]) == ref.argmax_first(z)
+    _flush(f"  {greedy_steps} of 13 sampled ids were also the argmax")
+    stack.set_sampling(0.0, 1.0, None)          # back to greedy
+    r_ids, r_log, _ = _generate(stack, s, wl, ids, 12, True, max_seq)
+    assert all(r_ids[t] == ref.argmax_first(r_log[t]) for t in range(13))
+
+
 def test_q4_13b_width_two_layer_stack_prompt512_vs_oracle():
     """Full-width layers of the 40-layer 13B 4-bit stack (dim 5120, 40 heads, ffn
     13824, vocab 32000, a 512-token prompt) at a depth the oracle can run.
