@@ -249,6 +249,15 @@ def bench_stack(wl, reps):
     tn = min(run(n) for _ in range(reps))
     step_ms = (tn - t1) / (n - 1)
     prompt_ms = t1 - step_ms
+    # the same loop with a sampled next id (temperature 0.8, nucleus 0.9, seeded
+    # draws) in place of the argmax
+    u = torch.from_numpy(W.Rng(wl.seed + 1).g.random(n + 1).astype(np.float32)).cuda()
+    stack.set_sampling(0.8, 0.9, u)
+    run(1)
+    s1 = min(run(1) for _ in range(reps))
+    sn = min(run(n) for _ in range(reps))
+    sampled_step_ms = (sn - s1) / (n - 1)
+    stack.set_sampling(0.0, 1.0, None)
     # bytes of one step at the mean cache length: every weight and cached K/V
     # byte once, plus the output head (4-bit) and the logits
     mean_cached = P + n / 2
@@ -260,6 +269,7 @@ def bench_stack(wl, reps):
             "prompt_tflops": round(flops / (prompt_ms * 1e-3) / 1e12, 1),
             "decode_steps": n, "decode_us_per_step": round(step_ms * 1e3, 1),
             "decode_tokens_per_s": round(1.0 / (step_ms * 1e-3), 1), "bytes_per_step": step_bytes,
+            "sampled_decode_us_per_step": round(sampled_step_ms * 1e3, 1),
             "hbm_frac_step": round(step_bytes / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 

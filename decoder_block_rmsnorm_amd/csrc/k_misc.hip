@@ -149,7 +149,10 @@ void launch_argmax(const float* logits, int rows, int vocab, int32_t* ids, hipSt
 //   in order, so the chunks' intervals [prefix, next prefix) tile [0, total)
 //   exactly and one chunk holds the crossing.
 // ---------------------------------------------------------------------------
-__device__ inline float block_reduce256(float v, bool is_max, float* red) {
+constexpr int kSampleThreads = 1024;
+constexpr int kSampleLds = 36864;   // e values kept in LDS (144 KB) up to this vocabulary
+
+__device__ inline float block_reduce_s(float v, bool is_max, float* red) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float w = __shfl_xor(v, o, 64);
@@ -158,42 +161,55 @@ __device__ inline float block_reduce256(float v, bool is_max, float* red) {
   __syncthreads();   // red is reused by consecutive reductions
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  return is_max ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) : (red[0] + red[1]) + (red[2] + red[3]);
+  float r = red[0];
+  for (int w = 1; w < kSampleThreads / 64; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+  return r;
 }
 
-__global__ __launch_bounds__(256) void k_sample(const float* logits, int vocab, float temperature, float top_p,
-                                                const float* u, const int32_t* u_off, int32_t* ids) {
+// CACHE: e_i computed once into LDS (vocab <= kSampleLds), else recomputed
+// by the same instructions in every pass
+template <bool CACHE>
+__global__ __launch_bounds__(kSampleThreads) void k_sample(const float* logits, int vocab, float temperature,
+                                                           float top_p, const float* u, const int32_t* u_off,
+                                                           int32_t* ids) {
+  extern __shared__ float e_s[];
   const float* z = logits + (size_t)blockIdx.x * vocab;
   const int tid = threadIdx.x;
-  __shared__ float red[4];
-  __shared__ float pre[257];
+  constexpr int NT = kSampleThreads;
+  __shared__ float red[NT / 64];
+  __shared__ float pre[NT + 1];
   __shared__ int found, last_kept;
   float m = -INFINITY;
-  for (int i = tid; i < vocab; i += 256) m = fmaxf(m, z[i]);
-  m = block_reduce256(m, true, red);
+  for (int i = tid; i < vocab; i += NT) m = fmaxf(m, z[i]);
+  m = block_reduce_s(m, true, red);
   const float k2 = 1.4426950408889634f / temperature;
-  auto e_of = [&](int i) { return __builtin_amdgcn_exp2f((z[i] - m) * k2); };
+  auto e_calc = [&](int i) { return __builtin_amdgcn_exp2f((z[i] - m) * k2); };
+  if constexpr (CACHE) {
+    for (int i = tid; i < vocab; i += NT) e_s[i] = e_calc(i);
+    __syncthreads();
+  }
+  auto e_of = [&](int i) { return CACHE ? e_s[i] : e_calc(i); };
   float thr = 0.f;
   if (top_p < 1.f) {
     float tot = 0.f;
-    for (int i = tid; i < vocab; i += 256) tot += e_of(i);
-    const float target = top_p * block_reduce256(tot, false, red);
+    for (int i = tid; i < vocab; i += NT) tot += e_of(i);
+    const float target = top_p * block_reduce_s(tot, false, red);
     // invariant: tail(lo) > target >= tail(hi); e <= 1, so tail(1 + ulp) = 0
     uint32_t lo = 0u, hi = 0x3f800001u;
     while (hi - lo > 1u) {
       const uint32_t mid = lo + ((hi - lo) >> 1);
       const float t = __uint_as_float(mid);
       float sm = 0.f;
-      for (int i = tid; i < vocab; i += 256) {
+      for (int i = tid; i < vocab; i += NT) {
         const float e = e_of(i);
         if (e >= t) sm += e;
       }
-      if (block_reduce256(sm, false, red) > target) lo = mid;
+      if (block_reduce_s(sm, false, red) > target) lo = mid;
       else hi = mid;
     }
     thr = __uint_as_float(lo);
   }
-  const int C = (vocab + 255) / 256;
+  const int C = (vocab + NT - 1) / NT;
   const int i0 = min(vocab, tid * C), i1 = min(vocab, i0 + C);
   float cs = 0.f;
   int lk = -1;
@@ -210,18 +226,32 @@ __global__ __launch_bounds__(256) void k_sample(const float* logits, int vocab, 
     last_kept = -1;
   }
   __syncthreads();
-  if (tid == 0) {
-    float run = 0.f;
-    for (int t = 0; t < 256; ++t) {
-      const float c = pre[t];
-      pre[t] = run;
+  // prefixes in chunk order by the first wavefront: lane l sums chunks
+  // 16 l .. 16 l + 15, the 64 lane sums are chained in order, then each lane
+  // writes its 16 prefixes from its start, one chunk sum at a time.  (Where a
+  // lane's last prefix and the next lane's start differ by rounding, two
+  // chunks' intervals may overlap but never leave a gap; the lower index wins.)
+  if (tid < 64) {
+    constexpr int PER = NT / 64;
+    float ls = 0.f;
+    for (int j = 0; j < PER; ++j) ls = ls + pre[tid * PER + j];
+    float base = 0.f;
+    for (int l = 0; l < 64; ++l) {
+      const float v = __shfl(ls, l, 64);
+      if (l == tid) ls = base;   // this lane's starting prefix
+      base = base + v;
+    }
+    float run = ls;
+    for (int j = 0; j < PER; ++j) {
+      const float c = pre[tid * PER + j];
+      pre[tid * PER + j] = run;
       run = run + c;
     }
-    pre[256] = run;
+    if (tid == 63) pre[NT] = run;
   }
   atomicMax(&last_kept, lk);
   __syncthreads();
-  const float target = u[u_off ? *u_off : blockIdx.x] * pre[256];
+  const float target = u[u_off ? *u_off : blockIdx.x] * pre[NT];
   if (pre[tid] <= target && target < pre[tid + 1]) {
     // the chunk holding the crossing (its own running sum may round short of
     // it: then its last kept token)
@@ -248,7 +278,19 @@ void launch_sample(const float* logits, int rows, int vocab, float temperature, 
                    const int32_t* u_off, int32_t* ids, hipStream_t s) {
   if (rows <= 0) return;
   if (temperature <= 0.f) return launch_argmax(logits, rows, vocab, ids, s);
-  hipLaunchKernelGGL(k_sample, dim3(rows), dim3(256), 0, s, logits, vocab, temperature, top_p, u, u_off, ids);
+  if (vocab <= kSampleLds) {
+    static bool attr = false;
+    const size_t lds = (size_t)kSampleLds * sizeof(float);
+    if (!attr) {
+      (void)hipFuncSetAttribute((const void*)k_sample<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      attr = true;
+    }
+    hipLaunchKernelGGL(k_sample<true>, dim3(rows), dim3(kSampleThreads), (size_t)vocab * sizeof(float), s, logits,
+                       vocab, temperature, top_p, u, u_off, ids);
+  } else {
+    hipLaunchKernelGGL(k_sample<false>, dim3(rows), dim3(kSampleThreads), 0, s, logits, vocab, temperature, top_p,
+                       u, u_off, ids);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -41,7 +41,7 @@ def _oracle_choices(z, temperature, top_p, u):
     return out
 
 
-@pytest.mark.parametrize("V", [32000, 1000, 97])
+@pytest.mark.parametrize("V", [32000, 40000, 1000, 97])
 @pytest.mark.parametrize("temperature,top_p", [(1.0, 1.0), (0.7, 0.9), (1.5, 0.5), (0.8, 0.05)])
 def test_sample_matches_oracle(V, temperature, top_p):
     rng = W.Rng(31)
