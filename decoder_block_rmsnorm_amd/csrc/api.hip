@@ -82,7 +82,6 @@ static llama_status check_config(const llama_block_config* c, Dims* o) {
   if (d.bf16) {
     if (d.d != 128) return fail(LLAMA_ERR_UNSUPPORTED, "bf16 path supports head_dim 128 only (got %d)", d.d);
     if (d.D % 64 || d.F % 64) return fail(LLAMA_ERR_UNSUPPORTED, "bf16 path needs dim and ffn_dim multiples of 64");
-    if (d.n_rep > 16) return fail(LLAMA_ERR_UNSUPPORTED, "bf16 decode supports n_heads / n_kv_heads <= 16");
     d.IB = 32;
   } else {
     if (d.d > 128) return fail(LLAMA_ERR_UNSUPPORTED, "fp32 path supports head_dim <= 128 (got %d)", d.d);
@@ -484,7 +483,8 @@ static const int kStackSplit = 64; // keys per chunk in the stack's single-seque
 // (measured: 70B-shaped GQA decode at batch 64, splits of 1024 keys).
 static int attn_split_len(const Dims& d, int B, int maxlen) {
   if (d.n_rep == 1) return kSplitLen;
-  const int ns = std::max(1, 2048 / (B * d.G));
+  // (query heads ride 16 to a wavefront: n_rep > 16 gives several per chunk)
+  const int ns = std::max(1, 2048 / (B * d.G * ((d.n_rep + 15) / 16)));
   const int sl = (maxlen + ns - 1) / ns;
   return std::max(kSplitLen, (sl + 63) / 64 * 64);
 }

@@ -13,8 +13,9 @@
 //                          "Transformer 块的内部结构" of the reading-notes page).
 //  * k_attn_decode_bf16  : split-K decode: each wavefront streams a 256-key
 //                          chunk of one (sequence, kv head) straight from the
-//                          pages with 128-bit loads, serving all n_rep query heads
-//                          of the group with 16x16x32 MFMA; k_attn_merge combines
+//                          pages with 128-bit loads, serving up to 16 query heads
+//                          of the group with 16x16x32 MFMA (more query heads: one
+//                          wavefront per 16 of them); k_attn_merge combines
 //                          the chunks with a log-sum-exp merge in a fixed order.
 #include "kernels.hpp"
 
@@ -292,7 +293,7 @@ void launch_attn_prefill_bf16(const bf16_t* q, KVView kv, int B, int L, int H, i
 // bf16 split-K decode, head_dim 128
 // ===========================================================================
 // One wavefront = one (sequence b, kv head g, key chunk c of split_len keys).
-// Query columns: the n_rep (<= 16) query heads of group g, padded to 16.
+// Query columns: up to 16 query heads of kv head g (a virtual group), padded to 16.
 // S^T (16 keys x 16 q) = K (16 x 32 d) Q^T via 16x16x32 MFMA, 4 d-chunks;
 // O^T (16 d x 16 q) += V^T (16 d x 32 keys) P^T, 8 d-subtiles.
 // Partials: part_o [B][H][n_splits][128], part_ml [B][H][n_splits][2] (max, sum).
@@ -316,26 +317,29 @@ __global__ __launch_bounds__(BM ? 512 : 256) __attribute__((amdgpu_waves_per_eu(
   const int l16 = lane & 15, hg = lane >> 4;
   // wave-uniform indices in scalar registers: the lens and block-table reads are
   // scalar loads, counted apart from the vector loads in flight
-  int c, g, b;
+  // a kv head's n_rep query heads go in virtual groups of at most 16 (the MFMA
+  // rows), each read against the same keys: nv per kv head, VG in all
+  const int n_rep = H / G, nv = (n_rep + 15) >> 4, VG = G * nv;
+  int c, vg, b;
   if constexpr (BM) {
     c = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    g = __builtin_amdgcn_readfirstlane(blockIdx.x % G);
-    b = __builtin_amdgcn_readfirstlane(blockIdx.x / G);
+    vg = __builtin_amdgcn_readfirstlane(blockIdx.x % VG);
+    b = __builtin_amdgcn_readfirstlane(blockIdx.x / VG);
   } else {
     const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
-    const int total = B * G * n_splits;
+    const int total = B * VG * n_splits;
     if (wid >= total) return;
     c = wid % n_splits;
-    g = (wid / n_splits) % G;
-    b = wid / (n_splits * G);
+    vg = (wid / n_splits) % VG;
+    b = wid / (n_splits * VG);
   }
-  const int n_rep = H / G;
+  const int g = vg / nv, h0 = (vg % nv) * 16, nr = min(16, n_rep - h0);
   const int pos = kv.lens[b];               // the new token's position; keys 0..pos
   const int nkeys = pos + 1;
   const int k_begin = c * split_len;
   const int k_end = min(nkeys, k_begin + split_len);
-  const bool qvalid = l16 < n_rep;
-  const int hq = g * n_rep + (qvalid ? l16 : 0);
+  const bool qvalid = l16 < nr;
+  const int hq = g * n_rep + h0 + (qvalid ? l16 : 0);
 
   // Q^T fragments: lane holds Q[q = l16][d = 32*kc + 8*hg .. +7]
   bf16x8 qf[4];
@@ -448,9 +452,9 @@ __global__ __launch_bounds__(BM ? 512 : 256) __attribute__((amdgpu_waves_per_eu(
       if (hg == 0) sml[c][l16] = make_float2(m_run, l_run);
     }
     __syncthreads();
-    // wavefront w merges query heads w, w + 8, ... of the group: o = sum_c
-    // e^(m_c - M) O_c / sum_c e^(m_c - M) l_c in split order
-    for (int r = c; r < n_rep; r += 8) {
+    // wavefront w merges query heads w, w + 8, ... of the virtual group: o =
+    // sum_c e^(m_c - M) O_c / sum_c e^(m_c - M) l_c in split order
+    for (int r = c; r < nr; r += 8) {
       float M = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 8; ++j) M = fmaxf(M, sml[j][r].x);
@@ -463,7 +467,7 @@ __global__ __launch_bounds__(BM ? 512 : 256) __attribute__((amdgpu_waves_per_eu(
         o0 += w * so[j][r][lane];
         o1 += w * so[j][r][lane + 64];
       }
-      bf16_t* orow = out + ((size_t)b * H + g * n_rep + r) * 128;
+      bf16_t* orow = out + ((size_t)b * H + g * n_rep + h0 + r) * 128;
       orow[lane] = f32_to_bf16(o0 / den);
       orow[lane + 64] = f32_to_bf16(o1 / den);
     }
@@ -540,16 +544,17 @@ void launch_attn_decode_bf16(const bf16_t* q, KVView kv, int B, int H, int G, in
   if (B <= 0) return;
   // the keys the splits cover (at least every cached key)
   const long keys = (long)n_splits * split_len;
-  if (B * G <= 128 && keys <= 2048) {
+  const int VG = G * ((H / G + 15) / 16);   // virtual groups of at most 16 query heads
+  if (B * VG <= 128 && keys <= 2048) {
     // few (b, g) pairs and a short cache: one block each, eight key ranges of
     // whole 64-key steps, merged in the block
     const int sl8 = (int)(((keys + 7) / 8 + 63) / 64 * 64);
-    hipExtLaunchKernelGGL(k_attn_decode_bf16<true>, dim3(B * G), dim3(512), 0, s, g_clock.start, g_clock.stop, 0, q,
+    hipExtLaunchKernelGGL(k_attn_decode_bf16<true>, dim3(B * VG), dim3(512), 0, s, g_clock.start, g_clock.stop, 0, q,
                           kv, B, H, G, 8, sl8, part_o, part_ml, out);
     g_clock = LaunchClock{};
     return;
   }
-  int waves = B * G * n_splits;
+  int waves = B * VG * n_splits;
   hipExtLaunchKernelGGL(k_attn_decode_bf16<false>, dim3((waves + 3) / 4), dim3(256), 0, s, g_clock.start, nullptr, 0, q, kv, B, H, G, n_splits,
                      split_len, part_o, part_ml, nullptr);
   int bh = B * H;

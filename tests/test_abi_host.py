@@ -57,7 +57,6 @@ def cfg(**kw):
     (dict(weight_format=L.LLAMA_W_Q4, act_dtype=L.LLAMA_F32, dim=256, n_heads=4, n_kv_heads=4, ffn_dim=688),
      L.LLAMA_ERR_UNSUPPORTED),
     (dict(weight_format=L.LLAMA_W_Q4, group_size=32), L.LLAMA_ERR_UNSUPPORTED),
-    (dict(n_heads=64, n_kv_heads=2, dim=8192), L.LLAMA_ERR_UNSUPPORTED),    # n_rep 32 > 16
 ])
 def test_invalid_configs_rejected_on_host(kw, status):
     c = cfg(**kw)

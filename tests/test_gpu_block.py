@@ -136,6 +136,18 @@ def test_bf16_prefill_mha_several_tiles_ragged(traditional):
     G.check("bf16", G.thost(v), r["v_new"][1], "cache V")
 
 
+def test_bf16_prefill_mqa():
+    s = MQA
+    rng = W.Rng(19)
+    x = rng.normal((2, 150, s.dim), 1.0, "bf16")
+    w = W.draw_block_weights(s, rng)
+    _flush("case: bf16 MQA prefill B=2 L=150")
+    blk, cache, sc, y = _run_prefill(s, w, x)
+    r = _oracle(s, w, x)
+    G.check("bf16", y, np.stack(r["y"]), "y")
+    _check_branches(s, blk, sc, r, y, 2, 150)
+
+
 def test_bf16_prefill_gqa_with_cached_prefix():
     s = SMALL_GQA
     rng = W.Rng(12)
@@ -162,14 +174,24 @@ def _long_split_lens():
     return [int(v) for v in r.g.integers(1, 2300, size=59)] + [0, 1, 319, 320, 2301]
 
 
+# multi-query attention: 32 query heads share one kv head, two wavefronts (or
+# in-block groups) of 16 query heads each read it
+MQA = W.BlockShape(dim=4096, n_heads=32, n_kv_heads=1, ffn_dim=512, dtype="bf16")
+
+
 # "empty_cache": sequences at position 0 (the token attends to itself only)
-# next to short ones, on the path that merges key ranges inside one block
-@pytest.mark.parametrize("shape", ["mha", "gqa", "gqa_long_splits", "empty_cache"])
+# next to short ones, on the path that merges key ranges inside one block;
+# "mqa_short" takes that path too, "mqa_long" (over 2048 keys) the split one
+@pytest.mark.parametrize("shape", ["mha", "gqa", "gqa_long_splits", "empty_cache", "mqa_short", "mqa_long"])
 def test_bf16_decode_ragged_lengths(shape):
     if shape == "gqa_long_splits":
         s, lens = WIDE_GQA, _long_split_lens()
     elif shape == "empty_cache":
         s, lens = SMALL_GQA, [0, 5, 0, 63]
+    elif shape == "mqa_short":
+        s, lens = MQA, [0, 77, 500]
+    elif shape == "mqa_long":
+        s, lens = dataclasses.replace(MQA, traditional=True), [2300, 5, 1000]
     else:
         s = dataclasses.replace(SMALL_MHA if shape == "mha" else SMALL_GQA, traditional=(shape == "mha"))
         lens = [300, 1, 64, 255, 257]
