@@ -258,6 +258,17 @@ def bench_stack(wl, reps):
     sn = min(run(n) for _ in range(reps))
     sampled_step_ms = (sn - s1) / (n - 1)
     stack.set_sampling(0.0, 1.0, None)
+    # the loop without the cache's reuse (every id re-runs the prompt pass over
+    # the sequence so far): nr ids, timed once
+    nr = 16
+    sc_r = torch.empty(stack.scratch_bytes(P + nr, max_seq), dtype=torch.uint8, device="cuda")
+    cache = G.make_cache(s, wl.n_layers, 1, max_seq)
+    torch.cuda.synchronize()
+    t0r = time.perf_counter()
+    stack.generate_recompute(cache, prompt, nr, out_ids, None, sc_r, stream=st)
+    torch.cuda.synchronize()
+    recompute_ms = (time.perf_counter() - t0r) * 1e3 / (nr + 1)
+    del cache, sc_r
     # bytes of one step at the mean cache length: every weight and cached K/V
     # byte once, plus the output head (4-bit) and the logits
     mean_cached = P + n / 2
@@ -270,6 +281,7 @@ def bench_stack(wl, reps):
             "decode_steps": n, "decode_us_per_step": round(step_ms * 1e3, 1),
             "decode_tokens_per_s": round(1.0 / (step_ms * 1e-3), 1), "bytes_per_step": step_bytes,
             "sampled_decode_us_per_step": round(sampled_step_ms * 1e3, 1),
+            "recompute_ms_per_id": round(recompute_ms, 3), "recompute_ids": nr + 1,
             "hbm_frac_step": round(step_bytes / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 

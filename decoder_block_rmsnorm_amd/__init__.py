@@ -197,6 +197,12 @@ def llama_stack_generate(st, cache, prompt, prompt_len, n_steps, ids_out, logits
                                       _ptr(scratch), scratch_bytes, use_graph, _stream(stream)))
 
 
+def llama_stack_generate_recompute(st, cache, prompt, prompt_len, n_steps, ids_out, logits_out, scratch,
+                                   scratch_bytes, stream=None) -> None:
+    _check(lib().llama_stack_generate_recompute(st, cache, _ptr(prompt), prompt_len, n_steps, _ptr(ids_out),
+                                                _ptr(logits_out), _ptr(scratch), scratch_bytes, _stream(stream)))
+
+
 def llama_last_error() -> str:
     return (lib().llama_last_error() or b"").decode()
 
@@ -328,6 +334,13 @@ class Stack:
                  stream=None) -> None:
         llama_stack_generate(self.handle, cache.handle, prompt, prompt.numel(), n_steps, ids_out, logits_out,
                              scratch, scratch.numel(), int(bool(use_graph)), stream)
+
+    def generate_recompute(self, cache: KVCache, prompt, n_steps: int, ids_out, logits_out, scratch,
+                           stream=None) -> None:
+        """No cache reuse: every id re-runs the prompt pass over the sequence so
+        far (scratch sized by scratch_bytes(prompt + n_steps, max_seq))."""
+        llama_stack_generate_recompute(self.handle, cache.handle, prompt, prompt.numel(), n_steps, ids_out,
+                                       logits_out, scratch, scratch.numel(), stream)
 
     def __del__(self):
         h = getattr(self, "handle", None)

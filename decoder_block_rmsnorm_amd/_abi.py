@@ -71,6 +71,7 @@ SIGNATURES = {
     "llama_stack_set_sampling": (I32, [P, F32, F32, P]),
     "llama_stack_scratch_bytes": (SZ, [P, I32, I32]),
     "llama_stack_generate": (I32, [P, P, P, I32, I32, P, P, P, SZ, I32, P]),
+    "llama_stack_generate_recompute": (I32, [P, P, P, I32, I32, P, P, P, SZ, P]),
     "llama_last_error": (C.c_char_p, []),
 }
 

@@ -1084,7 +1084,7 @@ extern "C" llama_status llama_stack_create(llama_block* const* blocks, int32_t n
 extern "C" void llama_stack_destroy(llama_stack* st) { delete st; }
 
 struct StLayout {
-  size_t x, blk, head, cur, cursor, total, blk_bytes, head_bytes;
+  size_t x, blk, head, cur, cursor, seq, total, blk_bytes, head_bytes;
 };
 static StLayout stack_layout(const llama_stack* st, int max_prompt, int max_seq) {
   const llama_block_config& c = st->blocks[0]->cfg;
@@ -1099,6 +1099,8 @@ static StLayout stack_layout(const llama_stack* st, int max_prompt, int max_seq)
   L.head = off; off = align256(off + L.head_bytes);
   L.cur = off; off = align256(off + 4);
   L.cursor = off; off = align256(off + 4);
+  // the growing sequence of the recompute loop: up to max_prompt ids
+  L.seq = off; off = align256(off + ((size_t)max_prompt + 1) * 4);
   L.total = off;
   return L;
 }
@@ -1197,5 +1199,60 @@ extern "C" llama_status llama_stack_generate(llama_stack* st, llama_kvcache* cac
   }
   HIP_TRY(hipStreamSynchronize(s), "generate");
   for (int l = 0; l < NL; ++l) cache->lens_host[(size_t)l * cache->cfg.max_batch] = P + n_steps;
+  return LLAMA_OK;
+}
+
+// The loop without the cache's reuse (LLaMA.generate on page 二 runs the model
+// over the whole sequence for every new token; the reading-notes page times
+// generation with and without the KV cache, "流处理与 KV Cache"): each emitted
+// id re-runs the prompt pass over the prompt and the ids so far, from an empty
+// cache; the ids stay on the device.
+extern "C" llama_status llama_stack_generate_recompute(llama_stack* st, llama_kvcache* cache, const int32_t* prompt,
+                                                       int32_t P, int32_t n_steps, int32_t* ids_out,
+                                                       float* logits_out, void* scratch, size_t sbytes,
+                                                       void* stream) {
+  if (!st || !cache || !prompt || !ids_out || !scratch)
+    return fail(LLAMA_ERR_INVALID_ARG, "stack, cache, prompt, ids_out and scratch must be non-NULL");
+  if (P <= 0 || n_steps < 0) return fail(LLAMA_ERR_INVALID_ARG, "prompt_len must be > 0 and n_steps >= 0");
+  hipStream_t s = (hipStream_t)stream;
+  const int NL = (int)st->blocks.size();
+  const llama_block_config& c = st->blocks[0]->cfg;
+  if (cache->cfg.n_layers < NL) return fail(LLAMA_ERR_INVALID_ARG, "cache has %d layers, stack %d", cache->cfg.n_layers, NL);
+  const int cap = std::min(cache->cfg.max_seq, c.max_seq);
+  const int Pmax = P + n_steps;
+  if ((long)Pmax > cap) return fail(LLAMA_ERR_CAPACITY, "prompt + steps (%d) exceed capacity %d", Pmax, cap);
+  StLayout L = stack_layout(st, Pmax, cache->cfg.max_seq);
+  if (sbytes < L.total) return fail(LLAMA_ERR_CAPACITY, "stack scratch too small: %zu < %zu", sbytes, L.total);
+  char* sc = (char*)scratch;
+  bf16_t* x = (bf16_t*)(sc + L.x);
+  void* bs = sc + L.blk;
+  void* hs = sc + L.head;
+  int32_t* cur = (int32_t*)(sc + L.cur);
+  int32_t* cursor = (int32_t*)(sc + L.cursor);
+  int32_t* seq = (int32_t*)(sc + L.seq);
+  float* hlog = (float*)((char*)hs + head_layout(1, c.dim, st->vocab).logits);
+  const int D = c.dim, V = st->vocab, MB = cache->cfg.max_batch;
+  HIP_TRY(hipMemcpyAsync(seq, prompt, (size_t)P * 4, hipMemcpyDeviceToDevice, s), "recompute prompt copy");
+  launch_fill_i32(cursor, 1, 0, s);
+  for (int t = 0; t <= n_steps; ++t) {
+    const int n = P + t;
+    // an empty cache for sequence 0 in every layer
+    launch_fill_strided_i32(cache->lens, NL, MB, 0, s);
+    for (int l = 0; l < NL; ++l) cache->lens_host[(size_t)l * MB] = 0;
+    launch_embed<bf16_t>((const bf16_t*)st->emb, V, D, seq, n, x, s);
+    for (int l = 0; l < NL; ++l) {
+      llama_status r = enqueue(st->blocks[l], cache, l, x, x, 1, n, bs, L.blk_bytes, false, 0, 0, s);
+      if (r != LLAMA_OK) return r;
+    }
+    Sampling smp = st->smp;
+    smp.u_off = cursor;
+    llama_status r = head_enqueue(&st->head, c.weight_format, c.group_size, LLAMA_BF16, st->fnorm, c.norm_eps,
+                                  x + (size_t)(n - 1) * D, 1, D, V, hlog, cur, hs, L.head_bytes, s, smp);
+    if (r != LLAMA_OK) return r;
+    // emitted id t -> seq[P + t] (the next pass's last token) and logits row t
+    launch_emit(cur, seq + P, cursor, hlog, logits_out, V, s);
+  }
+  HIP_TRY(hipMemcpyAsync(ids_out, seq + P, (size_t)(n_steps + 1) * 4, hipMemcpyDeviceToDevice, s), "recompute ids");
+  HIP_TRY(hipStreamSynchronize(s), "generate (recompute)");
   return LLAMA_OK;
 }

@@ -547,6 +547,16 @@ __global__ __launch_bounds__(256) void k_emit(const int32_t* cur_id, int32_t* id
   if (threadIdx.x == 0) *cursor = c + 1;
 }
 
+// p[i * stride] = v for i < n (one lens entry per cache layer)
+__global__ __launch_bounds__(64) void k_fill_strided_i32(int32_t* p, int n, int stride, int32_t v) {
+  for (int i = threadIdx.x; i < n; i += 64) p[(size_t)i * stride] = v;
+}
+
+void launch_fill_strided_i32(int32_t* p, int n, int stride, int32_t v, hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_fill_strided_i32, dim3(1), dim3(64), 0, s, p, n, stride, v);
+}
+
 void launch_emit(const int32_t* cur_id, int32_t* ids_out, int32_t* cursor, const float* logits, float* logits_out,
                  int V, hipStream_t s) {
   hipLaunchKernelGGL(k_emit, dim3(1), dim3(256), 0, s, cur_id, ids_out, cursor, logits, logits_out, V);

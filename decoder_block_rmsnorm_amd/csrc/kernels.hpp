@@ -75,6 +75,7 @@ void launch_kv_write(KVView kv, int seq, int pos0, int n, const T* k, const T* v
 template <typename T>
 void launch_kv_read(KVView kv, int seq, int pos0, int n, T* k, T* v, hipStream_t s);
 void launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
+void launch_fill_strided_i32(int32_t* p, int n, int stride, int32_t v, hipStream_t s);
 // Row repack.  Source row r first moves inside its head when perm_d > 0
 // (local index j -> j/2 for even j, perm_d/2 + j/2 for odd j: interleaved pairs
 // become (i, i + d/2) pairs), then lands at dst row row0 + (r'/ib)*ib_stride + r'%ib.

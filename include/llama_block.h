@@ -281,6 +281,19 @@ llama_status llama_stack_generate(llama_stack* st, llama_kvcache* cache, const i
                                   float* logits_out_dev, void* scratch, size_t scratch_bytes,
                                   int32_t use_graph, void* stream);
 
+/* The same loop without reusing the cache (LLaMA.generate on page 二 re-runs
+ * the model over the whole sequence for each new token; "流处理与 KV Cache" on
+ * the reading-notes page times generation with and without the cache): emitted
+ * id j re-runs the prompt pass over the prompt and ids 0 .. j-1 from an empty
+ * cache (sequence 0's lens set to 0 in every layer first).  Same arguments and
+ * next-id rule as llama_stack_generate; scratch >= llama_stack_scratch_bytes(st,
+ * prompt_len + n_steps, max_seq).  Kernels are launched directly (no graph).
+ * On return the cache holds the last pass: prompt_len + n_steps positions. */
+llama_status llama_stack_generate_recompute(llama_stack* st, llama_kvcache* cache, const int32_t* prompt_dev,
+                                            int32_t prompt_len, int32_t n_steps, int32_t* ids_out_dev,
+                                            float* logits_out_dev, void* scratch, size_t scratch_bytes,
+                                            void* stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* llama_last_error(void);
 

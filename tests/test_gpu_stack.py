@@ -135,6 +135,34 @@ def test_small_q4_stack_sampled_generation():
     assert all(r_ids[t] == ref.argmax_first(r_log[t]) for t in range(13))
 
 
+def test_small_q4_stack_recompute_equals_cached_generation():
+    """The no-cache loop (each id re-runs the prompt pass over the sequence so
+    far) reproduces the cached generation: logits within the bf16 bar at every
+    step and ids equal up to the first near-tie (the cached GPU run serves as
+    the reference; their agreement in exact arithmetic is pinned on the
+    oracle)."""
+    s = W.BlockShape(dim=512, n_heads=4, n_kv_heads=4, ffn_dim=1536, dtype="bf16", weight_format="q4",
+                     traditional=True)
+    wl = W.Workload("small_q4_stack", s, "stack", batch=1, seq_len=40, decode_steps=12, n_layers=2, vocab=1000,
+                    seed=31)
+    _flush("case: small 4-bit stack, recompute vs cached generation, 12 steps")
+    max_seq = 64
+    s, ids, layers_np, head, blocks, stack, keep = _build(wl, max_seq)
+    c_ids, c_log, _ = _generate(stack, s, wl, ids, 12, True, max_seq)
+    cache = G.make_cache(s, wl.n_layers, 1, max_seq)
+    sc = torch.empty(stack.scratch_bytes(ids.size + 12, max_seq), dtype=torch.uint8, device="cuda")
+    prompt = torch.from_numpy(ids.reshape(-1).astype(np.int32)).cuda()
+    r_ids = torch.zeros(13, dtype=torch.int32, device="cuda")
+    r_log = torch.zeros((13, wl.vocab), dtype=torch.float32, device="cuda")
+    stack.generate_recompute(cache, prompt, 12, r_ids, r_log, sc)
+    torch.cuda.synchronize()
+    assert cache.get_lens(0, 1) == [40 + 12]
+    n = _compare_greedy(r_ids.cpu().numpy(), r_log.cpu().numpy(), {"ids": c_ids, "logits": c_log.astype(np.float64)},
+                        tol=2e-2)
+    _flush(f"  recompute ids equal to the cached run's for {n} of 13 steps")
+    assert n >= 1
+
+
 def test_q4_13b_width_two_layer_stack_prompt512_vs_oracle():
     """Full-width layers of the 40-layer 13B 4-bit stack (dim 5120, 40 heads, ffn
     13824, vocab 32000, a 512-token prompt) at a depth the oracle can run.
