@@ -28,7 +28,8 @@ reason in the design notes of the repository):
 * RoPE "traditional" = adjacent pairs (2i, 2i+1) with the same frequencies and
   rotation sign as the rotate-half form;
 * GQA maps query head h to kv head floor(h / n_rep);
-* future keys are excluded (weight exactly 0);
+* future keys are excluded (weight exactly 0); a sliding window W keeps the
+  W most recent positions, the query's own included;
 * 4-bit weights dequantize as scale * code + bias per group of 64 inputs;
 * a sampled token is chosen by a given uniform u, cumulative mass taken in
   vocabulary order; ties with the last nucleus token are kept.
@@ -125,11 +126,15 @@ def kv_head_of(h: int, n_heads: int, n_kv_heads: int) -> int:
     return h // (n_heads // n_kv_heads)
 
 
-def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndarray) -> np.ndarray:
+def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndarray, window: int = 0) -> np.ndarray:
     """One sequence.
 
     q: [L, H, d] (post-RoPE), k, v: [S, G, d] with key j at position j,
-    q_pos: [L] absolute positions; query i attends keys j <= q_pos[i].
+    q_pos: [L] absolute positions; query i attends keys j <= q_pos[i], and
+    with a sliding window W > 0 only keys j > q_pos[i] - W (the W most recent
+    positions, its own included: the sliding-window attention named in
+    "流处理与 KV Cache" of the reading-notes page, whose window rule the pages
+    leave open).
     Returns [L, H, d].
     """
     q = np.asarray(q, dtype=F64)
@@ -144,6 +149,8 @@ def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndar
         s = (q[:, h, :] @ k[:, g, :].T) * scale             # [L, S]
         j = np.arange(k.shape[0])
         allowed = j[None, :] <= np.asarray(q_pos)[:, None]
+        if window > 0:
+            allowed &= j[None, :] > np.asarray(q_pos)[:, None] - window
         s = np.where(allowed, s, -np.inf)
         m = np.max(s, axis=1, keepdims=True)
         p = np.exp(s - m)
@@ -212,7 +219,7 @@ def block_forward(x: np.ndarray, w: Dict[str, object], shape, k_cache: Optional[
             v_all = np.concatenate([np.asarray(v_cache[b], dtype=F64), v_new], axis=0)
         else:
             k_all, v_all = k_new, v_new
-        o = causal_attention(q, k_all, v_all, pos[rows]).reshape(len(rows), H * d)
+        o = causal_attention(q, k_all, v_all, pos[rows], getattr(shape, "window", 0)).reshape(len(rows), H * d)
         h = x[b, rows] + linear(o, w["wo"])
         f = swiglu_ffn(rmsnorm(h, w["ffn_norm"], shape.eps), w["w1"], w["w2"], w["w3"])
         res["y"].append(h + f)

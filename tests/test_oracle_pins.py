@@ -438,3 +438,37 @@ def test_sample_limits_are_argmax():
         assert ref.sample(z, 0.0, 0.9, 0.7) == best
         assert ref.sample(z, 1e-6, 1.0, float(rng.random())) == best
         assert ref.sample(z, 1.0, 1e-9, float(rng.random())) == best
+
+
+# ------------------------------------------------------------ sliding window --
+# Sliding-window attention ("流处理与 KV Cache", reading-notes page; window rule
+# ours: the W most recent positions, the query's own included).  Pins: W = 1
+# returns the query's own value row; W at least the sequence length is plain
+# causal attention; brute force against an explicit per-query loop.
+
+def test_window_one_returns_own_value():
+    rng = np.random.default_rng(11)
+    L, H, G, d = 7, 4, 2, 8
+    q, k, v = rng.normal(size=(L, H, d)), rng.normal(size=(L, G, d)), rng.normal(size=(L, G, d))
+    out = ref.causal_attention(q, k, v, np.arange(L), window=1)
+    for h in range(H):
+        assert np.allclose(out[:, h], v[:, h // 2], atol=1e-12)
+
+
+def test_window_covering_everything_is_causal_and_brute_force():
+    rng = np.random.default_rng(12)
+    L, S, H, G, d = 9, 5, 2, 1, 16
+    q = rng.normal(size=(L, H, d))
+    k, v = rng.normal(size=(S + L, G, d)), rng.normal(size=(S + L, G, d))
+    pos = S + np.arange(L)
+    assert np.allclose(ref.causal_attention(q, k, v, pos, window=S + L),
+                       ref.causal_attention(q, k, v, pos), atol=1e-12)
+    W = 4
+    out = ref.causal_attention(q, k, v, pos, window=W)
+    for i in range(L):
+        keys = [j for j in range(S + L) if pos[i] - W < j <= pos[i]]
+        for h in range(H):
+            sc = np.array([q[i, h] @ k[j, 0] / np.sqrt(d) for j in keys])
+            p = np.exp(sc - sc.max())
+            p /= p.sum()
+            assert np.allclose(out[i, h], sum(pj * v[j, 0] for pj, j in zip(p, keys)), atol=1e-12)

@@ -52,6 +52,7 @@ class BlockShape:
     dtype: str = "bf16"                # "f32" | "bf16"
     weight_format: str = "dense"       # "dense" | "q4"
     group_size: int = 64
+    window: int = 0                    # sliding-window attention: W most recent positions (0 = full causal)
 
     @property
     def head_dim(self) -> int:
