@@ -209,9 +209,10 @@ def llama_last_error() -> str:
 
 # ------------------------------------------------------------- owners
 def block_config(dim, n_heads, n_kv_heads, ffn_dim, norm_eps=1e-5, rope_theta=10000.0, rope_traditional=False,
-                 act_dtype=LLAMA_BF16, weight_format=LLAMA_W_DENSE, group_size=64, max_seq=4096) -> llama_block_config:
+                 act_dtype=LLAMA_BF16, weight_format=LLAMA_W_DENSE, group_size=64, max_seq=4096,
+                 sliding_window=0) -> llama_block_config:
     return llama_block_config(dim, n_heads, n_kv_heads, ffn_dim, norm_eps, rope_theta, int(bool(rope_traditional)),
-                              act_dtype, weight_format, group_size, max_seq)
+                              act_dtype, weight_format, group_size, max_seq, sliding_window)
 
 
 def _device_bytes(n: int, device="cuda"):

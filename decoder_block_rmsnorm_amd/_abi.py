@@ -21,7 +21,7 @@ class llama_block_config(C.Structure):
     _fields_ = [("dim", C.c_int32), ("n_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("ffn_dim", C.c_int32),
                 ("norm_eps", C.c_float), ("rope_theta", C.c_float), ("rope_traditional", C.c_int32),
                 ("act_dtype", C.c_int32), ("weight_format", C.c_int32), ("group_size", C.c_int32),
-                ("max_seq", C.c_int32)]
+                ("max_seq", C.c_int32), ("sliding_window", C.c_int32)]
 
 
 class llama_linear(C.Structure):

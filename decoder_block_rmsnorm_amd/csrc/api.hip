@@ -58,6 +58,7 @@ static llama_status check_config(const llama_block_config* c, Dims* o) {
     return fail(LLAMA_ERR_INVALID_ARG, "dim, n_heads, n_kv_heads, ffn_dim and max_seq must be positive");
   if (c->n_heads % c->n_kv_heads)
     return fail(LLAMA_ERR_INVALID_ARG, "n_heads (%d) must be a multiple of n_kv_heads (%d)", c->n_heads, c->n_kv_heads);
+  if (c->sliding_window < 0) return fail(LLAMA_ERR_INVALID_ARG, "sliding_window must be >= 0");
   if (c->dim % c->n_heads) return fail(LLAMA_ERR_INVALID_ARG, "dim (%d) must be a multiple of n_heads (%d)", c->dim, c->n_heads);
   if (!(c->norm_eps > 0.f) || !std::isfinite(c->norm_eps)) return fail(LLAMA_ERR_INVALID_ARG, "norm_eps must be > 0");
   if (!(c->rope_theta > 0.f) || !std::isfinite(c->rope_theta)) return fail(LLAMA_ERR_INVALID_ARG, "rope_theta must be > 0");
@@ -435,6 +436,7 @@ static KVView kv_view(const llama_kvcache* c, int layer) {
   v.ps = c->cfg.page_size;
   v.pps = c->pps;
   v.tiled = c->cfg.dtype == LLAMA_BF16 && c->cfg.head_dim == 128;
+  v.window = 0;
   return v;
 }
 
@@ -909,6 +911,7 @@ static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const
                                n_splits_override > 0 ? split_len_override : kSplitLen, &S);
   if (st != LLAMA_OK) return st;
   KVView kv = kv_view(c, layer);
+  kv.window = blk->cfg.sliding_window;
   char* sc = (char*)scratch;
   const Dims& d = blk->dm;
   Marker mk;

@@ -91,6 +91,7 @@ struct KVView {
   int32_t* lens;        // this layer's lens [max_batch]
   int32_t G, d, ps, pps;
   int32_t tiled;        // bf16 / d = 128 operand-order layout (see above)
+  int32_t window;       // sliding window: keys pos - window + 1 .. pos (0 = all keys up to pos)
   __device__ __host__ inline size_t page_base(int b, int pos) const {
     int page = table[(size_t)b * pps + pos / ps];
     return (size_t)page * G * ps * d;

@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void k_attn_simt(const T* q, KVView kv, int B,
   const T* K = (const T*)kv.k;
   const T* V = (const T*)kv.v;
   float mx = -INFINITY, den = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int j = 0; j <= pos; ++j) {
+  for (int j = kv.window > 0 ? max(0, pos - kv.window + 1) : 0; j <= pos; ++j) {
     float part = 0.f;
     if (lane < d) part += q0 * Elt<T>::load(K, kv.k_off(b, j, g, lane));
     if (lane + 64 < d) part += q1 * Elt<T>::load(K, kv.k_off(b, j, g, lane + 64));
@@ -116,6 +116,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
   const int nq_valid = L - q_first;       // queries of this block that exist
   const int kmax_block = S + min(q_first + BQ, L);   // keys [0, kmax_block)
   const int n_tiles = (kmax_block + BK - 1) / BK;
+  // sliding window: the block's earliest query sees keys from S + q_first - W + 1
+  const int W = kv.window;
+  const int t_first = W > 0 ? max(0, S + q_first - W + 1) / BK : 0;
   const int my_q = wq0 + l32;             // query handled by this lane (as an S^T column)
   const int my_pos = S + my_q;
   const int wave_kmax = S + min(wq0 + 32, L);        // keys this wave needs: [0, wave_kmax)
@@ -182,14 +185,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
 
-  if (n_tiles > 0) load_tile(0);
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
+  if (t_first < n_tiles) load_tile(t_first);
+  for (int t = t_first; t < n_tiles; ++t) {
+    const int buf = (t - t_first) & 1;
     store_tile(buf);
     __syncthreads();
     if (t + 1 < n_tiles) load_tile(t + 1);
     const int key0 = t * BK;
-    if (key0 < wave_kmax && nq_valid > wave * 32) {
+    // (W > 0: tiles wholly before the window of this wave's first query skip)
+    if (key0 < wave_kmax && nq_valid > wave * 32 && (W == 0 || key0 + BK > S + wq0 - W + 1)) {
       const bf16_t* ks = smem + buf * (K_ELEMS + V_ELEMS);
       const bf16_t* vs = ks + K_ELEMS;
       // S^T = K Q^T : 2 key subtiles of 32.  A-row r = 8a + 4h + m of subtile st
@@ -210,7 +214,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
       // scale, causal mask, online softmax (query = column l32; rows = keys)
       // (scores stay unscaled; the running max m is kept in log2 units, so
       // p = 2^(s * log2(e)/sqrt(d) - m) is one fma and one v_exp_f32)
-      const bool need_mask = key0 + BK - 1 > S + wq0;  // some key may exceed some query position
+      // some key may exceed some query position, or (window) lie before one
+      // query's window
+      const bool need_mask = key0 + BK - 1 > S + wq0 || (W > 0 && key0 < S + wq0 + 32 - W);
       float tmax = -INFINITY;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
@@ -219,7 +225,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
           float v = s_acc[st][i];
           if (need_mask) {
             int key = key0 + st * 32 + 16 * (i >> 3) + 8 * hg + (i & 7);
-            if (key > my_pos) v = -INFINITY;
+            if (key > my_pos || (W > 0 && key <= my_pos - W)) v = -INFINITY;
           }
           s_acc[st][i] = v;
           tmax = fmaxf(tmax, v);
@@ -336,6 +342,7 @@ __global__ __launch_bounds__(BM ? 512 : 256) __attribute__((amdgpu_waves_per_eu(
   const int g = vg / nv, h0 = (vg % nv) * 16, nr = min(16, n_rep - h0);
   const int pos = kv.lens[b];               // the new token's position; keys 0..pos
   const int nkeys = pos + 1;
+  const int k_lo = kv.window > 0 ? max(0, nkeys - kv.window) : 0;   // sliding window: keys k_lo..pos
   const int k_begin = c * split_len;
   const int k_end = min(nkeys, k_begin + split_len);
   const bool qvalid = l16 < nr;
@@ -355,7 +362,9 @@ __global__ __launch_bounds__(BM ? 512 : 256) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int i = 0; i < 8; ++i) o_acc[i] = (f32x4){};
   float m_run = -INFINITY, l_run = 0.f;
-  for (int k0 = k_begin; k0 < k_end; k0 += 64) {
+  // (64-key steps wholly before the window skip; k_begin and the step stay
+  // multiples of 64)
+  for (int k0 = max(k_begin, k_lo & ~63); k0 < k_end; k0 += 64) {
     const size_t base = kv.page_base(b, k0);
     // this head's K and V blocks, 64-slot sub-block of k0 (tiled layout)
     const size_t sub = base + (size_t)g * kv.ps * 128 + (size_t)((k0 % kv.ps) >> 6) * (64 * 128);
@@ -385,7 +394,7 @@ __global__ __launch_bounds__(BM ? 512 : 256) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = k0 + 32 * (st >> 1) + 8 * hg + 4 * (st & 1) + i;
-        const float v = key < k_end ? s_acc[st][i] : -INFINITY;
+        const float v = key < k_end && key >= k_lo ? s_acc[st][i] : -INFINITY;
         s_acc[st][i] = v;
         tmax = fmaxf(tmax, v);
       }

@@ -66,7 +66,11 @@ enum { LLAMA_W_DENSE = 0, LLAMA_W_Q4 = 1 };         /* weight format */
  *   (i, i + head_dim/2).  Both use angle = position * rope_theta^(-2i/head_dim).
  *   weight_format LLAMA_W_Q4 (bf16 activations only): every linear weight is 4-bit
  *   group-affine, W = scale * code + bias per group of group_size (= 64) inputs.
- *   max_seq: positions 0 .. max_seq-1 may occur (sizes the RoPE table). */
+ *   max_seq: positions 0 .. max_seq-1 may occur (sizes the RoPE table).
+ *   sliding_window: 0 = every query attends all keys up to its position; W > 0 =
+ *   only the W most recent positions, its own included (sliding-window attention,
+ *   named in "流处理与 KV Cache" of the reading-notes page without a window rule;
+ *   the cache still keeps every position). */
 typedef struct {
   int32_t dim, n_heads, n_kv_heads, ffn_dim;
   float norm_eps, rope_theta;
@@ -74,6 +78,7 @@ typedef struct {
   int32_t act_dtype;
   int32_t weight_format, group_size;
   int32_t max_seq;
+  int32_t sliding_window;
 } llama_block_config;
 
 /* One linear weight [out, in] (nn.Linear convention).

@@ -29,7 +29,7 @@ def make_config(s: W.BlockShape, max_seq: int):
     return L.block_config(s.dim, s.n_heads, s.n_kv_heads, s.ffn_dim, norm_eps=s.eps, rope_theta=s.rope_theta,
                           rope_traditional=s.traditional, act_dtype=act_code(s.dtype),
                           weight_format=L.LLAMA_W_Q4 if s.weight_format == "q4" else L.LLAMA_W_DENSE,
-                          group_size=s.group_size, max_seq=max_seq)
+                          group_size=s.group_size, max_seq=max_seq, sliding_window=s.window)
 
 
 def q4_dev(lin) -> dict:

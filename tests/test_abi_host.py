@@ -45,6 +45,7 @@ def cfg(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(n_kv_heads=5), L.LLAMA_ERR_INVALID_ARG),          # H % G != 0
+    (dict(sliding_window=-1), L.LLAMA_ERR_INVALID_ARG),     # negative window
     (dict(dim=4000), L.LLAMA_ERR_INVALID_ARG),             # dim % n_heads != 0
     (dict(norm_eps=0.0), L.LLAMA_ERR_INVALID_ARG),
     (dict(norm_eps=-1e-5), L.LLAMA_ERR_INVALID_ARG),

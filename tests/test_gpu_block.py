@@ -148,6 +148,81 @@ def test_bf16_prefill_mqa():
     _check_branches(s, blk, sc, r, y, 2, 150)
 
 
+# sliding-window attention: each query sees its W most recent positions.
+# Prefill over a cached prefix (windows that start inside the prefix, inside
+# the new tokens, and key tiles wholly before a wave's window), then decode on
+# both attention paths (a window shorter than a 64-key step and one that spans
+# several splits); fp32 on the tiny shape.
+@pytest.mark.parametrize("win", [1, 100, 300])
+def test_bf16_prefill_sliding_window(win):
+    s = dataclasses.replace(SMALL_GQA, window=win)
+    rng = W.Rng(23)
+    B, L, S = 2, 200, 150
+    x = rng.normal((B, L, s.dim), 1.0, "bf16")
+    kv = (rng.normal((B, S, s.n_kv_heads, s.head_dim), 1.0, "bf16"),
+          rng.normal((B, S, s.n_kv_heads, s.head_dim), 1.0, "bf16"))
+    w = W.draw_block_weights(s, rng)
+    lens = [S, 40]
+    kvl = ([kv[0][0], kv[0][1][:40]], [kv[1][0], kv[1][1][:40]])
+    _flush(f"case: bf16 prefill sliding window W={win} lens={lens} L={L}")
+    blk, cache, sc, y = _run_prefill(s, w, x, lens=lens, kv=kvl)
+    r = ref.block_forward(x, w, s, kvl[0], kvl[1])
+    G.check("bf16", y, np.stack(r["y"]), "y")
+    _check_branches(s, blk, sc, r, y, B, L)
+
+
+@pytest.mark.parametrize("win,lens", [(37, [0, 5, 300, 64]), (700, [2300, 5, 1000, 699])])
+def test_bf16_decode_sliding_window(win, lens):
+    s = dataclasses.replace(SMALL_GQA, window=win)
+    rng = W.Rng(24)
+    B, S = len(lens), max(lens)
+    x = rng.normal((B, 1, s.dim), 1.0, "bf16")
+    kv = (rng.normal((B, S, s.n_kv_heads, s.head_dim), 1.0, "bf16"),
+          rng.normal((B, S, s.n_kv_heads, s.head_dim), 1.0, "bf16"))
+    w = W.draw_block_weights(s, rng)
+    _flush(f"case: bf16 decode sliding window W={win} lens={lens}")
+    max_seq = (S + 1 + 63) // 64 * 64
+    blk, wd = G.make_block(s, w, max_seq)
+    cache = G.make_cache(s, 1, B, max_seq)
+    for b in range(B):
+        if lens[b]:
+            cache.write(0, b, 0, G.tdev(kv[0][b, :lens[b]], s.dtype), G.tdev(kv[1][b, :lens[b]], s.dtype))
+    cache.set_lens(0, lens)
+    sc = G.scratch(blk, B, B, max_seq)
+    blk.set_diag(True)
+    xd = G.tdev(x.reshape(B, s.dim), s.dtype)
+    y = torch.empty_like(xd)
+    blk.decode(cache, 0, xd, y, B, sc)
+    torch.cuda.synchronize()
+    r = _oracle(s, w, x, lens, kv)
+    got = G.thost(y).reshape(B, 1, s.dim)
+    G.check("bf16", got, np.stack(r["y"]), "y")
+    _check_branches(s, blk, sc, r, got, B, 1)
+
+
+def test_fp32_sliding_window_prefill_then_decode():
+    wl = W.get("tiny_f32_d256_prefill32_decode8")
+    inp = W.draw_block_workload(wl)
+    s, w, x = dataclasses.replace(wl.shape, window=9), inp["weights"], inp["x"]
+    _flush("case: fp32 tiny, sliding window 9, prefill 32 then 8 decode steps")
+    max_seq = 48
+    blk, wd = G.make_block(s, w, max_seq)
+    cache = G.make_cache(s, 1, 1, max_seq)
+    sc = G.scratch(blk, 32, 1, max_seq)
+    xd = G.tdev(x[0, :32], "f32")
+    y = torch.empty_like(xd)
+    blk.prefill(cache, 0, xd, y, 1, 32, sc)
+    outs = [G.thost(y)]
+    for t in range(32, 40):
+        xt = G.tdev(x[0, t:t + 1], "f32")
+        yt = torch.empty_like(xt)
+        blk.decode(cache, 0, xt, yt, 1, sc)
+        outs.append(G.thost(yt))
+    torch.cuda.synchronize()
+    full = np.stack(ref.block_forward(x[:, :40], w, s)["y"])[0]
+    G.check("f32", np.concatenate(outs, 0), full, "prefill + decode with a window vs one windowed prefill")
+
+
 def test_bf16_prefill_gqa_with_cached_prefix():
     s = SMALL_GQA
     rng = W.Rng(12)
