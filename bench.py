@@ -366,6 +366,8 @@ def main():
     ap.add_argument("--workload", default="llama7b_block_prefill_b1_l2048")
     ap.add_argument("--decode-workload", default="llama13b_block_decode_b16_kv4096",
                     help="decode workload reported beside the prefill line ('' to skip)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="run the decode workload with sliding-window attention of this many positions")
     ap.add_argument("--stack-workload", default="",
                     help="also time the 40-layer 4-bit stack workload (prompt pass and greedy steps)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -403,6 +405,10 @@ def main():
     }
     if args.decode_workload:
         dw = W.get(args.decode_workload)
+        if args.window > 0:
+            import dataclasses
+            dw = dataclasses.replace(dw, name=f"{dw.name}_window{args.window}",
+                                     shape=dataclasses.replace(dw.shape, window=args.window))
         del pre
         torch.cuda.empty_cache()
         log(f"[bench] decode {dw.name}")

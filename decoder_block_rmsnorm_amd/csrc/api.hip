@@ -672,8 +672,12 @@ static llama_status check_call(const llama_block* blk, const llama_kvcache* c, i
   }
   SLayout lo = scratch_layout(blk->cfg, d, batch * L, batch, c->cfg.max_seq, decode, split_min);
   if (sbytes < lo.total) return fail(LLAMA_ERR_CAPACITY, "scratch too small: %zu < %zu bytes", sbytes, lo.total);
-  lo.split_len = attn_split_len(d, batch, maxlen);
-  lo.n_splits = (maxlen + lo.split_len - 1) / lo.split_len;
+  // (a sliding window: the splits cover the window, from its start rounded
+  // down to a 64-key step)
+  const int W = blk->cfg.sliding_window;
+  const int span = W > 0 ? std::min(maxlen, W + 64) : maxlen;
+  lo.split_len = attn_split_len(d, batch, span);
+  lo.n_splits = (span + lo.split_len - 1) / lo.split_len;
   *lay = lo;
   return LLAMA_OK;
 }
@@ -1167,7 +1171,9 @@ extern "C" llama_status llama_stack_generate(llama_stack* st, llama_kvcache* cac
 
   // one sequence: short key splits (more wavefronts for a short cache), fixed
   // for the whole capture
-  const int n_splits = (P + n_steps + kStackSplit - 1) / kStackSplit;
+  const int Wst = c.sliding_window;
+  const int span = Wst > 0 ? std::min(P + n_steps, Wst + 64) : P + n_steps;
+  const int n_splits = (span + kStackSplit - 1) / kStackSplit;
   auto step = [&]() -> llama_status {
     launch_embed<bf16_t>((const bf16_t*)st->emb, V, D, cur, 1, x, s);
     for (int l = 0; l < NL; ++l) {

@@ -343,7 +343,8 @@ __global__ __launch_bounds__(BM ? 512 : 256) __attribute__((amdgpu_waves_per_eu(
   const int pos = kv.lens[b];               // the new token's position; keys 0..pos
   const int nkeys = pos + 1;
   const int k_lo = kv.window > 0 ? max(0, nkeys - kv.window) : 0;   // sliding window: keys k_lo..pos
-  const int k_begin = c * split_len;
+  // splits tile the keys from the window's start (rounded down to a 64-key step)
+  const int k_begin = (k_lo & ~63) + c * split_len;
   const int k_end = min(nkeys, k_begin + split_len);
   const bool qvalid = l16 < nr;
   const int hq = g * n_rep + h0 + (qvalid ? l16 : 0);
@@ -362,9 +363,7 @@ __global__ __launch_bounds__(BM ? 512 : 256) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int i = 0; i < 8; ++i) o_acc[i] = (f32x4){};
   float m_run = -INFINITY, l_run = 0.f;
-  // (64-key steps wholly before the window skip; k_begin and the step stay
-  // multiples of 64)
-  for (int k0 = max(k_begin, k_lo & ~63); k0 < k_end; k0 += 64) {
+  for (int k0 = k_begin; k0 < k_end; k0 += 64) {
     const size_t base = kv.page_base(b, k0);
     // this head's K and V blocks, 64-slot sub-block of k0 (tiled layout)
     const size_t sub = base + (size_t)g * kv.ps * 128 + (size_t)((k0 % kv.ps) >> 6) * (64 * 128);

@@ -282,10 +282,12 @@ def weight_bytes(s: BlockShape) -> float:
 
 
 def decode_bytes(s: BlockShape, batch: int, cached: int) -> dict:
-    """One decode step: every weight byte once, every cached K/V byte once (keys 0..cached),
+    """One decode step: every weight byte once, every cached K/V byte once (keys 0..cached, or the
+    last `window` of them),
     the new K/V rows written, block input read and output written."""
     e = 4 if s.dtype == "f32" else 2
-    kv_read = batch * (cached + 1) * s.n_kv_heads * s.head_dim * 2 * e
+    keys = min(cached + 1, s.window) if s.window > 0 else cached + 1   # a sliding window reads its W keys
+    kv_read = batch * keys * s.n_kv_heads * s.head_dim * 2 * e
     kv_write = batch * s.n_kv_heads * s.head_dim * 2 * e
     act = batch * s.dim * 2 * e
     w = weight_bytes(s)
