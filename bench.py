@@ -366,6 +366,8 @@ def main():
     ap.add_argument("--workload", default="llama7b_block_prefill_b1_l2048")
     ap.add_argument("--decode-workload", default="llama13b_block_decode_b16_kv4096",
                     help="decode workload reported beside the prefill line ('' to skip)")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="run the decode workload with this many kv heads (1 = multi-query attention)")
     ap.add_argument("--window", type=int, default=0,
                     help="run the decode workload with sliding-window attention of this many positions")
     ap.add_argument("--stack-workload", default="",
@@ -405,8 +407,11 @@ def main():
     }
     if args.decode_workload:
         dw = W.get(args.decode_workload)
+        import dataclasses
+        if args.kv_heads > 0:
+            dw = dataclasses.replace(dw, name=f"{dw.name}_kvheads{args.kv_heads}",
+                                     shape=dataclasses.replace(dw.shape, n_kv_heads=args.kv_heads))
         if args.window > 0:
-            import dataclasses
             dw = dataclasses.replace(dw, name=f"{dw.name}_window{args.window}",
                                      shape=dataclasses.replace(dw.shape, window=args.window))
         del pre
