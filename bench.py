@@ -378,8 +378,8 @@ def main():
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the block's data-parallel "
-              "sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (no collectives, no sharded "
+              "weights); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     import workloads as W
