@@ -370,8 +370,9 @@ def main():
                     help="run the decode workload with this many kv heads (1 = multi-query attention)")
     ap.add_argument("--window", type=int, default=0,
                     help="run the decode workload with sliding-window attention of this many positions")
-    ap.add_argument("--stack-workload", default="",
-                    help="also time the 40-layer 4-bit stack workload (prompt pass and greedy steps)")
+    ap.add_argument("--stack-workload", default="q4_llama13b_stack40_prompt512_greedy128",
+                    help="also time the 40-layer 4-bit stack workload (prompt pass, greedy, sampled and "
+                         "no-cache steps); '' to skip")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="minimum seconds of oracle time for the CPU baseline (0: skip)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
