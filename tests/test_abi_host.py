@@ -128,6 +128,12 @@ def test_sample_argument_validation():
     with pytest.raises(L.LlamaError) as e:
         L.llama_stack_set_sampling(None, 1.0, 0.9, 1)
     assert e.value.status == L.LLAMA_ERR_INVALID_ARG
+    # the no-cache loop checks its arguments before any device work
+    for args in [(None, 1, 1, 4, 2, 1, None, 1, 1 << 20), (1, None, 1, 4, 2, 1, None, 1, 1 << 20),
+                 (1, 1, 1, 0, 2, 1, None, 1, 1 << 20), (1, 1, 1, 4, -1, 1, None, 1, 1 << 20)]:
+        with pytest.raises(L.LlamaError) as e:
+            L.llama_stack_generate_recompute(*args, 0)
+        assert e.value.status == L.LLAMA_ERR_INVALID_ARG
 
 
 def test_product_path_does_not_import_the_oracle():
