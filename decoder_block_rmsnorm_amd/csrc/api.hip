@@ -1046,6 +1046,7 @@ extern "C" llama_status llama_sample(const float* logits, int32_t batch, int32_t
     return fail(LLAMA_ERR_INVALID_ARG, "logits, ids and (temperature > 0) u must be non-NULL");
   if (batch <= 0 || vocab <= 0) return fail(LLAMA_ERR_INVALID_ARG, "batch and vocab must be positive");
   if (!(top_p > 0.f && top_p <= 1.f)) return fail(LLAMA_ERR_INVALID_ARG, "top_p must lie in (0, 1]");
+  if (temperature != temperature) return fail(LLAMA_ERR_INVALID_ARG, "temperature is NaN");
   launch_sample(logits, batch, vocab, temperature, top_p, u, nullptr, ids, (hipStream_t)stream);
   return hip_check("sample");
 }
@@ -1116,6 +1117,7 @@ extern "C" llama_status llama_stack_set_sampling(llama_stack* st, float temperat
   if (!st) return fail(LLAMA_ERR_INVALID_ARG, "stack must be non-NULL");
   if (temperature > 0.f && !u) return fail(LLAMA_ERR_INVALID_ARG, "temperature > 0 needs the draws u");
   if (!(top_p > 0.f && top_p <= 1.f)) return fail(LLAMA_ERR_INVALID_ARG, "top_p must lie in (0, 1]");
+  if (temperature != temperature) return fail(LLAMA_ERR_INVALID_ARG, "temperature is NaN");
   st->smp.temperature = temperature;
   st->smp.top_p = top_p;
   st->smp.u = temperature > 0.f ? u : nullptr;
@@ -1192,7 +1194,10 @@ extern "C" llama_status llama_stack_generate(llama_stack* st, llama_kvcache* cac
       HIP_TRY(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "begin capture");
       llama_status q = step();
       hipError_t e = hipStreamEndCapture(s, &graph);
-      if (q != LLAMA_OK) return q;
+      if (q != LLAMA_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return q;
+      }
       if (e != hipSuccess) return fail(LLAMA_ERR_HIP, "end capture: %s", hipGetErrorString(e));
       e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
       if (e == hipSuccess)

@@ -249,8 +249,8 @@ llama_status llama_lm_head_argmax(const llama_linear* head, int32_t weight_forma
  * which the cumulative kept probability exceeds u_dev[b] times the kept
  * probability; tokens tied with the last nucleus token are kept; top_p = 1 keeps
  * every token.  Temperature <= 0: the argmax, lowest index on ties.
- * Errors: LLAMA_ERR_INVALID_ARG for NULL pointers, batch or vocab <= 0, or top_p
- * outside (0, 1]. */
+ * Errors: LLAMA_ERR_INVALID_ARG for NULL pointers, batch or vocab <= 0, top_p
+ * outside (0, 1], or a NaN temperature. */
 llama_status llama_sample(const float* logits_dev, int32_t batch, int32_t vocab, float temperature, float top_p,
                           const float* u_dev, int32_t* ids_dev, void* stream);
 

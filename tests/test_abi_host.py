@@ -121,13 +121,15 @@ def test_null_handles_and_head_validation():
 def test_sample_argument_validation():
     # every check happens before any device work (the pointers are never used)
     for args in [(1, 1, 10, 1.0, 1.5, 1, 1), (1, 1, 10, 1.0, 0.0, 1, 1), (1, 0, 10, 1.0, 0.9, 1, 1),
-                 (1, 1, 0, 1.0, 0.9, 1, 1), (1, 1, 10, 1.0, 0.9, None, 1), (None, 1, 10, 0.0, 1.0, None, 1)]:
+                 (1, 1, 0, 1.0, 0.9, 1, 1), (1, 1, 10, 1.0, 0.9, None, 1), (None, 1, 10, 0.0, 1.0, None, 1),
+                 (1, 1, 10, float("nan"), 0.9, 1, 1)]:
         with pytest.raises(L.LlamaError) as e:
             L.llama_sample(*args, 0)
         assert e.value.status == L.LLAMA_ERR_INVALID_ARG
-    with pytest.raises(L.LlamaError) as e:
-        L.llama_stack_set_sampling(None, 1.0, 0.9, 1)
-    assert e.value.status == L.LLAMA_ERR_INVALID_ARG
+    for args in [(None, 1.0, 0.9, 1), (1, float("nan"), 0.9, 1)]:
+        with pytest.raises(L.LlamaError) as e:
+            L.llama_stack_set_sampling(*args)
+        assert e.value.status == L.LLAMA_ERR_INVALID_ARG
     # the no-cache loop checks its arguments before any device work
     for args in [(None, 1, 1, 4, 2, 1, None, 1, 1 << 20), (1, None, 1, 4, 2, 1, None, 1, 1 << 20),
                  (1, 1, 1, 0, 2, 1, None, 1, 1 << 20), (1, 1, 1, 4, -1, 1, None, 1, 1 << 20)]:
