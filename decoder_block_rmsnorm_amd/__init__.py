@@ -328,11 +328,29 @@ class Stack:
     def set_sampling(self, temperature: float, top_p: float = 1.0, u=None) -> None:
         """Greedy at temperature <= 0; else u (fp32 [n_steps + 1] on the device,
         kept alive here) gives the draw of each emitted id."""
-        self._u = u
         llama_stack_set_sampling(self.handle, temperature, top_p, u)
+        # (replaced only once the library took it: it keeps reading the old draws until then)
+        self._u = u if temperature > 0 else None
+
+    def _check_sizes(self, n_steps: int, ids_out, logits_out) -> None:
+        # the device buffers the kernels write or read per emitted id; their sizes
+        # cannot be seen through the C ABI
+        # (raw addresses pass unchecked)
+        n = n_steps + 1
+        size = lambda t: t.numel() if hasattr(t, "numel") else None  # noqa: E731
+        if n_steps < 0:
+            return
+        if size(ids_out) is not None and size(ids_out) < n:
+            raise ValueError(f"ids_out holds {size(ids_out)} ids, {n} are emitted")
+        if size(logits_out) is not None and size(logits_out) < n * self.vocab:
+            raise ValueError(f"logits_out holds {size(logits_out)} values, {n} rows of {self.vocab} are written")
+        u = getattr(self, "_u", None)
+        if size(u) is not None and size(u) < n:
+            raise ValueError(f"the sampling draws hold {size(u)} values, {n} ids are drawn")
 
     def generate(self, cache: KVCache, prompt, n_steps: int, ids_out, logits_out, scratch, use_graph=True,
                  stream=None) -> None:
+        self._check_sizes(n_steps, ids_out, logits_out)
         llama_stack_generate(self.handle, cache.handle, prompt, prompt.numel(), n_steps, ids_out, logits_out,
                              scratch, scratch.numel(), int(bool(use_graph)), stream)
 
@@ -340,6 +358,7 @@ class Stack:
                            stream=None) -> None:
         """No cache reuse: every id re-runs the prompt pass over the sequence so
         far (scratch sized by scratch_bytes(prompt + n_steps, max_seq))."""
+        self._check_sizes(n_steps, ids_out, logits_out)
         llama_stack_generate_recompute(self.handle, cache.handle, prompt, prompt.numel(), n_steps, ids_out,
                                        logits_out, scratch, scratch.numel(), stream)
 

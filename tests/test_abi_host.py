@@ -138,6 +138,25 @@ def test_sample_argument_validation():
         assert e.value.status == L.LLAMA_ERR_INVALID_ARG
 
 
+def test_stack_binding_checks_output_and_draw_sizes():
+    # the sizes of the per-id device buffers are checked before any call
+    import torch
+    st = L.Stack.__new__(L.Stack)
+    st.handle, st.vocab, st._u = None, 100, None
+    ids, logits = torch.zeros(5, dtype=torch.int32), torch.zeros(5 * 100)
+    st._check_sizes(4, ids, logits)
+    st._check_sizes(4, 0x1000, None)                 # raw addresses are not checked
+    for n_steps, i, lg in [(5, ids, None), (4, ids, torch.zeros(499)), (4, torch.zeros(4, dtype=torch.int32), None)]:
+        with pytest.raises(ValueError):
+            st._check_sizes(n_steps, i, lg)
+    st._u = torch.zeros(3)
+    with pytest.raises(ValueError):
+        st.generate(None, None, 4, ids, None, None)
+    with pytest.raises(ValueError):
+        st.generate_recompute(None, None, 4, ids, None, None)
+    st.handle = None
+
+
 def test_product_path_does_not_import_the_oracle():
     import decoder_block_rmsnorm_amd
     pkg = os.path.dirname(decoder_block_rmsnorm_amd.__file__)
