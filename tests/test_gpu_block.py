@@ -223,7 +223,10 @@ def test_fp32_sliding_window_prefill_then_decode():
     G.check("f32", np.concatenate(outs, 0), full, "prefill + decode with a window vs one windowed prefill")
 
 
-def test_bf16_prefill_gqa_with_cached_prefix():
+# "full": the cache and the rotation table hold exactly 130 + 200 positions, so
+# the second sequence's prompt ends on the last one
+@pytest.mark.parametrize("full", [False, True])
+def test_bf16_prefill_gqa_with_cached_prefix(full):
     s = SMALL_GQA
     rng = W.Rng(12)
     x = rng.normal((2, 200, s.dim), 1.0, "bf16")
@@ -231,11 +234,12 @@ def test_bf16_prefill_gqa_with_cached_prefix():
     kv = (rng.normal((2, 130, s.n_kv_heads, s.head_dim), 1.0, "bf16"),
           rng.normal((2, 130, s.n_kv_heads, s.head_dim), 1.0, "bf16"))
     w = W.draw_block_weights(s, rng)
-    _flush("case: bf16 GQA(4) chunked prefill B=2 L=200 after 64/130 cached")
-    blk, cache, sc, y = _run_prefill(s, w, x, lens, kv)
+    _flush(f"case: bf16 GQA(4) chunked prefill B=2 L=200 after 64/130 cached full={full}")
+    blk, cache, sc, y = _run_prefill(s, w, x, lens, kv, max_seq=330 if full else None)
     r = _oracle(s, w, x, lens, kv)
     G.check("bf16", y, np.stack(r["y"]), "y")
     _check_branches(s, blk, sc, r, y, 2, 200)
+    assert cache.get_lens(0, 2) == [264, 330]
 
 
 # 64 sequences x 4 kv heads of 8 query heads each: the decode attention
@@ -255,7 +259,8 @@ MQA = W.BlockShape(dim=4096, n_heads=32, n_kv_heads=1, ffn_dim=512, dtype="bf16"
 
 
 # "empty_cache": sequences at position 0 (the token attends to itself only)
-# next to short ones, on the path that merges key ranges inside one block;
+# next to short ones, on the path that merges key ranges inside one block (its
+# 63-key sequence decodes into the last slot of a 64-position cache);
 # "mqa_short" takes that path too, "mqa_long" (over 2048 keys) the split one
 @pytest.mark.parametrize("shape", ["mha", "gqa", "gqa_long_splits", "empty_cache", "mqa_short", "mqa_long"])
 def test_bf16_decode_ragged_lengths(shape):
