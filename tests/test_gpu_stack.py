@@ -79,13 +79,15 @@ def _compare_greedy(gpu_ids, gpu_logits, oracle, tol=1e-2):
     return checked
 
 
-def test_small_q4_stack_generate_graph_equals_eager_and_oracle():
+# max_seq 52: the prompt and the steps fill the cache and the rotation table
+# to their last position
+@pytest.mark.parametrize("max_seq", [64, 52])
+def test_small_q4_stack_generate_graph_equals_eager_and_oracle(max_seq):
     s = W.BlockShape(dim=512, n_heads=4, n_kv_heads=4, ffn_dim=1536, dtype="bf16", weight_format="q4",
                      traditional=True)
     wl = W.Workload("small_q4_stack", s, "stack", batch=1, seq_len=40, decode_steps=12, n_layers=2, vocab=1000,
                     seed=31)
-    _flush("case: small 4-bit stack, 2 layers, prompt 40, 12 steps")
-    max_seq = 64
+    _flush(f"case: small 4-bit stack, 2 layers, prompt 40, 12 steps, max_seq {max_seq}")
     s, ids, layers_np, head, blocks, stack, keep = _build(wl, max_seq)
     g_ids, g_log, cache = _generate(stack, s, wl, ids, 12, True, max_seq)
     e_ids, e_log, _ = _generate(stack, s, wl, ids, 12, False, max_seq)
