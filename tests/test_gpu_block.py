@@ -261,11 +261,16 @@ MQA = W.BlockShape(dim=4096, n_heads=32, n_kv_heads=1, ffn_dim=512, dtype="bf16"
 # "empty_cache": sequences at position 0 (the token attends to itself only)
 # next to short ones, on the path that merges key ranges inside one block (its
 # 63-key sequence decodes into the last slot of a 64-position cache);
-# "mqa_short" takes that path too, "mqa_long" (over 2048 keys) the split one
-@pytest.mark.parametrize("shape", ["mha", "gqa", "gqa_long_splits", "empty_cache", "mqa_short", "mqa_long"])
+# "mqa_short" takes that path too, "mqa_long" (over 2048 keys) the split one;
+# "full_split": a 2367-key sequence decodes into the last slot of a
+# 2368-position cache on the split path
+@pytest.mark.parametrize("shape", ["mha", "gqa", "gqa_long_splits", "empty_cache", "mqa_short", "mqa_long",
+                                   "full_split"])
 def test_bf16_decode_ragged_lengths(shape):
     if shape == "gqa_long_splits":
         s, lens = WIDE_GQA, _long_split_lens()
+    elif shape == "full_split":
+        s, lens = WIDE_GQA, [2367, 0, 1000]
     elif shape == "empty_cache":
         s, lens = SMALL_GQA, [0, 5, 0, 63]
     elif shape == "mqa_short":
