@@ -68,9 +68,10 @@ def dequant_q4(lin: Dict[str, np.ndarray], codes: Optional[np.ndarray] = None) -
         from workloads import unpack_q4_codes
         codes = unpack_q4_codes(lin["packed"])
     g = int(lin["group"])
-    s = np.repeat(np.asarray(lin["scales"], dtype=F64), g, axis=1)
-    b = np.repeat(np.asarray(lin["biases"], dtype=F64), g, axis=1)
-    return s * codes.astype(F64) + b
+    n, k = codes.shape
+    s = np.asarray(lin["scales"], dtype=F64)[:, :, None]      # one scale and bias per group
+    b = np.asarray(lin["biases"], dtype=F64)[:, :, None]
+    return (s * codes.reshape(n, k // g, g).astype(F64) + b).reshape(n, k)
 
 
 def weight_matrix(w) -> np.ndarray:
@@ -249,6 +250,31 @@ def embed(table: np.ndarray, ids: np.ndarray) -> np.ndarray:
 
 def lm_head_logits(x_last: np.ndarray, norm_w: np.ndarray, eps: float, head) -> np.ndarray:
     return linear(rmsnorm(x_last, norm_w, eps), head)
+
+
+def stack_forward(ids: np.ndarray, layers, head: Dict[str, object], shape, rows: Sequence[int],
+                  record=None) -> np.ndarray:
+    """The model's forward pass over a whole token sequence, with no cache
+    (LLaMA.forward on page 二: embedding, every block causally over all
+    positions, final RMSNorm, output head), returning the logits of the
+    positions in `rows` [len(rows), vocab].
+
+    ids: [L] token ids.  layers: the blocks' weights in order (an iterable,
+    consumed once: each layer's 4-bit weights are dequantized by its own block
+    call).  record(i, x_in, res), if given, sees every block: its input
+    [L, D] and the block_forward result (k_new / v_new: what it caches).
+    By causality the logits of position t equal those of a forward over the
+    first t + 1 tokens alone: the no-cache generation of LLaMA.generate, which
+    re-runs the model on the sequence so far for every new token.
+    """
+    x = embed(head["embedding"], np.asarray(ids).reshape(1, -1))          # [1, L, D]
+    for i, w in enumerate(layers):
+        r = block_forward(x, w, shape)
+        if record is not None:
+            record(i, x[0], r)
+        x = stack_arrays(r, "y")
+    out = weight_matrix(head["output"])
+    return np.stack([lm_head_logits(x[0, t], head["norm"], shape.eps, out) for t in rows])
 
 
 def argmax_first(v: np.ndarray) -> int:

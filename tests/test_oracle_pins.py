@@ -472,3 +472,50 @@ def test_window_covering_everything_is_causal_and_brute_force():
             p = np.exp(sc - sc.max())
             p /= p.sum()
             assert np.allclose(out[i, h], sum(pj * v[j, 0] for pj, j in zip(p, keys)), atol=1e-12)
+
+
+# ------------------------------------------------------------- stack ends --
+def test_embed_is_one_hot_product():
+    # "1. 嵌入层" (MLX page): the embedding of id i is row i of the table; as a
+    # product, onehot(i) . E, which picks that row exactly (every other term is 0)
+    E = _rand(37, 24)
+    ids = np.array([[0, 36, 5, 5, 17], [36, 0, 1, 2, 3]])
+    got = ref.embed(E, ids)
+    onehot = np.zeros(ids.shape + (37,))
+    for idx in np.ndindex(ids.shape):
+        onehot[idx + (ids[idx],)] = 1.0
+    assert got.shape == (2, 5, 24)
+    assert np.array_equal(got, onehot @ E)
+    assert np.array_equal(got[0, 2], got[0, 3])              # a repeated id gives the same row
+
+
+def test_stack_forward_is_the_no_cache_generation():
+    # LLaMA.forward over the whole sequence: the logits of position t equal the
+    # cached generation's logits for the id it emitted at t (the page's generate
+    # without a cache re-runs this forward every step); the record hook sees
+    # every block's input and cached keys
+    s = W.BlockShape(dim=64, n_heads=4, n_kv_heads=2, ffn_dim=96, traditional=False, dtype="f32")
+    r = W.Rng(12)
+    layers = [W.draw_block_weights(s, r) for _ in range(3)]
+    head = {"embedding": r.normal((40, 64), 1.0, "f32"), "norm": r.norm_weight(64, "f32"),
+            "output": r.normal((40, 64), 0.2, "f32")}
+    ids = r.ids((1, 5), 40)
+    gen = ref.greedy_generate(ids, layers, head, s, steps=4)
+    seq = np.concatenate([ids[0], gen["ids"][:-1]])
+    seen = []
+    got = ref.stack_forward(seq, iter(layers), head, s, rows=range(4, 9),
+                            record=lambda i, x, res: seen.append((i, x.shape, res["k_new"][0].shape)))
+    np.testing.assert_allclose(got, np.stack(gen["logits"]), rtol=1e-10, atol=1e-12)
+    assert seen == [(i, (9, 64), (9, 2, 16)) for i in range(3)]
+    # a 4-bit stack too: the same weights once dequantized
+    q = W.BlockShape(dim=128, n_heads=2, n_kv_heads=2, ffn_dim=128, dtype="bf16", weight_format="q4",
+                     traditional=True)
+    rq = W.Rng(13)
+    ql = [W.draw_block_weights(q, rq) for _ in range(2)]
+    qh = {"embedding": rq.normal((64, 128), 0.5, "bf16"), "norm": rq.norm_weight(128, "bf16"),
+          "output": W.draw_q4_linear(rq, 64, 128)}
+    qids = rq.ids((1, 6), 64)
+    gen = ref.greedy_generate(qids, ql, qh, q, steps=3)
+    seq = np.concatenate([qids[0], gen["ids"][:-1]])
+    got = ref.stack_forward(seq, ql, qh, q, rows=range(5, 9))
+    np.testing.assert_allclose(got, np.stack(gen["logits"]), rtol=1e-10, atol=1e-12)
