@@ -164,3 +164,27 @@ def test_lm_head_argmax(fmt):
         torch.cuda.synchronize()
         l0 = logits[0].cpu().numpy()
         assert l0[3] == l0[7] and int(ids[0]) == ref.argmax_first(l0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_embed_bitexact(dtype):
+    """llama_embed ("1. 嵌入层", MLX page) equals the oracle's lookup bit for bit
+    (a copy of table rows: ids 0 and vocab-1, repeats, a run longer than one
+    block); ids outside [0, vocab) give zero rows, as the header states."""
+    _flush(f"case: embedding lookup {dtype}")
+    rng = W.Rng(29)
+    V, D = 3001, 640
+    table = rng.normal((V, D), 0.02 if dtype == "bf16" else 1.0, dtype)
+    ids = np.concatenate([[0, V - 1, 5, 5, V - 1], rng.ids((700,), V).ravel()]).astype(np.int32)
+    td = G.tdev(table, dtype)
+    idd = torch.from_numpy(ids).cuda()
+    out = torch.empty((ids.size, D), device="cuda", dtype=td.dtype)
+    L.llama_embed(td, V, D, G.act_code(dtype), idd, ids.size, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.thost(out), ref.embed(table, ids))
+    bad = torch.tensor([-1, V, 7], dtype=torch.int32, device="cuda")
+    out2 = torch.full((3, D), 7.0, device="cuda", dtype=td.dtype)
+    L.llama_embed(td, V, D, G.act_code(dtype), bad, 3, out2)
+    torch.cuda.synchronize()
+    got = G.thost(out2)
+    assert not got[:2].any() and np.array_equal(got[2], ref.embed(table, [7])[0])

@@ -1,12 +1,19 @@
 """The 4-bit stack: embedding -> n blocks -> final RMSNorm -> output head ->
-greedy argmax, prompt pass then single-token steps replayed from a HIP graph.
+greedy argmax, prompt pass then single-token steps replayed from a HIP graph
+(the generation loop of "生成过程" on the MLX page), and the same loop without
+the cache's reuse (LLaMA.generate on page 二).
 
-Token ids: several results can be correct where two logits nearly tie, so ids
-are compared with the oracle step by step while the oracle's top-2 margin
-exceeds 4x the largest logit error of that step; at the first near-tie the
-GPU's choice must be within that bound of the oracle's best, and the
-comparison stops there (after it, the two sequences legitimately differ).
+Token ids are checked at every step, teacher-forced: the oracle runs one
+causal forward over the prompt and the GPU's own emitted ids, which gives its
+logits for every step on the same context (by causality, what re-running the
+model on the sequence so far gives).  Where the oracle's top-2 margin exceeds
+delta = 4 x the step's largest logit error, the GPU's id must be the oracle's
+argmax; where it does not (a near-tie that bf16 rounding may decide either
+way), the GPU's id must be within delta of the oracle's best.  The device argmax
+is also compared bit for bit with the CPU argmax of the GPU's own logits.
 """
+import concurrent.futures as cf
+
 import numpy as np
 import pytest
 import torch
@@ -59,57 +66,89 @@ def _generate(stack, s, wl, ids, steps, use_graph, max_seq):
     return out_ids.cpu().numpy(), logits.cpu().numpy(), cache
 
 
-def _compare_greedy(gpu_ids, gpu_logits, oracle, tol=1e-2):
-    checked = 0
+def _dequantized(layers_np, workers=3):
+    """The layers' weights dequantized to float64 ahead of their use, a few at a
+    time in background threads (each dequantization is the oracle's own)."""
+    def conv(w):
+        return {k: (v if k.endswith("norm") else ref.weight_matrix(v)) for k, v in w.items()}
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        futs = [ex.submit(conv, w) for w in layers_np[:workers]]
+        for i in range(len(layers_np)):
+            w = futs[i].result()
+            futs[i] = None
+            if i + workers < len(layers_np):
+                futs.append(ex.submit(conv, layers_np[i + workers]))
+            yield w
+
+
+def _teacher_forced(ids, gen_ids, layers_np, head, s, record=None):
+    """Oracle logits for every emitted id: one causal forward over the prompt and
+    the GPU's ids, rows P-1 .. P+n-1 (n + 1 rows for n + 1 emitted ids)."""
+    P, n1 = ids.size, len(gen_ids)
+    seq = np.concatenate([ids.reshape(-1), np.asarray(gen_ids[:-1], dtype=np.int64)])
+    return ref.stack_forward(seq, _dequantized(layers_np), head, s, rows=range(P - 1, P - 1 + n1), record=record)
+
+
+def _check_ids(gpu_ids, gpu_logits, o_logits, tol, what):
+    """Every step: logits within `tol` (relative L2), the device argmax equal to
+    the CPU argmax of the same logits, and the margin rule against the oracle.
+    Returns (steps decided by the margin, near-ties, largest logit error)."""
+    decided = near = 0
+    worst = 0.0
     for t in range(len(gpu_ids)):
-        ol = oracle["logits"][t]
         gl = gpu_logits[t].astype(np.float64)
+        ol = np.asarray(o_logits[t], dtype=np.float64)
+        assert gpu_ids[t] == ref.argmax_first(gpu_logits[t]), f"{what} step {t}: device argmax differs"
+        worst = max(worst, G.check("bf16", gl, ol, f"{what} logits step {t}", tol_bf16=tol))
         delta = 4.0 * float(np.max(np.abs(gl - ol)))
         top = np.sort(ol)[-2:]
-        margin = float(top[1] - top[0])
-        G.check("bf16", gl, ol, f"logits step {t}", tol_bf16=tol)
-        if margin > delta:
-            assert gpu_ids[t] == oracle["ids"][t], f"step {t}: id {gpu_ids[t]} != {oracle['ids'][t]}"
-            checked += 1
-            continue
-        assert ol[gpu_ids[t]] >= ol.max() - delta, f"step {t}: near tie but GPU id outside the error bound"
-        if gpu_ids[t] != oracle["ids"][t]:
-            break
-        checked += 1
-    return checked
+        if top[1] - top[0] > delta:
+            assert gpu_ids[t] == ref.argmax_first(ol), f"{what} step {t}: id {gpu_ids[t]} != {ref.argmax_first(ol)}"
+            decided += 1
+        else:
+            assert ol[gpu_ids[t]] >= ol.max() - delta, f"{what} step {t}: near-tie, GPU id outside the error bound"
+            near += 1
+    return decided, near, worst
+
+
+def _small():
+    s = W.BlockShape(dim=512, n_heads=4, n_kv_heads=4, ffn_dim=1536, dtype="bf16", weight_format="q4",
+                     traditional=True)
+    return W.Workload("small_q4_stack", s, "stack", batch=1, seq_len=40, decode_steps=12, n_layers=2, vocab=1000,
+                      seed=31)
 
 
 # max_seq 52: the prompt and the steps fill the cache and the rotation table
 # to their last position
 @pytest.mark.parametrize("max_seq", [64, 52])
 def test_small_q4_stack_generate_graph_equals_eager_and_oracle(max_seq):
-    s = W.BlockShape(dim=512, n_heads=4, n_kv_heads=4, ffn_dim=1536, dtype="bf16", weight_format="q4",
-                     traditional=True)
-    wl = W.Workload("small_q4_stack", s, "stack", batch=1, seq_len=40, decode_steps=12, n_layers=2, vocab=1000,
-                    seed=31)
+    wl = _small()
     _flush(f"case: small 4-bit stack, 2 layers, prompt 40, 12 steps, max_seq {max_seq}")
     s, ids, layers_np, head, blocks, stack, keep = _build(wl, max_seq)
     g_ids, g_log, cache = _generate(stack, s, wl, ids, 12, True, max_seq)
     e_ids, e_log, _ = _generate(stack, s, wl, ids, 12, False, max_seq)
     assert np.array_equal(g_ids, e_ids) and np.array_equal(g_log, e_log), "graph replay differs from eager launches"
     assert cache.get_lens(1, 1) == [40 + 12]
-    for t in range(13):
-        assert g_ids[t] == ref.argmax_first(g_log[t])      # device argmax == CPU argmax of the same logits
+    o_log = _teacher_forced(ids, g_ids, layers_np, head, s)
+    dec, near, worst = _check_ids(g_ids, g_log, o_log, 1e-2, "cached generation")
+    _flush(f"  13 of 13 steps checked: {dec} decided by the margin, {near} near-ties; worst logits rel L2 {worst:.2e}")
+    # where the GPU followed the oracle's own greedy choices, the oracle's cached
+    # generation gives the same logits
     orc = ref.greedy_generate(ids, layers_np, head, s, steps=12)
-    n = _compare_greedy(g_ids, g_log, orc)
-    _flush(f"  ids equal to the oracle's for {n} of 13 steps")
-    assert n >= 1
+    t = 0
+    while t < 13 and (t == 0 or g_ids[t - 1] == orc["ids"][t - 1]):
+        np.testing.assert_allclose(o_log[t], orc["logits"][t], rtol=1e-9, atol=1e-9)
+        t += 1
+    _flush(f"  teacher-forced oracle equals the oracle's own greedy generation on its first {t} steps")
 
 
 def test_small_q4_stack_sampled_generation():
     """Sampled generate loop (temperature 0.8, nucleus 0.9; the draws u are
     seeded inputs): graph replay equals eager launches, every emitted id is
     llama_sample's choice on that step's logits with the same draw, and one the
-    oracle's sampler allows on those logits (within a 1e-5 band of the draw)."""
-    s = W.BlockShape(dim=512, n_heads=4, n_kv_heads=4, ffn_dim=1536, dtype="bf16", weight_format="q4",
-                     traditional=True)
-    wl = W.Workload("small_q4_stack", s, "stack", batch=1, seq_len=40, decode_steps=12, n_layers=2, vocab=1000,
-                    seed=31)
+    oracle's sampler allows on those logits (within a 1e-5 band of the draw);
+    the logits match the oracle's teacher-forced logits at every step."""
+    wl = _small()
     _flush("case: small 4-bit stack, sampled generation T=0.8 top_p=0.9")
     max_seq = 64
     s, ids, layers_np, head, blocks, stack, keep = _build(wl, max_seq)
@@ -132,25 +171,24 @@ def test_small_q4_stack_sampled_generation():
         assert int(g_ids[t]) in allowed
         greedy_steps += int(g_ids[t]) == ref.argmax_first(z)
     _flush(f"  {greedy_steps} of 13 sampled ids were also the argmax")
+    o_log = _teacher_forced(ids, g_ids, layers_np, head, s)
+    for t in range(13):
+        G.check("bf16", g_log[t], o_log[t], f"sampled generation logits step {t}")
     stack.set_sampling(0.0, 1.0, None)          # back to greedy
     r_ids, r_log, _ = _generate(stack, s, wl, ids, 12, True, max_seq)
     assert all(r_ids[t] == ref.argmax_first(r_log[t]) for t in range(13))
 
 
-def test_small_q4_stack_recompute_equals_cached_generation():
+def test_small_q4_stack_recompute_vs_oracle():
     """The no-cache loop (each id re-runs the prompt pass over the sequence so
-    far) reproduces the cached generation: logits within the bf16 bar at every
-    step and ids equal up to the first near-tie (the cached GPU run serves as
-    the reference; their agreement in exact arithmetic is pinned on the
-    oracle)."""
-    s = W.BlockShape(dim=512, n_heads=4, n_kv_heads=4, ffn_dim=1536, dtype="bf16", weight_format="q4",
-                     traditional=True)
-    wl = W.Workload("small_q4_stack", s, "stack", batch=1, seq_len=40, decode_steps=12, n_layers=2, vocab=1000,
-                    seed=31)
-    _flush("case: small 4-bit stack, recompute vs cached generation, 12 steps")
+    far, LLaMA.generate on page 二) against the oracle at every step: its logits
+    within the bf16 bar of the oracle's forward over the same sequence, ids by
+    the margin rule; where it followed the oracle's own greedy choices, also
+    equal (to fp64 rounding) to ref.greedy_generate's logits."""
+    wl = _small()
+    _flush("case: small 4-bit stack, no-cache recompute generation vs the oracle, 12 steps")
     max_seq = 64
     s, ids, layers_np, head, blocks, stack, keep = _build(wl, max_seq)
-    c_ids, c_log, _ = _generate(stack, s, wl, ids, 12, True, max_seq)
     cache = G.make_cache(s, wl.n_layers, 1, max_seq)
     sc = torch.empty(stack.scratch_bytes(ids.size + 12, max_seq), dtype=torch.uint8, device="cuda")
     prompt = torch.from_numpy(ids.reshape(-1).astype(np.int32)).cuda()
@@ -159,80 +197,224 @@ def test_small_q4_stack_recompute_equals_cached_generation():
     stack.generate_recompute(cache, prompt, 12, r_ids, r_log, sc)
     torch.cuda.synchronize()
     assert cache.get_lens(0, 1) == [40 + 12]
-    n = _compare_greedy(r_ids.cpu().numpy(), r_log.cpu().numpy(), {"ids": c_ids, "logits": c_log.astype(np.float64)},
-                        tol=2e-2)
-    _flush(f"  recompute ids equal to the cached run's for {n} of 13 steps")
-    assert n >= 1
+    g_ids, g_log = r_ids.cpu().numpy(), r_log.cpu().numpy()
+    o_log = _teacher_forced(ids, g_ids, layers_np, head, s)
+    dec, near, worst = _check_ids(g_ids, g_log, o_log, 1e-2, "recompute generation")
+    _flush(f"  13 of 13 steps checked: {dec} decided by the margin, {near} near-ties; worst logits rel L2 {worst:.2e}")
+    orc = ref.greedy_generate(ids, layers_np, head, s, steps=12)
+    t = 0
+    while t < 13 and (t == 0 or g_ids[t - 1] == orc["ids"][t - 1]):
+        G.check("bf16", g_log[t], orc["logits"][t], f"recompute logits step {t} vs ref.greedy_generate")
+        t += 1
+    _flush(f"  logits equal to ref.greedy_generate's (within the bar) on its first {t} steps")
+    assert t >= 1
 
+
+def _layer_errors(blocks, s, xs, ks, vs, P, max_seq, n_dec):
+    """Each GPU block on the oracle's own input of its layer (inputs flow from
+    the oracle to the GPU, never back): the P-token prompt pass (every row, and
+    the keys and values it caches), then n_dec decode steps against the oracle's
+    keys and values written into the cache.  Returns per layer the relative L2
+    errors {prefill, row (worst row of the prompt pass), cache, decode}."""
+    out = []
+    for l, blk in enumerate(blocks):
+        cache = G.make_cache(s, 1, 1, max_seq)
+        sc = G.scratch(blk, P, 1, max_seq)
+        xd = G.tdev(xs[l][:P], "bf16")
+        y = torch.empty_like(xd)
+        blk.prefill(cache, 0, xd, y, 1, P, sc)
+        torch.cuda.synchronize()
+        got = G.thost(y)
+        exp = xs[l + 1][:P]
+        e = {"prefill": G.rel_l2(got, exp),
+             "row": float(np.max(np.linalg.norm(got - exp, axis=1) / np.linalg.norm(exp, axis=1)))}
+        assert np.isfinite(got).all()
+        kd = torch.empty((P, s.n_kv_heads, s.head_dim), device="cuda", dtype=torch.bfloat16)
+        vd = torch.empty_like(kd)
+        cache.read(0, 0, 0, P, kd, vd)
+        torch.cuda.synchronize()
+        e["cache"] = max(G.rel_l2(G.thost(kd), ks[l][:P]), G.rel_l2(G.thost(vd), vs[l][:P]))
+        # the oracle's keys and values for the prompt, then the decode steps
+        cache.write(0, 0, 0, G.tdev(ks[l][:P], "bf16"), G.tdev(vs[l][:P], "bf16"))
+        sd = G.scratch(blk, 1, 1, max_seq)
+        e["decode"] = 0.0
+        for j in range(n_dec):
+            xj = G.tdev(xs[l][P + j:P + j + 1], "bf16")
+            yj = torch.empty_like(xj)
+            blk.decode(cache, 0, xj, yj, 1, sd)
+            torch.cuda.synchronize()
+            e["decode"] = max(e["decode"], G.rel_l2(G.thost(yj), xs[l + 1][P + j:P + j + 1]))
+            # (the slot the step appended now holds the oracle's key and value)
+            cache.write(0, 0, P + j, G.tdev(ks[l][P + j:P + j + 1], "bf16"), G.tdev(vs[l][P + j:P + j + 1], "bf16"))
+        e["lens"] = cache.get_lens(0, 1)[0]
+        out.append(e)
+        _flush(f"  layer {l}: prompt rel L2 {e['prefill']:.2e} (worst row {e['row']:.2e}), cache {e['cache']:.2e}, "
+               f"decode {e['decode']:.2e}")
+        del cache, sc, sd
+    return out
+
+
+def _head_logits(keep, s, vocab, rows_np):
+    """The GPU's final norm, 4-bit output head and argmax on given hidden rows."""
+    hw, fn = keep[2], keep[1]
+    lh = L.llama_linear(hw["w"].data_ptr(), hw["scales"].data_ptr(), hw["biases"].data_ptr())
+    n1 = rows_np.shape[0]
+    rows = G.tdev(rows_np, "bf16")
+    lg = torch.empty((n1, vocab), device="cuda", dtype=torch.float32)
+    gid = torch.empty(n1, device="cuda", dtype=torch.int32)
+    hsc = torch.empty(L.llama_head_scratch_bytes(4, s.dim, vocab), dtype=torch.uint8, device="cuda")
+    for r0 in range(0, n1, 4):
+        nb = min(4, n1 - r0)
+        L.llama_lm_head_argmax(lh, L.LLAMA_W_Q4, 64, L.LLAMA_BF16, fn, s.eps, rows[r0:r0 + nb], nb, s.dim,
+                               vocab, lg[r0:r0 + nb], gid[r0:r0 + nb], hsc, hsc.numel())
+    torch.cuda.synchronize()
+    return gid.cpu().numpy(), lg.cpu().numpy()
+
+
+def _recorder(store, n_layers):
+    """record() for ref.stack_forward: every layer's input, the keys and values
+    it caches, and the last layer's output."""
+    def record(i, x, res):
+        store["xs"].append(np.asarray(x, dtype=np.float64))
+        store["ks"].append(res["k_new"][0])
+        store["vs"].append(res["v_new"][0])
+        if i == n_layers - 1:
+            store["xs"].append(ref.stack_arrays(res, "y")[0])
+        if n_layers > 4:
+            _flush(f"  oracle layer {i} done")
+    return record
+
+
+# The chained comparison (the GPU's own generation, errors carried from layer to
+# layer) has no bar of its own on the pages; its bar here is the sum of the
+# components' own errors measured in the same test (each layer and the head on
+# the oracle's inputs): errors that each later component passes on at unit gain
+# add up at most to that sum (triangle inequality).
 
 def test_q4_13b_width_two_layer_stack_prompt512_vs_oracle():
     """Full-width layers of the 40-layer 13B 4-bit stack (dim 5120, 40 heads, ffn
-    13824, vocab 32000, a 512-token prompt) at a depth the oracle can run.
-
-    Per component: each GPU block and the GPU head run on the oracle's own input
-    activations (inputs flow from the oracle to the GPU, never back) and must match
-    the oracle's outputs to 1e-2.  Chained: the GPU's own generation is compared with
-    the oracle's by the margin rule; its logits error is reported, bounded by
-    n_layers + 1 times the per-component bar (errors of chained bf16 blocks add up).
-    """
+    13824, vocab 32000, a 512-token prompt) chained two deep.  Per component:
+    each GPU block (prompt pass and 4 decode steps) and the head on the oracle's
+    inputs, each within 1e-2.  Chained: the GPU's own generation (4 steps),
+    teacher-forced at every step, ids by the margin rule."""
     base = W.get("q4_llama13b_stack40_prompt512_greedy128")
     wl = base.replace(n_layers=2, decode_steps=4)
     _flush("case: 13B-width 4-bit stack, 2 layers, prompt 512, 4 steps")
     max_seq = 520
     s, ids, layers_np, head, blocks, stack, keep = _build(wl, max_seq)
-    P = ids.size
-    # oracle chain over the prompt
-    xs = [ref.embed(head["embedding"], ids)]
-    for w in layers_np:
-        xs.append(ref.stack_arrays(ref.block_forward(xs[-1], w, s), "y"))
-    o_logits = ref.lm_head_logits(xs[-1][0, -1], head["norm"], s.eps, head["output"])
-    # each GPU block on the oracle's input of that layer
-    for l, blk in enumerate(blocks):
-        cache = G.make_cache(s, 1, 1, max_seq)
-        sc = G.scratch(blk, P, 1, max_seq)
-        xd = G.tdev(xs[l][0], "bf16")
-        y = torch.empty_like(xd)
-        blk.prefill(cache, 0, xd, y, 1, P, sc)
-        torch.cuda.synchronize()
-        err = G.check("bf16", G.thost(y), xs[l + 1][0], f"layer {l} output on the oracle's input")
-        _flush(f"  layer {l}: rel L2 {err:.2e}")
-    # the GPU head on the oracle's last hidden row
-    hw = keep[2]
-    lh = L.llama_linear(hw["w"].data_ptr(), hw["scales"].data_ptr(), hw["biases"].data_ptr())
-    lg = torch.empty((1, wl.vocab), device="cuda", dtype=torch.float32)
-    gid = torch.empty(1, device="cuda", dtype=torch.int32)
-    hsc = torch.empty(L.llama_head_scratch_bytes(1, s.dim, wl.vocab), dtype=torch.uint8, device="cuda")
-    xl = G.tdev(xs[-1][0, -1:], "bf16")
-    L.llama_lm_head_argmax(lh, L.LLAMA_W_Q4, 64, L.LLAMA_BF16, keep[1], s.eps, xl, 1, s.dim, wl.vocab, lg, gid,
-                           hsc, hsc.numel())
-    torch.cuda.synchronize()
-    err = G.check("bf16", lg.cpu().numpy()[0], o_logits, "head logits on the oracle's input")
-    _flush(f"  head: rel L2 {err:.2e}")
-    # chained GPU generation vs the oracle's own generation
     g_ids, g_log, _ = _generate(stack, s, wl, ids, 4, True, max_seq)
-    orc = ref.greedy_generate(ids, layers_np, head, s, steps=4)
-    chained = G.rel_l2(g_log[0], orc["logits"][0])
-    _flush(f"  chained prompt-pass logits rel L2 {chained:.2e}")
-    assert chained <= (wl.n_layers + 1) * 1e-2
-    n = _compare_greedy(g_ids, g_log, orc, tol=(wl.n_layers + 1) * 1e-2)
-    _flush(f"  ids equal to the oracle's for {n} of 5 steps")
-    assert n >= 1
+    st = {"xs": [], "ks": [], "vs": []}
+    o_log = _teacher_forced(ids, g_ids, layers_np, head, s, record=_recorder(st, wl.n_layers))
+    errs = _layer_errors(blocks, s, st["xs"], st["ks"], st["vs"], wl.seq_len, max_seq, 4)
+    for l, e in enumerate(errs):
+        for k in ("prefill", "cache", "decode"):
+            assert e[k] <= 1e-2, f"layer {l} {k}: {e[k]:.3e}"
+    h_ids, h_log = _head_logits(keep, s, wl.vocab, st["xs"][-1][wl.seq_len - 1:wl.seq_len + 4])
+    hd, hn, he = _check_ids(h_ids, h_log, o_log, 1e-2, "head on the oracle's rows")
+    bar = sum(max(e["prefill"], e["decode"]) for e in errs) + he
+    dec, near, worst = _check_ids(g_ids, g_log, o_log, bar, "2-layer chain")
+    _flush(f"  components: layers {[round(max(e['prefill'], e['decode']), 5) for e in errs]}, head {he:.2e}")
+    _flush(f"  5 of 5 steps checked: {dec} decided by the margin, {near} near-ties; worst chained logits rel L2 "
+           f"{worst:.2e} (bar: the components' sum {bar:.2e})")
 
 
-def test_q4_13b_stack40_full_generation_properties():
-    """The full workload (40 layers, 512-token prompt, 128 greedy steps): graph and
-    eager launches agree bit for bit, ids are the argmax of the returned logits,
-    and every logit is finite."""
+# --------------------------------------------------------------------------
+# The full workload: 40 layers, a 512-token prompt, 128 greedy steps.
+# --------------------------------------------------------------------------
+_C5 = {}
+
+
+def _c5():
+    """GPU generation of the full workload plus the oracle's teacher-forced pass
+    over the 640 tokens (prompt + the GPU's ids): every layer's input, the keys
+    and values it caches, and the logits of all 129 steps.  Computed once per
+    session (the oracle pass dominates: 40 dequantized layers over 640 tokens)."""
+    if _C5:
+        return _C5
     wl = W.get("q4_llama13b_stack40_prompt512_greedy128")
-    _flush("case: 40-layer 4-bit stack, prompt 512, 128 steps")
     max_seq = wl.seq_len + wl.decode_steps
+    _flush("case: 40-layer 4-bit stack, prompt 512, 128 steps: GPU generation, then the oracle's pass")
     s, ids, layers_np, head, blocks, stack, keep = _build(wl, max_seq)
-    del layers_np
     g_ids, g_log, cache = _generate(stack, s, wl, ids, wl.decode_steps, True, max_seq)
     e_ids, e_log, _ = _generate(stack, s, wl, ids, wl.decode_steps, False, max_seq)
-    assert np.isfinite(g_log).all()
-    assert np.array_equal(g_ids, e_ids) and np.array_equal(g_log, e_log)
-    assert ((g_ids >= 0) & (g_ids < wl.vocab)).all()
-    for t in range(wl.decode_steps + 1):
-        assert g_ids[t] == ref.argmax_first(g_log[t])
-    assert cache.get_lens(wl.n_layers - 1, 1) == [max_seq]
+    st = {"xs": [], "ks": [], "vs": []}
+    o_log = _teacher_forced(ids, g_ids, layers_np, head, s, record=_recorder(st, wl.n_layers))
+    _C5.update(wl=wl, s=s, ids=ids, blocks=blocks, stack=stack, keep=keep, g_ids=g_ids, g_log=g_log,
+               e_ids=e_ids, e_log=e_log, cache=cache, o_log=o_log, max_seq=max_seq, **st)
+    return _C5
+
+
+def _c5_layers():
+    c = _c5()
+    if "layer_errors" not in c:
+        c["layer_errors"] = _layer_errors(c["blocks"], c["s"], c["xs"], c["ks"], c["vs"], c["wl"].seq_len,
+                                          c["max_seq"], 4)
+    return c["layer_errors"]
+
+
+def _c5_head():
+    c = _c5()
+    if "head" not in c:
+        P, n1 = c["wl"].seq_len, c["wl"].decode_steps + 1
+        c["head"] = _head_logits(c["keep"], c["s"], c["wl"].vocab, c["xs"][-1][P - 1:P - 1 + n1])
+    return c["head"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _release_c5():
+    yield
+    _C5.clear()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_q4_13b_stack40_full_generation_properties():
+    """Graph replay and eager launches agree bit for bit, every logit is finite,
+    the lengths are right."""
+    c = _c5()
+    wl = c["wl"]
+    assert np.isfinite(c["g_log"]).all()
+    assert np.array_equal(c["g_ids"], c["e_ids"]) and np.array_equal(c["g_log"], c["e_log"])
+    assert ((c["g_ids"] >= 0) & (c["g_ids"] < wl.vocab)).all()
+    assert c["cache"].get_lens(wl.n_layers - 1, 1) == [c["max_seq"]]
+
+
+@pytest.mark.timeout(900)
+def test_q4_13b_stack40_every_layer_on_oracle_input():
+    """Each of the 40 GPU blocks on the oracle's own input of that layer: the
+    512-token prompt pass (every row, and the keys and values it caches) and 4
+    decode steps against the oracle's keys and values, each within 1e-2."""
+    errs = _c5_layers()
+    P = _c5()["wl"].seq_len
+    for l, e in enumerate(errs):
+        for k in ("prefill", "cache", "decode"):
+            assert e[k] <= 1e-2, f"layer {l} {k}: {e[k]:.3e}"
+        assert e["lens"] == P + 4
+    worst = {k: max(e[k] for e in errs) for k in ("prefill", "row", "cache", "decode")}
+    _flush("  worst over 40 layers: " + ", ".join(f"{k} {v:.2e}" for k, v in worst.items()))
+
+
+@pytest.mark.timeout(900)
+def test_q4_13b_stack40_head_on_oracle_input():
+    """The GPU's final norm, 4-bit output head and argmax on the oracle's last
+    hidden rows of all 129 steps: logits within 1e-2, ids by the margin rule."""
+    c = _c5()
+    gid, lg = _c5_head()
+    dec, near, worst = _check_ids(gid, lg, c["o_log"], 1e-2, "head")
+    _flush(f"  head on the oracle's rows: {dec} of {len(gid)} decided by the margin, {near} near-ties; "
+           f"worst logits rel L2 {worst:.2e}")
+
+
+@pytest.mark.timeout(900)
+def test_q4_13b_stack40_ids_teacher_forced_every_step():
+    """All 129 emitted ids against the oracle, teacher-forced on the GPU's ids:
+    the margin rule at every step.  The chained logits (40 bf16 blocks deep)
+    stay within the sum of the 41 components' own errors."""
+    c = _c5()
+    errs = _c5_layers()
+    gid, lg = _c5_head()
+    he = max(G.rel_l2(lg[t], c["o_log"][t]) for t in range(len(gid)))
+    bar = sum(max(e["prefill"], e["decode"]) for e in errs) + he
+    dec, near, worst = _check_ids(c["g_ids"], c["g_log"], c["o_log"], bar, "40-layer chain")
+    _flush(f"  129 of 129 steps checked: {dec} decided by the margin, {near} near-ties; "
+           f"worst chained logits rel L2 {worst:.2e} (bar: the components' sum {bar:.2e})")
