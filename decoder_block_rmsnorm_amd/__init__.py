@@ -90,6 +90,12 @@ def llama_block_prefill(blk, cache, layer, x, y, batch, seq_len, scratch, scratc
                                      scratch_bytes, _stream(stream)))
 
 
+def llama_block_prefill_ragged(blk, cache, layer, x, y, batch, seq_lens_host: Sequence[int], scratch, scratch_bytes,
+                               stream=None) -> None:
+    _check(lib().llama_block_prefill_ragged(blk, cache, layer, _ptr(x), _ptr(y), batch, _i32_array(seq_lens_host),
+                                            _ptr(scratch), scratch_bytes, _stream(stream)))
+
+
 def llama_block_decode(blk, cache, layer, x, y, batch, scratch, scratch_bytes, stream=None) -> None:
     _check(lib().llama_block_decode(blk, cache, layer, _ptr(x), _ptr(y), batch, _ptr(scratch), scratch_bytes,
                                     _stream(stream)))
@@ -203,6 +209,10 @@ def llama_stack_generate_recompute(st, cache, prompt, prompt_len, n_steps, ids_o
                                                 _ptr(logits_out), _ptr(scratch), scratch_bytes, _stream(stream)))
 
 
+def llama_probe_mfma_bf16(blocks: int, iters: int, sink, stream=None) -> None:
+    _check(lib().llama_probe_mfma_bf16(blocks, iters, _ptr(sink), _stream(stream)))
+
+
 def llama_last_error() -> str:
     return (lib().llama_last_error() or b"").decode()
 
@@ -250,6 +260,12 @@ class Block:
 
     def prefill(self, cache: "KVCache", layer: int, x, y, batch: int, seq_len: int, scratch, stream=None) -> None:
         llama_block_prefill(self.handle, cache.handle, layer, x, y, batch, seq_len, scratch, scratch.numel(), stream)
+
+    def prefill_ragged(self, cache: "KVCache", layer: int, x, y, seq_lens: Sequence[int], scratch,
+                       stream=None) -> None:
+        """x, y: [sum(seq_lens), dim], sequence b's new tokens packed after those of 0 .. b-1."""
+        llama_block_prefill_ragged(self.handle, cache.handle, layer, x, y, len(seq_lens), seq_lens, scratch,
+                                   scratch.numel(), stream)
 
     def decode(self, cache: "KVCache", layer: int, x, y, batch: int, scratch, stream=None) -> None:
         llama_block_decode(self.handle, cache.handle, layer, x, y, batch, scratch, scratch.numel(), stream)

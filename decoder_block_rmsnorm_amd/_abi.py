@@ -49,6 +49,7 @@ SIGNATURES = {
     "llama_block_destroy": (None, [P]),
     "llama_scratch_bytes": (SZ, [C.POINTER(llama_block_config), I32, I32, I32]),
     "llama_block_prefill": (I32, [P, P, I32, P, P, I32, I32, P, SZ, P]),
+    "llama_block_prefill_ragged": (I32, [P, P, I32, P, P, I32, PI32, P, SZ, P]),
     "llama_block_decode": (I32, [P, P, I32, P, P, I32, P, SZ, P]),
     "llama_block_diag": (I32, [P, P, I32, I32, PP]),
     "llama_block_set_diag": (I32, [P, I32]),
@@ -72,6 +73,7 @@ SIGNATURES = {
     "llama_stack_scratch_bytes": (SZ, [P, I32, I32]),
     "llama_stack_generate": (I32, [P, P, P, I32, I32, P, P, P, SZ, I32, P]),
     "llama_stack_generate_recompute": (I32, [P, P, P, I32, I32, P, P, P, SZ, P]),
+    "llama_probe_mfma_bf16": (I32, [I32, I32, P, P]),
     "llama_last_error": (C.c_char_p, []),
 }
 

@@ -437,6 +437,8 @@ static KVView kv_view(const llama_kvcache* c, int layer) {
   v.pps = c->pps;
   v.tiled = c->cfg.dtype == LLAMA_BF16 && c->cfg.head_dim == 128;
   v.window = 0;
+  v.cu = nullptr;
+  v.n_seq = 0;
   return v;
 }
 
@@ -512,7 +514,7 @@ static bool q4_single(const Dims& d, int T, bool decode) {
 }
 
 struct SLayout {
-  size_t inv1, inv2, ssx, ssh, q, attn, h, g, ffn, part, ao, aml, xh, xsum, deq, a16, total;
+  size_t inv1, inv2, ssx, ssh, q, attn, h, g, ffn, part, ao, aml, xh, xsum, deq, a16, cu, total;
   int n_splits, split_len, ks_qkv, nb_h;
 };
 
@@ -577,6 +579,8 @@ static SLayout scratch_layout(const llama_block_config& c, const Dims& d, int T,
   L.deq = off; off = align256(off + deq);
   // 4-bit prompt pass: fp16 copy of a GEMM's A
   L.a16 = off; off = align256(off + ((d.q4 && !decode) ? (size_t)T * maxK * 2 : 0));
+  // a ragged prefill's first row of each sequence (B + 1 entries)
+  L.cu = off; off = align256(off + (decode ? 0 : (size_t)(B + 1) * 4));
   L.total = off;
   return L;
 }
@@ -646,9 +650,10 @@ extern "C" llama_status llama_block_set_diag(llama_block* blk, int32_t enable) {
 }
 
 // ---------------------------------------------------------------- block calls
+// Ls (ragged prefill): new tokens of each sequence, each >= 0; else L each.
 static llama_status check_call(const llama_block* blk, const llama_kvcache* c, int layer, const void* x, const void* y,
-                               int batch, int L, void* scratch, size_t sbytes, bool decode, int split_min,
-                               SLayout* lay) {
+                               int batch, int L, const int32_t* Ls, void* scratch, size_t sbytes, bool decode,
+                               int split_min, SLayout* lay) {
   if (!blk || !c) return fail(LLAMA_ERR_INVALID_ARG, "block and cache must be non-NULL");
   if (!x || !y || !scratch) return fail(LLAMA_ERR_INVALID_ARG, "x, y and scratch must be non-NULL");
   if (((uintptr_t)scratch) & 255) return fail(LLAMA_ERR_INVALID_ARG, "scratch must be 256-byte aligned");
@@ -656,7 +661,18 @@ static llama_status check_call(const llama_block* blk, const llama_kvcache* c, i
   if (layer < 0 || layer >= c->cfg.n_layers) return fail(LLAMA_ERR_INVALID_ARG, "layer %d out of range", layer);
   if (batch <= 0 || batch > c->cfg.max_batch)
     return fail(LLAMA_ERR_INVALID_ARG, "batch %d outside 1..%d", batch, c->cfg.max_batch);
-  if (L <= 0) return fail(LLAMA_ERR_INVALID_ARG, "seq_len must be positive");
+  long T = 0;
+  if (Ls) {
+    for (int b = 0; b < batch; ++b) {
+      if (Ls[b] < 0) return fail(LLAMA_ERR_INVALID_ARG, "seq_lens[%d] = %d is negative", b, Ls[b]);
+      T += Ls[b];
+    }
+    if (T <= 0) return fail(LLAMA_ERR_INVALID_ARG, "seq_lens are all 0: no tokens to prefill");
+  } else {
+    if (L <= 0) return fail(LLAMA_ERR_INVALID_ARG, "seq_len must be positive");
+    T = (long)batch * L;
+  }
+  if (T > (1L << 30)) return fail(LLAMA_ERR_UNSUPPORTED, "%ld tokens in one call", T);
   if (c->cfg.n_kv_heads != d.G || c->cfg.head_dim != d.d || c->cfg.dtype != blk->cfg.act_dtype)
     return fail(LLAMA_ERR_INVALID_ARG, "cache (kv heads %d, head_dim %d, dtype %d) does not match the block",
                 c->cfg.n_kv_heads, c->cfg.head_dim, c->cfg.dtype);
@@ -665,12 +681,12 @@ static llama_status check_call(const llama_block* blk, const llama_kvcache* c, i
   const int cap = std::min(c->cfg.max_seq, blk->cfg.max_seq);
   int maxlen = 0;
   for (int b = 0; b < batch; ++b) {
-    int len = c->lens_host[(size_t)layer * c->cfg.max_batch + b];
-    if ((long)len + L > cap)
-      return fail(LLAMA_ERR_CAPACITY, "sequence %d: %d cached + %d new exceeds capacity %d", b, len, L, cap);
-    maxlen = std::max(maxlen, len + L);
+    const int len = c->lens_host[(size_t)layer * c->cfg.max_batch + b], n = Ls ? Ls[b] : L;
+    if ((long)len + n > cap)
+      return fail(LLAMA_ERR_CAPACITY, "sequence %d: %d cached + %d new exceeds capacity %d", b, len, n, cap);
+    maxlen = std::max(maxlen, len + n);
   }
-  SLayout lo = scratch_layout(blk->cfg, d, batch * L, batch, c->cfg.max_seq, decode, split_min);
+  SLayout lo = scratch_layout(blk->cfg, d, (int)T, batch, c->cfg.max_seq, decode, split_min);
   if (sbytes < lo.total) return fail(LLAMA_ERR_CAPACITY, "scratch too small: %zu < %zu bytes", sbytes, lo.total);
   // (a sliding window: the splits cover the window, from its start rounded
   // down to a 64-key step)
@@ -682,11 +698,11 @@ static llama_status check_call(const llama_block* blk, const llama_kvcache* c, i
   return LLAMA_OK;
 }
 
+// M rows; L rows per sequence, or (ragged, kv.cu set) the most of any sequence
 template <typename T>
-static void fp32_path(const llama_block* blk, KVView kv, const void* x, void* y, int B, int L, char* sc,
+static void fp32_path(const llama_block* blk, KVView kv, const void* x, void* y, int B, int L, int M, char* sc,
                       const SLayout& S, Marker& mk, hipStream_t s) {
   const Dims& d = blk->dm;
-  const int M = B * L;
   float* inv1 = (float*)(sc + S.inv1);
   T* q = (T*)(sc + S.q);
   T* attn = (T*)(sc + S.attn);
@@ -703,7 +719,7 @@ static void fp32_path(const llama_block* blk, KVView kv, const void* x, void* y,
   st1.inv = inv1;
   launch_epi_qkv<T>(part, 1, M, d.Nq, d.Nkv, st1, L, blk->rope, blk->cfg.rope_traditional, q, kv, s);
   mk(s);
-  launch_attn_simt<T>(q, kv, B, L, d.H, d.G, d.d, attn, s);
+  launch_attn_simt<T>(q, kv, M, L, d.H, d.G, d.d, attn, s);
   mk(s);
   launch_gemm_simt<T>(attn, (const T*)blk->o.w, part, M, d.D, d.Nq, s);
   mk(s);
@@ -718,14 +734,14 @@ static void fp32_path(const llama_block* blk, KVView kv, const void* x, void* y,
   mk(s);
   launch_gemm_simt<T>(g, (const T*)blk->w2.w, part, M, d.D, d.F, s);
   mk(s);
-  launch_epi_resid<T>(part, 1, M, d.D, h, (T*)y, nullptr, kv.lens, L, B, blk->diag ? (T*)(sc + S.ffn) : nullptr, s);
+  launch_epi_resid<T>(part, 1, M, d.D, h, (T*)y, nullptr, kv.lens, L, B, blk->diag ? (T*)(sc + S.ffn) : nullptr, s,
+                      kv.cu);
   mk(s);
 }
 
-static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void* y, int B, int L, char* sc,
+static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void* y, int B, int L, int M, char* sc,
                          const SLayout& S, Marker& mk, hipStream_t s) {
   const Dims& d = blk->dm;
-  const int M = B * L;
   float* inv1 = (float*)(sc + S.inv1);
   float* inv2 = (float*)(sc + S.inv2);
   bf16_t* q = (bf16_t*)(sc + S.q);
@@ -780,9 +796,10 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
     if (ks > 1) {
       g.C = part; g.ksplit = ks;
       launch_gemm_mfma(EPI_F32, g, s);
-      launch_epi_resid<bf16_t>(part, ks, M, d.D, resid, out, nullptr, lens_add, lens_inc, B, branch, s);
+      launch_epi_resid<bf16_t>(part, ks, M, d.D, resid, out, nullptr, lens_add, lens_inc, B, branch, s, kv.cu);
     } else {
       g.resid = resid; g.out = out; g.lens_add = lens_add; g.lens_inc = lens_inc; g.n_seq = B; g.branch = branch;
+      g.lens_cu = kv.cu;
       launch_gemm_mfma(EPI_RESID, g, s);
     }
   };
@@ -907,16 +924,32 @@ static void bf16_decode(const llama_block* blk, KVView kv, const void* x, void* 
 // Enqueue one block call.  n_splits_override > 0 fixes the decode attention
 // grid, with splits of kSplitLen keys (graph capture, where lengths grow
 // between replays).
+// Ls (prefill only, may be null): a ragged call's new tokens per sequence.
 static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const void* x, void* y, int batch, int L,
                             void* scratch, size_t sbytes, bool decode, int n_splits_override, int split_len_override,
-                            hipStream_t s) {
+                            hipStream_t s, const int32_t* Ls = nullptr) {
   SLayout S;
-  llama_status st = check_call(blk, c, layer, x, y, batch, L, scratch, sbytes, decode,
+  llama_status st = check_call(blk, c, layer, x, y, batch, L, Ls, scratch, sbytes, decode,
                                n_splits_override > 0 ? split_len_override : kSplitLen, &S);
   if (st != LLAMA_OK) return st;
   KVView kv = kv_view(c, layer);
   kv.window = blk->cfg.sliding_window;
   char* sc = (char*)scratch;
+  int M = batch * L;
+  if (Ls) {
+    // the rows' sequence map goes to the device with the call (in a kernel's
+    // arguments, so nothing on the host has to outlive the call)
+    std::vector<int32_t> cu(batch + 1, 0);
+    L = 0;
+    for (int b = 0; b < batch; ++b) {
+      cu[b + 1] = cu[b] + Ls[b];
+      L = std::max(L, (int)Ls[b]);
+    }
+    M = cu[batch];
+    kv.cu = (const int32_t*)(sc + S.cu);
+    kv.n_seq = batch;
+    launch_set_i32(cu.data(), batch + 1, (int32_t*)(sc + S.cu), s);
+  }
   const Dims& d = blk->dm;
   Marker mk;
   if (blk->prof_calls < blk->prof_max) {
@@ -928,9 +961,9 @@ static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const
     if (mk.mask != 0 && (mk.mask & (mk.mask - 1)) == 0 && (mk.mask & clockable)) mk.clocked = __builtin_ctz(mk.mask);
   }
   if (!d.bf16) {
-    fp32_path<float>(blk, kv, x, y, batch, L, sc, S, mk, s);
+    fp32_path<float>(blk, kv, x, y, batch, L, M, sc, S, mk, s);
   } else if (!decode) {
-    bf16_prefill(blk, kv, x, y, batch, L, sc, S, mk, s);
+    bf16_prefill(blk, kv, x, y, batch, L, M, sc, S, mk, s);
   } else {
     if (n_splits_override > 0) bf16_decode(blk, kv, x, y, batch, sc, S, n_splits_override, split_len_override, mk, s);
     else bf16_decode(blk, kv, x, y, batch, sc, S, S.n_splits, S.split_len, mk, s);
@@ -939,13 +972,21 @@ static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const
   g_clock = LaunchClock{};
   st = hip_check(decode ? "block decode" : "block prefill");
   if (st != LLAMA_OK) return st;
-  for (int b = 0; b < batch; ++b) c->lens_host[(size_t)layer * c->cfg.max_batch + b] += L;
+  for (int b = 0; b < batch; ++b) c->lens_host[(size_t)layer * c->cfg.max_batch + b] += Ls ? Ls[b] : L;
   return LLAMA_OK;
 }
 
 extern "C" llama_status llama_block_prefill(llama_block* blk, llama_kvcache* c, int32_t layer, const void* x, void* y,
                                             int32_t batch, int32_t seq_len, void* scratch, size_t sbytes, void* stream) {
   return enqueue(blk, c, layer, x, y, batch, seq_len, scratch, sbytes, false, 0, 0, (hipStream_t)stream);
+}
+
+extern "C" llama_status llama_block_prefill_ragged(llama_block* blk, llama_kvcache* c, int32_t layer, const void* x,
+                                                   void* y, int32_t batch, const int32_t* seq_lens, void* scratch,
+                                                   size_t sbytes, void* stream) {
+  if (!seq_lens) return fail(LLAMA_ERR_INVALID_ARG, "seq_lens must be non-NULL");
+  if (batch > kMaxSetI32 - 1) return fail(LLAMA_ERR_UNSUPPORTED, "ragged prefill of more than %d sequences", kMaxSetI32 - 1);
+  return enqueue(blk, c, layer, x, y, batch, 1, scratch, sbytes, false, 0, 0, (hipStream_t)stream, seq_lens);
 }
 
 extern "C" llama_status llama_block_decode(llama_block* blk, llama_kvcache* c, int32_t layer, const void* x, void* y,

@@ -92,6 +92,25 @@ struct KVView {
   int32_t G, d, ps, pps;
   int32_t tiled;        // bf16 / d = 128 operand-order layout (see above)
   int32_t window;       // sliding window: keys pos - window + 1 .. pos (0 = all keys up to pos)
+  // The rows of a prefill call: a ragged call (sequences bringing different
+  // numbers of new tokens) gives cu[b] = first row of sequence b, for b <=
+  // n_seq (cu[n_seq] = rows of the call); otherwise cu is null and every
+  // sequence has L rows.
+  const int32_t* cu;
+  int32_t n_seq;
+  __device__ inline int first_row(int b, int L) const { return cu ? cu[b] : b * L; }
+  __device__ inline int rows_of(int b, int L) const { return cu ? cu[b + 1] - cu[b] : L; }
+  // the sequence row r belongs to (for a ragged call: the b with cu[b] <= r < cu[b + 1])
+  __device__ inline int seq_of_row(int r, int L) const {
+    if (!cu) return r / L;
+    int lo = 0, hi = n_seq;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cu[mid] <= r) lo = mid;
+      else hi = mid;
+    }
+    return lo;
+  }
   __device__ __host__ inline size_t page_base(int b, int pos) const {
     int page = table[(size_t)b * pps + pos / ps];
     return (size_t)page * G * ps * d;

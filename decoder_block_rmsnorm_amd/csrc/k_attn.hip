@@ -25,14 +25,14 @@ namespace lb {
 // generic (fp32 path)
 // ===========================================================================
 template <typename T>
-__global__ __launch_bounds__(256) void k_attn_simt(const T* q, KVView kv, int B, int L, int H, int G, int d,
+__global__ __launch_bounds__(256) void k_attn_simt(const T* q, KVView kv, int M, int L, int H, int G, int d,
                                                    T* out) {
   int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   int lane = threadIdx.x & 63;
-  if (wid >= B * L * H) return;
+  if (wid >= M * H) return;
   int h = wid % H;
   int m = wid / H;
-  int b = m / L, l = m % L;
+  int b = kv.seq_of_row(m, L), l = m - kv.first_row(b, L);
   int g = h / (H / G);
   int pos = kv.lens[b] + l;
   const T* qr = q + (size_t)m * H * d + (size_t)h * d;
@@ -63,10 +63,10 @@ __global__ __launch_bounds__(256) void k_attn_simt(const T* q, KVView kv, int B,
 }
 
 template <typename T>
-void launch_attn_simt(const T* q, KVView kv, int B, int L, int H, int G, int d, T* out, hipStream_t s) {
-  int waves = B * L * H;
+void launch_attn_simt(const T* q, KVView kv, int M, int L, int H, int G, int d, T* out, hipStream_t s) {
+  int waves = M * H;
   if (waves <= 0) return;
-  hipLaunchKernelGGL(k_attn_simt<T>, dim3((waves + 3) / 4), dim3(256), 0, s, q, kv, B, L, H, G, d, out);
+  hipLaunchKernelGGL(k_attn_simt<T>, dim3((waves + 3) / 4), dim3(256), 0, s, q, kv, M, L, H, G, d, out);
 }
 
 template void launch_attn_simt<float>(const float*, KVView, int, int, int, int, int, float*, hipStream_t);
@@ -103,6 +103,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int g = h / (H / G);
+  // (a ragged call: this sequence's own count of new tokens and first row)
+  const int row0 = kv.first_row(b, L);
+  L = kv.rows_of(b, L);
   for (int pass = 0; pass < 2; ++pass) {
   // unpaired: one tile per block, heavy (late) query tiles first
   const int qt = !paired ? n_qt - 1 - (int)blockIdx.z : pass == 0 ? n_qt - 1 - (int)blockIdx.z : (int)blockIdx.z;
@@ -112,6 +115,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
   const int l32 = lane & 31, hg = lane >> 5;
   const int S = kv.lens[b];               // tokens cached before this call
   const int q_first = qt * BQ;            // first query index (within the new tokens)
+  if (q_first >= L) break;                // (a shorter sequence of a ragged call: no queries here)
   const int wq0 = q_first + wave * 32;    // this wave's first query
   const int nq_valid = L - q_first;       // queries of this block that exist
   const int kmax_block = S + min(q_first + BQ, L);   // keys [0, kmax_block)
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
   bf16x8 qf[8];
   {
     const bool ok = my_q < L;
-    const bf16_t* qrow = q + ((size_t)(b * L + (ok ? my_q : 0)) * H + h) * D;
+    const bf16_t* qrow = q + ((size_t)(row0 + (ok ? my_q : 0)) * H + h) * D;
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       uint4 v = ok ? ld16(qrow + 16 * kc + 8 * hg) : make_uint4(0, 0, 0, 0);
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
   // write O[q][d] = O^T / l : lane holds q = l32, d = 32*ds + 8*(i/4) + 4*hg + i%4
   if (my_q < L) {
     const float inv = 1.0f / l_run;
-    bf16_t* orow = out + ((size_t)(b * L + my_q) * H + h) * D;
+    bf16_t* orow = out + ((size_t)(row0 + my_q) * H + h) * D;
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds)
 #pragma unroll

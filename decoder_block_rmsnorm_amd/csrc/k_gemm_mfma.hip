@@ -450,8 +450,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     for (int r = tid; r < BM; r += NT) {
       const int row = m0 + r;
       if (row < M) {
-        const int bseq = row / a.L;
-        const int pos = a.kv.lens[bseq] + (row - bseq * a.L);
+        const int bseq = a.kv.seq_of_row(row, a.L);
+        const int pos = a.kv.lens[bseq] + (row - a.kv.first_row(bseq, a.L));
         s_pos[r] = pos;
         s_page[r] = (long long)a.kv.page_base(bseq, pos);
       }
@@ -630,7 +630,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     });
   }
   if constexpr (EPI == EPI_RESID) {
-    if (a.lens_add && blockIdx.x == 0 && tid < a.n_seq) a.lens_add[tid] += a.lens_inc;
+    if (a.lens_add && blockIdx.x == 0 && tid < a.n_seq)
+      a.lens_add[tid] += a.lens_cu ? a.lens_cu[tid + 1] - a.lens_cu[tid] : a.lens_inc;
   }
 }
 

@@ -345,6 +345,21 @@ void launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s) {
   hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, s, p, n, v);
 }
 
+struct I32Vals {
+  int32_t n;
+  int32_t v[kMaxSetI32];
+};
+__global__ __launch_bounds__(256) void k_set_i32(I32Vals a, int32_t* dst) {
+  for (int i = threadIdx.x; i < a.n; i += 256) dst[i] = a.v[i];
+}
+void launch_set_i32(const int32_t* vals, int n, int32_t* dst, hipStream_t s) {
+  if (n <= 0) return;
+  I32Vals a{};
+  a.n = n < kMaxSetI32 ? n : kMaxSetI32;
+  for (int i = 0; i < a.n; ++i) a.v[i] = vals[i];
+  hipLaunchKernelGGL(k_set_i32, dim3(1), dim3(256), 0, s, a, dst);
+}
+
 // ---------------------------------------------------------------------------
 // Weight repacking (runs once at block creation).
 // ---------------------------------------------------------------------------

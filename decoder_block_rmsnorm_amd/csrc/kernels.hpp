@@ -75,6 +75,10 @@ void launch_kv_write(KVView kv, int seq, int pos0, int n, const T* k, const T* v
 template <typename T>
 void launch_kv_read(KVView kv, int seq, int pos0, int n, T* k, T* v, hipStream_t s);
 void launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
+// dst[0 .. n) = vals[0 .. n) (host values, n <= kMaxSetI32), carried in the
+// kernel's arguments: no host buffer has to outlive the call
+constexpr int kMaxSetI32 = 257;
+void launch_set_i32(const int32_t* vals, int n, int32_t* dst, hipStream_t s);
 void launch_fill_strided_i32(int32_t* p, int n, int stride, int32_t v, hipStream_t s);
 // Row repack.  Source row r first moves inside its head when perm_d > 0
 // (local index j -> j/2 for even j, perm_d/2 + j/2 for odd j: interleaved pairs
@@ -120,7 +124,7 @@ struct GemmArgs {
   const float* inv_rms;
   // EPI_QKV
   bf16_t* q_out;          // [M, Nq]
-  int Nq, Nkv, L;         // row m = b * L + l
+  int Nq, Nkv, L;         // row m = b * L + l (or the ragged rows of kv.cu)
   const float2* rope;     // [max_seq][64] (cos, sin)
   int traditional;
   KVView kv;
@@ -129,8 +133,9 @@ struct GemmArgs {
   // EPI_RESID
   const bf16_t* resid;    // [M, N]
   bf16_t* out;            // [M, N]
-  int32_t* lens_add;      // if non-null: lens_add[b] += lens_inc for b < n_seq (block 0)
-  int lens_inc, n_seq;
+  int32_t* lens_add;      // if non-null: lens_add[b] += lens_inc for b < n_seq (block 0),
+  int lens_inc, n_seq;    // or += lens_cu[b + 1] - lens_cu[b] when lens_cu is set
+  const int32_t* lens_cu;
   bf16_t* branch;         // if non-null: the product before the residual add [M, N]
 };
 void launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t s);
@@ -213,9 +218,12 @@ void launch_epi_qkv(const float* part, int ks, int M, int Nq, int Nkv, RowStat s
                     const float2* rope, int traditional, T* q_out, KVView kv, hipStream_t s);
 // out = resid + sum(part); ss_out (optional): per-256-column-block sums of squares of
 // the stored rows, [ceil(N/256)][M] (a RowStat source for the next RMSNorm).
+// lens_add (optional): lens_add[b] += lens_inc, or lens_cu[b + 1] - lens_cu[b]
+// when lens_cu is given, for b < n_seq.
 template <typename T>
 void launch_epi_resid(const float* part, int ks, int M, int N, const T* resid, T* out, float* ss_out,
-                      int32_t* lens_add, int lens_inc, int n_seq, T* branch, hipStream_t s);
+                      int32_t* lens_add, int lens_inc, int n_seq, T* branch, hipStream_t s,
+                      const int32_t* lens_cu = nullptr);
 template <typename T>
 void launch_epi_swiglu(const float* part, int ks, int M, int F2, int ib, RowStat stat, T* g_out,
                        hipStream_t s);
@@ -224,10 +232,12 @@ void launch_reduce_f32(const float* part, int ks, int M, int N, float* out, hipS
 
 // ---------------------------------------------------------------- k_attn.hip
 // generic causal attention over the paged cache (fp32 path):
-// q [T, H*d] with row m = b*L + l at position lens_before[b] + l; out [T, H*d]
+// q [M, H*d] with row m = b*L + l (or the ragged rows of kv.cu) at position
+// lens_before[b] + l; out [M, H*d]
 template <typename T>
-void launch_attn_simt(const T* q, KVView kv, int B, int L, int H, int G, int d, T* out, hipStream_t s);
-// bf16 flash prefill (d = 128)
+void launch_attn_simt(const T* q, KVView kv, int M, int L, int H, int G, int d, T* out, hipStream_t s);
+// bf16 flash prefill (d = 128); L = new tokens per sequence, or the most of any
+// sequence of a ragged call (kv.cu)
 void launch_attn_prefill_bf16(const bf16_t* q, KVView kv, int B, int L, int H, int G, bf16_t* out,
                               hipStream_t s);
 // bf16 split-K decode (d = 128): one token per sequence at position lens[b] (already appended)

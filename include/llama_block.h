@@ -131,6 +131,26 @@ llama_status llama_block_prefill(llama_block* blk, llama_kvcache* cache, int32_t
                                  void* y, int32_t batch, int32_t seq_len, void* scratch,
                                  size_t scratch_bytes, void* stream);
 
+/* Ragged prefill: the sequences of one call bring different numbers of new
+ * tokens (a chunked prefill of several prompts at once).  The position of a new
+ * token is the number of tokens its sequence has cached plus its index
+ * ("2. 注意力机制" on the MLX page: RoPE offset = cache length, new keys and
+ * values appended), so every sequence continues from its own lens[layer][b].
+ *   seq_lens_host: int32 [batch] host array, seq_lens_host[b] >= 0 new tokens of
+ *   sequence b (0 = the sequence is left untouched); T = their sum, T > 0.
+ *   x, y = act_dtype [T, dim] device buffers (y may alias x), packed: sequence
+ *   b's tokens are rows off_b .. off_b + seq_lens_host[b] - 1, with off_b the sum
+ *   of the counts before b.
+ * Token l of sequence b sits at position lens[layer][b] + l, attends causally to
+ * every cached key up to its position, and lens[layer][b] grows by
+ * seq_lens_host[b].  The call reads seq_lens_host before it returns.
+ * Errors: LLAMA_ERR_INVALID_ARG for a NULL seq_lens_host, a negative count or a
+ * zero total; LLAMA_ERR_CAPACITY if some lens + count exceeds max_seq or the
+ * scratch is smaller than llama_scratch_bytes(cfg, T, batch, max_seq). */
+llama_status llama_block_prefill_ragged(llama_block* blk, llama_kvcache* cache, int32_t layer, const void* x,
+                                        void* y, int32_t batch, const int32_t* seq_lens_host, void* scratch,
+                                        size_t scratch_bytes, void* stream);
+
 /* Decode: x, y = act_dtype [batch, dim] (y may alias x); sequence b's token sits
  * at position lens[layer][b], attends to keys 0 .. lens[layer][b] and is
  * appended; lens[layer][b] grows by 1.  Same errors as prefill. */
@@ -298,6 +318,17 @@ llama_status llama_stack_generate_recompute(llama_stack* st, llama_kvcache* cach
                                             int32_t prompt_len, int32_t n_steps, int32_t* ids_out_dev,
                                             float* logits_out_dev, void* scratch, size_t scratch_bytes,
                                             void* stream);
+
+/* ------------------------------------------------------ measurement aid */
+
+/* Not part of the block: a loop of bf16 matrix-core instructions on register
+ * operands (no memory traffic), `blocks` workgroups of 4 wavefronts, each
+ * wavefront issuing 8 * iters v_mfma_f32_32x32x16_bf16 (32768 flops each), to
+ * time the rate the matrix cores sustain on this part beside the published
+ * peak.  sink_dev: fp32 [blocks * 256] device buffer that receives the
+ * accumulator sums (so the loop is not optimised away).  Errors:
+ * LLAMA_ERR_INVALID_ARG for blocks or iters <= 0 or a NULL sink. */
+llama_status llama_probe_mfma_bf16(int32_t blocks, int32_t iters, float* sink_dev, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* llama_last_error(void);

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import decoder_block_rmsnorm_amd as L
 import workloads as W
 from oracle import ref
 from tests import gpu_util as G
@@ -400,3 +401,109 @@ def test_q4_prefill():
     r = _oracle(s, w, x)
     G.check("bf16", y, np.stack(r["y"]), "y")
     _check_branches(s, blk, sc, r, y, 1, 150)
+
+
+# ------------------------------------------------ ragged prefill (chunked) --
+# Sequences of one call bring different numbers of new tokens: each continues
+# from its own cached length (RoPE offset = cache length, "2. 注意力机制" on the
+# MLX page).  Two calls: the first from empty caches (one sequence brings no
+# token), the second continuing every sequence (one brings 0, one brings 1, the
+# others tails off the 128-query and 64-key tiles).
+RAGGED = {
+    "bf16_gqa": SMALL_GQA,
+    "bf16_mha_interleaved": dataclasses.replace(SMALL_MHA, traditional=True),
+    "bf16_gqa_window": dataclasses.replace(SMALL_GQA, window=100),
+    "q4": SMALL_Q4,
+    "f32_gqa": W.BlockShape(dim=256, n_heads=4, n_kv_heads=2, ffn_dim=688, dtype="f32", traditional=True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RAGGED))
+def test_ragged_prefill_two_calls(name):
+    s = RAGGED[name]
+    rng = W.Rng(51)
+    w = W.draw_block_weights(s, rng)
+    first, second = [0, 37, 130, 5, 64], [200, 1, 0, 129, 70]
+    B = len(first)
+    max_seq = max(a + b for a, b in zip(first, second)) + 3
+    xs = [[rng.normal((1, n, s.dim), 1.0, s.dtype) for n in call] for call in (first, second)]
+    _flush(f"case: ragged prefill {name}: counts {first} then {second}")
+    blk, wd = G.make_block(s, w, max_seq)
+    cache = G.make_cache(s, 1, B, max_seq)
+    sc = G.scratch(blk, max(sum(first), sum(second)), B, max_seq)
+    blk.set_diag(True)
+    dt = "f32" if s.dtype == "f32" else "bf16"
+    cdt = torch.float32 if s.dtype == "f32" else torch.bfloat16
+    kc = [np.zeros((0, s.n_kv_heads, s.head_dim)) for _ in range(B)]
+    vc = [np.zeros((0, s.n_kv_heads, s.head_dim)) for _ in range(B)]
+    before = None
+    for c, call in enumerate((first, second)):
+        x = np.concatenate([a[0] for a in xs[c]])
+        T = x.shape[0]
+        xd = G.tdev(x, s.dtype)
+        y = torch.empty_like(xd)
+        blk.prefill_ragged(cache, 0, xd, y, call, sc)
+        torch.cuda.synchronize()
+        got = {"y": G.thost(y), "attn": G.diag(blk, sc, 0, T, s.n_heads * s.head_dim, s.dtype),
+               "h": G.diag(blk, sc, 1, T, s.dim, s.dtype), "ffn": G.diag(blk, sc, 2, T, s.dim, s.dtype)}
+        exp = {k: [] for k in got}
+        for b in range(B):
+            if call[b] == 0:
+                continue
+            r = ref.block_forward(xs[c][b], w, s, [kc[b]], [vc[b]])
+            for k in got:
+                exp[k].append(r[k][0])
+            kc[b] = np.concatenate([kc[b], r["k_new"][0]])
+            vc[b] = np.concatenate([vc[b], r["v_new"][0]])
+        for k in got:
+            G.check(dt, got[k], np.concatenate(exp[k]), f"call {c} {k}")
+        # every sequence on its own too
+        off = 0
+        for b in range(B):
+            if call[b]:
+                r_y = exp["y"][sum(1 for j in range(b) if call[j])]
+                G.check(dt, got["y"][off:off + call[b]], r_y, f"call {c} sequence {b} y")
+            off += call[b]
+        assert cache.get_lens(0, B) == [sum(cl[b] for cl in (first, second)[:c + 1]) for b in range(B)]
+        # the cache holds every position the oracle produced
+        reads = []
+        for b in range(B):
+            n = kc[b].shape[0]
+            if n == 0:
+                reads.append(None)
+                continue
+            kd = torch.empty((n, s.n_kv_heads, s.head_dim), device="cuda", dtype=cdt)
+            vd = torch.empty_like(kd)
+            cache.read(0, b, 0, n, kd, vd)
+            torch.cuda.synchronize()
+            G.check(dt, G.thost(kd), kc[b], f"call {c} cache K seq {b}")
+            G.check(dt, G.thost(vd), vc[b], f"call {c} cache V seq {b}")
+            reads.append((G.thost(kd), G.thost(vd)))
+        if c == 0:
+            before = reads
+        else:
+            # the sequence that brought no token kept its cache bit for bit
+            assert np.array_equal(reads[2][0], before[2][0]) and np.array_equal(reads[2][1], before[2][1])
+
+
+def test_ragged_prefill_argument_errors_leave_cache_unchanged():
+    s = SMALL_GQA
+    rng = W.Rng(52)
+    w = W.draw_block_weights(s, rng)
+    _flush("case: ragged prefill argument errors")
+    blk, wd = G.make_block(s, w, 64)
+    cache = G.make_cache(s, 1, 3, 64)
+    sc = G.scratch(blk, 128, 3, 64)
+    x = G.tdev(rng.normal((100, s.dim), 1.0, "bf16"), "bf16")
+    for counts, status in (([5, -1, 2], L.LLAMA_ERR_INVALID_ARG), ([0, 0, 0], L.LLAMA_ERR_INVALID_ARG),
+                           ([10, 65, 0], L.LLAMA_ERR_CAPACITY)):
+        with pytest.raises(L.LlamaError) as e:
+            blk.prefill_ragged(cache, 0, x, x, counts, sc)
+        assert e.value.status == status
+        assert cache.get_lens(0, 3) == [0, 0, 0]
+    blk.prefill_ragged(cache, 0, x, x, [10, 64, 0], sc)      # fills sequence 1 to capacity
+    torch.cuda.synchronize()
+    assert cache.get_lens(0, 3) == [10, 64, 0]
+    with pytest.raises(L.LlamaError) as e:
+        blk.prefill_ragged(cache, 0, x, x, [1, 1, 1], sc)
+    assert e.value.status == L.LLAMA_ERR_CAPACITY and cache.get_lens(0, 3) == [10, 64, 0]
