@@ -2,20 +2,27 @@
 // (A = activations, B = repacked nn.Linear weights, both K-contiguous), fp32
 // accumulation on v_mfma_f32_32x32x16_bf16, with the block's element-wise work
 // fused into the epilogue so no fp32 intermediate reaches HBM:
-//   EPI_F32    : plain fp32 store;
+//   EPI_F32    : plain fp32 store (split-K partials);
 //   EPI_QKV    : RMSNorm row scale (gamma is folded into the weights), RoPE on
 //                q and k, q to a [M, Nq] buffer, k and v appended to the pages;
 //   EPI_SWIGLU : RMSNorm row scale, silu(w1 n) * (w3 n) on interleaved columns;
 //   EPI_RESID  : residual add (wo and w2).
 //
-// Tiling: BM x BN block tile (BM, BN in {128, 256}), K step 64, four wavefronts,
-// each owning a (BM / WM) x 128 tile so that one wavefront always holds whole
-// 128-wide heads (the RoPE partner columns i and i + 64 sit in the same lane).
-// Global -> registers -> LDS with the next K step prefetched during the MFMAs;
-// LDS rows padded to 72 bf16 (144 B) against bank conflicts; two LDS buffers,
-// one barrier per K step.  Blocks are renumbered XCD-major and walked in
-// GROUP_M-row bands so that co-resident blocks of one XCD share A and B tiles
-// in that XCD's L2.
+// Main path (DEPTH 0; every bf16 prefill GEMM whose N is a multiple of 256):
+// a 256 x 256 (or 128 x 256) block tile, four wavefronts, each owning a
+// (BM / 2) x 128 tile so that one wavefront always holds whole 128-wide heads
+// (the RoPE partner columns i and i + 64 sit in the same lane).  A and B stream
+// global -> LDS with direct loads (global_load_lds_dwordx4, no register
+// staging) into a four-stage ring of 32-wide K steps; the LDS image is laid out
+// in 16-row x 32-column blocks of 1 KB (the tiled weight format), so every
+// direct load of a wavefront fills one contiguous kilobyte and fragment reads
+// have no bank conflicts.  One load or fragment read is slotted after each
+// MFMA, with one barrier per K step.  Blocks are renumbered XCD-major and
+// walked in GROUP_M-row bands so that co-resident blocks of one XCD share A and
+// B tiles in that XCD's L2.
+// Other paths (DEPTH 1/2, register-staged 64-wide K steps through two padded
+// LDS buffers): split-K partials, N not a multiple of 256, and row-major fp16
+// B operands (4-bit weights dequantized for shapes the tiled layout misses).
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>

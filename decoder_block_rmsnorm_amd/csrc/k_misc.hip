@@ -136,18 +136,19 @@ void launch_argmax(const float* logits, int rows, int vocab, int32_t* ids, hipSt
 // Sampled next id ("生成过程", MLX page: a multinomial draw from
 // softmax(logits / T) when T > 0; LLaMA.generate, page 二: limited to the
 // nucleus, the most probable tokens up to and including the first at which
-// their cumulative probability exceeds top_p).  One block per row, 256 threads.
-//   e_i = 2^((z_i - max) * log2(e) / T), recomputed by the same instructions in
-//   every pass (so every pass sees the same values; no scratch);
+// their cumulative probability exceeds top_p).  One block per row, 1024 threads.
+//   e_i = 2^((z_i - max) * log2(e) / T), kept in LDS up to kSampleLds tokens,
+//   else recomputed by the same instructions in every pass (so every pass sees
+//   the same values; no scratch);
 //   nucleus: the kept tokens are e_i >= thr, thr = the largest e value whose
 //   tail mass (the sum of all e_j >= it) exceeds top_p * sum(e), found by
 //   bisection over the bit patterns of positive floats (ordered like their
 //   values); tokens tied with it are kept;
 //   draw: the first index, in vocabulary order, at which the cumulative kept
 //   mass exceeds u * (kept mass), u = u[*u_off or row].  Each thread sums one
-//   contiguous 1/256 of the row, one thread turns the 256 sums into prefixes
-//   in order, so the chunks' intervals [prefix, next prefix) tile [0, total)
-//   exactly and one chunk holds the crossing.
+//   contiguous 1/1024 of the row, the first wavefront chains the 1024 sums
+//   into prefixes in order, so the chunks' intervals [prefix, next prefix) tile
+//   [0, total) and one chunk holds the crossing.
 // ---------------------------------------------------------------------------
 constexpr int kSampleThreads = 1024;
 constexpr int kSampleLds = 36864;   // e values kept in LDS (144 KB) up to this vocabulary

@@ -197,7 +197,11 @@ llama_status llama_block_profile_read(llama_block* blk, float* phase_ms, int32_t
 
 /* ------------------------------------------------------------------ cache */
 
-/* Paged KV cache: per layer a pool of pages; page p of layer l holds, for every
+/* The KV cache of "2. 注意力机制" (MLX page): per layer, the rotated keys and the
+ * values of every position a sequence has seen, new positions appended at the
+ * end (the position offset of a new token is the cache's length).  Here it is
+ * preallocated and paged instead of concatenated.
+ * Paged KV cache: per layer a pool of pages; page p of layer l holds, for every
  * kv head g, page_size positions of keys as [g][slot][head_dim] and of values
  * transposed as [g][head_dim][slot].  A block table [max_batch][pages_per_seq]
  * (pages_per_seq = ceil(max_seq / page_size)) maps a sequence's logical page to
