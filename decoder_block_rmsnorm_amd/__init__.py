@@ -101,6 +101,10 @@ def llama_block_decode(blk, cache, layer, x, y, batch, scratch, scratch_bytes, s
                                     _stream(stream)))
 
 
+def llama_block_decode_noalloc(blk, cache, layer, x, y, batch, stream=None) -> None:
+    _check(lib().llama_block_decode_noalloc(blk, cache, layer, _ptr(x), _ptr(y), batch, _stream(stream)))
+
+
 def llama_block_diag(blk, scratch, which: int, tokens: int) -> int:
     out = C.c_void_p()
     _check(lib().llama_block_diag(blk, _ptr(scratch), which, tokens, C.byref(out)))

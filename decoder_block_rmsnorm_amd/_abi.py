@@ -51,6 +51,7 @@ SIGNATURES = {
     "llama_block_prefill": (I32, [P, P, I32, P, P, I32, I32, P, SZ, P]),
     "llama_block_prefill_ragged": (I32, [P, P, I32, P, P, I32, PI32, P, SZ, P]),
     "llama_block_decode": (I32, [P, P, I32, P, P, I32, P, SZ, P]),
+    "llama_block_decode_noalloc": (I32, [P, P, I32, P, P, I32, P]),
     "llama_block_diag": (I32, [P, P, I32, I32, PP]),
     "llama_block_set_diag": (I32, [P, I32]),
     "llama_block_profile_start": (I32, [P, I32, C.c_uint32]),

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -992,6 +993,54 @@ extern "C" llama_status llama_block_prefill_ragged(llama_block* blk, llama_kvcac
 extern "C" llama_status llama_block_decode(llama_block* blk, llama_kvcache* c, int32_t layer, const void* x, void* y,
                                            int32_t batch, void* scratch, size_t sbytes, void* stream) {
   return enqueue(blk, c, layer, x, y, batch, 1, scratch, sbytes, true, 0, 0, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------- decode without allocation
+// The transient values of llama_block_decode_noalloc live in this file-scope
+// device array instead of a caller's scratch buffer.  Every device the library
+// runs on holds its own copy from the code object's load until the process
+// ends.  In host code `scratch` names a host-side stand-in, not device memory:
+// host code uses only the address hipGetSymbolAddress returns for the current
+// device (noalloc_scratch below).  Nothing in a decode reads scratch before the
+// same call wrote it, so it needs no clearing between calls.
+static constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+static constexpr int kMaxDevices = 64;
+static void* g_noalloc_ptr[kMaxDevices];
+static std::mutex g_noalloc_mu;
+
+// Device address of `scratch` on the current device, looked up once per device.
+static llama_status noalloc_scratch(void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev), "no-allocation decode: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LLAMA_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "no-allocation decode: hipGetSymbolAddress");
+    if (!p) return fail(LLAMA_ERR_HIP, "no-allocation decode: no device address for the scratch array");
+    g_noalloc_ptr[dev] = p;
+  }
+  *out = g_noalloc_ptr[dev];
+  return LLAMA_OK;
+}
+
+extern "C" llama_status llama_block_decode_noalloc(llama_block* blk, llama_kvcache* c, int32_t layer, const void* x,
+                                                   void* y, int32_t batch, void* stream) {
+  if (!blk || !c) return fail(LLAMA_ERR_INVALID_ARG, "block and cache must be non-NULL");
+  if (batch > 0) {
+    const size_t need = scratch_layout(blk->cfg, blk->dm, batch, batch, c->cfg.max_seq, true).total;
+    if (need > kNoAllocScratchBytes)
+      return fail(LLAMA_ERR_CAPACITY,
+                  "no-allocation decode: %d sequences against a %d-position cache need %zu bytes of scratch, "
+                  "more than its fixed %zu bytes (use llama_block_decode with a scratch buffer)",
+                  batch, c->cfg.max_seq, need, kNoAllocScratchBytes);
+  }
+  void* sc = nullptr;
+  llama_status st = noalloc_scratch(&sc);
+  if (st != LLAMA_OK) return st;
+  return enqueue(blk, c, layer, x, y, batch, 1, sc, kNoAllocScratchBytes, true, 0, 0, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------- stack ends

@@ -158,6 +158,21 @@ llama_status llama_block_decode(llama_block* blk, llama_kvcache* cache, int32_t 
                                 void* y, int32_t batch, void* scratch, size_t scratch_bytes,
                                 void* stream);
 
+/* Decode without a scratch buffer, for callers that cannot allocate device
+ * memory (code under HIP graph capture, fixed serving loops, harnesses that
+ * forbid allocation): the same computation, kernels and results as
+ * llama_block_decode, with its transient values in a fixed 64 MiB array that
+ * the library keeps on each device it runs on until the process ends.  Every
+ * call on a device shares that device's array: calls that overlap on one device
+ * (concurrent streams, threads) race and must be ordered by the caller.  No
+ * allocation happens inside the call.  Same arguments (minus the scratch) and
+ * errors as llama_block_decode, plus LLAMA_ERR_CAPACITY when the call would need
+ * more than the 64 MiB (about: 64 sequences of a dim-8192 block against a
+ * 4.2k-position cache fit; llama_scratch_bytes(cfg, 0, batch, max_seq) gives the
+ * need). */
+llama_status llama_block_decode_noalloc(llama_block* blk, llama_kvcache* cache, int32_t layer, const void* x,
+                                        void* y, int32_t batch, void* stream);
+
 /* Diagnostics: after a prefill/decode call with the same token count and
  * scratch, points *ptr at a transient of that call inside scratch:
  *   LLAMA_DIAG_ATTN = attention output before wo, act_dtype [tokens, n_heads*head_dim];
