@@ -301,52 +301,70 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     for (int i = 0; i < BG; ++i) vob[i] = (uint32_t)(((wv * BG + i) * kTileElems + lane * 8) * 2);
     const char* abase = (const char*)Ag;
     const char* bbase = (const char*)Btile;
-    // direct load number idx (0 .. LPS-1) of step kt: 32-column block
+    // The loads of step t come from two wave-uniform global bases (A and B of
+    // that step) and land in stage t % STG.  Past the last step the global
+    // bases stay at the last step (the data then lands in a stage no later
+    // step reads), so every step issues the same loads: the wait counts below
+    // are constants and no branch sits between the MFMAs.
+    struct StepAddr {
+      const char* ga;
+      const char* gb;
+      uint32_t la;
+    };
+    auto step_addr = [&](int t) {
+      const int tc = min(t, KT - 1);
+      return StepAddr{abase + (size_t)(tc * BKS) * 2, bbase + tblk(kslice0 + tc * BKS) * 2,
+                      lds_base + (uint32_t)((t % STG) * (SA + SB)) * 2};
+    };
+    // direct load number idx (0 .. LPS-1) of a step: 32-column block
     // idx / (AG + BG); inside a block, A and B groups alternate while both
-    // last (A on even numbers), then the remaining B groups
-    auto issue_one = [&](int kt, int idx) {
-      const uint32_t la = lds_base + (uint32_t)((kt % STG) * (SA + SB)) * 2;
+    // last (A on even numbers), then the remaining B groups.  (A 32-wide K step
+    // starting on a multiple of 64 keeps the next 32 columns in the same
+    // 256-column chunk: B 1 KB further, A 64 bytes.)
+    auto issue_at = [&](const StepAddr& sa, int idx) {
       const int kb = idx / (AG + BG), q = idx % (AG + BG);
       const bool is_a = q < 2 * AG && (q & 1) == 0;
       const int i = q < 2 * AG ? q >> 1 : q - AG;
       if (is_a)
-        lds_dma16(voa[i], abase + (size_t)(kt * BKS + kb * 32) * 2, la + (kb * (BM / 16) + wv * AG + i) * 1024);
+        lds_dma16(voa[i], sa.ga + kb * 64, sa.la + (kb * (BM / 16) + wv * AG + i) * 1024);
       else
-        lds_dma16(vob[i], bbase + tblk(kslice0 + kt * BKS + kb * 32) * 2, la + SA * 2 + (kb * 16 + wv * BG + i) * 1024);
+        lds_dma16(vob[i], sa.gb + kb * 1024, sa.la + SA * 2 + (kb * 16 + wv * BG + i) * 1024);
     };
     // lane's piece inside a pair of groups: fragment rows 32t + l%32, k = 8*(l/32)
     const int fpiece = (16 * (lane >> 5) + r16) * 8 + ((lane >> 4) & 1) * 512;
-    // fragment read number q (0 .. MI+3): A tile q, or B tile q - MI
-    auto lfrag_one = [&](int st, int kk, int q, uint4(&a_)[MI], uint4(&b_)[4]) {
+    // Fragment reads go in the order A0, B0, B1, B2, B3, A1 .. A(MI-1), the
+    // order the MFMAs of a sub-step first need them (MFMA q takes A q/4, B q%4).
+    // Read number r (0 .. MI+3): A0 at 0, B j at 1 + j, A i at 4 + i.
+    auto lfrag_one = [&](int st, int kk, int r, uint4(&a_)[MI], uint4(&b_)[4]) {
       const bf16_t* la = lds + st * (SA + SB) + fpiece + (kk & 1) * 256;
-      if (q < MI) a_[q] = ld16(la + (kk >> 1) * (BM / 16) * 512 + (wm * (WTM / 16) + 2 * q) * 512);
-      else b_[q - MI] = ld16(la + SA + (kk >> 1) * 16 * 512 + (wn * 8 + 2 * (q - MI)) * 512);
-    };
-    // wait until this wavefront's loads of step t have landed, given the steps
-    // issued up to step `last`
-    auto wait_step = [&](int t, int last) {
-      const int later = max(0, min(STG - 1, last - t));
-      if constexpr (STG > 4) {
-        if (later >= 4) return wait_vmcnt<4 * LPS>();
-      }
-      if constexpr (STG > 3) {
-        if (later >= 3) return wait_vmcnt<3 * LPS>();
-      }
-      if constexpr (STG > 2) {
-        if (later >= 2) return wait_vmcnt<2 * LPS>();
-      }
-      if (later >= 1) return wait_vmcnt<LPS>();
-      wait_vmcnt<0>();
+      const bool is_a = r == 0 || r > 4;
+      const int i = r == 0 ? 0 : r - 4, j = r - 1;
+      if (is_a) a_[i] = ld16(la + (kk >> 1) * (BM / 16) * 512 + (wm * (WTM / 16) + 2 * i) * 512);
+      else b_[j] = ld16(la + SA + (kk >> 1) * 16 * 512 + (wn * 8 + 2 * j) * 512);
     };
     constexpr int NF = MI + 4;                 // fragment reads per sub-step
     constexpr int NM = MI * 4;                 // MFMAs per sub-step
     static_assert(NM >= NF, "interleave slots");
+    // Before MFMA q of a sub-step whose slots issue the next sub-step's reads:
+    // its two fragments (read during the previous sub-step) must have landed,
+    // while the reads after them and the min(q, NF) reads this sub-step has
+    // issued so far may still be in flight (LDS reads complete in order).
+    auto frag_wait = [](auto qc) {
+      constexpr int q = decltype(qc)::value;
+      constexpr int ra = q / 4 == 0 ? 0 : 4 + q / 4, rb = 1 + q % 4;
+      constexpr int need = ra > rb ? ra : rb;
+      constexpr int later = (NF - 1 - need) + (q < NF ? q : NF);
+      static_assert(later >= 0 && later < 16, "lgkm count");
+      __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (later << 8) | (3 << 14));
+    };
     // The MFMAs of one sub-step, with one other instruction slotted in after
     // each: while an MFMA runs the wavefront issues the next load, so the
-    // matrix core is never left waiting on an issue.
-    auto mfmas_with = [&](const uint4(&a_)[MI], const uint4(&b_)[4], auto&& slot) {
+    // matrix core is never left waiting on an issue.  STAGGER: each MFMA waits
+    // only for its own fragments (else the caller waited for all of them).
+    auto mfmas_with = [&](const uint4(&a_)[MI], const uint4(&b_)[4], auto&& slot, auto stagger) {
       static_for<0, NM>([&](auto qc) {
         constexpr int q = decltype(qc)::value;
+        if constexpr (decltype(stagger)::value) frag_wait(qc);
         if constexpr (F16)
           acc[q / 4][q % 4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(u4_as_f16x8(a_[q / 4]), u4_as_f16x8(b_[q % 4]),
                                                                      acc[q / 4][q % 4], 0, 0, 0);
@@ -359,54 +377,63 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     };
     uint4 fa[2][MI], fb[2][4];
 #pragma unroll
-    for (int t = 0; t < STG; ++t)
-      if (t < KT) {
+    for (int t = 0; t < STG; ++t) {
+      const StepAddr sa = step_addr(t);
 #pragma unroll
-        for (int idx = 0; idx < LPS; ++idx) issue_one(t, idx);
-      }
-    int last = min(STG, KT) - 1;
-    wait_step(0, last);
+      for (int idx = 0; idx < LPS; ++idx) issue_at(sa, idx);
+    }
+    // step 0 landed: the other STG - 1 steps may still be in flight
+    wait_vmcnt<(STG - 1) * LPS>();
     asm volatile("s_barrier" ::: "memory");
     // nothing but LDS reads may be pending on the lgkm counter inside the loop
     // (a scalar load in flight would force every fragment wait to lgkmcnt(0))
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
     for (int q = 0; q < NF; ++q) lfrag_one(0, 0, q, fa[0], fb[0]);
-    for (int kt = 0; kt < KT; ++kt) {
+    // A sub-step before the last of step kt: its fragments were read during
+    // the previous sub-step, and each MFMA waits for its own; its slots read the
+    // next sub-step's.
+    auto sub_first = [&](int kt, auto kc) {
+      constexpr int kk = decltype(kc)::value;
+      constexpr int cur = kk & 1;
       const int st = kt % STG;
-      static_for<0, NKK>([&](auto kc) {
-        constexpr int kk = decltype(kc)::value;
-        constexpr int cur = kk & 1;
-        // this sub-step's fragments were read during the previous one
-        __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (kk + 1 < NKK) {
-          mfmas_with(fa[cur], fb[cur], [&](int slot) {
-            if (slot < NF) lfrag_one(st, kk + 1, slot, fa[cur ^ 1], fb[cur ^ 1]);
-          });
-        } else {
-          // (after the last step this waits for nothing and reads an unused
-          // stage; kept unconditional so the reads stay in one straight line)
-          wait_step(kt + 1, last);
-          // this stage's fragment reads are complete (waited above); barrier:
-          // every wavefront is done with stage st, and step kt+1 has landed
-          asm volatile("s_barrier" ::: "memory");
-          const bool refill = kt + STG < KT;
-          const int nxt = (kt + 1) % STG;
-          __builtin_amdgcn_sched_barrier(0);
-          // slots: fragment reads of step kt+1 first (needed soonest), then the
-          // direct loads of step kt+STG into stage st
-          mfmas_with(fa[cur], fb[cur], [&](int slot) {
-            if (slot < NF) lfrag_one(nxt, 0, slot, fa[cur ^ 1], fb[cur ^ 1]);
-            else if (refill && slot - NF < LPS) issue_one(kt + STG, slot - NF);
-          });
-          if (refill) {
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas_with(fa[cur], fb[cur], [&](int slot) {
+        if (slot < NF) lfrag_one(st, kk + 1, slot, fa[cur ^ 1], fb[cur ^ 1]);
+      }, std::true_type{});
+    };
+    // The last sub-step of step kt: every read of stage st completes before the
+    // barrier that lets the other wavefronts refill it, and step kt+1 has
+    // landed (steps kt+2 .. kt+STG-1 may still be in flight; after the last
+    // step this waits for nothing and reads an unused stage, kept unconditional
+    // so the reads stay in one straight line).  Its slots read step kt+1's first
+    // fragments, then issue the direct loads of step kt+STG into stage st.
+    auto sub_last = [&](int kt) {
+      constexpr int cur = (NKK - 1) & 1;
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+      wait_vmcnt<(STG - 2) * LPS>();
+      asm volatile("s_barrier" ::: "memory");
+      const int nxt = (kt + 1) % STG;
+      const StepAddr sa = step_addr(kt + STG);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas_with(fa[cur], fb[cur], [&](int slot) {
+        if (slot < NF) lfrag_one(nxt, 0, slot, fa[cur ^ 1], fb[cur ^ 1]);
+        else if (slot - NF < LPS) issue_at(sa, slot - NF);
+      }, std::false_type{});
 #pragma unroll
-            for (int idx = NM - NF; idx < LPS; ++idx) issue_one(kt + STG, idx);
-            last = kt + STG;
-          }
-        }
-      });
+      for (int idx = NM - NF; idx < LPS; ++idx) issue_at(sa, idx);
+    };
+    // The loop body runs from one step's last sub-step into the next step's
+    // leading ones, so the staggered waits sit in straight-line code (at a loop
+    // head the compiler would merge them into a full wait).
+    static_for<0, NKK - 1>([&](auto kc) { sub_first(0, kc); });
+    for (int kt = 0; kt + 1 < KT; ++kt) {
+      sub_last(kt);
+      static_for<0, NKK - 1>([&](auto kc) { sub_first(kt + 1, kc); });
     }
+    sub_last(KT - 1);
+    // the loads issued past the last step land in LDS the epilogue reuses
+    wait_vmcnt<0>();
   } else if constexpr (DEPTH == 2) {
     const int KT = Kslice / BK;
     gload(0, ra0, rb0);
