@@ -103,6 +103,7 @@ struct Lin {            // a repacked linear inside the block's device memory
   void* w = nullptr;    // dense E[N, K] or q4 uint32 [N, K/8]
   bf16_t* s = nullptr;  // q4 scales [N, K/64]
   bf16_t* b = nullptr;  // q4 biases
+  uint32_t* pairs = nullptr;  // q4 (scale, bias) pairs [K/64][N] for the prompt-pass GEMM
   int N = 0, K = 0;
 };
 
@@ -151,7 +152,7 @@ struct Marker {
 
 struct WLayout {
   size_t rope, g1, g2, total;
-  size_t lin[4][3];  // per linear: w, s, b offsets
+  size_t lin[4][4];  // per linear: w, s, b, pairs offsets
 };
 
 static void lin_shapes(const Dims& d, int NK[4][2]) {
@@ -176,6 +177,7 @@ static WLayout weight_layout(const llama_block_config& c, const Dims& d) {
       off = align256(off + N * K / 2);
       L.lin[i][1] = off; off = align256(off + N * (K / 64) * 2);
       L.lin[i][2] = off; off = align256(off + N * (K / 64) * 2);
+      L.lin[i][3] = off; off = align256(off + N * (K / 64) * 4);
     } else if (d.bf16) {
       // tiled layout: K padded to whole 256-column chunks
       off = align256(off + N * (size_t)tiled_chunks((int)K) * kTileK * 2);
@@ -248,6 +250,7 @@ extern "C" llama_status llama_block_create(const llama_block_config* cfg, const 
     lins[i]->w = base + L.lin[i][0];
     lins[i]->s = d.q4 ? (bf16_t*)(base + L.lin[i][1]) : nullptr;
     lins[i]->b = d.q4 ? (bf16_t*)(base + L.lin[i][2]) : nullptr;
+    lins[i]->pairs = d.q4 ? (uint32_t*)(base + L.lin[i][3]) : nullptr;
     lins[i]->N = NK[i][0];
     lins[i]->K = NK[i][1];
   }
@@ -285,6 +288,8 @@ extern "C" llama_status llama_block_create(const llama_block_config* cfg, const 
     repack_linear(d, dt, b->w13, w->w1, d.F, d.D, g2, 0, d.IB, 2 * d.IB, 0, s);
     repack_linear(d, dt, b->w13, w->w3, d.F, d.D, g2, d.IB, d.IB, 2 * d.IB, 0, s);
     repack_linear(d, dt, b->w2, w->w2, d.D, d.F, nullptr, 0, big, 0, 0, s);
+    if (d.q4)
+      for (int i = 0; i < 4; ++i) launch_q4_pairs(lins[i]->s, lins[i]->b, lins[i]->N, lins[i]->K / 64, lins[i]->pairs, s);
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -752,9 +757,11 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
   _Float16* deq = (_Float16*)(sc + S.deq);
   _Float16* a16 = (_Float16*)(sc + S.a16);
   const float eps = blk->cfg.norm_eps;
-  // 4-bit weights: dequantized (gamma folded) to fp16 right before their GEMM,
-  // which then runs on fp16 MFMA; where the shape allows, B tiled and A copied
-  // to fp16 so that the GEMM takes the direct-to-LDS tiles
+  // 4-bit weights run on fp16 MFMA.  Where the shape allows, the GEMM
+  // dequantizes the codes itself and A is copied to fp16 with the norm weight
+  // applied (x * gamma, one rounding); else the weights are dequantized (gamma
+  // folded) to fp16 right before the GEMM, tiled for the direct-to-LDS tiles
+  // when A can be copied to fp16 too.
   auto operands = [&](GemmArgs& g, const bf16_t* A, const Lin& lin, const float* gamma) {
     g.A = A;
     if (!d.q4) {
@@ -762,6 +769,15 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
       return;
     }
     g.b_f16 = 1;
+    if (gemm_q4_direct_ok(M, lin.N, lin.K)) {
+      g.a_f16 = 1;
+      g.q4w = (const uint32_t*)lin.w;
+      g.q4sb = lin.pairs;
+      g.B = nullptr;
+      launch_bf16_to_f16(A, a16, (size_t)M * lin.K, s, gamma, lin.K);
+      g.A = (const bf16_t*)a16;
+      return;
+    }
     g.a_f16 = gemm_f16_direct_ok(M, lin.N, lin.K);
     launch_q4_dequant((const uint32_t*)lin.w, lin.s, lin.b, lin.N, lin.K, 64, gamma, g.a_f16, deq, s);
     g.B = (const bf16_t*)deq;

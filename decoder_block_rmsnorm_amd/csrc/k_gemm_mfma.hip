@@ -105,7 +105,11 @@ __device__ inline f16x8 u4_as_f16x8(uint4 v) {
 // (1 or 2 register sets).  DEPTH 0 (bf16 tiled B, 256 x 256, 4 wavefronts):
 // global -> LDS direct loads (global_load_lds_dwordx4) into a four-stage ring of
 // 32-wide K steps, no register staging; see the main loop below.
-template <int BM, int BN, int NW, int DEPTH, int EPI, bool F16>
+// Q4 (DEPTH 0, F16): B is 4-bit group-affine weights dequantized inside the
+// kernel: each step's codes and group scale/bias pairs come into the ring stage
+// with the A tile (direct loads), and every thread turns its row's 32 codes
+// into fp16 s * q + b in the stage's B tile one step before the MFMAs read it.
+template <int BM, int BN, int NW, int DEPTH, int EPI, bool F16, bool Q4 = false>
 __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
   using namespace gm;
   constexpr int NT = NW * 64;
@@ -282,11 +286,18 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     constexpr int STG = DEPTH == 0 ? 4 : DEPTH == 3 ? 2 : 5;   // stages
     constexpr int NKB = BKS / 32;                      // 32-column blocks per step
     constexpr int NKK = BKS / 16;                      // MFMA sub-steps per step
-    constexpr int LPS = (BM / 64 + 4) * NKB;           // direct loads per wavefront per step
+    // direct loads per wavefront per step: A and B groups, or (Q4) A groups,
+    // this wavefront's 64 rows of codes and a copy of the 256 rows' scale/bias pairs
+    constexpr int LPS = Q4 ? BM / 64 + 2 : (BM / 64 + 4) * NKB;
     static_assert((!F16 || DEPTH == 0) && NW == 4 && BN == 256 && (BM == 256 || (BM == 128 && DEPTH == 0)),
                   "direct-LDS configuration");
+    static_assert(!Q4 || (F16 && DEPTH == 0), "4-bit B: fp16 MFMA on the four-stage ring");
     constexpr int AG = BM / 64, BG = 4;                // A and B row groups each wavefront loads
     constexpr int SA = BM * BKS, SB = BN * BKS;        // bf16 per stage
+    // (Q4) per stage after the B tile: codes, 16 bytes per row; NW copies of the
+    // pairs, 4 bytes per row (in 2-byte units)
+    constexpr int SC = Q4 ? BN * 8 : 0, SS = Q4 ? NW * BN * 2 : 0;
+    constexpr int STS = SA + SB + SC + SS;             // 2-byte units per stage
     const int KT = Kslice / BKS;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int r16 = lane & 15, j4 = lane >> 4;
@@ -313,15 +324,33 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     };
     auto step_addr = [&](int t) {
       const int tc = min(t, KT - 1);
-      return StepAddr{abase + (size_t)(tc * BKS) * 2, bbase + tblk(kslice0 + tc * BKS) * 2,
-                      lds_base + (uint32_t)((t % STG) * (SA + SB)) * 2};
+      return StepAddr{abase + (size_t)(tc * BKS) * 2, Q4 ? nullptr : bbase + tblk(kslice0 + tc * BKS) * 2,
+                      lds_base + (uint32_t)((t % STG) * STS) * 2};
     };
     // direct load number idx (0 .. LPS-1) of a step: 32-column block
     // idx / (AG + BG); inside a block, A and B groups alternate while both
     // last (A on even numbers), then the remaining B groups.  (A 32-wide K step
     // starting on a multiple of 64 keeps the next 32 columns in the same
     // 256-column chunk: B 1 KB further, A 64 bytes.)
+    // (Q4) codes: lane l of wavefront w brings row n0 + 64 w + l, the 32 codes
+    // of the step (16 bytes); pairs: the group's [N] row of transposed pairs,
+    // rows n0 .. n0+255 (1 KB, 4 rows per lane)
+    const int kw = K / 8;                                    // code words per row
+    const uint32_t voc = Q4 ? (uint32_t)((n0 + 64 * wv + lane) * kw) * 4 : 0u;
+    const char* cbase = Q4 ? (const char*)a.q4w : nullptr;
+    const char* pbase = Q4 ? (const char*)(a.q4sb + n0) : nullptr;
     auto issue_at = [&](const StepAddr& sa, int idx) {
+      if constexpr (Q4) {
+        // (a step past the last one repeats the last step's loads: sa.ga)
+        const int kc = (int)((sa.ga - abase) / 2) + kslice0;   // first column of the step
+        if (idx < AG)
+          lds_dma16(voa[idx], sa.ga, sa.la + (wv * AG + idx) * 1024);
+        else if (idx == AG)
+          lds_dma16(voc, cbase + (size_t)(kc / 8) * 4, sa.la + (SA + SB) * 2 + wv * 1024);
+        else
+          lds_dma16((uint32_t)lane * 16, pbase + (size_t)(kc / 64) * a.N * 4, sa.la + (SA + SB + SC) * 2 + wv * 1024);
+        return;
+      }
       const int kb = idx / (AG + BG), q = idx % (AG + BG);
       const bool is_a = q < 2 * AG && (q & 1) == 0;
       const int i = q < 2 * AG ? q >> 1 : q - AG;
@@ -336,7 +365,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     // order the MFMAs of a sub-step first need them (MFMA q takes A q/4, B q%4).
     // Read number r (0 .. MI+3): A0 at 0, B j at 1 + j, A i at 4 + i.
     auto lfrag_one = [&](int st, int kk, int r, uint4(&a_)[MI], uint4(&b_)[4]) {
-      const bf16_t* la = lds + st * (SA + SB) + fpiece + (kk & 1) * 256;
+      const bf16_t* la = lds + st * STS + fpiece + (kk & 1) * 256;
       const bool is_a = r == 0 || r > 4;
       const int i = r == 0 ? 0 : r - 4, j = r - 1;
       if (is_a) a_[i] = ld16(la + (kk >> 1) * (BM / 16) * 512 + (wm * (WTM / 16) + 2 * i) * 512);
@@ -349,11 +378,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     // its two fragments (read during the previous sub-step) must have landed,
     // while the reads after them and the min(q, NF) reads this sub-step has
     // issued so far may still be in flight (LDS reads complete in order).
+    // (Q4: the B tile built in slot NF adds 6 LDS operations after it.)
     auto frag_wait = [](auto qc) {
       constexpr int q = decltype(qc)::value;
       constexpr int ra = q / 4 == 0 ? 0 : 4 + q / 4, rb = 1 + q % 4;
       constexpr int need = ra > rb ? ra : rb;
-      constexpr int later = (NF - 1 - need) + (q < NF ? q : NF);
+      constexpr int later = (NF - 1 - need) + (q < NF ? q : NF) + (Q4 && q > NF ? 6 : 0);
       static_assert(later >= 0 && later < 16, "lgkm count");
       __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (later << 8) | (3 << 14));
     };
@@ -375,6 +405,36 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       });
     };
+    // (Q4) B tile of step t from its codes and pairs in stage t % STG: thread
+    // tid owns row tid, whose fp16 s * q + b for columns 8j .. 8j+7 form piece
+    // 16 j + tid % 16 of the 1 KB block of row group tid / 16 (the layout of
+    // the direct-loaded tiles).  Only this wavefront's own loads are read, so
+    // its vmcnt wait suffices (no barrier).
+    auto dequant_b = [&](int t) {
+      if constexpr (Q4) {
+        const int sti = t % STG;
+        const bf16_t* sb0 = lds + sti * STS + SA + SB;
+        const uint4 cw = ld16(sb0 + tid * 8);
+        const uint32_t pr = *reinterpret_cast<const uint32_t*>(sb0 + SC + wv * 512 + tid * 2);
+        const float sc = bf16_to_f32((bf16_t)(pr & 0xffffu)), bi = bf16_to_f32((bf16_t)(pr >> 16));
+        bf16_t* dst = lds + sti * STS + SA + (tid >> 4) * 512 + (tid & 15) * 8;
+        const uint32_t w4[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const _Float16 h0 = (_Float16)__builtin_fmaf(sc, (float)((w4[j] >> (8 * e)) & 15u), bi);
+            const _Float16 h1 = (_Float16)__builtin_fmaf(sc, (float)((w4[j] >> (8 * e + 4)) & 15u), bi);
+            uint16_t u0, u1;
+            __builtin_memcpy(&u0, &h0, 2);
+            __builtin_memcpy(&u1, &h1, 2);
+            o[e] = (uint32_t)u0 | ((uint32_t)u1 << 16);
+          }
+          st16(dst + j * 128, make_uint4(o[0], o[1], o[2], o[3]));
+        }
+      }
+    };
     uint4 fa[2][MI], fb[2][4];
 #pragma unroll
     for (int t = 0; t < STG; ++t) {
@@ -382,8 +442,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
 #pragma unroll
       for (int idx = 0; idx < LPS; ++idx) issue_at(sa, idx);
     }
-    // step 0 landed: the other STG - 1 steps may still be in flight
+    // step 0 landed: the other STG - 1 steps may still be in flight; (Q4)
+    // step 0's B tile, then every wavefront's writes complete before the barrier
     wait_vmcnt<(STG - 1) * LPS>();
+    if constexpr (Q4) {
+      dequant_b(0);
+      __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    }
     asm volatile("s_barrier" ::: "memory");
     // nothing but LDS reads may be pending on the lgkm counter inside the loop
     // (a scalar load in flight would force every fragment wait to lgkmcnt(0))
@@ -392,13 +457,22 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     // A sub-step before the last of step kt: its fragments were read during
     // the previous sub-step, and each MFMA waits for its own; its slots read the
     // next sub-step's.
+    // (Q4) The first sub-step of step kt also builds the B tile of step kt+1
+    // (its stage was freed by the barrier of step kt+1-STG; the barrier of step
+    // kt's last sub-step publishes it): wait for that step's own loads (those of
+    // the STG-2 later steps may still be in flight), then dequantize in the
+    // slots after the fragment reads.
     auto sub_first = [&](int kt, auto kc) {
       constexpr int kk = decltype(kc)::value;
       constexpr int cur = kk & 1;
       const int st = kt % STG;
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (Q4 && kk == 0) wait_vmcnt<(STG - 2) * LPS>();
       mfmas_with(fa[cur], fb[cur], [&](int slot) {
         if (slot < NF) lfrag_one(st, kk + 1, slot, fa[cur ^ 1], fb[cur ^ 1]);
+        if constexpr (Q4 && kk == 0) {
+          if (slot == NF) dequant_b(kt + 1);
+        }
       }, std::true_type{});
     };
     // The last sub-step of step kt: every read of stage st completes before the
@@ -669,49 +743,40 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
   }
 }
 
-template <int BM, int BN, int NW, int DEPTH, int EPI, bool F16>
+template <int BM, int BN, int NW, int DEPTH, int EPI, bool F16, bool Q4 = false>
 static void launch_cfg(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * (a.N / BN) * (EPI == EPI_F32 && a.ksplit > 1 ? a.ksplit : 1);
-  const size_t lds = DEPTH == 4 ? (size_t)(BM + BN) * 160 * sizeof(bf16_t)
+  const size_t lds = Q4 ? (size_t)4 * ((BM + BN) * 32 + BN * 8 + NW * BN * 2) * sizeof(bf16_t)
+                     : DEPTH == 4 ? (size_t)(BM + BN) * 160 * sizeof(bf16_t)
                      : DEPTH == 0 || DEPTH == 3 ? std::max<size_t>((size_t)(BM + BN) * 128 * sizeof(bf16_t), 4096 + 4 * 17408)
                                 : (size_t)2 * (BM + BN) * gm::LDS_ST * sizeof(bf16_t);
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)k_gemm_mfma<BM, BN, NW, DEPTH, EPI, F16>,
+    (void)hipFuncSetAttribute((const void*)k_gemm_mfma<BM, BN, NW, DEPTH, EPI, F16, Q4>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_set = true;
   }
-  hipExtLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, DEPTH, EPI, F16>), dim3(tiles), dim3(NW * 64), lds, s,
+  hipExtLaunchKernelGGL((k_gemm_mfma<BM, BN, NW, DEPTH, EPI, F16, Q4>), dim3(tiles), dim3(NW * 64), lds, s,
                         g_clock.start, g_clock.stop, 0, a);
   g_clock = LaunchClock{};
 }
 
-// Tile choice; LLAMA_BLOCK_GEMM_TILE = "256x256d" (direct-to-LDS), "256x256w8",
-// "256x256w4", "128x256w4" or "128x128w4" forces one (for measurements).
-static int forced_tile() {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("LLAMA_BLOCK_GEMM_TILE");
-    v = 0;
-    if (e) {
-      if (!strcmp(e, "256x256w8")) v = 1;
-      else if (!strcmp(e, "256x256w4")) v = 2;
-      else if (!strcmp(e, "128x256w4")) v = 3;
-      else if (!strcmp(e, "128x128w4")) v = 4;
-      else if (!strcmp(e, "256x256d")) v = 5;
-      else if (!strcmp(e, "256x256d64")) v = 6;
-      else if (!strcmp(e, "256x256d5")) v = 7;
-      else if (!strcmp(e, "128x256d")) v = 8;
-    }
-  }
-  return v;
-}
-
+// Tile choice: the direct-to-LDS ring where the shape allows, 128-row tiles
+// when their rounds of 256 blocks finish sooner (half the work each, counted
+// 20% dearer: measured) than those of 256-row tiles; register-staged tiles
+// otherwise.
 template <int EPI, bool F16>
 static void launch_epi(const GemmArgs& a, hipStream_t s) {
   const bool n256 = (a.N % 256) == 0;
-  const int f = forced_tile();
   if constexpr (F16) {
+    if (a.q4w) {
+      // 4-bit B dequantized in the kernel (gemm_q4_direct_ok shapes), fp16 A
+      const long t256 = (long)((a.M + 255) / 256) * (a.N / 256), t128 = (long)((a.M + 127) / 128) * (a.N / 256);
+      const bool use128 = ((t128 + 255) / 256) * 0.6 < (double)((t256 + 255) / 256);
+      if ((EPI == EPI_F32 && a.ksplit > 1) || (t256 >= 240 && !use128))
+        return launch_cfg<256, 256, 4, 0, EPI, true, true>(a, s);
+      return launch_cfg<128, 256, 4, 0, EPI, true, true>(a, s);
+    }
     if (a.a_f16) {
       // fp16 A and tiled fp16 B (gemm_f16_direct_ok): direct-to-LDS tiles,
       // the tile height chosen as for bf16
@@ -729,20 +794,13 @@ static void launch_epi(const GemmArgs& a, hipStream_t s) {
     // work each, counted 20% dearer: measured) than those of 256-row tiles
     const long t256 = (long)((a.M + 255) / 256) * (a.N / 256), t128 = (long)((a.M + 127) / 128) * (a.N / 256);
     const bool use128 = ((t128 + 255) / 256) * 0.6 < (double)((t256 + 255) / 256);
-    if (f == 8 && a32 && n256) return launch_cfg<128, 256, 4, 0, EPI, F16>(a, s);
-    if (f == 0 && big && use128 && !(EPI == EPI_F32 && a.ksplit > 1)) return launch_cfg<128, 256, 4, 0, EPI, F16>(a, s);
-    if (f == 0 && !big && a32 && n256 && t128 >= 240 && !(EPI == EPI_F32 && a.ksplit > 1))
+    if (big && use128 && !(EPI == EPI_F32 && a.ksplit > 1)) return launch_cfg<128, 256, 4, 0, EPI, F16>(a, s);
+    if (!big && a32 && n256 && t128 >= 240 && !(EPI == EPI_F32 && a.ksplit > 1))
       return launch_cfg<128, 256, 4, 0, EPI, F16>(a, s);
-    if (f == 6 && big) return launch_cfg<256, 256, 4, 3, EPI, F16>(a, s);
-    if (f == 7 && big) return launch_cfg<256, 256, 4, 4, EPI, F16>(a, s);
-    if ((f == 0 || f == 5) && big) return launch_cfg<256, 256, 4, 0, EPI, F16>(a, s);
+    if (big) return launch_cfg<256, 256, 4, 0, EPI, F16>(a, s);
   }
   if (EPI == EPI_F32 && a.ksplit > 1) return launch_cfg<256, 256, 8, 2, EPI, F16>(a, s);
-  if (f == 1 && n256) return launch_cfg<256, 256, 8, 2, EPI, F16>(a, s);
-  if (f == 2 && n256) return launch_cfg<256, 256, 4, 1, EPI, F16>(a, s);
-  if (f == 3 && n256) return launch_cfg<128, 256, 4, 2, EPI, F16>(a, s);
-  if (f == 4) return launch_cfg<128, 128, 4, 2, EPI, F16>(a, s);
-  // default: the largest tile that still gives about one wave of blocks per CU
+  // register-staged: the largest tile that still gives about one wave of blocks per CU
   const long t256 = (long)((a.M + 255) / 256) * (a.N / 256);
   if (n256 && t256 >= 240) return launch_cfg<256, 256, 8, 2, EPI, F16>(a, s);
   if (n256) return launch_cfg<128, 256, 4, 2, EPI, F16>(a, s);
@@ -761,6 +819,10 @@ static void launch_any(int epi, const GemmArgs& a, hipStream_t s) {
 
 bool gemm_f16_direct_ok(int M, int N, int K) {
   return N % 256 == 0 && (size_t)M * K * sizeof(bf16_t) < ((size_t)1 << 32);
+}
+
+bool gemm_q4_direct_ok(int M, int N, int K) {
+  return gemm_f16_direct_ok(M, N, K) && K % 64 == 0 && (size_t)N * K / 2 < ((size_t)1 << 32);
 }
 
 int gemm_split_k(int M, int N, int K, bool b_f16) {

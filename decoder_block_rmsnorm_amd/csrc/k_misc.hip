@@ -514,16 +514,31 @@ void launch_q4_dequant(const uint32_t* words, const bf16_t* scales, const bf16_t
     hipLaunchKernelGGL(k_q4_dequant, dim3(N), dim3(256), 0, s, words, scales, biases, N, K, gs, gamma, out);
 }
 
-// fp16 copy of bf16 values, 8 per thread (n % 8 == 0; |v| < 65504 on its uses)
-__global__ __launch_bounds__(256) void k_bf16_to_f16(const bf16_t* src, _Float16* dst, size_t n8) {
+// fp16 copy of bf16 values, 8 per thread (n % 8 == 0; |v| < 65504 on its
+// uses), times gamma[column] for rows of K columns when gamma is given (the
+// RMSNorm weight of a 4-bit GEMM's input; one rounding of the exact product)
+__global__ __launch_bounds__(256) void k_bf16_to_f16(const bf16_t* src, _Float16* dst, size_t n8, const float* gamma,
+                                                     int K) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n8) return;
   const uint4 v = ld16(src + i * 8);
   const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+  float gm[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+  if (gamma) {
+    const int c0 = (int)((i * 8) % (size_t)K);   // (K % 8 == 0: the 8 values share a row)
+    const f32x4 g0 = *reinterpret_cast<const f32x4*>(gamma + c0);
+    const f32x4 g1 = *reinterpret_cast<const f32x4*>(gamma + c0 + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      gm[e] = g0[e];
+      gm[e + 4] = g1[e];
+    }
+  }
   uint32_t o[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const _Float16 lo = (_Float16)__uint_as_float(in[j] << 16), hi = (_Float16)__uint_as_float(in[j] & 0xffff0000u);
+    const _Float16 lo = (_Float16)(__uint_as_float(in[j] << 16) * gm[2 * j]);
+    const _Float16 hi = (_Float16)(__uint_as_float(in[j] & 0xffff0000u) * gm[2 * j + 1]);
     uint16_t l, h;
     __builtin_memcpy(&l, &lo, 2);
     __builtin_memcpy(&h, &hi, 2);
@@ -532,10 +547,24 @@ __global__ __launch_bounds__(256) void k_bf16_to_f16(const bf16_t* src, _Float16
   st16(dst + i * 8, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-void launch_bf16_to_f16(const bf16_t* src, _Float16* dst, size_t n, hipStream_t s) {
+void launch_bf16_to_f16(const bf16_t* src, _Float16* dst, size_t n, hipStream_t s, const float* gamma, int K) {
   const size_t n8 = n / 8;
   if (!n8) return;
-  hipLaunchKernelGGL(k_bf16_to_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, src, dst, n8);
+  hipLaunchKernelGGL(k_bf16_to_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, src, dst, n8, gamma, K);
+}
+
+// Group scale/bias pairs transposed to [G][N], one 32-bit word per (group,
+// row): the 4-bit prompt-pass GEMM loads a group's pairs for 256 rows at once.
+__global__ __launch_bounds__(256) void k_q4_pairs(const bf16_t* scales, const bf16_t* biases, int N, int G,
+                                                  uint32_t* pairs) {
+  const int n = blockIdx.x * 256 + threadIdx.x, g = blockIdx.y;
+  if (n >= N) return;
+  pairs[(size_t)g * N + n] = (uint32_t)scales[(size_t)n * G + g] | ((uint32_t)biases[(size_t)n * G + g] << 16);
+}
+
+void launch_q4_pairs(const bf16_t* scales, const bf16_t* biases, int N, int G, uint32_t* pairs, hipStream_t s) {
+  if (N <= 0 || G <= 0) return;
+  hipLaunchKernelGGL(k_q4_pairs, dim3((N + 255) / 256, G), dim3(256), 0, s, scales, biases, N, G, pairs);
 }
 
 template <typename T>

@@ -95,7 +95,11 @@ void launch_repack_bytes(uint8_t* dst, const uint8_t* src, int rows, int row_byt
 // 256 columns, zero past K)
 void launch_q4_dequant(const uint32_t* words, const bf16_t* scales, const bf16_t* biases, int N, int K,
                        int gs, const float* gamma, bool tiled, _Float16* out, hipStream_t s);
-void launch_bf16_to_f16(const bf16_t* src, _Float16* dst, size_t n, hipStream_t s);
+// dst = fp16(src), or fp16(src * gamma[column]) for rows of K columns when gamma is given
+void launch_bf16_to_f16(const bf16_t* src, _Float16* dst, size_t n, hipStream_t s, const float* gamma = nullptr,
+                        int K = 0);
+// pairs[g][n] = scales[n][g] | biases[n][g] << 16 (bf16 bit patterns), G groups per row
+void launch_q4_pairs(const bf16_t* scales, const bf16_t* biases, int N, int G, uint32_t* pairs, hipStream_t s);
 template <typename T>
 void launch_to_f32(const T* src, float* dst, int n, hipStream_t s);
 // ids_out[*cursor] = *cur_id; logits_out[*cursor] = logits (if logits_out); ++*cursor
@@ -137,6 +141,12 @@ struct GemmArgs {
   int lens_inc, n_seq;    // or += lens_cu[b + 1] - lens_cu[b] when lens_cu is set
   const int32_t* lens_cu;
   bf16_t* branch;         // if non-null: the product before the residual add [M, N]
+  // 4-bit B (with b_f16 and a_f16, gemm_q4_direct_ok shapes): B dequantized in
+  // the kernel from codes q4w [N][K/8] words (code k at bits 4*(k%8)) and group
+  // scale/bias pairs q4sb [K/64][N] (scale in the low 16 bits, bias in the
+  // high, bf16): B[n][k] = fp16(scale * code + bias); B itself is unused
+  const uint32_t* q4w;
+  const uint32_t* q4sb;
 };
 void launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t s);
 // K slices (1, 2 or 4) for an [M, N] x K product (B in fp16 when b_f16) whose
@@ -146,6 +156,8 @@ constexpr int kMaxSplitK = 4;
 int gemm_split_k(int M, int N, int K, bool b_f16);
 // shapes whose fp16 GEMM can take A fp16 and B tiled (direct-to-LDS tiles)
 bool gemm_f16_direct_ok(int M, int N, int K);
+// shapes whose fp16 GEMM can take 4-bit B dequantized in the kernel
+bool gemm_q4_direct_ok(int M, int N, int K);
 
 // ---------------------------------------------------------------- k_gemv.hip
 // partial[ks][M][N] (fp32) = X[M, kslice] * W[N, kslice]^T (bf16, M <= 64),
