@@ -336,7 +336,7 @@ __global__ __launch_bounds__(BM ? 512 : 256) __attribute__((amdgpu_waves_per_eu(
     vg = __builtin_amdgcn_readfirstlane(blockIdx.x % VG);
     b = __builtin_amdgcn_readfirstlane(blockIdx.x / VG);
   } else {
-    const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+    const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
     const int total = B * VG * n_splits;
     if (wid >= total) return;
     c = wid % n_splits;
@@ -506,7 +506,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
                                                     const float* __restrict__ part_ml, int BH, int n_splits,
                                                     bf16_t* __restrict__ out) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wid = blockIdx.x * 4 + wave;
+  const int wid = blockIdx.x * (blockDim.x >> 6) + wave;
   if (wid >= BH) return;
   const float* ml = part_ml + (size_t)wid * n_splits * 2;
   const float* po = part_o + (size_t)wid * n_splits * 128;
@@ -566,12 +566,14 @@ void launch_attn_decode_bf16(const bf16_t* q, KVView kv, int B, int H, int G, in
     g_clock = LaunchClock{};
     return;
   }
-  int waves = B * VG * n_splits;
-  hipExtLaunchKernelGGL(k_attn_decode_bf16<false>, dim3((waves + 3) / 4), dim3(256), 0, s, g_clock.start, nullptr, 0, q, kv, B, H, G, n_splits,
-                     split_len, part_o, part_ml, nullptr);
-  int bh = B * H;
-  hipExtLaunchKernelGGL(k_attn_merge, dim3((bh + 3) / 4), dim3(256), 0, s, nullptr, g_clock.stop, 0, part_o, part_ml,
-                        bh, n_splits, out);
+  // (a grid of fewer wavefronts than a round of the chip goes one wavefront
+  // per block, so the dispatcher spreads it over all compute units)
+  const int waves = B * VG * n_splits, wpb = waves < 1024 ? 1 : 4;
+  hipExtLaunchKernelGGL(k_attn_decode_bf16<false>, dim3((waves + wpb - 1) / wpb), dim3(64 * wpb), 0, s, g_clock.start,
+                        nullptr, 0, q, kv, B, H, G, n_splits, split_len, part_o, part_ml, nullptr);
+  const int bh = B * H, mpb = bh < 1024 ? 1 : 4;
+  hipExtLaunchKernelGGL(k_attn_merge, dim3((bh + mpb - 1) / mpb), dim3(64 * mpb), 0, s, nullptr, g_clock.stop, 0,
+                        part_o, part_ml, bh, n_splits, out);
   g_clock = LaunchClock{};
 }
 

@@ -525,18 +525,99 @@ __device__ inline int q4_row(const Q4Fused& e, int RB, int lr, bool& ok) {
   return (p / hd) * e.kv.d + p % hd + hi * hd;
 }
 
-template <int NI, int KP, int R, int NB, int EPI>
+// the value of lane l ^ M (M a power of two below 64): quad permutes and row
+// rotates (DPP) within 16 lanes, lane-row swaps across 16 and 32
+template <int M>
+__device__ inline float xor_lane(float v, int lane) {
+  const int b = __builtin_bit_cast(int, v);
+  if constexpr (M == 1) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  } else if constexpr (M == 2) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  } else if constexpr (M == 4) {
+    const int up = __builtin_amdgcn_update_dpp(0, b, 0x114, 0xF, 0xF, false);  // row_shr:4 (lane - 4)
+    const int dn = __builtin_amdgcn_update_dpp(0, b, 0x104, 0xF, 0xF, false);  // row_shl:4 (lane + 4)
+    return __builtin_bit_cast(float, (lane & 4) ? up : dn);
+  } else if constexpr (M == 8) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0x128, 0xF, 0xF, false));  // row_ror:8
+  } else {
+    // swap(v, v): the first result holds the partner's value in the odd
+    // 16-/32-lane rows, the second in the even ones
+    const auto p = M == 16 ? __builtin_amdgcn_permlane16_swap(b, b, false, false)
+                           : __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    return __builtin_bit_cast(float, (int)((lane & M) ? p[0] : p[1]));
+  }
+}
+
+// One step of a transposed wavefront reduction: lanes with bit M set keep the
+// rows of `hi`, the others those of `lo`, and each adds its partner's copy of
+// the rows it keeps (two row sets summed over a lane pair in one exchange).
+template <int M>
+__device__ inline float reduce_split(float lo, float hi, int lane) {
+  if constexpr (M >= 16) {
+    // vdst = lo, src = hi: afterwards the first result holds lo of the pair in
+    // the even rows and hi of the partner in the odd rows, the second the
+    // partner's lo in the even rows and hi in the odd rows
+    const auto p = M == 16 ? __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi),
+                                                              false, false)
+                           : __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi),
+                                                              false, false);
+    return __builtin_bit_cast(float, (int)p[0]) + __builtin_bit_cast(float, (int)p[1]);
+  } else {
+    const bool up = lane & M;
+    return (up ? hi : lo) + xor_lane<M>(up ? lo : hi, lane);
+  }
+}
+
+// Sums each of the wavefront's RW row accumulators over the 64 lanes: log2(RW)
+// split steps (lane bits 5, 4, ...) leave one value per lane, the remaining
+// lane bits are summed plainly.  Returns the sum of row `row` (same in every
+// lane whose low 6 - log2(RW) bits are zero).
+template <int RW>
+__device__ inline float reduce_rows(float (&v)[RW], int lane, int& row) {
+  constexpr int LG = RW == 1 ? 0 : RW == 2 ? 1 : RW == 4 ? 2 : RW == 8 ? 3 : 4;
+  static_assert((1 << LG) == RW, "rows per wavefront: a power of two up to 16");
+  static_for<0, LG>([&](auto sc) {
+    constexpr int s = decltype(sc)::value, M = 32 >> s, H = RW >> (s + 1);
+    static_for<0, H>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      v[j] = reduce_split<M>(v[j], v[j + H], lane);
+    });
+  });
+  static_for<LG, 6>([&](auto sc) {
+    constexpr int M = 32 >> decltype(sc)::value;
+    v[0] += xor_lane<M>(v[0], lane);
+  });
+  row = 0;
+#pragma unroll
+  for (int s = 0; s < LG; ++s) row += ((lane >> (5 - s)) & 1) * (RW >> (s + 1));
+  return v[0];
+}
+
+// Block: 4 wavefronts = KP K parts x NSETS = 4 / KP row sets of RW rows (RB =
+// NSETS * RW rows per block).  A wavefront's rows are unrolled at compile time:
+// the codes and scale/bias of row r + D are requested before row r is
+// multiplied (a ring of D + 1 rows in registers), so every wait is a partial
+// count and nothing is loaded past the last row.  Row bases are wave-uniform
+// (scalar); each lane's chunk offsets are fixed for all rows.  Each lane keeps
+// one partial sum per row; one transposed reduction at the end.
+template <int NI, int KP, int RW, int D, int EPI>
 __global__ __launch_bounds__(256) void k_q4_fused(const bf16_t* __restrict__ X, const uint32_t* __restrict__ words,
                                                  const bf16_t* __restrict__ scales,
                                                  const bf16_t* __restrict__ biases, Q4Fused e) {
-  constexpr int kp = KP, NSETS = 4 / KP;   // K parts, row sets (wavefronts per part)
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int NSETS = 4 / KP, RB = NSETS * RW, half = RB / 2;
+  static_assert(RB <= kQ4MaxRB, "rows per block");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = e.K, nchunk = K / 32, ngrp = K / 64;
-  const int kpi = wave % kp, rs = wave / kp;
-  const int c0 = kpi * nchunk / kp, c1 = (kpi + 1) * nchunk / kp;
-  const int rpw = e.rpw, RB = 4 * rpw / kp, half = RB >> 1;
-  const float* gamma = e.norm ? e.gamma : nullptr;
-  __shared__ float ys[4][kQ4MaxRB];
+  const int kpi = wave % KP, rs = wave / KP;
+  const int c0 = kpi * nchunk / KP, c1 = (kpi + 1) * nchunk / KP;
+  // (a residual epilogue's projection takes no RMSNorm: its input is the
+  // attention output or the SwiGLU product)
+  constexpr bool NORMED = EPI != Q4E_RESID;
+  const int norm = NORMED ? e.norm : 0;
+  const float* gamma = norm ? e.gamma : nullptr;
+  __shared__ float ys[KP][RB];
   __shared__ float ssq_w[4];
   __shared__ float red[4];
   // x-hat shared by the wavefronts of a part: unit (i, t) of lane l
@@ -549,7 +630,7 @@ __global__ __launch_bounds__(256) void k_q4_fused(const bf16_t* __restrict__ X, 
   constexpr int SU = 8;
   float sp[SU];
   float r_inv = 1.f;
-  if (e.norm == 2) {
+  if (norm == 2) {
     if (e.stat.inv) {
       r_inv = e.stat.inv[0];
     } else if (e.stat.ss) {
@@ -578,30 +659,40 @@ __global__ __launch_bounds__(256) void k_q4_fused(const bf16_t* __restrict__ X, 
       }
     }
   }
-  // a ring of NB buffers of R rows: NB - 1 groups in flight
-  uint4 wc[NB][R][NI];
-  float sv[NB][R][NI], bv[NB][R][NI];
-  // rows past the set's last one repeat it, rows that do not exist read the
-  // block's first row, lanes past the part repeat its last chunk (all loaded,
-  // never used)
-  auto load_group = [&](int g, auto bc) {
-    constexpr int b = decltype(bc)::value;
+  // the lane's chunks (lanes past the part repeat its last chunk: loaded, and
+  // multiplied by zero activations)
+  uint32_t offw[NI], offs[NI];
 #pragma unroll
-    for (int q = 0; q < R; ++q) {
-      bool ok;
-      int n = q4_row<EPI>(e, RB, rs * rpw + min(g * R + q, rpw - 1), ok);
-      if (!ok) n = q4_row<EPI>(e, RB, 0, ok);
+  for (int i = 0; i < NI; ++i) {
+    const int c = min(c0 + lane + 64 * i, c1 - 1);
+    offw[i] = (uint32_t)c * 16;
+    offs[i] = (uint32_t)(c >> 1) * 2;
+  }
+  // the wavefront's weight rows, lane j computing row j's index once (rows
+  // that do not exist read the block's first); row r is read back into a
+  // scalar register where it is used
+  int n_lane;
+  {
+    bool ok;
+    n_lane = q4_row<EPI>(e, RB, rs * RW + min(lane, RW - 1), ok);
+    if (!ok) n_lane = q4_row<EPI>(e, RB, 0, ok);
+  }
+  uint4 wc[D + 1][NI];
+  uint32_t sv[D + 1][NI], bv[D + 1][NI];
+  auto load_row = [&](auto rc) {
+    constexpr int r = decltype(rc)::value, b = r % (D + 1);
+    const int n = __builtin_amdgcn_readlane(n_lane, r);
+    const char* wrow = reinterpret_cast<const char*>(words) + (size_t)n * (K / 2);
+    const char* srow = reinterpret_cast<const char*>(scales) + (size_t)n * ngrp * 2;
+    const char* brow = reinterpret_cast<const char*>(biases) + (size_t)n * ngrp * 2;
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int c = min(c0 + lane + 64 * i, c1 - 1);
-        wc[b][q][i] = ld16(words + (size_t)n * (K / 8) + c * 4);
-        sv[b][q][i] = bf16_to_f32(scales[(size_t)n * ngrp + c / 2]);
-        bv[b][q][i] = bf16_to_f32(biases[(size_t)n * ngrp + c / 2]);
-      }
+    for (int i = 0; i < NI; ++i) {
+      wc[b][i] = ld16(wrow + offw[i]);
+      sv[b][i] = *reinterpret_cast<const uint16_t*>(srow + offs[i]);
+      bv[b][i] = *reinterpret_cast<const uint16_t*>(brow + offs[i]);
     }
   };
-  // the first NB - 1 groups' codes go out first, then the epilogue's own operands
-  static_for<0, NB - 1>([&](auto j) { load_group(decltype(j)::value, j); });
+  static_for<0, (D < RW ? D : RW)>([&](auto j) { load_row(j); });
   // (loads with clamped indices, not under a condition: a conditional load is
   // waited for at once, and that wait would cover the codes requested above)
   bool own_ok = false;
@@ -662,51 +753,48 @@ __global__ __launch_bounds__(256) void k_q4_fused(const bf16_t* __restrict__ X, 
     ssq = q4_xhat<NI>(X, gamma, c0, c1, lane, xw, hs, xs);
   }
   // every wavefront's x^2 covers a disjoint share of K, together all of it
-  if (e.norm == 1) {
+  if (norm == 1) {
     ssq = warp_sum(ssq);
     if (lane == 0) ssq_w[wave] = ssq;
   }
-  auto group = [&](int g, auto bc) {
-    constexpr int b = decltype(bc)::value;
-    // (unconditional, so the compiler's waits for this group stay exact; past
-    // the last group it repeats rows just read)
-    load_group(g + NB - 1, std::integral_constant<int, (b + NB - 1) % NB>{});
+  // nibble masks and the fp16 exponent pattern in registers (opaque to the
+  // compiler), so each (code & mask) | 0x6400 pair is one three-input bit op
+  uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, magic = 0x64006400u;
+  asm("" : "+v"(m_lo), "+v"(m_hi), "+v"(magic));
+  float acc[RW];
+  static_for<0, RW>([&](auto rc) {
+    constexpr int r = decltype(rc)::value, b = r % (D + 1);
+    if constexpr (r + D < RW) load_row(std::integral_constant<int, r + D>{});
+    float a_row = 0.f;
 #pragma unroll
-    for (int q = 0; q < R; ++q) {
-      float acc = 0.f;
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t wv4[4] = {wc[b][i].x, wc[b][i].y, wc[b][i].z, wc[b][i].w};
+      float a = 0.f;
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        if (c0 + lane + 64 * i < c1) {
-          const uint32_t wv4[4] = {wc[b][q][i].x, wc[b][q][i].y, wc[b][q][i].z, wc[b][q][i].w};
-          float a = 0.f;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t u = wv4[t], u8 = wv4[t] >> 8;
-            a = __builtin_amdgcn_fdot2(u32_as_h2((u & 0x000F000Fu) | 0x64006400u), u32_as_h2(xw[i][4 * t + 0]), a, false);
-            a = __builtin_amdgcn_fdot2(u32_as_h2((u & 0x00F000F0u) | 0x64006400u), u32_as_h2(xw[i][4 * t + 1]), a, false);
-            a = __builtin_amdgcn_fdot2(u32_as_h2((u8 & 0x000F000Fu) | 0x64006400u), u32_as_h2(xw[i][4 * t + 2]), a, false);
-            a = __builtin_amdgcn_fdot2(u32_as_h2((u8 & 0x00F000F0u) | 0x64006400u), u32_as_h2(xw[i][4 * t + 3]), a, false);
-          }
-          acc += sv[b][q][i] * (a - 1024.0f * hs[i]) + bv[b][q][i] * xs[i];
-        }
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t u = wv4[t], u8 = wv4[t] >> 8;
+        a = __builtin_amdgcn_fdot2(u32_as_h2((u & m_lo) | (magic & ~m_lo)), u32_as_h2(xw[i][4 * t + 0]), a, false);
+        a = __builtin_amdgcn_fdot2(u32_as_h2((u & m_hi) | (magic & ~m_hi)), u32_as_h2(xw[i][4 * t + 1]), a, false);
+        a = __builtin_amdgcn_fdot2(u32_as_h2((u8 & m_lo) | (magic & ~m_lo)), u32_as_h2(xw[i][4 * t + 2]), a, false);
+        a = __builtin_amdgcn_fdot2(u32_as_h2((u8 & m_hi) | (magic & ~m_hi)), u32_as_h2(xw[i][4 * t + 3]), a, false);
       }
-      acc = warp_sum(acc);
-      if (lane == 0 && g * R + q < rpw) ys[kpi][rs * rpw + g * R + q] = acc;
+      const float s = __builtin_bit_cast(float, sv[b][i] << 16), bi = __builtin_bit_cast(float, bv[b][i] << 16);
+      a_row += s * (a - 1024.0f * hs[i]) + bi * xs[i];
     }
-  };
-  const int ngroups = (rpw + R - 1) / R;
-  for (int g = 0; g < ngroups; g += NB) {
-    static_for<0, NB>([&](auto j) {
-      if (g + decltype(j)::value < ngroups) group(g + decltype(j)::value, j);
-    });
+    acc[r] = a_row;
+  });
+  {
+    int row;
+    const float v = reduce_rows<RW>(acc, lane, row);
+    if ((lane & (64 / RW - 1)) == 0) ys[kpi][rs * RW + row] = v;
   }
   __syncthreads();
   // row scale: 1 (norm 0), from the row's mean square over all of K (norm 1),
   // or from the producer's statistic (norm 2)
   float r = 1.0f;
-  if (e.norm == 1) {
+  if (norm == 1) {
     r = 1.0f / sqrtf(((ssq_w[0] + ssq_w[1]) + (ssq_w[2] + ssq_w[3])) / (float)K + e.eps);
-  } else if (e.norm == 2) {
+  } else if (norm == 2) {
     if (e.stat.inv) {
       r = r_inv;
     } else if (e.stat.ss) {
@@ -721,7 +809,7 @@ __global__ __launch_bounds__(256) void k_q4_fused(const bf16_t* __restrict__ X, 
   }
   auto sum_row = [&](int lr) {
     float v = 0.f;
-    for (int k = 0; k < kp; ++k) v += ys[k][lr];
+    for (int k = 0; k < KP; ++k) v += ys[k][lr];
     return v * r;
   };
   if (EPI == Q4E_PLAIN) {
@@ -777,52 +865,65 @@ __global__ __launch_bounds__(256) void k_q4_fused(const bf16_t* __restrict__ X, 
 
 // K parts per block, chunks per lane and rows per wavefront of the single-row
 // kernel; false when K is too long for one block (more than 1024 chunks)
-static bool q4_fused_shape(int N, int K, int& kp, int& ni, int& rpw) {
+static bool q4_fused_shape(int N, int K, int& kp, int& ni, int& rw) {
   const int nchunk = K / 32;
   if (nchunk < 1 || nchunk > 1024) return false;
   kp = nchunk <= 256 ? 1 : nchunk <= 512 ? 2 : 4;
   ni = ((nchunk + kp - 1) / kp + 63) / 64;
-  // rows per wavefront: at least 4 (to amortize the conversion of x), else
-  // few enough for a grid of at most 512 blocks, two per compute unit (more,
-  // shorter blocks measured slower); the block's rows even (pairs) and at most
-  // kQ4MaxRB
-  rpw = std::max(4, (N * kp + 2047) / 2048);
-  rpw = std::min(rpw, kQ4MaxRB * kp / 4);
-  if (kp == 4) rpw = (rpw + 1) & ~1;
+  // rows per wavefront: the fewest of 4, 8 and 16 that keep the grid at most
+  // 512 blocks, two per compute unit (fewer rows convert x more often for the
+  // same weights; more blocks than that measured slower)
+  const int sets = 4 / kp;
+  rw = 4;
+  while (rw < 16 && (N + sets * rw - 1) / (sets * rw) > 512) rw *= 2;
   return true;
 }
 
 int q4_fused_blocks(int N, int K) {
-  int kp, ni, rpw;
-  if (!q4_fused_shape(N, K, kp, ni, rpw)) return 0;
-  const int RB = 4 * rpw / kp;
+  int kp, ni, rw;
+  if (!q4_fused_shape(N, K, kp, ni, rw)) return 0;
+  const int RB = 4 / kp * rw;
   return (N + RB - 1) / RB;
 }
 
+// rows requested ahead of the one being multiplied: 3 with 16 rows per
+// wavefront, else 2 (measured: deeper rings were slower at every shape of the
+// 13B-width layer, and 2 beat 3 for the shorter wavefronts)
+template <int RW>
+constexpr int q4_depth() { return RW >= 16 ? 3 : 2; }
+
 bool launch_q4_fused(const bf16_t* X, const uint32_t* words, const bf16_t* scales, const bf16_t* biases,
                      Q4Fused e, hipStream_t s) {
-  int kp, ni, rpw;
+  int kp, ni, rw;
   if (e.N <= 0) return true;
-  if (!q4_fused_shape(e.N, e.K, kp, ni, rpw)) return false;
+  if (!q4_fused_shape(e.N, e.K, kp, ni, rw)) return false;
   if (e.epi != Q4E_PLAIN && e.epi != Q4E_RESID && (e.N & 1)) return false;
+  if (e.epi == Q4E_RESID && e.norm != 0) return false;
   e.kp = kp;
-  e.rpw = rpw;
+  e.rpw = rw;
   const dim3 grid(q4_fused_blocks(e.N, e.K));
-#define Q4F(n, k, r, nb, E)                                                                               \
-  if (ni == n && kp == k) {                                                                               \
-    hipLaunchKernelGGL((k_q4_fused<n, k, r, nb, E>), grid, dim3(256), 0, s, X, words, scales, biases, e); \
-    return true;                                                                                          \
+#define Q4L(n, k, r, E) \
+  hipLaunchKernelGGL((k_q4_fused<n, k, r, q4_depth<r>(), E>), grid, dim3(256), 0, s, X, words, scales, biases, e)
+#define Q4F(n, k, E)               \
+  if (ni == n && kp == k) {        \
+    if (rw == 4)                   \
+      Q4L(n, k, 4, E);             \
+    else if (rw == 8)              \
+      Q4L(n, k, 8, E);             \
+    else                           \
+      Q4L(n, k, 16, E);            \
+    return true;                   \
   }
   // (a part of more than 256 chunks is split further, so parts of kp > 1
   // hold more than 128 chunks: 3 or 4 per lane)
-#define Q4FE(E)                                                                                   \
-  case E:                                                                                         \
-    Q4F(1, 1, 1, 2, E) Q4F(2, 1, 1, 2, E) Q4F(3, 1, 1, 2, E) Q4F(4, 1, 1, 2, E) Q4F(3, 2, 1, 2, E)   \
-    Q4F(4, 2, 1, 2, E) Q4F(3, 4, 1, 2, E) Q4F(4, 4, 1, 2, E)                                       \
+#define Q4FE(E)                                                                                     \
+  case E:                                                                                           \
+    Q4F(1, 1, E) Q4F(2, 1, E) Q4F(3, 1, E) Q4F(4, 1, E) Q4F(3, 2, E) Q4F(4, 2, E) Q4F(3, 4, E) Q4F(4, 4, E) \
     break;
   switch (e.epi) { Q4FE(Q4E_PLAIN) Q4FE(Q4E_QKV) Q4FE(Q4E_RESID) Q4FE(Q4E_SWIGLU) }
 #undef Q4FE
 #undef Q4F
+#undef Q4L
   return false;
 }
 

@@ -217,7 +217,8 @@ struct Q4Fused {
   int ib;
   bf16_t* g_out;
 };
-// false (nothing launched) when K > 32768 or a paired epilogue has odd N
+// false (nothing launched) when K > 32768, a paired epilogue has odd N or a
+// residual epilogue asks for a norm
 bool launch_q4_fused(const bf16_t* X, const uint32_t* words, const bf16_t* scales, const bf16_t* biases,
                      Q4Fused e, hipStream_t s);
 // blocks of the single-row kernel for [N, K] (0: not supported)
