@@ -12,7 +12,7 @@
 //
 // k_gemv_q4: 4-bit group-affine weights (group 64 along the input dim, the MLX
 //   quantization config of "模型配置"): W = s * code + b.  Per 8-code word,
-//   one shift and four v_and_or_b32 turn nibble pairs into fp16 pairs
+//   one shift and four three-input bit operations turn nibble pairs into fp16 pairs
 //   (1024 + code or 1024 + 16 code, exact), v_dot2_f32_f16 multiplies them with
 //   pre-scaled fp16 activations; the 1024 offset and the bias are removed per
 //   32-code chunk with precomputed activation sums:
@@ -415,11 +415,10 @@ __global__ __launch_bounds__(256) void k_gemv_q4(const _Float16* __restrict__ xh
 // c0 + l + 64 i (i < NI) of its part and keeps x-hat for them in registers
 // (gamma applied, fp16 pairs in the word order of the nibble trick, the two
 // chunk sums) for all the rows of its set; the wavefronts of a part convert a
-// share of it each and exchange it through LDS.  Rows go in groups of R
-// through a ring of NB register buffers, the codes and group scales of group
-// g + NB - 1 requested before group g is multiplied (R = 1, NB = 2 measured
-// best: fewer registers, three wavefronts per SIMD, beat deeper rings).  Row
-// sums land in LDS; after one barrier the
+// share of it each and exchange it through LDS.  A wavefront's rows (RW of
+// them, unrolled) go through a ring of D + 1 register buffers; each lane keeps
+// a partial sum per row and one transposed reduction at the end leaves every
+// row's sum in one lane.  Row sums land in LDS; after one barrier the
 // block applies the RMSNorm row scale (a per-row scalar, so it multiplies the
 // sum) and its epilogue, one thread per output element:
 //   Q4E_PLAIN : y[n] = the projection (fp32);
