@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decoder-block prefill TFLOP/s + decode tokens/s; % MFMA / HBM roofline"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-PREFILL_PHASES = ["rms_x", "qkv_gemm_rope_append", "attention_prefill", "wo_gemm_residual", "rms_h",
+PREFILL_PHASES = ["rms_x", "qkv_gemm_rope_append", "attention_prefill", "wo_gemm_residual_h_stats",
                   "w13_gemm_swiglu", "w2_gemm_residual"]
 DECODE_PHASES = ["qkv_gemv_and_x_stats", "qkv_finish_rope_append", "attention_decode", "wo_gemv",
                  "wo_residual_h_stats", "w13_gemv_swiglu", "w2_gemv", "w2_residual"]
@@ -99,7 +99,8 @@ def bench_prefill(wl, steps, warmup, inp=None):
     flops = W.prefill_flops(s, B, Lq)
     lin = W.linear_flops(s, B * Lq)
     attn_flops = flops - sum(lin.values())
-    ph_flops = [0.0, lin["qkv"], attn_flops, lin["wo"], 0.0, lin["w13"], lin["w2"]]
+    ph_flops = [0.0, lin["qkv"], attn_flops, lin["wo"], lin["w13"], lin["w2"]]
+    assert len(ph_flops) == len(PREFILL_PHASES)
     # breakdown pass
     torch.cuda.synchronize()
     blk.profile_start(steps)

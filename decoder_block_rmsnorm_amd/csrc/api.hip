@@ -533,15 +533,16 @@ static SLayout scratch_layout(const llama_block_config& c, const Dims& d, int T,
   size_t off = 0;
   L.inv1 = off; off = align256(off + (size_t)T * 4);
   L.inv2 = off; off = align256(off + (size_t)T * 4);
-  // partial row statistics: of x per K slice of the decode QKV projection, of h
-  // per 256-column block of the residual epilogue
+  // partial row statistics: of x per K slice of the decode QKV projection (in a
+  // stack's prompt pass, per 128 columns from the writer of x), of h per
+  // 256-column block of the residual epilogue kernel (per 128 columns in prefill)
   // (one partial per block of the single-row 4-bit wo kernel); sized alike for
   // prefill and decode so that the buffers after it sit at the same offsets
   L.ks_qkv = gemv_ks(T, d.Nqkv, d.D);
   const int nb_q4 = d.q4 ? q4_fused_blocks(d.D, d.Nq) : 0;
   L.nb_h = q4_single(d, T, decode) ? nb_q4 : (d.D + 255) / 256;
-  L.ssx = off; off = align256(off + (size_t)L.ks_qkv * T * 4);
-  L.ssh = off; off = align256(off + (size_t)std::max(nb_q4, (d.D + 255) / 256) * T * 4);
+  L.ssx = off; off = align256(off + (size_t)std::max(L.ks_qkv, (d.D + 127) / 128) * T * 4);
+  L.ssh = off; off = align256(off + (size_t)std::max(nb_q4, (d.D + 127) / 128) * T * 4);
   L.q = off; off = align256(off + (size_t)T * d.Nq * E);
   L.attn = off; off = align256(off + (size_t)T * d.Nq * E);
   L.h = off; off = align256(off + (size_t)T * d.D * E);
@@ -745,8 +746,11 @@ static void fp32_path(const llama_block* blk, KVView kv, const void* x, void* y,
   mk(s);
 }
 
+// xstat bit 0: x's sums of squares per 128 columns are already in S.ssx (from
+// the writer of x), so RMSNorm #1 needs no statistic pass; bit 1: the W2
+// residual epilogue writes y's there for the next block
 static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void* y, int B, int L, int M, char* sc,
-                         const SLayout& S, Marker& mk, hipStream_t s) {
+                         const SLayout& S, Marker& mk, hipStream_t s, int xstat) {
   const Dims& d = blk->dm;
   float* inv1 = (float*)(sc + S.inv1);
   float* inv2 = (float*)(sc + S.inv2);
@@ -786,13 +790,22 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
       g.A = (const bf16_t*)a16;
     }
   };
+  // row statistics as partial sums of squares per 128 columns, at most
+  // kGemmMaxRowPartials per row
+  const bool stat128 = d.D % 128 == 0 && d.D / 128 <= kGemmMaxRowPartials;
+  float* ssx = (float*)(sc + S.ssx);
+  const bool x_in = stat128 && (xstat & 1);
   mk(s);
-  launch_rms_inv<bf16_t>((const bf16_t*)x, M, d.D, eps, inv1, s);
+  if (!x_in) launch_rms_inv<bf16_t>((const bf16_t*)x, M, d.D, eps, inv1, s);
   mk(s);
   GemmArgs a{};
   operands(a, (const bf16_t*)x, blk->qkv, blk->gamma1);
   a.M = M; a.N = d.Nqkv; a.K = d.D;
-  a.inv_rms = inv1;
+  if (x_in) {
+    a.rstat.ss = ssx; a.rstat.nb = d.D / 128; a.rstat.M = M; a.rstat.n = d.D; a.rstat.eps = eps;
+  } else {
+    a.inv_rms = inv1;
+  }
   a.q_out = q; a.Nq = d.Nq; a.Nkv = d.Nkv; a.L = L;
   a.rope = blk->rope; a.traditional = blk->cfg.rope_traditional;
   a.kv = kv;
@@ -804,8 +817,9 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
   // split, every slice writes fp32 partials and the residual epilogue kernel
   // adds them (in slice order) to the residual.
   float* part = (float*)(sc + S.part);
+  // ss_out (optional): the stored rows' sums of squares per 128 columns
   auto resid_gemm = [&](const bf16_t* A, const Lin& lin, const bf16_t* resid, bf16_t* out, int K, int32_t* lens_add,
-                        int lens_inc, bf16_t* branch) {
+                        int lens_inc, bf16_t* branch, float* ss_out) {
     GemmArgs g{};
     operands(g, A, lin, nullptr);
     g.M = M; g.N = d.D; g.K = K;
@@ -813,24 +827,33 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
     if (ks > 1) {
       g.C = part; g.ksplit = ks;
       launch_gemm_mfma(EPI_F32, g, s);
-      launch_epi_resid<bf16_t>(part, ks, M, d.D, resid, out, nullptr, lens_add, lens_inc, B, branch, s, kv.cu);
-    } else {
-      g.resid = resid; g.out = out; g.lens_add = lens_add; g.lens_inc = lens_inc; g.n_seq = B; g.branch = branch;
-      g.lens_cu = kv.cu;
-      launch_gemm_mfma(EPI_RESID, g, s);
+      launch_epi_resid<bf16_t>(part, ks, M, d.D, resid, out, ss_out, lens_add, lens_inc, B, branch, s, kv.cu, 1);
+      return;
     }
+    g.resid = resid; g.out = out; g.lens_add = lens_add; g.lens_inc = lens_inc; g.n_seq = B; g.branch = branch;
+    g.lens_cu = kv.cu; g.ss_out = ss_out;
+    launch_gemm_mfma(EPI_RESID, g, s);
   };
-  resid_gemm(attn, blk->o, (const bf16_t*)x, h, d.Nq, nullptr, 0, nullptr);
-  mk(s);
-  launch_rms_inv<bf16_t>(h, M, d.D, eps, inv2, s);
+  // RMSNorm #2's statistic comes from the Wo epilogue (the rows' sums of
+  // squares as stored), reduced by the W1/W3 GEMM into its row scales; a model
+  // dim past 64 partials per row falls back to a statistic pass over h
+  float* ssh = (float*)(sc + S.ssh);
+  resid_gemm(attn, blk->o, (const bf16_t*)x, h, d.Nq, nullptr, 0, nullptr, stat128 ? ssh : nullptr);
+  if (!stat128) launch_rms_inv<bf16_t>(h, M, d.D, eps, inv2, s);
   mk(s);
   GemmArgs f{};
   operands(f, h, blk->w13, blk->gamma2);
   f.M = M; f.N = 2 * d.F; f.K = d.D;
-  f.inv_rms = inv2; f.g_out = g;
+  f.g_out = g;
+  if (stat128) {
+    f.rstat.ss = ssh; f.rstat.nb = d.D / 128; f.rstat.M = M; f.rstat.n = d.D; f.rstat.eps = eps;
+  } else {
+    f.inv_rms = inv2;
+  }
   launch_gemm_mfma(EPI_SWIGLU, f, s);
   mk(s);
-  resid_gemm(g, blk->w2, h, (bf16_t*)y, d.F, kv.lens, L, blk->diag ? (bf16_t*)(sc + S.ffn) : nullptr);
+  resid_gemm(g, blk->w2, h, (bf16_t*)y, d.F, kv.lens, L, blk->diag ? (bf16_t*)(sc + S.ffn) : nullptr,
+             stat128 && (xstat & 2) ? ssx : nullptr);
   mk(s);
 }
 
@@ -944,7 +967,7 @@ static void bf16_decode(const llama_block* blk, KVView kv, const void* x, void* 
 // Ls (prefill only, may be null): a ragged call's new tokens per sequence.
 static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const void* x, void* y, int batch, int L,
                             void* scratch, size_t sbytes, bool decode, int n_splits_override, int split_len_override,
-                            hipStream_t s, const int32_t* Ls = nullptr) {
+                            hipStream_t s, const int32_t* Ls = nullptr, int xstat = 0) {
   SLayout S;
   llama_status st = check_call(blk, c, layer, x, y, batch, L, Ls, scratch, sbytes, decode,
                                n_splits_override > 0 ? split_len_override : kSplitLen, &S);
@@ -973,14 +996,14 @@ static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const
     mk.ev = &blk->ev[(size_t)(blk->prof_calls++) * kMaxMarks];
     mk.mask = blk->prof_mask;
     // phases whose kernels take launch-attached events: the w1/w3 GEMM of the
-    // bf16 prefill (phase 5) and the decode attention (phase 2)
-    const uint32_t clockable = !d.bf16 ? 0u : decode ? (1u << 2) : (1u << 5);
+    // bf16 prefill (phase 4) and the decode attention (phase 2)
+    const uint32_t clockable = !d.bf16 ? 0u : decode ? (1u << 2) : (1u << 4);
     if (mk.mask != 0 && (mk.mask & (mk.mask - 1)) == 0 && (mk.mask & clockable)) mk.clocked = __builtin_ctz(mk.mask);
   }
   if (!d.bf16) {
     fp32_path<float>(blk, kv, x, y, batch, L, M, sc, S, mk, s);
   } else if (!decode) {
-    bf16_prefill(blk, kv, x, y, batch, L, M, sc, S, mk, s);
+    bf16_prefill(blk, kv, x, y, batch, L, M, sc, S, mk, s, xstat);
   } else {
     if (n_splits_override > 0) bf16_decode(blk, kv, x, y, batch, sc, S, n_splits_override, split_len_override, mk, s);
     else bf16_decode(blk, kv, x, y, batch, sc, S, S.n_splits, S.split_len, mk, s);
@@ -1235,6 +1258,17 @@ extern "C" size_t llama_stack_scratch_bytes(const llama_stack* st, int32_t max_p
   return stack_layout(st, max_prompt, max_seq).total;
 }
 
+// A stack's prompt pass hands each block the statistic of its input: the
+// embedding writes x's sums of squares per 128 columns into the block scratch
+// where the first block's prefill reads them, and every block's W2 epilogue
+// writes them for the next (model dims up to 64 partials per row).  Returns
+// where they go in the block scratch of a T-row pass, or null without them.
+static float* stack_x_stats(const llama_stack* st, void* bs, int T) {
+  const Dims& d = st->blocks[0]->dm;
+  if (!d.bf16 || d.D % 128 != 0 || d.D / 128 > kGemmMaxRowPartials) return nullptr;
+  return (float*)((char*)bs + scratch_layout(st->blocks[0]->cfg, d, T, 1, st->blocks[0]->cfg.max_seq, false).ssx);
+}
+
 extern "C" llama_status llama_stack_generate(llama_stack* st, llama_kvcache* cache, const int32_t* prompt, int32_t P,
                                              int32_t n_steps, int32_t* ids_out, float* logits_out, void* scratch,
                                              size_t sbytes, int32_t use_graph, void* stream) {
@@ -1271,9 +1305,13 @@ extern "C" llama_status llama_stack_generate(llama_stack* st, llama_kvcache* cac
   };
 
   launch_fill_i32(cursor, 1, 0, s);
-  launch_embed<bf16_t>((const bf16_t*)st->emb, V, D, prompt, P, x, s);
-  for (int l = 0; l < NL; ++l)
-    if ((r = enqueue(st->blocks[l], cache, l, x, x, 1, P, bs, L.blk_bytes, false, 0, 0, s)) != LLAMA_OK) return r;
+  float* xs = stack_x_stats(st, bs, P);
+  launch_embed<bf16_t>((const bf16_t*)st->emb, V, D, prompt, P, x, s, xs);
+  for (int l = 0; l < NL; ++l) {
+    const int xstat = xs ? 1 | (l + 1 < NL ? 2 : 0) : 0;
+    if ((r = enqueue(st->blocks[l], cache, l, x, x, 1, P, bs, L.blk_bytes, false, 0, 0, s, nullptr, xstat)) != LLAMA_OK)
+      return r;
+  }
   if ((r = head(x + (size_t)(P - 1) * D)) != LLAMA_OK) return r;
   launch_emit(cur, ids_out, cursor, hlog, logits_out, V, s);
 
@@ -1359,9 +1397,11 @@ extern "C" llama_status llama_stack_generate_recompute(llama_stack* st, llama_kv
     // an empty cache for sequence 0 in every layer
     launch_fill_strided_i32(cache->lens, NL, MB, 0, s);
     for (int l = 0; l < NL; ++l) cache->lens_host[(size_t)l * MB] = 0;
-    launch_embed<bf16_t>((const bf16_t*)st->emb, V, D, seq, n, x, s);
+    float* xs = stack_x_stats(st, bs, n);
+    launch_embed<bf16_t>((const bf16_t*)st->emb, V, D, seq, n, x, s, xs);
     for (int l = 0; l < NL; ++l) {
-      llama_status r = enqueue(st->blocks[l], cache, l, x, x, 1, n, bs, L.blk_bytes, false, 0, 0, s);
+      const int xstat = xs ? 1 | (l + 1 < NL ? 2 : 0) : 0;
+      llama_status r = enqueue(st->blocks[l], cache, l, x, x, 1, n, bs, L.blk_bytes, false, 0, 0, s, nullptr, xstat);
       if (r != LLAMA_OK) return r;
     }
     Sampling smp = st->smp;

@@ -104,7 +104,7 @@ void launch_epi_qkv(const float* part, int ks, int M, int Nq, int Nkv, RowStat s
 template <typename T>
 __global__ __launch_bounds__(256) void k_epi_resid(const float* part, int ks, int M, int N, const T* resid, T* out,
                                                    float* ss_out, int32_t* lens_add, int lens_inc, int n_seq,
-                                                   T* branch, const int32_t* lens_cu) {
+                                                   T* branch, const int32_t* lens_cu, int ss_128) {
   const int m = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
   const size_t stride = (size_t)M * N;
@@ -121,7 +121,15 @@ __global__ __launch_bounds__(256) void k_epi_resid(const float* part, int ks, in
     const float ss = warp_sum(v * v);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
-    if (threadIdx.x == 0) ss_out[(size_t)blockIdx.x * M + m] = (red[0] + red[1]) + (red[2] + red[3]);
+    if (threadIdx.x == 0) {
+      if (!ss_128) {
+        ss_out[(size_t)blockIdx.x * M + m] = (red[0] + red[1]) + (red[2] + red[3]);
+      } else {
+        // one partial per 128 columns (two wavefronts each)
+        ss_out[(size_t)(2 * blockIdx.x) * M + m] = red[0] + red[1];
+        if ((2 * blockIdx.x + 1) * 128 < N) ss_out[(size_t)(2 * blockIdx.x + 1) * M + m] = red[2] + red[3];
+      }
+    }
   }
   if (lens_add && m == 0 && blockIdx.x == 0 && (int)threadIdx.x < n_seq)
     lens_add[threadIdx.x] += lens_cu ? lens_cu[threadIdx.x + 1] - lens_cu[threadIdx.x] : lens_inc;
@@ -129,11 +137,12 @@ __global__ __launch_bounds__(256) void k_epi_resid(const float* part, int ks, in
 
 template <typename T>
 void launch_epi_resid(const float* part, int ks, int M, int N, const T* resid, T* out, float* ss_out,
-                      int32_t* lens_add, int lens_inc, int n_seq, T* branch, hipStream_t s, const int32_t* lens_cu) {
+                      int32_t* lens_add, int lens_inc, int n_seq, T* branch, hipStream_t s, const int32_t* lens_cu,
+                      int ss_128) {
   if (M <= 0) return;
   dim3 grid((N + 255) / 256, M);
   hipLaunchKernelGGL(k_epi_resid<T>, grid, dim3(256), 0, s, part, ks, M, N, resid, out, ss_out, lens_add,
-                     lens_inc, n_seq, branch, lens_cu);
+                     lens_inc, n_seq, branch, lens_cu, ss_128);
 }
 
 // ---------------------------------------------------------------------------
@@ -184,7 +193,7 @@ void launch_reduce_f32(const float* part, int ks, int M, int N, float* out, hipS
   template void launch_epi_qkv<T>(const float*, int, int, int, int, RowStat, int, const float2*, int, T*, KVView, \
                                   hipStream_t);                                                                 \
   template void launch_epi_resid<T>(const float*, int, int, int, const T*, T*, float*, int32_t*, int, int, T*,    \
-                                    hipStream_t, const int32_t*);                                               \
+                                    hipStream_t, const int32_t*, int);                                          \
   template void launch_epi_swiglu<T>(const float*, int, int, int, int, RowStat, T*, hipStream_t);
 INST(float)
 INST(bf16_t)

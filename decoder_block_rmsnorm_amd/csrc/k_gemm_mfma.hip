@@ -6,7 +6,9 @@
 //   EPI_QKV    : RMSNorm row scale (gamma is folded into the weights), RoPE on
 //                q and k, q to a [M, Nq] buffer, k and v appended to the pages;
 //   EPI_SWIGLU : RMSNorm row scale, silu(w1 n) * (w3 n) on interleaved columns;
-//   EPI_RESID  : residual add (wo and w2).
+//   EPI_RESID  : residual add (wo and w2), optionally with the sums of squares
+//                of the stored rows per 128 columns: the statistic of the next
+//                RMSNorm, which the W1/W3 GEMM reduces into its row scales.
 //
 // Main path (DEPTH 0; every bf16 prefill GEMM whose N is a multiple of 256):
 // a 256 x 256 (or 128 x 256) block tile, four wavefronts, each owning a
@@ -542,7 +544,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
   // residual loads) are 16-byte pieces of contiguous rows.
   const int wcol0 = n0 + wn * 128;  // first column of this wavefront (head aligned)
   __syncthreads();                  // main-loop LDS is free
-  // [0, 4 KB): per-row cache metadata (EPI_QKV); then 17 KB per wavefront
+  // [0, 4 KB): per-row data (EPI_QKV, EPI_SWIGLU); then 17 KB per wavefront
   char* stage = reinterpret_cast<char*>(lds) + 4096 + wave * 17408;
   auto wave_sync = [&]() {
     // LDS accesses of one wavefront complete in order once waited for
@@ -550,11 +552,36 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
   };
+  // RMSNorm row scales of the block's rows into s_rs[BM] (the caller
+  // synchronizes): from inv_rms, or reduced from the producer's partial sums of
+  // squares, every partial of a row requested at once and summed in order
+  auto row_scales = [&](float* s_rs) {
+    for (int r = tid; r < BM; r += NT) {
+      const int row = m0 + r, rr = min(row, M - 1);
+      float v;
+      if (a.inv_rms) {
+        v = a.inv_rms[rr];
+      } else {
+        const RowStat& st = a.rstat;
+        float p[kGemmMaxRowPartials];
+#pragma unroll
+        for (int j = 0; j < kGemmMaxRowPartials; ++j) p[j] = st.ss[(size_t)min(j, st.nb - 1) * st.M + rr];
+        float t = 0.f;
+#pragma unroll
+        for (int j = 0; j < kGemmMaxRowPartials; ++j)
+          if (j < st.nb) t += p[j];
+        v = 1.0f / sqrtf(t / (float)st.n + st.eps);
+      }
+      s_rs[r] = row < M ? v : 0.f;
+    }
+  };
   if constexpr (EPI == EPI_QKV) {
-    // Per-row cache metadata once per block: position, and the element offset
-    // of the row's page.
+    // Per-row data once per block: position, RMSNorm row scale and the element
+    // offset of the row's page (bytes [0, 4 BM), [4 BM, 8 BM), [8 BM, 16 BM)).
     int* s_pos = reinterpret_cast<int*>(lds);
-    long long* s_page = reinterpret_cast<long long*>(lds + 4 * BM);  // 8-byte aligned
+    float* s_rs = reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + 4 * BM);
+    long long* s_page = reinterpret_cast<long long*>(lds + 4 * BM);  // byte 8 BM: 8-byte aligned
+    row_scales(s_rs);
     for (int r = tid; r < BM; r += NT) {
       const int row = m0 + r;
       if (row < M) {
@@ -583,7 +610,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
         const int lr = 8 * (r >> 2) + 4 * hg + (r & 3);
         const int row = m0 + rb + lr;
         const int pos = row < M ? s_pos[rb + lr] : 0;
-        rsv[r] = row < M ? a.inv_rms[row] : 0.f;
+        rsv[r] = s_rs[rb + lr];
         static_for<0, 2>([&](auto jc) {
           constexpr int jp = decltype(jc)::value;
           csv[r][jp] = (is_q || is_k) ? a.rope[(size_t)pos * 64 + jp * 32 + l32] : make_float2(1.f, 0.f);
@@ -685,6 +712,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
       for (int t = 0; t < 8; ++t) {
         const int c = lane + 64 * t, lr = c >> 4, pc = c & 15;
         const int row = m0 + rb + lr;
+        float ssq = 0.f;
         if (row < M) {
           const size_t idx = (size_t)row * N + wcol0 + 8 * pc;
           const float4 f0 = *reinterpret_cast<const float4*>(sf + lr * FST + 8 * pc);
@@ -701,6 +729,24 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
           }
           st16(a.out + idx, make_uint4(ow[0], ow[1], ow[2], ow[3]));
           if (a.branch) st16(a.branch + idx, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+          if (a.ss_out) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float o0 = __builtin_bit_cast(float, ow[e] << 16);
+              const float o1 = __builtin_bit_cast(float, ow[e] & 0xffff0000u);
+              ssq += o0 * o0 + o1 * o1;
+            }
+          }
+        }
+        if (a.ss_out) {
+          // the row's 16 pieces sit in 16 consecutive lanes: sum them, in a
+          // fixed order, and the first lane writes this 128-column block's partial
+          float v = ssq;
+          v += __shfl_xor(v, 1, 64);
+          v += __shfl_xor(v, 2, 64);
+          v += __shfl_xor(v, 4, 64);
+          v += __shfl_xor(v, 8, 64);
+          if (pc == 0 && row < M) a.ss_out[(size_t)(wcol0 >> 7) * M + row] = v;
         }
       }
       wave_sync();
@@ -712,14 +758,16 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     // interleave blocks of 32: columns wcol0 + 64*jp .. +31 are w1 rows, the
     // next 32 the matching w3 rows; this wave's g columns start at wcol0 / 2
     const int gcol0 = wcol0 >> 1;
+    float* s_rs = reinterpret_cast<float*>(lds);   // [BM] (below the staging areas)
+    row_scales(s_rs);
+    __syncthreads();
     static_for<0, MI>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       const int rb = wm * WTM + i * 32;
       static_for<0, 16>([&](auto rc) {
         constexpr int r = decltype(rc)::value;
         const int lr = 8 * (r >> 2) + 4 * hg + (r & 3);
-        const int row = m0 + rb + lr;
-        const float rs = row < M ? a.inv_rms[row] : 0.f;
+        const float rs = s_rs[rb + lr];
 #pragma unroll
         for (int jp = 0; jp < 2; ++jp) {
           const float gt = acc[i][2 * jp][r] * rs, up = acc[i][2 * jp + 1][r] * rs;

@@ -79,20 +79,41 @@ void launch_rmsnorm_apply(const T* x, const T* gamma, int rows, int D, float eps
 
 // ---------------------------------------------------------------------------
 // Embedding lookup -- "1. 嵌入层" of the MLX page: out[i] = table[ids[i]].
+// ss_out (optional): the rows' sums of squares per 128 columns, [ceil(D/128)][n]
+// (the statistic of the first block's RMSNorm)
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void k_embed(const T* table, int vocab, int D, const int32_t* ids, T* out) {
+__global__ __launch_bounds__(256) void k_embed(const T* table, int vocab, int D, const int32_t* ids, T* out,
+                                               float* ss_out, int n) {
   int i = blockIdx.x;
   int id = ids[i];
   bool ok = id >= 0 && id < vocab;
-  for (int c = threadIdx.x; c < D; c += 256)
-    out[(size_t)i * D + c] = ok ? table[(size_t)id * D + c] : T(0);
+  __shared__ float red[4];
+  for (int c0 = 0; c0 < D; c0 += 256) {
+    const int c = c0 + threadIdx.x;
+    float v = 0.f;
+    if (c < D) {
+      const T e = ok ? table[(size_t)id * D + c] : T(0);
+      out[(size_t)i * D + c] = e;
+      v = Elt<T>::to_f(e);
+    }
+    if (ss_out) {
+      const float t = warp_sum(v * v);
+      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        ss_out[(size_t)(c0 / 128) * n + i] = red[0] + red[1];
+        if (c0 + 128 < D) ss_out[(size_t)(c0 / 128 + 1) * n + i] = red[2] + red[3];
+      }
+      __syncthreads();
+    }
+  }
 }
 
 template <typename T>
-void launch_embed(const T* table, int vocab, int D, const int32_t* ids, int n, T* out, hipStream_t s) {
+void launch_embed(const T* table, int vocab, int D, const int32_t* ids, int n, T* out, hipStream_t s, float* ss_out) {
   if (n <= 0) return;
-  hipLaunchKernelGGL(k_embed<T>, dim3(n), dim3(256), 0, s, table, vocab, D, ids, out);
+  hipLaunchKernelGGL(k_embed<T>, dim3(n), dim3(256), 0, s, table, vocab, D, ids, out, ss_out, n);
 }
 
 // ---------------------------------------------------------------------------
@@ -611,7 +632,7 @@ void launch_emit(const int32_t* cur_id, int32_t* ids_out, int32_t* cursor, const
 #define INST(T)                                                                                     \
   template void launch_rms_inv<T>(const T*, int, int, float, float*, hipStream_t);                  \
   template void launch_rmsnorm_apply<T>(const T*, const T*, int, int, float, T*, hipStream_t);      \
-  template void launch_embed<T>(const T*, int, int, const int32_t*, int, T*, hipStream_t);          \
+  template void launch_embed<T>(const T*, int, int, const int32_t*, int, T*, hipStream_t, float*);  \
   template void launch_kv_write<T>(KVView, int, int, int, const T*, const T*, hipStream_t);         \
   template void launch_kv_read<T>(KVView, int, int, int, T*, T*, hipStream_t);                      \
   template void launch_repack_rows<T>(T*, const T*, int, int, const T*, int, int, int, int, int, hipStream_t); \

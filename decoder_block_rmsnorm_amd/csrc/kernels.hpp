@@ -62,7 +62,8 @@ void launch_rms_inv(const T* x, int rows, int D, float eps, float* inv_rms, hipS
 template <typename T>
 void launch_rmsnorm_apply(const T* x, const T* gamma, int rows, int D, float eps, T* out, hipStream_t s);
 template <typename T>
-void launch_embed(const T* table, int vocab, int D, const int32_t* ids, int n, T* out, hipStream_t s);
+void launch_embed(const T* table, int vocab, int D, const int32_t* ids, int n, T* out, hipStream_t s,
+                  float* ss_out = nullptr);
 // ids[r] = first index of the max of logits[r, :vocab]
 void launch_argmax(const float* logits, int rows, int vocab, int32_t* ids, hipStream_t s);
 // ids[r] = sampled id of row r (temperature <= 0: argmax), draw u[*u_off] when
@@ -124,8 +125,11 @@ struct GemmArgs {
   int ksplit;       // EPI_F32 only: K split into ksplit slices, slice s -> C + s*M*N
   // EPI_F32
   float* C;
-  // row scale (QKV / SWIGLU): inv_rms[M]
+  // row scale (QKV / SWIGLU): inv_rms[M], or, when inv_rms is null, 1/rms from
+  // rstat's partial sums of squares (rstat.ss[j * rstat.M + m], j < rstat.nb <=
+  // kGemmMaxRowPartials), reduced once per block
   const float* inv_rms;
+  RowStat rstat;
   // EPI_QKV
   bf16_t* q_out;          // [M, Nq]
   int Nq, Nkv, L;         // row m = b * L + l (or the ragged rows of kv.cu)
@@ -141,6 +145,8 @@ struct GemmArgs {
   int lens_inc, n_seq;    // or += lens_cu[b + 1] - lens_cu[b] when lens_cu is set
   const int32_t* lens_cu;
   bf16_t* branch;         // if non-null: the product before the residual add [M, N]
+  float* ss_out;          // if non-null: sums of squares of the stored rows, one per
+                          // 128-column block: ss_out[(col / 128) * M + row]
   // 4-bit B (with b_f16 and a_f16, gemm_q4_direct_ok shapes): B dequantized in
   // the kernel from codes q4w [N][K/8] words (code k at bits 4*(k%8)) and group
   // scale/bias pairs q4sb [K/64][N] (scale in the low 16 bits, bias in the
@@ -148,6 +154,7 @@ struct GemmArgs {
   const uint32_t* q4w;
   const uint32_t* q4sb;
 };
+constexpr int kGemmMaxRowPartials = 64;
 void launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t s);
 // K slices (1, 2 or 4) for an [M, N] x K product (B in fp16 when b_f16) whose
 // tile grid alone leaves the chip short of work; slice s writes fp32 partials
@@ -230,13 +237,14 @@ template <typename T>
 void launch_epi_qkv(const float* part, int ks, int M, int Nq, int Nkv, RowStat stat, int L,
                     const float2* rope, int traditional, T* q_out, KVView kv, hipStream_t s);
 // out = resid + sum(part); ss_out (optional): per-256-column-block sums of squares of
-// the stored rows, [ceil(N/256)][M] (a RowStat source for the next RMSNorm).
+// the stored rows, [ceil(N/256)][M] (a RowStat source for the next RMSNorm), or per
+// 128 columns, [ceil(N/128)][M], with ss_128.
 // lens_add (optional): lens_add[b] += lens_inc, or lens_cu[b + 1] - lens_cu[b]
 // when lens_cu is given, for b < n_seq.
 template <typename T>
 void launch_epi_resid(const float* part, int ks, int M, int N, const T* resid, T* out, float* ss_out,
                       int32_t* lens_add, int lens_inc, int n_seq, T* branch, hipStream_t s,
-                      const int32_t* lens_cu = nullptr);
+                      const int32_t* lens_cu = nullptr, int ss_128 = 0);
 template <typename T>
 void launch_epi_swiglu(const float* part, int ks, int M, int F2, int ib, RowStat stat, T* g_out,
                        hipStream_t s);

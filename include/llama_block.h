@@ -194,8 +194,8 @@ llama_status llama_block_set_diag(llama_block* blk, int32_t enable);
  * device, writes the summed milliseconds of each phase over the recorded calls to
  * phase_ms[0 .. *n_phases) (at most max_phases; 0 for phases not selected), the
  * number of calls to *n_calls, and disarms.  Phases, in launch order:
- *   bf16 prefill : rms(x), qkv gemm+rope+append, attention, wo gemm+residual,
- *                  rms(h), w1/w3 gemm+swiglu, w2 gemm+residual            (7)
+ *   bf16 prefill : rms(x), qkv gemm+rope+append, attention, wo gemm+residual
+ *                  (+ h statistics), w1/w3 gemm+swiglu, w2 gemm+residual    (6)
  *   fp32         : rms(x), qkv projection, qkv finish, attention, wo projection,
  *                  residual, w1/w3 projection, swiglu, w2 projection, residual (10)
  *   bf16 decode  : qkv projection (+ x statistics), qkv finish, attention,
