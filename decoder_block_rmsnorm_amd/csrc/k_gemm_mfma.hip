@@ -697,6 +697,23 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
   } else if constexpr (EPI == EPI_RESID) {
     float* sf = reinterpret_cast<float*>(stage);   // [32 rows][132] fp32
     constexpr int FST = 132;
+    // the residual pieces of subtile i (piece t: row (lane + 64 t) / 16, 8
+    // columns at 8 ((lane + 64 t) % 16); rows past M read row M - 1, unused).
+    // Subtile i + 1's pieces are requested before subtile i's stores: loads and
+    // stores share one counter, so waiting for them then never waits for the
+    // stores' completion.
+    uint4 rres[2][8];
+    auto load_resid = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int rb = wm * WTM + i * 32;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int c = lane + 64 * t, lr = c >> 4, pc = c & 15;
+        const int row = min(m0 + rb + lr, M - 1);
+        rres[i & 1][t] = ld16(a.resid + (size_t)row * N + wcol0 + 8 * pc);
+      }
+    };
+    load_resid(std::integral_constant<int, 0>{});
     static_for<0, MI>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       const int rb = wm * WTM + i * 32;
@@ -707,6 +724,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
         for (int j = 0; j < 4; ++j) sf[lr * FST + j * 32 + l32] = acc[i][j][r];
       });
       wave_sync();
+      if constexpr (i + 1 < MI) load_resid(std::integral_constant<int, i + 1>{});
       // 32 rows x 16 pieces of 8 columns: out = resid + acc, rounded once
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -718,7 +736,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
           const float4 f0 = *reinterpret_cast<const float4*>(sf + lr * FST + 8 * pc);
           const float4 f1 = *reinterpret_cast<const float4*>(sf + lr * FST + 8 * pc + 4);
           const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-          const uint4 rv = ld16(a.resid + idx);
+          const uint4 rv = rres[i & 1][t];
           const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
           uint32_t ow[4], bw[4];
 #pragma unroll
