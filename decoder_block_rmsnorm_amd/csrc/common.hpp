@@ -141,7 +141,10 @@ __device__ inline float warp_max(float v) {
   return v;
 }
 
-__device__ inline float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z), the quotient by the hardware reciprocal (1 ulp;
+// every caller rounds the product to bf16 or sums it in fp32): z -> -inf gives
+// -0, z -> +inf gives z
+__device__ inline float silu_f(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // 16-byte vector load/store helpers.
 // Tiled layout of the bf16 dense weights [N][K] (N a multiple of 16): 16-row
