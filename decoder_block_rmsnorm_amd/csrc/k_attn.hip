@@ -235,10 +235,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
           tmax = fmaxf(tmax, v);
         }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax * sl2);
+      // The exponent base m only has to stay within 2^8 below the running max
+      // (then p <= 256, exact in fp32 and safe in bf16, and o / l does not
+      // depend on m): it is raised, and o and l rescaled, only when some query
+      // of the wavefront needs it, so most tiles skip the 64 multiplies.
+      const bool raise = tmax * sl2 > m_run + 8.0f;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float m_new = raise ? tmax * sl2 : m_run;
+        // (a fully masked row so far keeps m = -inf, so alpha = 0 scales nothing)
+        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds) o_acc[ds] *= alpha;
+        m_run = m_new;
+      }
       // a fully masked row so far keeps m = -inf; use 0 as the exponent base then
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
       float psum = 0.f;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
@@ -249,10 +261,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
           psum += p;
         }
       psum += __shfl_xor(psum, 32, 64);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds) o_acc[ds] *= alpha;
+      l_run += psum;
       // O^T += V^T P^T : 4 key chunks of 16 (B operand straight from S^T registers)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
