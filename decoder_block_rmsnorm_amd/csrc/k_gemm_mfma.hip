@@ -464,14 +464,33 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     // kt's last sub-step publishes it): wait for that step's own loads (those of
     // the STG-2 later steps may still be in flight), then dequantize in the
     // slots after the fragment reads.
-    auto sub_first = [&](int kt, auto kc) {
+    // SPREAD: a step's direct loads are not issued together right after the
+    // barrier, where the four wavefronts it releases would all hand theirs to
+    // the address unit at once (and an MFMA stuck behind a load that cannot
+    // issue leaves the matrix core idle): LPS1 of them go out in the last
+    // sub-step, the rest on every other slot of the next step's first
+    // sub-step from SLOT0 (measured on 256-row tiles: 2 after the barrier and 6
+    // spread beat 4 + 4, 0 + 8 and all 8 together).  Every wait still finds the
+    // loads of the two steps after the one it waits for issued, so the counts
+    // are unchanged.
+    constexpr bool SPREAD = !Q4 && NKK == 2 && ((MI == 4 && NM == 2 * NF) || MI == 2);
+    constexpr int LPS1 = SPREAD ? 2 : LPS;
+    constexpr int SLOT0 = MI == 4 ? 5 : 1;
+    auto sub_first = [&](int kt, auto kc, auto with_loads) {
       constexpr int kk = decltype(kc)::value;
       constexpr int cur = kk & 1;
       const int st = kt % STG;
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (Q4 && kk == 0) wait_vmcnt<(STG - 2) * LPS>();
+      // (SPREAD: the rest of step kt-1+STG's loads)
+      [[maybe_unused]] StepAddr sa{};
+      if constexpr (SPREAD && decltype(with_loads)::value) sa = step_addr(kt - 1 + STG);
       mfmas_with(fa[cur], fb[cur], [&](int slot) {
         if (slot < NF) lfrag_one(st, kk + 1, slot, fa[cur ^ 1], fb[cur ^ 1]);
+        if constexpr (SPREAD && kk == 0 && decltype(with_loads)::value) {
+          if (slot >= SLOT0 && ((slot - SLOT0) & 1) == 0 && LPS1 + (slot - SLOT0) / 2 < LPS)
+            issue_at(sa, LPS1 + (slot - SLOT0) / 2);
+        }
         if constexpr (Q4 && kk == 0) {
           if (slot == NF) dequant_b(kt + 1);
         }
@@ -493,19 +512,28 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
       const StepAddr sa = step_addr(kt + STG);
       __builtin_amdgcn_sched_barrier(0);
       mfmas_with(fa[cur], fb[cur], [&](int slot) {
-        if (slot < NF) lfrag_one(nxt, 0, slot, fa[cur ^ 1], fb[cur ^ 1]);
-        else if (slot - NF < LPS) issue_at(sa, slot - NF);
+        if constexpr (SPREAD && MI == 4) {
+          // reads on the even slots, the two loads on slots 1 and 9
+          if ((slot & 1) == 0) lfrag_one(nxt, 0, slot / 2, fa[cur ^ 1], fb[cur ^ 1]);
+          else if (slot == 1 || slot == 9) issue_at(sa, slot / 8);
+        } else {
+          if (slot < NF) lfrag_one(nxt, 0, slot, fa[cur ^ 1], fb[cur ^ 1]);
+          else if (slot - NF < LPS1) issue_at(sa, slot - NF);
+        }
       }, std::false_type{});
+      if constexpr (!SPREAD) {
 #pragma unroll
-      for (int idx = NM - NF; idx < LPS; ++idx) issue_at(sa, idx);
+        for (int idx = NM - NF; idx < LPS; ++idx) issue_at(sa, idx);
+      }
+      static_assert(!SPREAD || (MI == 4 ? LPS1 == 2 : LPS1 <= NM - NF), "loads after the barrier");
     };
     // The loop body runs from one step's last sub-step into the next step's
     // leading ones, so the staggered waits sit in straight-line code (at a loop
     // head the compiler would merge them into a full wait).
-    static_for<0, NKK - 1>([&](auto kc) { sub_first(0, kc); });
+    static_for<0, NKK - 1>([&](auto kc) { sub_first(0, kc, std::false_type{}); });
     for (int kt = 0; kt + 1 < KT; ++kt) {
       sub_last(kt);
-      static_for<0, NKK - 1>([&](auto kc) { sub_first(kt + 1, kc); });
+      static_for<0, NKK - 1>([&](auto kc) { sub_first(kt + 1, kc, std::true_type{}); });
     }
     sub_last(KT - 1);
     // the loads issued past the last step land in LDS the epilogue reuses
