@@ -470,10 +470,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
     // issue leaves the matrix core idle): LPS1 of them go out in the last
     // sub-step, the rest on every other slot of the next step's first
     // sub-step from SLOT0 (measured on 256-row tiles: 2 after the barrier and 6
-    // spread beat 4 + 4, 0 + 8 and all 8 together).  Every wait still finds the
-    // loads of the two steps after the one it waits for issued, so the counts
-    // are unchanged.
-    constexpr bool SPREAD = !Q4 && NKK == 2 && ((MI == 4 && NM == 2 * NF) || MI == 2);
+    // spread beat 4 + 4, 0 + 8 and all 8 together).  The barrier's wait still
+    // finds the loads of the two steps after the one it waits for issued, so
+    // its count is unchanged; (Q4) the first sub-step's wait for the next step
+    // finds the step after that issued and only LPS1 loads of the one after.
+    constexpr bool SPREAD = NKK == 2 && ((MI == 4 && NM == 2 * NF) || MI == 2);
     constexpr int LPS1 = SPREAD ? 2 : LPS;
     constexpr int SLOT0 = MI == 4 ? 5 : 1;
     auto sub_first = [&](int kt, auto kc, auto with_loads) {
@@ -481,7 +482,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
       constexpr int cur = kk & 1;
       const int st = kt % STG;
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (Q4 && kk == 0) wait_vmcnt<(STG - 2) * LPS>();
+      if constexpr (Q4 && kk == 0) wait_vmcnt<SPREAD ? (STG - 3) * LPS + LPS1 : (STG - 2) * LPS>();
       // (SPREAD: the rest of step kt-1+STG's loads)
       [[maybe_unused]] StepAddr sa{};
       if constexpr (SPREAD && decltype(with_loads)::value) sa = step_addr(kt - 1 + STG);
