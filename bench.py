@@ -521,6 +521,33 @@ def copy_probe(mb, reps):
     print(json.dumps({"copy_probe_bytes": mb << 20, "reps": reps}), flush=True)
 
 
+def blas_probe(workload, steps, warmup):
+    """The workload's W1/W3 product through torch.matmul (hipBLASLt), timed with
+    events: the vendor library's rate on the same shape, for the profiles that
+    set it beside the block's own GEMM (same bf16 operands, fp32 accumulation;
+    hipBLASLt writes the whole product, the block's GEMM only g)."""
+    import torch
+    import workloads as W
+    wl = W.get(workload)
+    M, K, N = wl.batch * wl.seq_len, wl.shape.dim, 2 * wl.shape.ffn_dim
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(N, K, device="cuda", dtype=torch.bfloat16, generator=g) * 0.02
+    for _ in range(warmup):
+        c = torch.matmul(a, b.t())
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        c = torch.matmul(a, b.t())
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / max(steps, 1)
+    del c
+    print(json.dumps({"blas_probe": f"torch.matmul {M}x{K} . ({N}x{K})^T bf16", "workload": wl.name,
+                      "ms": round(ms, 4), "tflops": round(2.0 * M * K * N / (ms * 1e-3) / 1e12, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -541,6 +568,8 @@ def main():
                     help="minimum seconds of oracle time on the headline workload (0: no CPU baselines)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--blas-probe", action="store_true",
+                    help="only time the headline workload's W1/W3 product through torch.matmul and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (no collectives, no sharded "
@@ -553,6 +582,8 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         return copy_probe(args.copy_probe, max(args.steps, 1))
+    if args.blas_probe:
+        return blas_probe(args.workload, args.steps, args.warmup)
     cpu = args.cpu_seconds > 0
     cpu_rows = {}
     wl = W.get(args.workload)
