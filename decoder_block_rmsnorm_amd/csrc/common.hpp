@@ -130,6 +130,30 @@ struct KVView {
 // not for its global loads in flight.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// the value of lane l ^ M (M a power of two below 64): quad permutes and row
+// rotates (DPP) within 16 lanes, lane-row swaps across 16 and 32
+template <int M>
+__device__ inline float xor_lane(float v, int lane) {
+  const int b = __builtin_bit_cast(int, v);
+  if constexpr (M == 1) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  } else if constexpr (M == 2) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  } else if constexpr (M == 4) {
+    const int up = __builtin_amdgcn_update_dpp(0, b, 0x114, 0xF, 0xF, false);  // row_shr:4 (lane - 4)
+    const int dn = __builtin_amdgcn_update_dpp(0, b, 0x104, 0xF, 0xF, false);  // row_shl:4 (lane + 4)
+    return __builtin_bit_cast(float, (lane & 4) ? up : dn);
+  } else if constexpr (M == 8) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, b, 0x128, 0xF, 0xF, false));  // row_ror:8
+  } else {
+    // swap(v, v): the first result holds the partner's value in the odd
+    // 16-/32-lane rows, the second in the even ones
+    const auto p = M == 16 ? __builtin_amdgcn_permlane16_swap(b, b, false, false)
+                           : __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    return __builtin_bit_cast(float, (int)((lane & M) ? p[0] : p[1]));
+  }
+}
+
 __device__ inline float warp_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

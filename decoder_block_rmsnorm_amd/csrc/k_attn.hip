@@ -353,15 +353,21 @@ __global__ __launch_bounds__(BM ? 512 : 256) __attribute__((amdgpu_waves_per_eu(
     b = wid / (n_splits * VG);
   }
   const int g = vg / nv, h0 = (vg % nv) * 16, nr = min(16, n_rep - h0);
-  const int pos = kv.lens[b];               // the new token's position; keys 0..pos
-  const int nkeys = pos + 1;
-  const int k_lo = kv.window > 0 ? max(0, nkeys - kv.window) : 0;   // sliding window: keys k_lo..pos
-  // splits tile the keys from the window's start (rounded down to a 64-key step)
-  const int k_begin = (k_lo & ~63) + c * split_len;
-  const int k_end = min(nkeys, k_begin + split_len);
   const bool qvalid = l16 < nr;
   const int hq = g * n_rep + h0 + (qvalid ? l16 : 0);
-
+  // BM without a window: the page-table entries of the wavefront's first
+  // kBMPages steps (its range starts at c * split_len) are requested together
+  // with the length and the query, so the first K/V loads wait for one
+  // round trip, not two; entries past the last key are read (clamped to the
+  // table row) and not used
+  constexpr int kBMPages = 4;
+  const int32_t* trow = kv.table + (size_t)b * kv.pps;
+  int pg[kBMPages];
+  if constexpr (BM) {
+#pragma unroll
+    for (int j = 0; j < kBMPages; ++j) pg[j] = trow[min((c * split_len + 64 * j) / kv.ps, kv.pps - 1)];
+  }
+  const int pos = kv.lens[b];               // the new token's position; keys 0..pos
   // Q^T fragments: lane holds Q[q = l16][d = 32*kc + 8*hg .. +7]
   bf16x8 qf[4];
   {
@@ -369,6 +375,14 @@ __global__ __launch_bounds__(BM ? 512 : 256) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) qf[kc] = as_bf16x8(qvalid ? ld16(qrow + 32 * kc + 8 * hg) : make_uint4(0, 0, 0, 0));
   }
+  // (one wait for all of them here, before anything depends on the length)
+  if constexpr (BM) asm volatile("" ::"s"(pg[0]), "s"(pg[1]), "s"(pg[2]), "s"(pg[3]), "s"(pos));
+  const int nkeys = pos + 1;
+  const int k_lo = kv.window > 0 ? max(0, nkeys - kv.window) : 0;   // sliding window: keys k_lo..pos
+  // splits tile the keys from the window's start (rounded down to a 64-key step)
+  const int k_begin = (k_lo & ~63) + c * split_len;
+  const int k_end = min(nkeys, k_begin + split_len);
+
   const bf16_t* Kp = (const bf16_t*)kv.k;
   const bf16_t* Vp = (const bf16_t*)kv.v;
   const float sl2 = 1.4426950408889634f / sqrtf(128.f);
@@ -377,7 +391,13 @@ __global__ __launch_bounds__(BM ? 512 : 256) __attribute__((amdgpu_waves_per_eu(
   for (int i = 0; i < 8; ++i) o_acc[i] = (f32x4){};
   float m_run = -INFINITY, l_run = 0.f;
   for (int k0 = k_begin; k0 < k_end; k0 += 64) {
-    const size_t base = kv.page_base(b, k0);
+    const int j = (k0 - k_begin) >> 6;
+    int page;
+    if (BM && kv.window <= 0 && j < kBMPages)
+      page = j == 0 ? pg[0] : j == 1 ? pg[1] : j == 2 ? pg[2] : pg[3];
+    else
+      page = trow[k0 / kv.ps];
+    const size_t base = (size_t)page * kv.G * kv.ps * 128;
     // this head's K and V blocks, 64-slot sub-block of k0 (tiled layout)
     const size_t sub = base + (size_t)g * kv.ps * 128 + (size_t)((k0 % kv.ps) >> 6) * (64 * 128);
     const bf16_t* kpage = Kp + sub + lane * 8;
@@ -410,8 +430,10 @@ __global__ __launch_bounds__(BM ? 512 : 256) __attribute__((amdgpu_waves_per_eu(
         s_acc[st][i] = v;
         tmax = fmaxf(tmax, v);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    // (lane-row swaps, not LDS permutes: nothing else in the loop waits on the
+    // LDS / scalar counter)
+    tmax = fmaxf(tmax, xor_lane<16>(tmax, lane));
+    tmax = fmaxf(tmax, xor_lane<32>(tmax, lane));
     // running max in log2 units: p = 2^(s * log2(e)/sqrt(d) - m), one fma + v_exp_f32
     const float m_new = fmaxf(m_run, tmax * sl2);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -424,8 +446,8 @@ __global__ __launch_bounds__(BM ? 512 : 256) __attribute__((amdgpu_waves_per_eu(
         s_acc[st][i] = p;
         psum += p;
       }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
+    psum += xor_lane<16>(psum, lane);
+    psum += xor_lane<32>(psum, lane);
     l_run = l_run * alpha + psum;
     m_run = m_new;
     bf16x8 pb[2];

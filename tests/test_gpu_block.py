@@ -364,15 +364,28 @@ def test_q4_decode_single_row_empty_cache():
     _q4_decode_case(SMALL_Q4, 1, 18, lens=[0])
 
 
-def _q4_decode_case(s, B, seed, lens=None):
+# One sequence with a cache of 1024 positions: each head's keys go to eight
+# 128-key ranges merged in one block.  Ranges past the last key are empty (all
+# but the first at 0 cached keys); 511 cached keys end one range exactly, 512
+# put the new token alone in the next; 900 reach the last range; and six ranges
+# with two query heads per kv head.
+@pytest.mark.parametrize("case", ["empty", "range_full", "one_key_next", "all_ranges", "gqa_six_ranges"])
+def test_q4_decode_single_row_longer_cache(case):
+    lens = {"empty": 0, "range_full": 511, "one_key_next": 512, "all_ranges": 900, "gqa_six_ranges": 700}[case]
+    s = Q4_SINGLE["gqa_halves_k2"] if case == "gqa_six_ranges" else SMALL_Q4
+    _q4_decode_case(s, 1, 19, lens=[lens], max_seq=1024)
+
+
+def _q4_decode_case(s, B, seed, lens=None, max_seq=256):
     rng = W.Rng(seed)
     lens = lens or [77, 200, 3][:B]
+    S = max(200, max(lens))
     x = rng.normal((B, 1, s.dim), 1.0, "bf16")
-    kv = (rng.normal((B, 200, s.n_kv_heads, s.head_dim), 1.0, "bf16"),
-          rng.normal((B, 200, s.n_kv_heads, s.head_dim), 1.0, "bf16"))
+    kv = (rng.normal((B, S, s.n_kv_heads, s.head_dim), 1.0, "bf16"),
+          rng.normal((B, S, s.n_kv_heads, s.head_dim), 1.0, "bf16"))
     w = W.draw_block_weights(s, rng)
-    _flush(f"case: 4-bit decode B={B} dim={s.dim} ffn={s.ffn_dim} kv_heads={s.n_kv_heads}")
-    max_seq = 256
+    _flush(f"case: 4-bit decode B={B} dim={s.dim} ffn={s.ffn_dim} kv_heads={s.n_kv_heads} lens={lens} "
+           f"max_seq={max_seq}")
     blk, wd = G.make_block(s, w, max_seq)
     cache = G.make_cache(s, 1, B, max_seq)
     for b in range(B):
