@@ -128,7 +128,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
   auto Bs = [&](int b) { return lds + b * (BM + BN) * LDS_ST + BM * LDS_ST; };
 
   const int M = a.M, N = a.N;
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = N / BN;
+  const int n_lo = a.n_lo, n_hi = a.n_hi > 0 ? a.n_hi : N;   // this launch's columns
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (n_hi - n_lo) / BN;
   // XCD-major renumbering, then grouped ordering; K slice = slowest index
   const int nblk = gridDim.x;
   int bid = blockIdx.x;
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
   const int gsz = min(tiles_m - first_m, GROUP_M);
   const int tm = first_m + (bid % per_group) % gsz;
   const int tn = (bid % per_group) / gsz;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = n_lo + tn * BN;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hg = lane >> 5;
@@ -840,7 +841,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
 
 template <int BM, int BN, int NW, int DEPTH, int EPI, bool F16, bool Q4 = false>
 static void launch_cfg(const GemmArgs& a, hipStream_t s) {
-  const int tiles = ((a.M + BM - 1) / BM) * (a.N / BN) * (EPI == EPI_F32 && a.ksplit > 1 ? a.ksplit : 1);
+  const int ncols = (a.n_hi > 0 ? a.n_hi : a.N) - a.n_lo;
+  const int tiles = ((a.M + BM - 1) / BM) * (ncols / BN) * (EPI == EPI_F32 && a.ksplit > 1 ? a.ksplit : 1);
   const size_t lds = Q4 ? (size_t)4 * ((BM + BN) * 32 + BN * 8 + NW * BN * 2) * sizeof(bf16_t)
                      : DEPTH == 4 ? (size_t)(BM + BN) * 160 * sizeof(bf16_t)
                      : DEPTH == 0 || DEPTH == 3 ? std::max<size_t>((size_t)(BM + BN) * 128 * sizeof(bf16_t), 4096 + 4 * 17408)
@@ -856,9 +858,34 @@ static void launch_cfg(const GemmArgs& a, hipStream_t s) {
   g_clock = LaunchClock{};
 }
 
+// Rounds of 256 blocks, 128-row tiles counted at 0.6 of a 256-row round (half
+// the work each, 20% dearer: measured).  Returns the 256-column tile columns
+// to run as 256-row tiles before the rest run as 128-row tiles (0: one shape),
+// the split that ends soonest when the 256-row grid leaves a partial round;
+// `cost` is its time in rounds.
+static int gemm_two_shapes(int M, int N, double& cost) {
+  const long tm2 = (M + 255) / 256, tm1 = (M + 127) / 128, tn = N / 256;
+  auto rounds = [](long t) { return (double)((t + 255) / 256); };
+  const double c256 = rounds(tm2 * tn), c128 = 0.6 * rounds(tm1 * tn);
+  cost = std::min(c256, c128);
+  int best = 0;
+  // the first launch: the tile columns that fill r whole rounds
+  for (long r = 1; r * 256 < tm2 * tn; ++r) {
+    const long nb = r * 256 / tm2;
+    if (nb <= 0 || nb >= tn) continue;
+    const double c = rounds(nb * tm2) + 0.6 * rounds((tn - nb) * tm1);
+    if (c < cost - 1e-9) {
+      cost = c;
+      best = (int)nb;
+    }
+  }
+  return best;
+}
+
 // Tile choice: the direct-to-LDS ring where the shape allows, 128-row tiles
-// when their rounds of 256 blocks finish sooner (half the work each, counted
-// 20% dearer: measured) than those of 256-row tiles; register-staged tiles
+// when their rounds of 256 blocks finish sooner than those of 256-row tiles,
+// and both (two launches over disjoint columns) when the 256-row grid's last
+// round would run part empty and the split ends sooner; register-staged tiles
 // otherwise.
 template <int EPI, bool F16>
 static void launch_epi(const GemmArgs& a, hipStream_t s) {
@@ -889,6 +916,24 @@ static void launch_epi(const GemmArgs& a, hipStream_t s) {
     // work each, counted 20% dearer: measured) than those of 256-row tiles
     const long t256 = (long)((a.M + 255) / 256) * (a.N / 256), t128 = (long)((a.M + 127) / 128) * (a.N / 256);
     const bool use128 = ((t128 + 255) / 256) * 0.6 < (double)((t256 + 255) / 256);
+    if (big && !(EPI == EPI_F32 && a.ksplit > 1) && a.n_hi == 0) {
+      double cost;
+      const int nb = gemm_two_shapes(a.M, a.N, cost);
+      if (nb > 0) {
+        // (a launch clock brackets both launches; block 0 of the first alone
+        // advances the lengths)
+        const LaunchClock clk = g_clock;
+        GemmArgs a1 = a, a2 = a;
+        a1.n_hi = nb * 256;
+        a2.n_lo = nb * 256;
+        a2.lens_add = nullptr;
+        g_clock = LaunchClock{clk.start, nullptr};
+        launch_cfg<256, 256, 4, 0, EPI, F16>(a1, s);
+        g_clock = LaunchClock{nullptr, clk.stop};
+        launch_cfg<128, 256, 4, 0, EPI, F16>(a2, s);
+        return;
+      }
+    }
     if (big && use128 && !(EPI == EPI_F32 && a.ksplit > 1)) return launch_cfg<128, 256, 4, 0, EPI, F16>(a, s);
     if (!big && a32 && n256 && t128 >= 240 && !(EPI == EPI_F32 && a.ksplit > 1))
       return launch_cfg<128, 256, 4, 0, EPI, F16>(a, s);

@@ -153,6 +153,9 @@ struct GemmArgs {
   // high, bf16): B[n][k] = fp16(scale * code + bias); B itself is unused
   const uint32_t* q4w;
   const uint32_t* q4sb;
+  // columns [n_lo, n_hi) of the product only (n_hi = 0: up to N); set by the
+  // launcher when it splits one product over two tile shapes
+  int n_lo, n_hi;
 };
 constexpr int kGemmMaxRowPartials = 64;
 void launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t s);

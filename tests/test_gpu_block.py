@@ -308,6 +308,22 @@ def test_bf16_decode_ragged_lengths(shape):
     assert cache.get_lens(0, B) == [l + 1 for l in lens]
 
 
+# A 512-token prompt with a 16640-wide feed-forward: the W1/W3 product is 2 x
+# 130 tiles of 256 x 256 (one round of 256 blocks and 4 more), so it runs as
+# two launches, 256-row tiles over its first 128 tile columns and 128-row
+# tiles over the last 2 (the same product as one tile shape, column for column)
+def test_bf16_prefill_gemm_over_two_tile_shapes():
+    s = W.BlockShape(dim=512, n_heads=4, n_kv_heads=4, ffn_dim=16640, dtype="bf16")
+    rng = W.Rng(15)
+    x = rng.normal((1, 512, s.dim), 1.0, "bf16")
+    w = W.draw_block_weights(s, rng)
+    _flush("case: bf16 prefill 512 tokens, ffn 16640 (W1/W3 over two tile shapes)")
+    blk, cache, sc, y = _run_prefill(s, w, x)
+    r = _oracle(s, w, x)
+    G.check("bf16", y, np.stack(r["y"]), "y")
+    _check_branches(s, blk, sc, r, y, 1, 512)
+
+
 def test_bf16_prefill_then_decode_steps_match_oracle():
     s = SMALL_GQA
     rng = W.Rng(14)
