@@ -229,21 +229,26 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
       // p = 2^(s * log2(e)/sqrt(d) - m) is one fma and one v_exp_f32)
       // some key may exceed some query position, or (window) lie before one
       // query's window
+      // (a wave-uniform branch around per-lane selects: no divergent branch
+      // per score on the tiles that need no mask)
       const bool need_mask = key0 + BK - 1 > S + wq0 || (W > 0 && key0 < S + wq0 + 32 - W);
+      if (need_mask) {
+        const int rel = my_pos - key0 - 8 * hg;   // key offset (st * 32 + 16 (i / 8) + i % 8) past which to mask
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int ko = st * 32 + 16 * (i >> 3) + (i & 7);
+            const bool out = ko > rel || (W > 0 && ko <= rel - W);
+            s_acc[st][i] = out ? -INFINITY : s_acc[st][i];
+          }
+      }
       float tmax = -INFINITY;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float v = s_acc[st][i];
-          if (need_mask) {
-            int key = key0 + st * 32 + 16 * (i >> 3) + 8 * hg + (i & 7);
-            if (key > my_pos || (W > 0 && key <= my_pos - W)) v = -INFINITY;
-          }
-          s_acc[st][i] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s_acc[st][i]);
+      tmax = fmaxf(tmax, xor_lane<32>(tmax, lane));
       // The exponent base m only has to stay within 2^8 below the running max
       // (then p <= 256, exact in fp32 and safe in bf16, and o / l does not
       // depend on m): it is raised, and o and l rescaled, only when some query
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
           s_acc[st][i] = p;
           psum += p;
         }
-      psum += __shfl_xor(psum, 32, 64);
+      psum += xor_lane<32>(psum, lane);
       l_run += psum;
       // O^T += V^T P^T : 4 key chunks of 16 (B operand straight from S^T registers)
 #pragma unroll
