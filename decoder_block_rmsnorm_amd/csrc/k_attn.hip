@@ -147,28 +147,45 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
   // block's last tile are read and not used)
   const int32_t* trow = kv.table + (size_t)b * kv.pps;
   auto page_of = [&](int t) { return trow[min(t * BK / kv.ps, kv.pps - 1)]; };
+  // A tile is the 64-slot block (slot0 / 64) of one page: contiguous in the
+  // tiled layout, where a thread's elements sit at offsets fixed for every
+  // tile (slot0 is a multiple of 64), computed once here.
+  int offk[4], offv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    offk[i] = kv_tiled_k(c >> 4, (c & 15) * 8);
+    offv[i] = kv_tiled_v((c & 7) * 8, c >> 3);
+  }
   auto load_tile = [&](int t, int page) {
-    int key0 = t * BK;
-    size_t base = (size_t)page * kv.G * kv.ps * D;
-    int slot0 = key0 % kv.ps;
-    int nvalid = kmax_block - key0;
+    const int key0 = t * BK;
+    // this head's K (and V) block of the page, its 64-slot block of key0
+    const size_t blk = ((size_t)page * kv.G + g) * kv.ps * D + (size_t)((key0 % kv.ps) >> 6) * (BK * D);
+    const bf16_t* kb = Kp + blk;
+    const bf16_t* vb = Vp + blk;
+    const int nvalid = kmax_block - key0;
+    if (nvalid >= BK) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int c = tid + 256 * i;
-      int kr = c >> 4, kc = c & 15;
-      const size_t blk = base + (size_t)g * kv.ps * D;   // this head's K (and V) block of the page
-      kreg[i] = kr < nvalid ? ld16(Kp + blk + kv_tiled_k(slot0 + kr, kc * 8)) : make_uint4(0, 0, 0, 0);
-      int vr = c >> 3, vc = c & 7;
-      uint4 v = ld16(Vp + blk + kv_tiled_v(slot0 + vc * 8, vr));
-      int nok = nvalid - vc * 8;
-      if (nok < 8) {
-        uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (e >= nok) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-        v = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int i = 0; i < 4; ++i) {
+        kreg[i] = ld16(kb + offk[i]);
+        vreg[i] = ld16(vb + offv[i]);
       }
-      vreg[i] = v;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = tid + 256 * i;
+        kreg[i] = (c >> 4) < nvalid ? ld16(kb + offk[i]) : make_uint4(0, 0, 0, 0);
+        uint4 v = ld16(vb + offv[i]);
+        const int nok = nvalid - (c & 7) * 8;
+        if (nok < 8) {
+          uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e >= nok) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          v = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        vreg[i] = v;
+      }
     }
   };
   auto store_tile = [&](int buf) {
@@ -233,14 +250,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
       // per score on the tiles that need no mask)
       const bool need_mask = key0 + BK - 1 > S + wq0 || (W > 0 && key0 < S + wq0 + 32 - W);
       if (need_mask) {
-        const int rel = my_pos - key0 - 8 * hg;   // key offset (st * 32 + 16 (i / 8) + i % 8) past which to mask
+        // key offsets ko = st * 32 + 16 (i / 8) + i % 8 kept: lo < ko <= rel,
+        // i.e. ko - lo - 1 in [0, n_keep) (one unsigned compare per score)
+        const int rel = my_pos - key0 - 8 * hg;
+        const int lo = W > 0 ? rel - W : -1;
+        const unsigned n_keep = rel > lo ? (unsigned)(rel - lo) : 0u;
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int ko = st * 32 + 16 * (i >> 3) + (i & 7);
-            const bool out = ko > rel || (W > 0 && ko <= rel - W);
-            s_acc[st][i] = out ? -INFINITY : s_acc[st][i];
+            s_acc[st][i] = (unsigned)(ko - lo - 1) < n_keep ? s_acc[st][i] : -INFINITY;
           }
       }
       float tmax = -INFINITY;
