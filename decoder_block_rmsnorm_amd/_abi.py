@@ -89,6 +89,12 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m decoder_block_rmsnorm_amd.build` "
                            f"(or __graft_entry__.build()); the decoder block has no non-HIP implementation")
+    # torch's HIP runtime first: the library then binds to the copy torch
+    # already holds (two runtimes in one process do not share devices)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = C.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

@@ -972,6 +972,12 @@ static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const
   llama_status st = check_call(blk, c, layer, x, y, batch, L, Ls, scratch, sbytes, decode,
                                n_splits_override > 0 ? split_len_override : kSplitLen, &S);
   if (st != LLAMA_OK) return st;
+  if (plan_log_on())
+    plan_log("block %s: layer %d, %d sequences, %s, %s weights%s; decode attention %d splits of %d keys",
+             decode ? "decode" : "prefill", layer, batch,
+             Ls ? "ragged new-token counts" : decode ? "one token each" : "equal new-token counts",
+             blk->dm.q4 ? "4-bit" : blk->dm.bf16 ? "bf16" : "fp32", xstat ? ", x statistic from its writer" : "",
+             S.n_splits, S.split_len);
   KVView kv = kv_view(c, layer);
   kv.window = blk->cfg.sliding_window;
   char* sc = (char*)scratch;
@@ -1018,12 +1024,14 @@ static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const
 
 extern "C" llama_status llama_block_prefill(llama_block* blk, llama_kvcache* c, int32_t layer, const void* x, void* y,
                                             int32_t batch, int32_t seq_len, void* scratch, size_t sbytes, void* stream) {
+  TraceRange trace_("llama_block_prefill");
   return enqueue(blk, c, layer, x, y, batch, seq_len, scratch, sbytes, false, 0, 0, (hipStream_t)stream);
 }
 
 extern "C" llama_status llama_block_prefill_ragged(llama_block* blk, llama_kvcache* c, int32_t layer, const void* x,
                                                    void* y, int32_t batch, const int32_t* seq_lens, void* scratch,
                                                    size_t sbytes, void* stream) {
+  TraceRange trace_("llama_block_prefill_ragged");
   if (!seq_lens) return fail(LLAMA_ERR_INVALID_ARG, "seq_lens must be non-NULL");
   if (batch > kMaxSetI32 - 1) return fail(LLAMA_ERR_UNSUPPORTED, "ragged prefill of more than %d sequences", kMaxSetI32 - 1);
   return enqueue(blk, c, layer, x, y, batch, 1, scratch, sbytes, false, 0, 0, (hipStream_t)stream, seq_lens);
@@ -1031,6 +1039,7 @@ extern "C" llama_status llama_block_prefill_ragged(llama_block* blk, llama_kvcac
 
 extern "C" llama_status llama_block_decode(llama_block* blk, llama_kvcache* c, int32_t layer, const void* x, void* y,
                                            int32_t batch, void* scratch, size_t sbytes, void* stream) {
+  TraceRange trace_("llama_block_decode");
   return enqueue(blk, c, layer, x, y, batch, 1, scratch, sbytes, true, 0, 0, (hipStream_t)stream);
 }
 
@@ -1067,6 +1076,7 @@ static llama_status noalloc_scratch(void** out) {
 
 extern "C" llama_status llama_block_decode_noalloc(llama_block* blk, llama_kvcache* c, int32_t layer, const void* x,
                                                    void* y, int32_t batch, void* stream) {
+  TraceRange trace_("llama_block_decode_noalloc");
   if (!blk || !c) return fail(LLAMA_ERR_INVALID_ARG, "block and cache must be non-NULL");
   if (batch > 0) {
     const size_t need = scratch_layout(blk->cfg, blk->dm, batch, batch, c->cfg.max_seq, true).total;
@@ -1085,6 +1095,7 @@ extern "C" llama_status llama_block_decode_noalloc(llama_block* blk, llama_kvcac
 // ---------------------------------------------------------------- stack ends
 extern "C" llama_status llama_embed(const void* table, int32_t vocab, int32_t dim, int32_t dtype, const int32_t* ids,
                                     int32_t n, void* out, void* stream) {
+  TraceRange trace_("llama_embed");
   if (!table || !ids || !out) return fail(LLAMA_ERR_INVALID_ARG, "table, ids and out must be non-NULL");
   if (vocab <= 0 || dim <= 0 || n < 0) return fail(LLAMA_ERR_INVALID_ARG, "vocab and dim must be positive, n >= 0");
   if (dtype == LLAMA_F32)
@@ -1166,11 +1177,13 @@ extern "C" llama_status llama_lm_head_argmax(const llama_linear* head, int32_t w
                                              const void* fnorm, float eps, const void* x, int32_t B, int32_t D,
                                              int32_t V, float* logits, int32_t* ids, void* scratch, size_t sbytes,
                                              void* stream) {
+  TraceRange trace_("llama_lm_head_argmax");
   return head_enqueue(head, wf, gs, dt, fnorm, eps, x, B, D, V, logits, ids, scratch, sbytes, (hipStream_t)stream);
 }
 
 extern "C" llama_status llama_sample(const float* logits, int32_t batch, int32_t vocab, float temperature,
                                      float top_p, const float* u, int32_t* ids, void* stream) {
+  TraceRange trace_("llama_sample");
   if (!logits || !ids || (temperature > 0.f && !u))
     return fail(LLAMA_ERR_INVALID_ARG, "logits, ids and (temperature > 0) u must be non-NULL");
   if (batch <= 0 || vocab <= 0) return fail(LLAMA_ERR_INVALID_ARG, "batch and vocab must be positive");
@@ -1272,6 +1285,7 @@ static float* stack_x_stats(const llama_stack* st, void* bs, int T) {
 extern "C" llama_status llama_stack_generate(llama_stack* st, llama_kvcache* cache, const int32_t* prompt, int32_t P,
                                              int32_t n_steps, int32_t* ids_out, float* logits_out, void* scratch,
                                              size_t sbytes, int32_t use_graph, void* stream) {
+  TraceRange trace_("llama_stack_generate");
   if (!st || !cache || !prompt || !ids_out || !scratch)
     return fail(LLAMA_ERR_INVALID_ARG, "stack, cache, prompt, ids_out and scratch must be non-NULL");
   if (P <= 0 || n_steps < 0) return fail(LLAMA_ERR_INVALID_ARG, "prompt_len must be > 0 and n_steps >= 0");
@@ -1369,6 +1383,7 @@ extern "C" llama_status llama_stack_generate_recompute(llama_stack* st, llama_kv
                                                        int32_t P, int32_t n_steps, int32_t* ids_out,
                                                        float* logits_out, void* scratch, size_t sbytes,
                                                        void* stream) {
+  TraceRange trace_("llama_stack_generate_recompute");
   if (!st || !cache || !prompt || !ids_out || !scratch)
     return fail(LLAMA_ERR_INVALID_ARG, "stack, cache, prompt, ids_out and scratch must be non-NULL");
   if (P <= 0 || n_steps < 0) return fail(LLAMA_ERR_INVALID_ARG, "prompt_len must be > 0 and n_steps >= 0");

@@ -341,6 +341,8 @@ void launch_attn_prefill_bf16(const bf16_t* q, KVView kv, int B, int L, int H, i
   // tiles per block, complementary ones, measured no faster.)
   const long blocks = (long)H * B * n_qt;
   const int flip = blocks <= 512 ? 1 : 0;
+  plan_log("attention prefill: %d heads (%d kv) x %d sequences x %d query tiles of %d, %s order", H, G, B, n_qt,
+           fa::BQ, flip ? "half-flipped" : "heavy-first");
   dim3 grid(H, B, n_qt);
   hipLaunchKernelGGL(k_attn_prefill_bf16, grid, dim3(256), 0, s, q, kv, B, L, H, G, n_qt, flip, out);
 }
@@ -629,6 +631,8 @@ void launch_attn_decode_bf16(const bf16_t* q, KVView kv, int B, int H, int G, in
     // few (b, g) pairs and a short cache: one block each, eight key ranges of
     // whole 64-key steps, merged in the block
     const int sl8 = (int)(((keys + 7) / 8 + 63) / 64 * 64);
+    plan_log("attention decode: %d sequences x %d head groups, one block each, 8 ranges of %d keys merged in LDS", B,
+             VG, sl8);
     hipExtLaunchKernelGGL(k_attn_decode_bf16<true>, dim3(B * VG), dim3(512), 0, s, g_clock.start, g_clock.stop, 0, q,
                           kv, B, H, G, 8, sl8, part_o, part_ml, out);
     g_clock = LaunchClock{};
@@ -637,6 +641,8 @@ void launch_attn_decode_bf16(const bf16_t* q, KVView kv, int B, int H, int G, in
   // (a grid of fewer wavefronts than a round of the chip goes one wavefront
   // per block, so the dispatcher spreads it over all compute units)
   const int waves = B * VG * n_splits, wpb = waves < 1024 ? 1 : 4;
+  plan_log("attention decode: %d sequences x %d head groups x %d splits of %d keys, %d wavefronts per block, merge "
+           "kernel", B, VG, n_splits, split_len, wpb);
   hipExtLaunchKernelGGL(k_attn_decode_bf16<false>, dim3((waves + wpb - 1) / wpb), dim3(64 * wpb), 0, s, g_clock.start,
                         nullptr, 0, q, kv, B, H, G, n_splits, split_len, part_o, part_ml, nullptr);
   const int bh = B * H, mpb = bh < 1024 ? 1 : 4;

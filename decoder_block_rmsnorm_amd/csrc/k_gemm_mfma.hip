@@ -847,6 +847,11 @@ static void launch_cfg(const GemmArgs& a, hipStream_t s) {
                      : DEPTH == 4 ? (size_t)(BM + BN) * 160 * sizeof(bf16_t)
                      : DEPTH == 0 || DEPTH == 3 ? std::max<size_t>((size_t)(BM + BN) * 128 * sizeof(bf16_t), 4096 + 4 * 17408)
                                 : (size_t)2 * (BM + BN) * gm::LDS_ST * sizeof(bf16_t);
+  if (plan_log_on())
+    plan_log("gemm M %d N %d K %d cols [%d, %d): %dx%d tiles, %d waves, %s, split-K %d, epilogue %d%s, %d blocks",
+             a.M, a.N, a.K, a.n_lo, a.n_hi > 0 ? a.n_hi : a.N, BM, BN, NW,
+             DEPTH == 0 ? "direct-to-LDS 4-stage ring" : "register-staged", a.ksplit > 0 ? a.ksplit : 1, EPI,
+             Q4 ? ", 4-bit B dequantized in LDS" : F16 ? ", fp16" : "", tiles);
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void*)k_gemm_mfma<BM, BN, NW, DEPTH, EPI, F16, Q4>,

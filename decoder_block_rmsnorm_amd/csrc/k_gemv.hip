@@ -251,6 +251,9 @@ template <int NW, bool TILED, bool SS, int EPI>
 static void gemv_mt(const bf16_t* X, const bf16_t* W, float* partial, int M, int N, int K, int ks, float* ss_out,
                     const GemvSwiglu& e, hipStream_t s) {
   dim3 grid(N / (64 * NW), ks);
+  plan_log("gemv M %d N %d K %d: %d columns per block, split-K %d (%d blocks), %s weights%s%s", M, N, K, 64 * NW, ks,
+           (int)(grid.x * grid.y), TILED ? "tiled" : "row-strip", SS ? ", x statistic" : "",
+           EPI == EPI_SWIGLU ? ", SwiGLU in the kernel" : "");
   if (M <= 16)
     hipLaunchKernelGGL((k_gemv_bf16<NW, 1, TILED, SS, EPI>), grid, dim3(256), 0, s, X, W, partial, M, N, K, ks,
                        ss_out, e);
@@ -877,6 +880,8 @@ bool launch_q4_fused(const bf16_t* X, const uint32_t* words, const bf16_t* scale
   e.kp = kp;
   e.rpw = rw;
   const dim3 grid(q4_fused_blocks(e.N, e.K));
+  plan_log("4-bit gemv (one row) N %d K %d: %d blocks, %d rows per wavefront, %d K parts, %d chunks per lane, "
+           "epilogue %d", e.N, e.K, (int)grid.x, rw, kp, ni, e.epi);
 #define Q4L(n, k, r, E) \
   hipLaunchKernelGGL((k_q4_fused<n, k, r, q4_depth<r>(), E>), grid, dim3(256), 0, s, X, words, scales, biases, e)
 #define Q4F(n, k, E)               \
@@ -921,6 +926,7 @@ void launch_gemv_q4(const bf16_t* X, int norm, RowStat stat, float eps, const fl
   hipLaunchKernelGGL(k_q4_prep, dim3(M), dim3(1024), 0, s, X, norm, stat, eps, gamma, M, K, xh_buf, xsum_buf);
   const int rpw = 2;
   const int blocks = (N + 4 * rpw - 1) / (4 * rpw);
+  plan_log("4-bit gemv M %d N %d K %d: prepared activations, %d blocks of %d rows", M, N, K, blocks, 4 * rpw);
   if (M == 1)
     hipLaunchKernelGGL(k_gemv_q4<1>, dim3(blocks), dim3(256), 0, s, xh_buf, xsum_buf, words, scales, biases, y, M,
                        N, K, gs, rpw);

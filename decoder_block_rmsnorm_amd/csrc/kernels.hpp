@@ -1,6 +1,7 @@
 // Host-side launchers of the gfx950 kernels (one definition per .hip file).
 #pragma once
 #include "common.hpp"
+#include "trace.hpp"
 
 namespace lb {
 
