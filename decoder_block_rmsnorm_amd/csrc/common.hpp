@@ -126,6 +126,26 @@ struct KVView {
   }
 };
 
+// s_waitcnt with only the vector-memory counter constrained (vmcnt <= n)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at LDS byte address lds_addr + 16 l (lds_addr wave-uniform, passed in M0).
+// Written as inline asm so that the compiler, which cannot tell the stages of
+// the ring apart, does not make every LDS read wait for every load in flight;
+// the kernel waits on the vector-memory counter itself (wait_vmcnt) before the
+// barrier that publishes a stage.  The instruction has no register result: its
+// address registers are read at issue.  M0 is set in the same statement.
+// Address = sbase (wave-uniform, scalar registers) + voff (per lane, 32-bit).
+__device__ __forceinline__ void lds_dma16(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // Workgroup barrier for LDS communication: waits for this wave's LDS accesses,
 // not for its global loads in flight.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }

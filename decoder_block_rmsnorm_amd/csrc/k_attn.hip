@@ -17,6 +17,8 @@
 //                          of the group with 16x16x32 MFMA (more query heads: one
 //                          wavefront per 16 of them); k_attn_merge combines
 //                          the chunks with a log-sum-exp merge in a fixed order.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace lb {
@@ -75,14 +77,21 @@ template void launch_attn_simt<bf16_t>(const bf16_t*, KVView, int, int, int, int
 // ===========================================================================
 // bf16 flash prefill, head_dim 128
 // ===========================================================================
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E), so that
+// register arrays are indexed by constants.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for_fa(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for_fa<B + 1, E>(f);
+  }
+}
+
 namespace fa {
 constexpr int D = 128;
 constexpr int BQ = 128;        // queries per block (4 waves x 32)
 constexpr int BK = 64;         // keys per tile
-constexpr int KST = D + 8;     // LDS row stride (bf16) of the K tile  [key][d]
-constexpr int VST = BK + 8;    // LDS row stride (bf16) of the V^T tile [d][key]
-constexpr int K_ELEMS = BK * KST;
-constexpr int V_ELEMS = D * VST;
+constexpr int TB = BK * D * 2; // bytes of one K (or V) tile: one 64-slot block of a page
 }  // namespace fa
 
 __device__ inline bf16x8 as_bf16x8(uint4 v) {
@@ -91,15 +100,30 @@ __device__ inline bf16x8 as_bf16x8(uint4 v) {
   return r;
 }
 
-
 // One block per (head, sequence, query tile of 128), heavy (late) query tiles
 // first; with `flip`, the second half of the grid's tiles light first, so that
 // blocks z and z + n_qt / 2 of a head together take n_qt + 1 key tiles.
+//
+// A key tile is one 64-slot block of a page, 16 KB of K and 16 KB of V in the
+// cache's tiled layout, copied into LDS as it is by direct loads (each
+// wavefront instruction moves one contiguous kilobyte; no register staging).
+// Two K and two V tiles are resident: during step t the block holds K(t+1)
+// and V(t) while the loads of K(t+2) and V(t+1) land in the other halves.
+// The operands are read from those images directly.  S^T = K Q^T uses A-row r
+// of a 32-key half for key (r & 3) + 8 ((r >> 2) & 3) + 4 (r >> 4), so that the
+// 16 lanes of each read phase take 16 consecutive 16-byte pieces of one
+// kilobyte (no bank conflicts), and lane group hg of a query column then holds
+// the aligned key octets 8 hg + 0..7 and 16 + 8 hg + 0..7 of the half: one
+// 16-byte V^T operand each, also conflict-free.
+// Each wavefront runs its steps software-pipelined: the S MFMAs of tile t+1 are
+// issued one at a time between the softmax instructions of tile t (the matrix
+// core works while the vector ALU exponentiates), then O^T += V^T P^T for t.
 __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __restrict__ q, KVView kv, int B,
                                                              int L, int H, int G, int n_qt, int flip,
                                                              bf16_t* __restrict__ out) {
   using namespace fa;
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (K_ELEMS + V_ELEMS)];
+  // K tiles at bytes 0 and TB, V tiles at 2 TB and 3 TB
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[4 * BK * D];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int g = h / (H / G);
@@ -108,12 +132,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
   L = kv.rows_of(b, L);
   const int zh = n_qt >> 1, z = blockIdx.z;
   const int qt = flip && z >= zh ? z - zh : n_qt - 1 - z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hg = lane >> 5;
   const int S = kv.lens[b];               // tokens cached before this call
   const int q_first = qt * BQ;            // first query index (within the new tokens)
   if (q_first >= L) return;               // (a shorter sequence of a ragged call: no queries here)
-  const int wq0 = q_first + wave * 32;    // this wave's first query
+  const int wq0 = q_first + wv * 32;      // this wave's first query
   const int nq_valid = L - q_first;       // queries of this block that exist
   const int kmax_block = S + min(q_first + BQ, L);   // keys [0, kmax_block)
   const int n_tiles = (kmax_block + BK - 1) / BK;
@@ -136,69 +161,34 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
     }
   }
 
-  const bf16_t* Kp = (const bf16_t*)kv.k;
-  const bf16_t* Vp = (const bf16_t*)kv.v;
-  // tile loader: K tile 64 keys x 128 d (16 chunks of 16 B per key row); V^T tile
-  // 128 d rows x 64 keys (8 chunks per row).  1024 chunks each, 4 per thread.
-  // Slots at or past kmax_block hold no key of this call (stale or never
-  // written); they are zeroed so that a 0 softmax weight never meets a NaN.
-  uint4 kreg[4], vreg[4];
   // page-table entry of key tile t (clamped to the table row: entries past the
   // block's last tile are read and not used)
   const int32_t* trow = kv.table + (size_t)b * kv.pps;
-  auto page_of = [&](int t) { return trow[min(t * BK / kv.ps, kv.pps - 1)]; };
-  // A tile is the 64-slot block (slot0 / 64) of one page: contiguous in the
-  // tiled layout, where a thread's elements sit at offsets fixed for every
-  // tile (slot0 is a multiple of 64), computed once here.
-  int offk[4], offv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    offk[i] = kv_tiled_k(c >> 4, (c & 15) * 8);
-    offv[i] = kv_tiled_v((c & 7) * 8, c >> 3);
-  }
-  auto load_tile = [&](int t, int page) {
-    const int key0 = t * BK;
-    // this head's K (and V) block of the page, its 64-slot block of key0
-    const size_t blk = ((size_t)page * kv.G + g) * kv.ps * D + (size_t)((key0 % kv.ps) >> 6) * (BK * D);
-    const bf16_t* kb = Kp + blk;
-    const bf16_t* vb = Vp + blk;
-    const int nvalid = kmax_block - key0;
-    if (nvalid >= BK) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kreg[i] = ld16(kb + offk[i]);
-        vreg[i] = ld16(vb + offv[i]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i;
-        kreg[i] = (c >> 4) < nvalid ? ld16(kb + offk[i]) : make_uint4(0, 0, 0, 0);
-        uint4 v = ld16(vb + offv[i]);
-        const int nok = nvalid - (c & 7) * 8;
-        if (nok < 8) {
-          uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e >= nok) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          v = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-        vreg[i] = v;
-      }
-    }
+  auto page_of = [&](int t) __attribute__((always_inline)) { return trow[min(t * BK / kv.ps, kv.pps - 1)]; };
+  // byte offset of this head's 64-slot block of tile t in the K (or V) pool
+  auto tile_off = [&](int t, int page) __attribute__((always_inline)) {
+    return ((size_t)page * kv.G + g) * kv.ps * (D * 2) + (size_t)(((t * BK) % kv.ps) >> 6) * TB;
   };
-  auto store_tile = [&](int buf) {
-    bf16_t* ks = smem + buf * (K_ELEMS + V_ELEMS);
-    bf16_t* vs = ks + K_ELEMS;
+  const char* Kg = (const char*)kv.k;
+  const char* Vg = (const char*)kv.v;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)(char*)smem);
+  const uint32_t vlane = (uint32_t)lane * 16;
+  // wavefront wv copies kilobytes 4 wv .. 4 wv + 3 of a tile
+  auto copy_tile = [&](const char* pool, size_t off, uint32_t lds_byte) __attribute__((always_inline)) {
+    const char* src = pool + off + wv * 4096;
+    const uint32_t dst = lds0 + lds_byte + wv * 4096;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int c = tid + 256 * i;
-      int kr = c >> 4, kc = c & 15;
-      st16(ks + kr * KST + kc * 8, kreg[i]);
-      int vr = c >> 3, vc = c & 7;
-      st16(vs + vr * VST + vc * 8, vreg[i]);
-    }
+    for (int i = 0; i < 4; ++i) lds_dma16(vlane, src + i * 1024, dst + i * 1024);
+  };
+  const char* sm = (const char*)smem;
+  // fragment byte offsets inside a tile image (see the layout note above)
+  const uint32_t klane = (l32 >> 4) * 4096 + hg * 256 + (l32 & 15) * 16;
+  const uint32_t vl = (l32 >> 4) * 2048 + hg * 256 + (l32 & 15) * 16;
+  auto kfrag = [&](int t, int st2, int kc) __attribute__((always_inline)) {
+    return as_bf16x8(ld16(sm + (t & 1) * TB + klane + st2 * 8192 + (kc >> 1) * 1024 + (kc & 1) * 512));
+  };
+  auto vfrag = [&](int t, int ds, int c) __attribute__((always_inline)) {
+    return ld16(sm + 2 * TB + (t & 1) * TB + vl + ds * 4096 + (c >> 1) * 1024 + (c & 1) * 512);
   };
 
   f32x16 o_acc[4];
@@ -207,113 +197,210 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
 
-  // a tile's page entry is requested with the loads of the tile before it, so
-  // the wait for those loads covers it and no wait stands between the barrier
-  // and the next tile's loads
-  int pg_next = page_of(t_first + 1);
-  if (t_first < n_tiles) load_tile(t_first, page_of(t_first));
-  for (int t = t_first; t < n_tiles; ++t) {
-    const int buf = (t - t_first) & 1;
-    store_tile(buf);
-    __syncthreads();
-    if (t + 1 < n_tiles) {
-      const int pg = pg_next;
-      pg_next = page_of(t + 2);
-      load_tile(t + 1, pg);
-    }
+  // does this wavefront take key tile t (causal end, its queries, the window)
+  auto need = [&](int t) __attribute__((always_inline)) {
     const int key0 = t * BK;
-    // (W > 0: tiles wholly before the window of this wave's first query skip)
-    if (key0 < wave_kmax && nq_valid > wave * 32 && (W == 0 || key0 + BK > S + wq0 - W + 1)) {
-      const bf16_t* ks = smem + buf * (K_ELEMS + V_ELEMS);
-      const bf16_t* vs = ks + K_ELEMS;
-      // S^T = K Q^T : 2 key subtiles of 32.  A-row r = 8a + 4h + m of subtile st
-      // holds key 32 st + 16 (a / 2) + 8 h + 4 (a % 2) + m, so that afterwards
-      // lane group hg holds keys 16 c + 8 hg + 0..7 of each 16-key chunk c: the
-      // P.V operands are then 8 consecutive keys (one 16-byte V^T read).
-      const int krow = 16 * (l32 >> 4) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
-      f32x16 s_acc[2];
+    return key0 < wave_kmax && nq_valid > wv * 32 && (W == 0 || key0 + BK > S + wq0 - W + 1);
+  };
+  // some key of tile t may exceed some query position, or (window) lie
+  // before one query's window
+  auto need_mask = [&](int t) __attribute__((always_inline)) {
+    const int key0 = t * BK;
+    return key0 + BK - 1 > S + wq0 || (W > 0 && key0 < S + wq0 + 32 - W);
+  };
+  // key offset (minus 8 hg) of score i of half st2 in the tile
+  auto kofs = [](int st2, int i) { return 32 * st2 + (i & 3) + 16 * ((i >> 2) & 1) + 4 * (i >> 3); };
+
+  auto qk = [&](int t, f32x16(&s)[2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        s_acc[st] = (f32x16){};
+    for (int st2 = 0; st2 < 2; ++st2) {
+      s[st2] = (f32x16){};
 #pragma unroll
-        for (int kc = 0; kc < 8; ++kc) {
-          bf16x8 a = as_bf16x8(ld16(ks + (st * 32 + krow) * KST + kc * 16 + hg * 8));
-          s_acc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s_acc[st], 0, 0, 0);
-        }
-      }
-      // scale, causal mask, online softmax (query = column l32; rows = keys)
-      // (scores stay unscaled; the running max m is kept in log2 units, so
-      // p = 2^(s * log2(e)/sqrt(d) - m) is one fma and one v_exp_f32)
-      // some key may exceed some query position, or (window) lie before one
-      // query's window
-      // (a wave-uniform branch around per-lane selects: no divergent branch
-      // per score on the tiles that need no mask)
-      const bool need_mask = key0 + BK - 1 > S + wq0 || (W > 0 && key0 < S + wq0 + 32 - W);
-      if (need_mask) {
-        // key offsets ko = st * 32 + 16 (i / 8) + i % 8 kept: lo < ko <= rel,
-        // i.e. ko - lo - 1 in [0, n_keep) (one unsigned compare per score)
-        const int rel = my_pos - key0 - 8 * hg;
-        const int lo = W > 0 ? rel - W : -1;
-        const unsigned n_keep = rel > lo ? (unsigned)(rel - lo) : 0u;
+      for (int kc = 0; kc < 8; ++kc) s[st2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(t, st2, kc), qf[kc], s[st2], 0, 0, 0);
+    }
+  };
+  // scores -> row max; raise the exponent base (and rescale o, l) only when a
+  // query's tile maximum exceeds it by more than 2^8, decided per wavefront:
+  // p <= 256 stays exact in fp32 and safe in bf16, and o / l does not depend
+  // on the base.  Returns the base to use (0 while a row is fully masked).
+  auto rebase = [&](f32x16(&s)[2]) __attribute__((always_inline)) {
+    float tmax = -INFINITY;
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+    for (int st2 = 0; st2 < 2; ++st2)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int ko = st * 32 + 16 * (i >> 3) + (i & 7);
-            s_acc[st][i] = (unsigned)(ko - lo - 1) < n_keep ? s_acc[st][i] : -INFINITY;
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[st2][i]);
+    tmax = fmaxf(tmax, xor_lane<32>(tmax, lane));
+    const bool raise = tmax * sl2 > m_run + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float m_new = raise ? tmax * sl2 : m_run;
+      // (a fully masked row so far keeps m = -inf, so alpha = 0 scales nothing)
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) o_acc[ds] *= alpha;
+      m_run = m_new;
+    }
+    return m_run == -INFINITY ? 0.f : m_run;
+  };
+  // O^T += V^T P^T for tile t; chunk c of 16 keys takes the lane's octet of
+  // half c / 2: scores 0-3, 8-11 (c even) or 4-7, 12-15 (c odd).  On the last
+  // tile, V of slots at or past kmax_block (stale or never written) is zeroed
+  // in the operand, so that a 0 weight never meets a NaN.
+  auto pv = [&](int t, const f32x16(&s)[2]) __attribute__((always_inline)) {
+    const int nvalid = kmax_block - t * BK;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int st2 = c >> 1, r0 = 4 * (c & 1);
+      uint4 pw;
+      pw.x = pack_bf16x2(s[st2][r0 + 0], s[st2][r0 + 1]);
+      pw.y = pack_bf16x2(s[st2][r0 + 2], s[st2][r0 + 3]);
+      pw.z = pack_bf16x2(s[st2][r0 + 8], s[st2][r0 + 9]);
+      pw.w = pack_bf16x2(s[st2][r0 + 10], s[st2][r0 + 11]);
+      const bf16x8 pb = as_bf16x8(pw);   // P^T: keys 16 c + 8 hg + 0..7 of query l32
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) {
+        uint4 v = vfrag(t, ds, c);
+        if (nvalid < BK) {
+          const int nok = nvalid - 16 * c - 8 * hg;
+          if (nok < 8) {
+            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (e >= nok) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            v = make_uint4(w[0], w[1], w[2], w[3]);
           }
-      }
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s_acc[st][i]);
-      tmax = fmaxf(tmax, xor_lane<32>(tmax, lane));
-      // The exponent base m only has to stay within 2^8 below the running max
-      // (then p <= 256, exact in fp32 and safe in bf16, and o / l does not
-      // depend on m): it is raised, and o and l rescaled, only when some query
-      // of the wavefront needs it, so most tiles skip the 64 multiplies.
-      const bool raise = tmax * sl2 > m_run + 8.0f;
-      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-        const float m_new = raise ? tmax * sl2 : m_run;
-        // (a fully masked row so far keeps m = -inf, so alpha = 0 scales nothing)
-        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int ds = 0; ds < 4; ++ds) o_acc[ds] *= alpha;
-        m_run = m_new;
-      }
-      // a fully masked row so far keeps m = -inf; use 0 as the exponent base then
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float psum = 0.f;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[st][i], sl2, -m_use));
-          s_acc[st][i] = p;
-          psum += p;
         }
-      psum += xor_lane<32>(psum, lane);
-      l_run += psum;
-      // O^T += V^T P^T : 4 key chunks of 16 (B operand straight from S^T registers)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int st = c >> 1, r0 = 8 * (c & 1);
-        uint4 pw;
-        pw.x = pack_bf16x2(s_acc[st][r0 + 0], s_acc[st][r0 + 1]);
-        pw.y = pack_bf16x2(s_acc[st][r0 + 2], s_acc[st][r0 + 3]);
-        pw.z = pack_bf16x2(s_acc[st][r0 + 4], s_acc[st][r0 + 5]);
-        pw.w = pack_bf16x2(s_acc[st][r0 + 6], s_acc[st][r0 + 7]);
-        bf16x8 pb = as_bf16x8(pw);   // P^T: keys 16 c + 8 hg + 0..7 of query l32
-#pragma unroll
-        for (int ds = 0; ds < 4; ++ds) {
-          bf16x8 a = as_bf16x8(ld16(vs + (ds * 32 + l32) * VST + 16 * c + 8 * hg));
-          o_acc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o_acc[ds], 0, 0, 0);
-        }
+        o_acc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(v), pb, o_acc[ds], 0, 0, 0);
       }
     }
+  };
+  // softmax and P.V of tile t (any tile: causal / window mask as needed)
+  auto softmax_pv = [&](int t, f32x16(&s)[2]) __attribute__((always_inline)) {
+    if (need_mask(t)) {
+      // keep key offsets ko (minus 8 hg) with lo < ko <= rel: one unsigned
+      // compare per score
+      const int rel = my_pos - t * BK - 8 * hg;
+      const int lo = W > 0 ? rel - W : -1;
+      const unsigned n_keep = rel > lo ? (unsigned)(rel - lo) : 0u;
+#pragma unroll
+      for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          s[st2][i] = (unsigned)(kofs(st2, i) - lo - 1) < n_keep ? s[st2][i] : -INFINITY;
+    }
+    const float m_use = rebase(s);
+    float psum = 0.f;
+#pragma unroll
+    for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st2][i], sl2, -m_use));
+        s[st2][i] = p;
+        psum += p;
+      }
+    psum += xor_lane<32>(psum, lane);
+    l_run += psum;
+    pv(t, s);
+  };
+  // an unmasked tile t whose successor this wavefront also takes: the 16 S
+  // MFMAs of tile t + 1 go out one per group of two exponentials of tile t
+  // (the fences keep that order), each fragment read four MFMAs ahead
+  auto fused = [&](int t, f32x16(&sc)[2], f32x16(&sn)[2]) __attribute__((always_inline)) {
+    constexpr int AHEAD = 4;
+    bf16x8 kf[AHEAD];
+    // MFMA j: half j & 1, d chunk j >> 1 (the two halves' chains alternate)
+#pragma unroll
+    for (int j = 0; j < AHEAD; ++j) kf[j] = kfrag(t + 1, j & 1, j >> 1);
+    const float m_use = rebase(sc);
+    sn[0] = (f32x16){};
+    sn[1] = (f32x16){};
+    float psum = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for_fa<0, 16>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      sn[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % AHEAD], qf[j >> 1], sn[j & 1], 0, 0, 0);
+      if constexpr (j + AHEAD < 16) kf[j % AHEAD] = kfrag(t + 1, (j + AHEAD) & 1, (j + AHEAD) >> 1);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        constexpr int dummy = 0;
+        (void)dummy;
+        const int i = 2 * j + u;            // score i % 16 of half i / 16
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i >> 4][i & 15], sl2, -m_use));
+        sc[i >> 4][i & 15] = p;
+        psum += p;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    psum += xor_lane<32>(psum, lane);
+    l_run += psum;
+    pv(t, sc);
+  };
+
+  // prologue: K(t0), V(t0), K(t0+1) resident, S(t0) computed
+  const int t0 = t_first;
+  if (t0 >= n_tiles) return;
+  int pg1 = page_of(t0 + 1), pg2 = page_of(t0 + 2);
+  {
+    const int p0 = page_of(t0);
+    copy_tile(Kg, tile_off(t0, p0), (t0 & 1) * TB);
+    copy_tile(Vg, tile_off(t0, p0), 2 * TB + (t0 & 1) * TB);
+    if (t0 + 1 < n_tiles) copy_tile(Kg, tile_off(t0 + 1, pg1), ((t0 + 1) & 1) * TB);
+    wait_vmcnt<0>();
+    lds_barrier();
   }
+  f32x16 sA[2], sB[2];
+  if (need(t0)) qk(t0, sA);
+  // step t: S(t) in sc; K(t+1) and V(t) resident after the barrier.  FUSED:
+  // a tile in the wavefront's unmasked interior (it also takes tile t+1)
+  auto step = [&](int t, f32x16(&sc)[2], f32x16(&sn)[2], auto fused_c) __attribute__((always_inline)) {
+    // this wavefront's loads of the previous step have landed; after the
+    // barrier every wavefront's have, and every wavefront is done with step
+    // t - 1 (its reads of K(t) and V(t-1), whose buffers are refilled now)
+    wait_vmcnt<0>();
+    lds_barrier();
+    const int pg3 = page_of(t + 3);   // requested a step before its use
+    if (t + 2 < n_tiles) copy_tile(Kg, tile_off(t + 2, pg2), (t & 1) * TB);
+    if (t + 1 < n_tiles) copy_tile(Vg, tile_off(t + 1, pg1), 2 * TB + ((t + 1) & 1) * TB);
+    pg1 = pg2;
+    pg2 = pg3;
+    if constexpr (decltype(fused_c)::value) {
+      fused(t, sc, sn);
+    } else {
+      if (t + 1 < n_tiles && need(t + 1)) qk(t + 1, sn);
+      if (need(t)) softmax_pv(t, sc);
+    }
+  };
+  // The steps up to n_tiles in three runs (bounds wave-uniform): tiles before
+  // the unmasked interior, the interior [lo, hi), the rest.  Every wavefront
+  // takes every step (one barrier each); each run alternates the two score
+  // sets, and a run of odd length hands S over with one copy.
+  int lo = t0, hi = t0;
+  if (nq_valid > wv * 32) {
+    const int te = (wave_kmax + BK - 1) / BK;                 // tiles [.., te) needed
+    // window: tiles whose keys all lie inside every query's window
+    if (W > 0) lo = max(lo, (S + wq0 + 32 - W + BK - 1) / BK);
+    // causal: tiles wholly below the wave's first query, and a successor taken
+    const int diag = S + wq0 - (BK - 1) >= 0 ? (S + wq0 - (BK - 1)) / BK + 1 : 0;
+    hi = min(te - 1, diag);
+    if (hi < lo) hi = lo;
+  }
+  int t = t0;
+  auto run = [&](int t_end, auto fused_c) __attribute__((always_inline)) {
+    for (; t + 1 < t_end; t += 2) {
+      step(t, sA, sB, fused_c);
+      step(t + 1, sB, sA, fused_c);
+    }
+    if (t < t_end) {
+      step(t, sA, sB, fused_c);
+      sA[0] = sB[0];
+      sA[1] = sB[1];
+      ++t;
+    }
+  };
+  run(lo, std::false_type{});
+  run(hi, std::true_type{});
+  run(n_tiles, std::false_type{});
+
   // write O[q][d] = O^T / l : lane holds q = l32, d = 32*ds + 8*(i/4) + 4*hg + i%4
   if (my_q < L) {
     const float inv = 1.0f / l_run;
