@@ -89,7 +89,6 @@ __device__ __forceinline__ void static_for_fa(F&& f) {
 
 namespace fa {
 constexpr int D = 128;
-constexpr int BQ = 128;        // queries per block (4 waves x 32)
 constexpr int BK = 64;         // keys per tile
 constexpr int TB = BK * D * 2; // bytes of one K (or V) tile: one 64-slot block of a page
 }  // namespace fa
@@ -118,7 +117,8 @@ __device__ inline bf16x8 as_bf16x8(uint4 v) {
 // Each wavefront runs its steps software-pipelined: the S MFMAs of tile t+1 are
 // issued one at a time between the softmax instructions of tile t (the matrix
 // core works while the vector ALU exponentiates), then O^T += V^T P^T for t.
-__global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __restrict__ q, KVView kv, int B,
+template <int NWV>
+__global__ __launch_bounds__(NWV * 64, 2) void k_attn_prefill_bf16(const bf16_t* __restrict__ q, KVView kv, int B,
                                                              int L, int H, int G, int n_qt, int flip,
                                                              bf16_t* __restrict__ out) {
   using namespace fa;
@@ -136,6 +136,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hg = lane >> 5;
   const int S = kv.lens[b];               // tokens cached before this call
+  constexpr int BQ = 32 * NWV;            // queries per block (32 per wavefront)
   const int q_first = qt * BQ;            // first query index (within the new tokens)
   if (q_first >= L) return;               // (a shorter sequence of a ragged call: no queries here)
   const int wq0 = q_first + wv * 32;      // this wave's first query
@@ -175,10 +176,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
   const uint32_t vlane = (uint32_t)lane * 16;
   // wavefront wv copies kilobytes 4 wv .. 4 wv + 3 of a tile
   auto copy_tile = [&](const char* pool, size_t off, uint32_t lds_byte) __attribute__((always_inline)) {
-    const char* src = pool + off + wv * 4096;
-    const uint32_t dst = lds0 + lds_byte + wv * 4096;
+    constexpr int PER = TB / NWV;         // bytes of a tile each wavefront copies
+    const char* src = pool + off + wv * PER;
+    const uint32_t dst = lds0 + lds_byte + wv * PER;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(vlane, src + i * 1024, dst + i * 1024);
+    for (int i = 0; i < PER / 1024; ++i) lds_dma16(vlane, src + i * 1024, dst + i * 1024);
   };
   const char* sm = (const char*)smem;
   // fragment byte offsets inside a tile image (see the layout note above)
@@ -420,18 +422,20 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_bf16(const bf16_t* __re
 
 void launch_attn_prefill_bf16(const bf16_t* q, KVView kv, int B, int L, int H, int G, bf16_t* out, hipStream_t s) {
   if (B <= 0 || L <= 0) return;
-  const int n_qt = (L + fa::BQ - 1) / fa::BQ;
+  constexpr int NWV = 4;                    // wavefronts (32 queries each) per block
+  constexpr int BQ = 32 * NWV;
+  const int n_qt = (L + BQ - 1) / BQ;
   // A grid of one round of blocks (two per compute unit) puts its second half
   // light first: block i and block i + half then take complementary query
   // tiles (measured: 3-4% faster at 32 heads x 16 tiles); heavy-first order
   // otherwise, which dynamic dispatch balances over several rounds.  (Two
   // tiles per block, complementary ones, measured no faster.)
   const long blocks = (long)H * B * n_qt;
-  const int flip = blocks <= 512 ? 1 : 0;
+  const int flip = blocks <= 256 * (8 / NWV) ? 1 : 0;
   plan_log("attention prefill: %d heads (%d kv) x %d sequences x %d query tiles of %d, %s order", H, G, B, n_qt,
-           fa::BQ, flip ? "half-flipped" : "heavy-first");
+           BQ, flip ? "half-flipped" : "heavy-first");
   dim3 grid(H, B, n_qt);
-  hipLaunchKernelGGL(k_attn_prefill_bf16, grid, dim3(256), 0, s, q, kv, B, L, H, G, n_qt, flip, out);
+  hipLaunchKernelGGL(k_attn_prefill_bf16<NWV>, grid, dim3(NWV * 64), 0, s, q, kv, B, L, H, G, n_qt, flip, out);
 }
 
 // ===========================================================================
