@@ -399,20 +399,29 @@ __global__ __launch_bounds__(NW * 64, 1) void k_gemm_mfma(GemmArgs a) {
         const bf16_t* sb0 = lds + sti * STS + SA + SB;
         const uint4 cw = ld16(sb0 + tid * 8);
         const uint32_t pr = *reinterpret_cast<const uint32_t*>(sb0 + SC + wv * 512 + tid * 2);
-        const float sc = bf16_to_f32((bf16_t)(pr & 0xffffu)), bi = bf16_to_f32((bf16_t)(pr >> 16));
+        // Packed fp16: the codes of columns 2e and 2e + 1 become the fp16
+        // pair (1024 + q0, 1024 + q1) by placing each code in the low
+        // mantissa bits of 1024.0 (bit pattern 0x6400); subtracting 1024 is
+        // exact, and one fused multiply-add per pair gives s q + b rounded
+        // once to fp16 (s and b, bf16 values, are exact in fp16 inside its
+        // normal range).  About 2.4 instructions per code.
+        const _Float16 s16 = (_Float16)bf16_to_f32((bf16_t)(pr & 0xffffu));
+        const _Float16 b16 = (_Float16)bf16_to_f32((bf16_t)(pr >> 16));
+        const f16x2 sv = {s16, s16}, bv = {b16, b16}, k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
         bf16_t* dst = lds + sti * STS + SA + (tid >> 4) * 512 + (tid & 15) * 8;
         const uint32_t w4[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+          // even-column codes in the bytes of lo, odd-column codes in those of hi
+          const uint32_t lo = w4[j] & 0x0f0f0f0fu, hi = (w4[j] >> 4) & 0x0f0f0f0fu;
           uint32_t o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const _Float16 h0 = (_Float16)__builtin_fmaf(sc, (float)((w4[j] >> (8 * e)) & 15u), bi);
-            const _Float16 h1 = (_Float16)__builtin_fmaf(sc, (float)((w4[j] >> (8 * e + 4)) & 15u), bi);
-            uint16_t u0, u1;
-            __builtin_memcpy(&u0, &h0, 2);
-            __builtin_memcpy(&u1, &h1, 2);
-            o[e] = (uint32_t)u0 | ((uint32_t)u1 << 16);
+            // byte e of lo -> byte 0, byte e of hi -> byte 2, zero bytes 1 and 3
+            const uint32_t sel = (uint32_t)e | (0x0cu << 8) | ((uint32_t)(4 + e) << 16) | (0x0cu << 24);
+            const uint32_t x = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+            const f16x2 q = __builtin_bit_cast(f16x2, x) - k1024;
+            o[e] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, sv, bv));
           }
           st16(dst + j * 128, make_uint4(o[0], o[1], o[2], o[3]));
         }
