@@ -564,6 +564,9 @@ static SLayout scratch_layout(const llama_block_config& c, const Dims& d, int T,
     // needs fewer than 200 tiles of 256 x 256, which bounds the rows it covers
     const long rows_split = 256L * std::max(0L, (199L * 256 / d.D));
     part = (size_t)kMaxSplitK * std::min<long>(T, rows_split) * d.D * 4;
+    // 4-bit weights: up to kMaxSplitKQ4 slices while slices x tiles stay
+    // within one round of 256 blocks, so at most 256 tiles of 256 x 256 fp32
+    if (d.q4) part = std::max(part, std::min((size_t)kMaxSplitKQ4 * T * d.D * 4, (size_t)256 * 256 * 256 * 4));
   }
   L.part = off; off = align256(off + part);
   L.n_splits = (max_seq + split_min - 1) / split_min;
@@ -823,7 +826,7 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
     GemmArgs g{};
     operands(g, A, lin, nullptr);
     g.M = M; g.N = d.D; g.K = K;
-    const int ks = gemm_split_k(M, d.D, K, g.b_f16 && !g.a_f16);
+    const int ks = g.q4w ? gemm_split_k_q4(M, d.D, K) : gemm_split_k(M, d.D, K, g.b_f16 && !g.a_f16);
     if (ks > 1) {
       g.C = part; g.ksplit = ks;
       launch_gemm_mfma(EPI_F32, g, s);

@@ -886,11 +886,13 @@ static void launch_epi(const GemmArgs& a, hipStream_t s) {
   const bool n256 = (a.N % 256) == 0;
   if constexpr (F16) {
     if (a.q4w) {
-      // 4-bit B dequantized in the kernel (gemm_q4_direct_ok shapes), fp16 A
+      // 4-bit B dequantized in the kernel (gemm_q4_direct_ok shapes), fp16 A.
+      // 256-row tiles unless the rounds of 256 blocks of 128-row tiles end
+      // sooner (a 128-row round counted at 0.6 of a 256-row one, as measured
+      // for bf16; the B tile's dequantization favours the taller tile further)
       const long t256 = (long)((a.M + 255) / 256) * (a.N / 256), t128 = (long)((a.M + 127) / 128) * (a.N / 256);
       const bool use128 = ((t128 + 255) / 256) * 0.6 < (double)((t256 + 255) / 256);
-      if ((EPI == EPI_F32 && a.ksplit > 1) || (t256 >= 240 && !use128))
-        return launch_cfg<256, 256, 4, 0, EPI, true, true>(a, s);
+      if ((EPI == EPI_F32 && a.ksplit > 1) || !use128) return launch_cfg<256, 256, 4, 0, EPI, true, true>(a, s);
       return launch_cfg<128, 256, 4, 0, EPI, true, true>(a, s);
     }
     if (a.a_f16) {
@@ -971,6 +973,20 @@ int gemm_split_k(int M, int N, int K, bool b_f16) {
   // at least 512 of K in whole 64-wide steps
   while (ks < kMaxSplitK && ks * t256 < 200 && K % (128 * ks) == 0 && K / (2 * ks) >= 512) ks *= 2;
   return ks;
+}
+
+int gemm_split_k_q4(int M, int N, int K) {
+  if (N % 256) return 1;
+  const long t256 = (long)((M + 255) / 256) * (N / 256);
+  if (t256 >= 200) return 1;
+  // The most slices that keep the grid within one round of 256 blocks, each
+  // slice whole 64-column groups and at least 512 columns: the per-step
+  // dequantization is paid once per block whatever its row count, so filling
+  // the chip with slices of 256-row tiles beats fewer, longer blocks.
+  int best = 1;
+  for (int ks = 2; ks <= kMaxSplitKQ4; ++ks)
+    if (ks * t256 <= 256 && K % (64 * ks) == 0 && K / ks >= 512) best = ks;
+  return best;
 }
 
 void launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t s) {

@@ -165,6 +165,10 @@ void launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t s);
 // at C + s*M*N
 constexpr int kMaxSplitK = 4;
 int gemm_split_k(int M, int N, int K, bool b_f16);
+// 4-bit weights dequantized inside the GEMM: any slice count up to
+// kMaxSplitKQ4 (slices x 256 x 256 tiles within one round of 256 blocks)
+constexpr int kMaxSplitKQ4 = 8;
+int gemm_split_k_q4(int M, int N, int K);
 // shapes whose fp16 GEMM can take A fp16 and B tiled (direct-to-LDS tiles)
 bool gemm_f16_direct_ok(int M, int N, int K);
 // shapes whose fp16 GEMM can take 4-bit B dequantized in the kernel
