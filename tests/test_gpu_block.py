@@ -432,6 +432,23 @@ def test_q4_prefill():
     _check_branches(s, blk, sc, r, y, 1, 150)
 
 
+def test_q4_prefill_odd_k_slices():
+    """4-bit prompt pass whose Wo and W2 products split K into 3 and 7 slices
+    (dim 1536, ffn 3584: the most slices of whole 64-column groups, at least
+    512 columns each, that keep slices x 256 x 256 tiles within one round of
+    256 blocks), on 150 rows (a ragged tail off every tile); grouped heads."""
+    s = W.BlockShape(dim=1536, n_heads=12, n_kv_heads=4, ffn_dim=3584, dtype="bf16", weight_format="q4",
+                     traditional=False)
+    rng = W.Rng(61)
+    x = rng.normal((1, 150, s.dim), 1.0, "bf16")
+    w = W.draw_block_weights(s, rng)
+    _flush("case: 4-bit prefill L=150, dim 1536, K slices 3 (wo) and 7 (w2)")
+    blk, cache, sc, y = _run_prefill(s, w, x)
+    r = _oracle(s, w, x)
+    G.check("bf16", y, np.stack(r["y"]), "y")
+    _check_branches(s, blk, sc, r, y, 1, 150)
+
+
 # ------------------------------------------------ ragged prefill (chunked) --
 # Sequences of one call bring different numbers of new tokens: each continues
 # from its own cached length (RoPE offset = cache length, "2. 注意力机制" on the
