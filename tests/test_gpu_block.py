@@ -449,6 +449,53 @@ def test_q4_prefill_odd_k_slices():
     _check_branches(s, blk, sc, r, y, 1, 150)
 
 
+@pytest.mark.parametrize("page_size", [128, 256])
+def test_prefill_then_decode_pages_larger_than_a_tile(page_size):
+    """Pages of 128 and 256 slots (each holds two or four 64-slot blocks, the
+    unit the attention kernels copy): a permuted block table, every slot NaN
+    before the real rows are written, cached prefixes of 0, 150 and 301
+    positions, a 200-token chunked prefill (ragged tails off every tile) and
+    then one decode step, both against the oracle."""
+    s = SMALL_GQA
+    rng = W.Rng(71 + page_size)
+    w = W.draw_block_weights(s, rng)
+    lens = [0, 150, 301]
+    B, Lq = len(lens), 200
+    max_seq = 520
+    kv = (rng.normal((B, max(lens), s.n_kv_heads, s.head_dim), 1.0, "bf16"),
+          rng.normal((B, max(lens), s.n_kv_heads, s.head_dim), 1.0, "bf16"))
+    x = rng.normal((B, Lq + 1, s.dim), 1.0, "bf16")
+    _flush(f"case: prefill 200 over cached 0/150/301, then decode, page size {page_size}")
+    blk, wd = G.make_block(s, w, max_seq)
+    cache = G.make_cache(s, 1, B, max_seq, page_size)
+    perm = np.random.default_rng(page_size).permutation(B * cache.pages_per_seq).tolist()
+    cache.set_block_table(perm)
+    nan = torch.full((max_seq, s.n_kv_heads, s.head_dim), float("nan"), device="cuda", dtype=torch.bfloat16)
+    for b in range(B):
+        cache.write(0, b, 0, nan, nan)
+        if lens[b]:
+            cache.write(0, b, 0, G.tdev(kv[0][b, :lens[b]], "bf16"), G.tdev(kv[1][b, :lens[b]], "bf16"))
+    cache.set_lens(0, lens)
+    sc = G.scratch(blk, B * Lq, B, max_seq)
+    blk.set_diag(True)
+    xp = G.tdev(np.ascontiguousarray(x[:, :Lq]).reshape(B * Lq, s.dim), "bf16")
+    yp = torch.empty_like(xp)
+    blk.prefill(cache, 0, xp, yp, B, Lq, sc)
+    torch.cuda.synchronize()
+    r = _oracle(s, w, np.ascontiguousarray(x[:, :Lq]), lens, kv)
+    got = G.thost(yp).reshape(B, Lq, s.dim)
+    G.check("bf16", got, np.stack(r["y"]), "prefill y")
+    _check_branches(s, blk, sc, r, got, B, Lq)
+    # the decode step attends to the prefix, the prefill's rows and itself
+    xd = G.tdev(np.ascontiguousarray(x[:, Lq]), "bf16")
+    yd = torch.empty_like(xd)
+    blk.decode(cache, 0, xd, yd, B, sc)
+    torch.cuda.synchronize()
+    rd = ref.block_forward(x, w, s, [kv[0][b][:lens[b]] for b in range(B)], [kv[1][b][:lens[b]] for b in range(B)])
+    G.check("bf16", G.thost(yd).reshape(B, s.dim), np.stack([yb[Lq] for yb in rd["y"]]), "decode y")
+    assert list(cache.get_lens(0, B)) == [n + Lq + 1 for n in lens]
+
+
 # ------------------------------------------------ ragged prefill (chunked) --
 # Sequences of one call bring different numbers of new tokens: each continues
 # from its own cached length (RoPE offset = cache length, "2. 注意力机制" on the
