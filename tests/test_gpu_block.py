@@ -496,6 +496,45 @@ def test_prefill_then_decode_pages_larger_than_a_tile(page_size):
     assert list(cache.get_lens(0, B)) == [n + Lq + 1 for n in lens]
 
 
+def _random_attention_case(seed):
+    """A seeded random prefill configuration: heads and kv heads, window,
+    batch, cached prefix per sequence and new tokens (equal counts)."""
+    r = np.random.default_rng(1000 + seed)
+    nh, ng = [(8, 2), (4, 4), (8, 1), (16, 2), (4, 2), (8, 8)][seed % 6]
+    W_ = int(r.integers(1, 400)) if seed % 3 == 2 else 0
+    B = int(r.integers(1, 4))
+    L = int(r.choice([int(r.integers(1, 64)), int(r.integers(64, 330))]))
+    lens = [int(r.choice([0, int(r.integers(1, 420))])) for _ in range(B)]
+    return nh, ng, W_, B, L, lens
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_prefill_attention_random_configurations(seed):
+    """Seeded random configurations of the flash prefill path (grouped, MQA and
+    plain heads; windows; cached prefixes of any length; new-token counts below
+    and across the 128-query and 64-key tiles), each followed by a decode step;
+    y and the attention branch against the oracle."""
+    nh, ng, W_, B, L, lens = _random_attention_case(seed)
+    s = W.BlockShape(dim=nh * 128, n_heads=nh, n_kv_heads=ng, ffn_dim=768, dtype="bf16", traditional=bool(seed & 1),
+                     window=W_)
+    rng = W.Rng(2000 + seed)
+    w = W.draw_block_weights(s, rng)
+    kv = (rng.normal((B, max(max(lens), 1), ng, 128), 1.0, "bf16"),
+          rng.normal((B, max(max(lens), 1), ng, 128), 1.0, "bf16"))
+    x = rng.normal((B, L + 1, s.dim), 1.0, "bf16")
+    _flush(f"case: random seed {seed}: heads {nh} kv heads {ng} window {W_} B {B} L {L} cached {lens}")
+    blk, cache, sc, y = _run_prefill(s, w, np.ascontiguousarray(x[:, :L]), lens, kv, max_seq=max(lens) + L + 9)
+    r = _oracle(s, w, np.ascontiguousarray(x[:, :L]), lens, kv)
+    G.check("bf16", y, np.stack(r["y"]), "prefill y")
+    _check_branches(s, blk, sc, r, y, B, L)
+    xd = G.tdev(np.ascontiguousarray(x[:, L]), "bf16")
+    yd = torch.empty_like(xd)
+    blk.decode(cache, 0, xd, yd, B, sc)
+    torch.cuda.synchronize()
+    rd = ref.block_forward(x, w, s, [kv[0][b][:lens[b]] for b in range(B)], [kv[1][b][:lens[b]] for b in range(B)])
+    G.check("bf16", G.thost(yd).reshape(B, s.dim), np.stack([yb[L] for yb in rd["y"]]), "decode y")
+
+
 # ------------------------------------------------ ragged prefill (chunked) --
 # Sequences of one call bring different numbers of new tokens: each continues
 # from its own cached length (RoPE offset = cache length, "2. 注意力机制" on the
