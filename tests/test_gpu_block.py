@@ -535,6 +535,40 @@ def test_prefill_attention_random_configurations(seed):
     G.check("bf16", G.thost(yd).reshape(B, s.dim), np.stack([yb[L] for yb in rd["y"]]), "decode y")
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_q4_prefill_decode_random_configurations(seed):
+    """Seeded random 4-bit blocks: model widths that are and are not multiples
+    of 256 (the in-GEMM dequantization, or the dequantized-weight fallback),
+    grouped heads, windows, cached prefixes and a decode step after the
+    prefill; y and the branches against the oracle."""
+    r = np.random.default_rng(3000 + seed)
+    nh, ng = [(4, 2), (3, 3), (6, 2), (2, 1), (4, 4), (5, 1)][seed]
+    ffn = [1536, 1152, 2048, 640, 1024, 1408][seed]
+    W_ = int(r.integers(1, 300)) if seed % 2 else 0
+    B = int(r.integers(1, 4))
+    L = int(r.integers(1, 260))
+    lens = [int(r.choice([0, int(r.integers(1, 300))])) for _ in range(B)]
+    s = W.BlockShape(dim=nh * 128, n_heads=nh, n_kv_heads=ng, ffn_dim=ffn, dtype="bf16", weight_format="q4",
+                     traditional=bool(seed & 2), window=W_)
+    rng = W.Rng(4000 + seed)
+    w = W.draw_block_weights(s, rng)
+    kv = (rng.normal((B, max(max(lens), 1), ng, 128), 1.0, "bf16"),
+          rng.normal((B, max(max(lens), 1), ng, 128), 1.0, "bf16"))
+    x = rng.normal((B, L + 1, s.dim), 1.0, "bf16")
+    _flush(f"case: 4-bit random seed {seed}: dim {s.dim} ffn {ffn} heads {nh}/{ng} window {W_} B {B} L {L} "
+           f"cached {lens}")
+    blk, cache, sc, y = _run_prefill(s, w, np.ascontiguousarray(x[:, :L]), lens, kv, max_seq=max(lens) + L + 9)
+    rp = _oracle(s, w, np.ascontiguousarray(x[:, :L]), lens, kv)
+    G.check("bf16", y, np.stack(rp["y"]), "prefill y")
+    _check_branches(s, blk, sc, rp, y, B, L)
+    xd = G.tdev(np.ascontiguousarray(x[:, L]), "bf16")
+    yd = torch.empty_like(xd)
+    blk.decode(cache, 0, xd, yd, B, sc)
+    torch.cuda.synchronize()
+    rd = ref.block_forward(x, w, s, [kv[0][b][:lens[b]] for b in range(B)], [kv[1][b][:lens[b]] for b in range(B)])
+    G.check("bf16", G.thost(yd).reshape(B, s.dim), np.stack([yb[L] for yb in rd["y"]]), "decode y")
+
+
 # ------------------------------------------------ ragged prefill (chunked) --
 # Sequences of one call bring different numbers of new tokens: each continues
 # from its own cached length (RoPE offset = cache length, "2. 注意力机制" on the
