@@ -7,9 +7,11 @@
 //  * k_attn_simt         : one wavefront per (token, head), lanes over head_dim,
 //                          online softmax over keys (fp32 path).
 //  * k_attn_prefill_bf16 : flash-style prefill: 128 queries of one head per
-//                          block, 64-key K / V^T tiles staged in LDS, S^T = K Q^T
-//                          and O^T = V^T P^T on 32x32x16 bf16 MFMA, fp32 online
-//                          softmax (the tiling idea credited to FlashAttention in
+//                          block, 64-key K / V tiles copied from the tiled pages
+//                          into LDS by direct loads, S^T = K Q^T and O^T = V^T P^T
+//                          on 32x32x16 bf16 MFMA, fp32 online softmax, the next
+//                          tile's S interleaved with this tile's exponentials
+//                          (the tiling idea credited to FlashAttention in
 //                          "Transformer 块的内部结构" of the reading-notes page).
 //  * k_attn_decode_bf16  : split-K decode: each wavefront streams a 256-key
 //                          chunk of one (sequence, kv head) straight from the
@@ -324,8 +326,6 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_attn_prefill_bf16(const bf16_t*
       if constexpr (j + AHEAD < 16) kf[j % AHEAD] = kfrag(t + 1, (j + AHEAD) & 1, (j + AHEAD) >> 1);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        constexpr int dummy = 0;
-        (void)dummy;
         const int i = 2 * j + u;            // score i % 16 of half i / 16
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i >> 4][i & 15], sl2, -m_use));
         sc[i >> 4][i & 15] = p;
