@@ -769,7 +769,8 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
   // applied (x * gamma, one rounding); else the weights are dequantized (gamma
   // folded) to fp16 right before the GEMM, tiled for the direct-to-LDS tiles
   // when A can be copied to fp16 too.
-  auto operands = [&](GemmArgs& g, const bf16_t* A, const Lin& lin, const float* gamma) {
+  // a_ready: the fp16 copy of A (gamma applied) is already in a16
+  auto operands = [&](GemmArgs& g, const bf16_t* A, const Lin& lin, const float* gamma, bool a_ready = false) {
     g.A = A;
     if (!d.q4) {
       g.B = (const bf16_t*)lin.w;
@@ -781,7 +782,7 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
       g.q4w = (const uint32_t*)lin.w;
       g.q4sb = lin.pairs;
       g.B = nullptr;
-      launch_bf16_to_f16(A, a16, (size_t)M * lin.K, s, gamma, lin.K);
+      if (!a_ready) launch_bf16_to_f16(A, a16, (size_t)M * lin.K, s, gamma, lin.K);
       g.A = (const bf16_t*)a16;
       return;
     }
@@ -821,8 +822,11 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
   // adds them (in slice order) to the residual.
   float* part = (float*)(sc + S.part);
   // ss_out (optional): the stored rows' sums of squares per 128 columns
+  // out16 / gamma16 (optional): with a K split, the residual kernel also writes
+  // fp16(out * gamma16) there; returns whether it did
   auto resid_gemm = [&](const bf16_t* A, const Lin& lin, const bf16_t* resid, bf16_t* out, int K, int32_t* lens_add,
-                        int lens_inc, bf16_t* branch, float* ss_out) {
+                        int lens_inc, bf16_t* branch, float* ss_out, _Float16* out16 = nullptr,
+                        const float* gamma16 = nullptr) {
     GemmArgs g{};
     operands(g, A, lin, nullptr);
     g.M = M; g.N = d.D; g.K = K;
@@ -830,22 +834,28 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
     if (ks > 1) {
       g.C = part; g.ksplit = ks;
       launch_gemm_mfma(EPI_F32, g, s);
-      launch_epi_resid<bf16_t>(part, ks, M, d.D, resid, out, ss_out, lens_add, lens_inc, B, branch, s, kv.cu, 1);
-      return;
+      launch_epi_resid<bf16_t>(part, ks, M, d.D, resid, out, ss_out, lens_add, lens_inc, B, branch, s, kv.cu, 1,
+                               out16, gamma16);
+      return out16 != nullptr;
     }
     g.resid = resid; g.out = out; g.lens_add = lens_add; g.lens_inc = lens_inc; g.n_seq = B; g.branch = branch;
     g.lens_cu = kv.cu; g.ss_out = ss_out;
     launch_gemm_mfma(EPI_RESID, g, s);
+    return false;
   };
   // RMSNorm #2's statistic comes from the Wo epilogue (the rows' sums of
   // squares as stored), reduced by the W1/W3 GEMM into its row scales; a model
   // dim past 64 partials per row falls back to a statistic pass over h
   float* ssh = (float*)(sc + S.ssh);
-  resid_gemm(attn, blk->o, (const bf16_t*)x, h, d.Nq, nullptr, 0, nullptr, stat128 ? ssh : nullptr);
+  // (4-bit W1/W3 on the direct path: its fp16 A, h * gamma2, comes from the
+  // Wo residual kernel when Wo splits K)
+  const bool h16 = d.q4 && gemm_q4_direct_ok(M, 2 * d.F, d.D);
+  const bool h16_done = resid_gemm(attn, blk->o, (const bf16_t*)x, h, d.Nq, nullptr, 0, nullptr,
+                                   stat128 ? ssh : nullptr, h16 ? a16 : nullptr, blk->gamma2);
   if (!stat128) launch_rms_inv<bf16_t>(h, M, d.D, eps, inv2, s);
   mk(s);
   GemmArgs f{};
-  operands(f, h, blk->w13, blk->gamma2);
+  operands(f, h, blk->w13, blk->gamma2, h16_done);
   f.M = M; f.N = 2 * d.F; f.K = d.D;
   f.g_out = g;
   if (stat128) {

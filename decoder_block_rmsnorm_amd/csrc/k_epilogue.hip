@@ -104,7 +104,8 @@ void launch_epi_qkv(const float* part, int ks, int M, int Nq, int Nkv, RowStat s
 template <typename T>
 __global__ __launch_bounds__(256) void k_epi_resid(const float* part, int ks, int M, int N, const T* resid, T* out,
                                                    float* ss_out, int32_t* lens_add, int lens_inc, int n_seq,
-                                                   T* branch, const int32_t* lens_cu, int ss_128) {
+                                                   T* branch, const int32_t* lens_cu, int ss_128,
+                                                   _Float16* out16, const float* gamma16) {
   const int m = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
   const size_t stride = (size_t)M * N;
@@ -115,6 +116,9 @@ __global__ __launch_bounds__(256) void k_epi_resid(const float* part, int ks, in
     if (branch) Elt<T>::store(branch, idx, f);
     v = Elt<T>::round(Elt<T>::load(resid, idx) + f);
     Elt<T>::store(out, idx, v);
+    // (optional) the stored value times the next RMSNorm's weight, in fp16: the
+    // A operand of a 4-bit GEMM, rounded as its copy kernel would round it
+    if (out16) out16[idx] = (_Float16)(v * gamma16[c]);
   }
   if (ss_out) {
     __shared__ float red[4];
@@ -138,11 +142,11 @@ __global__ __launch_bounds__(256) void k_epi_resid(const float* part, int ks, in
 template <typename T>
 void launch_epi_resid(const float* part, int ks, int M, int N, const T* resid, T* out, float* ss_out,
                       int32_t* lens_add, int lens_inc, int n_seq, T* branch, hipStream_t s, const int32_t* lens_cu,
-                      int ss_128) {
+                      int ss_128, _Float16* out16, const float* gamma16) {
   if (M <= 0) return;
   dim3 grid((N + 255) / 256, M);
   hipLaunchKernelGGL(k_epi_resid<T>, grid, dim3(256), 0, s, part, ks, M, N, resid, out, ss_out, lens_add,
-                     lens_inc, n_seq, branch, lens_cu, ss_128);
+                     lens_inc, n_seq, branch, lens_cu, ss_128, out16, gamma16);
 }
 
 // ---------------------------------------------------------------------------
@@ -193,7 +197,7 @@ void launch_reduce_f32(const float* part, int ks, int M, int N, float* out, hipS
   template void launch_epi_qkv<T>(const float*, int, int, int, int, RowStat, int, const float2*, int, T*, KVView, \
                                   hipStream_t);                                                                 \
   template void launch_epi_resid<T>(const float*, int, int, int, const T*, T*, float*, int32_t*, int, int, T*,    \
-                                    hipStream_t, const int32_t*, int);                                          \
+                                    hipStream_t, const int32_t*, int, _Float16*, const float*);                 \
   template void launch_epi_swiglu<T>(const float*, int, int, int, int, RowStat, T*, hipStream_t);
 INST(float)
 INST(bf16_t)

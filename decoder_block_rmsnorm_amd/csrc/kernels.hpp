@@ -252,7 +252,8 @@ void launch_epi_qkv(const float* part, int ks, int M, int Nq, int Nkv, RowStat s
 template <typename T>
 void launch_epi_resid(const float* part, int ks, int M, int N, const T* resid, T* out, float* ss_out,
                       int32_t* lens_add, int lens_inc, int n_seq, T* branch, hipStream_t s,
-                      const int32_t* lens_cu = nullptr, int ss_128 = 0);
+                      const int32_t* lens_cu = nullptr, int ss_128 = 0, _Float16* out16 = nullptr,
+                      const float* gamma16 = nullptr);
 template <typename T>
 void launch_epi_swiglu(const float* part, int ks, int M, int F2, int ib, RowStat stat, T* g_out,
                        hipStream_t s);
