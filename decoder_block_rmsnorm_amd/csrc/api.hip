@@ -749,11 +749,21 @@ static void fp32_path(const llama_block* blk, KVView kv, const void* x, void* y,
   mk(s);
 }
 
+// A 4-bit block whose W2 product splits K (its residual then runs as a kernel
+// of its own) and whose QKV product reads fp16 A: in a stack's prompt pass the
+// W2 residual kernel can write the next block's fp16 A, y * gamma1 (next).
+static bool q4_x16_chain(const Dims& d, int M) {
+  return d.q4 && gemm_q4_direct_ok(M, d.D, d.F) && gemm_split_k_q4(M, d.D, d.F) > 1 &&
+         gemm_q4_direct_ok(M, d.Nqkv, d.D);
+}
+
 // xstat bit 0: x's sums of squares per 128 columns are already in S.ssx (from
 // the writer of x), so RMSNorm #1 needs no statistic pass; bit 1: the W2
-// residual epilogue writes y's there for the next block
+// residual epilogue writes y's there for the next block; bit 2 (with
+// next_g1, honoured when q4_x16_chain holds): it also writes fp16(y * next_g1)
+// to the fp16 A buffer; bit 3: that buffer already holds fp16(x * gamma1)
 static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void* y, int B, int L, int M, char* sc,
-                         const SLayout& S, Marker& mk, hipStream_t s, int xstat) {
+                         const SLayout& S, Marker& mk, hipStream_t s, int xstat, const float* next_g1) {
   const Dims& d = blk->dm;
   float* inv1 = (float*)(sc + S.inv1);
   float* inv2 = (float*)(sc + S.inv2);
@@ -803,7 +813,7 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
   if (!x_in) launch_rms_inv<bf16_t>((const bf16_t*)x, M, d.D, eps, inv1, s);
   mk(s);
   GemmArgs a{};
-  operands(a, (const bf16_t*)x, blk->qkv, blk->gamma1);
+  operands(a, (const bf16_t*)x, blk->qkv, blk->gamma1, (xstat & 8) != 0 && q4_x16_chain(d, M));
   a.M = M; a.N = d.Nqkv; a.K = d.D;
   if (x_in) {
     a.rstat.ss = ssx; a.rstat.nb = d.D / 128; a.rstat.M = M; a.rstat.n = d.D; a.rstat.eps = eps;
@@ -865,8 +875,9 @@ static void bf16_prefill(const llama_block* blk, KVView kv, const void* x, void*
   }
   launch_gemm_mfma(EPI_SWIGLU, f, s);
   mk(s);
+  const bool x16 = (xstat & 4) && next_g1 && q4_x16_chain(d, M);
   resid_gemm(g, blk->w2, h, (bf16_t*)y, d.F, kv.lens, L, blk->diag ? (bf16_t*)(sc + S.ffn) : nullptr,
-             stat128 && (xstat & 2) ? ssx : nullptr);
+             stat128 && (xstat & 2) ? ssx : nullptr, x16 ? a16 : nullptr, next_g1);
   mk(s);
 }
 
@@ -980,7 +991,8 @@ static void bf16_decode(const llama_block* blk, KVView kv, const void* x, void* 
 // Ls (prefill only, may be null): a ragged call's new tokens per sequence.
 static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const void* x, void* y, int batch, int L,
                             void* scratch, size_t sbytes, bool decode, int n_splits_override, int split_len_override,
-                            hipStream_t s, const int32_t* Ls = nullptr, int xstat = 0) {
+                            hipStream_t s, const int32_t* Ls = nullptr, int xstat = 0,
+                            const float* next_g1 = nullptr) {
   SLayout S;
   llama_status st = check_call(blk, c, layer, x, y, batch, L, Ls, scratch, sbytes, decode,
                                n_splits_override > 0 ? split_len_override : kSplitLen, &S);
@@ -1022,7 +1034,7 @@ static llama_status enqueue(llama_block* blk, llama_kvcache* c, int layer, const
   if (!d.bf16) {
     fp32_path<float>(blk, kv, x, y, batch, L, M, sc, S, mk, s);
   } else if (!decode) {
-    bf16_prefill(blk, kv, x, y, batch, L, M, sc, S, mk, s, xstat);
+    bf16_prefill(blk, kv, x, y, batch, L, M, sc, S, mk, s, xstat, next_g1);
   } else {
     if (n_splits_override > 0) bf16_decode(blk, kv, x, y, batch, sc, S, n_splits_override, split_len_override, mk, s);
     else bf16_decode(blk, kv, x, y, batch, sc, S, S.n_splits, S.split_len, mk, s);
@@ -1295,6 +1307,19 @@ static float* stack_x_stats(const llama_stack* st, void* bs, int T) {
   return (float*)((char*)bs + scratch_layout(st->blocks[0]->cfg, d, T, 1, st->blocks[0]->cfg.max_seq, false).ssx);
 }
 
+// prompt-pass flags of layer l over n rows (bf16_prefill's xstat): statistics
+// of x from its writer when xs; with 4-bit layers whose W2 residual runs as a
+// kernel of its own, each layer's fp16 A written by the layer before it
+static int stack_xstat(const llama_stack* st, int l, int n, bool xs) {
+  const int NL = (int)st->blocks.size();
+  int f = xs ? 1 | (l + 1 < NL ? 2 : 0) : 0;
+  if (q4_x16_chain(st->blocks[l]->dm, n)) {
+    if (l + 1 < NL) f |= 4;
+    if (l > 0) f |= 8;
+  }
+  return f;
+}
+
 extern "C" llama_status llama_stack_generate(llama_stack* st, llama_kvcache* cache, const int32_t* prompt, int32_t P,
                                              int32_t n_steps, int32_t* ids_out, float* logits_out, void* scratch,
                                              size_t sbytes, int32_t use_graph, void* stream) {
@@ -1335,8 +1360,9 @@ extern "C" llama_status llama_stack_generate(llama_stack* st, llama_kvcache* cac
   float* xs = stack_x_stats(st, bs, P);
   launch_embed<bf16_t>((const bf16_t*)st->emb, V, D, prompt, P, x, s, xs);
   for (int l = 0; l < NL; ++l) {
-    const int xstat = xs ? 1 | (l + 1 < NL ? 2 : 0) : 0;
-    if ((r = enqueue(st->blocks[l], cache, l, x, x, 1, P, bs, L.blk_bytes, false, 0, 0, s, nullptr, xstat)) != LLAMA_OK)
+    const int xstat = stack_xstat(st, l, P, xs != nullptr);
+    if ((r = enqueue(st->blocks[l], cache, l, x, x, 1, P, bs, L.blk_bytes, false, 0, 0, s, nullptr, xstat,
+                     l + 1 < NL ? st->blocks[l + 1]->gamma1 : nullptr)) != LLAMA_OK)
       return r;
   }
   if ((r = head(x + (size_t)(P - 1) * D)) != LLAMA_OK) return r;
@@ -1428,8 +1454,9 @@ extern "C" llama_status llama_stack_generate_recompute(llama_stack* st, llama_kv
     float* xs = stack_x_stats(st, bs, n);
     launch_embed<bf16_t>((const bf16_t*)st->emb, V, D, seq, n, x, s, xs);
     for (int l = 0; l < NL; ++l) {
-      const int xstat = xs ? 1 | (l + 1 < NL ? 2 : 0) : 0;
-      llama_status r = enqueue(st->blocks[l], cache, l, x, x, 1, n, bs, L.blk_bytes, false, 0, 0, s, nullptr, xstat);
+      const int xstat = stack_xstat(st, l, n, xs != nullptr);
+      llama_status r = enqueue(st->blocks[l], cache, l, x, x, 1, n, bs, L.blk_bytes, false, 0, 0, s, nullptr, xstat,
+                               l + 1 < NL ? st->blocks[l + 1]->gamma1 : nullptr);
       if (r != LLAMA_OK) return r;
     }
     Sampling smp = st->smp;
