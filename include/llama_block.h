@@ -34,6 +34,10 @@
  *  - Activation dtype is LLAMA_F32 (fp32) or LLAMA_BF16 (bf16, fp32 accumulate).
  *  - Nothing in the library is thread-safe against concurrent calls on the same
  *    handle; distinct handles may be used from distinct threads.
+ *  - Tracing: every block, stack, head, sampling and embedding entry point opens
+ *    a roctx range named after itself (seen by rocprofv3 --marker-trace); with
+ *    the environment variable LLAMA_LOG set to a value other than 0 the library
+ *    prints each launch plan it picks to stderr (read once per process).
  */
 #ifndef LLAMA_BLOCK_H_
 #define LLAMA_BLOCK_H_
