@@ -320,6 +320,9 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_attn_prefill_bf16(const bf16_t*
     sn[1] = (f32x16){};
     float psum = 0.f;
     __builtin_amdgcn_sched_barrier(0);
+    // (raised issue priority while this wavefront feeds the matrix core: the
+    // SIMD's other wavefront, often in its vector-only softmax, yields to it)
+    __builtin_amdgcn_s_setprio(1);
     static_for_fa<0, 16>([&](auto jc) __attribute__((always_inline)) {
       constexpr int j = decltype(jc)::value;
       sn[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j % AHEAD], qf[j >> 1], sn[j & 1], 0, 0, 0);
@@ -336,6 +339,7 @@ __global__ __launch_bounds__(NWV * 64, 2) void k_attn_prefill_bf16(const bf16_t*
     psum += xor_lane<32>(psum, lane);
     l_run += psum;
     pv(t, sc);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // prologue: K(t0), V(t0), K(t0+1) resident, S(t0) computed
